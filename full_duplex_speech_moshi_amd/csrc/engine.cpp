@@ -1,0 +1,743 @@
+// Host side of libpp.so: argument validation, per-slot session state
+// (position, previous column, forced-frame queue), arena layout, and the tick
+// graph (all kernels of one tick captured once per handle and replayed each
+// tick; guide "架构": static shapes and a fixed-capacity ring so the whole
+// step can be captured).
+#include <hip/hip_runtime.h>
+
+#include <array>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <functional>
+#include <string>
+#include <vector>
+
+#include "../../include/pp.h"
+#include "kernels.h"
+
+using namespace pp;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int DEP_WINDOW = 16;  // depformer per-frame keys (one per codebook step)
+
+struct Layout {
+  // byte offsets into the arena
+  size_t ring, dkv, x, xa, part, q, att_part, o, m, hidden, text_logits, amax_v, amax_i, u, y, ya, dpart, dq, dout,
+      dm, dep_logits, ti, to, inv_freq, total;
+  int max_chunks, n_amax;
+  long ring_slot_elems, ring_layer_elems, ring_v_off;
+  long dkv_slot_elems, dkv_layer_elems, dkv_v_off;
+};
+
+bool dims_ok(const pp_dims* dm, std::string* why) {
+  auto fail = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (!dm) return fail("dims is NULL");
+  if (dm->n_q != 8 || dm->dep_q != 16) return fail("n_q must be 8 and dep_q 16 (17-row column)");
+  if (dm->d <= 0 || dm->n_layers <= 0 || dm->n_heads <= 0 || dm->ffn <= 0) return fail("bad temporal dims");
+  if (dm->dep_d <= 0 || dm->dep_layers <= 0 || dm->dep_heads <= 0 || dm->dep_ffn <= 0) return fail("bad depformer dims");
+  if (dm->d % dm->n_heads || dm->dep_d % dm->dep_heads) return fail("d not divisible by heads");
+  const int hd = dm->d / dm->n_heads, dhd = dm->dep_d / dm->dep_heads;
+  if ((hd != 32 && hd != 64 && hd != 128) || (dhd != 32 && dhd != 64 && dhd != 128))
+    return fail("head_dim must be 32, 64 or 128");
+  if (dm->d % 32 || dm->ffn % 32 || dm->dep_d % 32 || dm->dep_ffn % 32) return fail("d and ffn must be multiples of 32");
+  if (dm->text_card < 2 || dm->audio_card < 2) return fail("vocabulary too small");
+  if (!(dm->norm_eps >= 0.f) || !(dm->rope_base > 0.f)) return fail("bad eps or rope base");
+  return true;
+}
+
+Layout make_layout(const pp_dims& dm, int B, int W) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + ALIGN - 1) / ALIGN * ALIGN;
+    return o;
+  };
+  const long d = dm.d, H = dm.n_heads, hd = d / H, F = dm.ffn, Vt = dm.text_card, A = dm.audio_card;
+  const long dd = dm.dep_d, dH = dm.dep_heads, dhd = dd / dH, dF = dm.dep_ffn, Q = dm.dep_q;
+  L.ring_layer_elems = 2 * H * (long)W * hd;
+  L.ring_slot_elems = dm.n_layers * L.ring_layer_elems;
+  L.ring_v_off = H * (long)W * hd;
+  L.dkv_layer_elems = 2 * dH * DEP_WINDOW * dhd;
+  L.dkv_slot_elems = dm.dep_layers * L.dkv_layer_elems;
+  L.dkv_v_off = dH * DEP_WINDOW * dhd;
+  L.max_chunks = (W + ATT_CHUNK - 1) / ATT_CHUNK;
+  L.n_amax = (int)((std::max(Vt, A) + ROWS - 1) / ROWS);
+  L.ring = take((size_t)B * L.ring_slot_elems * 2);
+  L.dkv = take((size_t)B * L.dkv_slot_elems * 2);
+  L.x = take(B * d * 4);
+  L.xa = take(B * d * 2);
+  L.part = take(B * (d / 16) * 4);
+  L.q = take(B * d * 4);
+  L.att_part = take((size_t)B * H * L.max_chunks * (hd + 2) * 4);
+  L.o = take(B * d * 2);
+  L.m = take(B * F * 2);
+  L.hidden = take((size_t)(dm.n_layers + 1) * B * d * 4);
+  L.text_logits = take(B * Vt * 4);
+  L.amax_v = take((size_t)B * L.n_amax * 4);
+  L.amax_i = take((size_t)B * L.n_amax * 4);
+  L.u = take(B * Q * dd * 4);
+  L.y = take(B * dd * 4);
+  L.ya = take(B * dd * 2);
+  L.dpart = take(B * (dd / 16) * 4);
+  L.dq = take(B * dd * 4);
+  L.dout = take(B * dd * 2);
+  L.dm = take(B * dF * 2);
+  L.dep_logits = take(B * Q * A * 4);
+  L.ti = take(B * TI_STRIDE * 4);
+  L.to = take(B * TO_STRIDE * 4);
+  L.inv_freq = take((hd / 2) * 8);
+  L.total = off;
+  return L;
+}
+
+struct Slot {
+  int64_t pos = 0;
+  int32_t prev[9];
+  std::deque<std::array<int32_t, 17>> queue;
+  bool live = false, ticked = false;
+};
+
+thread_local std::string g_create_error;
+
+}  // namespace
+
+struct pp_handle {
+  pp_dims dm;
+  int B, W;
+  pp_weights w;
+  Layout lay;
+  char* arena = nullptr;
+  hipStream_t stream = nullptr, cap = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int32_t* ti_host = nullptr;
+  int32_t* to_host = nullptr;
+  std::vector<Slot> slots;
+  std::function<void(hipStream_t)> timed[6];
+  double timed_bytes[6] = {0, 0, 0, 0, 0, 0};
+  std::string err;
+  bool poisoned = false;
+
+  template <class T>
+  T* at(size_t off) const { return reinterpret_cast<T*>(arena + off); }
+
+  int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    err = buf;
+    if (code == PP_EDEVICE) poisoned = true;
+    return code;
+  }
+};
+
+#define HIP_OR_FAIL(h, call)                                                                  \
+  do {                                                                                        \
+    hipError_t e_ = (call);                                                                   \
+    if (e_ != hipSuccess) return (h)->fail(PP_EDEVICE, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+namespace {
+
+void reset_slot(const pp_dims& dm, Slot& s) {
+  s.pos = 0;
+  s.prev[0] = dm.text_card;
+  for (int i = 1; i < 9; ++i) s.prev[i] = dm.audio_card;
+  s.queue.clear();
+  s.live = false;
+  s.ticked = false;
+}
+
+// Record every kernel of one tick on stream s.
+void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
+  const pp_dims& dm = h->dm;
+  const Layout& L = h->lay;
+  const int B = h->B, W = h->W;
+  const int d = dm.d, H = dm.n_heads, hd = d / H, F = dm.ffn, Vt = dm.text_card, A = dm.audio_card;
+  const int dd = dm.dep_d, dH = dm.dep_heads, dhd = dd / dH, dF = dm.dep_ffn, Q = dm.dep_q;
+  const pp_weights& w = h->w;
+  const int* ti = h->at<int>(L.ti);
+  int* to = h->at<int>(L.to);
+  const double* inv_freq = h->at<double>(L.inv_freq);
+
+  EmbedArgs ea{};
+  ea.ti = ti;
+  ea.B = B;
+  ea.d = d;
+  ea.emb_text = w.emb_text;
+  ea.emb_audio = w.emb_audio;
+  ea.text_rows = Vt + 1;
+  ea.audio_rows = A + 1;
+  ea.alpha = w.attn_norm;
+  ea.x = h->at<float>(L.x);
+  ea.xa = h->at<bf16_t>(L.xa);
+  ea.part = h->at<float>(L.part);
+  ea.tap = h->at<float>(L.hidden);
+  launch_embed(ea, s);
+
+  for (int l = 0; l < dm.n_layers; ++l) {
+    bf16_t* ring_l = h->at<bf16_t>(L.ring) + (long)l * L.ring_layer_elems;
+    // fused QKV + rotation + ring write
+    GemmArgs g{};
+    g.W = w.wqkv + (long)l * 3 * d * d;
+    g.X = h->at<bf16_t>(L.xa);
+    g.M = 3 * d;
+    g.K = d;
+    g.ldx = d;
+    g.B = B;
+    g.part_in = h->at<float>(L.part);
+    g.n_part = d / 16;
+    g.feat = d;
+    g.eps = dm.norm_eps;
+    g.q_out = h->at<float>(L.q);
+    g.ldq = d;
+    g.kv = ring_l;
+    g.kv_slot_stride = L.ring_slot_elems;
+    g.kv_v_off = L.ring_v_off;
+    g.n_heads = H;
+    g.head_dim = hd;
+    g.window = W;
+    g.ti = ti;
+    g.inv_freq = inv_freq;
+    launch_gemm(EPI_QKV, g, s);
+    if (keep_timed && l == 0) {
+      h->timed[0] = [g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); };
+      h->timed_bytes[0] = 2.0 * 3 * d * d + B * (2.0 * d + 4.0 * d / 16 + 4.0 * d + 4.0 * d);
+    }
+
+    AttnArgs at{};
+    at.q = h->at<float>(L.q);
+    at.ldq = d;
+    at.kv = ring_l;
+    at.kv_slot_stride = L.ring_slot_elems;
+    at.kv_v_off = L.ring_v_off;
+    at.n_heads = H;
+    at.head_dim = hd;
+    at.window = W;
+    at.B = B;
+    at.ti = ti;
+    at.part = h->at<float>(L.att_part);
+    at.max_chunks = L.max_chunks;
+    at.o = h->at<bf16_t>(L.o);
+    at.ldo = d;
+    launch_attention(at, s);
+    launch_attention_combine(at, s);
+    if (keep_timed && l == 0) {
+      h->timed[1] = [at](hipStream_t st) { launch_attention(at, st); };
+      h->timed_bytes[1] = -1;  // depends on positions; computed at timing
+    }
+
+    GemmArgs go{};
+    go.W = w.wo + (long)l * d * d;
+    go.X = h->at<bf16_t>(L.o);
+    go.M = d;
+    go.K = d;
+    go.ldx = d;
+    go.B = B;
+    go.x = h->at<float>(L.x);
+    go.ldres = d;
+    go.xa_out = h->at<bf16_t>(L.xa);
+    go.alpha_next = w.mlp_norm + (long)l * d;
+    go.part_out = h->at<float>(L.part);
+    launch_gemm(EPI_RESID, go, s);
+    if (keep_timed && l == 0) {
+      h->timed[2] = [go](hipStream_t st) { launch_gemm(EPI_RESID, go, st); };
+      h->timed_bytes[2] = 2.0 * d * d + B * (2.0 * d + 4.0 * d + 4.0 * d + 2.0 * d + 4.0 * d / 16);
+    }
+
+    GemmArgs gu{};
+    gu.W = w.w_in + (long)l * 2 * F * d;
+    gu.X = h->at<bf16_t>(L.xa);
+    gu.M = F;
+    gu.K = d;
+    gu.ldx = d;
+    gu.B = B;
+    gu.gate_off = F;
+    gu.part_in = h->at<float>(L.part);
+    gu.n_part = d / 16;
+    gu.feat = d;
+    gu.eps = dm.norm_eps;
+    gu.m_out = h->at<bf16_t>(L.m);
+    gu.ldm = F;
+    launch_gemm(EPI_GATED, gu, s);
+    if (keep_timed && l == 0) {
+      h->timed[3] = [gu](hipStream_t st) { launch_gemm(EPI_GATED, gu, st); };
+      h->timed_bytes[3] = 2.0 * 2 * F * d + B * (2.0 * d + 4.0 * d / 16 + 2.0 * F);
+    }
+
+    GemmArgs gd{};
+    gd.W = w.w_out + (long)l * d * F;
+    gd.X = h->at<bf16_t>(L.m);
+    gd.M = d;
+    gd.K = F;
+    gd.ldx = F;
+    gd.B = B;
+    gd.x = h->at<float>(L.x);
+    gd.ldres = d;
+    gd.xa_out = h->at<bf16_t>(L.xa);
+    gd.alpha_next = (l + 1 < dm.n_layers) ? w.attn_norm + (long)(l + 1) * d : w.out_norm;
+    gd.part_out = h->at<float>(L.part);
+    gd.tap = h->at<float>(L.hidden) + (long)(l + 1) * B * d;
+    launch_gemm(EPI_RESID, gd, s);
+    if (keep_timed && l == 0) {
+      h->timed[4] = [gd](hipStream_t st) { launch_gemm(EPI_RESID, gd, st); };
+      h->timed_bytes[4] = 2.0 * d * F + B * (2.0 * F + 4.0 * d + 4.0 * d + 2.0 * d + 4.0 * d + 4.0 * d / 16);
+    }
+  }
+
+  // text head + greedy partials
+  GemmArgs gt{};
+  gt.W = w.text_head;
+  gt.X = h->at<bf16_t>(L.xa);
+  gt.M = Vt;
+  gt.K = d;
+  gt.ldx = d;
+  gt.B = B;
+  gt.part_in = h->at<float>(L.part);
+  gt.n_part = d / 16;
+  gt.feat = d;
+  gt.eps = dm.norm_eps;
+  gt.f_out = h->at<float>(L.text_logits);
+  gt.ldf = Vt;
+  gt.amax_v = h->at<float>(L.amax_v);
+  gt.amax_i = h->at<int>(L.amax_i);
+  gt.ld_amax = L.n_amax;
+  launch_gemm(EPI_LOGITS, gt, s);
+  if (keep_timed) {
+    h->timed[5] = [gt](hipStream_t st) { launch_gemm(EPI_LOGITS, gt, st); };
+    h->timed_bytes[5] = 2.0 * Vt * d + B * (2.0 * d + 4.0 * d / 16 + 4.0 * Vt);
+  }
+
+  // all 16 depformer input projections of z at once
+  GemmArgs gp{};
+  gp.W = w.dep_in_proj;
+  gp.X = h->at<bf16_t>(L.xa);
+  gp.M = Q * dd;
+  gp.K = d;
+  gp.ldx = d;
+  gp.B = B;
+  gp.part_in = h->at<float>(L.part);
+  gp.n_part = d / 16;
+  gp.feat = d;
+  gp.eps = dm.norm_eps;
+  gp.f_out = h->at<float>(L.u);
+  gp.ldf = (long)Q * dd;
+  launch_gemm(EPI_STORE, gp, s);
+
+  FinishArgs fa{};
+  fa.B = B;
+  fa.step = -1;
+  fa.n_part = (Vt + ROWS - 1) / ROWS;
+  fa.amax_v = h->at<float>(L.amax_v);
+  fa.amax_i = h->at<int>(L.amax_i);
+  fa.ld_amax = L.n_amax;
+  fa.ti = ti;
+  fa.to = to;
+  fa.dep_q = Q;
+  fa.dd = dd;
+  fa.u = h->at<float>(L.u);
+  fa.table = w.dep_emb_text;
+  fa.alpha = w.dep_attn_norm;
+  fa.y = h->at<float>(L.y);
+  fa.ya = h->at<bf16_t>(L.ya);
+  fa.part = h->at<float>(L.dpart);
+  launch_finish(fa, s);
+
+  for (int k = 0; k < Q; ++k) {
+    for (int l = 0; l < dm.dep_layers; ++l) {
+      bf16_t* dkv_l = h->at<bf16_t>(L.dkv) + (long)l * L.dkv_layer_elems;
+      GemmArgs g{};
+      g.W = w.dep_wqkv + (long)l * 3 * dd * dd;
+      g.X = h->at<bf16_t>(L.ya);
+      g.M = 3 * dd;
+      g.K = dd;
+      g.ldx = dd;
+      g.B = B;
+      g.part_in = h->at<float>(L.dpart);
+      g.n_part = dd / 16;
+      g.feat = dd;
+      g.eps = dm.norm_eps;
+      g.q_out = h->at<float>(L.dq);
+      g.ldq = dd;
+      g.kv = dkv_l;
+      g.kv_slot_stride = L.dkv_slot_elems;
+      g.kv_v_off = L.dkv_v_off;
+      g.n_heads = dH;
+      g.head_dim = dhd;
+      g.window = DEP_WINDOW;
+      g.ti = nullptr;
+      g.pos_const = k;
+      g.inv_freq = nullptr;
+      launch_gemm(EPI_QKV, g, s);
+
+      AttnArgs at{};
+      at.q = h->at<float>(L.dq);
+      at.ldq = dd;
+      at.kv = dkv_l;
+      at.kv_slot_stride = L.dkv_slot_elems;
+      at.kv_v_off = L.dkv_v_off;
+      at.n_heads = dH;
+      at.head_dim = dhd;
+      at.window = DEP_WINDOW;
+      at.B = B;
+      at.ti = nullptr;
+      at.pos_const = k;
+      at.part = nullptr;
+      at.max_chunks = 1;
+      at.o = h->at<bf16_t>(L.dout);
+      at.ldo = dd;
+      launch_attention(at, s);
+
+      GemmArgs go{};
+      go.W = w.dep_wo + (long)l * dd * dd;
+      go.X = h->at<bf16_t>(L.dout);
+      go.M = dd;
+      go.K = dd;
+      go.ldx = dd;
+      go.B = B;
+      go.x = h->at<float>(L.y);
+      go.ldres = dd;
+      go.xa_out = h->at<bf16_t>(L.ya);
+      go.alpha_next = w.dep_mlp_norm + (long)l * dd;
+      go.part_out = h->at<float>(L.dpart);
+      launch_gemm(EPI_RESID, go, s);
+
+      GemmArgs gu{};
+      gu.W = w.dep_w_in + (long)l * 2 * dF * dd;
+      gu.X = h->at<bf16_t>(L.ya);
+      gu.M = dF;
+      gu.K = dd;
+      gu.ldx = dd;
+      gu.B = B;
+      gu.gate_off = dF;
+      gu.part_in = h->at<float>(L.dpart);
+      gu.n_part = dd / 16;
+      gu.feat = dd;
+      gu.eps = dm.norm_eps;
+      gu.m_out = h->at<bf16_t>(L.dm);
+      gu.ldm = dF;
+      launch_gemm(EPI_GATED, gu, s);
+
+      GemmArgs gd{};
+      gd.W = w.dep_w_out + (long)l * dd * dF;
+      gd.X = h->at<bf16_t>(L.dm);
+      gd.M = dd;
+      gd.K = dF;
+      gd.ldx = dF;
+      gd.B = B;
+      gd.x = h->at<float>(L.y);
+      gd.ldres = dd;
+      gd.xa_out = h->at<bf16_t>(L.ya);
+      gd.alpha_next = (l + 1 < dm.dep_layers) ? w.dep_attn_norm + (long)(l + 1) * dd : w.dep_out_norm;
+      gd.part_out = h->at<float>(L.dpart);
+      launch_gemm(EPI_RESID, gd, s);
+    }
+    GemmArgs gh{};
+    gh.W = w.dep_heads + (long)k * A * dd;
+    gh.X = h->at<bf16_t>(L.ya);
+    gh.M = A;
+    gh.K = dd;
+    gh.ldx = dd;
+    gh.B = B;
+    gh.part_in = h->at<float>(L.dpart);
+    gh.n_part = dd / 16;
+    gh.feat = dd;
+    gh.eps = dm.norm_eps;
+    gh.f_out = h->at<float>(L.dep_logits) + (long)k * A;
+    gh.ldf = (long)Q * A;
+    gh.amax_v = h->at<float>(L.amax_v);
+    gh.amax_i = h->at<int>(L.amax_i);
+    gh.ld_amax = L.n_amax;
+    launch_gemm(EPI_LOGITS, gh, s);
+
+    FinishArgs f = fa;
+    f.step = k;
+    f.n_part = (A + ROWS - 1) / ROWS;
+    f.table = (k + 1 < Q) ? w.dep_emb_audio + (long)k * (A + 1) * dd : nullptr;
+    launch_finish(f, s);
+  }
+}
+
+// Fill the tick-input staging buffer from slot state; frames[b] = forced
+// frame consumed this tick or nullptr.
+void build_tick_input(pp_handle* h, const int32_t* user_codes, const std::array<int32_t, 17>** frames) {
+  for (int b = 0; b < h->B; ++b) {
+    int32_t* t = h->ti_host + b * TI_STRIDE;
+    const Slot& s = h->slots[b];
+    t[TI_POS] = (int32_t)s.pos;
+    for (int i = 0; i < 9; ++i) t[TI_COL + i] = s.prev[i];
+    const std::array<int32_t, 17>* f = frames ? frames[b] : nullptr;
+    for (int i = 0; i < 8; ++i) t[TI_COL + 9 + i] = f ? (*f)[9 + i] : (user_codes ? user_codes[b * 8 + i] : 0);
+    for (int i = 0; i < 9; ++i) t[TI_FORCE + i] = f ? (*f)[i] : -1;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int pp_arena_bytes(const pp_dims* dims, int B, int window, size_t* out_bytes) {
+  std::string why;
+  if (!out_bytes || !dims_ok(dims, &why) || B < 1 || B > PP_MAX_BATCH || window < 1) return PP_EINVAL;
+  *out_bytes = make_layout(*dims, B, window).total;
+  return PP_OK;
+}
+
+int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void* arena, size_t arena_bytes,
+              void* stream, pp_handle** out) {
+  std::string why;
+  if (!out) { g_create_error = "out is NULL"; return PP_EINVAL; }
+  *out = nullptr;
+  if (!dims_ok(dims, &why)) { g_create_error = why; return PP_EINVAL; }
+  if (B < 1 || B > PP_MAX_BATCH) { g_create_error = "B out of [1, 32]"; return PP_EINVAL; }
+  if (window < 1) { g_create_error = "window < 1"; return PP_EINVAL; }
+  if (!w || !arena) { g_create_error = "weights or arena is NULL"; return PP_EINVAL; }
+  const void* const* wp = reinterpret_cast<const void* const*>(w);
+  for (size_t i = 0; i < sizeof(pp_weights) / sizeof(void*); ++i)
+    if (!wp[i]) { g_create_error = "a weight pointer is NULL"; return PP_EINVAL; }
+  if (reinterpret_cast<uintptr_t>(arena) % ALIGN) { g_create_error = "arena not 256-byte aligned"; return PP_EINVAL; }
+  const Layout lay = make_layout(*dims, B, window);
+  if (arena_bytes < lay.total) { g_create_error = "arena too small"; return PP_ENOSPC; }
+
+  pp_handle* h = new (std::nothrow) pp_handle();
+  if (!h) { g_create_error = "out of host memory"; return PP_ENOSPC; }
+  h->dm = *dims;
+  h->B = B;
+  h->W = window;
+  h->w = *w;
+  h->lay = lay;
+  h->arena = static_cast<char*>(arena);
+  h->stream = static_cast<hipStream_t>(stream);
+  h->slots.resize(B);
+  for (auto& s : h->slots) reset_slot(*dims, s);
+
+  auto bail = [&](const char* what, hipError_t e) {
+    g_create_error = std::string(what) + ": " + hipGetErrorString(e);
+    pp_destroy(h);
+    return PP_EDEVICE;
+  };
+  hipError_t e;
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->ti_host), B * TI_STRIDE * 4, hipHostMallocDefault)) != hipSuccess)
+    return bail("hipHostMalloc", e);
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->to_host), B * TO_STRIDE * 4, hipHostMallocDefault)) != hipSuccess)
+    return bail("hipHostMalloc", e);
+  std::memset(h->ti_host, 0, B * TI_STRIDE * 4);
+  std::memset(h->to_host, 0, B * TO_STRIDE * 4);
+
+  // RoPE frequencies base^(-2i/head_dim), fp64 host math.
+  const int hd = dims->d / dims->n_heads;
+  std::vector<double> freq(hd / 2);
+  for (int i = 0; i < hd / 2; ++i) freq[i] = std::pow((double)dims->rope_base, -2.0 * i / hd);
+  if ((e = hipMemcpyAsync(h->at<double>(lay.inv_freq), freq.data(), freq.size() * 8, hipMemcpyHostToDevice,
+                          h->stream)) != hipSuccess)
+    return bail("hipMemcpyAsync", e);
+  build_tick_input(h, nullptr, nullptr);
+  if ((e = hipMemcpyAsync(h->at<int>(lay.ti), h->ti_host, B * TI_STRIDE * 4, hipMemcpyHostToDevice, h->stream)) !=
+      hipSuccess)
+    return bail("hipMemcpyAsync", e);
+  if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
+
+  if ((e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
+  if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess)
+    return bail("hipStreamBeginCapture", e);
+  record_tick(h, h->cap, true);
+  if ((e = hipStreamEndCapture(h->cap, &h->graph)) != hipSuccess) return bail("hipStreamEndCapture", e);
+  if ((e = hipGetLastError()) != hipSuccess) return bail("kernel launch during capture", e);
+  if ((e = hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0)) != hipSuccess)
+    return bail("hipGraphInstantiate", e);
+  *out = h;
+  return PP_OK;
+}
+
+int pp_prefill_forced(pp_handle* h, int slot, const int32_t* frames, int n) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (slot < 0 || slot >= h->B) return h->fail(PP_EINVAL, "slot %d out of [0,%d)", slot, h->B);
+  if (n < 0 || (n > 0 && !frames)) return h->fail(PP_EINVAL, "bad frame count or NULL frames");
+  Slot& s = h->slots[slot];
+  if (s.live) return h->fail(PP_EBUSY, "slot %d is free-running; persona and voice are fixed at open", slot);
+  if (s.queue.size() + (size_t)n > PP_MAX_QUEUE) return h->fail(PP_ENOSPC, "forced queue full");
+  const int Vt = h->dm.text_card, A = h->dm.audio_card;
+  for (int i = 0; i < n; ++i) {
+    const int32_t* f = frames + i * 17;
+    if (f[0] < -1 || f[0] >= Vt) return h->fail(PP_EINVAL, "frame %d: text token %d out of range", i, f[0]);
+    for (int r = 1; r < 9; ++r)
+      if (f[r] < -1 || f[r] >= A) return h->fail(PP_EINVAL, "frame %d: agent code %d out of range", i, f[r]);
+    for (int r = 9; r < 17; ++r)
+      if (f[r] < 0 || f[r] >= A) return h->fail(PP_EINVAL, "frame %d: user code %d out of range", i, f[r]);
+  }
+  for (int i = 0; i < n; ++i) {
+    std::array<int32_t, 17> a;
+    std::memcpy(a.data(), frames + i * 17, sizeof a);
+    s.queue.push_back(a);
+  }
+  return PP_OK;
+}
+
+int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (!user_codes || !tokens) return h->fail(PP_EINVAL, "NULL user_codes or tokens");
+  const int A = h->dm.audio_card;
+  for (int b = 0; b < h->B; ++b) {
+    if (h->slots[b].pos >= 0x7fffffff) return h->fail(PP_EINVAL, "slot %d position overflow", b);
+    if (!h->slots[b].queue.empty()) continue;  // codes of this slot are replaced by the forced frame
+    for (int i = 0; i < 8; ++i) {
+      const int32_t c = user_codes[b * 8 + i];
+      if (c < 0 || c >= A) return h->fail(PP_EINVAL, "slot %d user code %d out of range", b, c);
+    }
+  }
+  std::vector<const std::array<int32_t, 17>*> frames(h->B, nullptr);
+  for (int b = 0; b < h->B; ++b)
+    if (!h->slots[b].queue.empty()) frames[b] = &h->slots[b].queue.front();
+  build_tick_input(h, user_codes, frames.data());
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.ti), h->ti_host, h->B * TI_STRIDE * 4, hipMemcpyHostToDevice,
+                                h->stream));
+  HIP_OR_FAIL(h, hipGraphLaunch(h->exec, h->stream));
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->to_host, h->at<int>(h->lay.to), h->B * TO_STRIDE * 4, hipMemcpyDeviceToHost,
+                                h->stream));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  for (int b = 0; b < h->B; ++b) {
+    Slot& s = h->slots[b];
+    const int32_t* o = h->to_host + b * TO_STRIDE;
+    for (int i = 0; i < 9; ++i) {
+      tokens[b * 9 + i] = o[TO_PRED + i];
+      s.prev[i] = o[TO_CHOSEN + i];
+    }
+    if (frames[b]) s.queue.pop_front();
+    else s.live = true;
+    s.ticked = true;
+    s.pos += 1;
+  }
+  return PP_OK;
+}
+
+int pp_slot_reset(pp_handle* h, int slot) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (slot < 0 || slot >= h->B) return h->fail(PP_EINVAL, "slot %d out of [0,%d)", slot, h->B);
+  reset_slot(h->dm, h->slots[slot]);
+  return PP_OK;
+}
+
+int pp_ring_fill(pp_handle* h, int slot, int n, const uint16_t* k, const uint16_t* v) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (slot < 0 || slot >= h->B) return h->fail(PP_EINVAL, "slot %d out of [0,%d)", slot, h->B);
+  if (n < 0 || n > h->W) return h->fail(PP_EINVAL, "fill of %d frames outside [0, window=%d]", n, h->W);
+  if (n > 0 && (!k || !v)) return h->fail(PP_EINVAL, "NULL keys or values");
+  Slot& s = h->slots[slot];
+  if (s.ticked || !s.queue.empty()) return h->fail(PP_EBUSY, "fill only before any tick or prefill of the slot");
+  const int L = h->dm.n_layers, H = h->dm.n_heads, hd = h->dm.d / H;
+  std::vector<uint16_t> tmp((size_t)H * n * hd);
+  for (int l = 0; l < L && n > 0; ++l) {
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* src = (kv ? v : k) + (size_t)l * n * H * hd;
+      for (int p = 0; p < n; ++p)
+        for (int hh = 0; hh < H; ++hh)
+          std::memcpy(&tmp[((size_t)hh * n + p) * hd], src + ((size_t)p * H + hh) * hd, hd * 2);
+      bf16_t* dst = h->at<bf16_t>(h->lay.ring) + (long)slot * h->lay.ring_slot_elems + (long)l * h->lay.ring_layer_elems +
+                    (kv ? h->lay.ring_v_off : 0);
+      HIP_OR_FAIL(h, hipMemcpy2DAsync(dst, (size_t)h->W * hd * 2, tmp.data(), (size_t)n * hd * 2, (size_t)n * hd * 2,
+                                      H, hipMemcpyHostToDevice, h->stream));
+      HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+    }
+  }
+  s.pos = n;
+  return PP_OK;
+}
+
+int pp_taps(const pp_handle* h, pp_taps_t* out) {
+  if (!h || !out) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  out->hidden = h->at<float>(h->lay.hidden);
+  out->text_logits = h->at<float>(h->lay.text_logits);
+  out->dep_logits = h->at<float>(h->lay.dep_logits);
+  out->tokens = h->at<int32_t>(h->lay.to);
+  return PP_OK;
+}
+
+int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* bytes) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (which < 0 || which > 5 || iters < 1 || !avg_ms) return h->fail(PP_EINVAL, "bad kernel id, iters or output");
+  double by = h->timed_bytes[which];
+  if (which == 1) {  // attention: KV bytes from each slot's current window
+    const int H = h->dm.n_heads, hd = h->dm.d / H;
+    by = 0;
+    for (int b = 0; b < h->B; ++b) {
+      const long n = std::min<long>(h->slots[b].pos + 1, h->W);
+      by += 2.0 * n * H * hd * 2 + 4.0 * h->dm.d + 2.0 * h->dm.d;
+    }
+  }
+  if (bytes) *bytes = by;
+  build_tick_input(h, nullptr, nullptr);
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.ti), h->ti_host, h->B * TI_STRIDE * 4, hipMemcpyHostToDevice,
+                                h->stream));
+  hipEvent_t e0, e1;
+  HIP_OR_FAIL(h, hipEventCreate(&e0));
+  HIP_OR_FAIL(h, hipEventCreate(&e1));
+  h->timed[which](h->stream);  // warm
+  HIP_OR_FAIL(h, hipEventRecord(e0, h->stream));
+  for (int i = 0; i < iters; ++i) h->timed[which](h->stream);
+  HIP_OR_FAIL(h, hipEventRecord(e1, h->stream));
+  HIP_OR_FAIL(h, hipEventSynchronize(e1));
+  float ms = 0;
+  HIP_OR_FAIL(h, hipEventElapsedTime(&ms, e0, e1));
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  HIP_OR_FAIL(h, hipGetLastError());
+  *avg_ms = ms / iters;
+  return PP_OK;
+}
+
+int pp_time_graph(pp_handle* h, int iters, float* avg_ms) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (iters < 1 || !avg_ms) return h->fail(PP_EINVAL, "bad iters or output");
+  build_tick_input(h, nullptr, nullptr);
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.ti), h->ti_host, h->B * TI_STRIDE * 4, hipMemcpyHostToDevice,
+                                h->stream));
+  hipEvent_t e0, e1;
+  HIP_OR_FAIL(h, hipEventCreate(&e0));
+  HIP_OR_FAIL(h, hipEventCreate(&e1));
+  HIP_OR_FAIL(h, hipGraphLaunch(h->exec, h->stream));
+  HIP_OR_FAIL(h, hipEventRecord(e0, h->stream));
+  for (int i = 0; i < iters; ++i) HIP_OR_FAIL(h, hipGraphLaunch(h->exec, h->stream));
+  HIP_OR_FAIL(h, hipEventRecord(e1, h->stream));
+  HIP_OR_FAIL(h, hipEventSynchronize(e1));
+  float ms = 0;
+  HIP_OR_FAIL(h, hipEventElapsedTime(&ms, e0, e1));
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *avg_ms = ms / iters;
+  return PP_OK;
+}
+
+void pp_destroy(pp_handle* h) {
+  if (!h) return;
+  if (h->exec) (void)hipGraphExecDestroy(h->exec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  if (h->cap) (void)hipStreamDestroy(h->cap);
+  if (h->ti_host) (void)hipHostFree(h->ti_host);
+  if (h->to_host) (void)hipHostFree(h->to_host);
+  delete h;
+}
+
+const char* pp_last_error(const pp_handle* h) {
+  if (!h) return g_create_error.c_str();
+  return h->err.c_str();
+}
+
+}  // extern "C"

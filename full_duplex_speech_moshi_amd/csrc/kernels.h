@@ -1,0 +1,103 @@
+// Kernel launchers of the lockstep tick (gfx950).  Internal to libpp.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pp {
+
+typedef uint16_t bf16_t;
+
+// Per-tick device input, int32 [B][TI_STRIDE].
+enum {
+  TI_POS = 0,        // absolute position of this tick
+  TI_COL = 1,        // 17 column rows: [1..9] previous chosen text+agent, [10..17] user codes
+  TI_FORCE = 18,     // 9 forced choices for text, agent 0..7 (-1 = free)
+  TI_STRIDE = 32
+};
+
+// Per-tick device output, int32 [B][TO_STRIDE].
+enum {
+  TO_PRED = 0,       // 9: text, agent 0..7 predictions
+  TO_USER = 9,       // 8: depformer steps 8..15 predictions
+  TO_CHOSEN = 17,    // 9: chosen text, agent 0..7
+  TO_TOK = 26,       // 1: the token fed to the next depformer step
+  TO_STRIDE = 32
+};
+
+constexpr int ROWS = 16;           // MFMA row tile
+constexpr int GEMM_WAVES = 8;      // waves per GEMM workgroup (split K)
+constexpr int ATT_CHUNK = 256;     // keys per split of the flash-decoding pass
+constexpr int MAX_COLS = 32;       // slots per launch (two 16-wide column tiles)
+
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GATED = 2, EPI_LOGITS = 3, EPI_STORE = 4 };
+
+struct GemmArgs {
+  const bf16_t* W;      // [M][K] (gated: gate rows, up rows start at W + gate_off*K)
+  const bf16_t* X;      // [B][ldx] bf16 activations
+  int M, K, ldx, B;
+  long gate_off;        // gated: row offset of the up half
+  // inverse-RMS source: sum-of-squares partials [B][n_part] (one per 16 features)
+  const float* part_in; int n_part; int feat; float eps;
+  // EPI_QKV
+  float* q_out;         // [B][ldq] fp32 (rotated queries)
+  int ldq;
+  bf16_t* kv;           // ring base for this layer: slot b at kv + b*kv_slot_stride; K at +0, V at +kv_v_off
+  long kv_slot_stride, kv_v_off;
+  int n_heads, head_dim, window;
+  const int* ti;        // tick input (positions) or null
+  int pos_const;        // position when ti == null
+  const double* inv_freq; // [head_dim/2] or null (no rotation)
+  // EPI_RESID
+  float* x;             // [B][ldres] residual stream (read-modify-write)
+  int ldres;
+  bf16_t* xa_out;       // [B][ldres] bf16(x * alpha_next)
+  const float* alpha_next;
+  float* part_out;      // [B][M/16] sum of squares per 16 rows
+  float* tap;           // [B][ldres] copy of x (nullable)
+  // EPI_GATED / EPI_STORE / EPI_LOGITS
+  bf16_t* m_out; int ldm;        // gated: [B][ldm] bf16 silu(g)*u
+  float* f_out; long ldf;        // store / logits: [B][ldf] fp32
+  float* amax_v; int* amax_i; int ld_amax;  // logits: per-workgroup (max, argmax) [B][ld_amax]
+};
+
+void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const float* q;       // [B][ldq], head h at q + h*head_dim
+  int ldq;
+  const bf16_t* kv;     // ring base of this layer (see GemmArgs)
+  long kv_slot_stride, kv_v_off;
+  int n_heads, head_dim, window, B;
+  const int* ti; int pos_const;
+  float* part;          // [B][n_heads][max_chunks][head_dim + 2] (m, l, o...)
+  int max_chunks;
+  bf16_t* o;            // [B][ldo] bf16 output
+  int ldo;
+};
+
+void launch_attention(const AttnArgs& a, hipStream_t s);
+void launch_attention_combine(const AttnArgs& a, hipStream_t s);
+
+struct EmbedArgs {
+  const int* ti; int B, d;
+  const bf16_t* emb_text; const bf16_t* emb_audio; int text_rows, audio_rows;
+  const float* alpha;   // first attention-norm alpha
+  float* x; bf16_t* xa; float* part; float* tap;
+};
+void launch_embed(const EmbedArgs& a, hipStream_t s);
+
+struct FinishArgs {
+  int B, step;          // step -1: text head; 0..dep_q-1: depformer codebook step
+  int n_part;           // argmax partials per slot
+  const float* amax_v; const int* amax_i; int ld_amax;
+  const int* ti; int* to;
+  // next depformer input (step + 1 < dep_q)
+  int dep_q, dd;
+  const float* u;        // [B][dep_q][dd] input projections of z
+  const bf16_t* table;   // input table of step+1 ([rows][dd])
+  const float* alpha;    // first depformer attention-norm alpha
+  float* y; bf16_t* ya; float* part;
+};
+void launch_finish(const FinishArgs& a, hipStream_t s);
+
+}  // namespace pp

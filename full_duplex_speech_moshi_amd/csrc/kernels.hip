@@ -1,0 +1,567 @@
+// HIP kernels of the lockstep tick, written for gfx950 (CDNA4, 64-lane waves).
+//
+// Every kernel is batch-invariant: the arithmetic that produces slot b's
+// values (instruction sequence, summation order, split points) depends only
+// on slot b's own inputs and position, never on B or on other slots, so a
+// session computes the same bits alone or in a full batch ("greedy isolation
+// is bit-exact", PersonaPlex recipe, Summary / Notes).
+#include "kernels.h"
+
+#include <math.h>
+
+namespace pp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf_lo(v[i]);
+    f[2 * i + 1] = bf_hi(v[i]);
+  }
+}
+
+// Fixed butterfly over the 64 lanes of a wave (same order on every call).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Skinny GEMM family  Y[b][m] = sum_k W[m][k] * X[b][k],  b < B <= 32.
+//
+// One workgroup = 8 waves owns a 16-row tile (two tiles, gate and up, for the
+// gated MLP) over the whole K; the waves split K into 8 contiguous ranges and
+// their partial tiles are summed in LDS in wave order.  Each wave streams its
+// weight rows with 16-byte loads (4 lanes cover 64 contiguous bytes of a row)
+// straight into v_mfma_f32_16x16x32_bf16 as the A operand; the slots are the
+// 16 columns of the B operand, zero beyond B.  The MFMA computes every output
+// column from that column alone, so a slot's result does not depend on what
+// occupies the other columns.  Weight streaming is the bound (HBM); the
+// matrix cores are idle most of the time even at B = 32.
+//
+// Normalised inputs: the producer of x stores bf16(x * alpha) and per-16-row
+// sums of squares; the consumer scales its output column b by
+// 1/sqrt(mean(x_b^2) + eps) in the epilogue (RMSNorm commutes with the
+// projection), so no separate normalisation pass is needed.
+// ---------------------------------------------------------------------------
+
+template <int RT, int NT>
+struct GemmSmem {
+  float red[GEMM_WAVES][RT * NT][256];
+  float fin[RT][ROWS][NT * 16];
+  float inv_rms[NT * 16];
+};
+
+template <int NT>
+__device__ __forceinline__ void compute_inv_rms(const GemmArgs& a, float* inv_rms) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int c = wave; c < NT * 16; c += GEMM_WAVES) {
+    float s = 0.f;
+    if (c < a.B) {
+      const float* p = a.part_in + (long)c * a.n_part;
+      for (int i = lane; i < a.n_part; i += 64) s += p[i];
+    }
+    s = wave_sum(s);
+    if (lane == 0) inv_rms[c] = 1.0f / sqrtf(s / (float)a.feat + a.eps);
+  }
+}
+
+template <int EPI, int NT>
+__global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
+  constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
+  constexpr int U = 8;
+  __shared__ GemmSmem<RT, NT> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x;
+  const int ksteps = a.K >> 5;
+  const int s0 = (ksteps * wave) / GEMM_WAVES;
+  const int s1 = (ksteps * (wave + 1)) / GEMM_WAVES;
+
+  const int row = tile * ROWS + r16;
+  const bool a_ok = row < a.M;
+  const bf16_t* arow[RT];
+  arow[0] = a.W + (long)(a_ok ? row : 0) * a.K + g * 8;
+  if (RT == 2) arow[RT - 1] = a.W + (long)((a_ok ? row : 0) + a.gate_off) * a.K + g * 8;
+  const bf16_t* xrow[NT];
+  bool b_ok[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    const int c = ct * 16 + r16;
+    b_ok[ct] = c < a.B;
+    xrow[ct] = a.X + (long)(b_ok[ct] ? c : 0) * a.ldx + g * 8;
+  }
+
+  f32x4 acc[RT][NT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[rt][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+  for (int s = s0; s < s1; s += U) {
+    u32x4 av[RT][U], bv[NT][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = (s + u) < s1;
+      const int k = (s + u) * 32;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) av[rt][u] = (ok && a_ok) ? ld16(arow[rt] + k) : zero;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) bv[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + k) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av[rt][u]), __builtin_bit_cast(bf16x8, bv[ct][u]), acc[rt][ct], 0, 0, 0);
+  }
+
+  // Partial tiles to LDS, then a fixed-order sum over the 8 waves.
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.red[wave][rt * NT + ct][j * 64 + lane] = acc[rt][ct][j];
+  if (EPI != EPI_RESID) compute_inv_rms<NT>(a, sm.inv_rms);
+  __syncthreads();
+  for (int idx = tid; idx < RT * NT * 256; idx += 512) {
+    const int t = idx >> 8, e = idx & 255;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < GEMM_WAVES; ++w) s += sm.red[w][t][e];
+    const int rt = t / NT, ct = t % NT, j = e >> 6, ln = e & 63;
+    sm.fin[rt][4 * (ln >> 4) + j][ct * 16 + (ln & 15)] = s;
+  }
+  __syncthreads();
+
+  const int row0 = tile * ROWS;
+  if constexpr (EPI == EPI_QKV) {
+    const int d = a.n_heads * a.head_dim;
+    for (int idx = tid; idx < 8 * NT * 16; idx += 512) {
+      const int pr = idx & 7, c = idx >> 3;
+      if (c >= a.B) continue;
+      const int r = row0 + 2 * pr;
+      if (r >= a.M) continue;
+      float y0 = sm.fin[0][2 * pr][c] * sm.inv_rms[c];
+      float y1 = sm.fin[0][2 * pr + 1][c] * sm.inv_rms[c];
+      const int which = r / d;  // 0 q, 1 k, 2 v
+      const int rr = r - which * d;
+      const int h = rr / a.head_dim, dd = rr - h * a.head_dim;
+      const int pos = a.ti ? a.ti[c * TI_STRIDE + TI_POS] : a.pos_const;
+      if (which < 2 && a.inv_freq) {
+        const double th = (double)pos * a.inv_freq[dd >> 1];
+        const float cs = (float)cos(th), sn = (float)sin(th);
+        const float r0 = y0 * cs - y1 * sn;
+        const float r1 = y0 * sn + y1 * cs;
+        y0 = r0;
+        y1 = r1;
+      }
+      if (which == 0) {
+        a.q_out[(long)c * a.ldq + rr] = y0;
+        a.q_out[(long)c * a.ldq + rr + 1] = y1;
+      } else {
+        bf16_t* dst = a.kv + (long)c * a.kv_slot_stride + (which == 2 ? a.kv_v_off : 0) +
+                      ((long)h * a.window + (pos % a.window)) * a.head_dim + dd;
+        dst[0] = f2bf(y0);
+        dst[1] = f2bf(y1);
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
+      const int r = idx & 15, c = idx >> 4;
+      if (c >= a.B) continue;
+      const int m = row0 + r;
+      const long o = (long)c * a.ldres + m;
+      const float xn = a.x[o] + sm.fin[0][r][c];
+      a.x[o] = xn;
+      a.xa_out[o] = f2bf(xn * a.alpha_next[m]);
+      if (a.tap) a.tap[o] = xn;
+      sm.fin[0][r][c] = xn;
+    }
+    __syncthreads();
+    if (tid < a.B) {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) s += sm.fin[0][r][tid] * sm.fin[0][r][tid];
+      a.part_out[(long)tid * (a.M / ROWS) + tile] = s;
+    }
+  } else if constexpr (EPI == EPI_GATED) {
+    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
+      const int r = idx & 15, c = idx >> 4;
+      if (c >= a.B) continue;
+      const int m = row0 + r;
+      if (m >= a.M) continue;
+      const float gt = sm.fin[0][r][c] * sm.inv_rms[c];
+      const float up = sm.fin[1][r][c] * sm.inv_rms[c];
+      a.m_out[(long)c * a.ldm + m] = f2bf(gt / (1.0f + expf(-gt)) * up);
+    }
+  } else if constexpr (EPI == EPI_STORE) {
+    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
+      const int r = idx & 15, c = idx >> 4;
+      if (c >= a.B) continue;
+      const int m = row0 + r;
+      if (m >= a.M) continue;
+      a.f_out[(long)c * a.ldf + m] = sm.fin[0][r][c] * sm.inv_rms[c];
+    }
+  } else {  // EPI_LOGITS
+    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
+      const int r = idx & 15, c = idx >> 4;
+      if (c >= a.B) continue;
+      const int m = row0 + r;
+      if (m >= a.M) continue;
+      const float v = sm.fin[0][r][c] * sm.inv_rms[c];
+      a.f_out[(long)c * a.ldf + m] = v;
+      sm.fin[0][r][c] = v;
+    }
+    __syncthreads();
+    if (tid < a.B) {
+      // strict '>' in row order: the lowest index wins a tie
+      float best = sm.fin[0][0][tid];
+      int bi = row0;
+      for (int r = 1; r < ROWS && row0 + r < a.M; ++r) {
+        const float v = sm.fin[0][r][tid];
+        if (v > best) { best = v; bi = row0 + r; }
+      }
+      a.amax_v[(long)tid * a.ld_amax + tile] = best;
+      a.amax_i[(long)tid * a.ld_amax + tile] = bi;
+    }
+  }
+}
+
+template <int EPI>
+static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
+  const int tiles = (a.M + ROWS - 1) / ROWS;
+  if (a.B > 16)
+    hipLaunchKernelGGL((gemm_kernel<EPI, 2>), dim3(tiles), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<EPI, 1>), dim3(tiles), dim3(512), 0, s, a);
+}
+
+void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_QKV: launch_gemm_nt<EPI_QKV>(a, s); break;
+    case EPI_RESID: launch_gemm_nt<EPI_RESID>(a, s); break;
+    case EPI_GATED: launch_gemm_nt<EPI_GATED>(a, s); break;
+    case EPI_LOGITS: launch_gemm_nt<EPI_LOGITS>(a, s); break;
+    case EPI_STORE: launch_gemm_nt<EPI_STORE>(a, s); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K flash-decoding over the ring.
+//
+// Slot b at absolute position pos attends to the n = min(pos+1, W) most
+// recent positions p = pos-n+1 .. pos, stored at ring index p mod W (guide,
+// "架构": fixed-capacity ring KV; recipe: sliding window 3000 frames).  The
+// keys are visited in position order in fixed splits of ATT_CHUNK keys; one
+// workgroup (4 waves x 64 keys) per (head, slot, split) produces the split's
+// running max, sum of exponentials and unnormalised output; a second pass
+// combines the splits in split order.  With a single split the workgroup
+// writes the normalised output itself.  Lanes: head_dim/8 lanes share one key
+// (16 bytes each, coalesced 256-byte rows for head_dim 128).
+// ---------------------------------------------------------------------------
+
+struct AttnPos {
+  int pos, n, lo, nc;
+};
+
+__device__ __forceinline__ AttnPos attn_pos(const AttnArgs& a, int b) {
+  AttnPos p;
+  p.pos = a.ti ? a.ti[b * TI_STRIDE + TI_POS] : a.pos_const;
+  p.n = min(p.pos + 1, a.window);
+  p.lo = p.pos + 1 - p.n;
+  p.nc = (p.n + ATT_CHUNK - 1) / ATT_CHUNK;
+  return p;
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  constexpr int LPK = DH / 8;
+  constexpr int KPI = 64 / LPK;
+  constexpr int ITER = 64 / KPI;
+  const int h = blockIdx.x, b = blockIdx.y, c = blockIdx.z;
+  const AttnPos P = attn_pos(a, b);
+  if (c >= P.nc) return;
+  const int k0 = c * ATT_CHUNK;
+  const int kn = min(ATT_CHUNK, P.n - k0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPK, kg = lane / LPK;
+  const float scale = 1.0f / sqrtf((float)DH);
+
+  float qv[8];
+  {
+    const float* qp = a.q + (long)b * a.ldq + h * DH + sub * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = qp[i];
+  }
+  const bf16_t* kb = a.kv + (long)b * a.kv_slot_stride + (long)h * a.window * DH + sub * 8;
+  const bf16_t* vb = kb + a.kv_v_off;
+
+  float s[ITER];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int j = wave * 64 + it * KPI + kg;
+    float dot = 0.f;
+    if (j < kn) {
+      const int slot = (P.lo + k0 + j) % a.window;
+      float kf[8];
+      unpack8(ld16(kb + (long)slot * DH), kf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot += qv[i] * kf[i];
+    }
+#pragma unroll
+    for (int off = LPK / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+    s[it] = (j < kn) ? dot * scale : -INFINITY;
+    mloc = fmaxf(mloc, s[it]);
+  }
+  mloc = wave_max(mloc);
+
+  float lsum = 0.f;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int j = wave * 64 + it * KPI + kg;
+    if (j < kn) {
+      const float p = expf(s[it] - mloc);
+      if (sub == 0) lsum += p;
+      const int slot = (P.lo + k0 + j) % a.window;
+      float vf[8];
+      unpack8(ld16(vb + (long)slot * DH), vf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] += p * vf[i];
+    }
+  }
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] += __shfl_xor(o[i], off);
+  lsum = wave_sum(lsum);
+
+  __shared__ float sm_m[4], sm_l[4], sm_o[4][DH];
+  if (lane == 0) {
+    sm_m[wave] = mloc;
+    sm_l[wave] = lsum;
+  }
+  if (kg == 0)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sm_o[wave][sub * 8 + i] = o[i];
+  __syncthreads();
+  if (threadIdx.x < DH) {
+    const int e = threadIdx.x;
+    const float M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (sm_m[w] == -INFINITY) ? 0.f : expf(sm_m[w] - M);
+      L += sm_l[w] * f;
+      O += sm_o[w][e] * f;
+    }
+    if (P.nc == 1) {
+      a.o[(long)b * a.ldo + h * DH + e] = f2bf(O / L);
+    } else {
+      float* pp = a.part + (((long)b * a.n_heads + h) * a.max_chunks + c) * (DH + 2);
+      pp[2 + e] = O;
+      if (e == 0) {
+        pp[0] = M;
+        pp[1] = L;
+      }
+    }
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(DH) void attn_combine_kernel(AttnArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const AttnPos P = attn_pos(a, b);
+  if (P.nc == 1) return;
+  const int e = threadIdx.x;
+  const float* base = a.part + ((long)b * a.n_heads + h) * a.max_chunks * (DH + 2);
+  float M = -INFINITY;
+  for (int c = 0; c < P.nc; ++c) M = fmaxf(M, base[c * (DH + 2)]);
+  float L = 0.f, O = 0.f;
+  for (int c = 0; c < P.nc; ++c) {
+    const float* pp = base + c * (DH + 2);
+    const float f = expf(pp[0] - M);
+    L += pp[1] * f;
+    O += pp[2 + e] * f;
+  }
+  a.o[(long)b * a.ldo + h * DH + e] = f2bf(O / L);
+}
+
+template <int DH>
+static void launch_attn_dh(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((attn_kernel<DH>), dim3(a.n_heads, a.B, a.max_chunks), dim3(256), 0, s, a);
+}
+
+void launch_attention(const AttnArgs& a, hipStream_t s) {
+  switch (a.head_dim) {
+    case 32: launch_attn_dh<32>(a, s); break;
+    case 64: launch_attn_dh<64>(a, s); break;
+    default: launch_attn_dh<128>(a, s); break;
+  }
+}
+
+void launch_attention_combine(const AttnArgs& a, hipStream_t s) {
+  switch (a.head_dim) {
+    case 32: hipLaunchKernelGGL((attn_combine_kernel<32>), dim3(a.n_heads, a.B), dim3(32), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(a.n_heads, a.B), dim3(64), 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(a.n_heads, a.B), dim3(128), 0, s, a); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 17-way embedding gather-sum: x_b = sum over rows r of table_r[col_b[r]], in
+// row order in fp32 (column layout: recipe, "Architecture").  Also stores
+// bf16(x * alpha) for the first QKV projection, the per-16 sums of squares
+// and the hidden-state tap.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+  const int b = blockIdx.x;
+  const int* t = a.ti + b * TI_STRIDE + TI_COL;
+  const long off = (long)b * a.d;
+  for (int grp = threadIdx.x; grp < a.d / 16; grp += blockDim.x) {
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int r = 0; r < 17; ++r) {
+      const bf16_t* e = (r == 0) ? a.emb_text + (long)t[0] * a.d
+                                 : a.emb_audio + ((long)(r - 1) * a.audio_rows + t[r]) * a.d;
+      e += grp * 16;
+      float f[16];
+      unpack8(ld16(e), f);
+      unpack8(ld16(e + 8), f + 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += f[i];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = grp * 16 + i;
+      a.x[off + m] = acc[i];
+      a.tap[off + m] = acc[i];
+      a.xa[off + m] = f2bf(acc[i] * a.alpha[m]);
+      ss += acc[i] * acc[i];
+    }
+    a.part[(long)b * (a.d / 16) + grp] = ss;
+  }
+}
+
+void launch_embed(const EmbedArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(a.B), dim3(256), 0, s, a);
+}
+
+// ---------------------------------------------------------------------------
+// Head finisher: greedy token of one head (text or depformer codebook `step`)
+// from the per-workgroup (max, argmax) partials, forced choice applied
+// (recipe: voice forces the agent stream, persona the text stream), and the
+// next depformer step's input e = P_{k+1} z + table_{k+1}[chosen] with its
+// normalisation partials.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  // per-thread contiguous range, strict '>' so the lowest index wins ties
+  const int per = (a.n_part + 255) / 256;
+  const int t0 = tid * per, t1 = min(a.n_part, t0 + per);
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int t = t0; t < t1; ++t) {
+    const float v = a.amax_v[(long)b * a.ld_amax + t];
+    const int i = a.amax_i[(long)b * a.ld_amax + t];
+    if (v > bv || bi == 0x7fffffff) { bv = v; bi = i; }
+  }
+  sv[tid] = bv;
+  si[tid] = bi;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) {
+      const float v2 = sv[tid + w];
+      const int i2 = si[tid + w];
+      if (i2 != 0x7fffffff && (si[tid] == 0x7fffffff || v2 > sv[tid] || (v2 == sv[tid] && i2 < si[tid]))) {
+        sv[tid] = v2;
+        si[tid] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  __shared__ int chosen_s;
+  if (tid == 0) {
+    const int pred = si[0];
+    int* to = a.to + b * TO_STRIDE;
+    const int* ti = a.ti + b * TI_STRIDE;
+    int forced = -1;
+    if (a.step < 8) forced = ti[TI_FORCE + 1 + a.step];  // step -1 -> text force
+    const int chosen = forced >= 0 ? forced : pred;
+    if (a.step < 8) {
+      to[TO_PRED + 1 + a.step] = pred;
+      to[TO_CHOSEN + 1 + a.step] = chosen;
+    } else {
+      to[TO_USER + a.step - 8] = pred;
+    }
+    to[TO_TOK] = chosen;
+    chosen_s = chosen;
+  }
+  __syncthreads();
+  const int nk = a.step + 1;
+  if (nk >= a.dep_q) return;
+  const int tok = chosen_s;
+  const float* u = a.u + ((long)b * a.dep_q + nk) * a.dd;
+  const bf16_t* e = a.table + (long)tok * a.dd;
+  for (int grp = tid; grp < a.dd / 16; grp += 256) {
+    float f[16];
+    unpack8(ld16(e + grp * 16), f);
+    unpack8(ld16(e + grp * 16 + 8), f + 8);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = grp * 16 + i;
+      const float v = u[m] + f[i];
+      a.y[(long)b * a.dd + m] = v;
+      a.ya[(long)b * a.dd + m] = f2bf(v * a.alpha[m]);
+      ss += v * v;
+    }
+    a.part[(long)b * (a.dd / 16) + grp] = ss;
+  }
+}
+
+void launch_finish(const FinishArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(finish_kernel, dim3(a.B), dim3(256), 0, s, a);
+}
+
+}  // namespace pp

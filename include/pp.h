@@ -1,0 +1,192 @@
+/*
+ * pp.h -- C ABI of the lockstep tick library (libpp.so) for MI355X (gfx950).
+ *
+ * One call of pp_step runs one 80 ms lockstep tick of a Moshi/PersonaPlex
+ * RQ-Transformer for B concurrent session slots:
+ *
+ *   PersonaPlex recipe (vLLM-Omni), "Architecture (Moshi RQ-Transformer, all
+ *   native)": a per-frame token column [B, 17, 1] (row 0 inner-monologue
+ *   text, rows 1-8 agent audio, rows 9-16 user audio) goes through the
+ *   temporal transformer (4096-d / 32 layers / 32 heads) decoding one frame
+ *   against a ring KV cache with a 3000-frame sliding window and per-slot
+ *   recycle; then the depformer (1024-d / 6 layers / 16 heads) runs
+ *   autoregressively over 16 codebooks, reset each frame.  "1 user frame in
+ *   -> 1 agent frame + 1 text token" per tick ("Why it is different from
+ *   MiniCPM-o / JoyVL duplex").
+ *
+ *   vLLM-Omni PersonaPlex guide (mhpq.cn), "架构": RMSNorm with fp32 alpha,
+ *   fused in-projection attention, interleaved RoPE at absolute positions,
+ *   SiLU-gated MLP, fixed-capacity ring KV with static shapes so the whole
+ *   step can be captured in a graph; "贪心解码与 Parity 约束": greedy only,
+ *   one token per tick; "运维要点与注意事项": a recycled slot is bit-exact
+ *   with a fresh engine for the same inputs.
+ *
+ * Conventions
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *   - Device pointers are plain HIP device addresses (for instance the
+ *     data_ptr() of a torch tensor); host pointers are ordinary memory.
+ *   - The caller allocates and owns every device buffer (weights, arena) and
+ *     the stream; the library keeps raw pointers, so the buffers must stay
+ *     alive until pp_destroy.  The library allocates no device memory; it
+ *     allocates small pinned host staging buffers and one internal stream
+ *     used only to capture the tick graph.
+ *   - Host arrays passed in are copied before the call returns.
+ *   - A handle is single-threaded and bound to the stream given to pp_create.
+ *   - Return codes: PP_OK, or a negative PP_E* code.  On every error except
+ *     PP_EDEVICE no state changes (arguments are validated before anything
+ *     is committed).  PP_EDEVICE means a HIP call failed; the handle is then
+ *     poisoned and every later call returns PP_EDEVICE.  pp_last_error gives
+ *     a message.  No C++ exception crosses this interface.
+ */
+#ifndef PP_H
+#define PP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PP_OK       0
+#define PP_EINVAL  (-1)  /* null pointer, bad dims, slot out of [0,B), token out of range, n > window */
+#define PP_EBUSY   (-2)  /* prefill or fill on a slot that is already free-running (or fill after a prefill) */
+#define PP_ENOSPC  (-3)  /* arena too small, or forced-frame queue full */
+#define PP_EDEVICE (-4)  /* a HIP call failed; handle poisoned */
+
+#define PP_MAX_BATCH     32    /* slots per handle */
+#define PP_MAX_QUEUE     4096  /* forced frames queued per slot */
+#define PP_COLUMN_ROWS   17    /* token column: text, 8 agent, 8 user */
+
+/* Model shape.  Constraints (checked by pp_create / pp_arena_bytes):
+ * n_q == 8, dep_q == 16, d % n_heads == 0 with head_dim in {32,64,128},
+ * dep_d % dep_heads == 0 with head_dim in {32,64,128}, d, ffn, dep_d,
+ * dep_ffn multiples of 32, text_card >= 2, audio_card >= 2. */
+typedef struct pp_dims {
+  int32_t d, n_layers, n_heads, ffn;   /* temporal transformer */
+  int32_t text_card;                   /* text vocabulary (TEXT_INITIAL_TOKEN == text_card) */
+  int32_t audio_card;                  /* codec cardinality (AUDIO_INITIAL_TOKEN == audio_card) */
+  int32_t n_q;                         /* audio codebooks per stream in the column: 8 */
+  int32_t dep_d, dep_layers, dep_heads, dep_ffn;
+  int32_t dep_q;                       /* depformer codebooks per frame: 16 */
+  float norm_eps;                      /* RMSNorm epsilon (inside the square root) */
+  float rope_base;                     /* RoPE base; pair (2i,2i+1) turns by pos*base^(-2i/head_dim) */
+} pp_dims;
+
+/* Weights: device pointers, read-only, stacked per tensor kind.
+ * L = n_layers, Ld = dep_layers, F = ffn, Fd = dep_ffn, A = audio_card,
+ * Vt = text_card.  Matrices are [out][in] row-major: y = W x. */
+typedef struct pp_weights {
+  const uint16_t* emb_text;      /* [Vt+1][d]           table of column row 0 */
+  const uint16_t* emb_audio;     /* [16][A+1][d]        tables of column rows 1..16 */
+  const float*    attn_norm;     /* [L][d]              fp32 alpha */
+  const uint16_t* wqkv;          /* [L][3d][d]          rows [q; k; v], heads contiguous */
+  const uint16_t* wo;            /* [L][d][d] */
+  const float*    mlp_norm;      /* [L][d] */
+  const uint16_t* w_in;          /* [L][2F][d]          rows [gate; up] */
+  const uint16_t* w_out;         /* [L][d][F] */
+  const float*    out_norm;      /* [d] */
+  const uint16_t* text_head;     /* [Vt][d] */
+  const uint16_t* dep_in_proj;   /* [16][dep_d][d]      one projection per codebook step */
+  const uint16_t* dep_emb_text;  /* [Vt+1][dep_d]       input table of step 0 */
+  const uint16_t* dep_emb_audio; /* [15][A+1][dep_d]    input tables of steps 1..15 */
+  const float*    dep_attn_norm; /* [Ld][dep_d] */
+  const uint16_t* dep_wqkv;      /* [Ld][3dep_d][dep_d] */
+  const uint16_t* dep_wo;        /* [Ld][dep_d][dep_d] */
+  const float*    dep_mlp_norm;  /* [Ld][dep_d] */
+  const uint16_t* dep_w_in;      /* [Ld][2Fd][dep_d] */
+  const uint16_t* dep_w_out;     /* [Ld][dep_d][Fd] */
+  const float*    dep_out_norm;  /* [dep_d] */
+  const uint16_t* dep_heads;     /* [16][A][dep_d] */
+} pp_weights;
+
+/* Device views into the arena, valid after each pp_step (overwritten by the
+ * next one).  Strides are dense. */
+typedef struct pp_taps_t {
+  const float*   hidden;       /* [L+1][B][d]   embedding sum, then the residual stream after each layer */
+  const float*   text_logits;  /* [B][Vt] */
+  const float*   dep_logits;   /* [B][16][A] */
+  const int32_t* tokens;       /* [B][32]: [0..8] predictions (text, agent 0..7),
+                                  [9..16] user-stream predictions (depformer steps 8..15),
+                                  [17..25] chosen tokens (forced where forced, else predicted) */
+} pp_taps_t;
+
+typedef struct pp_handle pp_handle;
+
+/* Bytes of device arena a handle needs for (dims, B, window).  Pure host
+ * computation.  The arena holds the ring KV ([B][L][2][H][window][head_dim]
+ * bf16), activations, taps and work buffers.  PP_EINVAL on bad arguments. */
+int pp_arena_bytes(const pp_dims* dims, int B, int window, size_t* out_bytes);
+
+/* Create a handle for B slots (1..PP_MAX_BATCH) and a ring of `window`
+ * frames per slot.  arena: device buffer of at least pp_arena_bytes bytes,
+ * 256-byte aligned.  stream: the hipStream_t every later call runs on (NULL =
+ * the null stream).  Captures the tick graph.  All slots start reset.
+ * PP_EINVAL (bad args), PP_ENOSPC (arena too small), PP_EDEVICE. */
+int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w,
+              void* arena, size_t arena_bytes, void* stream, pp_handle** out);
+
+/* Queue n forced frames (host int32 [n][17]) for `slot`, consumed one per
+ * tick by the following pp_step calls (session open: voice codes force the
+ * agent rows, persona tokens force the text row, silence frames between;
+ * recipe "Architecture", guide "Persona Voice 注入").  Row layout: rows 0-8
+ * are the token to choose for this tick's text / agent 0..7 output, or -1
+ * for "use the greedy prediction"; rows 9-16 are this tick's user codes and
+ * replace that slot's user_codes.  Ranges: row 0 in [-1,Vt), rows 1-8 in
+ * [-1,A), rows 9-16 in [0,A).  Legal only before the slot's first
+ * free-running tick (else PP_EBUSY, as persona/voice cannot change after
+ * session open).  PP_ENOSPC if the queue would exceed PP_MAX_QUEUE. */
+int pp_prefill_forced(pp_handle* h, int slot, const int32_t* frames, int n);
+
+/* One lockstep tick for all B slots.  user_codes: host int32 [B][8] in
+ * [0,A) (ignored for slots consuming a forced frame).  tokens: host int32
+ * [B][9] receives each slot's greedy predictions [text, agent 0..7] -- the
+ * model's own predictions even on forced ticks.  Synchronous: returns after
+ * the tokens are on the host.  A slot whose forced queue is empty at this
+ * tick becomes free-running.  Every slot computes every tick. */
+int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens);
+
+/* Recycle `slot`: position 0, column back to the initial tokens
+ * [Vt, A x 8], forced queue cleared, ring logically empty.  A recycled slot
+ * then computes bit-identically to a fresh handle fed the same inputs. */
+int pp_slot_reset(pp_handle* h, int slot);
+
+/* Test / measurement hook: set the ring of `slot` to n frames of given keys
+ * and values at absolute positions 0..n-1 (host bf16 [L][n][H][head_dim]
+ * each; the stored, already rotated values); the slot's next tick runs at
+ * position n.  Legal only on a slot with no tick and no queued frame since
+ * its last reset (else PP_EBUSY).  n in [0, window] (else PP_EINVAL). */
+int pp_ring_fill(pp_handle* h, int slot, int n, const uint16_t* k, const uint16_t* v);
+
+/* Device views of the last tick's intermediate results (see pp_taps_t). */
+int pp_taps(const pp_handle* h, pp_taps_t* out);
+
+/* Measurement hook: launch one kernel of the tick graph `iters` times on the
+ * handle's stream outside the graph, with the same arguments it has inside
+ * the graph, and report its mean duration from HIP events.  which:
+ *   0 temporal fused QKV GEMM, 1 temporal attention (split-K decode),
+ *   2 temporal out-projection, 3 temporal gate/up GEMM, 4 temporal down
+ *   projection, 5 text head;  all for layer 0.
+ * Kernels 2 and 4 accumulate into the residual stream, so a tick's results
+ * are meaningless after timing them until the slots are reset.
+ * Reports the algorithmic bytes one launch moves in *bytes (weights read +
+ * activations read and written, KV read and written; see DESIGN notes in
+ * the repository). */
+int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* bytes);
+
+/* Time `iters` back-to-back tick-graph launches on the handle's stream with
+ * HIP events (no host copies); *avg_ms = mean device time per tick.  The
+ * launches recompute the tick for the current tick inputs without advancing
+ * any slot, so they leave slot state (positions, columns, queues) as is. */
+int pp_time_graph(pp_handle* h, int iters, float* avg_ms);
+
+void pp_destroy(pp_handle* h);
+
+/* Message of the last error on h (or of the last failed pp_create when h is
+ * NULL).  Valid until the next call on h. */
+const char* pp_last_error(const pp_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PP_H */

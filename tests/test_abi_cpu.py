@@ -1,0 +1,86 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+entry point include/pp.h declares, and its pure-host calls validate their
+arguments.  No compute call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from full_duplex_speech_moshi_amd import pp, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "pp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pp_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pp.LIB_PATH):
+        pytest.fail("libpp.so not built: run python -m full_duplex_speech_moshi_amd.build")
+    return pp.load_library()
+
+
+def test_exports_every_declared_entry_point(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    assert set(names) == set(pp.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_arena_bytes_matches_ring_layout(lib):
+    dims = pp.make_dims(synth.FULL)
+    n1 = pp.pp_arena_bytes(dims, 1, 3000)
+    n2 = pp.pp_arena_bytes(dims, 2, 3000)
+    ring_per_slot = 32 * 2 * 32 * 3000 * 128 * 2     # [L][2][H][W][Dh] bf16
+    assert n1 > ring_per_slot
+    assert n2 - n1 >= ring_per_slot
+    assert n2 - n1 < ring_per_slot + 64 * 2**20      # activations are small beside the ring
+
+
+@pytest.mark.parametrize("field,value", [("n_q", 4), ("dep_q", 8), ("n_heads", 3), ("d", 250), ("ffn", 700)])
+def test_bad_dims_rejected(lib, field, value):
+    import dataclasses
+    dm = dataclasses.replace(synth.TINY, **{field: value})
+    out = ctypes.c_size_t()
+    assert lib.pp_arena_bytes(ctypes.byref(pp.make_dims(dm)), 1, 32, ctypes.byref(out)) == pp.PP_EINVAL
+
+
+@pytest.mark.parametrize("B,W", [(0, 32), (33, 32), (1, 0)])
+def test_bad_batch_or_window_rejected(lib, B, W):
+    out = ctypes.c_size_t()
+    assert lib.pp_arena_bytes(ctypes.byref(pp.make_dims(synth.TINY)), B, W, ctypes.byref(out)) == pp.PP_EINVAL
+
+
+def test_create_validates_before_touching_the_device(lib):
+    dims = pp.make_dims(synth.TINY)
+    h = ctypes.c_void_p()
+    w = pp.PPWeights()            # all NULL
+    rc = lib.pp_create(ctypes.byref(dims), 1, 32, ctypes.byref(w), ctypes.c_void_p(256), 1 << 20, None, ctypes.byref(h))
+    assert rc == pp.PP_EINVAL and not h.value
+    assert b"NULL" in lib.pp_last_error(None)
+    w = pp.PPWeights(**{f: 4096 for f in pp.WEIGHT_FIELDS})
+    rc = lib.pp_create(ctypes.byref(dims), 1, 32, ctypes.byref(w), ctypes.c_void_p(256), 16, None, ctypes.byref(h))
+    assert rc == pp.PP_ENOSPC
+    rc = lib.pp_create(ctypes.byref(dims), 1, 32, ctypes.byref(w), ctypes.c_void_p(100), 1 << 30, None, ctypes.byref(h))
+    assert rc == pp.PP_EINVAL   # misaligned arena
+
+
+def test_null_handle_calls_are_rejected(lib):
+    assert lib.pp_step(None, None, None) == pp.PP_EINVAL
+    assert lib.pp_slot_reset(None, 0) == pp.PP_EINVAL
+    assert lib.pp_prefill_forced(None, 0, None, 0) == pp.PP_EINVAL
+    lib.pp_destroy(None)
+
+
+def test_engine_refuses_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(RuntimeError):
+        pp.Engine(synth.TINY, {}, 1, 32)

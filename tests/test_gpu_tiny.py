@@ -1,0 +1,239 @@
+"""GPU parity of the tick at the tiny shape (d 256, 2 layers, ring window 32
+so the ring wraps), through the C-ABI library, against the CPU oracle."""
+import numpy as np
+import pytest
+
+from full_duplex_speech_moshi_amd import synth
+from oracle.tick import Oracle
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DM = synth.TINY
+W = synth.TINY_WINDOW
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev(tiny_weights):
+    import torch
+    from full_duplex_speech_moshi_amd import pp
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return pp.upload_weights(DM, tiny_weights, torch.device("cuda:0"))
+
+
+def engine(tiny_weights, dev, B, window=W):
+    from full_duplex_speech_moshi_amd import pp
+    return pp.Engine(DM, tiny_weights, B, window, device_weights=dev)
+
+
+def test_c0_teacher_forced_parity(tiny_weights, dev):
+    """100 ticks, B = 1, W = 32 (three wraps); user codes uniform from seed 1;
+    the text/agent rows replay the oracle's own choices."""
+    _say("case: C0 teacher-forced parity, 100 ticks, B=1, W=32")
+    n = 100
+    codes = synth.user_codes(1, n)
+    recs = parity.oracle_run(Oracle(DM, tiny_weights, 1, W), codes)
+    frames = parity.teacher_frames(recs, codes)
+    e = engine(tiny_weights, dev, 1)
+    e.prefill_forced(0, frames)
+    fails, report = [], {}
+    for t in range(n):
+        tok = e.step(np.zeros((1, 8), np.int32))
+        tp = e.taps()
+        g = parity.gpu_slot(tp, 0)
+        np.testing.assert_array_equal(tok[0], g["tokens"])
+        # the embedding sum is exact: same fp32 adds in the same row order
+        np.testing.assert_array_equal(g["hidden"][0], recs[t]["hidden"][0])
+        np.testing.assert_array_equal(g["chosen"], recs[t]["chosen"])
+        fails += parity.compare_tick(g, recs[t], t, report)
+    e.close()
+    _say(f"worst hidden rel-L2 {max(report['hidden_rel_l2']):.3e}, text logit abs "
+         f"{max(report['text_logit_abs']):.3e}, dep logit abs {max(report['dep_logit_abs']):.3e}, "
+         f"tokens checked {report.get('tok_checked', 0)}")
+    assert not fails, "\n".join(fails[:20])
+
+
+def test_c0_free_running_matches_oracle_until_low_margin(tiny_weights, dev):
+    """Free-running (no forcing): the GPU's greedy tokens equal the oracle's
+    until the first tick where the oracle's top-2 margin is below 1e-2."""
+    _say("case: C0 free-running agreement, B=1")
+    n = 100
+    codes = synth.user_codes(1, n)
+    recs = parity.oracle_run(Oracle(DM, tiny_weights, 1, W), codes)
+    e = engine(tiny_weights, dev, 1)
+    agree = 0
+    for t in range(n):
+        tok = e.step(codes[t:t + 1])
+        tp = e.taps()
+        r = recs[t]
+        low = parity.margin(r["text_logits"]) <= parity.MARGIN or any(
+            parity.margin(r["dep_logits"][k]) <= parity.MARGIN for k in range(8))
+        if not np.array_equal(tok[0], r["tokens"]):
+            assert low, f"tick {t}: tokens differ at high margin: {tok[0]} vs {r['tokens']}"
+            break
+        agree += 1
+        if low:
+            break
+    e.close()
+    _say(f"free-running ticks in agreement: {agree}")
+    assert agree >= 1
+
+
+def test_slot_isolation_bit_exact_across_batch_and_column_tiles(tiny_weights, dev):
+    """B = 17 engine (slot 16 in the second 16-wide column tile) vs B = 1
+    engines: each slot's tokens and taps are bit-identical."""
+    _say("case: slot isolation B=17 vs B=1")
+    B, n = 17, 8
+    codes = [synth.user_codes(100 + b, n) for b in range(B)]
+    frames = synth.session_open(3, text_card=DM.text_card, n_voice=3, n_persona=2)
+    eb = engine(tiny_weights, dev, B)
+    eb.prefill_forced(5, frames)
+    toks, taps = [], []
+    for t in range(n):
+        toks.append(eb.step(np.stack([codes[b][t] for b in range(B)])))
+        taps.append(eb.taps())
+    eb.close()
+    for b in (0, 5, 15, 16):
+        e1 = engine(tiny_weights, dev, 1)
+        if b == 5:
+            e1.prefill_forced(0, frames)
+        for t in range(n):
+            tk = e1.step(codes[b][t:t + 1])
+            tp = e1.taps()
+            np.testing.assert_array_equal(tk[0], toks[t][b])
+            np.testing.assert_array_equal(tp["hidden"][:, 0], taps[t]["hidden"][:, b])
+            np.testing.assert_array_equal(tp["text_logits"][0], taps[t]["text_logits"][b])
+            np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
+            np.testing.assert_array_equal(tp["user_pred"][0], taps[t]["user_pred"][b])
+        e1.close()
+
+
+def test_recycled_slot_bit_exact_with_fresh_engine(tiny_weights, dev):
+    _say("case: recycle == fresh")
+    codes = synth.user_codes(7, 45)
+    e = engine(tiny_weights, dev, 2)
+    for t in range(40):     # wraps the ring
+        e.step(np.concatenate([codes[t:t + 1], codes[t:t + 1]]))
+    e.slot_reset(1)
+    f = engine(tiny_weights, dev, 1)
+    for t in range(5):
+        a = e.step(np.concatenate([codes[40 + t:41 + t], codes[t:t + 1]]))
+        ta = e.taps()
+        b = f.step(codes[t:t + 1])
+        tb = f.taps()
+        np.testing.assert_array_equal(a[1], b[0])
+        np.testing.assert_array_equal(ta["hidden"][:, 1], tb["hidden"][:, 0])
+        np.testing.assert_array_equal(ta["dep_logits"][1], tb["dep_logits"][0])
+    e.close()
+    f.close()
+
+
+def test_replay_is_deterministic(tiny_weights, dev):
+    """Two handles fed the same inputs produce the same bits; timing replays
+    of the graph in between do not disturb the slot state."""
+    _say("case: determinism across handles and replays")
+    codes = synth.user_codes(9, 6)
+    a, b = engine(tiny_weights, dev, 3), engine(tiny_weights, dev, 3)
+    for t in range(6):
+        c = np.stack([codes[t]] * 3)
+        ta = a.step(c)
+        tap_a = a.taps()
+        a.time_graph(3)          # replays with other inputs; slot state must not move
+        tb = b.step(c)
+        tap_b = b.taps()
+        np.testing.assert_array_equal(ta, tb)
+        for k in ("hidden", "text_logits", "dep_logits", "user_pred"):
+            np.testing.assert_array_equal(tap_a[k], tap_b[k])
+    a.close()
+    b.close()
+
+
+def test_ring_fill_then_teacher_forced_parity(tiny_weights, dev):
+    """Ring pre-filled with 20 frames of N(0,1) bf16 keys/values; 15 ticks
+    from position 20 slide the 32-frame window."""
+    _say("case: ring fill 20 + 15 ticks")
+    kb, vb = synth.ring_fill(DM, 3, 20)
+    codes = synth.alternating_codes(15, block=4)
+    o = Oracle(DM, tiny_weights, 1, W)
+    o.ring_fill(0, kb, vb)
+    recs = parity.oracle_run(o, codes)
+    e = engine(tiny_weights, dev, 1)
+    e.ring_fill(0, kb, vb)
+    e.prefill_forced(0, parity.teacher_frames(recs, codes))
+    fails, rep = [], {}
+    for t in range(15):
+        e.step(np.zeros((1, 8), np.int32))
+        fails += parity.compare_tick(parity.gpu_slot(e.taps(), 0), recs[t], t, rep)
+    e.close()
+    _say(f"worst hidden rel-L2 {max(rep['hidden_rel_l2']):.3e}")
+    assert not fails, "\n".join(fails[:20])
+
+
+def test_session_open_schedule_parity(tiny_weights, dev):
+    """Session-open forced schedule (voice, silence, persona, silence) then free
+    ticks, B = 2 with different schedules, teacher-forced on free rows."""
+    _say("case: session-open schedule, B=2")
+    B, n_free = 2, 6
+    sched = [synth.session_open(b, text_card=DM.text_card, n_voice=4, n_persona=5) for b in range(B)]
+    n = len(sched[0]) + n_free
+    codes = [synth.user_codes(1000 + b, n) for b in range(B)]
+    recs = []
+    for b in range(B):
+        o = Oracle(DM, tiny_weights, 1, W)
+        o.prefill_forced(0, sched[b])
+        recs.append(parity.oracle_run(o, codes[b]))
+    e = engine(tiny_weights, dev, B)
+    for b in range(B):
+        e.prefill_forced(b, parity.teacher_frames(recs[b], codes[b], sched[b]))
+    fails, rep = [], {}
+    for t in range(n):
+        e.step(np.zeros((B, 8), np.int32))
+        tp = e.taps()
+        for b in range(B):
+            np.testing.assert_array_equal(tp["chosen"][b], recs[b][t]["chosen"])
+            fails += parity.compare_tick(parity.gpu_slot(tp, b), recs[b][t], t, rep)
+    e.close()
+    assert not fails, "\n".join(fails[:20])
+
+
+def test_errors_leave_state_unchanged(tiny_weights, dev):
+    from full_duplex_speech_moshi_amd import pp
+    _say("case: error paths")
+    e = engine(tiny_weights, dev, 2)
+    ref = engine(tiny_weights, dev, 2)
+    codes = synth.user_codes(11, 4).reshape(2, 2, 8)
+    with pytest.raises(pp.PPError) as ei:
+        e.slot_reset(2)
+    assert ei.value.code == pp.PP_EINVAL
+    bad = codes[0].copy()
+    bad[1, 3] = DM.audio_card
+    with pytest.raises(pp.PPError) as ei:
+        e.step(bad)
+    assert ei.value.code == pp.PP_EINVAL
+    bad_frame = np.full((1, 17), -1, np.int32)
+    bad_frame[0, 9:] = 0
+    bad_frame[0, 0] = DM.text_card
+    with pytest.raises(pp.PPError) as ei:
+        e.prefill_forced(0, bad_frame)
+    assert ei.value.code == pp.PP_EINVAL
+    kb, vb = synth.ring_fill(DM, 3, W + 1)
+    with pytest.raises(pp.PPError) as ei:
+        e.ring_fill(0, kb, vb)
+    assert ei.value.code == pp.PP_EINVAL
+    # nothing above changed any state: same results as an untouched handle
+    np.testing.assert_array_equal(e.step(codes[0]), ref.step(codes[0]))
+    with pytest.raises(pp.PPError) as ei:           # both slots now free-running
+        e.prefill_forced(1, np.zeros((1, 17), np.int32))
+    assert ei.value.code == pp.PP_EBUSY
+    kb, vb = synth.ring_fill(DM, 3, 4)
+    with pytest.raises(pp.PPError) as ei:
+        e.ring_fill(0, kb, vb)
+    assert ei.value.code == pp.PP_EBUSY
+    np.testing.assert_array_equal(e.step(codes[1]), ref.step(codes[1]))
+    e.close()
+    ref.close()
