@@ -74,23 +74,23 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.ring = take((size_t)B * L.ring_slot_elems * 2);
   L.dkv = take((size_t)B * L.dkv_slot_elems * 2);
   L.x = take(B * d * 4);
-  L.xa = take(B * d * 2);
+  L.xa = take(2 * B * d * 2);  // activations feeding GEMMs: bf16 hi plane then lo plane
   L.part = take(B * (d / 16) * 4);
   L.q = take(B * d * 4);
   L.att_part = take((size_t)B * H * L.max_chunks * (hd + 2) * 4);
-  L.o = take(B * d * 2);
-  L.m = take(B * F * 2);
+  L.o = take(2 * B * d * 2);
+  L.m = take(2 * B * F * 2);
   L.hidden = take((size_t)(dm.n_layers + 1) * B * d * 4);
   L.text_logits = take(B * Vt * 4);
   L.amax_v = take((size_t)B * L.n_amax * 4);
   L.amax_i = take((size_t)B * L.n_amax * 4);
   L.u = take(B * Q * dd * 4);
   L.y = take(B * dd * 4);
-  L.ya = take(B * dd * 2);
+  L.ya = take(2 * B * dd * 2);
   L.dpart = take(B * (dd / 16) * 4);
   L.dq = take(B * dd * 4);
-  L.dout = take(B * dd * 2);
-  L.dm = take(B * dF * 2);
+  L.dout = take(2 * B * dd * 2);
+  L.dm = take(2 * B * dF * 2);
   L.dep_logits = take(B * Q * A * 4);
   L.ti = take(B * TI_STRIDE * 4);
   L.to = take(B * TO_STRIDE * 4);
@@ -122,7 +122,7 @@ struct pp_handle {
   int32_t* ti_host = nullptr;
   int32_t* to_host = nullptr;
   std::vector<Slot> slots;
-  std::function<void(hipStream_t)> timed[6];
+  std::vector<std::function<void(hipStream_t)>> timed[6];  // per layer
   double timed_bytes[6] = {0, 0, 0, 0, 0, 0};
   std::string err;
   bool poisoned = false;
@@ -182,6 +182,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   ea.alpha = w.attn_norm;
   ea.x = h->at<float>(L.x);
   ea.xa = h->at<bf16_t>(L.xa);
+  ea.xa_lo = (long)B * d;
   ea.part = h->at<float>(L.part);
   ea.tap = h->at<float>(L.hidden);
   launch_embed(ea, s);
@@ -192,6 +193,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     GemmArgs g{};
     g.W = w.wqkv + (long)l * 3 * d * d;
     g.X = h->at<bf16_t>(L.xa);
+    g.x_lo = (long)B * d;
     g.M = 3 * d;
     g.K = d;
     g.ldx = d;
@@ -211,9 +213,9 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     g.ti = ti;
     g.inv_freq = inv_freq;
     launch_gemm(EPI_QKV, g, s);
+    if (keep_timed) h->timed[0].push_back([g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); });
     if (keep_timed && l == 0) {
-      h->timed[0] = [g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); };
-      h->timed_bytes[0] = 2.0 * 3 * d * d + B * (2.0 * d + 4.0 * d / 16 + 4.0 * d + 4.0 * d);
+      h->timed_bytes[0] = 2.0 * 3 * d * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * d + 4.0 * d);
     }
 
     AttnArgs at{};
@@ -231,16 +233,18 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     at.max_chunks = L.max_chunks;
     at.o = h->at<bf16_t>(L.o);
     at.ldo = d;
+    at.o_lo = (long)B * d;
     launch_attention(at, s);
     launch_attention_combine(at, s);
+    if (keep_timed) h->timed[1].push_back([at](hipStream_t st) { launch_attention(at, st); });
     if (keep_timed && l == 0) {
-      h->timed[1] = [at](hipStream_t st) { launch_attention(at, st); };
       h->timed_bytes[1] = -1;  // depends on positions; computed at timing
     }
 
     GemmArgs go{};
     go.W = w.wo + (long)l * d * d;
     go.X = h->at<bf16_t>(L.o);
+    go.x_lo = (long)B * d;
     go.M = d;
     go.K = d;
     go.ldx = d;
@@ -248,17 +252,19 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     go.x = h->at<float>(L.x);
     go.ldres = d;
     go.xa_out = h->at<bf16_t>(L.xa);
+    go.xa_lo = (long)B * d;
     go.alpha_next = w.mlp_norm + (long)l * d;
     go.part_out = h->at<float>(L.part);
     launch_gemm(EPI_RESID, go, s);
+    if (keep_timed) h->timed[2].push_back([go](hipStream_t st) { launch_gemm(EPI_RESID, go, st); });
     if (keep_timed && l == 0) {
-      h->timed[2] = [go](hipStream_t st) { launch_gemm(EPI_RESID, go, st); };
-      h->timed_bytes[2] = 2.0 * d * d + B * (2.0 * d + 4.0 * d + 4.0 * d + 2.0 * d + 4.0 * d / 16);
+      h->timed_bytes[2] = 2.0 * d * d + B * (4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d / 16);
     }
 
     GemmArgs gu{};
     gu.W = w.w_in + (long)l * 2 * F * d;
     gu.X = h->at<bf16_t>(L.xa);
+    gu.x_lo = (long)B * d;
     gu.M = F;
     gu.K = d;
     gu.ldx = d;
@@ -270,15 +276,17 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gu.eps = dm.norm_eps;
     gu.m_out = h->at<bf16_t>(L.m);
     gu.ldm = F;
+    gu.m_lo = (long)B * F;
     launch_gemm(EPI_GATED, gu, s);
+    if (keep_timed) h->timed[3].push_back([gu](hipStream_t st) { launch_gemm(EPI_GATED, gu, st); });
     if (keep_timed && l == 0) {
-      h->timed[3] = [gu](hipStream_t st) { launch_gemm(EPI_GATED, gu, st); };
-      h->timed_bytes[3] = 2.0 * 2 * F * d + B * (2.0 * d + 4.0 * d / 16 + 2.0 * F);
+      h->timed_bytes[3] = 2.0 * 2 * F * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * F);
     }
 
     GemmArgs gd{};
     gd.W = w.w_out + (long)l * d * F;
     gd.X = h->at<bf16_t>(L.m);
+    gd.x_lo = (long)B * F;
     gd.M = d;
     gd.K = F;
     gd.ldx = F;
@@ -286,13 +294,14 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gd.x = h->at<float>(L.x);
     gd.ldres = d;
     gd.xa_out = h->at<bf16_t>(L.xa);
+    gd.xa_lo = (long)B * d;
     gd.alpha_next = (l + 1 < dm.n_layers) ? w.attn_norm + (long)(l + 1) * d : w.out_norm;
     gd.part_out = h->at<float>(L.part);
     gd.tap = h->at<float>(L.hidden) + (long)(l + 1) * B * d;
     launch_gemm(EPI_RESID, gd, s);
+    if (keep_timed) h->timed[4].push_back([gd](hipStream_t st) { launch_gemm(EPI_RESID, gd, st); });
     if (keep_timed && l == 0) {
-      h->timed[4] = [gd](hipStream_t st) { launch_gemm(EPI_RESID, gd, st); };
-      h->timed_bytes[4] = 2.0 * d * F + B * (2.0 * F + 4.0 * d + 4.0 * d + 2.0 * d + 4.0 * d + 4.0 * d / 16);
+      h->timed_bytes[4] = 2.0 * d * F + B * (4.0 * F + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d / 16);
     }
   }
 
@@ -300,6 +309,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   GemmArgs gt{};
   gt.W = w.text_head;
   gt.X = h->at<bf16_t>(L.xa);
+  gt.x_lo = (long)B * d;
   gt.M = Vt;
   gt.K = d;
   gt.ldx = d;
@@ -315,14 +325,15 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gt.ld_amax = L.n_amax;
   launch_gemm(EPI_LOGITS, gt, s);
   if (keep_timed) {
-    h->timed[5] = [gt](hipStream_t st) { launch_gemm(EPI_LOGITS, gt, st); };
-    h->timed_bytes[5] = 2.0 * Vt * d + B * (2.0 * d + 4.0 * d / 16 + 4.0 * Vt);
+    h->timed[5].push_back([gt](hipStream_t st) { launch_gemm(EPI_LOGITS, gt, st); });
+    h->timed_bytes[5] = 2.0 * Vt * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * Vt);
   }
 
   // all 16 depformer input projections of z at once
   GemmArgs gp{};
   gp.W = w.dep_in_proj;
   gp.X = h->at<bf16_t>(L.xa);
+  gp.x_lo = (long)B * d;
   gp.M = Q * dd;
   gp.K = d;
   gp.ldx = d;
@@ -351,6 +362,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   fa.alpha = w.dep_attn_norm;
   fa.y = h->at<float>(L.y);
   fa.ya = h->at<bf16_t>(L.ya);
+  fa.ya_lo = (long)B * dd;
   fa.part = h->at<float>(L.dpart);
   launch_finish(fa, s);
 
@@ -360,6 +372,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       GemmArgs g{};
       g.W = w.dep_wqkv + (long)l * 3 * dd * dd;
       g.X = h->at<bf16_t>(L.ya);
+      g.x_lo = (long)B * dd;
       g.M = 3 * dd;
       g.K = dd;
       g.ldx = dd;
@@ -397,11 +410,13 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       at.max_chunks = 1;
       at.o = h->at<bf16_t>(L.dout);
       at.ldo = dd;
+      at.o_lo = (long)B * dd;
       launch_attention(at, s);
 
       GemmArgs go{};
       go.W = w.dep_wo + (long)l * dd * dd;
       go.X = h->at<bf16_t>(L.dout);
+      go.x_lo = (long)B * dd;
       go.M = dd;
       go.K = dd;
       go.ldx = dd;
@@ -409,6 +424,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       go.x = h->at<float>(L.y);
       go.ldres = dd;
       go.xa_out = h->at<bf16_t>(L.ya);
+      go.xa_lo = (long)B * dd;
       go.alpha_next = w.dep_mlp_norm + (long)l * dd;
       go.part_out = h->at<float>(L.dpart);
       launch_gemm(EPI_RESID, go, s);
@@ -416,6 +432,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       GemmArgs gu{};
       gu.W = w.dep_w_in + (long)l * 2 * dF * dd;
       gu.X = h->at<bf16_t>(L.ya);
+      gu.x_lo = (long)B * dd;
       gu.M = dF;
       gu.K = dd;
       gu.ldx = dd;
@@ -427,11 +444,13 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       gu.eps = dm.norm_eps;
       gu.m_out = h->at<bf16_t>(L.dm);
       gu.ldm = dF;
+      gu.m_lo = (long)B * dF;
       launch_gemm(EPI_GATED, gu, s);
 
       GemmArgs gd{};
       gd.W = w.dep_w_out + (long)l * dd * dF;
       gd.X = h->at<bf16_t>(L.dm);
+      gd.x_lo = (long)B * dF;
       gd.M = dd;
       gd.K = dF;
       gd.ldx = dF;
@@ -439,6 +458,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       gd.x = h->at<float>(L.y);
       gd.ldres = dd;
       gd.xa_out = h->at<bf16_t>(L.ya);
+      gd.xa_lo = (long)B * dd;
       gd.alpha_next = (l + 1 < dm.dep_layers) ? w.dep_attn_norm + (long)(l + 1) * dd : w.dep_out_norm;
       gd.part_out = h->at<float>(L.dpart);
       launch_gemm(EPI_RESID, gd, s);
@@ -446,6 +466,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     GemmArgs gh{};
     gh.W = w.dep_heads + (long)k * A * dd;
     gh.X = h->at<bf16_t>(L.ya);
+    gh.x_lo = (long)B * dd;
     gh.M = A;
     gh.K = dd;
     gh.ldx = dd;
@@ -678,7 +699,7 @@ int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* by
     by = 0;
     for (int b = 0; b < h->B; ++b) {
       const long n = std::min<long>(h->slots[b].pos + 1, h->W);
-      by += 2.0 * n * H * hd * 2 + 4.0 * h->dm.d + 2.0 * h->dm.d;
+      by += 2.0 * n * H * hd * 2 + 4.0 * h->dm.d + 4.0 * h->dm.d;
     }
   }
   if (bytes) *bytes = by;
@@ -688,9 +709,13 @@ int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* by
   hipEvent_t e0, e1;
   HIP_OR_FAIL(h, hipEventCreate(&e0));
   HIP_OR_FAIL(h, hipEventCreate(&e1));
-  h->timed[which](h->stream);  // warm
+  // One round = the kernel for every layer in order, each with that layer's
+  // weights, as in the tick (weights are not cache-resident between uses).
+  const auto& fns = h->timed[which];
+  for (const auto& f : fns) f(h->stream);  // warm
   HIP_OR_FAIL(h, hipEventRecord(e0, h->stream));
-  for (int i = 0; i < iters; ++i) h->timed[which](h->stream);
+  for (int i = 0; i < iters; ++i)
+    for (const auto& f : fns) f(h->stream);
   HIP_OR_FAIL(h, hipEventRecord(e1, h->stream));
   HIP_OR_FAIL(h, hipEventSynchronize(e1));
   float ms = 0;
@@ -698,7 +723,7 @@ int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* by
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   HIP_OR_FAIL(h, hipGetLastError());
-  *avg_ms = ms / iters;
+  *avg_ms = ms / (iters * (float)fns.size());
   return PP_OK;
 }
 

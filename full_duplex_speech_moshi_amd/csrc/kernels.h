@@ -33,7 +33,8 @@ enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GATED = 2, EPI_LOGITS = 3, EPI_STORE 
 
 struct GemmArgs {
   const bf16_t* W;      // [M][K] (gated: gate rows, up rows start at W + gate_off*K)
-  const bf16_t* X;      // [B][ldx] bf16 activations
+  const bf16_t* X;      // activations as a bf16 pair: hi plane [B][ldx], lo plane at X + x_lo
+  long x_lo;
   int M, K, ldx, B;
   long gate_off;        // gated: row offset of the up half
   // inverse-RMS source: sum-of-squares partials [B][n_part] (one per 16 features)
@@ -50,12 +51,14 @@ struct GemmArgs {
   // EPI_RESID
   float* x;             // [B][ldres] residual stream (read-modify-write)
   int ldres;
-  bf16_t* xa_out;       // [B][ldres] bf16(x * alpha_next)
+  bf16_t* xa_out;       // [B][ldres] x * alpha_next as a bf16 hi/lo pair (lo plane at + xa_lo)
+  long xa_lo;
   const float* alpha_next;
   float* part_out;      // [B][M/16] sum of squares per 16 rows
   float* tap;           // [B][ldres] copy of x (nullable)
   // EPI_GATED / EPI_STORE / EPI_LOGITS
-  bf16_t* m_out; int ldm;        // gated: [B][ldm] bf16 silu(g)*u
+  bf16_t* m_out; int ldm;        // gated: [B][ldm] silu(g)*u as a bf16 hi/lo pair
+  long m_lo;
   float* f_out; long ldf;        // store / logits: [B][ldf] fp32
   float* amax_v; int* amax_i; int ld_amax;  // logits: per-workgroup (max, argmax) [B][ld_amax]
 };
@@ -71,8 +74,9 @@ struct AttnArgs {
   const int* ti; int pos_const;
   float* part;          // [B][n_heads][max_chunks][head_dim + 2] (m, l, o...)
   int max_chunks;
-  bf16_t* o;            // [B][ldo] bf16 output
+  bf16_t* o;            // [B][ldo] output as a bf16 hi/lo pair (lo plane at o + o_lo)
   int ldo;
+  long o_lo;
 };
 
 void launch_attention(const AttnArgs& a, hipStream_t s);
@@ -82,7 +86,7 @@ struct EmbedArgs {
   const int* ti; int B, d;
   const bf16_t* emb_text; const bf16_t* emb_audio; int text_rows, audio_rows;
   const float* alpha;   // first attention-norm alpha
-  float* x; bf16_t* xa; float* part; float* tap;
+  float* x; bf16_t* xa; long xa_lo; float* part; float* tap;
 };
 void launch_embed(const EmbedArgs& a, hipStream_t s);
 
@@ -96,7 +100,7 @@ struct FinishArgs {
   const float* u;        // [B][dep_q][dd] input projections of z
   const bf16_t* table;   // input table of step+1 ([rows][dd])
   const float* alpha;    // first depformer attention-norm alpha
-  float* y; bf16_t* ya; float* part;
+  float* y; bf16_t* ya; long ya_lo; float* part;
 };
 void launch_finish(const FinishArgs& a, hipStream_t s);
 

@@ -27,6 +27,15 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// Store v as a bf16 pair (hi, lo) with hi = bf16(v), lo = bf16(v - hi):
+// hi + lo carries 16 significant bits, so a GEMM fed both planes sees its
+// input to within 2^-17 relative while the weights stay plain bf16.
+__device__ __forceinline__ void store_split(bf16_t* p, long lo, float v) {
+  const bf16_t h = f2bf(v);
+  p[0] = h;
+  p[lo] = f2bf(v - bf2f(h));
+}
+
 __device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
@@ -57,7 +66,9 @@ __device__ __forceinline__ float wave_max(float v) {
 // their partial tiles are summed in LDS in wave order.  Each wave streams its
 // weight rows with 16-byte loads (4 lanes cover 64 contiguous bytes of a row)
 // straight into v_mfma_f32_16x16x32_bf16 as the A operand; the slots are the
-// 16 columns of the B operand, zero beyond B.  The MFMA computes every output
+// 16 columns of the B operand, zero beyond B.  Activations arrive as a bf16
+// hi/lo pair and each k-step issues one MFMA per plane into the same fp32
+// accumulator, so the products are exact and the input carries 16 bits.  The MFMA computes every output
 // column from that column alone, so a slot's result does not depend on what
 // occupies the other columns.  Weight streaming is the bound (HBM); the
 // matrix cores are idle most of the time even at B = 32.
@@ -92,7 +103,7 @@ __device__ __forceinline__ void compute_inv_rms(const GemmArgs& a, float* inv_rm
 template <int EPI, int NT>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
   constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
-  constexpr int U = 8;
+  constexpr int U = (RT * NT > 1) ? 4 : 8;
   __shared__ GemmSmem<RT, NT> sm;
 
   const int tid = threadIdx.x;
@@ -125,7 +136,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
 
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
   for (int s = s0; s < s1; s += U) {
-    u32x4 av[RT][U], bv[NT][U];
+    u32x4 av[RT][U], bh[NT][U], bl[NT][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = (s + u) < s1;
@@ -133,16 +144,23 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) av[rt][u] = (ok && a_ok) ? ld16(arow[rt] + k) : zero;
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) bv[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + k) : zero;
+      for (int ct = 0; ct < NT; ++ct) {
+        bh[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + k) : zero;
+        bl[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + a.x_lo + k) : zero;
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, av[rt][u]), __builtin_bit_cast(bf16x8, bv[ct][u]), acc[rt][ct], 0, 0, 0);
+        for (int ct = 0; ct < NT; ++ct) {
+          const bf16x8 w8 = __builtin_bit_cast(bf16x8, av[rt][u]);
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh[ct][u]),
+                                                                acc[rt][ct], 0, 0, 0);
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl[ct][u]),
+                                                                acc[rt][ct], 0, 0, 0);
+        }
   }
 
   // Partial tiles to LDS, then a fixed-order sum over the 8 waves.
@@ -204,7 +222,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
       const long o = (long)c * a.ldres + m;
       const float xn = a.x[o] + sm.fin[0][r][c];
       a.x[o] = xn;
-      a.xa_out[o] = f2bf(xn * a.alpha_next[m]);
+      store_split(a.xa_out + o, a.xa_lo, xn * a.alpha_next[m]);
       if (a.tap) a.tap[o] = xn;
       sm.fin[0][r][c] = xn;
     }
@@ -223,7 +241,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
       if (m >= a.M) continue;
       const float gt = sm.fin[0][r][c] * sm.inv_rms[c];
       const float up = sm.fin[1][r][c] * sm.inv_rms[c];
-      a.m_out[(long)c * a.ldm + m] = f2bf(gt / (1.0f + expf(-gt)) * up);
+      store_split(a.m_out + (long)c * a.ldm + m, a.m_lo, gt / (1.0f + expf(-gt)) * up);
     }
   } else if constexpr (EPI == EPI_STORE) {
     for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
@@ -390,7 +408,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       O += sm_o[w][e] * f;
     }
     if (P.nc == 1) {
-      a.o[(long)b * a.ldo + h * DH + e] = f2bf(O / L);
+      store_split(a.o + (long)b * a.ldo + h * DH + e, a.o_lo, O / L);
     } else {
       float* pp = a.part + (((long)b * a.n_heads + h) * a.max_chunks + c) * (DH + 2);
       pp[2 + e] = O;
@@ -418,7 +436,7 @@ __global__ __launch_bounds__(DH) void attn_combine_kernel(AttnArgs a) {
     L += pp[1] * f;
     O += pp[2 + e] * f;
   }
-  a.o[(long)b * a.ldo + h * DH + e] = f2bf(O / L);
+  store_split(a.o + (long)b * a.ldo + h * DH + e, a.o_lo, O / L);
 }
 
 template <int DH>
@@ -473,7 +491,7 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
       const int m = grp * 16 + i;
       a.x[off + m] = acc[i];
       a.tap[off + m] = acc[i];
-      a.xa[off + m] = f2bf(acc[i] * a.alpha[m]);
+      store_split(a.xa + off + m, a.xa_lo, acc[i] * a.alpha[m]);
       ss += acc[i] * acc[i];
     }
     a.part[(long)b * (a.d / 16) + grp] = ss;
@@ -553,7 +571,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
       const int m = grp * 16 + i;
       const float v = u[m] + f[i];
       a.y[(long)b * a.dd + m] = v;
-      a.ya[(long)b * a.dd + m] = f2bf(v * a.alpha[m]);
+      store_split(a.ya + (long)b * a.dd + m, a.ya_lo, v * a.alpha[m]);
       ss += v * v;
     }
     a.part[(long)b * (a.dd / 16) + grp] = ss;

@@ -161,17 +161,16 @@ int pp_ring_fill(pp_handle* h, int slot, int n, const uint16_t* k, const uint16_
 /* Device views of the last tick's intermediate results (see pp_taps_t). */
 int pp_taps(const pp_handle* h, pp_taps_t* out);
 
-/* Measurement hook: launch one kernel of the tick graph `iters` times on the
- * handle's stream outside the graph, with the same arguments it has inside
- * the graph, and report its mean duration from HIP events.  which:
- *   0 temporal fused QKV GEMM, 1 temporal attention (split-K decode),
- *   2 temporal out-projection, 3 temporal gate/up GEMM, 4 temporal down
- *   projection, 5 text head;  all for layer 0.
- * Kernels 2 and 4 accumulate into the residual stream, so a tick's results
- * are meaningless after timing them until the slots are reset.
- * Reports the algorithmic bytes one launch moves in *bytes (weights read +
- * activations read and written, KV read and written; see DESIGN notes in
- * the repository). */
+/* Measurement hook: launch one kernel of the tick graph outside the graph,
+ * on the handle's stream, with the arguments it has inside the graph, once
+ * per layer in layer order (each launch streams that layer's own weights, as
+ * in a tick), `iters` rounds; *avg_ms = mean duration of one launch from HIP
+ * events.  which: 0 temporal fused QKV GEMM, 1 temporal attention (split-K
+ * decode pass), 2 temporal out-projection, 3 temporal gate/up GEMM,
+ * 4 temporal down projection, 5 text head (one launch per round).
+ * *bytes = the algorithmic bytes of one launch (weights read, activations read
+ * and written, keys/values read and written).  The launches recompute values
+ * that the next tick recomputes before use, so slot state is not disturbed. */
 int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* bytes);
 
 /* Time `iters` back-to-back tick-graph launches on the handle's stream with

@@ -37,6 +37,12 @@ Arithmetic: weights are the exact bf16 values upcast to `dtype` (fp32 by
 default, fp64 for the shadow run); everything else is `dtype`, except the RoPE
 angle, which is fp64 with cos/sin cast to `dtype`.  Slots are processed one
 at a time.
+
+Cache storage: the ring and the depformer's per-frame keys/values hold bf16
+values (each stored key/value rounded to the nearest bf16, ties to even), as
+the served model keeps its caches in the model's bf16 dtype (the guide singles
+out only the RMSNorm alpha as fp32).  kv_store="exact" keeps them in `dtype`
+instead (used by the fp64 shadow and closed-form checks).
 """
 from __future__ import annotations
 
@@ -49,8 +55,10 @@ USER_ROWS = slice(9, 17)
 
 def upcast_bf16(bits: np.ndarray, dtype=np.float32) -> np.ndarray:
     """bf16 bit patterns -> values (exact in fp32 and fp64)."""
-    f = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
-    return f.astype(dtype, copy=False)
+    b = np.asarray(bits, dtype=np.uint16)
+    u = np.empty(b.shape, dtype=np.uint32)
+    np.left_shift(b, 16, out=u, dtype=np.uint32)
+    return u.view(np.float32).astype(dtype, copy=False)
 
 
 def rmsnorm(x: np.ndarray, alpha: np.ndarray, eps: float) -> np.ndarray:
@@ -97,6 +105,15 @@ def softmax_attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndar
     return np.einsum("hn,nhd->hd", p, vals)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value of each element (ties to even), returned as float32.
+    fp64 input is first rounded to fp32."""
+    u = np.array(x, dtype=np.float32).view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32)
+
+
 def greedy(logits: np.ndarray) -> int:
     """Greedy decoding ("贪心解码与 Parity 约束": temperature 0, top_k 1);
     the first maximum wins a tie.  NaN logits are an error."""
@@ -128,7 +145,10 @@ class Oracle:
     tables, fp32 for RMSNorm alphas, named as in the weight manifest of the
     input generator.  window: ring capacity W (frames)."""
 
-    def __init__(self, dims, weights, B, window, dtype=np.float32, cache_weights=None):
+    def __init__(self, dims, weights, B, window, dtype=np.float32, cache_weights=None, kv_store="bf16"):
+        if kv_store not in ("bf16", "exact"):
+            raise ValueError("kv_store must be 'bf16' or 'exact'")
+        self.kv_store = kv_store
         self.dm = dims
         self.B = int(B)
         self.W = int(window)
@@ -138,6 +158,10 @@ class Oracle:
         self._cache = {} if (cache_weights if cache_weights is not None else total < 50_000_000) else None
         self.slots = [_Slot(dims, self.W, self.dt) for _ in range(self.B)]
         self.taps = {}
+
+    def _store(self, v):
+        """Value as kept in a key/value cache."""
+        return round_bf16(v).astype(self.dt) if self.kv_store == "bf16" else v
 
     # ------------------------------------------------------------ weights
     def w(self, name):
@@ -154,7 +178,8 @@ class Oracle:
         """Row i of table `name` as `dtype` values (an embedding lookup)."""
         if self._cache is not None and name in self._cache:
             return self._cache[name][i]
-        return upcast_bf16(self._raw[name][i], self.dt)
+        a = self._raw[name]
+        return upcast_bf16(a[i], self.dt) if a.dtype == np.uint16 else a[i].astype(self.dt)
 
     # ------------------------------------------------------------ session control
     def slot_reset(self, s):
@@ -244,8 +269,8 @@ class Oracle:
             v = qkv[2 * d:3 * d].reshape(H, Dh)
             q = rope_interleaved(q, pos, dm.rope_base)
             k = rope_interleaved(k, pos, dm.rope_base)
-            st.K[l, pos % W] = k
-            st.V[l, pos % W] = v
+            st.K[l, pos % W] = self._store(k)
+            st.V[l, pos % W] = self._store(v)
             o = softmax_attend(q, st.K[l, ring_idx], st.V[l, ring_idx])
             x = x + self.w(f"layers.{l}.wo") @ o.reshape(d)
             h = rmsnorm(x, self.w(f"layers.{l}.mlp_norm"), eps)
@@ -279,8 +304,8 @@ class Oracle:
                 h = rmsnorm(y, lw["attn_norm"], eps)
                 qkv = lw["wqkv"] @ h
                 q = qkv[0:dd].reshape(dH, dDh)
-                dK[l, kq] = qkv[dd:2 * dd].reshape(dH, dDh)
-                dV[l, kq] = qkv[2 * dd:3 * dd].reshape(dH, dDh)
+                dK[l, kq] = self._store(qkv[dd:2 * dd].reshape(dH, dDh))
+                dV[l, kq] = self._store(qkv[2 * dd:3 * dd].reshape(dH, dDh))
                 o = softmax_attend(q, dK[l, :kq + 1], dV[l, :kq + 1])
                 y = y + lw["wo"] @ o.reshape(dd)
                 h = rmsnorm(y, lw["mlp_norm"], eps)

@@ -1,0 +1,136 @@
+"""GPU parity at the full 7B shape (4096-d, 32 layers, window 3000), in the
+launch configuration the benchmark times, on sampled ticks the CPU oracle can
+afford: the first ticks from an empty ring, ticks against a ring pre-filled
+to 3000 frames, and bit-exact slot isolation with mixed occupancy."""
+import numpy as np
+import pytest
+
+from full_duplex_speech_moshi_amd import synth
+from oracle.tick import Oracle
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DM = synth.FULL
+W = synth.FULL_WINDOW
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def full():
+    import torch
+    from full_duplex_speech_moshi_amd import pp
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    _say("generating 7B weights")
+    w = synth.make_weights(DM, seed=0)
+    dev = pp.upload_weights(DM, w, torch.device("cuda:0"))
+    torch.cuda.synchronize()
+    return w, dev
+
+
+@pytest.fixture(scope="module")
+def w32(full):
+    """The same weights as fp32 values, shared by the oracles of this module
+    (upcast once instead of on every tick)."""
+    from oracle.tick import upcast_bf16
+    w, _ = full
+    if not _cache_ok():
+        return w
+    return {k: upcast_bf16(v) if v.dtype == np.uint16 else v for k, v in w.items()}
+
+
+def _cache_ok():
+    try:
+        import psutil
+        return psutil.virtual_memory().available > 100 * 2**30
+    except Exception:
+        return False
+
+
+def _engine(full, B):
+    from full_duplex_speech_moshi_amd import pp
+    w, dev = full
+    return pp.Engine(DM, w, B, W, device_weights=dev)
+
+
+def _parity_run(full, w32, n_ticks, fill_seed=None, codes=None):
+    codes = synth.user_codes(1, n_ticks) if codes is None else codes
+    kb = vb = None
+    if fill_seed is not None:
+        kb, vb = synth.ring_fill(DM, fill_seed, W)
+    recs, recs_exact = [], []
+    for store, out in (("bf16", recs), ("exact", recs_exact)):
+        o = Oracle(DM, w32, 1, W, cache_weights=False, kv_store=store)
+        if kb is not None:
+            o.ring_fill(0, kb, vb)
+        for t in range(n_ticks):
+            out += parity.oracle_run(o, codes[t:t + 1])
+        _say(f"oracle ({store} caches) {n_ticks} ticks done")
+    e = _engine(full, 1)
+    if kb is not None:
+        e.ring_fill(0, kb, vb)
+    e.prefill_forced(0, parity.teacher_frames(recs, codes))
+    fails, rep = [], {}
+    for t in range(n_ticks):
+        e.step(np.zeros((1, 8), np.int32))
+        g = parity.gpu_slot(e.taps(), 0)
+        np.testing.assert_array_equal(g["hidden"][0], recs[t]["hidden"][0])
+        fails += parity.compare_tick(g, recs[t], t, rep)
+        # information only: distance to an oracle that keeps its caches unrounded
+        rep.setdefault("exact_cache_hidden", []).append(
+            max(parity.rel_l2(g["hidden"][j], recs_exact[t]["hidden"][j]) for j in range(DM.n_layers + 1)))
+    e.close()
+    _say(f"worst hidden rel-L2 {max(rep['hidden_rel_l2']):.3e}, text logit abs {max(rep['text_logit_abs']):.3e}, "
+         f"dep logit abs {max(rep['dep_logit_abs']):.3e}, tokens checked {rep.get('tok_checked', 0)}; "
+         f"vs unrounded-cache oracle: hidden rel-L2 {max(rep['exact_cache_hidden']):.3e}")
+    return fails
+
+
+@pytest.mark.timeout(900)
+def test_full_empty_ring_teacher_forced(full, w32):
+    _say("case: 7B, B=1, empty ring, 3 teacher-forced ticks")
+    fails = _parity_run(full, w32, 3)
+    assert not fails, "\n".join(fails[:20])
+
+
+@pytest.mark.timeout(900)
+def test_full_window_teacher_forced(full, w32):
+    """Ring pre-filled with 3000 frames of N(0,1) keys/values (seed 3): every
+    tick attends over exactly 3000 keys in 12 splits, and the ring slides."""
+    _say("case: 7B, B=1, ring full at 3000, 2 teacher-forced ticks")
+    fails = _parity_run(full, w32, 2, fill_seed=3, codes=synth.alternating_codes(2))
+    assert not fails, "\n".join(fails[:20])
+
+
+@pytest.mark.timeout(900)
+def test_full_isolation_mixed_occupancy_bit_exact(full):
+    """B = 3 slots with occupancies 0, 1500 and 3000 vs one B = 1 handle per
+    slot: identical bits."""
+    _say("case: 7B isolation, B=3 vs B=1, occupancy 0/1500/3000")
+    occ = [0, 1500, 3000]
+    fills = [synth.ring_fill(DM, 100 + b, n) if n else None for b, n in enumerate(occ)]
+    codes = [synth.user_codes(1000 + b, 3) for b in range(3)]
+    eb = _engine(full, 3)
+    for b, f in enumerate(fills):
+        if f is not None:
+            eb.ring_fill(b, *f)
+    toks, taps = [], []
+    for t in range(3):
+        toks.append(eb.step(np.stack([codes[b][t] for b in range(3)])))
+        taps.append(eb.taps())
+    eb.close()
+    for b in range(3):
+        e1 = _engine(full, 1)
+        if fills[b] is not None:
+            e1.ring_fill(0, *fills[b])
+        for t in range(3):
+            tk = e1.step(codes[b][t:t + 1])
+            tp = e1.taps()
+            np.testing.assert_array_equal(tk[0], toks[t][b])
+            np.testing.assert_array_equal(tp["hidden"][:, 0], taps[t]["hidden"][:, b])
+            np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
+        e1.close()

@@ -204,7 +204,7 @@ def test_attention_block_closed_form(tiny_weights):
     w["layers.0.w_in"] = zeros_bf((2 * dm.ffn, d))
     w["layers.0.w_out"] = zeros_bf((d, dm.ffn))
     Wn = 8
-    o = Oracle(dm, w, 1, Wn, dtype=np.float64)
+    o = Oracle(dm, w, 1, Wn, dtype=np.float64, kv_store="exact")
     f = teacher_frames(20, seed=6)
     o.prefill_forced(0, f)
     alpha = w["layers.0.attn_norm"].astype(np.float64)
@@ -246,9 +246,11 @@ def base_pows(Dh, base):
 
 # ------------------------------------------------------------------ ring = brute force
 
-def _brute_force_hidden(dm, w, frames, window, dtype):
+def _brute_force_hidden(dm, w, frames, window, dtype, kv_bf16=False):
     """Temporal stack over an unbounded history list, attending to the last
-    `window` frames by slicing (no ring, no modulo)."""
+    `window` frames by slicing (no ring, no modulo).  kv_bf16: keep the stored
+    keys/values as bf16 values (the input generator's RNE rounding)."""
+    keep = (lambda a: synth.bf16_bits_to_f32(synth.to_bf16_bits(a)).astype(dtype)) if kv_bf16 else (lambda a: a)
     up = lambda n: ot.upcast_bf16(w[n], dtype) if w[n].dtype == np.uint16 else w[n].astype(dtype)
     d, H, Dh, F = dm.d, dm.n_heads, dm.head_dim, dm.ffn
     Ks = [[] for _ in range(dm.n_layers)]
@@ -266,8 +268,8 @@ def _brute_force_hidden(dm, w, frames, window, dtype):
             h = ot.rmsnorm(x, up(f"layers.{l}.attn_norm"), dm.norm_eps)
             qkv = up(f"layers.{l}.wqkv") @ h
             q = ot.rope_interleaved(qkv[:d].reshape(H, Dh), t, dm.rope_base)
-            Ks[l].append(ot.rope_interleaved(qkv[d:2 * d].reshape(H, Dh), t, dm.rope_base))
-            Vs[l].append(qkv[2 * d:].reshape(H, Dh))
+            Ks[l].append(keep(ot.rope_interleaved(qkv[d:2 * d].reshape(H, Dh), t, dm.rope_base)))
+            Vs[l].append(keep(qkv[2 * d:].reshape(H, Dh)))
             o = ot.softmax_attend(q, np.stack(Ks[l][-window:]), np.stack(Vs[l][-window:]))
             x = x + up(f"layers.{l}.wo") @ o.reshape(d)
             h = ot.rmsnorm(x, up(f"layers.{l}.mlp_norm"), dm.norm_eps)
@@ -286,19 +288,25 @@ def test_ring_equals_brute_force_over_last_W_positions(tiny_weights):
     an fp64 brute force."""
     n = 100
     f = teacher_frames(n, seed=8)
-    o = Oracle(DM, tiny_weights, 1, W)
-    o.prefill_forced(0, f)
-    got = []
-    for t in range(n):
-        o.step(np.zeros((1, 8)))
-        got.append(o.taps["hidden"][:, 0].copy())
-    got = np.stack(got)
-    ref32 = _brute_force_hidden(DM, tiny_weights, f, W, np.float32)
+
+    def run(kv_store):
+        o = Oracle(DM, tiny_weights, 1, W, kv_store=kv_store)
+        o.prefill_forced(0, f)
+        out = []
+        for t in range(n):
+            o.step(np.zeros((1, 8)))
+            out.append(o.taps["hidden"][:, 0].copy())
+        return np.stack(out)
+
+    got = run("bf16")
+    ref32 = _brute_force_hidden(DM, tiny_weights, f, W, np.float32, kv_bf16=True)
     np.testing.assert_array_equal(got, ref32)
+    exact = run("exact")
+    np.testing.assert_array_equal(exact, _brute_force_hidden(DM, tiny_weights, f, W, np.float32))
     ref64 = _brute_force_hidden(DM, tiny_weights, f, W, np.float64)
-    assert rel_l2(got, ref64) < 1e-5
+    assert rel_l2(exact, ref64) < 1e-5
     # and the window matters: an unbounded window gives different states once it wraps
-    ref_inf = _brute_force_hidden(DM, tiny_weights, f[:40], 10 ** 9, np.float32)
+    ref_inf = _brute_force_hidden(DM, tiny_weights, f[:40], 10 ** 9, np.float32, kv_bf16=True)
     assert rel_l2(got[W:40], ref_inf[W:40]) > 1e-4
     np.testing.assert_array_equal(got[:W], ref_inf[:W])
 
@@ -408,7 +416,7 @@ def test_depformer_attention_closed_form(tiny_weights):
     w["dep.layers.0.wo"] = bf(np.eye(dd))
     w["dep.layers.0.w_out"] = zeros_bf((dd, dF))
     f = teacher_frames(1, seed=17)
-    o = Oracle(dm, w, 1, W, dtype=np.float64)
+    o = Oracle(dm, w, 1, W, dtype=np.float64, kv_store="exact")
     o.prefill_forced(0, f)
     o.step(np.zeros((1, 8)))
     up = lambda n: ot.upcast_bf16(w[n], np.float64)
@@ -486,7 +494,7 @@ def test_ring_fill_then_ticks_equal_independent_brute_force(tiny_weights):
     unbounded history (complex-number rotation of q and k at the absolute
     position, scipy softmax, logistic-form SiLU)."""
     k, v = synth.ring_fill(DM, 3, 20)
-    o = Oracle(DM, tiny_weights, 1, W, dtype=np.float64)
+    o = Oracle(DM, tiny_weights, 1, W, dtype=np.float64, kv_store="exact")
     o.ring_fill(0, k, v)
     assert o.slots[0].pos == 20
     f = teacher_frames(15, seed=14)
@@ -525,12 +533,30 @@ def test_ring_fill_then_ticks_equal_independent_brute_force(tiny_weights):
         prev = list(f[t, :9])
 
 
+def test_caches_hold_bf16_rounded_values(tiny_weights):
+    """Default storage: each stored key/value is the nearest bf16 value (ties
+    to even) of the exact one, in the ring and in the depformer's cache."""
+    a = Oracle(DM, tiny_weights, 1, W)
+    b = Oracle(DM, tiny_weights, 1, W, kv_store="exact")
+    c = synth.user_codes(1, 1)
+    a.step(c)
+    b.step(c)
+    # layer 0 sees identical inputs in both runs (deeper layers do not)
+    for arr_a, arr_b in ((a.slots[0].K, b.slots[0].K), (a.slots[0].V, b.slots[0].V)):
+        want = synth.bf16_bits_to_f32(synth.to_bf16_bits(arr_b[0, 0]))
+        np.testing.assert_array_equal(arr_a[0, 0], want)
+    assert not np.array_equal(a.slots[0].K[0, 0], b.slots[0].K[0, 0])
+    # the first depformer step attends to its own (rounded) value only
+    np.testing.assert_array_equal(ot.round_bf16(np.array([1.00390625, -1.01171875, 3.0e-3], np.float32)),
+                                  synth.bf16_bits_to_f32(synth.to_bf16_bits(np.array([1.00390625, -1.01171875, 3.0e-3], np.float32))))
+
+
 def test_fp64_shadow_bounds_fp32_oracle_error(tiny_weights):
     """fp32 oracle vs the same oracle in fp64, 100 teacher-forced C0 ticks:
     hidden states agree far below the 1e-2 rel-L2 GPU gate."""
     f = teacher_frames(100, seed=15)
-    a = Oracle(DM, tiny_weights, 1, W, np.float32)
-    b = Oracle(DM, tiny_weights, 1, W, np.float64)
+    a = Oracle(DM, tiny_weights, 1, W, np.float32, kv_store="exact")
+    b = Oracle(DM, tiny_weights, 1, W, np.float64, kv_store="exact")
     a.prefill_forced(0, f)
     b.prefill_forced(0, f)
     worst_h, worst_l = 0.0, 0.0
