@@ -47,14 +47,65 @@ def slot_bytes(dm, n_keys: int) -> int:
     return emb + kv
 
 
+class Workload:
+    """Slots, ring occupancy, forced schedules and per-tick user codes of one
+    benchmark configuration.  Ring fills share one seeded N(0,1) bf16 fill
+    (seed 3): cost depends only on occupancy, not on the values."""
+
+    def __init__(self, name, dm, W, B, K, WU, synth):
+        self.name, self.dm, self.W, self.B = name, dm, W, B
+        self.fill_n = [0] * B
+        self.sched = [None] * B
+        self.events = None
+        n = WU + K
+        if name in ("C0", "C1"):
+            self.codes = [synth.user_codes(1 + 1000 * b, n) for b in range(B)]
+        elif name == "C2":
+            self.fill_n = [W] * B
+            self.codes = [synth.alternating_codes(n) for _ in range(B)]
+        elif name == "C3":
+            self.fill_n = [int(x) for x in synth.batch_occupancy(B, W)]
+            self.sched = [synth.session_open(b, text_card=dm.text_card) for b in range(B)]
+            self.codes = [synth.user_codes(1000 + b, n) for b in range(B)]
+        elif name == "C4":
+            sessions, events = synth.elastic_schedule(B, n, W)
+            self.sessions, self.events = sessions, events
+            for sess in sessions:
+                if sess["start_tick"] == 0:
+                    self.fill_n[sess["slot"]] = sess["fill_n"]
+            self.codes = [np.zeros((n, 8), np.int32) for _ in range(B)]
+            for si, sess in enumerate(sessions):
+                end = next((t for t in range(sess["start_tick"] + 1, n) if sess["slot"] in events[t]), n)
+                c = synth.user_codes(sess["code_seed"], n)
+                self.codes[sess["slot"]][sess["start_tick"]:end] = c[:end - sess["start_tick"]]
+        elif name in ("sweep", "sweep_empty"):
+            self.fill_n = [W if name == "sweep" else 0] * B
+            self.codes = [synth.user_codes(1 + 1000 * b, n) for b in range(B)]
+        self.fill = None
+        need = max(self.fill_n + [s["fill_n"] for s in getattr(self, "sessions", [])] + [0])
+        if need:
+            self.fill = synth.ring_fill(dm, 3, need)
+
+    def open_slot(self, eng, b, n_fill, sched):
+        eng.slot_reset(b)
+        if n_fill:
+            eng.ring_fill(b, self.fill[0][:, :n_fill], self.fill[1][:, :n_fill])
+        if sched is not None:
+            eng.prefill_forced(b, sched)
+
+    def setup(self, eng):
+        for b in range(self.B):
+            self.open_slot(eng, b, self.fill_n[b], self.sched[b])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=250)
+    ap.add_argument("--steps", type=int, default=None, help="timed ticks (default: the config's own count)")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="C1", choices=["C0", "C1", "C2", "sweep"])
-    ap.add_argument("--batch", type=int, default=1, help="slots (sweep / C2 only)")
-    ap.add_argument("--cpu-ticks", type=int, default=2, help="oracle ticks timed on the host (0: skip)")
+    ap.add_argument("--config", default="C1", choices=["C0", "C1", "C2", "C3", "C4", "sweep", "sweep_empty"])
+    ap.add_argument("--batch", type=int, default=None, help="slots (default: the config's own B)")
+    ap.add_argument("--cpu-ticks", type=int, default=1, help="oracle ticks timed on the host (0: skip)")
     ap.add_argument("--kernel-iters", type=int, default=30)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -73,8 +124,10 @@ def main():
     tiny = args.config == "C0"
     dm = synth.TINY if tiny else synth.FULL
     W = synth.TINY_WINDOW if tiny else synth.FULL_WINDOW
-    B = 1 if args.config in ("C0", "C1") else args.batch
-    K, WU = args.steps, args.warmup
+    B = args.batch or {"C0": 1, "C1": 1, "C2": 1, "C3": 8, "C4": 32, "sweep": 32, "sweep_empty": 32}[args.config]
+    K = args.steps or {"C0": 100, "C1": 250, "C2": 500, "C3": 292, "C4": 300, "sweep": 100,
+                       "sweep_empty": 100}[args.config]
+    WU = args.warmup
 
     t0 = time.time()
     weights = synth.make_weights(dm, seed=0)
@@ -82,28 +135,18 @@ def main():
     t0 = time.time()
     dw = pp.upload_weights(dm, weights, dev)
     torch.cuda.synchronize()
-    log(f"weights uploaded in {time.time() - t0:.1f} s")
+    log(f"weights uploaded and packed in {time.time() - t0:.1f} s")
     eng = pp.Engine(dm, weights, B, W, device=dev, device_weights=dw)
     log(f"engine created: B={B} W={W} arena {eng.arena.numel() / 2**30:.2f} GiB")
+    wl = Workload(args.config, dm, W, B, K, WU, synth)
 
-    fill_n = [0] * B
-    if args.config in ("C2", "sweep") and not tiny:
-        fill_n = [W] * B
-
-    def setup():
-        for b in range(B):
-            eng.slot_reset(b)
-            if fill_n[b]:
-                kb, vb = synth.ring_fill(dm, 3 + 1000 * b, fill_n[b])
-                eng.ring_fill(b, kb, vb)
-
-    codes = [synth.user_codes(1 if b == 0 else 1000 + b, WU + K) if args.config != "C2"
-             else synth.alternating_codes(WU + K) for b in range(B)]
-
-    setup()
+    t0 = time.time()
+    wl.setup(eng)
+    log(f"slots opened in {time.time() - t0:.1f} s")
+    pos = list(wl.fill_n)
     for t in range(WU):
-        eng.step(np.stack([codes[b][t] for b in range(B)]))
-    setup()
+        eng.step(np.stack([wl.codes[b][t] for b in range(B)]))
+    wl.setup(eng)
     log(f"warmup {WU} ticks done; timing {K} ticks")
 
     tick_ms = np.empty(K)
@@ -111,12 +154,18 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for t in range(K):
-        c = np.stack([codes[b][WU + t] for b in range(B)])
+        if wl.events is not None:
+            for b in wl.events[WU + t] if WU + t > 0 else []:
+                sess = next(x for x in wl.sessions if x["slot"] == b and x["start_tick"] == WU + t)
+                wl.open_slot(eng, b, sess["fill_n"], None)
+                pos[b] = sess["fill_n"]
+        c = np.stack([wl.codes[b][WU + t] for b in range(B)])
         a = time.perf_counter()
         eng.step(c)
         tick_ms[t] = (time.perf_counter() - a) * 1e3
         for b in range(B):
-            n_keys[t, b] = min(fill_n[b] + t + 1, W)
+            n_keys[t, b] = min(pos[b] + 1, W)
+            pos[b] += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"timed {K} ticks in {wall:.3f} s")
@@ -152,7 +201,10 @@ def main():
         "config": {"workload": {"C0": "tiny RQ-Transformer tick, B=1, ring window 32",
                                 "C1": "7B RQ-Transformer tick, B=1, empty ring, 250 ticks",
                                 "C2": "7B RQ-Transformer tick, ring pre-filled to 3000 frames",
-                                "sweep": "7B RQ-Transformer tick, all rings full"}[args.config],
+                                "C3": "7B RQ-Transformer tick, B=8, occupancy U[0,3000], 92-frame session open",
+                                "C4": "7B RQ-Transformer tick, B=32 elastic, mixed occupancy, p=0.01 turnover",
+                                "sweep": "7B RQ-Transformer tick, all rings full",
+                                "sweep_empty": "7B RQ-Transformer tick, all rings empty"}[args.config],
                    "B": B, "window": W, "config": args.config},
         "p50_tick_ms": float(np.median(tick_ms)),
         "p90_tick_ms": float(np.percentile(tick_ms, 90)),
@@ -171,7 +223,7 @@ def main():
         from oracle.tick import Oracle
         cores = len(os.sched_getaffinity(0))
         o = Oracle(dm, weights, 1, W)
-        c0 = codes[0]
+        c0 = wl.codes[0]
         ts = []
         for t in range(args.cpu_ticks):
             a = time.perf_counter()

@@ -464,7 +464,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       launch_gemm(EPI_RESID, gd, s);
     }
     GemmArgs gh{};
-    gh.W = w.dep_heads + (long)k * A * dd;
+    gh.W = w.dep_heads + (long)k * packed_elems(A, dd);
     gh.X = h->at<bf16_t>(L.ya);
     gh.x_lo = (long)B * dd;
     gh.M = A;
@@ -748,6 +748,17 @@ int pp_time_graph(pp_handle* h, int iters, float* avg_ms) {
   (void)hipEventDestroy(e1);
   *avg_ms = ms / iters;
   return PP_OK;
+}
+
+size_t pp_packed_elems(int M, int K) {
+  if (M < 1 || K < 32 || K % 32) return 0;
+  return (size_t)packed_elems(M, K);
+}
+
+int pp_pack_matrix(const uint16_t* src, int M, int K, uint16_t* dst, void* stream) {
+  if (!src || !dst || M < 1 || K < 32 || K % 32) return PP_EINVAL;
+  launch_pack(src, M, K, dst, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? PP_OK : PP_EDEVICE;
 }
 
 void pp_destroy(pp_handle* h) {

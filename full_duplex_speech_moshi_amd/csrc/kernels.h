@@ -32,7 +32,7 @@ constexpr int MAX_COLS = 32;       // slots per launch (two 16-wide column tiles
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GATED = 2, EPI_LOGITS = 3, EPI_STORE = 4 };
 
 struct GemmArgs {
-  const bf16_t* W;      // [M][K] (gated: gate rows, up rows start at W + gate_off*K)
+  const bf16_t* W;      // [M][K] in the tile layout (gated: gate rows, up rows from row gate_off)
   const bf16_t* X;      // activations as a bf16 pair: hi plane [B][ldx], lo plane at X + x_lo
   long x_lo;
   int M, K, ldx, B;
@@ -64,6 +64,8 @@ struct GemmArgs {
 };
 
 void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s);
+void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s);
+inline long packed_elems(int M, int K) { return (long)((M + ROWS - 1) / ROWS) * ROWS * K; }
 
 struct AttnArgs {
   const float* q;       // [B][ldq], head h at q + h*head_dim

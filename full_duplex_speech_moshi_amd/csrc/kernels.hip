@@ -61,6 +61,12 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---------------------------------------------------------------------------
 // Skinny GEMM family  Y[b][m] = sum_k W[m][k] * X[b][k],  b < B <= 32.
 //
+// Arithmetic contract (the same for every B, so a slot's bits never depend on
+// the batch): the K/32 k-steps are cut into 8 ranges R_w = [floor(ks*w/8),
+// floor(ks*(w+1)/8)); partial p_w accumulates, in increasing k-step order,
+// one MFMA on the hi plane then one on the lo plane of the input; the result
+// is ((p_0 + p_1) + ...) + p_7 in fp32.
+//
 // One workgroup = 8 waves owns a 16-row tile (two tiles, gate and up, for the
 // gated MLP) over the whole K; the waves split K into 8 contiguous ranges and
 // their partial tiles are summed in LDS in wave order.  Each wave streams its
@@ -100,25 +106,27 @@ __device__ __forceinline__ void compute_inv_rms(const GemmArgs& a, float* inv_rm
   }
 }
 
+// One 16-row tile (gate+up pair for EPI_GATED) of the GEMM, computed by a
+// 512-thread workgroup; `smem` holds a GemmSmem<RT, NT>.
 template <int EPI, int NT>
-__global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
+__device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
   constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
   constexpr int U = (RT * NT > 1) ? 4 : 8;
-  __shared__ GemmSmem<RT, NT> sm;
+  GemmSmem<RT, NT>& sm = *reinterpret_cast<GemmSmem<RT, NT>*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.x;
   const int ksteps = a.K >> 5;
   const int s0 = (ksteps * wave) / GEMM_WAVES;
   const int s1 = (ksteps * (wave + 1)) / GEMM_WAVES;
 
-  const int row = tile * ROWS + r16;
-  const bool a_ok = row < a.M;
+  // Weights in the tile layout: block (row tile T, k-step s) is 1 KB at
+  // (T * ksteps + s) * 512 elements, lane l's 8 elements at l * 8.  Rows past
+  // M are zero in that layout, so the loads need no row mask.
   const bf16_t* arow[RT];
-  arow[0] = a.W + (long)(a_ok ? row : 0) * a.K + g * 8;
-  if (RT == 2) arow[RT - 1] = a.W + (long)((a_ok ? row : 0) + a.gate_off) * a.K + g * 8;
+  arow[0] = a.W + (long)tile * ksteps * 512 + lane * 8;
+  if (RT == 2) arow[RT - 1] = a.W + ((long)tile + a.gate_off / ROWS) * ksteps * 512 + lane * 8;
   const bf16_t* xrow[NT];
   bool b_ok[NT];
 #pragma unroll
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
       const bool ok = (s + u) < s1;
       const int k = (s + u) * 32;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) av[rt][u] = (ok && a_ok) ? ld16(arow[rt] + k) : zero;
+      for (int rt = 0; rt < RT; ++rt) av[rt][u] = ok ? ld16(arow[rt] + (long)(s + u) * 512) : zero;
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
         bh[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + k) : zero;
@@ -274,6 +282,37 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
       a.amax_i[(long)tid * a.ld_amax + tile] = bi;
     }
   }
+  __syncthreads();  // LDS is reused by the next unit
+}
+
+constexpr size_t GEMM_SMEM_BYTES = sizeof(GemmSmem<2, 2>);
+
+template <int EPI, int NT>
+__global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
+  gemm_unit<EPI, NT>(a, blockIdx.x, smem);
+}
+
+// Row-major [M][K] bf16 -> tile layout (see gemm_unit); one thread moves the
+// 16 bytes of one lane of one (tile, k-step) block; rows past M become zero.
+__global__ __launch_bounds__(256) void pack_kernel(const bf16_t* src, int M, int K, bf16_t* dst) {
+  const int ks = K >> 5;
+  const long nblk = (long)((M + ROWS - 1) / ROWS) * ks;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // (block, lane)
+  if (i >= nblk * 64) return;
+  const long blk = i >> 6;
+  const int lane = (int)(i & 63);
+  const long T = blk / ks;
+  const int s = (int)(blk - T * ks);
+  const long row = T * ROWS + (lane & 15);
+  u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+  if (row < M) v = ld16(src + row * K + s * 32 + (lane >> 4) * 8);
+  *reinterpret_cast<u32x4*>(dst + i * 8) = v;
+}
+
+void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s) {
+  const long n = (long)((M + ROWS - 1) / ROWS) * (K >> 5) * 64;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, M, K, dst);
 }
 
 template <int EPI>
@@ -322,14 +361,16 @@ __device__ __forceinline__ AttnPos attn_pos(const AttnArgs& a, int b) {
   return p;
 }
 
+// One (head, slot, split) of the decode pass, computed by waves 0..3 of the
+// workgroup (waves beyond 3 of a larger workgroup only join the barriers).
 template <int DH>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int c) {
   constexpr int LPK = DH / 8;
   constexpr int KPI = 64 / LPK;
   constexpr int ITER = 64 / KPI;
-  const int h = blockIdx.x, b = blockIdx.y, c = blockIdx.z;
   const AttnPos P = attn_pos(a, b);
   if (c >= P.nc) return;
+  const bool active = threadIdx.x < 256;
   const int k0 = c * ATT_CHUNK;
   const int kn = min(ATT_CHUNK, P.n - k0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -349,7 +390,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   float mloc = -INFINITY;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int j = wave * 64 + it * KPI + kg;
+    const int j = active ? wave * 64 + it * KPI + kg : ATT_CHUNK;
     float dot = 0.f;
     if (j < kn) {
       const int slot = (P.lo + k0 + j) % a.window;
@@ -371,7 +412,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int j = wave * 64 + it * KPI + kg;
+    const int j = active ? wave * 64 + it * KPI + kg : ATT_CHUNK;
     if (j < kn) {
       const float p = expf(s[it] - mloc);
       if (sub == 0) lsum += p;
@@ -389,11 +430,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   lsum = wave_sum(lsum);
 
   __shared__ float sm_m[4], sm_l[4], sm_o[4][DH];
-  if (lane == 0) {
+  if (active && lane == 0) {
     sm_m[wave] = mloc;
     sm_l[wave] = lsum;
   }
-  if (kg == 0)
+  if (active && kg == 0)
 #pragma unroll
     for (int i = 0; i < 8; ++i) sm_o[wave][sub * 8 + i] = o[i];
   __syncthreads();
@@ -418,6 +459,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
     }
   }
+  __syncthreads();  // LDS is reused by the next unit
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  attn_unit<DH>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 template <int DH>
@@ -510,12 +557,15 @@ void launch_embed(const EmbedArgs& a, hipStream_t s) {
 // normalisation partials.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
-  const int b = blockIdx.x, tid = threadIdx.x;
-  __shared__ float sv[256];
-  __shared__ int si[256];
+// Slot b of the finisher, computed by the whole workgroup (up to 512
+// threads).  The argmax selection (largest value, then lowest index) does not
+// depend on the reduction tree, so the block size does not change results.
+__device__ void finish_unit(const FinishArgs& a, const int b) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  __shared__ float sv[512];
+  __shared__ int si[512];
   // per-thread contiguous range, strict '>' so the lowest index wins ties
-  const int per = (a.n_part + 255) / 256;
+  const int per = (a.n_part + nt - 1) / nt;
   const int t0 = tid * per, t1 = min(a.n_part, t0 + per);
   float bv = -INFINITY;
   int bi = 0x7fffffff;
@@ -527,7 +577,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   sv[tid] = bv;
   si[tid] = bi;
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
+  for (int w = nt / 2; w >= 1; w >>= 1) {
     if (tid < w) {
       const float v2 = sv[tid + w];
       const int i2 = si[tid + w];
@@ -557,11 +607,10 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   }
   __syncthreads();
   const int nk = a.step + 1;
-  if (nk >= a.dep_q) return;
   const int tok = chosen_s;
   const float* u = a.u + ((long)b * a.dep_q + nk) * a.dd;
   const bf16_t* e = a.table + (long)tok * a.dd;
-  for (int grp = tid; grp < a.dd / 16; grp += 256) {
+  for (int grp = tid; nk < a.dep_q && grp < a.dd / 16; grp += nt) {
     float f[16];
     unpack8(ld16(e + grp * 16), f);
     unpack8(ld16(e + grp * 16 + 8), f + 8);
@@ -576,7 +625,10 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
     }
     a.part[(long)b * (a.dd / 16) + grp] = ss;
   }
+  __syncthreads();  // LDS is reused by the next unit
 }
+
+__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) { finish_unit(a, blockIdx.x); }
 
 void launch_finish(const FinishArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(finish_kernel, dim3(a.B), dim3(256), 0, s, a);

@@ -19,7 +19,7 @@ TO_STRIDE = 32
 
 EXPORTS = ("pp_arena_bytes", "pp_create", "pp_prefill_forced", "pp_step", "pp_slot_reset",
            "pp_ring_fill", "pp_taps", "pp_time_kernel", "pp_time_graph", "pp_destroy",
-           "pp_last_error")
+           "pp_last_error", "pp_packed_elems", "pp_pack_matrix")
 
 KERNELS = {"qkv": 0, "attention": 1, "out_proj": 2, "gate_up": 3, "down": 4, "text_head": 5}
 
@@ -78,8 +78,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pp_destroy.restype = None
     lib.pp_last_error.argtypes = [P]
     lib.pp_last_error.restype = ctypes.c_char_p
+    lib.pp_packed_elems.argtypes = [I, I]
+    lib.pp_packed_elems.restype = SZ
+    lib.pp_pack_matrix.argtypes = [P, I, I, P, P]
     for n in EXPORTS:
-        if n not in ("pp_destroy", "pp_last_error"):
+        if n not in ("pp_destroy", "pp_last_error", "pp_packed_elems"):
             getattr(lib, n).restype = I
     _lib = lib
     return lib
@@ -164,6 +167,15 @@ def pp_time_graph(h: int, iters: int) -> float:
     return ms.value
 
 
+def pp_packed_elems(M: int, K: int) -> int:
+    return load_library().pp_packed_elems(M, K)
+
+
+def pp_pack_matrix(src_ptr: int, M: int, K: int, dst_ptr: int, stream_ptr: int) -> None:
+    _check(load_library().pp_pack_matrix(ctypes.c_void_p(src_ptr), M, K, ctypes.c_void_p(dst_ptr),
+                                         ctypes.c_void_p(stream_ptr)))
+
+
 def pp_destroy(h: int) -> None:
     if h:
         load_library().pp_destroy(h)
@@ -187,24 +199,44 @@ def _per_layer_groups(dm):
             ("dep_out_norm", "dep.out_norm", None), ("dep_heads", "dep.head.{}", (0, Q))]
 
 
+def _matrix_shape(dm, field):
+    """(rows, cols) of each matrix of a stacked matrix field, or None for
+    tables and alphas (which stay row-major)."""
+    d, F, dd, dF = dm.d, dm.ffn, dm.dep_d, dm.dep_ffn
+    return {"wqkv": (3 * d, d), "wo": (d, d), "w_in": (2 * F, d), "w_out": (d, F),
+            "text_head": (dm.text_card, d), "dep_in_proj": (dd, d), "dep_wqkv": (3 * dd, dd),
+            "dep_wo": (dd, dd), "dep_w_in": (2 * dF, dd), "dep_w_out": (dd, dF),
+            "dep_heads": (dm.audio_card, dd)}.get(field)
+
+
 def upload_weights(dm, w: dict, device):
-    """Copy manifest-named host weights to device tensors in the stacked
-    layout, one manifest entry at a time (no stacked host copy)."""
+    """Copy manifest-named host weights to device tensors in the library's
+    stacked layout, one manifest entry at a time; matrices are packed into the
+    tile layout on the device by pp_pack_matrix."""
     import torch
+    stream = torch.cuda.current_stream(device)
     tensors = {}
     for field, pat, rng in _per_layer_groups(dm):
         names = [pat] if rng is None else [pat.format(i) for i in range(*rng)]
         first = w[names[0]]
-        tdt = torch.int16 if first.dtype == np.uint16 else torch.float32
-        shape = first.shape if rng is None else (len(names),) + first.shape
-        t = torch.empty(shape, dtype=tdt, device=device)
-        for i, n in enumerate(names):
-            a = w[n]
-            src = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
-            if rng is None:
-                t.copy_(src)
-            else:
-                t[i].copy_(src)
+        shape = _matrix_shape(dm, field)
+        if shape is None:
+            tdt = torch.int16 if first.dtype == np.uint16 else torch.float32
+            tshape = first.shape if rng is None else (len(names),) + first.shape
+            t = torch.empty(tshape, dtype=tdt, device=device)
+            for i, n in enumerate(names):
+                a = w[n]
+                src = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+                (t if rng is None else t[i]).copy_(src)
+        else:
+            M, K = shape
+            pe = pp_packed_elems(M, K)
+            t = torch.empty(len(names) * pe, dtype=torch.int16, device=device)
+            for i, n in enumerate(names):
+                src = torch.from_numpy(w[n].view(np.int16)).to(device)
+                pp_pack_matrix(src.data_ptr(), M, K, t.data_ptr() + 2 * i * pe, stream.cuda_stream)
+                stream.synchronize()
+                del src
         tensors[field] = t
     ptrs = PPWeights(**{f: tensors[f].data_ptr() for f in WEIGHT_FIELDS})
     return tensors, ptrs

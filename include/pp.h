@@ -75,29 +75,35 @@ typedef struct pp_dims {
 
 /* Weights: device pointers, read-only, stacked per tensor kind.
  * L = n_layers, Ld = dep_layers, F = ffn, Fd = dep_ffn, A = audio_card,
- * Vt = text_card.  Matrices are [out][in] row-major: y = W x. */
+ * Vt = text_card.  Tables and alphas are row-major.  Every matrix (y = W x,
+ * W of M rows and K columns) is in the TILE LAYOUT produced by
+ * pp_pack_matrix and occupies pp_packed_elems(M, K) elements; a stack of
+ * matrices is those blocks back to back.  Tile layout: 16-row tiles, each
+ * cut into K/32 steps of 32 columns; block (tile t, step s) is 512 elements
+ * at offset (t*(K/32) + s)*512, in which element e of lane l (l < 64, e < 8)
+ * is W[16t + l%16][32s + 8(l/16) + e]; rows past M are zero. */
 typedef struct pp_weights {
   const uint16_t* emb_text;      /* [Vt+1][d]           table of column row 0 */
   const uint16_t* emb_audio;     /* [16][A+1][d]        tables of column rows 1..16 */
   const float*    attn_norm;     /* [L][d]              fp32 alpha */
-  const uint16_t* wqkv;          /* [L][3d][d]          rows [q; k; v], heads contiguous */
-  const uint16_t* wo;            /* [L][d][d] */
+  const uint16_t* wqkv;          /* L x [3d][d]         rows [q; k; v], heads contiguous */
+  const uint16_t* wo;            /* L x [d][d] */
   const float*    mlp_norm;      /* [L][d] */
-  const uint16_t* w_in;          /* [L][2F][d]          rows [gate; up] */
-  const uint16_t* w_out;         /* [L][d][F] */
+  const uint16_t* w_in;          /* L x [2F][d]         rows [gate; up] */
+  const uint16_t* w_out;         /* L x [d][F] */
   const float*    out_norm;      /* [d] */
   const uint16_t* text_head;     /* [Vt][d] */
-  const uint16_t* dep_in_proj;   /* [16][dep_d][d]      one projection per codebook step */
+  const uint16_t* dep_in_proj;   /* [16*dep_d][d]       one projection per codebook step, stacked */
   const uint16_t* dep_emb_text;  /* [Vt+1][dep_d]       input table of step 0 */
   const uint16_t* dep_emb_audio; /* [15][A+1][dep_d]    input tables of steps 1..15 */
   const float*    dep_attn_norm; /* [Ld][dep_d] */
-  const uint16_t* dep_wqkv;      /* [Ld][3dep_d][dep_d] */
-  const uint16_t* dep_wo;        /* [Ld][dep_d][dep_d] */
+  const uint16_t* dep_wqkv;      /* Ld x [3dep_d][dep_d] */
+  const uint16_t* dep_wo;        /* Ld x [dep_d][dep_d] */
   const float*    dep_mlp_norm;  /* [Ld][dep_d] */
-  const uint16_t* dep_w_in;      /* [Ld][2Fd][dep_d] */
-  const uint16_t* dep_w_out;     /* [Ld][dep_d][Fd] */
+  const uint16_t* dep_w_in;      /* Ld x [2Fd][dep_d] */
+  const uint16_t* dep_w_out;     /* Ld x [dep_d][Fd] */
   const float*    dep_out_norm;  /* [dep_d] */
-  const uint16_t* dep_heads;     /* [16][A][dep_d] */
+  const uint16_t* dep_heads;     /* 16 x [A][dep_d] */
 } pp_weights;
 
 /* Device views into the arena, valid after each pp_step (overwritten by the
@@ -112,6 +118,16 @@ typedef struct pp_taps_t {
 } pp_taps_t;
 
 typedef struct pp_handle pp_handle;
+
+/* Elements of one [M][K] matrix in the tile layout: ceil(M/16)*16*K.
+ * 0 if M < 1 or K is not a positive multiple of 32.  Pure host. */
+size_t pp_packed_elems(int M, int K);
+
+/* Repack a row-major bf16 matrix src [M][K] (device) into the tile layout at
+ * dst (device, pp_packed_elems(M, K) elements, caller-allocated, must not
+ * overlap src), asynchronously on `stream` (NULL = null stream).
+ * PP_EINVAL on NULL pointers, M < 1, or K not a positive multiple of 32. */
+int pp_pack_matrix(const uint16_t* src, int M, int K, uint16_t* dst, void* stream);
 
 /* Bytes of device arena a handle needs for (dims, B, window).  Pure host
  * computation.  The arena holds the ring KV ([B][L][2][H][window][head_dim]

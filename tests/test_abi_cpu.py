@@ -84,3 +84,11 @@ def test_engine_refuses_without_gpu():
         pytest.skip("a GPU is visible")
     with pytest.raises(RuntimeError):
         pp.Engine(synth.TINY, {}, 1, 32)
+
+
+def test_packed_elems(lib):
+    assert pp.pp_packed_elems(1000, 256) == 1008 * 256     # ragged rows pad to a 16-row tile
+    assert pp.pp_packed_elems(12288, 4096) == 12288 * 4096
+    assert pp.pp_packed_elems(16, 100) == 0                 # K must be a multiple of 32
+    assert pp.pp_packed_elems(0, 32) == 0
+    assert lib.pp_pack_matrix(None, 16, 32, None, None) == pp.PP_EINVAL
