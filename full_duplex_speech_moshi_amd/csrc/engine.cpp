@@ -28,7 +28,8 @@ constexpr int DEP_WINDOW = 16;  // depformer per-frame keys (one per codebook st
 struct Layout {
   // byte offsets into the arena
   size_t ring, dkv, x, xa, part, q, att_part, o, m, hidden, text_logits, amax_v, amax_i, u, y, ya, dpart, dq, dout,
-      dm, dep_logits, ti, to, inv_freq, total;
+      dm, dep_logits, ti, to, inv_freq, split_part, split_cnt, att_cnt, total;
+  long split_groups_max;
   int max_chunks, n_amax;
   long ring_slot_elems, ring_layer_elems, ring_v_off;
   long dkv_slot_elems, dkv_layer_elems, dkv_v_off;
@@ -95,6 +96,15 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.ti = take(B * TI_STRIDE * 4);
   L.to = take(B * TO_STRIDE * 4);
   L.inv_freq = take((hd / 2) * 8);
+  // scratch of the large-batch GEMM path: the largest group count of any GEMM of the tick
+  const long sg[] = {split_groups(EPI_QKV, 3 * d), split_groups(EPI_RESID, d), split_groups(EPI_GATED, F),
+                     split_groups(EPI_LOGITS, Vt), split_groups(EPI_STORE, Q * dd), split_groups(EPI_QKV, 3 * dd),
+                     split_groups(EPI_RESID, dd), split_groups(EPI_GATED, dF), split_groups(EPI_LOGITS, A)};
+  L.split_groups_max = 0;
+  for (long v : sg) L.split_groups_max = std::max(L.split_groups_max, v);
+  L.split_part = B > 16 ? take((size_t)L.split_groups_max * SPLIT_PART_PER_GROUP * 4) : take(0);
+  L.split_cnt = take((size_t)L.split_groups_max * 4);
+  L.att_cnt = take((size_t)B * H * 4);
   L.total = off;
   return L;
 }
@@ -170,6 +180,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   const int* ti = h->at<int>(L.ti);
   int* to = h->at<int>(L.to);
   const double* inv_freq = h->at<double>(L.inv_freq);
+  float* split_part = h->at<float>(L.split_part);
+  unsigned* split_cnt = h->at<unsigned>(L.split_cnt);
 
   EmbedArgs ea{};
   ea.ti = ti;
@@ -212,6 +224,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     g.window = W;
     g.ti = ti;
     g.inv_freq = inv_freq;
+    g.split_part = split_part;
+    g.split_cnt = split_cnt;
     launch_gemm(EPI_QKV, g, s);
     if (keep_timed) h->timed[0].push_back([g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); });
     if (keep_timed && l == 0) {
@@ -234,8 +248,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     at.o = h->at<bf16_t>(L.o);
     at.ldo = d;
     at.o_lo = (long)B * d;
+    at.cnt = h->at<unsigned>(L.att_cnt);
     launch_attention(at, s);
-    launch_attention_combine(at, s);
     if (keep_timed) h->timed[1].push_back([at](hipStream_t st) { launch_attention(at, st); });
     if (keep_timed && l == 0) {
       h->timed_bytes[1] = -1;  // depends on positions; computed at timing
@@ -255,6 +269,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     go.xa_lo = (long)B * d;
     go.alpha_next = w.mlp_norm + (long)l * d;
     go.part_out = h->at<float>(L.part);
+    go.split_part = split_part;
+    go.split_cnt = split_cnt;
     launch_gemm(EPI_RESID, go, s);
     if (keep_timed) h->timed[2].push_back([go](hipStream_t st) { launch_gemm(EPI_RESID, go, st); });
     if (keep_timed && l == 0) {
@@ -277,6 +293,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gu.m_out = h->at<bf16_t>(L.m);
     gu.ldm = F;
     gu.m_lo = (long)B * F;
+    gu.split_part = split_part;
+    gu.split_cnt = split_cnt;
     launch_gemm(EPI_GATED, gu, s);
     if (keep_timed) h->timed[3].push_back([gu](hipStream_t st) { launch_gemm(EPI_GATED, gu, st); });
     if (keep_timed && l == 0) {
@@ -298,6 +316,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gd.alpha_next = (l + 1 < dm.n_layers) ? w.attn_norm + (long)(l + 1) * d : w.out_norm;
     gd.part_out = h->at<float>(L.part);
     gd.tap = h->at<float>(L.hidden) + (long)(l + 1) * B * d;
+    gd.split_part = split_part;
+    gd.split_cnt = split_cnt;
     launch_gemm(EPI_RESID, gd, s);
     if (keep_timed) h->timed[4].push_back([gd](hipStream_t st) { launch_gemm(EPI_RESID, gd, st); });
     if (keep_timed && l == 0) {
@@ -323,6 +343,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gt.amax_v = h->at<float>(L.amax_v);
   gt.amax_i = h->at<int>(L.amax_i);
   gt.ld_amax = L.n_amax;
+  gt.split_part = split_part;
+  gt.split_cnt = split_cnt;
   launch_gemm(EPI_LOGITS, gt, s);
   if (keep_timed) {
     h->timed[5].push_back([gt](hipStream_t st) { launch_gemm(EPI_LOGITS, gt, st); });
@@ -344,6 +366,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gp.eps = dm.norm_eps;
   gp.f_out = h->at<float>(L.u);
   gp.ldf = (long)Q * dd;
+  gp.split_part = split_part;
+  gp.split_cnt = split_cnt;
   launch_gemm(EPI_STORE, gp, s);
 
   FinishArgs fa{};
@@ -392,6 +416,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       g.ti = nullptr;
       g.pos_const = k;
       g.inv_freq = nullptr;
+      g.split_part = split_part;
+      g.split_cnt = split_cnt;
       launch_gemm(EPI_QKV, g, s);
 
       AttnArgs at{};
@@ -427,6 +453,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       go.xa_lo = (long)B * dd;
       go.alpha_next = w.dep_mlp_norm + (long)l * dd;
       go.part_out = h->at<float>(L.dpart);
+      go.split_part = split_part;
+      go.split_cnt = split_cnt;
       launch_gemm(EPI_RESID, go, s);
 
       GemmArgs gu{};
@@ -445,6 +473,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       gu.m_out = h->at<bf16_t>(L.dm);
       gu.ldm = dF;
       gu.m_lo = (long)B * dF;
+      gu.split_part = split_part;
+      gu.split_cnt = split_cnt;
       launch_gemm(EPI_GATED, gu, s);
 
       GemmArgs gd{};
@@ -461,6 +491,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       gd.xa_lo = (long)B * dd;
       gd.alpha_next = (l + 1 < dm.dep_layers) ? w.dep_attn_norm + (long)(l + 1) * dd : w.dep_out_norm;
       gd.part_out = h->at<float>(L.dpart);
+      gd.split_part = split_part;
+      gd.split_cnt = split_cnt;
       launch_gemm(EPI_RESID, gd, s);
     }
     GemmArgs gh{};
@@ -480,6 +512,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gh.amax_v = h->at<float>(L.amax_v);
     gh.amax_i = h->at<int>(L.amax_i);
     gh.ld_amax = L.n_amax;
+    gh.split_part = split_part;
+    gh.split_cnt = split_cnt;
     launch_gemm(EPI_LOGITS, gh, s);
 
     FinishArgs f = fa;
@@ -569,6 +603,12 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
     return bail("hipMemcpyAsync", e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
 
+  // arrival tickets of the large-batch GEMM path start at zero (each launch leaves them at zero)
+  if ((e = hipMemsetAsync(h->at<char>(lay.split_cnt), 0, (size_t)lay.split_groups_max * 4, h->stream)) != hipSuccess)
+    return bail("hipMemsetAsync", e);
+  if ((e = hipMemsetAsync(h->at<char>(lay.att_cnt), 0, (size_t)B * dims->n_heads * 4, h->stream)) != hipSuccess)
+    return bail("hipMemsetAsync", e);
+  if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
   if ((e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
   if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess)
     return bail("hipStreamBeginCapture", e);

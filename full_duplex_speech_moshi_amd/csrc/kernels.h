@@ -61,7 +61,17 @@ struct GemmArgs {
   long m_lo;
   float* f_out; long ldf;        // store / logits: [B][ldf] fp32
   float* amax_v; int* amax_i; int ld_amax;  // logits: per-workgroup (max, argmax) [B][ld_amax]
+  // large-batch path (B > 16): per-group partial sums and arrival tickets
+  float* split_part;    // [groups][8][8][2][256] fp32
+  unsigned* split_cnt;  // [groups], zero between launches
 };
+
+// Row tiles (gate/up pairs when gated) one split-path group finishes.
+inline int split_tiles_per_group(int epi) { return epi == EPI_GATED ? 4 : 8; }
+inline long split_groups(int epi, int M) {
+  return ((M + ROWS - 1) / ROWS + split_tiles_per_group(epi) - 1) / split_tiles_per_group(epi);
+}
+constexpr long SPLIT_PART_PER_GROUP = 8L * 8 * 2 * 256;  // floats
 
 void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s);
 void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s);
@@ -79,10 +89,10 @@ struct AttnArgs {
   bf16_t* o;            // [B][ldo] output as a bf16 hi/lo pair (lo plane at o + o_lo)
   int ldo;
   long o_lo;
+  unsigned* cnt;        // [B][n_heads] split tickets, zero between launches (unused with one split)
 };
 
 void launch_attention(const AttnArgs& a, hipStream_t s);
-void launch_attention_combine(const AttnArgs& a, hipStream_t s);
 
 struct EmbedArgs {
   const int* ti; int B, d;

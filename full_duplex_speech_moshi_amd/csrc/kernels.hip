@@ -86,10 +86,15 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---------------------------------------------------------------------------
 
 template <int RT, int NT>
+struct EpiSmem {
+  float fin[RT][ROWS][NT * 16];   // the finished tile(s), [row][slot]
+  float inv_rms[NT * 16];
+};
+
+template <int RT, int NT>
 struct GemmSmem {
   float red[GEMM_WAVES][RT * NT][256];
-  float fin[RT][ROWS][NT * 16];
-  float inv_rms[NT * 16];
+  EpiSmem<RT, NT> e;
 };
 
 template <int NT>
@@ -103,6 +108,105 @@ __device__ __forceinline__ void compute_inv_rms(const GemmArgs& a, float* inv_rm
     }
     s = wave_sum(s);
     if (lane == 0) inv_rms[c] = 1.0f / sqrtf(s / (float)a.feat + a.eps);
+  }
+}
+
+// Epilogue of one finished tile (rows 16*tile..): e.fin holds W x for the
+// tile's rows and every slot, e.inv_rms the slots' inverse RMS where needed.
+template <int EPI, int NT>
+__device__ void gemm_epilogue(const GemmArgs& a, const int tile, EpiSmem<(EPI == EPI_GATED) ? 2 : 1, NT>& e) {
+  const int tid = threadIdx.x;
+  const int row0 = tile * ROWS;
+  if constexpr (EPI == EPI_QKV) {
+    const int d = a.n_heads * a.head_dim;
+    for (int idx = tid; idx < 8 * NT * 16; idx += 512) {
+      const int pr = idx & 7, c = idx >> 3;
+      if (c >= a.B) continue;
+      const int r = row0 + 2 * pr;
+      if (r >= a.M) continue;
+      float y0 = e.fin[0][2 * pr][c] * e.inv_rms[c];
+      float y1 = e.fin[0][2 * pr + 1][c] * e.inv_rms[c];
+      const int which = r / d;  // 0 q, 1 k, 2 v
+      const int rr = r - which * d;
+      const int h = rr / a.head_dim, dd = rr - h * a.head_dim;
+      const int pos = a.ti ? a.ti[c * TI_STRIDE + TI_POS] : a.pos_const;
+      if (which < 2 && a.inv_freq) {
+        const double th = (double)pos * a.inv_freq[dd >> 1];
+        const float cs = (float)cos(th), sn = (float)sin(th);
+        const float r0 = y0 * cs - y1 * sn;
+        const float r1 = y0 * sn + y1 * cs;
+        y0 = r0;
+        y1 = r1;
+      }
+      if (which == 0) {
+        a.q_out[(long)c * a.ldq + rr] = y0;
+        a.q_out[(long)c * a.ldq + rr + 1] = y1;
+      } else {
+        bf16_t* dst = a.kv + (long)c * a.kv_slot_stride + (which == 2 ? a.kv_v_off : 0) +
+                      ((long)h * a.window + (pos % a.window)) * a.head_dim + dd;
+        dst[0] = f2bf(y0);
+        dst[1] = f2bf(y1);
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
+      const int r = idx & 15, c = idx >> 4;
+      if (c >= a.B) continue;
+      const int m = row0 + r;
+      const long o = (long)c * a.ldres + m;
+      const float xn = a.x[o] + e.fin[0][r][c];
+      a.x[o] = xn;
+      store_split(a.xa_out + o, a.xa_lo, xn * a.alpha_next[m]);
+      if (a.tap) a.tap[o] = xn;
+      e.fin[0][r][c] = xn;
+    }
+    __syncthreads();
+    if (tid < a.B) {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) s += e.fin[0][r][tid] * e.fin[0][r][tid];
+      a.part_out[(long)tid * (a.M / ROWS) + tile] = s;
+    }
+  } else if constexpr (EPI == EPI_GATED) {
+    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
+      const int r = idx & 15, c = idx >> 4;
+      if (c >= a.B) continue;
+      const int m = row0 + r;
+      if (m >= a.M) continue;
+      const float gt = e.fin[0][r][c] * e.inv_rms[c];
+      const float up = e.fin[1][r][c] * e.inv_rms[c];
+      store_split(a.m_out + (long)c * a.ldm + m, a.m_lo, gt / (1.0f + expf(-gt)) * up);
+    }
+  } else if constexpr (EPI == EPI_STORE) {
+    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
+      const int r = idx & 15, c = idx >> 4;
+      if (c >= a.B) continue;
+      const int m = row0 + r;
+      if (m >= a.M) continue;
+      a.f_out[(long)c * a.ldf + m] = e.fin[0][r][c] * e.inv_rms[c];
+    }
+  } else {  // EPI_LOGITS
+    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
+      const int r = idx & 15, c = idx >> 4;
+      if (c >= a.B) continue;
+      const int m = row0 + r;
+      if (m >= a.M) continue;
+      const float v = e.fin[0][r][c] * e.inv_rms[c];
+      a.f_out[(long)c * a.ldf + m] = v;
+      e.fin[0][r][c] = v;
+    }
+    __syncthreads();
+    if (tid < a.B) {
+      // strict '>' in row order: the lowest index wins a tie
+      float best = e.fin[0][0][tid];
+      int bi = row0;
+      for (int r = 1; r < ROWS && row0 + r < a.M; ++r) {
+        const float v = e.fin[0][r][tid];
+        if (v > best) { best = v; bi = row0 + r; }
+      }
+      a.amax_v[(long)tid * a.ld_amax + tile] = best;
+      a.amax_i[(long)tid * a.ld_amax + tile] = bi;
+    }
   }
 }
 
@@ -178,7 +282,7 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
     for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.red[wave][rt * NT + ct][j * 64 + lane] = acc[rt][ct][j];
-  if (EPI != EPI_RESID) compute_inv_rms<NT>(a, sm.inv_rms);
+  if (EPI != EPI_RESID) compute_inv_rms<NT>(a, sm.e.inv_rms);
   __syncthreads();
   for (int idx = tid; idx < RT * NT * 256; idx += 512) {
     const int t = idx >> 8, e = idx & 255;
@@ -186,102 +290,10 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
 #pragma unroll
     for (int w = 0; w < GEMM_WAVES; ++w) s += sm.red[w][t][e];
     const int rt = t / NT, ct = t % NT, j = e >> 6, ln = e & 63;
-    sm.fin[rt][4 * (ln >> 4) + j][ct * 16 + (ln & 15)] = s;
+    sm.e.fin[rt][4 * (ln >> 4) + j][ct * 16 + (ln & 15)] = s;
   }
   __syncthreads();
-
-  const int row0 = tile * ROWS;
-  if constexpr (EPI == EPI_QKV) {
-    const int d = a.n_heads * a.head_dim;
-    for (int idx = tid; idx < 8 * NT * 16; idx += 512) {
-      const int pr = idx & 7, c = idx >> 3;
-      if (c >= a.B) continue;
-      const int r = row0 + 2 * pr;
-      if (r >= a.M) continue;
-      float y0 = sm.fin[0][2 * pr][c] * sm.inv_rms[c];
-      float y1 = sm.fin[0][2 * pr + 1][c] * sm.inv_rms[c];
-      const int which = r / d;  // 0 q, 1 k, 2 v
-      const int rr = r - which * d;
-      const int h = rr / a.head_dim, dd = rr - h * a.head_dim;
-      const int pos = a.ti ? a.ti[c * TI_STRIDE + TI_POS] : a.pos_const;
-      if (which < 2 && a.inv_freq) {
-        const double th = (double)pos * a.inv_freq[dd >> 1];
-        const float cs = (float)cos(th), sn = (float)sin(th);
-        const float r0 = y0 * cs - y1 * sn;
-        const float r1 = y0 * sn + y1 * cs;
-        y0 = r0;
-        y1 = r1;
-      }
-      if (which == 0) {
-        a.q_out[(long)c * a.ldq + rr] = y0;
-        a.q_out[(long)c * a.ldq + rr + 1] = y1;
-      } else {
-        bf16_t* dst = a.kv + (long)c * a.kv_slot_stride + (which == 2 ? a.kv_v_off : 0) +
-                      ((long)h * a.window + (pos % a.window)) * a.head_dim + dd;
-        dst[0] = f2bf(y0);
-        dst[1] = f2bf(y1);
-      }
-    }
-  } else if constexpr (EPI == EPI_RESID) {
-    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
-      const int r = idx & 15, c = idx >> 4;
-      if (c >= a.B) continue;
-      const int m = row0 + r;
-      const long o = (long)c * a.ldres + m;
-      const float xn = a.x[o] + sm.fin[0][r][c];
-      a.x[o] = xn;
-      store_split(a.xa_out + o, a.xa_lo, xn * a.alpha_next[m]);
-      if (a.tap) a.tap[o] = xn;
-      sm.fin[0][r][c] = xn;
-    }
-    __syncthreads();
-    if (tid < a.B) {
-      float s = 0.f;
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) s += sm.fin[0][r][tid] * sm.fin[0][r][tid];
-      a.part_out[(long)tid * (a.M / ROWS) + tile] = s;
-    }
-  } else if constexpr (EPI == EPI_GATED) {
-    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
-      const int r = idx & 15, c = idx >> 4;
-      if (c >= a.B) continue;
-      const int m = row0 + r;
-      if (m >= a.M) continue;
-      const float gt = sm.fin[0][r][c] * sm.inv_rms[c];
-      const float up = sm.fin[1][r][c] * sm.inv_rms[c];
-      store_split(a.m_out + (long)c * a.ldm + m, a.m_lo, gt / (1.0f + expf(-gt)) * up);
-    }
-  } else if constexpr (EPI == EPI_STORE) {
-    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
-      const int r = idx & 15, c = idx >> 4;
-      if (c >= a.B) continue;
-      const int m = row0 + r;
-      if (m >= a.M) continue;
-      a.f_out[(long)c * a.ldf + m] = sm.fin[0][r][c] * sm.inv_rms[c];
-    }
-  } else {  // EPI_LOGITS
-    for (int idx = tid; idx < ROWS * NT * 16; idx += 512) {
-      const int r = idx & 15, c = idx >> 4;
-      if (c >= a.B) continue;
-      const int m = row0 + r;
-      if (m >= a.M) continue;
-      const float v = sm.fin[0][r][c] * sm.inv_rms[c];
-      a.f_out[(long)c * a.ldf + m] = v;
-      sm.fin[0][r][c] = v;
-    }
-    __syncthreads();
-    if (tid < a.B) {
-      // strict '>' in row order: the lowest index wins a tie
-      float best = sm.fin[0][0][tid];
-      int bi = row0;
-      for (int r = 1; r < ROWS && row0 + r < a.M; ++r) {
-        const float v = sm.fin[0][r][tid];
-        if (v > best) { best = v; bi = row0 + r; }
-      }
-      a.amax_v[(long)tid * a.ld_amax + tile] = best;
-      a.amax_i[(long)tid * a.ld_amax + tile] = bi;
-    }
-  }
+  gemm_epilogue<EPI, NT>(a, tile, sm.e);
   __syncthreads();  // LDS is reused by the next unit
 }
 
@@ -291,6 +303,128 @@ template <int EPI, int NT>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
   gemm_unit<EPI, NT>(a, blockIdx.x, smem);
+}
+
+// ---------------------------------------------------------------------------
+// The same GEMM for large batches (B > 16).  The per-slot arithmetic is the
+// contract above, computed in another order of work: workgroup (g, j) takes
+// the 8 tiles of row group g over k-range R_j only, with that slice of the
+// activations staged in LDS and shared by its 8 waves (at B = 32 the
+// activation operand is 4x the weight bytes, and re-reading it from L2 per
+// tile saturates the CU's vector-memory pipe).  Each wave writes its partial
+// p_j to a scratch area; the last of the group's 8 workgroups to arrive (an
+// integer ticket) sums p_0..p_7 in order and runs the common epilogue.  For
+// the gated MLP a group is 4 (gate, up) tile pairs.
+// ---------------------------------------------------------------------------
+
+constexpr int SUBK = 8;  // k-steps of activations staged in LDS at a time
+
+template <int EPI, int NT>
+__global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
+  constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
+  constexpr int TPG = (EPI == EPI_GATED) ? 4 : 8;  // epilogue tiles per group
+  constexpr int NTC = NT * 16;
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][SUBK][NTC][32];
+  __shared__ EpiSmem<RT, NT> e;
+  __shared__ float fin_all[8][ROWS][NTC];  // finished tiles of the group (last arriver)
+  __shared__ int is_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int grp = blockIdx.x / GEMM_WAVES, j = blockIdx.x % GEMM_WAVES;
+  const int ks = a.K >> 5;
+  const int s0 = (ks * j) / GEMM_WAVES, s1 = (ks * (j + 1)) / GEMM_WAVES;
+  const int n_tiles = (a.M + ROWS - 1) / ROWS;
+
+  // this wave's weight tile
+  const int unit = grp * TPG + (RT == 2 ? (wave & 3) : wave);
+  const bool w_ok = unit < n_tiles;
+  const long T = (RT == 2 && wave >= 4) ? (long)unit + a.gate_off / ROWS : (long)unit;
+  const bf16_t* arow = a.W + (w_ok ? T : 0) * ks * 512 + lane * 8;
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+
+  for (int sc = s0; sc < s1; sc += SUBK) {
+    const int nsub = min(SUBK, s1 - sc);
+    u32x4 av[SUBK];
+#pragma unroll
+    for (int q = 0; q < SUBK; ++q) av[q] = (w_ok && q < nsub) ? ld16(arow + (long)(sc + q) * 512) : zero;
+    __syncthreads();  // the previous stage has been consumed
+    for (int i = tid; i < 2 * nsub * NTC * 4; i += 512) {
+      const int part = i & 3, c = (i >> 2) % NTC, q = ((i >> 2) / NTC) % nsub, pl = (i >> 2) / NTC / nsub;
+      u32x4 v = zero;
+      if (c < a.B) v = ld16(a.X + (pl ? a.x_lo : 0) + (long)c * a.ldx + (sc + q) * 32 + part * 8);
+      *reinterpret_cast<u32x4*>(&xs[pl][q][c][part * 8]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < SUBK; ++q) {
+      if (q < nsub) {
+        const bf16x8 w8 = __builtin_bit_cast(bf16x8, av[q]);
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[0][q][ct * 16 + r16][g * 8]);
+          const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[1][q][ct * 16 + r16][g * 8]);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh), acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl), acc[ct], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Partial p_j of this wave's tile -> [group][j][wave][ct][256].  The
+  // partials travel between workgroups (and XCDs) through device-coherent
+  // stores and loads (agent-scope atomics: written through and read past the
+  // per-XCD L2), so no L2 write-back or invalidate is needed: every wave waits
+  // until its stores are acknowledged, then one thread takes the ticket.
+  float* P = a.split_part + (((long)grp * GEMM_WAVES + j) * GEMM_WAVES + wave) * (NT * 256);
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __hip_atomic_store(P + ct * 256 + q * 64 + lane, acc[ct][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.split_cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev == GEMM_WAVES - 1;
+    if (is_last) __hip_atomic_store(a.split_cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+
+  if (EPI != EPI_RESID) compute_inv_rms<NT>(a, e.inv_rms);
+  // sum p_0..p_7 of all 8 wave tiles at once (all loads in flight together)
+  float* G = a.split_part + (long)grp * GEMM_WAVES * GEMM_WAVES * (NT * 256);
+#pragma unroll 2
+  for (int idx = tid; idx < GEMM_WAVES * NT * 256; idx += 512) {
+    const int w = idx / (NT * 256), rem = idx % (NT * 256), ct = rem >> 8, el = rem & 255;
+    float v[GEMM_WAVES];
+#pragma unroll
+    for (int jj = 0; jj < GEMM_WAVES; ++jj)
+      v[jj] = __hip_atomic_load(G + ((long)jj * GEMM_WAVES + w) * (NT * 256) + rem, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+    float acc_s = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < GEMM_WAVES; ++jj) acc_s += v[jj];
+    const int q = el >> 6, ln = el & 63;
+    fin_all[w][4 * (ln >> 4) + q][ct * 16 + (ln & 15)] = acc_s;
+  }
+  for (int u = 0; u < TPG; ++u) {
+    const int tile = grp * TPG + u;
+    if (tile >= n_tiles) break;
+    __syncthreads();
+    for (int idx = tid; idx < RT * ROWS * NTC; idx += 512) {
+      const int rt = idx / (ROWS * NTC), r = (idx / NTC) % ROWS, c = idx % NTC;
+      e.fin[rt][r][c] = fin_all[(RT == 2 && rt == 1) ? u + 4 : u][r][c];
+    }
+    __syncthreads();
+    gemm_epilogue<EPI, NT>(a, tile, e);
+  }
 }
 
 // Row-major [M][K] bf16 -> tile layout (see gemm_unit); one thread moves the
@@ -315,13 +449,23 @@ void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s) {
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, M, K, dst);
 }
 
+// Path choice per launch: both paths compute the same bits (the contract),
+// so the choice only moves time.  The k-range split pays off once the
+// activation operand outweighs the weights (B > 16) and the k-ranges are long
+// enough to amortise staging and the partial exchange (K >= 4096).
+static bool use_split(const GemmArgs& a) { return a.B > 16 && a.K >= 4096; }
+
 template <int EPI>
 static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
   const int tiles = (a.M + ROWS - 1) / ROWS;
-  if (a.B > 16)
+  if (use_split(a)) {
+    const int groups = (tiles + split_tiles_per_group(EPI) - 1) / split_tiles_per_group(EPI);
+    hipLaunchKernelGGL((gemm_split_kernel<EPI, 2>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, a);
+  } else if (a.B > 16) {
     hipLaunchKernelGGL((gemm_kernel<EPI, 2>), dim3(tiles), dim3(512), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((gemm_kernel<EPI, 1>), dim3(tiles), dim3(512), 0, s, a);
+  }
 }
 
 void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s) {
@@ -342,9 +486,9 @@ void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s) {
 // "架构": fixed-capacity ring KV; recipe: sliding window 3000 frames).  The
 // keys are visited in position order in fixed splits of ATT_CHUNK keys; one
 // workgroup (4 waves x 64 keys) per (head, slot, split) produces the split's
-// running max, sum of exponentials and unnormalised output; a second pass
-// combines the splits in split order.  With a single split the workgroup
-// writes the normalised output itself.  Lanes: head_dim/8 lanes share one key
+// running max, sum of exponentials and unnormalised output; the last split to
+// finish combines all of them in split order.  With a single split the
+// workgroup writes the normalised output itself.  Lanes: head_dim/8 lanes share one key
 // (16 bytes each, coalesced 256-byte rows for head_dim 128).
 // ---------------------------------------------------------------------------
 
@@ -362,7 +506,11 @@ __device__ __forceinline__ AttnPos attn_pos(const AttnArgs& a, int b) {
 }
 
 // One (head, slot, split) of the decode pass, computed by waves 0..3 of the
-// workgroup (waves beyond 3 of a larger workgroup only join the barriers).
+// workgroup.  Keys and values of the split are requested together up front
+// (the values do not depend on the scores).  With several splits, each
+// writes (max, sum of exponentials, unnormalised output) through
+// device-coherent stores and takes an integer ticket; the last split of the
+// (slot, head) combines all splits in split order and writes the output.
 template <int DH>
 __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int c) {
   constexpr int LPK = DH / 8;
@@ -386,19 +534,30 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
   const bf16_t* kb = a.kv + (long)b * a.kv_slot_stride + (long)h * a.window * DH + sub * 8;
   const bf16_t* vb = kb + a.kv_v_off;
 
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+  u32x4 kr[ITER], vr[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int j = active ? wave * 64 + it * KPI + kg : ATT_CHUNK;
+    kr[it] = zero;
+    vr[it] = zero;
+    if (j < kn) {
+      const long off = (long)((P.lo + k0 + j) % a.window) * DH;
+      kr[it] = ld16(kb + off);
+      vr[it] = ld16(vb + off);
+    }
+  }
+
   float s[ITER];
   float mloc = -INFINITY;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int j = active ? wave * 64 + it * KPI + kg : ATT_CHUNK;
+    float kf[8];
+    unpack8(kr[it], kf);
     float dot = 0.f;
-    if (j < kn) {
-      const int slot = (P.lo + k0 + j) % a.window;
-      float kf[8];
-      unpack8(ld16(kb + (long)slot * DH), kf);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dot += qv[i] * kf[i];
-    }
+    for (int i = 0; i < 8; ++i) dot += qv[i] * kf[i];
 #pragma unroll
     for (int off = LPK / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
     s[it] = (j < kn) ? dot * scale : -INFINITY;
@@ -416,9 +575,8 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
     if (j < kn) {
       const float p = expf(s[it] - mloc);
       if (sub == 0) lsum += p;
-      const int slot = (P.lo + k0 + j) % a.window;
       float vf[8];
-      unpack8(ld16(vb + (long)slot * DH), vf);
+      unpack8(vr[it], vf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] += p * vf[i];
     }
@@ -430,6 +588,7 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
   lsum = wave_sum(lsum);
 
   __shared__ float sm_m[4], sm_l[4], sm_o[4][DH];
+  __shared__ int is_last;
   if (active && lane == 0) {
     sm_m[wave] = mloc;
     sm_l[wave] = lsum;
@@ -438,26 +597,52 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
 #pragma unroll
     for (int i = 0; i < 8; ++i) sm_o[wave][sub * 8 + i] = o[i];
   __syncthreads();
-  if (threadIdx.x < DH) {
-    const int e = threadIdx.x;
-    const float M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
-    float L = 0.f, O = 0.f;
+  const int e = threadIdx.x;
+  float M = 0.f, L = 0.f, O = 0.f;
+  if (e < DH) {
+    M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float f = (sm_m[w] == -INFINITY) ? 0.f : expf(sm_m[w] - M);
       L += sm_l[w] * f;
       O += sm_o[w][e] * f;
     }
-    if (P.nc == 1) {
-      store_split(a.o + (long)b * a.ldo + h * DH + e, a.o_lo, O / L);
-    } else {
-      float* pp = a.part + (((long)b * a.n_heads + h) * a.max_chunks + c) * (DH + 2);
-      pp[2 + e] = O;
-      if (e == 0) {
-        pp[0] = M;
-        pp[1] = L;
-      }
+  }
+  if (P.nc == 1) {
+    if (e < DH) store_split(a.o + (long)b * a.ldo + h * DH + e, a.o_lo, O / L);
+    __syncthreads();  // LDS is reused by the next unit
+    return;
+  }
+  float* base = a.part + ((long)b * a.n_heads + h) * a.max_chunks * (DH + 2);
+  if (e < DH) {
+    float* pp = base + c * (DH + 2);
+    __hip_atomic_store(pp + 2 + e, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (e == 0) {
+      __hip_atomic_store(pp, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pp + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = a.cnt + (long)b * a.n_heads + h;
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev == (unsigned)P.nc - 1;
+    if (is_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (is_last && e < DH) {
+    float Mx = -INFINITY;
+    for (int cc = 0; cc < P.nc; ++cc)
+      Mx = fmaxf(Mx, __hip_atomic_load(base + cc * (DH + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    float Lx = 0.f, Ox = 0.f;
+    for (int cc = 0; cc < P.nc; ++cc) {
+      float* pp = base + cc * (DH + 2);
+      const float f = expf(__hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - Mx);
+      Lx += __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
+      Ox += __hip_atomic_load(pp + 2 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
+    }
+    store_split(a.o + (long)b * a.ldo + h * DH + e, a.o_lo, Ox / Lx);
   }
   __syncthreads();  // LDS is reused by the next unit
 }
@@ -465,25 +650,6 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
 template <int DH>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   attn_unit<DH>(a, blockIdx.x, blockIdx.y, blockIdx.z);
-}
-
-template <int DH>
-__global__ __launch_bounds__(DH) void attn_combine_kernel(AttnArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const AttnPos P = attn_pos(a, b);
-  if (P.nc == 1) return;
-  const int e = threadIdx.x;
-  const float* base = a.part + ((long)b * a.n_heads + h) * a.max_chunks * (DH + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < P.nc; ++c) M = fmaxf(M, base[c * (DH + 2)]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < P.nc; ++c) {
-    const float* pp = base + c * (DH + 2);
-    const float f = expf(pp[0] - M);
-    L += pp[1] * f;
-    O += pp[2 + e] * f;
-  }
-  store_split(a.o + (long)b * a.ldo + h * DH + e, a.o_lo, O / L);
 }
 
 template <int DH>
@@ -499,13 +665,6 @@ void launch_attention(const AttnArgs& a, hipStream_t s) {
   }
 }
 
-void launch_attention_combine(const AttnArgs& a, hipStream_t s) {
-  switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL((attn_combine_kernel<32>), dim3(a.n_heads, a.B), dim3(32), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(a.n_heads, a.B), dim3(64), 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(a.n_heads, a.B), dim3(128), 0, s, a); break;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // 17-way embedding gather-sum: x_b = sum over rows r of table_r[col_b[r]], in

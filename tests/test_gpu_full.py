@@ -134,3 +134,33 @@ def test_full_isolation_mixed_occupancy_bit_exact(full):
             np.testing.assert_array_equal(tp["hidden"][:, 0], taps[t]["hidden"][:, b])
             np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
         e1.close()
+
+
+@pytest.mark.timeout(900)
+def test_full_isolation_large_batch_path_bit_exact(full):
+    """B = 20 uses the large-batch GEMM path (k-range split across
+    workgroups, partials summed in fixed order); slots 0 and 19 must equal
+    B = 1 handles (small-batch path) bit for bit."""
+    _say("case: 7B isolation, B=20 (split-K GEMM path) vs B=1")
+    B = 20
+    fill = synth.ring_fill(DM, 7, 40)
+    codes = [synth.user_codes(500 + b, 2) for b in range(B)]
+    eb = _engine(full, B)
+    eb.ring_fill(19, *fill)
+    toks, taps = [], []
+    for t in range(2):
+        toks.append(eb.step(np.stack([codes[b][t] for b in range(B)])))
+        taps.append(eb.taps())
+    eb.close()
+    for b in (0, 19):
+        e1 = _engine(full, 1)
+        if b == 19:
+            e1.ring_fill(0, *fill)
+        for t in range(2):
+            tk = e1.step(codes[b][t:t + 1])
+            tp = e1.taps()
+            np.testing.assert_array_equal(tk[0], toks[t][b])
+            np.testing.assert_array_equal(tp["hidden"][:, 0], taps[t]["hidden"][:, b])
+            np.testing.assert_array_equal(tp["text_logits"][0], taps[t]["text_logits"][b])
+            np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
+        e1.close()
