@@ -97,24 +97,74 @@ struct GemmSmem {
   EpiSmem<RT, NT> e;
 };
 
+// Inverse RMS of each slot's input from the per-16-feature sums of squares.
+// The loads are issued early (rms_preload, before the weight stream) and the
+// sums formed later (rms_finish); lane sums run over i = lane, lane+64, ...
+// and then a fixed butterfly, whichever way the loads were issued.
+constexpr int RMS_PRE = 4;  // partials per lane held in registers
 template <int NT>
-__device__ __forceinline__ void compute_inv_rms(const GemmArgs& a, float* inv_rms) {
+struct RmsPre {
+  float v[(NT * 16 + GEMM_WAVES - 1) / GEMM_WAVES][RMS_PRE];
+};
+
+template <int NT>
+__device__ __forceinline__ void rms_preload(const GemmArgs& a, RmsPre<NT>& rp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int c = wave; c < NT * 16; c += GEMM_WAVES) {
+#pragma unroll
+  for (int k = 0; k < (NT * 16 + GEMM_WAVES - 1) / GEMM_WAVES; ++k) {
+    const int c = wave + k * GEMM_WAVES;
+#pragma unroll
+    for (int q = 0; q < RMS_PRE; ++q) {
+      const int i = lane + 64 * q;
+      rp.v[k][q] = (c < a.B && i < a.n_part) ? a.part_in[(long)c * a.n_part + i] : 0.f;
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void rms_finish(const GemmArgs& a, const RmsPre<NT>& rp, float* inv_rms) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < (NT * 16 + GEMM_WAVES - 1) / GEMM_WAVES; ++k) {
+    const int c = wave + k * GEMM_WAVES;
     float s = 0.f;
     if (c < a.B) {
-      const float* p = a.part_in + (long)c * a.n_part;
-      for (int i = lane; i < a.n_part; i += 64) s += p[i];
+#pragma unroll
+      for (int q = 0; q < RMS_PRE; ++q)
+        if (lane + 64 * q < a.n_part) s += rp.v[k][q];
+      for (int i = lane + 64 * RMS_PRE; i < a.n_part; i += 64) s += a.part_in[(long)c * a.n_part + i];
     }
     s = wave_sum(s);
-    if (lane == 0) inv_rms[c] = 1.0f / sqrtf(s / (float)a.feat + a.eps);
+    if (lane == 0 && c < NT * 16) inv_rms[c] = 1.0f / sqrtf(s / (float)a.feat + a.eps);
   }
+}
+
+// Per-thread epilogue inputs loaded before the weight stream: for EPI_RESID
+// the old residual value and the next norm's alpha of item (row tid%16, slot
+// tid/16).
+struct EpiPre {
+  float x0, x1;
+};
+
+template <int EPI, int NT>
+__device__ __forceinline__ EpiPre epi_preload(const GemmArgs& a, const int tile) {
+  EpiPre p{0.f, 0.f};
+  const int tid = threadIdx.x, row0 = tile * ROWS;
+  if constexpr (EPI == EPI_RESID) {
+    const int r = tid & 15, c = tid >> 4;
+    if (c < a.B && c < NT * 16) {
+      p.x0 = a.x[(long)c * a.ldres + row0 + r];
+      p.x1 = a.alpha_next[row0 + r];
+    }
+  }
+  return p;
 }
 
 // Epilogue of one finished tile (rows 16*tile..): e.fin holds W x for the
 // tile's rows and every slot, e.inv_rms the slots' inverse RMS where needed.
 template <int EPI, int NT>
-__device__ void gemm_epilogue(const GemmArgs& a, const int tile, EpiSmem<(EPI == EPI_GATED) ? 2 : 1, NT>& e) {
+__device__ void gemm_epilogue(const GemmArgs& a, const int tile, EpiSmem<(EPI == EPI_GATED) ? 2 : 1, NT>& e,
+                              const EpiPre& pre) {
   const int tid = threadIdx.x;
   const int row0 = tile * ROWS;
   if constexpr (EPI == EPI_QKV) {
@@ -154,9 +204,9 @@ __device__ void gemm_epilogue(const GemmArgs& a, const int tile, EpiSmem<(EPI ==
       if (c >= a.B) continue;
       const int m = row0 + r;
       const long o = (long)c * a.ldres + m;
-      const float xn = a.x[o] + e.fin[0][r][c];
+      const float xn = pre.x0 + e.fin[0][r][c];  // item idx == tid: pre holds x[o], alpha_next[m]
       a.x[o] = xn;
-      store_split(a.xa_out + o, a.xa_lo, xn * a.alpha_next[m]);
+      store_split(a.xa_out + o, a.xa_lo, xn * pre.x1);
       if (a.tap) a.tap[o] = xn;
       e.fin[0][r][c] = xn;
     }
@@ -246,6 +296,11 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) acc[rt][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+  // epilogue inputs requested now, consumed after the weight stream
+  const EpiPre pre = epi_preload<EPI, NT>(a, tile);
+  RmsPre<NT> rp;
+  if (EPI != EPI_RESID) rms_preload<NT>(a, rp);
+
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
   for (int s = s0; s < s1; s += U) {
     u32x4 av[RT][U], bh[NT][U], bl[NT][U];
@@ -282,7 +337,7 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
     for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.red[wave][rt * NT + ct][j * 64 + lane] = acc[rt][ct][j];
-  if (EPI != EPI_RESID) compute_inv_rms<NT>(a, sm.e.inv_rms);
+  if (EPI != EPI_RESID) rms_finish<NT>(a, rp, sm.e.inv_rms);
   __syncthreads();
   for (int idx = tid; idx < RT * NT * 256; idx += 512) {
     const int t = idx >> 8, e = idx & 255;
@@ -293,7 +348,7 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
     sm.e.fin[rt][4 * (ln >> 4) + j][ct * 16 + (ln & 15)] = s;
   }
   __syncthreads();
-  gemm_epilogue<EPI, NT>(a, tile, sm.e);
+  gemm_epilogue<EPI, NT>(a, tile, sm.e, pre);
   __syncthreads();  // LDS is reused by the next unit
 }
 
@@ -397,7 +452,11 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   __syncthreads();
   if (!is_last) return;
 
-  if (EPI != EPI_RESID) compute_inv_rms<NT>(a, e.inv_rms);
+  if (EPI != EPI_RESID) {
+    RmsPre<NT> rp;
+    rms_preload<NT>(a, rp);
+    rms_finish<NT>(a, rp, e.inv_rms);
+  }
   // sum p_0..p_7 of all 8 wave tiles at once (all loads in flight together)
   float* G = a.split_part + (long)grp * GEMM_WAVES * GEMM_WAVES * (NT * 256);
 #pragma unroll 2
@@ -422,8 +481,9 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
       const int rt = idx / (ROWS * NTC), r = (idx / NTC) % ROWS, c = idx % NTC;
       e.fin[rt][r][c] = fin_all[(RT == 2 && rt == 1) ? u + 4 : u][r][c];
     }
+    const EpiPre pre = epi_preload<EPI, NT>(a, tile);
     __syncthreads();
-    gemm_epilogue<EPI, NT>(a, tile, e);
+    gemm_epilogue<EPI, NT>(a, tile, e, pre);
   }
 }
 
