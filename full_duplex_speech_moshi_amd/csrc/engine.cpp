@@ -28,8 +28,8 @@ constexpr int DEP_WINDOW = 16;  // depformer per-frame keys (one per codebook st
 struct Layout {
   // byte offsets into the arena
   size_t ring, dkv, x, xa, part, q, att_part, o, m, hidden, text_logits, amax_v, amax_i, u, y, ya, dpart, dq, dout,
-      dm, dep_logits, ti, to, inv_freq, split_part, split_cnt, att_cnt, total;
-  long split_groups_max;
+      dm, dep_logits, ti, to, inv_freq, split_part, att_cnt, total;
+  long wide_part_max;
   int max_chunks, n_amax;
   long ring_slot_elems, ring_layer_elems, ring_v_off;
   long dkv_slot_elems, dkv_layer_elems, dkv_v_off;
@@ -96,14 +96,13 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.ti = take(B * TI_STRIDE * 4);
   L.to = take(B * TO_STRIDE * 4);
   L.inv_freq = take((hd / 2) * 8);
-  // scratch of the large-batch GEMM path: the largest group count of any GEMM of the tick
-  const long sg[] = {split_groups(EPI_QKV, 3 * d), split_groups(EPI_RESID, d), split_groups(EPI_GATED, F),
-                     split_groups(EPI_LOGITS, Vt), split_groups(EPI_STORE, Q * dd), split_groups(EPI_QKV, 3 * dd),
-                     split_groups(EPI_RESID, dd), split_groups(EPI_GATED, dF), split_groups(EPI_LOGITS, A)};
-  L.split_groups_max = 0;
-  for (long v : sg) L.split_groups_max = std::max(L.split_groups_max, v);
-  L.split_part = B > 16 ? take((size_t)L.split_groups_max * SPLIT_PART_PER_GROUP * 4) : take(0);
-  L.split_cnt = take((size_t)L.split_groups_max * 4);
+  // scratch of the large-batch GEMM path: the largest partial area of any GEMM of the tick
+  const struct { Epi epi; long M; } wide[] = {{EPI_QKV, 3L * d}, {EPI_RESID, d}, {EPI_GATED, F}, {EPI_LOGITS, Vt},
+                                             {EPI_STORE, (long)Q * dd}, {EPI_QKV, 3L * dd}, {EPI_RESID, dd},
+                                             {EPI_GATED, dF}, {EPI_LOGITS, A}};
+  L.wide_part_max = 0;
+  for (const auto& g : wide) L.wide_part_max = std::max(L.wide_part_max, wide_part_floats(g.epi, (int)g.M));
+  L.split_part = B > 16 ? take((size_t)L.wide_part_max * 4) : take(0);
   L.att_cnt = take((size_t)B * H * 4);
   L.total = off;
   return L;
@@ -181,7 +180,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   int* to = h->at<int>(L.to);
   const double* inv_freq = h->at<double>(L.inv_freq);
   float* split_part = h->at<float>(L.split_part);
-  unsigned* split_cnt = h->at<unsigned>(L.split_cnt);
 
   EmbedArgs ea{};
   ea.ti = ti;
@@ -225,7 +223,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     g.ti = ti;
     g.inv_freq = inv_freq;
     g.split_part = split_part;
-    g.split_cnt = split_cnt;
     launch_gemm(EPI_QKV, g, s);
     if (keep_timed) h->timed[0].push_back([g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); });
     if (keep_timed && l == 0) {
@@ -270,7 +267,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     go.alpha_next = w.mlp_norm + (long)l * d;
     go.part_out = h->at<float>(L.part);
     go.split_part = split_part;
-    go.split_cnt = split_cnt;
     launch_gemm(EPI_RESID, go, s);
     if (keep_timed) h->timed[2].push_back([go](hipStream_t st) { launch_gemm(EPI_RESID, go, st); });
     if (keep_timed && l == 0) {
@@ -294,7 +290,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gu.ldm = F;
     gu.m_lo = (long)B * F;
     gu.split_part = split_part;
-    gu.split_cnt = split_cnt;
     launch_gemm(EPI_GATED, gu, s);
     if (keep_timed) h->timed[3].push_back([gu](hipStream_t st) { launch_gemm(EPI_GATED, gu, st); });
     if (keep_timed && l == 0) {
@@ -317,7 +312,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gd.part_out = h->at<float>(L.part);
     gd.tap = h->at<float>(L.hidden) + (long)(l + 1) * B * d;
     gd.split_part = split_part;
-    gd.split_cnt = split_cnt;
     launch_gemm(EPI_RESID, gd, s);
     if (keep_timed) h->timed[4].push_back([gd](hipStream_t st) { launch_gemm(EPI_RESID, gd, st); });
     if (keep_timed && l == 0) {
@@ -344,7 +338,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gt.amax_i = h->at<int>(L.amax_i);
   gt.ld_amax = L.n_amax;
   gt.split_part = split_part;
-  gt.split_cnt = split_cnt;
   launch_gemm(EPI_LOGITS, gt, s);
   if (keep_timed) {
     h->timed[5].push_back([gt](hipStream_t st) { launch_gemm(EPI_LOGITS, gt, st); });
@@ -367,7 +360,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gp.f_out = h->at<float>(L.u);
   gp.ldf = (long)Q * dd;
   gp.split_part = split_part;
-  gp.split_cnt = split_cnt;
   launch_gemm(EPI_STORE, gp, s);
 
   FinishArgs fa{};
@@ -417,7 +409,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       g.pos_const = k;
       g.inv_freq = nullptr;
       g.split_part = split_part;
-      g.split_cnt = split_cnt;
       launch_gemm(EPI_QKV, g, s);
 
       AttnArgs at{};
@@ -454,7 +445,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       go.alpha_next = w.dep_mlp_norm + (long)l * dd;
       go.part_out = h->at<float>(L.dpart);
       go.split_part = split_part;
-      go.split_cnt = split_cnt;
       launch_gemm(EPI_RESID, go, s);
 
       GemmArgs gu{};
@@ -474,7 +464,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       gu.ldm = dF;
       gu.m_lo = (long)B * dF;
       gu.split_part = split_part;
-      gu.split_cnt = split_cnt;
       launch_gemm(EPI_GATED, gu, s);
 
       GemmArgs gd{};
@@ -492,7 +481,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       gd.alpha_next = (l + 1 < dm.dep_layers) ? w.dep_attn_norm + (long)(l + 1) * dd : w.dep_out_norm;
       gd.part_out = h->at<float>(L.dpart);
       gd.split_part = split_part;
-      gd.split_cnt = split_cnt;
       launch_gemm(EPI_RESID, gd, s);
     }
     GemmArgs gh{};
@@ -513,7 +501,6 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gh.amax_i = h->at<int>(L.amax_i);
     gh.ld_amax = L.n_amax;
     gh.split_part = split_part;
-    gh.split_cnt = split_cnt;
     launch_gemm(EPI_LOGITS, gh, s);
 
     FinishArgs f = fa;
@@ -603,9 +590,6 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
     return bail("hipMemcpyAsync", e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
 
-  // arrival tickets of the large-batch GEMM path start at zero (each launch leaves them at zero)
-  if ((e = hipMemsetAsync(h->at<char>(lay.split_cnt), 0, (size_t)lay.split_groups_max * 4, h->stream)) != hipSuccess)
-    return bail("hipMemsetAsync", e);
   if ((e = hipMemsetAsync(h->at<char>(lay.att_cnt), 0, (size_t)B * dims->n_heads * 4, h->stream)) != hipSuccess)
     return bail("hipMemsetAsync", e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);

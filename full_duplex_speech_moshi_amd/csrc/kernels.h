@@ -61,17 +61,14 @@ struct GemmArgs {
   long m_lo;
   float* f_out; long ldf;        // store / logits: [B][ldf] fp32
   float* amax_v; int* amax_i; int ld_amax;  // logits: per-workgroup (max, argmax) [B][ld_amax]
-  // large-batch path (B > 16): per-group partial sums and arrival tickets
-  float* split_part;    // [groups][8][8][2][256] fp32
-  unsigned* split_cnt;  // [groups], zero between launches
+  // large-batch path (B > 16): per-tile partial sums
+  float* split_part;    // [weight tile][8 ranges][512] fp32
 };
 
-// Row tiles (gate/up pairs when gated) one split-path group finishes.
-inline int split_tiles_per_group(int epi) { return epi == EPI_GATED ? 4 : 8; }
-inline long split_groups(int epi, int M) {
-  return ((M + ROWS - 1) / ROWS + split_tiles_per_group(epi) - 1) / split_tiles_per_group(epi);
-}
-constexpr long SPLIT_PART_PER_GROUP = 8L * 8 * 2 * 256;  // floats
+// Large-batch path: weight tiles (gate and up tiles counted apart) and
+// partial floats (8 ranges x 512 per weight tile).
+inline long wide_tiles(int epi, int M) { return (epi == EPI_GATED ? 2L : 1L) * ((M + ROWS - 1) / ROWS); }
+inline long wide_part_floats(int epi, int M) { return wide_tiles(epi, M) * 8 * 512; }
 
 void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s);
 void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s);

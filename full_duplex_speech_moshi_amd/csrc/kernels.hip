@@ -37,6 +37,15 @@ __device__ __forceinline__ void store_split(bf16_t* p, long lo, float v) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Weight stream: read once per tick and far larger than the caches, so the
+// loads carry the non-temporal hint.
+#ifndef PP_WEIGHT_TEMPORAL
+__device__ __forceinline__ u32x4 ldw16(const bf16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+#else
+__device__ __forceinline__ u32x4 ldw16(const bf16_t* p) { return ld16(p); }
+#endif
 
 __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
 #pragma unroll
@@ -309,7 +318,7 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
       const bool ok = (s + u) < s1;
       const int k = (s + u) * 32;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) av[rt][u] = ok ? ld16(arow[rt] + (long)(s + u) * 512) : zero;
+      for (int rt = 0; rt < RT; ++rt) av[rt][u] = ok ? ldw16(arow[rt] + (long)(s + u) * 512) : zero;
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
         bh[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + k) : zero;
@@ -361,130 +370,112 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The same GEMM for large batches (B > 16).  The per-slot arithmetic is the
-// contract above, computed in another order of work: workgroup (g, j) takes
-// the 8 tiles of row group g over k-range R_j only, with that slice of the
-// activations staged in LDS and shared by its 8 waves (at B = 32 the
-// activation operand is 4x the weight bytes, and re-reading it from L2 per
-// tile saturates the CU's vector-memory pipe).  Each wave writes its partial
-// p_j to a scratch area; the last of the group's 8 workgroups to arrive (an
-// integer ticket) sums p_0..p_7 in order and runs the common epilogue.  For
-// the gated MLP a group is 4 (gate, up) tile pairs.
+// The same GEMM for large batches (B > 16, K >= 4096).  The per-slot
+// arithmetic is the contract above, computed in another order of work.  At
+// B = 32 the activation operand is 4x the weight bytes per k-step, so it is
+// staged in LDS and shared by 8 weight tiles:
+//
+//   * gemm_wide_kernel: workgroup (g, j), j = blockIdx % 8, takes k-range R_j
+//     of the 8 weight tiles 8g..8g+7, one per wave (for the gated MLP the
+//     gate tiles come first, then the up tiles).  Consecutive workgroups are
+//     spread over the XCDs round-robin, so all workgroups of range j share
+//     one XCD's L2 for their activation slice.  Each wave streams its tile's
+//     weights (non-temporal) through the staged slice and stores p_j;
+//   * gemm_wide_reduce: one workgroup per output tile sums p_0..p_7 in order
+//     and runs the common epilogue.
 // ---------------------------------------------------------------------------
 
-constexpr int SUBK = 8;  // k-steps of activations staged in LDS at a time
+constexpr int WIDE_SK = 8;  // k-steps of activations per LDS stage
+constexpr int WIDE_U = 4;   // weight loads in flight per wave
 
-template <int EPI, int NT>
-__global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
-  constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
-  constexpr int TPG = (EPI == EPI_GATED) ? 4 : 8;  // epilogue tiles per group
-  constexpr int NTC = NT * 16;
-  __shared__ __attribute__((aligned(16))) bf16_t xs[2][SUBK][NTC][32];
-  __shared__ EpiSmem<RT, NT> e;
-  __shared__ float fin_all[8][ROWS][NTC];  // finished tiles of the group (last arriver)
-  __shared__ int is_last;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int grp = blockIdx.x / GEMM_WAVES, j = blockIdx.x % GEMM_WAVES;
+template <int RT>
+__global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
+  constexpr int NT = 2, NTC = 32;
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][WIDE_SK][NTC][32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int j = blockIdx.x % GEMM_WAVES, grp = blockIdx.x / GEMM_WAVES;
   const int ks = a.K >> 5;
   const int s0 = (ks * j) / GEMM_WAVES, s1 = (ks * (j + 1)) / GEMM_WAVES;
-  const int n_tiles = (a.M + ROWS - 1) / ROWS;
-
-  // this wave's weight tile
-  const int unit = grp * TPG + (RT == 2 ? (wave & 3) : wave);
-  const bool w_ok = unit < n_tiles;
-  const long T = (RT == 2 && wave >= 4) ? (long)unit + a.gate_off / ROWS : (long)unit;
-  const bf16_t* arow = a.W + (w_ok ? T : 0) * ks * 512 + lane * 8;
+  const int n_out = (a.M + ROWS - 1) / ROWS;
+  const int t = grp * GEMM_WAVES + wave;  // this wave's weight tile
+  const bool t_ok = t < RT * n_out;
+  const long wt = (RT == 2 && t >= n_out) ? (long)(t - n_out) + a.gate_off / ROWS : (long)t;
+  const bf16_t* w = a.W + (t_ok ? wt : 0) * ks * 512 + lane * 8;
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
 
   f32x4 acc[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
 
-  for (int sc = s0; sc < s1; sc += SUBK) {
-    const int nsub = min(SUBK, s1 - sc);
-    u32x4 av[SUBK];
-#pragma unroll
-    for (int q = 0; q < SUBK; ++q) av[q] = (w_ok && q < nsub) ? ld16(arow + (long)(sc + q) * 512) : zero;
-    __syncthreads();  // the previous stage has been consumed
+  for (int c0 = s0; c0 < s1; c0 += WIDE_SK) {
+    const int nsub = min(WIDE_SK, s1 - c0);
+    if (c0 != s0) __syncthreads();  // the previous stage has been consumed
     for (int i = tid; i < 2 * nsub * NTC * 4; i += 512) {
       const int part = i & 3, c = (i >> 2) % NTC, q = ((i >> 2) / NTC) % nsub, pl = (i >> 2) / NTC / nsub;
       u32x4 v = zero;
-      if (c < a.B) v = ld16(a.X + (pl ? a.x_lo : 0) + (long)c * a.ldx + (sc + q) * 32 + part * 8);
+      if (c < a.B) v = ld16(a.X + (pl ? a.x_lo : 0) + (long)c * a.ldx + (c0 + q) * 32 + part * 8);
       *reinterpret_cast<u32x4*>(&xs[pl][q][c][part * 8]) = v;
     }
     __syncthreads();
+    for (int sb = 0; sb < nsub; sb += WIDE_U) {
+      u32x4 av[WIDE_U];
 #pragma unroll
-    for (int q = 0; q < SUBK; ++q) {
-      if (q < nsub) {
-        const bf16x8 w8 = __builtin_bit_cast(bf16x8, av[q]);
+      for (int u = 0; u < WIDE_U; ++u)
+        av[u] = (t_ok && sb + u < nsub) ? ldw16(w + (long)(c0 + sb + u) * 512) : zero;
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[0][q][ct * 16 + r16][g * 8]);
-          const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[1][q][ct * 16 + r16][g * 8]);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh), acc[ct], 0, 0, 0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl), acc[ct], 0, 0, 0);
+      for (int u = 0; u < WIDE_U; ++u) {
+        if (sb + u < nsub) {
+          const bf16x8 w8 = __builtin_bit_cast(bf16x8, av[u]);
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[0][sb + u][ct * 16 + r16][g4 * 8]);
+            const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[1][sb + u][ct * 16 + r16][g4 * 8]);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh), acc[ct], 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl), acc[ct], 0, 0, 0);
+          }
         }
       }
     }
   }
+  // p_j of tile t: [t][j][ct][q][lane]
+  if (t_ok) {
+    float* P = a.split_part + ((long)t * GEMM_WAVES + j) * (NT * 256) + lane;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) P[ct * 256 + q * 64] = acc[ct][q];
+  }
+}
 
-  // Partial p_j of this wave's tile -> [group][j][wave][ct][256].  The
-  // partials travel between workgroups (and XCDs) through device-coherent
-  // stores and loads (agent-scope atomics: written through and read past the
-  // per-XCD L2), so no L2 write-back or invalidate is needed: every wave waits
-  // until its stores are acknowledged, then one thread takes the ticket.
-  float* P = a.split_part + (((long)grp * GEMM_WAVES + j) * GEMM_WAVES + wave) * (NT * 256);
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_wide_reduce(GemmArgs a) {
+  constexpr int NT = 2, RT = (EPI == EPI_GATED) ? 2 : 1;
+  __shared__ EpiSmem<RT, NT> e;
+  const int tile = blockIdx.x, tid = threadIdx.x;
+  const int n_out = (a.M + ROWS - 1) / ROWS;
+  // element tid of the partial tile: column tile ct, accumulator q, lane ln
+  float v[RT][GEMM_WAVES];
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
+  for (int rt = 0; rt < RT; ++rt) {
+    const long tt = rt ? (long)tile + n_out : (long)tile;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __hip_atomic_store(P + ct * 256 + q * 64 + lane, acc[ct][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0);
+    for (int jj = 0; jj < GEMM_WAVES; ++jj) v[rt][jj] = a.split_part[(tt * GEMM_WAVES + jj) * (NT * 256) + tid];
+  }
+  RmsPre<NT> rp;
+  if (EPI != EPI_RESID) rms_preload<NT>(a, rp);
+  const EpiPre pre = epi_preload<EPI, NT>(a, tile);
+  const int ct = tid >> 8, q = (tid >> 6) & 3, ln = tid & 63;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float s = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < GEMM_WAVES; ++jj) s += v[rt][jj];
+    e.fin[rt][4 * (ln >> 4) + q][ct * 16 + (ln & 15)] = s;
+  }
+  if (EPI != EPI_RESID) rms_finish<NT>(a, rp, e.inv_rms);
   __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.split_cnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev == GEMM_WAVES - 1;
-    if (is_last) __hip_atomic_store(a.split_cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!is_last) return;
-
-  if (EPI != EPI_RESID) {
-    RmsPre<NT> rp;
-    rms_preload<NT>(a, rp);
-    rms_finish<NT>(a, rp, e.inv_rms);
-  }
-  // sum p_0..p_7 of all 8 wave tiles at once (all loads in flight together)
-  float* G = a.split_part + (long)grp * GEMM_WAVES * GEMM_WAVES * (NT * 256);
-#pragma unroll 2
-  for (int idx = tid; idx < GEMM_WAVES * NT * 256; idx += 512) {
-    const int w = idx / (NT * 256), rem = idx % (NT * 256), ct = rem >> 8, el = rem & 255;
-    float v[GEMM_WAVES];
-#pragma unroll
-    for (int jj = 0; jj < GEMM_WAVES; ++jj)
-      v[jj] = __hip_atomic_load(G + ((long)jj * GEMM_WAVES + w) * (NT * 256) + rem, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-    float acc_s = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < GEMM_WAVES; ++jj) acc_s += v[jj];
-    const int q = el >> 6, ln = el & 63;
-    fin_all[w][4 * (ln >> 4) + q][ct * 16 + (ln & 15)] = acc_s;
-  }
-  for (int u = 0; u < TPG; ++u) {
-    const int tile = grp * TPG + u;
-    if (tile >= n_tiles) break;
-    __syncthreads();
-    for (int idx = tid; idx < RT * ROWS * NTC; idx += 512) {
-      const int rt = idx / (ROWS * NTC), r = (idx / NTC) % ROWS, c = idx % NTC;
-      e.fin[rt][r][c] = fin_all[(RT == 2 && rt == 1) ? u + 4 : u][r][c];
-    }
-    const EpiPre pre = epi_preload<EPI, NT>(a, tile);
-    __syncthreads();
-    gemm_epilogue<EPI, NT>(a, tile, e, pre);
-  }
+  gemm_epilogue<EPI, NT>(a, tile, e, pre);
 }
 
 // Row-major [M][K] bf16 -> tile layout (see gemm_unit); one thread moves the
@@ -513,14 +504,15 @@ void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s) {
 // so the choice only moves time.  The k-range split pays off once the
 // activation operand outweighs the weights (B > 16) and the k-ranges are long
 // enough to amortise staging and the partial exchange (K >= 4096).
-static bool use_split(const GemmArgs& a) { return a.B > 16 && a.K >= 4096; }
+static bool use_wide(const GemmArgs& a) { return a.B > 16 && a.K >= 4096; }
 
 template <int EPI>
 static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
   const int tiles = (a.M + ROWS - 1) / ROWS;
-  if (use_split(a)) {
-    const int groups = (tiles + split_tiles_per_group(EPI) - 1) / split_tiles_per_group(EPI);
-    hipLaunchKernelGGL((gemm_split_kernel<EPI, 2>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, a);
+  if (use_wide(a)) {
+    const long groups = (wide_tiles(EPI, a.M) + GEMM_WAVES - 1) / GEMM_WAVES;
+    hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, a);
   } else if (a.B > 16) {
     hipLaunchKernelGGL((gemm_kernel<EPI, 2>), dim3(tiles), dim3(512), 0, s, a);
   } else {
@@ -733,39 +725,46 @@ void launch_attention(const AttnArgs& a, hipStream_t s) {
 // and the hidden-state tap.
 // ---------------------------------------------------------------------------
 
+// One thread per 8 features of one slot: the 17 row indices are read first,
+// then all 17 row segments are requested before any is summed, so the gather
+// costs one memory round trip.  Rows are summed in row order r = 0..16.
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
-  const int b = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g8 = blockIdx.x * blockDim.x + threadIdx.x;  // 8-feature group
+  if (g8 >= a.d / 8) return;                              // d % 16 == 0: pairs stay whole
   const int* t = a.ti + b * TI_STRIDE + TI_COL;
-  const long off = (long)b * a.d;
-  for (int grp = threadIdx.x; grp < a.d / 16; grp += blockDim.x) {
-    float acc[16];
+  u32x4 v[17];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    for (int r = 0; r < 17; ++r) {
-      const bf16_t* e = (r == 0) ? a.emb_text + (long)t[0] * a.d
-                                 : a.emb_audio + ((long)(r - 1) * a.audio_rows + t[r]) * a.d;
-      e += grp * 16;
-      float f[16];
-      unpack8(ld16(e), f);
-      unpack8(ld16(e + 8), f + 8);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] += f[i];
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = grp * 16 + i;
-      a.x[off + m] = acc[i];
-      a.tap[off + m] = acc[i];
-      store_split(a.xa + off + m, a.xa_lo, acc[i] * a.alpha[m]);
-      ss += acc[i] * acc[i];
-    }
-    a.part[(long)b * (a.d / 16) + grp] = ss;
+  for (int r = 0; r < 17; ++r) {
+    const bf16_t* e = (r == 0) ? a.emb_text + (long)t[0] * a.d
+                               : a.emb_audio + ((long)(r - 1) * a.audio_rows + t[r]) * a.d;
+    v[r] = ld16(e + g8 * 8);
   }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 17; ++r) {
+    float f[8];
+    unpack8(v[r], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += f[i];
+  }
+  const long off = (long)b * a.d + g8 * 8;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a.x[off + i] = acc[i];
+    a.tap[off + i] = acc[i];
+    store_split(a.xa + off + i, a.xa_lo, acc[i] * a.alpha[g8 * 8 + i]);
+    ss += acc[i] * acc[i];
+  }
+  ss += __shfl_xor(ss, 1);  // the two halves of a 16-feature group are adjacent lanes
+  if ((g8 & 1) == 0) a.part[(long)b * (a.d / 16) + g8 / 2] = ss;
 }
 
 void launch_embed(const EmbedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(embed_kernel, dim3((a.d / 8 + 255) / 256, a.B), dim3(256), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -783,15 +782,26 @@ __device__ void finish_unit(const FinishArgs& a, const int b) {
   const int tid = threadIdx.x, nt = blockDim.x;
   __shared__ float sv[512];
   __shared__ int si[512];
-  // per-thread contiguous range, strict '>' so the lowest index wins ties
+  // per-thread contiguous range, strict '>' so the lowest index wins ties;
+  // the range is read 8 entries at a time, all 8 requested before any is used
   const int per = (a.n_part + nt - 1) / nt;
   const int t0 = tid * per, t1 = min(a.n_part, t0 + per);
+  const float* pv = a.amax_v + (long)b * a.ld_amax;
+  const int* pi = a.amax_i + (long)b * a.ld_amax;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int t = t0; t < t1; ++t) {
-    const float v = a.amax_v[(long)b * a.ld_amax + t];
-    const int i = a.amax_i[(long)b * a.ld_amax + t];
-    if (v > bv || bi == 0x7fffffff) { bv = v; bi = i; }
+  for (int t = t0; t < t1; t += 8) {
+    float vv[8];
+    int ii[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = t + j < t1;
+      vv[j] = ok ? pv[t + j] : 0.f;
+      ii[j] = ok ? pi[t + j] : 0x7fffffff;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (ii[j] != 0x7fffffff && (vv[j] > bv || bi == 0x7fffffff)) { bv = vv[j]; bi = ii[j]; }
   }
   sv[tid] = bv;
   si[tid] = bi;
