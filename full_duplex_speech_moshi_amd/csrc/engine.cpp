@@ -24,6 +24,7 @@ namespace {
 
 constexpr size_t ALIGN = 256;
 constexpr int DEP_WINDOW = 16;  // depformer per-frame keys (one per codebook step)
+static_assert(DEP_WINDOW <= DEP_MAX_KEYS, "depformer attention holds at most DEP_MAX_KEYS keys");
 
 struct Layout {
   // byte offsets into the arena
@@ -70,7 +71,7 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.dkv_layer_elems = 2 * dH * DEP_WINDOW * dhd;
   L.dkv_slot_elems = dm.dep_layers * L.dkv_layer_elems;
   L.dkv_v_off = dH * DEP_WINDOW * dhd;
-  L.max_chunks = (W + ATT_CHUNK - 1) / ATT_CHUNK;
+  L.max_chunks = (W + ATT_CHUNK - 1) / ATT_CHUNK;  // <= ATT_MAX_SPLITS for W <= PP_MAX_WINDOW
   L.n_amax = (int)((std::max(Vt, A) + ROWS - 1) / ROWS);
   L.ring = take((size_t)B * L.ring_slot_elems * 2);
   L.dkv = take((size_t)B * L.dkv_slot_elems * 2);
@@ -387,6 +388,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       bf16_t* dkv_l = h->at<bf16_t>(L.dkv) + (long)l * L.dkv_layer_elems;
       GemmArgs g{};
       g.W = w.dep_wqkv + (long)l * 3 * dd * dd;
+      g.w_keep = 1;  // re-read at every codebook step
       g.X = h->at<bf16_t>(L.ya);
       g.x_lo = (long)B * dd;
       g.M = 3 * dd;
@@ -411,27 +413,28 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       g.split_part = split_part;
       launch_gemm(EPI_QKV, g, s);
 
-      AttnArgs at{};
-      at.q = h->at<float>(L.dq);
-      at.ldq = dd;
-      at.kv = dkv_l;
-      at.kv_slot_stride = L.dkv_slot_elems;
-      at.kv_v_off = L.dkv_v_off;
-      at.n_heads = dH;
-      at.head_dim = dhd;
-      at.window = DEP_WINDOW;
-      at.B = B;
-      at.ti = nullptr;
-      at.pos_const = k;
-      at.part = nullptr;
-      at.max_chunks = 1;
-      at.o = h->at<bf16_t>(L.dout);
-      at.ldo = dd;
-      at.o_lo = (long)B * dd;
-      launch_attention(at, s);
+      // attention over steps 0..k of this frame: inside the out-projection at
+      // small batch, else its own launch (same arithmetic either way)
+      DepAttnArgs da{};
+      da.q = h->at<float>(L.dq);
+      da.ldq = dd;
+      da.kv = dkv_l;
+      da.slot_stride = L.dkv_slot_elems;
+      da.v_off = L.dkv_v_off;
+      da.n_heads = dH;
+      da.head_dim = dhd;
+      da.window = DEP_WINDOW;
+      da.n_keys = k + 1;
+      da.B = B;
+      da.o = h->at<bf16_t>(L.dout);
+      da.ldo = dd;
+      da.o_lo = (long)B * dd;
+      const bool fuse_att = B <= DEP_FUSE_B && dd <= DEP_FUSE_D;
+      if (!fuse_att) launch_dep_attention(da, s);
 
       GemmArgs go{};
       go.W = w.dep_wo + (long)l * dd * dd;
+      go.w_keep = 1;  // re-read at every codebook step
       go.X = h->at<bf16_t>(L.dout);
       go.x_lo = (long)B * dd;
       go.M = dd;
@@ -445,10 +448,13 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       go.alpha_next = w.dep_mlp_norm + (long)l * dd;
       go.part_out = h->at<float>(L.dpart);
       go.split_part = split_part;
+      go.fuse_att = fuse_att;
+      go.att = da;
       launch_gemm(EPI_RESID, go, s);
 
       GemmArgs gu{};
       gu.W = w.dep_w_in + (long)l * 2 * dF * dd;
+      gu.w_keep = 1;  // re-read at every codebook step
       gu.X = h->at<bf16_t>(L.ya);
       gu.x_lo = (long)B * dd;
       gu.M = dF;
@@ -468,6 +474,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
 
       GemmArgs gd{};
       gd.W = w.dep_w_out + (long)l * dd * dF;
+      gd.w_keep = 1;  // re-read at every codebook step
       gd.X = h->at<bf16_t>(L.dm);
       gd.x_lo = (long)B * dF;
       gd.M = dd;
@@ -531,7 +538,9 @@ extern "C" {
 
 int pp_arena_bytes(const pp_dims* dims, int B, int window, size_t* out_bytes) {
   std::string why;
-  if (!out_bytes || !dims_ok(dims, &why) || B < 1 || B > PP_MAX_BATCH || window < 1) return PP_EINVAL;
+  if (!out_bytes || !dims_ok(dims, &why) || B < 1 || B > PP_MAX_BATCH || window < 1 ||
+      window > PP_MAX_WINDOW)
+    return PP_EINVAL;
   *out_bytes = make_layout(*dims, B, window).total;
   return PP_OK;
 }
@@ -543,7 +552,7 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
   *out = nullptr;
   if (!dims_ok(dims, &why)) { g_create_error = why; return PP_EINVAL; }
   if (B < 1 || B > PP_MAX_BATCH) { g_create_error = "B out of [1, 32]"; return PP_EINVAL; }
-  if (window < 1) { g_create_error = "window < 1"; return PP_EINVAL; }
+  if (window < 1 || window > PP_MAX_WINDOW) { g_create_error = "window outside 1..PP_MAX_WINDOW"; return PP_EINVAL; }
   if (!w || !arena) { g_create_error = "weights or arena is NULL"; return PP_EINVAL; }
   const void* const* wp = reinterpret_cast<const void* const*>(w);
   for (size_t i = 0; i < sizeof(pp_weights) / sizeof(void*); ++i)

@@ -27,12 +27,28 @@ enum {
 constexpr int ROWS = 16;           // MFMA row tile
 constexpr int GEMM_WAVES = 8;      // waves per GEMM workgroup (split K)
 constexpr int ATT_CHUNK = 256;     // keys per split of the flash-decoding pass
+constexpr int ATT_MAX_SPLITS = 16; // splits per (slot, head): windows up to 4096 keys
 constexpr int MAX_COLS = 32;       // slots per launch (two 16-wide column tiles)
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GATED = 2, EPI_LOGITS = 3, EPI_STORE = 4 };
 
+// Depformer attention of one codebook step: slot b, head h attends to the
+// keys of steps 0..n_keys-1 of its own frame (n_keys <= DEP_MAX_KEYS).
+constexpr int DEP_MAX_KEYS = 16;
+constexpr int DEP_FUSE_B = 2;     // up to this batch the attention runs inside the out-projection
+constexpr int DEP_FUSE_D = 1024;  // ... when the depformer width is at most this
+struct DepAttnArgs {
+  const float* q; int ldq;          // [B][ldq] fp32, head h at q + h*head_dim
+  const bf16_t* kv;                 // per-frame cache of this layer: slot b at kv + b*slot_stride, V at +v_off
+  long slot_stride, v_off;
+  int n_heads, head_dim, window, n_keys, B;
+  bf16_t* o; int ldo; long o_lo;    // [B][ldo] output as a bf16 hi/lo pair (standalone kernel)
+};
+void launch_dep_attention(const DepAttnArgs& a, hipStream_t s);
+
 struct GemmArgs {
   const bf16_t* W;      // [M][K] in the tile layout (gated: gate rows, up rows from row gate_off)
+  int w_keep;           // W is re-read within the tick: load it cacheable (else non-temporal)
   const bf16_t* X;      // activations as a bf16 pair: hi plane [B][ldx], lo plane at X + x_lo
   long x_lo;
   int M, K, ldx, B;
@@ -63,6 +79,10 @@ struct GemmArgs {
   float* amax_v; int* amax_i; int ld_amax;  // logits: per-workgroup (max, argmax) [B][ld_amax]
   // large-batch path (B > 16): per-tile partial sums
   float* split_part;    // [weight tile][8 ranges][512] fp32
+  // EPI_RESID with B <= DEP_FUSE_B: the input X is the depformer attention
+  // output, computed by every workgroup from `att` instead of read from X
+  int fuse_att;
+  DepAttnArgs att;
 };
 
 // Large-batch path: weight tiles (gate and up tiles counted apart) and

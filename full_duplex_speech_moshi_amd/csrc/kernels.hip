@@ -37,16 +37,15 @@ __device__ __forceinline__ void store_split(bf16_t* p, long lo, float v) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-// Weight stream: read once per tick and far larger than the caches, so the
-// loads carry the non-temporal hint.
-#ifndef PP_WEIGHT_TEMPORAL
+// Weight loads.  Weights read once per tick (temporal stack, heads, input
+// projections: far larger than the caches) carry the non-temporal hint; the
+// depformer layers, re-read at every codebook step, are loaded normally so
+// that they stay in the last-level cache.
+template <bool NTL>
 __device__ __forceinline__ u32x4 ldw16(const bf16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  if constexpr (NTL) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return ld16(p);
 }
-#else
-__device__ __forceinline__ u32x4 ldw16(const bf16_t* p) { return ld16(p); }
-#endif
-
 __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -269,10 +268,84 @@ __device__ void gemm_epilogue(const GemmArgs& a, const int tile, EpiSmem<(EPI ==
   }
 }
 
+// ---------------------------------------------------------------------------
+// Depformer attention (one codebook step, keys of steps 0..n-1 of this
+// frame, scale 1/sqrt(head_dim), softmax with max subtraction, keys in step
+// order).  One wave takes 128/head_dim consecutive (slot, head) pairs,
+// head_dim/2 lanes per pair and two features per lane; the dot products are
+// summed over the pair's lanes with a fixed butterfly.  The same function
+// serves the standalone kernel and the out-projection that computes its own
+// input, so a slot's result does not depend on which of them ran.
+// ---------------------------------------------------------------------------
+
+struct DepAttnOut {
+  float o0, o1;  // features feat, feat + 1 of pair `pair`
+  int pair, feat;
+  bool ok;
+};
+
+__device__ DepAttnOut dep_attend(const DepAttnArgs& d, const int pair0) {
+  const int lane = threadIdx.x & 63;
+  const int lp = d.head_dim >> 1;  // lanes per pair
+  const int pair = pair0 + lane / lp, f = 2 * (lane % lp);
+  const bool ok = pair < d.B * d.n_heads;
+  const int b = ok ? pair / d.n_heads : 0, h = ok ? pair - b * d.n_heads : 0;
+  const float* qp = d.q + (long)b * d.ldq + h * d.head_dim + f;
+  const float q0 = ok ? qp[0] : 0.f, q1 = ok ? qp[1] : 0.f;
+  const bf16_t* kb = d.kv + (long)b * d.slot_stride + (long)h * d.window * d.head_dim + f;
+  const uint32_t* kw = reinterpret_cast<const uint32_t*>(kb);
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(kb + d.v_off);
+  const int n = d.n_keys, row = d.head_dim >> 1;  // u32 words per key row
+  uint32_t kk[DEP_MAX_KEYS], vv[DEP_MAX_KEYS];
+#pragma unroll
+  for (int p = 0; p < DEP_MAX_KEYS; ++p) {
+    kk[p] = (ok && p < n) ? kw[p * row] : 0u;
+    vv[p] = (ok && p < n) ? vw[p * row] : 0u;
+  }
+  const float scale = 1.0f / sqrtf((float)d.head_dim);
+  float sc[DEP_MAX_KEYS];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < DEP_MAX_KEYS; ++p) {
+    if (p < n) {
+      float dot = __builtin_fmaf(q1, bf_hi(kk[p]), q0 * bf_lo(kk[p]));
+      for (int off = lp >> 1; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+      sc[p] = dot * scale;
+      mx = fmaxf(mx, sc[p]);
+    }
+  }
+  float l = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int p = 0; p < DEP_MAX_KEYS; ++p) {
+    if (p < n) {
+      const float e = expf(sc[p] - mx);
+      l += e;
+      o0 = __builtin_fmaf(e, bf_lo(vv[p]), o0);
+      o1 = __builtin_fmaf(e, bf_hi(vv[p]), o1);
+    }
+  }
+  return DepAttnOut{o0 / l, o1 / l, pair, f, ok};
+}
+
+__global__ __launch_bounds__(256) void dep_attn_kernel(DepAttnArgs d) {
+  const int ppw = 128 / d.head_dim;
+  const DepAttnOut r = dep_attend(d, (blockIdx.x * 4 + (threadIdx.x >> 6)) * ppw);
+  if (!r.ok) return;
+  const int b = r.pair / d.n_heads, h = r.pair - b * d.n_heads;
+  bf16_t* o = d.o + (long)b * d.ldo + h * d.head_dim + r.feat;
+  store_split(o, d.o_lo, r.o0);
+  store_split(o + 1, d.o_lo, r.o1);
+}
+
+void launch_dep_attention(const DepAttnArgs& d, hipStream_t s) {
+  const int waves = (d.B * d.n_heads * d.head_dim + 127) / 128;  // 128/head_dim pairs per wave
+  hipLaunchKernelGGL(dep_attn_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, d);
+}
+
 // One 16-row tile (gate+up pair for EPI_GATED) of the GEMM, computed by a
 // 512-thread workgroup; `smem` holds a GemmSmem<RT, NT>.
-template <int EPI, int NT>
-__device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
+template <int EPI, int NT, bool NTL, bool ATT = false>
+__device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t* olds = nullptr) {
   constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
   constexpr int U = (RT * NT > 1) ? 4 : 8;
   GemmSmem<RT, NT>& sm = *reinterpret_cast<GemmSmem<RT, NT>*>(smem);
@@ -311,6 +384,27 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
   if (EPI != EPI_RESID) rms_preload<NT>(a, rp);
 
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+  // ATT: the input is the depformer attention output, computed here into LDS
+  // ([plane][slot][DEP_FUSE_D]) while the first weight batch is in flight.
+  u32x4 pf[RT][U];
+  constexpr long OPL = (long)DEP_FUSE_B * DEP_FUSE_D;  // LDS plane stride
+  if constexpr (ATT) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) pf[rt][u] = (s0 + u < s1) ? ldw16<NTL>(arow[rt] + (long)(s0 + u) * 512) : zero;
+    const int ppw = 128 / a.att.head_dim;
+    for (int pp = wave * ppw; pp < a.B * a.att.n_heads; pp += GEMM_WAVES * ppw) {
+      const DepAttnOut r = dep_attend(a.att, pp);
+      if (r.ok) {
+        const int b = r.pair / a.att.n_heads, h = r.pair - b * a.att.n_heads;
+        bf16_t* o = olds + (long)b * DEP_FUSE_D + h * a.att.head_dim + r.feat;
+        store_split(o, OPL, r.o0);
+        store_split(o + 1, OPL, r.o1);
+      }
+    }
+    __syncthreads();
+  }
   for (int s = s0; s < s1; s += U) {
     u32x4 av[RT][U], bh[NT][U], bl[NT][U];
 #pragma unroll
@@ -318,11 +412,18 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
       const bool ok = (s + u) < s1;
       const int k = (s + u) * 32;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) av[rt][u] = ok ? ldw16(arow[rt] + (long)(s + u) * 512) : zero;
+      for (int rt = 0; rt < RT; ++rt)
+        av[rt][u] = (ATT && s == s0) ? pf[rt][u] : ok ? ldw16<NTL>(arow[rt] + (long)(s + u) * 512) : zero;
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        bh[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + k) : zero;
-        bl[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + a.x_lo + k) : zero;
+        if constexpr (ATT) {
+          const bf16_t* xo = olds + (long)(ct * 16 + r16) * DEP_FUSE_D + g * 8 + k;
+          bh[ct][u] = (ok && b_ok[ct]) ? *reinterpret_cast<const u32x4*>(xo) : zero;
+          bl[ct][u] = (ok && b_ok[ct]) ? *reinterpret_cast<const u32x4*>(xo + OPL) : zero;
+        } else {
+          bh[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + k) : zero;
+          bl[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + a.x_lo + k) : zero;
+        }
       }
     }
 #pragma unroll
@@ -363,10 +464,18 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem) {
 
 constexpr size_t GEMM_SMEM_BYTES = sizeof(GemmSmem<2, 2>);
 
-template <int EPI, int NT>
+template <int EPI, int NT, bool NTL>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
-  gemm_unit<EPI, NT>(a, blockIdx.x, smem);
+  gemm_unit<EPI, NT, NTL>(a, blockIdx.x, smem);
+}
+
+// Depformer out-projection that computes its input, the attention output,
+// itself (B <= DEP_FUSE_B): saves the attention launch of every layer-step.
+__global__ __launch_bounds__(512) void gemm_att_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) bf16_t olds[2 * DEP_FUSE_B * DEP_FUSE_D];
+  gemm_unit<EPI_RESID, 1, false, true>(a, blockIdx.x, smem, olds);
 }
 
 // ---------------------------------------------------------------------------
@@ -422,7 +531,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
       u32x4 av[WIDE_U];
 #pragma unroll
       for (int u = 0; u < WIDE_U; ++u)
-        av[u] = (t_ok && sb + u < nsub) ? ldw16(w + (long)(c0 + sb + u) * 512) : zero;
+        av[u] = (t_ok && sb + u < nsub) ? ldw16<true>(w + (long)(c0 + sb + u) * 512) : zero;
 #pragma unroll
       for (int u = 0; u < WIDE_U; ++u) {
         if (sb + u < nsub) {
@@ -509,14 +618,20 @@ static bool use_wide(const GemmArgs& a) { return a.B > 16 && a.K >= 4096; }
 template <int EPI>
 static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
   const int tiles = (a.M + ROWS - 1) / ROWS;
+  if (EPI == EPI_RESID && a.fuse_att) {  // caller guarantees B <= DEP_FUSE_B, K <= DEP_FUSE_D
+    hipLaunchKernelGGL(gemm_att_kernel, dim3(tiles), dim3(512), 0, s, a);
+    return;
+  }
   if (use_wide(a)) {
     const long groups = (wide_tiles(EPI, a.M) + GEMM_WAVES - 1) / GEMM_WAVES;
     hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, a);
     hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, a);
   } else if (a.B > 16) {
-    hipLaunchKernelGGL((gemm_kernel<EPI, 2>), dim3(tiles), dim3(512), 0, s, a);
+    if (a.w_keep) hipLaunchKernelGGL((gemm_kernel<EPI, 2, false>), dim3(tiles), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<EPI, 2, true>), dim3(tiles), dim3(512), 0, s, a);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<EPI, 1>), dim3(tiles), dim3(512), 0, s, a);
+    if (a.w_keep) hipLaunchKernelGGL((gemm_kernel<EPI, 1, false>), dim3(tiles), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<EPI, 1, true>), dim3(tiles), dim3(512), 0, s, a);
   }
 }
 
@@ -595,8 +710,8 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
     vr[it] = zero;
     if (j < kn) {
       const long off = (long)((P.lo + k0 + j) % a.window) * DH;
-      kr[it] = ld16(kb + off);
-      vr[it] = ld16(vb + off);
+      kr[it] = ldw16<true>(kb + off);  // read once per tick: non-temporal
+      vr[it] = ldw16<true>(vb + off);
     }
   }
 
@@ -684,15 +799,28 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
   }
   __syncthreads();
   if (is_last && e < DH) {
+    // every split's (max, sum, output) requested before any is used
+    float mv[ATT_MAX_SPLITS], lv[ATT_MAX_SPLITS], ov[ATT_MAX_SPLITS];
+#pragma unroll
+    for (int cc = 0; cc < ATT_MAX_SPLITS; ++cc) {
+      const float* pp = base + cc * (DH + 2);
+      const bool ok = cc < P.nc;
+      mv[cc] = ok ? __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
+      lv[cc] = ok ? __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+      ov[cc] = ok ? __hip_atomic_load(pp + 2 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+    }
     float Mx = -INFINITY;
-    for (int cc = 0; cc < P.nc; ++cc)
-      Mx = fmaxf(Mx, __hip_atomic_load(base + cc * (DH + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int cc = 0; cc < ATT_MAX_SPLITS; ++cc)
+      if (cc < P.nc) Mx = fmaxf(Mx, mv[cc]);
     float Lx = 0.f, Ox = 0.f;
-    for (int cc = 0; cc < P.nc; ++cc) {
-      float* pp = base + cc * (DH + 2);
-      const float f = expf(__hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - Mx);
-      Lx += __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
-      Ox += __hip_atomic_load(pp + 2 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
+#pragma unroll
+    for (int cc = 0; cc < ATT_MAX_SPLITS; ++cc) {
+      if (cc < P.nc) {
+        const float f = expf(mv[cc] - Mx);
+        Lx += lv[cc] * f;
+        Ox += ov[cc] * f;
+      }
     }
     store_split(a.o + (long)b * a.ldo + h * DH + e, a.o_lo, Ox / Lx);
   }

@@ -55,6 +55,7 @@ extern "C" {
 #define PP_EDEVICE (-4)  /* a HIP call failed; handle poisoned */
 
 #define PP_MAX_BATCH     32    /* slots per handle */
+#define PP_MAX_WINDOW    4096  /* ring frames per slot (the decode pass combines at most 16 splits of 256 keys) */
 #define PP_MAX_QUEUE     4096  /* forced frames queued per slot */
 #define PP_COLUMN_ROWS   17    /* token column: text, 8 agent, 8 user */
 
@@ -135,7 +136,7 @@ int pp_pack_matrix(const uint16_t* src, int M, int K, uint16_t* dst, void* strea
 int pp_arena_bytes(const pp_dims* dims, int B, int window, size_t* out_bytes);
 
 /* Create a handle for B slots (1..PP_MAX_BATCH) and a ring of `window`
- * frames per slot.  arena: device buffer of at least pp_arena_bytes bytes,
+ * (1..PP_MAX_WINDOW) frames per slot.  arena: device buffer of at least pp_arena_bytes bytes,
  * 256-byte aligned.  stream: the hipStream_t every later call runs on (NULL =
  * the null stream).  Captures the tick graph.  All slots start reset.
  * PP_EINVAL (bad args), PP_ENOSPC (arena too small), PP_EDEVICE. */

@@ -51,7 +51,7 @@ def test_bad_dims_rejected(lib, field, value):
     assert lib.pp_arena_bytes(ctypes.byref(pp.make_dims(dm)), 1, 32, ctypes.byref(out)) == pp.PP_EINVAL
 
 
-@pytest.mark.parametrize("B,W", [(0, 32), (33, 32), (1, 0)])
+@pytest.mark.parametrize("B,W", [(0, 32), (33, 32), (1, 0), (1, 4097)])
 def test_bad_batch_or_window_rejected(lib, B, W):
     out = ctypes.c_size_t()
     assert lib.pp_arena_bytes(ctypes.byref(pp.make_dims(synth.TINY)), B, W, ctypes.byref(out)) == pp.PP_EINVAL
