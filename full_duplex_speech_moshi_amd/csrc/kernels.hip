@@ -284,35 +284,39 @@ struct DepAttnOut {
   bool ok;
 };
 
+template <int DH>
 __device__ DepAttnOut dep_attend(const DepAttnArgs& d, const int pair0) {
+  constexpr int LP = DH / 2;  // lanes per pair
   const int lane = threadIdx.x & 63;
-  const int lp = d.head_dim >> 1;  // lanes per pair
-  const int pair = pair0 + lane / lp, f = 2 * (lane % lp);
+  const int pair = pair0 + lane / LP, f = 2 * (lane % LP);
   const bool ok = pair < d.B * d.n_heads;
   const int b = ok ? pair / d.n_heads : 0, h = ok ? pair - b * d.n_heads : 0;
-  const float* qp = d.q + (long)b * d.ldq + h * d.head_dim + f;
+  const float* qp = d.q + (long)b * d.ldq + h * DH + f;
   const float q0 = ok ? qp[0] : 0.f, q1 = ok ? qp[1] : 0.f;
-  const bf16_t* kb = d.kv + (long)b * d.slot_stride + (long)h * d.window * d.head_dim + f;
+  const bf16_t* kb = d.kv + (long)b * d.slot_stride + (long)h * d.window * DH + f;
   const uint32_t* kw = reinterpret_cast<const uint32_t*>(kb);
   const uint32_t* vw = reinterpret_cast<const uint32_t*>(kb + d.v_off);
-  const int n = d.n_keys, row = d.head_dim >> 1;  // u32 words per key row
+  const int n = d.n_keys;
   uint32_t kk[DEP_MAX_KEYS], vv[DEP_MAX_KEYS];
 #pragma unroll
   for (int p = 0; p < DEP_MAX_KEYS; ++p) {
-    kk[p] = (ok && p < n) ? kw[p * row] : 0u;
-    vv[p] = (ok && p < n) ? vw[p * row] : 0u;
+    kk[p] = (ok && p < n) ? kw[p * LP] : 0u;
+    vv[p] = (ok && p < n) ? vw[p * LP] : 0u;
   }
-  const float scale = 1.0f / sqrtf((float)d.head_dim);
+  // all keys' partial dots first, then their butterflies side by side
   float sc[DEP_MAX_KEYS];
+#pragma unroll
+  for (int p = 0; p < DEP_MAX_KEYS; ++p) sc[p] = __builtin_fmaf(q1, bf_hi(kk[p]), q0 * bf_lo(kk[p]));
+#pragma unroll
+  for (int off = LP / 2; off >= 1; off >>= 1)
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_KEYS; ++p) sc[p] += __shfl_xor(sc[p], off);
+  const float scale = 1.0f / sqrtf((float)DH);
   float mx = -INFINITY;
 #pragma unroll
   for (int p = 0; p < DEP_MAX_KEYS; ++p) {
-    if (p < n) {
-      float dot = __builtin_fmaf(q1, bf_hi(kk[p]), q0 * bf_lo(kk[p]));
-      for (int off = lp >> 1; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
-      sc[p] = dot * scale;
-      mx = fmaxf(mx, sc[p]);
-    }
+    sc[p] *= scale;
+    if (p < n) mx = fmaxf(mx, sc[p]);
   }
   float l = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
@@ -327,19 +331,25 @@ __device__ DepAttnOut dep_attend(const DepAttnArgs& d, const int pair0) {
   return DepAttnOut{o0 / l, o1 / l, pair, f, ok};
 }
 
+template <int DH>
 __global__ __launch_bounds__(256) void dep_attn_kernel(DepAttnArgs d) {
-  const int ppw = 128 / d.head_dim;
-  const DepAttnOut r = dep_attend(d, (blockIdx.x * 4 + (threadIdx.x >> 6)) * ppw);
+  constexpr int PPW = 128 / DH;
+  const DepAttnOut r = dep_attend<DH>(d, (blockIdx.x * 4 + (threadIdx.x >> 6)) * PPW);
   if (!r.ok) return;
   const int b = r.pair / d.n_heads, h = r.pair - b * d.n_heads;
-  bf16_t* o = d.o + (long)b * d.ldo + h * d.head_dim + r.feat;
+  bf16_t* o = d.o + (long)b * d.ldo + h * DH + r.feat;
   store_split(o, d.o_lo, r.o0);
   store_split(o + 1, d.o_lo, r.o1);
 }
 
 void launch_dep_attention(const DepAttnArgs& d, hipStream_t s) {
   const int waves = (d.B * d.n_heads * d.head_dim + 127) / 128;  // 128/head_dim pairs per wave
-  hipLaunchKernelGGL(dep_attn_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, d);
+  const dim3 grid((waves + 3) / 4);
+  switch (d.head_dim) {
+    case 32: hipLaunchKernelGGL(dep_attn_kernel<32>, grid, dim3(256), 0, s, d); break;
+    case 64: hipLaunchKernelGGL(dep_attn_kernel<64>, grid, dim3(256), 0, s, d); break;
+    default: hipLaunchKernelGGL(dep_attn_kernel<128>, grid, dim3(256), 0, s, d); break;
+  }
 }
 
 // One 16-row tile (gate+up pair for EPI_GATED) of the GEMM, computed by a
@@ -395,7 +405,9 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t*
       for (int rt = 0; rt < RT; ++rt) pf[rt][u] = (s0 + u < s1) ? ldw16<NTL>(arow[rt] + (long)(s0 + u) * 512) : zero;
     const int ppw = 128 / a.att.head_dim;
     for (int pp = wave * ppw; pp < a.B * a.att.n_heads; pp += GEMM_WAVES * ppw) {
-      const DepAttnOut r = dep_attend(a.att, pp);
+      const DepAttnOut r = a.att.head_dim == 32   ? dep_attend<32>(a.att, pp)
+                           : a.att.head_dim == 64 ? dep_attend<64>(a.att, pp)
+                                                  : dep_attend<128>(a.att, pp);
       if (r.ok) {
         const int b = r.pair / a.att.n_heads, h = r.pair - b * a.att.n_heads;
         bf16_t* o = olds + (long)b * DEP_FUSE_D + h * a.att.head_dim + r.feat;
@@ -906,10 +918,32 @@ void launch_embed(const EmbedArgs& a, hipStream_t s) {
 // Slot b of the finisher, computed by the whole workgroup (up to 512
 // threads).  The argmax selection (largest value, then lowest index) does not
 // depend on the reduction tree, so the block size does not change results.
+// (value, index) pairs: larger value wins, then the lower index; index
+// 0x7fffffff marks an empty pair.
+__device__ __forceinline__ bool amax_better(float v2, int i2, float v, int i) {
+  return i2 != 0x7fffffff && (i == 0x7fffffff || v2 > v || (v2 == v && i2 < i));
+}
+
 __device__ void finish_unit(const FinishArgs& a, const int b) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  __shared__ float sv[512];
-  __shared__ int si[512];
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float sv[8];
+  __shared__ int si[8];
+  __shared__ int chosen_s;
+  const int nk = a.step + 1;
+  const bool next = nk < a.dep_q;
+  // Requests that do not depend on the choice go out first: the forced
+  // token, and this thread's first 16-feature group of u_{k+1} and alpha.
+  const int forced = (tid == 0 && a.step < 8) ? a.ti[b * TI_STRIDE + TI_FORCE + 1 + a.step] : -1;
+  const float* u = a.u + ((long)b * a.dep_q + nk) * a.dd;
+  float u0[16], al0[16];
+  const bool has0 = next && tid < a.dd / 16;
+  if (has0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      u0[i] = u[tid * 16 + i];
+      al0[i] = a.alpha[tid * 16 + i];
+    }
+  }
   // per-thread contiguous range, strict '>' so the lowest index wins ties;
   // the range is read 8 entries at a time, all 8 requested before any is used
   const int per = (a.n_part + nt - 1) / nt;
@@ -931,28 +965,25 @@ __device__ void finish_unit(const FinishArgs& a, const int b) {
     for (int j = 0; j < 8; ++j)
       if (ii[j] != 0x7fffffff && (vv[j] > bv || bi == 0x7fffffff)) { bv = vv[j]; bi = ii[j]; }
   }
-  sv[tid] = bv;
-  si[tid] = bi;
-  __syncthreads();
-  for (int w = nt / 2; w >= 1; w >>= 1) {
-    if (tid < w) {
-      const float v2 = sv[tid + w];
-      const int i2 = si[tid + w];
-      if (i2 != 0x7fffffff && (si[tid] == 0x7fffffff || v2 > sv[tid] || (v2 == sv[tid] && i2 < si[tid]))) {
-        sv[tid] = v2;
-        si[tid] = i2;
-      }
-    }
-    __syncthreads();
+  // wave butterfly, then the waves' winners in LDS (the winner does not
+  // depend on the reduction order)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float v2 = __shfl_xor(bv, off);
+    const int i2 = __shfl_xor(bi, off);
+    if (amax_better(v2, i2, bv, bi)) { bv = v2; bi = i2; }
   }
-  __shared__ int chosen_s;
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
   if (tid == 0) {
-    const int pred = si[0];
+    for (int w = 1; w < nt / 64; ++w)
+      if (amax_better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    const int pred = bi;
     int* to = a.to + b * TO_STRIDE;
-    const int* ti = a.ti + b * TI_STRIDE;
-    int forced = -1;
-    if (a.step < 8) forced = ti[TI_FORCE + 1 + a.step];  // step -1 -> text force
-    const int chosen = forced >= 0 ? forced : pred;
+    const int chosen = forced >= 0 ? forced : pred;  // step -1 -> text force
     if (a.step < 8) {
       to[TO_PRED + 1 + a.step] = pred;
       to[TO_CHOSEN + 1 + a.step] = chosen;
@@ -963,11 +994,9 @@ __device__ void finish_unit(const FinishArgs& a, const int b) {
     chosen_s = chosen;
   }
   __syncthreads();
-  const int nk = a.step + 1;
   const int tok = chosen_s;
-  const float* u = a.u + ((long)b * a.dep_q + nk) * a.dd;
   const bf16_t* e = a.table + (long)tok * a.dd;
-  for (int grp = tid; nk < a.dep_q && grp < a.dd / 16; grp += nt) {
+  for (int grp = tid; next && grp < a.dd / 16; grp += nt) {
     float f[16];
     unpack8(ld16(e + grp * 16), f);
     unpack8(ld16(e + grp * 16 + 8), f + 8);
@@ -975,14 +1004,15 @@ __device__ void finish_unit(const FinishArgs& a, const int b) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = grp * 16 + i;
-      const float v = u[m] + f[i];
+      const float um = grp == tid ? u0[i] : u[m];
+      const float am = grp == tid ? al0[i] : a.alpha[m];
+      const float v = um + f[i];
       a.y[(long)b * a.dd + m] = v;
-      store_split(a.ya + (long)b * a.dd + m, a.ya_lo, v * a.alpha[m]);
+      store_split(a.ya + (long)b * a.dd + m, a.ya_lo, v * am);
       ss += v * v;
     }
     a.part[(long)b * (a.dd / 16) + grp] = ss;
   }
-  __syncthreads();  // LDS is reused by the next unit
 }
 
 __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) { finish_unit(a, blockIdx.x); }
