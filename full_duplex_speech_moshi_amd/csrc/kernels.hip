@@ -482,6 +482,39 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
   gemm_unit<EPI, NT, NTL>(a, blockIdx.x, smem);
 }
 
+// The arguments seen by slots s0 .. s0+n-1 only: every per-slot pointer
+// advanced by s0 slots and B = n.  Lets the 16-column kernel serve slots
+// 16..31 of a larger batch (blockIdx.y = slot half) with each slot's
+// arithmetic unchanged.
+__device__ __forceinline__ GemmArgs slot_view(const GemmArgs& a, const int s0, const int n) {
+  GemmArgs v = a;
+  v.B = n;
+  v.X = a.X + (long)s0 * a.ldx;
+  if (a.part_in) v.part_in = a.part_in + (long)s0 * a.n_part;
+  if (a.q_out) v.q_out = a.q_out + (long)s0 * a.ldq;
+  if (a.kv) v.kv = a.kv + (long)s0 * a.kv_slot_stride;
+  if (a.ti) v.ti = a.ti + (long)s0 * TI_STRIDE;
+  if (a.x) v.x = a.x + (long)s0 * a.ldres;
+  if (a.xa_out) v.xa_out = a.xa_out + (long)s0 * a.ldres;
+  if (a.part_out) v.part_out = a.part_out + (long)s0 * (a.M / ROWS);
+  if (a.tap) v.tap = a.tap + (long)s0 * a.ldres;
+  if (a.m_out) v.m_out = a.m_out + (long)s0 * a.ldm;
+  if (a.f_out) v.f_out = a.f_out + (long)s0 * a.ldf;
+  if (a.amax_v) v.amax_v = a.amax_v + (long)s0 * a.ld_amax;
+  if (a.amax_i) v.amax_i = a.amax_i + (long)s0 * a.ld_amax;
+  return v;
+}
+
+// B in 17..32 with cache-resident weights: two 16-slot halves (blockIdx.y),
+// each the B <= 16 kernel; the weights are read twice, from the cache.
+template <int EPI, bool NTL>
+__global__ __launch_bounds__(512) void gemm_halves_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
+  const int s0 = blockIdx.y * 16;
+  const GemmArgs v = slot_view(a, s0, min(16, a.B - s0));
+  gemm_unit<EPI, 1, NTL>(v, blockIdx.x, smem);
+}
+
 // Depformer out-projection that computes its input, the attention output,
 // itself (B <= DEP_FUSE_B): saves the attention launch of every layer-step.
 __global__ __launch_bounds__(512) void gemm_att_kernel(GemmArgs a) {
@@ -639,7 +672,7 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, a);
     hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, a);
   } else if (a.B > 16) {
-    if (a.w_keep) hipLaunchKernelGGL((gemm_kernel<EPI, 2, false>), dim3(tiles), dim3(512), 0, s, a);
+    if (a.w_keep) hipLaunchKernelGGL((gemm_halves_kernel<EPI, false>), dim3(tiles, 2), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gemm_kernel<EPI, 2, true>), dim3(tiles), dim3(512), 0, s, a);
   } else {
     if (a.w_keep) hipLaunchKernelGGL((gemm_kernel<EPI, 1, false>), dim3(tiles), dim3(512), 0, s, a);
