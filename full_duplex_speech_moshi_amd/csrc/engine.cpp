@@ -29,7 +29,7 @@ static_assert(DEP_WINDOW <= DEP_MAX_KEYS, "depformer attention holds at most DEP
 struct Layout {
   // byte offsets into the arena
   size_t ring, dkv, x, xa, part, q, att_part, o, m, hidden, text_logits, amax_v, amax_i, u, y, ya, dpart, dq, dout,
-      dm, dep_logits, ti, to, inv_freq, split_part, att_cnt, total;
+      dm, dep_logits, ti, to, inv_freq, split_part, wide_rms, att_cnt, total;
   long wide_part_max;
   int max_chunks, n_amax;
   long ring_slot_elems, ring_layer_elems, ring_v_off;
@@ -104,6 +104,7 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.wide_part_max = 0;
   for (const auto& g : wide) L.wide_part_max = std::max(L.wide_part_max, wide_part_floats(g.epi, (int)g.M));
   L.split_part = B > 16 ? take((size_t)L.wide_part_max * 4) : take(0);
+  L.wide_rms = take(MAX_COLS * 4);
   L.att_cnt = take((size_t)B * H * 4);
   L.total = off;
   return L;
@@ -181,6 +182,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   int* to = h->at<int>(L.to);
   const double* inv_freq = h->at<double>(L.inv_freq);
   float* split_part = h->at<float>(L.split_part);
+  float* wide_rms = h->at<float>(L.wide_rms);
 
   EmbedArgs ea{};
   ea.ti = ti;
@@ -224,6 +226,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     g.ti = ti;
     g.inv_freq = inv_freq;
     g.split_part = split_part;
+    g.wide_rms = wide_rms;
     launch_gemm(EPI_QKV, g, s);
     if (keep_timed) h->timed[0].push_back([g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); });
     if (keep_timed && l == 0) {
@@ -268,6 +271,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     go.alpha_next = w.mlp_norm + (long)l * d;
     go.part_out = h->at<float>(L.part);
     go.split_part = split_part;
+    go.wide_rms = wide_rms;
     launch_gemm(EPI_RESID, go, s);
     if (keep_timed) h->timed[2].push_back([go](hipStream_t st) { launch_gemm(EPI_RESID, go, st); });
     if (keep_timed && l == 0) {
@@ -291,6 +295,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gu.ldm = F;
     gu.m_lo = (long)B * F;
     gu.split_part = split_part;
+    gu.wide_rms = wide_rms;
     launch_gemm(EPI_GATED, gu, s);
     if (keep_timed) h->timed[3].push_back([gu](hipStream_t st) { launch_gemm(EPI_GATED, gu, st); });
     if (keep_timed && l == 0) {
@@ -313,6 +318,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gd.part_out = h->at<float>(L.part);
     gd.tap = h->at<float>(L.hidden) + (long)(l + 1) * B * d;
     gd.split_part = split_part;
+    gd.wide_rms = wide_rms;
     launch_gemm(EPI_RESID, gd, s);
     if (keep_timed) h->timed[4].push_back([gd](hipStream_t st) { launch_gemm(EPI_RESID, gd, st); });
     if (keep_timed && l == 0) {
@@ -339,6 +345,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gt.amax_i = h->at<int>(L.amax_i);
   gt.ld_amax = L.n_amax;
   gt.split_part = split_part;
+  gt.wide_rms = wide_rms;
   launch_gemm(EPI_LOGITS, gt, s);
   if (keep_timed) {
     h->timed[5].push_back([gt](hipStream_t st) { launch_gemm(EPI_LOGITS, gt, st); });
@@ -361,6 +368,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gp.f_out = h->at<float>(L.u);
   gp.ldf = (long)Q * dd;
   gp.split_part = split_part;
+  gp.wide_rms = wide_rms;
   launch_gemm(EPI_STORE, gp, s);
 
   FinishArgs fa{};
@@ -411,6 +419,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       g.pos_const = k;
       g.inv_freq = nullptr;
       g.split_part = split_part;
+      g.wide_rms = wide_rms;
       launch_gemm(EPI_QKV, g, s);
 
       // attention over steps 0..k of this frame: inside the out-projection at
@@ -448,6 +457,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       go.alpha_next = w.dep_mlp_norm + (long)l * dd;
       go.part_out = h->at<float>(L.dpart);
       go.split_part = split_part;
+      go.wide_rms = wide_rms;
       go.fuse_att = fuse_att;
       go.att = da;
       launch_gemm(EPI_RESID, go, s);
@@ -470,6 +480,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       gu.ldm = dF;
       gu.m_lo = (long)B * dF;
       gu.split_part = split_part;
+      gu.wide_rms = wide_rms;
       launch_gemm(EPI_GATED, gu, s);
 
       GemmArgs gd{};
@@ -488,6 +499,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
       gd.alpha_next = (l + 1 < dm.dep_layers) ? w.dep_attn_norm + (long)(l + 1) * dd : w.dep_out_norm;
       gd.part_out = h->at<float>(L.dpart);
       gd.split_part = split_part;
+      gd.wide_rms = wide_rms;
       launch_gemm(EPI_RESID, gd, s);
     }
     GemmArgs gh{};
@@ -508,6 +520,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     gh.amax_i = h->at<int>(L.amax_i);
     gh.ld_amax = L.n_amax;
     gh.split_part = split_part;
+    gh.wide_rms = wide_rms;
     launch_gemm(EPI_LOGITS, gh, s);
 
     FinishArgs f = fa;

@@ -77,8 +77,10 @@ struct GemmArgs {
   long m_lo;
   float* f_out; long ldf;        // store / logits: [B][ldf] fp32
   float* amax_v; int* amax_i; int ld_amax;  // logits: per-workgroup (max, argmax) [B][ld_amax]
-  // large-batch path (B > 16): per-tile partial sums
+  // large-batch path (B > 16): per-tile partial sums, and the slots' inverse
+  // RMS (computed once per launch by the main kernel, read by the reduce)
   float* split_part;    // [weight tile][8 ranges][512] fp32
+  float* wide_rms;      // [MAX_COLS] fp32
   // EPI_RESID with B <= DEP_FUSE_B: the input X is the depformer attention
   // output, computed by every workgroup from `att` instead of read from X
   int fuse_att;

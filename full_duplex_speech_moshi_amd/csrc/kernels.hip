@@ -558,6 +558,17 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
   const bf16_t* w = a.W + (t_ok ? wt : 0) * ks * 512 + lane * 8;
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
 
+  // workgroup 0 also forms the slots' inverse RMS for the reduce kernel (the
+  // same functions and order as every other path)
+  if (a.wide_rms && blockIdx.x == 0) {
+    __shared__ float inv[NTC];
+    RmsPre<NT> rp;
+    rms_preload<NT>(a, rp);
+    rms_finish<NT>(a, rp, inv);
+    __syncthreads();
+    if (tid < NTC) a.wide_rms[tid] = inv[tid];
+  }
+
   f32x4 acc[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -616,8 +627,7 @@ __global__ __launch_bounds__(512) void gemm_wide_reduce(GemmArgs a) {
 #pragma unroll
     for (int jj = 0; jj < GEMM_WAVES; ++jj) v[rt][jj] = a.split_part[(tt * GEMM_WAVES + jj) * (NT * 256) + tid];
   }
-  RmsPre<NT> rp;
-  if (EPI != EPI_RESID) rms_preload<NT>(a, rp);
+  if (EPI != EPI_RESID && tid < NT * 16) e.inv_rms[tid] = a.wide_rms[tid];
   const EpiPre pre = epi_preload<EPI, NT>(a, tile);
   const int ct = tid >> 8, q = (tid >> 6) & 3, ln = tid & 63;
 #pragma unroll
@@ -627,7 +637,6 @@ __global__ __launch_bounds__(512) void gemm_wide_reduce(GemmArgs a) {
     for (int jj = 0; jj < GEMM_WAVES; ++jj) s += v[rt][jj];
     e.fin[rt][4 * (ln >> 4) + q][ct * 16 + (ln & 15)] = s;
   }
-  if (EPI != EPI_RESID) rms_finish<NT>(a, rp, e.inv_rms);
   __syncthreads();
   gemm_epilogue<EPI, NT>(a, tile, e, pre);
 }
@@ -669,8 +678,10 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
   }
   if (use_wide(a)) {
     const long groups = (wide_tiles(EPI, a.M) + GEMM_WAVES - 1) / GEMM_WAVES;
-    hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, a);
-    hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, a);
+    GemmArgs w = a;
+    if (EPI == EPI_RESID) w.wide_rms = nullptr;  // no normalised input
+    hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, w);
+    hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, w);
   } else if (a.B > 16) {
     if (a.w_keep) hipLaunchKernelGGL((gemm_halves_kernel<EPI, false>), dim3(tiles, 2), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gemm_kernel<EPI, 2, true>), dim3(tiles), dim3(512), 0, s, a);
