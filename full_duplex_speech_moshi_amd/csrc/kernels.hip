@@ -627,7 +627,15 @@ __global__ __launch_bounds__(512) void gemm_wide_reduce(GemmArgs a) {
 #pragma unroll
     for (int jj = 0; jj < GEMM_WAVES; ++jj) v[rt][jj] = a.split_part[(tt * GEMM_WAVES + jj) * (NT * 256) + tid];
   }
-  if (EPI != EPI_RESID && tid < NT * 16) e.inv_rms[tid] = a.wide_rms[tid];
+  // inverse RMS: from the main kernel, or formed here when no buffer is given
+  RmsPre<NT> rp;
+  if (EPI != EPI_RESID) {
+    if (a.wide_rms) {
+      if (tid < NT * 16) e.inv_rms[tid] = a.wide_rms[tid];
+    } else {
+      rms_preload<NT>(a, rp);
+    }
+  }
   const EpiPre pre = epi_preload<EPI, NT>(a, tile);
   const int ct = tid >> 8, q = (tid >> 6) & 3, ln = tid & 63;
 #pragma unroll
@@ -637,6 +645,7 @@ __global__ __launch_bounds__(512) void gemm_wide_reduce(GemmArgs a) {
     for (int jj = 0; jj < GEMM_WAVES; ++jj) s += v[rt][jj];
     e.fin[rt][4 * (ln >> 4) + q][ct * 16 + (ln & 15)] = s;
   }
+  if (EPI != EPI_RESID && !a.wide_rms) rms_finish<NT>(a, rp, e.inv_rms);
   __syncthreads();
   gemm_epilogue<EPI, NT>(a, tile, e, pre);
 }
