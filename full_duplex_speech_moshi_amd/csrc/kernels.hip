@@ -60,6 +60,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
+// Sum over the 64 lanes in a fixed order, the same value in every lane:
+// within each 16-lane row by DPP (swap neighbours, swap pairs, mirror within
+// half-rows, mirror within rows), then across rows by two exchanges.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -118,13 +134,17 @@ struct RmsPre {
 template <int NT>
 __device__ __forceinline__ void rms_preload(const GemmArgs& a, RmsPre<NT>& rp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // every lane loads (from a clamped, valid address) and then selects: no
+  // branch per load, so the loads stay in flight together
 #pragma unroll
   for (int k = 0; k < (NT * 16 + GEMM_WAVES - 1) / GEMM_WAVES; ++k) {
     const int c = wave + k * GEMM_WAVES;
 #pragma unroll
     for (int q = 0; q < RMS_PRE; ++q) {
       const int i = lane + 64 * q;
-      rp.v[k][q] = (c < a.B && i < a.n_part) ? a.part_in[(long)c * a.n_part + i] : 0.f;
+      const bool ok = c < a.B && i < a.n_part;
+      const float v = a.part_in[ok ? (long)c * a.n_part + i : 0];
+      rp.v[k][q] = ok ? v : 0.f;
     }
   }
 }
@@ -135,14 +155,13 @@ __device__ __forceinline__ void rms_finish(const GemmArgs& a, const RmsPre<NT>& 
 #pragma unroll
   for (int k = 0; k < (NT * 16 + GEMM_WAVES - 1) / GEMM_WAVES; ++k) {
     const int c = wave + k * GEMM_WAVES;
+    if (c >= a.B) continue;  // wave-uniform: no slot here
     float s = 0.f;
-    if (c < a.B) {
 #pragma unroll
-      for (int q = 0; q < RMS_PRE; ++q)
-        if (lane + 64 * q < a.n_part) s += rp.v[k][q];
-      for (int i = lane + 64 * RMS_PRE; i < a.n_part; i += 64) s += a.part_in[(long)c * a.n_part + i];
-    }
-    s = wave_sum(s);
+    for (int q = 0; q < RMS_PRE; ++q)
+      if (lane + 64 * q < a.n_part) s += rp.v[k][q];
+    for (int i = lane + 64 * RMS_PRE; i < a.n_part; i += 64) s += a.part_in[(long)c * a.n_part + i];
+    s = wave_sum_rows(s);
     if (lane == 0 && c < NT * 16) inv_rms[c] = 1.0f / sqrtf(s / (float)a.feat + a.eps);
   }
 }
@@ -160,10 +179,11 @@ __device__ __forceinline__ EpiPre epi_preload(const GemmArgs& a, const int tile)
   const int tid = threadIdx.x, row0 = tile * ROWS;
   if constexpr (EPI == EPI_RESID) {
     const int r = tid & 15, c = tid >> 4;
-    if (c < a.B && c < NT * 16) {
-      p.x0 = a.x[(long)c * a.ldres + row0 + r];
-      p.x1 = a.alpha_next[row0 + r];
-    }
+    const bool ok = c < a.B && c < NT * 16;
+    const float x0 = a.x[(long)(ok ? c : 0) * a.ldres + row0 + r];  // valid address either way
+    const float x1 = a.alpha_next[row0 + r];
+    p.x0 = ok ? x0 : 0.f;
+    p.x1 = ok ? x1 : 0.f;
   }
   return p;
 }
@@ -361,7 +381,7 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t*
   GemmSmem<RT, NT>& sm = *reinterpret_cast<GemmSmem<RT, NT>*>(smem);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int ksteps = a.K >> 5;
   const int s0 = (ksteps * wave) / GEMM_WAVES;
@@ -438,6 +458,7 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t*
         }
       }
     }
+
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
