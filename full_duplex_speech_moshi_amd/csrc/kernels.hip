@@ -55,32 +55,35 @@ __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
 }
 
 // Fixed butterfly over the 64 lanes of a wave (same order on every call).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-// Sum over the 64 lanes in a fixed order, the same value in every lane:
-// within each 16-lane row by DPP (swap neighbours, swap pairs, mirror within
-// half-rows, mirror within rows), then across rows by two exchanges.
+// Reductions over aligned groups of G lanes (G a power of two up to 64), the
+// same result in every lane of the group and a fixed order: within 16-lane
+// rows by DPP (swap neighbours, swap pairs, mirror within half-rows, mirror
+// within rows), then across rows by exchanges.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float wave_sum_rows(float v) {
-  v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
-  v += dpp_f<0x141>(v);  // row_half_mirror
-  v += dpp_f<0x140>(v);  // row_mirror
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if (G >= 2) v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
+  if (G >= 4) v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
+  if (G >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if (G >= 16) v += dpp_f<0x140>(v); // row_mirror
+  if (G >= 32) v += __shfl_xor(v, 16);
+  if (G >= 64) v += __shfl_xor(v, 32);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  if (G >= 2) v = fmaxf(v, dpp_f<0xb1>(v));
+  if (G >= 4) v = fmaxf(v, dpp_f<0x4e>(v));
+  if (G >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+  if (G >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+  if (G >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (G >= 64) v = fmaxf(v, __shfl_xor(v, 32));
   return v;
 }
+__device__ __forceinline__ float wave_sum_rows(float v) { return group_sum<64>(v); }
 
 // ---------------------------------------------------------------------------
 // Skinny GEMM family  Y[b][m] = sum_k W[m][k] * X[b][k],  b < B <= 32.
@@ -328,9 +331,7 @@ __device__ DepAttnOut dep_attend(const DepAttnArgs& d, const int pair0) {
 #pragma unroll
   for (int p = 0; p < DEP_MAX_KEYS; ++p) sc[p] = __builtin_fmaf(q1, bf_hi(kk[p]), q0 * bf_lo(kk[p]));
 #pragma unroll
-  for (int off = LP / 2; off >= 1; off >>= 1)
-#pragma unroll
-    for (int p = 0; p < DEP_MAX_KEYS; ++p) sc[p] += __shfl_xor(sc[p], off);
+  for (int p = 0; p < DEP_MAX_KEYS; ++p) sc[p] = group_sum<LP>(sc[p]);
   const float scale = 1.0f / sqrtf((float)DH);
   float mx = -INFINITY;
 #pragma unroll
@@ -811,12 +812,11 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) dot += qv[i] * kf[i];
-#pragma unroll
-    for (int off = LPK / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+    dot = group_sum<LPK>(dot);
     s[it] = (j < kn) ? dot * scale : -INFINITY;
     mloc = fmaxf(mloc, s[it]);
   }
-  mloc = wave_max(mloc);
+  mloc = group_max<64>(mloc);
 
   float lsum = 0.f;
   float o[8];
@@ -838,7 +838,7 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
   for (int off = LPK; off < 64; off <<= 1)
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] += __shfl_xor(o[i], off);
-  lsum = wave_sum(lsum);
+  lsum = group_sum<64>(lsum);
 
   __shared__ float sm_m[4], sm_l[4], sm_o[4][DH];
   __shared__ int is_last;
