@@ -28,7 +28,7 @@ static_assert(DEP_WINDOW <= DEP_MAX_KEYS, "depformer attention holds at most DEP
 
 struct Layout {
   // byte offsets into the arena
-  size_t ring, dkv, x, xa, part, q, att_part, o, m, hidden, text_logits, amax_v, amax_i, u, y, ya, dpart, dq, dout,
+  size_t ring, dkv, x, xa, part, q, att_part, o, m, hidden, text_logits, amax_v, amax_i, tamax_v, tamax_i, u, y, ya, dpart, dq, dout,
       dm, dep_logits, ti, to, inv_freq, split_part, wide_rms, att_cnt, total;
   long wide_part_max;
   int max_chunks, n_amax;
@@ -84,8 +84,12 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.m = take(2 * B * F * 2);
   L.hidden = take((size_t)(dm.n_layers + 1) * B * d * 4);
   L.text_logits = take(B * Vt * 4);
+  // argmax partials: depformer heads, and the text head's own (the text head
+  // of tick t+1 runs while the user-stream codebooks of tick t still do)
   L.amax_v = take((size_t)B * L.n_amax * 4);
   L.amax_i = take((size_t)B * L.n_amax * 4);
+  L.tamax_v = take((size_t)B * L.n_amax * 4);
+  L.tamax_i = take((size_t)B * L.n_amax * 4);
   L.u = take(B * Q * dd * 4);
   L.y = take(B * dd * 4);
   L.ya = take(2 * B * dd * 2);
@@ -127,9 +131,15 @@ struct pp_handle {
   pp_weights w;
   Layout lay;
   char* arena = nullptr;
-  hipStream_t stream = nullptr, cap = nullptr;
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
+  // The tick is three graphs: PH_TEMPORAL (embedding, temporal stack, text
+  // head) and PH_AGENT (input projections, text finisher, codebooks 0..n_q-1)
+  // on the caller's stream, then PH_USER (the user-stream codebooks n_q..)
+  // on `side`, where it overlaps the next tick's PH_TEMPORAL.  PH_AGENT
+  // waits for the previous PH_USER (event `user_done`).
+  hipStream_t stream = nullptr, cap = nullptr, side = nullptr;
+  hipGraph_t graph[3] = {nullptr, nullptr, nullptr};
+  hipGraphExec_t exec[3] = {nullptr, nullptr, nullptr};
+  hipEvent_t agent_done = nullptr, user_done = nullptr;
   int32_t* ti_host = nullptr;
   int32_t* to_host = nullptr;
   std::vector<Slot> slots;
@@ -170,8 +180,10 @@ void reset_slot(const pp_dims& dm, Slot& s) {
   s.ticked = false;
 }
 
-// Record every kernel of one tick on stream s.
-void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
+enum Phase { PH_TEMPORAL = 0, PH_AGENT = 1, PH_USER = 2 };
+
+// Record the kernels of one phase of the tick on stream s.
+void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
   const pp_dims& dm = h->dm;
   const Layout& L = h->lay;
   const int B = h->B, W = h->W;
@@ -184,6 +196,7 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   float* split_part = h->at<float>(L.split_part);
   float* wide_rms = h->at<float>(L.wide_rms);
 
+  if (phase == PH_TEMPORAL) {
   EmbedArgs ea{};
   ea.ti = ti;
   ea.B = B;
@@ -341,8 +354,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gt.eps = dm.norm_eps;
   gt.f_out = h->at<float>(L.text_logits);
   gt.ldf = Vt;
-  gt.amax_v = h->at<float>(L.amax_v);
-  gt.amax_i = h->at<int>(L.amax_i);
+  gt.amax_v = h->at<float>(L.tamax_v);
+  gt.amax_i = h->at<int>(L.tamax_i);
   gt.ld_amax = L.n_amax;
   gt.split_part = split_part;
   gt.wide_rms = wide_rms;
@@ -352,6 +365,30 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     h->timed_bytes[5] = 2.0 * Vt * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * Vt);
   }
 
+  }  // PH_TEMPORAL
+
+  // the text finisher (greedy text token -> depformer step 0 input); the
+  // codebook finishers below copy it
+  FinishArgs fa{};
+  fa.B = B;
+  fa.step = -1;
+  fa.n_part = (Vt + ROWS - 1) / ROWS;
+  fa.amax_v = h->at<float>(L.tamax_v);
+  fa.amax_i = h->at<int>(L.tamax_i);
+  fa.ld_amax = L.n_amax;
+  fa.ti = ti;
+  fa.to = to;
+  fa.dep_q = Q;
+  fa.dd = dd;
+  fa.u = h->at<float>(L.u);
+  fa.table = w.dep_emb_text;
+  fa.alpha = w.dep_attn_norm;
+  fa.y = h->at<float>(L.y);
+  fa.ya = h->at<bf16_t>(L.ya);
+  fa.ya_lo = (long)B * dd;
+  fa.part = h->at<float>(L.dpart);
+
+  if (phase == PH_AGENT) {
   // all 16 depformer input projections of z at once
   GemmArgs gp{};
   gp.W = w.dep_in_proj;
@@ -371,27 +408,13 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
   gp.wide_rms = wide_rms;
   launch_gemm(EPI_STORE, gp, s);
 
-  FinishArgs fa{};
-  fa.B = B;
-  fa.step = -1;
-  fa.n_part = (Vt + ROWS - 1) / ROWS;
-  fa.amax_v = h->at<float>(L.amax_v);
-  fa.amax_i = h->at<int>(L.amax_i);
-  fa.ld_amax = L.n_amax;
-  fa.ti = ti;
-  fa.to = to;
-  fa.dep_q = Q;
-  fa.dd = dd;
-  fa.u = h->at<float>(L.u);
-  fa.table = w.dep_emb_text;
-  fa.alpha = w.dep_attn_norm;
-  fa.y = h->at<float>(L.y);
-  fa.ya = h->at<bf16_t>(L.ya);
-  fa.ya_lo = (long)B * dd;
-  fa.part = h->at<float>(L.dpart);
   launch_finish(fa, s);
+  }  // PH_AGENT: input projections and text finisher
 
-  for (int k = 0; k < Q; ++k) {
+  // codebook steps: the agent stream in PH_AGENT, the user stream in PH_USER
+  if (phase == PH_TEMPORAL) return;
+  const int k0 = phase == PH_AGENT ? 0 : dm.n_q, k1 = phase == PH_AGENT ? dm.n_q : Q;
+  for (int k = k0; k < k1; ++k) {
     for (int l = 0; l < dm.dep_layers; ++l) {
       bf16_t* dkv_l = h->at<bf16_t>(L.dkv) + (long)l * L.dkv_layer_elems;
       GemmArgs g{};
@@ -526,6 +549,8 @@ void record_tick(pp_handle* h, hipStream_t s, bool keep_timed) {
     FinishArgs f = fa;
     f.step = k;
     f.n_part = (A + ROWS - 1) / ROWS;
+    f.amax_v = h->at<float>(L.amax_v);
+    f.amax_i = h->at<int>(L.amax_i);
     f.table = (k + 1 < Q) ? w.dep_emb_audio + (long)k * (A + 1) * dd : nullptr;
     launch_finish(f, s);
   }
@@ -543,6 +568,19 @@ void build_tick_input(pp_handle* h, const int32_t* user_codes, const std::array<
     for (int i = 0; i < 8; ++i) t[TI_COL + 9 + i] = f ? (*f)[9 + i] : (user_codes ? user_codes[b * 8 + i] : 0);
     for (int i = 0; i < 9; ++i) t[TI_FORCE + i] = f ? (*f)[i] : -1;
   }
+}
+
+// Launch one tick: PH_TEMPORAL, then (after the previous tick's user-stream
+// codebooks) PH_AGENT on the handle's stream, then PH_USER on the side stream.
+hipError_t launch_tick(pp_handle* h) {
+  hipError_t e;
+  if ((e = hipGraphLaunch(h->exec[PH_TEMPORAL], h->stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(h->stream, h->user_done, 0)) != hipSuccess) return e;
+  if ((e = hipGraphLaunch(h->exec[PH_AGENT], h->stream)) != hipSuccess) return e;
+  if ((e = hipEventRecord(h->agent_done, h->stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(h->side, h->agent_done, 0)) != hipSuccess) return e;
+  if ((e = hipGraphLaunch(h->exec[PH_USER], h->side)) != hipSuccess) return e;
+  return hipEventRecord(h->user_done, h->side);
 }
 
 }  // namespace
@@ -616,13 +654,21 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
     return bail("hipMemsetAsync", e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
   if ((e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
-  if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess)
-    return bail("hipStreamBeginCapture", e);
-  record_tick(h, h->cap, true);
-  if ((e = hipStreamEndCapture(h->cap, &h->graph)) != hipSuccess) return bail("hipStreamEndCapture", e);
-  if ((e = hipGetLastError()) != hipSuccess) return bail("kernel launch during capture", e);
-  if ((e = hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0)) != hipSuccess)
-    return bail("hipGraphInstantiate", e);
+  if ((e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
+  if ((e = hipEventCreateWithFlags(&h->agent_done, hipEventDisableTiming)) != hipSuccess)
+    return bail("hipEventCreate", e);
+  if ((e = hipEventCreateWithFlags(&h->user_done, hipEventDisableTiming)) != hipSuccess)
+    return bail("hipEventCreate", e);
+  if ((e = hipEventRecord(h->user_done, h->side)) != hipSuccess) return bail("hipEventRecord", e);
+  for (int ph = 0; ph < 3; ++ph) {
+    if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess)
+      return bail("hipStreamBeginCapture", e);
+    record_tick(h, h->cap, static_cast<Phase>(ph), ph == PH_TEMPORAL);
+    if ((e = hipStreamEndCapture(h->cap, &h->graph[ph])) != hipSuccess) return bail("hipStreamEndCapture", e);
+    if ((e = hipGetLastError()) != hipSuccess) return bail("kernel launch during capture", e);
+    if ((e = hipGraphInstantiate(&h->exec[ph], h->graph[ph], nullptr, nullptr, 0)) != hipSuccess)
+      return bail("hipGraphInstantiate", e);
+  }
   *out = h;
   return PP_OK;
 }
@@ -671,9 +717,12 @@ int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
   build_tick_input(h, user_codes, frames.data());
   HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.ti), h->ti_host, h->B * TI_STRIDE * 4, hipMemcpyHostToDevice,
                                 h->stream));
-  HIP_OR_FAIL(h, hipGraphLaunch(h->exec, h->stream));
-  HIP_OR_FAIL(h, hipMemcpyAsync(h->to_host, h->at<int>(h->lay.to), h->B * TO_STRIDE * 4, hipMemcpyDeviceToHost,
-                                h->stream));
+  HIP_OR_FAIL(h, launch_tick(h));
+  // the agent outputs only (the user-stream codebooks may still be writing theirs)
+  HIP_OR_FAIL(h, hipMemcpy2DAsync(h->to_host + TO_PRED, TO_STRIDE * 4, h->at<int>(h->lay.to) + TO_PRED, TO_STRIDE * 4,
+                                  9 * 4, h->B, hipMemcpyDeviceToHost, h->stream));
+  HIP_OR_FAIL(h, hipMemcpy2DAsync(h->to_host + TO_CHOSEN, TO_STRIDE * 4, h->at<int>(h->lay.to) + TO_CHOSEN,
+                                  TO_STRIDE * 4, 9 * 4, h->B, hipMemcpyDeviceToHost, h->stream));
   HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
   for (int b = 0; b < h->B; ++b) {
     Slot& s = h->slots[b];
@@ -728,6 +777,8 @@ int pp_ring_fill(pp_handle* h, int slot, int n, const uint16_t* k, const uint16_
 int pp_taps(const pp_handle* h, pp_taps_t* out) {
   if (!h || !out) return PP_EINVAL;
   if (h->poisoned) return PP_EDEVICE;
+  // the tick's user-stream codebooks write the depformer logits and predictions
+  if (hipEventSynchronize(h->user_done) != hipSuccess) return PP_EDEVICE;
   out->hidden = h->at<float>(h->lay.hidden);
   out->text_logits = h->at<float>(h->lay.text_logits);
   out->dep_logits = h->at<float>(h->lay.dep_logits);
@@ -749,6 +800,7 @@ int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* by
     }
   }
   if (bytes) *bytes = by;
+  HIP_OR_FAIL(h, hipEventSynchronize(h->user_done));
   build_tick_input(h, nullptr, nullptr);
   HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.ti), h->ti_host, h->B * TI_STRIDE * 4, hipMemcpyHostToDevice,
                                 h->stream));
@@ -783,9 +835,13 @@ int pp_time_graph(pp_handle* h, int iters, float* avg_ms) {
   hipEvent_t e0, e1;
   HIP_OR_FAIL(h, hipEventCreate(&e0));
   HIP_OR_FAIL(h, hipEventCreate(&e1));
-  HIP_OR_FAIL(h, hipGraphLaunch(h->exec, h->stream));
+  // steady state of back-to-back ticks; the last tick's user-stream codebooks
+  // are included (the timer ends after them)
+  HIP_OR_FAIL(h, launch_tick(h));
+  HIP_OR_FAIL(h, hipStreamWaitEvent(h->stream, h->user_done, 0));
   HIP_OR_FAIL(h, hipEventRecord(e0, h->stream));
-  for (int i = 0; i < iters; ++i) HIP_OR_FAIL(h, hipGraphLaunch(h->exec, h->stream));
+  for (int i = 0; i < iters; ++i) HIP_OR_FAIL(h, launch_tick(h));
+  HIP_OR_FAIL(h, hipStreamWaitEvent(h->stream, h->user_done, 0));
   HIP_OR_FAIL(h, hipEventRecord(e1, h->stream));
   HIP_OR_FAIL(h, hipEventSynchronize(e1));
   float ms = 0;
@@ -809,8 +865,15 @@ int pp_pack_matrix(const uint16_t* src, int M, int K, uint16_t* dst, void* strea
 
 void pp_destroy(pp_handle* h) {
   if (!h) return;
-  if (h->exec) (void)hipGraphExecDestroy(h->exec);
-  if (h->graph) (void)hipGraphDestroy(h->graph);
+  if (h->side) (void)hipStreamSynchronize(h->side);
+  (void)hipStreamSynchronize(h->stream);
+  for (int ph = 0; ph < 3; ++ph) {
+    if (h->exec[ph]) (void)hipGraphExecDestroy(h->exec[ph]);
+    if (h->graph[ph]) (void)hipGraphDestroy(h->graph[ph]);
+  }
+  if (h->agent_done) (void)hipEventDestroy(h->agent_done);
+  if (h->user_done) (void)hipEventDestroy(h->user_done);
+  if (h->side) (void)hipStreamDestroy(h->side);
   if (h->cap) (void)hipStreamDestroy(h->cap);
   if (h->ti_host) (void)hipHostFree(h->ti_host);
   if (h->to_host) (void)hipHostFree(h->to_host);

@@ -28,8 +28,9 @@
  *   - The caller allocates and owns every device buffer (weights, arena) and
  *     the stream; the library keeps raw pointers, so the buffers must stay
  *     alive until pp_destroy.  The library allocates no device memory; it
- *     allocates small pinned host staging buffers and one internal stream
- *     used only to capture the tick graph.
+ *     allocates small pinned host staging buffers, one internal stream used
+ *     to capture the tick's graphs, and one internal stream (default
+ *     priority) that runs the user-stream half of the depformer (below).
  *   - Host arrays passed in are copied before the call returns.
  *   - A handle is single-threaded and bound to the stream given to pp_create.
  *   - Return codes: PP_OK, or a negative PP_E* code.  On every error except
@@ -107,8 +108,8 @@ typedef struct pp_weights {
   const uint16_t* dep_heads;     /* 16 x [A][dep_d] */
 } pp_weights;
 
-/* Device views into the arena, valid after each pp_step (overwritten by the
- * next one).  Strides are dense. */
+/* Device views into the arena, valid after each pp_taps call (overwritten by
+ * the next pp_step).  Strides are dense. */
 typedef struct pp_taps_t {
   const float*   hidden;       /* [L+1][B][d]   embedding sum, then the residual stream after each layer */
   const float*   text_logits;  /* [B][Vt] */
@@ -160,7 +161,14 @@ int pp_prefill_forced(pp_handle* h, int slot, const int32_t* frames, int n);
  * [B][9] receives each slot's greedy predictions [text, agent 0..7] -- the
  * model's own predictions even on forced ticks.  Synchronous: returns after
  * the tokens are on the host.  A slot whose forced queue is empty at this
- * tick becomes free-running.  Every slot computes every tick. */
+ * tick becomes free-running.  Every slot computes every tick.
+ *
+ * Pipelining: the depformer's user-stream codebooks (steps 8..15, which feed
+ * only the taps, never the next column) run on the library's internal stream
+ * after the agent codebooks, and may still be running when pp_step returns.
+ * They overlap the next tick's embedding and temporal stack; the next tick's
+ * depformer waits for them, and so do pp_taps, pp_time_kernel and
+ * pp_destroy.  The work and its results are those of the plain sequence. */
 int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens);
 
 /* Recycle `slot`: position 0, column back to the initial tokens
@@ -175,7 +183,8 @@ int pp_slot_reset(pp_handle* h, int slot);
  * its last reset (else PP_EBUSY).  n in [0, window] (else PP_EINVAL). */
 int pp_ring_fill(pp_handle* h, int slot, int n, const uint16_t* k, const uint16_t* v);
 
-/* Device views of the last tick's intermediate results (see pp_taps_t). */
+/* Device views of the last tick's intermediate results (see pp_taps_t).
+ * Waits for the tick's user-stream codebooks first. */
 int pp_taps(const pp_handle* h, pp_taps_t* out);
 
 /* Measurement hook: launch one kernel of the tick graph outside the graph,
@@ -190,12 +199,14 @@ int pp_taps(const pp_handle* h, pp_taps_t* out);
  * that the next tick recomputes before use, so slot state is not disturbed. */
 int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* bytes);
 
-/* Time `iters` back-to-back tick-graph launches on the handle's stream with
- * HIP events (no host copies); *avg_ms = mean device time per tick.  The
+/* Time `iters` back-to-back ticks (the three graphs of each, pipelined as in
+ * pp_step) with HIP events (no host copies); *avg_ms = mean device time per
+ * tick, the last tick's user-stream codebooks included.  The
  * launches recompute the tick for the current tick inputs without advancing
  * any slot, so they leave slot state (positions, columns, queues) as is. */
 int pp_time_graph(pp_handle* h, int iters, float* avg_ms);
 
+/* Waits for the handle's device work, then frees its host resources. */
 void pp_destroy(pp_handle* h);
 
 /* Message of the last error on h (or of the last failed pp_create when h is
