@@ -32,10 +32,11 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(algorithmic_bytes):
     """HBM bytes per launch of the dominant kernel from profiles/traffic.json
     (rocprofv3 FETCH_SIZE / WRITE_SIZE runs, calibrated on the copy probe),
-    or None when the kernels changed since the counters were taken."""
+    or None when the kernels changed since the counters were taken or the
+    kernel timed here is another shape than the one measured."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         t = json.load(open(path))
@@ -43,7 +44,54 @@ def measured_traffic():
         return None
     if t.get("kernels_hip_sha256_16") != kernel_source_hash():
         return None
+    if abs(t.get("algorithmic_bytes_per_launch", 0) - algorithmic_bytes) > 1e-3 * algorithmic_bytes:
+        return None
     return t.get("bytes_per_launch")
+
+
+DOMINANT_KERNEL = "gemm_kernel<2, 1, true>"  # temporal gate/up, B <= 16, weights read once per tick
+DOMINANT_WGS = 704                             # its workgroups at the 7B shape (one per gate/up row-tile pair)
+
+
+def summarize_traffic(run_dir):
+    """Write profiles/traffic.json from two rocprofv3 counter runs of
+    `bench.py --mode traffic` kept under run_dir: pmc_fetch/ (FETCH_SIZE) and
+    pmc_write/ (WRITE_SIZE), each with its *_counter_collection.csv, and
+    traffic_mode.json (the JSON line that mode printed).  The counters are
+    scaled by what they read for the copy probe (COPY_PROBE_BYTES read and
+    written); the dominant kernel's dispatches are averaged."""
+    import csv
+    import glob
+    meta = json.load(open(os.path.join(run_dir, "traffic_mode.json")))
+
+    def counter(sub, name):
+        path = glob.glob(os.path.join(run_dir, sub, "*counter_collection.csv"))[0]
+        copy, kern = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != name:
+                continue
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                copy.append(v)
+            elif DOMINANT_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == DOMINANT_WGS * int(r["Workgroup_Size"]):
+                kern.append(v)
+        return max(copy), sum(kern) / len(kern), len(kern)
+
+    f_copy, f_kern, n = counter("pmc_fetch", "FETCH_SIZE")
+    w_copy, w_kern, _ = counter("pmc_write", "WRITE_SIZE")
+    kib = meta["copy_probe_bytes"] / 1024
+    f_scale, w_scale = kib / f_copy, kib / w_copy
+    out = {
+        "kernel": f"{DOMINANT_KERNEL} temporal gate/up, 7B, B=1 ({DOMINANT_WGS} workgroups)",
+        "kernels_hip_sha256_16": kernel_source_hash(),
+        "bytes_per_launch": round(1024 * (f_kern * f_scale + w_kern * w_scale)),
+        "fetch_kib_raw": f_kern, "write_kib_raw": w_kern, "dispatches": n,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "copy_probe_bytes": meta["copy_probe_bytes"],
+        "algorithmic_bytes_per_launch": meta["algorithmic_bytes_per_launch"],
+    }
+    json.dump(out, open(os.path.join(ROOT, "profiles", "traffic.json"), "w"), indent=1)
+    print(json.dumps(out))
 
 
 def log(msg):
@@ -131,7 +179,12 @@ def main():
     ap.add_argument("--mode", default="bench", choices=["bench", "traffic"],
                     help="traffic: one tick, then the dominant kernel once per layer outside the graph and the "
                          "copy probe, nothing else (for rocprofv3 --pmc runs)")
+    ap.add_argument("--summarize-traffic", metavar="RUN_DIR", default=None,
+                    help="no GPU: write profiles/traffic.json from the counter runs of --mode traffic under RUN_DIR")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (sessions shard across GPUs "
               "with no exchange; run one process per GPU)", file=sys.stderr)
@@ -258,7 +311,7 @@ def main():
         "tick_bytes_p50": float(np.median(tick_bytes)),
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel<EPI_GATED> (temporal gate/up, layer 0)",
                      "achieved": dom["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": dom["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic()},
+                     "frac": dom["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic(dom["bytes"])},
         "kernels_us": {k: round(v["ms"] * 1e3, 2) for k, v in kern.items()},
         "kernels_gbs": {k: round(v["gbs"], 1) for k, v in kern.items()},
     }

@@ -388,28 +388,34 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
   fa.ya_lo = (long)B * dd;
   fa.part = h->at<float>(L.dpart);
 
-  if (phase == PH_AGENT) {
-  // all 16 depformer input projections of z at once
-  GemmArgs gp{};
-  gp.W = w.dep_in_proj;
-  gp.X = h->at<bf16_t>(L.xa);
-  gp.x_lo = (long)B * d;
-  gp.M = Q * dd;
-  gp.K = d;
-  gp.ldx = d;
-  gp.B = B;
-  gp.part_in = h->at<float>(L.part);
-  gp.n_part = d / 16;
-  gp.feat = d;
-  gp.eps = dm.norm_eps;
-  gp.f_out = h->at<float>(L.u);
-  gp.ldf = (long)Q * dd;
-  gp.split_part = split_part;
-  gp.wide_rms = wide_rms;
-  launch_gemm(EPI_STORE, gp, s);
+  // depformer input projections u_k = P_k z for codebooks [c0, c1), one GEMM
+  auto in_proj = [&](int c0, int c1) {
+    GemmArgs gp{};
+    gp.W = w.dep_in_proj + (long)c0 * packed_elems(dd, d);
+    gp.X = h->at<bf16_t>(L.xa);
+    gp.x_lo = (long)B * d;
+    gp.M = (c1 - c0) * dd;
+    gp.K = d;
+    gp.ldx = d;
+    gp.B = B;
+    gp.part_in = h->at<float>(L.part);
+    gp.n_part = d / 16;
+    gp.feat = d;
+    gp.eps = dm.norm_eps;
+    gp.f_out = h->at<float>(L.u) + (long)c0 * dd;
+    gp.ldf = (long)Q * dd;
+    gp.split_part = split_part;
+    gp.wide_rms = wide_rms;
+    launch_gemm(EPI_STORE, gp, s);
+  };
 
-  launch_finish(fa, s);
-  }  // PH_AGENT: input projections and text finisher
+  // All 16 projections run here: z (the normalised final hidden state) is
+  // overwritten by the next tick's temporal stack, which may run alongside
+  // this tick's user-stream codebooks.
+  if (phase == PH_AGENT) {
+    in_proj(0, Q);
+    launch_finish(fa, s);
+  }
 
   // codebook steps: the agent stream in PH_AGENT, the user stream in PH_USER
   if (phase == PH_TEMPORAL) return;
