@@ -164,3 +164,36 @@ def test_full_isolation_large_batch_path_bit_exact(full):
             np.testing.assert_array_equal(tp["text_logits"][0], taps[t]["text_logits"][b])
             np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
         e1.close()
+
+
+@pytest.mark.timeout(900)
+def test_full_isolation_b32_bit_exact(full):
+    """B = 32, the batch the large-batch benchmarks run (large-batch GEMM path,
+    depformer slot halves, standalone depformer attention): slots 0, 7 and 31
+    with occupancies 0, 300 and 700 equal B = 1 handles bit for bit."""
+    _say("case: 7B isolation, B=32 vs B=1, occupancy 0/300/700")
+    B = 32
+    occ = {7: 300, 31: 700}
+    fills = {b: synth.ring_fill(DM, 40 + b, n) for b, n in occ.items()}
+    codes = [synth.user_codes(700 + b, 2) for b in range(B)]
+    eb = _engine(full, B)
+    for b, f in fills.items():
+        eb.ring_fill(b, *f)
+    toks, taps = [], []
+    for t in range(2):
+        toks.append(eb.step(np.stack([codes[b][t] for b in range(B)])))
+        taps.append(eb.taps())
+    eb.close()
+    for b in (0, 7, 31):
+        e1 = _engine(full, 1)
+        if b in fills:
+            e1.ring_fill(0, *fills[b])
+        for t in range(2):
+            tk = e1.step(codes[b][t:t + 1])
+            tp = e1.taps()
+            np.testing.assert_array_equal(tk[0], toks[t][b])
+            np.testing.assert_array_equal(tp["hidden"][:, 0], taps[t]["hidden"][:, b])
+            np.testing.assert_array_equal(tp["text_logits"][0], taps[t]["text_logits"][b])
+            np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
+            np.testing.assert_array_equal(tp["user_pred"][0], taps[t]["user_pred"][b])
+        e1.close()

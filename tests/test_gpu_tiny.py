@@ -153,6 +153,35 @@ def test_replay_is_deterministic(tiny_weights, dev):
     b.close()
 
 
+def test_pipelined_ticks_match_tick_by_tick(tiny_weights, dev):
+    """Ticks issued back to back (the depformer's user-stream codebooks of one
+    tick still running beside the next tick's temporal stack) give the same
+    bits as ticks whose taps are read, and so waited for, one by one; a slot
+    reset and a session open in between included."""
+    _say("case: pipelined ticks vs tick-by-tick, B=3, 12 ticks")
+    B, n = 3, 12
+    codes = [synth.user_codes(300 + b, n) for b in range(B)]
+    frames = synth.session_open(4, text_card=DM.text_card, n_voice=2, n_persona=2)
+    a, b = engine(tiny_weights, dev, B), engine(tiny_weights, dev, B)
+    a.prefill_forced(2, frames)
+    b.prefill_forced(2, frames)
+    taps_b = None
+    for t in range(n):
+        if t == 6:
+            a.slot_reset(1)
+            b.slot_reset(1)
+        c = np.stack([codes[s][t] for s in range(B)])
+        ta = a.step(c)                 # no taps in between: overlapped
+        tb = b.step(c)
+        taps_b = b.taps()              # waits for this tick's user codebooks
+        np.testing.assert_array_equal(ta, tb)
+    taps_a = a.taps()
+    for k in ("hidden", "text_logits", "dep_logits", "user_pred", "chosen"):
+        np.testing.assert_array_equal(taps_a[k], taps_b[k])
+    a.close()
+    b.close()
+
+
 def test_ring_fill_then_teacher_forced_parity(tiny_weights, dev):
     """Ring pre-filled with 20 frames of N(0,1) bf16 keys/values; 15 ticks
     from position 20 slide the 32-frame window."""
