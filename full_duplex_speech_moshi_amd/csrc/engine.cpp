@@ -29,7 +29,7 @@ static_assert(DEP_WINDOW <= DEP_MAX_KEYS, "depformer attention holds at most DEP
 struct Layout {
   // byte offsets into the arena
   size_t ring, dkv, x, xa, part, q, att_part, o, m, hidden, text_logits, amax_v, amax_i, tamax_v, tamax_i, u, y, ya, dpart, dq, dout,
-      dm, dep_logits, ti, to, inv_freq, split_part, wide_rms, att_cnt, total;
+      dm, dep_logits, ti, to, inv_freq, split_part, wide_rms, rope, att_cnt, total;
   long wide_part_max;
   int max_chunks, n_amax;
   long ring_slot_elems, ring_layer_elems, ring_v_off;
@@ -109,6 +109,7 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   for (const auto& g : wide) L.wide_part_max = std::max(L.wide_part_max, wide_part_floats(g.epi, (int)g.M));
   L.split_part = B > 16 ? take((size_t)L.wide_part_max * 4) : take(0);
   L.wide_rms = take(MAX_COLS * 4);
+  L.rope = take((size_t)B * hd * 4);
   L.att_cnt = take((size_t)B * H * 4);
   L.total = off;
   return L;
@@ -211,6 +212,9 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
   ea.xa_lo = (long)B * d;
   ea.part = h->at<float>(L.part);
   ea.tap = h->at<float>(L.hidden);
+  ea.inv_freq = inv_freq;
+  ea.head_dim = hd;
+  ea.rope = h->at<float>(L.rope);
   launch_embed(ea, s);
 
   for (int l = 0; l < dm.n_layers; ++l) {
@@ -238,6 +242,7 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
     g.window = W;
     g.ti = ti;
     g.inv_freq = inv_freq;
+    g.rope = h->at<float>(L.rope);
     g.split_part = split_part;
     g.wide_rms = wide_rms;
     launch_gemm(EPI_QKV, g, s);

@@ -64,6 +64,7 @@ struct GemmArgs {
   const int* ti;        // tick input (positions) or null
   int pos_const;        // position when ti == null
   const double* inv_freq; // [head_dim/2] or null (no rotation)
+  const float* rope;      // [B][head_dim]: (cos, sin) of each frequency at the slot's position, or null
   // EPI_RESID
   float* x;             // [B][ldres] residual stream (read-modify-write)
   int ldres;
@@ -115,6 +116,7 @@ void launch_attention(const AttnArgs& a, hipStream_t s);
 
 struct EmbedArgs {
   const int* ti; int B, d;
+  const double* inv_freq; int head_dim; float* rope;  // RoPE table of the tick (see GemmArgs::rope)
   const bf16_t* emb_text; const bf16_t* emb_audio; int text_rows, audio_rows;
   const float* alpha;   // first attention-norm alpha
   float* x; bf16_t* xa; long xa_lo; float* part; float* tap;

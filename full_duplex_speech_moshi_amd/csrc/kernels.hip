@@ -173,13 +173,28 @@ __device__ __forceinline__ void rms_finish(const GemmArgs& a, const RmsPre<NT>& 
 // the old residual value and the next norm's alpha of item (row tid%16, slot
 // tid/16).
 struct EpiPre {
-  float x0, x1;
+  float x0, x1;  // EPI_RESID: old residual value, next norm's alpha
+  float cs, sn;  // EPI_QKV: rotation of the item's frequency at the slot's position
+  int pos;       // EPI_QKV: the slot's position
 };
 
 template <int EPI, int NT>
 __device__ __forceinline__ EpiPre epi_preload(const GemmArgs& a, const int tile) {
-  EpiPre p{0.f, 0.f};
+  EpiPre p{0.f, 0.f, 1.f, 0.f, 0};
   const int tid = threadIdx.x, row0 = tile * ROWS;
+  if constexpr (EPI == EPI_QKV) {
+    // item idx == tid of the epilogue: pair pr of rows, slot c
+    const int pr = tid & 7, c = tid >> 3;
+    const int cc = (c < a.B && c < NT * 16) ? c : 0;  // a valid slot for the loads
+    p.pos = a.ti ? a.ti[cc * TI_STRIDE + TI_POS] : a.pos_const;
+    const int d = a.n_heads * a.head_dim;
+    const int r = row0 + 2 * pr;
+    const int rr = r % d, dd = rr % a.head_dim;  // even: the pair's first feature
+    if (a.rope && r < 2 * d) {
+      p.cs = a.rope[(long)cc * a.head_dim + dd];
+      p.sn = a.rope[(long)cc * a.head_dim + dd + 1];
+    }
+  }
   if constexpr (EPI == EPI_RESID) {
     const int r = tid & 15, c = tid >> 4;
     const bool ok = c < a.B && c < NT * 16;
@@ -210,10 +225,15 @@ __device__ void gemm_epilogue(const GemmArgs& a, const int tile, EpiSmem<(EPI ==
       const int which = r / d;  // 0 q, 1 k, 2 v
       const int rr = r - which * d;
       const int h = rr / a.head_dim, dd = rr - h * a.head_dim;
-      const int pos = a.ti ? a.ti[c * TI_STRIDE + TI_POS] : a.pos_const;
+      // workgroup: item idx == tid, pre holds its position and rotation
+      const int pos = pre.pos;
       if (which < 2 && a.inv_freq) {
-        const double th = (double)pos * a.inv_freq[dd >> 1];
-        const float cs = (float)cos(th), sn = (float)sin(th);
+        float cs = pre.cs, sn = pre.sn;
+        if (!a.rope) {
+          const double th = (double)pos * a.inv_freq[dd >> 1];
+          cs = (float)cos(th);
+          sn = (float)sin(th);
+        }
         const float r0 = y0 * cs - y1 * sn;
         const float r1 = y0 * sn + y1 * cs;
         y0 = r0;
@@ -944,6 +964,16 @@ void launch_attention(const AttnArgs& a, hipStream_t s) {
 // costs one memory round trip.  Rows are summed in row order r = 0..16.
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   const int b = blockIdx.y;
+  // the tick's RoPE table for this slot: angle pos * base^(-2i/head_dim) in
+  // fp64, cos and sin rounded to fp32 (every layer's QKV epilogue reads it)
+  if (a.rope && blockIdx.x == 0) {
+    const int pos = a.ti[b * TI_STRIDE + TI_POS];
+    for (int i = threadIdx.x; i < a.head_dim / 2; i += blockDim.x) {
+      const double th = (double)pos * a.inv_freq[i];
+      a.rope[(long)b * a.head_dim + 2 * i] = (float)cos(th);
+      a.rope[(long)b * a.head_dim + 2 * i + 1] = (float)sin(th);
+    }
+  }
   const int g8 = blockIdx.x * blockDim.x + threadIdx.x;  // 8-feature group
   if (g8 >= a.d / 8) return;                              // d % 16 == 0: pairs stay whole
   const int* t = a.ti + b * TI_STRIDE + TI_COL;
