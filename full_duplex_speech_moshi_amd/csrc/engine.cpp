@@ -198,179 +198,179 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
   float* wide_rms = h->at<float>(L.wide_rms);
 
   if (phase == PH_TEMPORAL) {
-  EmbedArgs ea{};
-  ea.ti = ti;
-  ea.B = B;
-  ea.d = d;
-  ea.emb_text = w.emb_text;
-  ea.emb_audio = w.emb_audio;
-  ea.text_rows = Vt + 1;
-  ea.audio_rows = A + 1;
-  ea.alpha = w.attn_norm;
-  ea.x = h->at<float>(L.x);
-  ea.xa = h->at<bf16_t>(L.xa);
-  ea.xa_lo = (long)B * d;
-  ea.part = h->at<float>(L.part);
-  ea.tap = h->at<float>(L.hidden);
-  ea.inv_freq = inv_freq;
-  ea.head_dim = hd;
-  ea.rope = h->at<float>(L.rope);
-  launch_embed(ea, s);
+    EmbedArgs ea{};
+    ea.ti = ti;
+    ea.B = B;
+    ea.d = d;
+    ea.emb_text = w.emb_text;
+    ea.emb_audio = w.emb_audio;
+    ea.text_rows = Vt + 1;
+    ea.audio_rows = A + 1;
+    ea.alpha = w.attn_norm;
+    ea.x = h->at<float>(L.x);
+    ea.xa = h->at<bf16_t>(L.xa);
+    ea.xa_lo = (long)B * d;
+    ea.part = h->at<float>(L.part);
+    ea.tap = h->at<float>(L.hidden);
+    ea.inv_freq = inv_freq;
+    ea.head_dim = hd;
+    ea.rope = h->at<float>(L.rope);
+    launch_embed(ea, s);
 
-  for (int l = 0; l < dm.n_layers; ++l) {
-    bf16_t* ring_l = h->at<bf16_t>(L.ring) + (long)l * L.ring_layer_elems;
-    // fused QKV + rotation + ring write
-    GemmArgs g{};
-    g.W = w.wqkv + (long)l * 3 * d * d;
-    g.X = h->at<bf16_t>(L.xa);
-    g.x_lo = (long)B * d;
-    g.M = 3 * d;
-    g.K = d;
-    g.ldx = d;
-    g.B = B;
-    g.part_in = h->at<float>(L.part);
-    g.n_part = d / 16;
-    g.feat = d;
-    g.eps = dm.norm_eps;
-    g.q_out = h->at<float>(L.q);
-    g.ldq = d;
-    g.kv = ring_l;
-    g.kv_slot_stride = L.ring_slot_elems;
-    g.kv_v_off = L.ring_v_off;
-    g.n_heads = H;
-    g.head_dim = hd;
-    g.window = W;
-    g.ti = ti;
-    g.inv_freq = inv_freq;
-    g.rope = h->at<float>(L.rope);
-    g.split_part = split_part;
-    g.wide_rms = wide_rms;
-    launch_gemm(EPI_QKV, g, s);
-    if (keep_timed) h->timed[0].push_back([g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); });
-    if (keep_timed && l == 0) {
-      h->timed_bytes[0] = 2.0 * 3 * d * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * d + 4.0 * d);
+    for (int l = 0; l < dm.n_layers; ++l) {
+      bf16_t* ring_l = h->at<bf16_t>(L.ring) + (long)l * L.ring_layer_elems;
+      // fused QKV + rotation + ring write
+      GemmArgs g{};
+      g.W = w.wqkv + (long)l * 3 * d * d;
+      g.X = h->at<bf16_t>(L.xa);
+      g.x_lo = (long)B * d;
+      g.M = 3 * d;
+      g.K = d;
+      g.ldx = d;
+      g.B = B;
+      g.part_in = h->at<float>(L.part);
+      g.n_part = d / 16;
+      g.feat = d;
+      g.eps = dm.norm_eps;
+      g.q_out = h->at<float>(L.q);
+      g.ldq = d;
+      g.kv = ring_l;
+      g.kv_slot_stride = L.ring_slot_elems;
+      g.kv_v_off = L.ring_v_off;
+      g.n_heads = H;
+      g.head_dim = hd;
+      g.window = W;
+      g.ti = ti;
+      g.inv_freq = inv_freq;
+      g.rope = h->at<float>(L.rope);
+      g.split_part = split_part;
+      g.wide_rms = wide_rms;
+      launch_gemm(EPI_QKV, g, s);
+      if (keep_timed) h->timed[0].push_back([g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); });
+      if (keep_timed && l == 0) {
+        h->timed_bytes[0] = 2.0 * 3 * d * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * d + 4.0 * d);
+      }
+
+      AttnArgs at{};
+      at.q = h->at<float>(L.q);
+      at.ldq = d;
+      at.kv = ring_l;
+      at.kv_slot_stride = L.ring_slot_elems;
+      at.kv_v_off = L.ring_v_off;
+      at.n_heads = H;
+      at.head_dim = hd;
+      at.window = W;
+      at.B = B;
+      at.ti = ti;
+      at.part = h->at<float>(L.att_part);
+      at.max_chunks = L.max_chunks;
+      at.o = h->at<bf16_t>(L.o);
+      at.ldo = d;
+      at.o_lo = (long)B * d;
+      at.cnt = h->at<unsigned>(L.att_cnt);
+      launch_attention(at, s);
+      if (keep_timed) h->timed[1].push_back([at](hipStream_t st) { launch_attention(at, st); });
+      if (keep_timed && l == 0) {
+        h->timed_bytes[1] = -1;  // depends on positions; computed at timing
+      }
+
+      GemmArgs go{};
+      go.W = w.wo + (long)l * d * d;
+      go.X = h->at<bf16_t>(L.o);
+      go.x_lo = (long)B * d;
+      go.M = d;
+      go.K = d;
+      go.ldx = d;
+      go.B = B;
+      go.x = h->at<float>(L.x);
+      go.ldres = d;
+      go.xa_out = h->at<bf16_t>(L.xa);
+      go.xa_lo = (long)B * d;
+      go.alpha_next = w.mlp_norm + (long)l * d;
+      go.part_out = h->at<float>(L.part);
+      go.split_part = split_part;
+      go.wide_rms = wide_rms;
+      launch_gemm(EPI_RESID, go, s);
+      if (keep_timed) h->timed[2].push_back([go](hipStream_t st) { launch_gemm(EPI_RESID, go, st); });
+      if (keep_timed && l == 0) {
+        h->timed_bytes[2] = 2.0 * d * d + B * (4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d / 16);
+      }
+
+      GemmArgs gu{};
+      gu.W = w.w_in + (long)l * 2 * F * d;
+      gu.X = h->at<bf16_t>(L.xa);
+      gu.x_lo = (long)B * d;
+      gu.M = F;
+      gu.K = d;
+      gu.ldx = d;
+      gu.B = B;
+      gu.gate_off = F;
+      gu.part_in = h->at<float>(L.part);
+      gu.n_part = d / 16;
+      gu.feat = d;
+      gu.eps = dm.norm_eps;
+      gu.m_out = h->at<bf16_t>(L.m);
+      gu.ldm = F;
+      gu.m_lo = (long)B * F;
+      gu.split_part = split_part;
+      gu.wide_rms = wide_rms;
+      launch_gemm(EPI_GATED, gu, s);
+      if (keep_timed) h->timed[3].push_back([gu](hipStream_t st) { launch_gemm(EPI_GATED, gu, st); });
+      if (keep_timed && l == 0) {
+        h->timed_bytes[3] = 2.0 * 2 * F * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * F);
+      }
+
+      GemmArgs gd{};
+      gd.W = w.w_out + (long)l * d * F;
+      gd.X = h->at<bf16_t>(L.m);
+      gd.x_lo = (long)B * F;
+      gd.M = d;
+      gd.K = F;
+      gd.ldx = F;
+      gd.B = B;
+      gd.x = h->at<float>(L.x);
+      gd.ldres = d;
+      gd.xa_out = h->at<bf16_t>(L.xa);
+      gd.xa_lo = (long)B * d;
+      gd.alpha_next = (l + 1 < dm.n_layers) ? w.attn_norm + (long)(l + 1) * d : w.out_norm;
+      gd.part_out = h->at<float>(L.part);
+      gd.tap = h->at<float>(L.hidden) + (long)(l + 1) * B * d;
+      gd.split_part = split_part;
+      gd.wide_rms = wide_rms;
+      launch_gemm(EPI_RESID, gd, s);
+      if (keep_timed) h->timed[4].push_back([gd](hipStream_t st) { launch_gemm(EPI_RESID, gd, st); });
+      if (keep_timed && l == 0) {
+        h->timed_bytes[4] = 2.0 * d * F + B * (4.0 * F + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d / 16);
+      }
     }
 
-    AttnArgs at{};
-    at.q = h->at<float>(L.q);
-    at.ldq = d;
-    at.kv = ring_l;
-    at.kv_slot_stride = L.ring_slot_elems;
-    at.kv_v_off = L.ring_v_off;
-    at.n_heads = H;
-    at.head_dim = hd;
-    at.window = W;
-    at.B = B;
-    at.ti = ti;
-    at.part = h->at<float>(L.att_part);
-    at.max_chunks = L.max_chunks;
-    at.o = h->at<bf16_t>(L.o);
-    at.ldo = d;
-    at.o_lo = (long)B * d;
-    at.cnt = h->at<unsigned>(L.att_cnt);
-    launch_attention(at, s);
-    if (keep_timed) h->timed[1].push_back([at](hipStream_t st) { launch_attention(at, st); });
-    if (keep_timed && l == 0) {
-      h->timed_bytes[1] = -1;  // depends on positions; computed at timing
+    // text head + greedy partials
+    GemmArgs gt{};
+    gt.W = w.text_head;
+    gt.X = h->at<bf16_t>(L.xa);
+    gt.x_lo = (long)B * d;
+    gt.M = Vt;
+    gt.K = d;
+    gt.ldx = d;
+    gt.B = B;
+    gt.part_in = h->at<float>(L.part);
+    gt.n_part = d / 16;
+    gt.feat = d;
+    gt.eps = dm.norm_eps;
+    gt.f_out = h->at<float>(L.text_logits);
+    gt.ldf = Vt;
+    gt.amax_v = h->at<float>(L.tamax_v);
+    gt.amax_i = h->at<int>(L.tamax_i);
+    gt.ld_amax = L.n_amax;
+    gt.split_part = split_part;
+    gt.wide_rms = wide_rms;
+    launch_gemm(EPI_LOGITS, gt, s);
+    if (keep_timed) {
+      h->timed[5].push_back([gt](hipStream_t st) { launch_gemm(EPI_LOGITS, gt, st); });
+      h->timed_bytes[5] = 2.0 * Vt * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * Vt);
     }
 
-    GemmArgs go{};
-    go.W = w.wo + (long)l * d * d;
-    go.X = h->at<bf16_t>(L.o);
-    go.x_lo = (long)B * d;
-    go.M = d;
-    go.K = d;
-    go.ldx = d;
-    go.B = B;
-    go.x = h->at<float>(L.x);
-    go.ldres = d;
-    go.xa_out = h->at<bf16_t>(L.xa);
-    go.xa_lo = (long)B * d;
-    go.alpha_next = w.mlp_norm + (long)l * d;
-    go.part_out = h->at<float>(L.part);
-    go.split_part = split_part;
-    go.wide_rms = wide_rms;
-    launch_gemm(EPI_RESID, go, s);
-    if (keep_timed) h->timed[2].push_back([go](hipStream_t st) { launch_gemm(EPI_RESID, go, st); });
-    if (keep_timed && l == 0) {
-      h->timed_bytes[2] = 2.0 * d * d + B * (4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d / 16);
-    }
-
-    GemmArgs gu{};
-    gu.W = w.w_in + (long)l * 2 * F * d;
-    gu.X = h->at<bf16_t>(L.xa);
-    gu.x_lo = (long)B * d;
-    gu.M = F;
-    gu.K = d;
-    gu.ldx = d;
-    gu.B = B;
-    gu.gate_off = F;
-    gu.part_in = h->at<float>(L.part);
-    gu.n_part = d / 16;
-    gu.feat = d;
-    gu.eps = dm.norm_eps;
-    gu.m_out = h->at<bf16_t>(L.m);
-    gu.ldm = F;
-    gu.m_lo = (long)B * F;
-    gu.split_part = split_part;
-    gu.wide_rms = wide_rms;
-    launch_gemm(EPI_GATED, gu, s);
-    if (keep_timed) h->timed[3].push_back([gu](hipStream_t st) { launch_gemm(EPI_GATED, gu, st); });
-    if (keep_timed && l == 0) {
-      h->timed_bytes[3] = 2.0 * 2 * F * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * F);
-    }
-
-    GemmArgs gd{};
-    gd.W = w.w_out + (long)l * d * F;
-    gd.X = h->at<bf16_t>(L.m);
-    gd.x_lo = (long)B * F;
-    gd.M = d;
-    gd.K = F;
-    gd.ldx = F;
-    gd.B = B;
-    gd.x = h->at<float>(L.x);
-    gd.ldres = d;
-    gd.xa_out = h->at<bf16_t>(L.xa);
-    gd.xa_lo = (long)B * d;
-    gd.alpha_next = (l + 1 < dm.n_layers) ? w.attn_norm + (long)(l + 1) * d : w.out_norm;
-    gd.part_out = h->at<float>(L.part);
-    gd.tap = h->at<float>(L.hidden) + (long)(l + 1) * B * d;
-    gd.split_part = split_part;
-    gd.wide_rms = wide_rms;
-    launch_gemm(EPI_RESID, gd, s);
-    if (keep_timed) h->timed[4].push_back([gd](hipStream_t st) { launch_gemm(EPI_RESID, gd, st); });
-    if (keep_timed && l == 0) {
-      h->timed_bytes[4] = 2.0 * d * F + B * (4.0 * F + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d + 4.0 * d / 16);
-    }
-  }
-
-  // text head + greedy partials
-  GemmArgs gt{};
-  gt.W = w.text_head;
-  gt.X = h->at<bf16_t>(L.xa);
-  gt.x_lo = (long)B * d;
-  gt.M = Vt;
-  gt.K = d;
-  gt.ldx = d;
-  gt.B = B;
-  gt.part_in = h->at<float>(L.part);
-  gt.n_part = d / 16;
-  gt.feat = d;
-  gt.eps = dm.norm_eps;
-  gt.f_out = h->at<float>(L.text_logits);
-  gt.ldf = Vt;
-  gt.amax_v = h->at<float>(L.tamax_v);
-  gt.amax_i = h->at<int>(L.tamax_i);
-  gt.ld_amax = L.n_amax;
-  gt.split_part = split_part;
-  gt.wide_rms = wide_rms;
-  launch_gemm(EPI_LOGITS, gt, s);
-  if (keep_timed) {
-    h->timed[5].push_back([gt](hipStream_t st) { launch_gemm(EPI_LOGITS, gt, st); });
-    h->timed_bytes[5] = 2.0 * Vt * d + B * (4.0 * d + 4.0 * d / 16 + 4.0 * Vt);
-  }
-
-  }  // PH_TEMPORAL
+  }  // PH_TEMPORAL: embedding, temporal stack, text head
 
   // the text finisher (greedy text token -> depformer step 0 input); the
   // codebook finishers below copy it
