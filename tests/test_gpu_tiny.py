@@ -182,6 +182,25 @@ def test_pipelined_ticks_match_tick_by_tick(tiny_weights, dev):
     b.close()
 
 
+@pytest.mark.parametrize("window", [1, 2])
+def test_degenerate_window_teacher_forced_parity(tiny_weights, dev, window):
+    """A ring of 1 or 2 frames: each tick attends to its own key (and the one
+    before); 12 teacher-forced ticks against the oracle with the same window."""
+    _say(f"case: window {window}, 12 teacher-forced ticks, B=1")
+    n = 12
+    codes = synth.user_codes(11, n)
+    recs = parity.oracle_run(Oracle(DM, tiny_weights, 1, window), codes)
+    e = engine(tiny_weights, dev, 1, window)
+    e.prefill_forced(0, parity.teacher_frames(recs, codes))
+    fails, report = [], {}
+    for t in range(n):
+        e.step(np.zeros((1, 8), np.int32))
+        fails += parity.compare_tick(parity.gpu_slot(e.taps(), 0), recs[t], t, report)
+    e.close()
+    _say(f"worst hidden rel-L2 {max(report['hidden_rel_l2']):.3e}")
+    assert not fails, "\n".join(fails[:20])
+
+
 def test_ring_fill_then_teacher_forced_parity(tiny_weights, dev):
     """Ring pre-filled with 20 frames of N(0,1) bf16 keys/values; 15 ticks
     from position 20 slide the 32-frame window."""
