@@ -28,8 +28,11 @@ static_assert(DEP_WINDOW <= DEP_MAX_KEYS, "depformer attention holds at most DEP
 
 struct Layout {
   // byte offsets into the arena
-  size_t ring, dkv, x, xa, part, q, att_part, o, m, hidden, text_logits, amax_v, amax_i, tamax_v, tamax_i, u, y, ya, dpart, dq, dout,
-      dm, dep_logits, ti, to, inv_freq, split_part, wide_rms, rope, att_cnt, total;
+  size_t ring, x, xa, part, q, att_part, o, m, hidden, text_logits, tamax_v, tamax_i, dep_logits, ti, to, inv_freq,
+      split_part, wide_rms, rope, att_cnt, total;
+  // depformer buffers, two sets: the agent codebooks of tick t+1 run beside
+  // the user-stream codebooks of tick t, which keep using the other set
+  size_t dkv[2], amax_v[2], amax_i[2], u[2], y[2], ya[2], dpart[2], dq[2], dout[2], dm[2];
   long wide_part_max;
   int max_chunks, n_amax;
   long ring_slot_elems, ring_layer_elems, ring_v_off;
@@ -74,7 +77,6 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.max_chunks = (W + ATT_CHUNK - 1) / ATT_CHUNK;  // <= ATT_MAX_SPLITS for W <= PP_MAX_WINDOW
   L.n_amax = (int)((std::max(Vt, A) + ROWS - 1) / ROWS);
   L.ring = take((size_t)B * L.ring_slot_elems * 2);
-  L.dkv = take((size_t)B * L.dkv_slot_elems * 2);
   L.x = take(B * d * 4);
   L.xa = take(2 * B * d * 2);  // activations feeding GEMMs: bf16 hi plane then lo plane
   L.part = take(B * (d / 16) * 4);
@@ -84,19 +86,22 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.m = take(2 * B * F * 2);
   L.hidden = take((size_t)(dm.n_layers + 1) * B * d * 4);
   L.text_logits = take(B * Vt * 4);
-  // argmax partials: depformer heads, and the text head's own (the text head
-  // of tick t+1 runs while the user-stream codebooks of tick t still do)
-  L.amax_v = take((size_t)B * L.n_amax * 4);
-  L.amax_i = take((size_t)B * L.n_amax * 4);
+  // argmax partials of the text head (its own: the user-stream codebooks of
+  // the previous tick may run beside it)
   L.tamax_v = take((size_t)B * L.n_amax * 4);
   L.tamax_i = take((size_t)B * L.n_amax * 4);
-  L.u = take(B * Q * dd * 4);
-  L.y = take(B * dd * 4);
-  L.ya = take(2 * B * dd * 2);
-  L.dpart = take(B * (dd / 16) * 4);
-  L.dq = take(B * dd * 4);
-  L.dout = take(2 * B * dd * 2);
-  L.dm = take(2 * B * dF * 2);
+  for (int s = 0; s < 2; ++s) {
+    L.dkv[s] = take((size_t)B * L.dkv_slot_elems * 2);
+    L.amax_v[s] = take((size_t)B * L.n_amax * 4);
+    L.amax_i[s] = take((size_t)B * L.n_amax * 4);
+    L.u[s] = take(B * Q * dd * 4);
+    L.y[s] = take(B * dd * 4);
+    L.ya[s] = take(2 * B * dd * 2);
+    L.dpart[s] = take(B * (dd / 16) * 4);
+    L.dq[s] = take(B * dd * 4);
+    L.dout[s] = take(2 * B * dd * 2);
+    L.dm[s] = take(2 * B * dF * 2);
+  }
   L.dep_logits = take(B * Q * A * 4);
   L.ti = take(B * TI_STRIDE * 4);
   L.to = take(B * TO_STRIDE * 4);
@@ -132,15 +137,20 @@ struct pp_handle {
   pp_weights w;
   Layout lay;
   char* arena = nullptr;
-  // The tick is three graphs: PH_TEMPORAL (embedding, temporal stack, text
+  // The tick is three phases: PH_TEMPORAL (embedding, temporal stack, text
   // head) and PH_AGENT (input projections, text finisher, codebooks 0..n_q-1)
-  // on the caller's stream, then PH_USER (the user-stream codebooks n_q..)
-  // on `side`, where it overlaps the next tick's PH_TEMPORAL.  PH_AGENT
-  // waits for the previous PH_USER (event `user_done`).
+  // on the caller's stream, and PH_USER (the user-stream codebooks n_q..) on
+  // `side`.  PH_USER of tick t is launched by tick t+1, after its
+  // PH_TEMPORAL, so that it runs beside PH_AGENT of tick t+1; the two use
+  // different depformer buffer sets (set = tick parity), one graph each.
+  // exec[0] = PH_TEMPORAL, exec[1 + s] = PH_AGENT on set s, exec[3 + s] =
+  // PH_USER on set s.
   hipStream_t stream = nullptr, cap = nullptr, side = nullptr;
-  hipGraph_t graph[3] = {nullptr, nullptr, nullptr};
-  hipGraphExec_t exec[3] = {nullptr, nullptr, nullptr};
-  hipEvent_t agent_done = nullptr, user_done = nullptr;
+  hipGraph_t graph[5] = {};
+  hipGraphExec_t exec[5] = {};
+  hipEvent_t temporal_done = nullptr, agent_done = nullptr, user_done[2] = {nullptr, nullptr};
+  int parity = 0;             // depformer buffer set of the next tick
+  bool user_pending = false;  // PH_USER of the last tick not launched yet
   int32_t* ti_host = nullptr;
   int32_t* to_host = nullptr;
   std::vector<Slot> slots;
@@ -184,7 +194,8 @@ void reset_slot(const pp_dims& dm, Slot& s) {
 enum Phase { PH_TEMPORAL = 0, PH_AGENT = 1, PH_USER = 2 };
 
 // Record the kernels of one phase of the tick on stream s.
-void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
+// `ds`: the depformer buffer set (PH_AGENT and PH_USER of one tick share one).
+void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_timed) {
   const pp_dims& dm = h->dm;
   const Layout& L = h->lay;
   const int B = h->B, W = h->W;
@@ -385,13 +396,13 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
   fa.to = to;
   fa.dep_q = Q;
   fa.dd = dd;
-  fa.u = h->at<float>(L.u);
+  fa.u = h->at<float>(L.u[ds]);
   fa.table = w.dep_emb_text;
   fa.alpha = w.dep_attn_norm;
-  fa.y = h->at<float>(L.y);
-  fa.ya = h->at<bf16_t>(L.ya);
+  fa.y = h->at<float>(L.y[ds]);
+  fa.ya = h->at<bf16_t>(L.ya[ds]);
   fa.ya_lo = (long)B * dd;
-  fa.part = h->at<float>(L.dpart);
+  fa.part = h->at<float>(L.dpart[ds]);
 
   // depformer input projections u_k = P_k z for codebooks [c0, c1), one GEMM
   auto in_proj = [&](int c0, int c1) {
@@ -407,7 +418,7 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
     gp.n_part = d / 16;
     gp.feat = d;
     gp.eps = dm.norm_eps;
-    gp.f_out = h->at<float>(L.u) + (long)c0 * dd;
+    gp.f_out = h->at<float>(L.u[ds]) + (long)c0 * dd;
     gp.ldf = (long)Q * dd;
     gp.split_part = split_part;
     gp.wide_rms = wide_rms;
@@ -427,21 +438,21 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
   const int k0 = phase == PH_AGENT ? 0 : dm.n_q, k1 = phase == PH_AGENT ? dm.n_q : Q;
   for (int k = k0; k < k1; ++k) {
     for (int l = 0; l < dm.dep_layers; ++l) {
-      bf16_t* dkv_l = h->at<bf16_t>(L.dkv) + (long)l * L.dkv_layer_elems;
+      bf16_t* dkv_l = h->at<bf16_t>(L.dkv[ds]) + (long)l * L.dkv_layer_elems;
       GemmArgs g{};
       g.W = w.dep_wqkv + (long)l * 3 * dd * dd;
       g.w_keep = 1;  // re-read at every codebook step
-      g.X = h->at<bf16_t>(L.ya);
+      g.X = h->at<bf16_t>(L.ya[ds]);
       g.x_lo = (long)B * dd;
       g.M = 3 * dd;
       g.K = dd;
       g.ldx = dd;
       g.B = B;
-      g.part_in = h->at<float>(L.dpart);
+      g.part_in = h->at<float>(L.dpart[ds]);
       g.n_part = dd / 16;
       g.feat = dd;
       g.eps = dm.norm_eps;
-      g.q_out = h->at<float>(L.dq);
+      g.q_out = h->at<float>(L.dq[ds]);
       g.ldq = dd;
       g.kv = dkv_l;
       g.kv_slot_stride = L.dkv_slot_elems;
@@ -459,7 +470,7 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
       // attention over steps 0..k of this frame: inside the out-projection at
       // small batch, else its own launch (same arithmetic either way)
       DepAttnArgs da{};
-      da.q = h->at<float>(L.dq);
+      da.q = h->at<float>(L.dq[ds]);
       da.ldq = dd;
       da.kv = dkv_l;
       da.slot_stride = L.dkv_slot_elems;
@@ -469,7 +480,7 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
       da.window = DEP_WINDOW;
       da.n_keys = k + 1;
       da.B = B;
-      da.o = h->at<bf16_t>(L.dout);
+      da.o = h->at<bf16_t>(L.dout[ds]);
       da.ldo = dd;
       da.o_lo = (long)B * dd;
       const bool fuse_att = B <= DEP_FUSE_B && dd <= DEP_FUSE_D;
@@ -478,18 +489,18 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
       GemmArgs go{};
       go.W = w.dep_wo + (long)l * dd * dd;
       go.w_keep = 1;  // re-read at every codebook step
-      go.X = h->at<bf16_t>(L.dout);
+      go.X = h->at<bf16_t>(L.dout[ds]);
       go.x_lo = (long)B * dd;
       go.M = dd;
       go.K = dd;
       go.ldx = dd;
       go.B = B;
-      go.x = h->at<float>(L.y);
+      go.x = h->at<float>(L.y[ds]);
       go.ldres = dd;
-      go.xa_out = h->at<bf16_t>(L.ya);
+      go.xa_out = h->at<bf16_t>(L.ya[ds]);
       go.xa_lo = (long)B * dd;
       go.alpha_next = w.dep_mlp_norm + (long)l * dd;
-      go.part_out = h->at<float>(L.dpart);
+      go.part_out = h->at<float>(L.dpart[ds]);
       go.split_part = split_part;
       go.wide_rms = wide_rms;
       go.fuse_att = fuse_att;
@@ -499,18 +510,18 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
       GemmArgs gu{};
       gu.W = w.dep_w_in + (long)l * 2 * dF * dd;
       gu.w_keep = 1;  // re-read at every codebook step
-      gu.X = h->at<bf16_t>(L.ya);
+      gu.X = h->at<bf16_t>(L.ya[ds]);
       gu.x_lo = (long)B * dd;
       gu.M = dF;
       gu.K = dd;
       gu.ldx = dd;
       gu.B = B;
       gu.gate_off = dF;
-      gu.part_in = h->at<float>(L.dpart);
+      gu.part_in = h->at<float>(L.dpart[ds]);
       gu.n_part = dd / 16;
       gu.feat = dd;
       gu.eps = dm.norm_eps;
-      gu.m_out = h->at<bf16_t>(L.dm);
+      gu.m_out = h->at<bf16_t>(L.dm[ds]);
       gu.ldm = dF;
       gu.m_lo = (long)B * dF;
       gu.split_part = split_part;
@@ -520,38 +531,38 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
       GemmArgs gd{};
       gd.W = w.dep_w_out + (long)l * dd * dF;
       gd.w_keep = 1;  // re-read at every codebook step
-      gd.X = h->at<bf16_t>(L.dm);
+      gd.X = h->at<bf16_t>(L.dm[ds]);
       gd.x_lo = (long)B * dF;
       gd.M = dd;
       gd.K = dF;
       gd.ldx = dF;
       gd.B = B;
-      gd.x = h->at<float>(L.y);
+      gd.x = h->at<float>(L.y[ds]);
       gd.ldres = dd;
-      gd.xa_out = h->at<bf16_t>(L.ya);
+      gd.xa_out = h->at<bf16_t>(L.ya[ds]);
       gd.xa_lo = (long)B * dd;
       gd.alpha_next = (l + 1 < dm.dep_layers) ? w.dep_attn_norm + (long)(l + 1) * dd : w.dep_out_norm;
-      gd.part_out = h->at<float>(L.dpart);
+      gd.part_out = h->at<float>(L.dpart[ds]);
       gd.split_part = split_part;
       gd.wide_rms = wide_rms;
       launch_gemm(EPI_RESID, gd, s);
     }
     GemmArgs gh{};
     gh.W = w.dep_heads + (long)k * packed_elems(A, dd);
-    gh.X = h->at<bf16_t>(L.ya);
+    gh.X = h->at<bf16_t>(L.ya[ds]);
     gh.x_lo = (long)B * dd;
     gh.M = A;
     gh.K = dd;
     gh.ldx = dd;
     gh.B = B;
-    gh.part_in = h->at<float>(L.dpart);
+    gh.part_in = h->at<float>(L.dpart[ds]);
     gh.n_part = dd / 16;
     gh.feat = dd;
     gh.eps = dm.norm_eps;
     gh.f_out = h->at<float>(L.dep_logits) + (long)k * A;
     gh.ldf = (long)Q * A;
-    gh.amax_v = h->at<float>(L.amax_v);
-    gh.amax_i = h->at<int>(L.amax_i);
+    gh.amax_v = h->at<float>(L.amax_v[ds]);
+    gh.amax_i = h->at<int>(L.amax_i[ds]);
     gh.ld_amax = L.n_amax;
     gh.split_part = split_part;
     gh.wide_rms = wide_rms;
@@ -560,8 +571,8 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, bool keep_timed) {
     FinishArgs f = fa;
     f.step = k;
     f.n_part = (A + ROWS - 1) / ROWS;
-    f.amax_v = h->at<float>(L.amax_v);
-    f.amax_i = h->at<int>(L.amax_i);
+    f.amax_v = h->at<float>(L.amax_v[ds]);
+    f.amax_i = h->at<int>(L.amax_i[ds]);
     f.table = (k + 1 < Q) ? w.dep_emb_audio + (long)k * (A + 1) * dd : nullptr;
     launch_finish(f, s);
   }
@@ -581,17 +592,45 @@ void build_tick_input(pp_handle* h, const int32_t* user_codes, const std::array<
   }
 }
 
-// Launch one tick: PH_TEMPORAL, then (after the previous tick's user-stream
-// codebooks) PH_AGENT on the handle's stream, then PH_USER on the side stream.
-hipError_t launch_tick(pp_handle* h) {
+// Launch the last tick's PH_USER on the side stream, after that tick's
+// PH_AGENT (the most recent record of `agent_done`) and, when `after` is
+// given, after that event too.
+hipError_t launch_user(pp_handle* h, hipEvent_t after) {
+  if (!h->user_pending) return hipSuccess;
+  const int ds = 1 - h->parity;
   hipError_t e;
-  if ((e = hipGraphLaunch(h->exec[PH_TEMPORAL], h->stream)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(h->stream, h->user_done, 0)) != hipSuccess) return e;
-  if ((e = hipGraphLaunch(h->exec[PH_AGENT], h->stream)) != hipSuccess) return e;
-  if ((e = hipEventRecord(h->agent_done, h->stream)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(h->side, h->agent_done, 0)) != hipSuccess) return e;
-  if ((e = hipGraphLaunch(h->exec[PH_USER], h->side)) != hipSuccess) return e;
-  return hipEventRecord(h->user_done, h->side);
+  if (after && (e = hipStreamWaitEvent(h->side, after, 0)) != hipSuccess) return e;
+  if ((e = hipGraphLaunch(h->exec[3 + ds], h->side)) != hipSuccess) return e;
+  if ((e = hipEventRecord(h->user_done[ds], h->side)) != hipSuccess) return e;
+  h->user_pending = false;
+  return hipSuccess;
+}
+
+// Launch one tick: PH_TEMPORAL; then the previous tick's PH_USER on the side
+// stream; then, once PH_USER of two ticks back has released this tick's
+// buffer set, PH_AGENT.  This tick's PH_USER is left pending.
+hipError_t launch_tick(pp_handle* h) {
+  const int ds = h->parity;
+  hipError_t e;
+  if ((e = hipGraphLaunch(h->exec[0], h->stream)) != hipSuccess) return e;
+  if ((e = hipEventRecord(h->temporal_done, h->stream)) != hipSuccess) return e;
+  if ((e = launch_user(h, h->temporal_done)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(h->stream, h->user_done[ds], 0)) != hipSuccess) return e;
+  if ((e = hipGraphLaunch(h->exec[1 + ds], h->stream)) != hipSuccess) return e;
+  if ((e = hipEventRecord(h->agent_done, h->stream)) != hipSuccess) return e;
+  h->user_pending = true;
+  h->parity = 1 - ds;
+  return hipSuccess;
+}
+
+// Launch the pending PH_USER, if any, and make `s` wait for every PH_USER.
+hipError_t flush_user(pp_handle* h, hipStream_t s) {
+  hipError_t e;
+  if ((e = launch_user(h, nullptr)) != hipSuccess) return e;
+  for (int i = 0; i < 2; ++i)
+    if ((e = hipStreamWaitEvent(s, h->user_done[i], 0)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -666,18 +705,19 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
   if ((e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
   if ((e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
-  if ((e = hipEventCreateWithFlags(&h->agent_done, hipEventDisableTiming)) != hipSuccess)
-    return bail("hipEventCreate", e);
-  if ((e = hipEventCreateWithFlags(&h->user_done, hipEventDisableTiming)) != hipSuccess)
-    return bail("hipEventCreate", e);
-  if ((e = hipEventRecord(h->user_done, h->side)) != hipSuccess) return bail("hipEventRecord", e);
-  for (int ph = 0; ph < 3; ++ph) {
+  for (hipEvent_t* ev : {&h->temporal_done, &h->agent_done, &h->user_done[0], &h->user_done[1]}) {
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return bail("hipEventCreate", e);
+    if ((e = hipEventRecord(*ev, h->side)) != hipSuccess) return bail("hipEventRecord", e);
+  }
+  for (int g = 0; g < 5; ++g) {
+    const Phase ph = g == 0 ? PH_TEMPORAL : g < 3 ? PH_AGENT : PH_USER;
+    const int ds = g == 0 ? 0 : (g - 1) % 2;
     if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess)
       return bail("hipStreamBeginCapture", e);
-    record_tick(h, h->cap, static_cast<Phase>(ph), ph == PH_TEMPORAL);
-    if ((e = hipStreamEndCapture(h->cap, &h->graph[ph])) != hipSuccess) return bail("hipStreamEndCapture", e);
+    record_tick(h, h->cap, ph, ds, ph == PH_TEMPORAL);
+    if ((e = hipStreamEndCapture(h->cap, &h->graph[g])) != hipSuccess) return bail("hipStreamEndCapture", e);
     if ((e = hipGetLastError()) != hipSuccess) return bail("kernel launch during capture", e);
-    if ((e = hipGraphInstantiate(&h->exec[ph], h->graph[ph], nullptr, nullptr, 0)) != hipSuccess)
+    if ((e = hipGraphInstantiate(&h->exec[g], h->graph[g], nullptr, nullptr, 0)) != hipSuccess)
       return bail("hipGraphInstantiate", e);
   }
   *out = h;
@@ -788,8 +828,13 @@ int pp_ring_fill(pp_handle* h, int slot, int n, const uint16_t* k, const uint16_
 int pp_taps(const pp_handle* h, pp_taps_t* out) {
   if (!h || !out) return PP_EINVAL;
   if (h->poisoned) return PP_EDEVICE;
-  // the tick's user-stream codebooks write the depformer logits and predictions
-  if (hipEventSynchronize(h->user_done) != hipSuccess) return PP_EDEVICE;
+  // the last tick's user-stream codebooks write the depformer logits and
+  // predictions: launch them if still pending, and wait
+  pp_handle* hm = const_cast<pp_handle*>(h);
+  if (flush_user(hm, hm->side) != hipSuccess || hipStreamSynchronize(hm->side) != hipSuccess) {
+    hm->poisoned = true;
+    return PP_EDEVICE;
+  }
   out->hidden = h->at<float>(h->lay.hidden);
   out->text_logits = h->at<float>(h->lay.text_logits);
   out->dep_logits = h->at<float>(h->lay.dep_logits);
@@ -811,7 +856,7 @@ int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* by
     }
   }
   if (bytes) *bytes = by;
-  HIP_OR_FAIL(h, hipEventSynchronize(h->user_done));
+  HIP_OR_FAIL(h, flush_user(h, h->stream));
   build_tick_input(h, nullptr, nullptr);
   HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.ti), h->ti_host, h->B * TI_STRIDE * 4, hipMemcpyHostToDevice,
                                 h->stream));
@@ -846,13 +891,12 @@ int pp_time_graph(pp_handle* h, int iters, float* avg_ms) {
   hipEvent_t e0, e1;
   HIP_OR_FAIL(h, hipEventCreate(&e0));
   HIP_OR_FAIL(h, hipEventCreate(&e1));
-  // steady state of back-to-back ticks; the last tick's user-stream codebooks
-  // are included (the timer ends after them)
-  HIP_OR_FAIL(h, launch_tick(h));
-  HIP_OR_FAIL(h, hipStreamWaitEvent(h->stream, h->user_done, 0));
+  // steady state of back-to-back ticks, timed from the end of the previous
+  // tick's PH_USER to the end of the last one (the timer includes it)
+  HIP_OR_FAIL(h, flush_user(h, h->stream));
   HIP_OR_FAIL(h, hipEventRecord(e0, h->stream));
   for (int i = 0; i < iters; ++i) HIP_OR_FAIL(h, launch_tick(h));
-  HIP_OR_FAIL(h, hipStreamWaitEvent(h->stream, h->user_done, 0));
+  HIP_OR_FAIL(h, flush_user(h, h->stream));
   HIP_OR_FAIL(h, hipEventRecord(e1, h->stream));
   HIP_OR_FAIL(h, hipEventSynchronize(e1));
   float ms = 0;
@@ -876,14 +920,15 @@ int pp_pack_matrix(const uint16_t* src, int M, int K, uint16_t* dst, void* strea
 
 void pp_destroy(pp_handle* h) {
   if (!h) return;
+  // a pending PH_USER is dropped: nothing reads its results after this
   if (h->side) (void)hipStreamSynchronize(h->side);
   (void)hipStreamSynchronize(h->stream);
-  for (int ph = 0; ph < 3; ++ph) {
-    if (h->exec[ph]) (void)hipGraphExecDestroy(h->exec[ph]);
-    if (h->graph[ph]) (void)hipGraphDestroy(h->graph[ph]);
+  for (int g = 0; g < 5; ++g) {
+    if (h->exec[g]) (void)hipGraphExecDestroy(h->exec[g]);
+    if (h->graph[g]) (void)hipGraphDestroy(h->graph[g]);
   }
-  if (h->agent_done) (void)hipEventDestroy(h->agent_done);
-  if (h->user_done) (void)hipEventDestroy(h->user_done);
+  for (hipEvent_t ev : {h->temporal_done, h->agent_done, h->user_done[0], h->user_done[1]})
+    if (ev) (void)hipEventDestroy(ev);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->cap) (void)hipStreamDestroy(h->cap);
   if (h->ti_host) (void)hipHostFree(h->ti_host);

@@ -20,7 +20,6 @@ enum {
   TO_PRED = 0,       // 9: text, agent 0..7 predictions
   TO_USER = 9,       // 8: depformer steps 8..15 predictions
   TO_CHOSEN = 17,    // 9: chosen text, agent 0..7
-  TO_TOK = 26,       // 1: the token fed to the next depformer step
   TO_STRIDE = 32
 };
 

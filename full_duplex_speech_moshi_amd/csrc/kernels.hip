@@ -1094,7 +1094,6 @@ __device__ void finish_unit(const FinishArgs& a, const int b) {
     } else {
       to[TO_USER + a.step - 8] = pred;
     }
-    to[TO_TOK] = chosen;
     chosen_s = chosen;
   }
   __syncthreads();

@@ -164,11 +164,12 @@ int pp_prefill_forced(pp_handle* h, int slot, const int32_t* frames, int n);
  * tick becomes free-running.  Every slot computes every tick.
  *
  * Pipelining: the depformer's user-stream codebooks (steps 8..15, which feed
- * only the taps, never the next column) run on the library's internal stream
- * after the agent codebooks, and may still be running when pp_step returns.
- * They overlap the next tick's embedding and temporal stack; the next tick's
- * depformer waits for them, and so do pp_taps, pp_time_kernel and
- * pp_destroy.  The work and its results are those of the plain sequence. */
+ * only the taps, never the next column) are launched by the next pp_step, on
+ * the library's internal stream, once that tick's temporal stack is done:
+ * they run beside the next tick's agent codebooks, in a second set of
+ * depformer buffers.  pp_taps, pp_time_kernel and pp_time_graph launch them
+ * if still pending and wait for them; pp_destroy drops them.  The work and
+ * its results are those of the plain sequence. */
 int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens);
 
 /* Recycle `slot`: position 0, column back to the initial tokens
@@ -184,7 +185,8 @@ int pp_slot_reset(pp_handle* h, int slot);
 int pp_ring_fill(pp_handle* h, int slot, int n, const uint16_t* k, const uint16_t* v);
 
 /* Device views of the last tick's intermediate results (see pp_taps_t).
- * Waits for the tick's user-stream codebooks first. */
+ * Launches the tick's user-stream codebooks if still pending and waits for
+ * them first. */
 int pp_taps(const pp_handle* h, pp_taps_t* out);
 
 /* Measurement hook: launch one kernel of the tick graph outside the graph,
