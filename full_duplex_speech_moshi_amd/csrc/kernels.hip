@@ -581,13 +581,18 @@ __global__ __launch_bounds__(512) void gemm_att_kernel(GemmArgs a) {
 //     and runs the common epilogue.
 // ---------------------------------------------------------------------------
 
-constexpr int WIDE_SK = 8;  // k-steps of activations per LDS stage
-constexpr int WIDE_U = 4;   // weight loads in flight per wave
+constexpr int WIDE_SK = 8;  // k-steps per stage (activations in LDS, weights in registers)
+constexpr int WIDE_XL = 2 * WIDE_SK * 32 * 4 / 512;  // 16-byte activation pieces per thread per stage
 
+// Stage st of the k-range is software-pipelined: while the waves multiply
+// stage st (weights in registers, activations in LDS buffer st & 1), the
+// weights and activations of stage st + 1 are in flight; one barrier per
+// stage.  Every wave still accumulates its k-range in k-step order, hi then
+// lo, as the contract requires.
 template <int RT>
 __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
   constexpr int NT = 2, NTC = 32;
-  __shared__ __attribute__((aligned(16))) bf16_t xs[2][WIDE_SK][NTC][32];
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][2][WIDE_SK][NTC][32];  // [buffer][hi/lo][k-step][column]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int j = blockIdx.x % GEMM_WAVES, grp = blockIdx.x / GEMM_WAVES;
@@ -611,39 +616,67 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
     if (tid < NTC) a.wide_rms[tid] = inv[tid];
   }
 
+  // activation piece i of a stage (i = tid + 512 u): 16 bytes of plane
+  // i >> 10, k-step (i >> 7) & 7, column (i >> 2) & 31, part i & 3
+  auto load_x = [&](int c0, int nsub, u32x4 (&xr)[WIDE_XL]) {
+#pragma unroll
+    for (int u = 0; u < WIDE_XL; ++u) {
+      const int i = tid + 512 * u;
+      const int part = i & 3, c = (i >> 2) & 31, q = (i >> 7) & 7, pl = i >> 10;
+      xr[u] = (q < nsub && c < a.B) ? ld16(a.X + (pl ? a.x_lo : 0) + (long)c * a.ldx + (c0 + q) * 32 + part * 8) : zero;
+    }
+  };
+  auto store_x = [&](int buf, const u32x4 (&xr)[WIDE_XL]) {
+#pragma unroll
+    for (int u = 0; u < WIDE_XL; ++u) {
+      const int i = tid + 512 * u;
+      const int part = i & 3, c = (i >> 2) & 31, q = (i >> 7) & 7, pl = i >> 10;
+      *reinterpret_cast<u32x4*>(&xs[buf][pl][q][c][part * 8]) = xr[u];
+    }
+  };
+  auto load_w = [&](int c0, int nsub, u32x4 (&wr)[WIDE_SK]) {
+#pragma unroll
+    for (int u = 0; u < WIDE_SK; ++u) wr[u] = (t_ok && u < nsub) ? ldw16<true>(w + (long)(c0 + u) * 512) : zero;
+  };
+
   f32x4 acc[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = s0; c0 < s1; c0 += WIDE_SK) {
-    const int nsub = min(WIDE_SK, s1 - c0);
-    if (c0 != s0) __syncthreads();  // the previous stage has been consumed
-    for (int i = tid; i < 2 * nsub * NTC * 4; i += 512) {
-      const int part = i & 3, c = (i >> 2) % NTC, q = ((i >> 2) / NTC) % nsub, pl = (i >> 2) / NTC / nsub;
-      u32x4 v = zero;
-      if (c < a.B) v = ld16(a.X + (pl ? a.x_lo : 0) + (long)c * a.ldx + (c0 + q) * 32 + part * 8);
-      *reinterpret_cast<u32x4*>(&xs[pl][q][c][part * 8]) = v;
+  u32x4 xr[WIDE_XL], wr[WIDE_SK];
+  load_x(s0, min(WIDE_SK, s1 - s0), xr);
+  load_w(s0, min(WIDE_SK, s1 - s0), wr);
+  store_x(0, xr);
+  __syncthreads();
+  for (int st = 0;; ++st) {
+    const int c0 = s0 + st * WIDE_SK, nsub = min(WIDE_SK, s1 - c0);
+    const int cn = c0 + WIDE_SK, nn = min(WIDE_SK, s1 - cn);
+    const int buf = st & 1;
+    u32x4 wn[WIDE_SK];
+    if (nn > 0) {
+      load_w(cn, nn, wn);
+      load_x(cn, nn, xr);
     }
-    __syncthreads();
-    for (int sb = 0; sb < nsub; sb += WIDE_U) {
-      u32x4 av[WIDE_U];
 #pragma unroll
-      for (int u = 0; u < WIDE_U; ++u)
-        av[u] = (t_ok && sb + u < nsub) ? ldw16<true>(w + (long)(c0 + sb + u) * 512) : zero;
+    for (int u = 0; u < WIDE_SK; ++u) {
+      if (u < nsub) {
+        const bf16x8 w8 = __builtin_bit_cast(bf16x8, wr[u]);
 #pragma unroll
-      for (int u = 0; u < WIDE_U; ++u) {
-        if (sb + u < nsub) {
-          const bf16x8 w8 = __builtin_bit_cast(bf16x8, av[u]);
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) {
-            const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[0][sb + u][ct * 16 + r16][g4 * 8]);
-            const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[1][sb + u][ct * 16 + r16][g4 * 8]);
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh), acc[ct], 0, 0, 0);
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl), acc[ct], 0, 0, 0);
-          }
+        for (int ct = 0; ct < NT; ++ct) {
+          const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[buf][0][u][ct * 16 + r16][g4 * 8]);
+          const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[buf][1][u][ct * 16 + r16][g4 * 8]);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh), acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl), acc[ct], 0, 0, 0);
         }
       }
     }
+    if (nn <= 0) break;
+    // buffer buf ^ 1 was last read in stage st - 1, before the barrier that
+    // ended it
+    store_x(buf ^ 1, xr);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < WIDE_SK; ++u) wr[u] = wn[u];
   }
   // p_j of tile t: [t][j][ct][q][lane]
   if (t_ok) {
