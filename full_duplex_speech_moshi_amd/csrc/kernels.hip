@@ -582,6 +582,12 @@ __global__ __launch_bounds__(512) void gemm_att_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int WIDE_SK = 8;  // k-steps per stage (activations in LDS, weights in registers)
+
+// LDS rows of the activation slice are 64 bytes (32 bf16 of one column);
+// the 16-byte chunk `part` of column c is stored at chunk part ^ ((c >> 1) & 3),
+// so the 8 lanes of a 128-bit read (8 consecutive columns, one chunk) hit 8
+// different bank groups instead of 2.
+__device__ __forceinline__ int xs_chunk(int c, int part) { return part ^ ((c >> 1) & 3); }
 constexpr int WIDE_XL = 2 * WIDE_SK * 32 * 4 / 512;  // 16-byte activation pieces per thread per stage
 
 // Stage st of the k-range is software-pipelined: while the waves multiply
@@ -631,7 +637,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
     for (int u = 0; u < WIDE_XL; ++u) {
       const int i = tid + 512 * u;
       const int part = i & 3, c = (i >> 2) & 31, q = (i >> 7) & 7, pl = i >> 10;
-      *reinterpret_cast<u32x4*>(&xs[buf][pl][q][c][part * 8]) = xr[u];
+      *reinterpret_cast<u32x4*>(&xs[buf][pl][q][c][xs_chunk(c, part) * 8]) = xr[u];
     }
   };
   auto load_w = [&](int c0, int nsub, u32x4 (&wr)[WIDE_SK]) {
@@ -663,8 +669,8 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
         const bf16x8 w8 = __builtin_bit_cast(bf16x8, wr[u]);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-          const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[buf][0][u][ct * 16 + r16][g4 * 8]);
-          const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[buf][1][u][ct * 16 + r16][g4 * 8]);
+          const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[buf][0][u][ct * 16 + r16][xs_chunk(r16, g4) * 8]);
+          const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[buf][1][u][ct * 16 + r16][xs_chunk(r16, g4) * 8]);
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh), acc[ct], 0, 0, 0);
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl), acc[ct], 0, 0, 0);
         }
@@ -685,6 +691,109 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
     for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
       for (int q = 0; q < 4; ++q) P[ct * 256 + q * 64] = acc[ct][q];
+  }
+}
+
+// The same partials for k-ranges of exactly WIDE_RES k-steps (K = 4096):
+// workgroup (p, j), j = blockIdx % 8, loads the activation slice of range
+// R_j into LDS once, then each wave streams the weights of tiles
+// p * 8 + wave + i * 8P (P = gridDim / 8, i < tiles per wave) through it.
+// The weights roll: once k-step q of tile i has been multiplied, its
+// registers are refilled with k-step q of tile i + 1, so a whole range of
+// loads stays in flight per wave; no barrier after the slice is loaded.  Per
+// tile, a wave's accumulation is the contract's k-step order, hi then lo.
+constexpr int WIDE_RES = 16;  // k-steps of one range held in LDS
+constexpr int WIDE_RES_WGS = 512;  // workgroups: two per compute unit
+
+inline int wide_res_tpw(long tiles) { return (int)((tiles + 8L * (WIDE_RES_WGS / 8) - 1) / (8L * (WIDE_RES_WGS / 8))); }
+
+template <int RT>
+__global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
+  constexpr int NT = 2, NTC = 32;
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][WIDE_RES][NTC][32];  // [hi/lo][k-step][column]
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int j = blockIdx.x % GEMM_WAVES, p = blockIdx.x / GEMM_WAVES, P = gridDim.x / GEMM_WAVES;
+  const int ks = a.K >> 5;  // = GEMM_WAVES * WIDE_RES
+  const int s0 = j * WIDE_RES;
+  const int n_out = (a.M + ROWS - 1) / ROWS;
+  const long T = (long)RT * n_out;
+  const int tpw = (int)((T + 8L * P - 1) / (8L * P));
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+
+  if (a.wide_rms && blockIdx.x == 0) {
+    __shared__ float inv[NTC];
+    RmsPre<NT> rp;
+    rms_preload<NT>(a, rp);
+    rms_finish<NT>(a, rp, inv);
+    __syncthreads();
+    if (tid < NTC) a.wide_rms[tid] = inv[tid];
+  }
+
+  // the wave's i-th tile: its weights at k-step s0 (nullptr past the last tile)
+  auto tile_w = [&](int i) -> const bf16_t* {
+    const long t = (long)p * GEMM_WAVES + wave + (long)i * 8 * P;
+    if (i >= tpw || t >= T) return nullptr;
+    const long wt = (RT == 2 && t >= n_out) ? t - n_out + a.gate_off / ROWS : t;
+    return a.W + (wt * ks + s0) * 512 + lane * 8;
+  };
+
+  // (branches on tile validity are wave-uniform, so the loads stay in
+  // straight-line code and only wait for their own k-step)
+  u32x4 wr[WIDE_RES];
+  if (const bf16_t* w = tile_w(0)) {
+#pragma unroll
+    for (int q = 0; q < WIDE_RES; ++q) wr[q] = ldw16<true>(w + (long)q * 512);
+  } else {
+#pragma unroll
+    for (int q = 0; q < WIDE_RES; ++q) wr[q] = zero;
+  }
+  // the range's activation slice: piece i = tid + 512 u is 16 bytes of plane
+  // i >> 11, k-step (i >> 7) & 15, column (i >> 2) & 31, part i & 3
+#pragma unroll
+  for (int u = 0; u < 2 * WIDE_RES * NTC * 4 / 512; ++u) {
+    const int i = tid + 512 * u;
+    const int part = i & 3, c = (i >> 2) & 31, q = (i >> 7) & 15, pl = i >> 11;
+    const u32x4 v = ld16(a.X + (pl ? a.x_lo : 0) + (long)min(c, a.B - 1) * a.ldx + (s0 + q) * 32 + part * 8);
+    *reinterpret_cast<u32x4*>(&xs[pl][q][c][xs_chunk(c, part) * 8]) = c < a.B ? v : zero;
+  }
+  __syncthreads();
+
+  auto mul = [&](int q, f32x4 (&acc)[NT]) {
+    const bf16x8 w8 = __builtin_bit_cast(bf16x8, wr[q]);
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[0][q][ct * 16 + r16][xs_chunk(r16, g4) * 8]);
+      const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[1][q][ct * 16 + r16][xs_chunk(r16, g4) * 8]);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh), acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl), acc[ct], 0, 0, 0);
+    }
+  };
+
+  for (int i = 0; i < tpw; ++i) {
+    const long t = (long)p * GEMM_WAVES + wave + (long)i * 8 * P;
+    const bf16_t* wn = tile_w(i + 1);
+    f32x4 acc[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (wn) {
+#pragma unroll
+      for (int q = 0; q < WIDE_RES; ++q) {
+        mul(q, acc);
+        wr[q] = ldw16<true>(wn + (long)q * 512);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < WIDE_RES; ++q) mul(q, acc);
+    }
+    // p_j of tile t: [t][j][ct][q][lane]
+    if (t < T) {
+      float* Pp = a.split_part + (t * GEMM_WAVES + j) * (NT * 256) + lane;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Pp[ct * 256 + q * 64] = acc[ct][q];
+    }
   }
 }
 
@@ -764,7 +873,14 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
     const long groups = (wide_tiles(EPI, a.M) + GEMM_WAVES - 1) / GEMM_WAVES;
     GemmArgs w = a;
     if (EPI == EPI_RESID) w.wide_rms = nullptr;  // no normalised input
-    hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, w);
+    if ((a.K >> 5) == GEMM_WAVES * WIDE_RES) {
+      const long T = wide_tiles(EPI, a.M);
+      const long P = (T + 8L * wide_res_tpw(T) - 1) / (8L * wide_res_tpw(T));
+      hipLaunchKernelGGL((gemm_wide_res_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(P * GEMM_WAVES), dim3(512), 0, s, w);
+    } else {
+      hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s,
+                         w);
+    }
     hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, w);
   } else if (a.B > 16) {
     if (a.w_keep) hipLaunchKernelGGL((gemm_halves_kernel<EPI, false>), dim3(tiles, 2), dim3(512), 0, s, a);
