@@ -33,6 +33,18 @@ encoding; depformer codebooks 0-7 are the agent rows, 8-15 predict the user
 stream; argmax ties go to the lowest index; forced tokens replace the model's
 choice but the model's own predictions are still returned.
 
+Acoustic delay and embedding-form prefill (the recipe's interruption-latency
+table: an 80 ms frame plus an 80 ms acoustic delay; its prompt injection:
+voice embedding rows, silence frames and persona tokens are assembled into
+prefill embeddings).  With a delay of D frames, codebooks 1-7 of both audio
+streams run D ticks behind the text row and codebook 0: the column's user
+rows 10-16 and the forced choices of agent rows 2-8 come from the frame D
+ticks earlier (the initial audio token / no force before the first), and the
+agent frame f is complete at tick f + D (codebook 0 chosen at tick f, 1-7 at
+tick f + D).  An embedding-form prefill frame supplies the temporal input x
+itself, in place of the 17-way gather-sum, with the same per-row forced
+choices as a token frame.
+
 Arithmetic: weights are the exact bf16 values upcast to `dtype` (fp32 by
 default, fp64 for the shadow run); everything else is `dtype`, except the RoPE
 angle, which is fp64 with cos/sin cast to `dtype`.  Slots are processed one
@@ -131,7 +143,11 @@ class _Slot:
     def reset(self, dm):
         self.pos = 0
         self.prev = np.array([dm.text_card] + [dm.audio_card] * 8, np.int64)
-        self.queue = []
+        self.queue = []        # prefill frames: dict(force=[9], user=[8] | None, x=[d] | None)
+        self.ticks = 0         # ticks since the last reset
+        self.user_hist = []    # frame-aligned user frames of past ticks (None: none given)
+        self.force_hist = []   # frame-aligned forced agent rows of past ticks (-1: free)
+        self.chosen_hist = []  # chosen agent rows of past ticks
         self.live = False      # True after the first free-running tick
         self.ticked = False    # True after any tick since the last reset
         self.K[...] = 0
@@ -158,6 +174,7 @@ class Oracle:
         self._cache = {} if (cache_weights if cache_weights is not None else total < 50_000_000) else None
         self.slots = [_Slot(dims, self.W, self.dt) for _ in range(self.B)]
         self.taps = {}
+        self.delay = 0
 
     def _store(self, v):
         """Value as kept in a key/value cache."""
@@ -209,7 +226,28 @@ class Oracle:
         if st.live:
             raise RuntimeError("prefill on a live slot")
         for f in np.asarray(frames, np.int64).reshape(-1, 17):
-            st.queue.append(f.copy())
+            st.queue.append(dict(force=f[:9].copy(), user=f[9:].copy(), x=None))
+
+    def prefill_embed(self, s, x, force=None):
+        """Queue embedding-form prefill frames for slot s: x [n, d] is that
+        tick's temporal input (replacing the gather-sum); force [n, 9] the
+        tokens to choose for the text and agent rows or -1 (default all -1)."""
+        st = self.slots[s]
+        if st.live:
+            raise RuntimeError("prefill on a live slot")
+        x = np.asarray(x).reshape(-1, self.dm.d)
+        force = np.full((len(x), 9), -1, np.int64) if force is None else np.asarray(force, np.int64).reshape(-1, 9)
+        for xi, fi in zip(x, force):
+            st.queue.append(dict(force=fi.copy(), user=None, x=xi.astype(self.dt)))
+
+    def set_acoustic_delay(self, frames):
+        """Delay of audio codebooks 1-7 behind the text row and codebook 0,
+        in frames; only before any slot has ticked."""
+        if any(st.ticked for st in self.slots):
+            raise RuntimeError("delay change after a tick")
+        if not 0 <= int(frames) <= 4:
+            raise ValueError("delay outside 0..4")
+        self.delay = int(frames)
 
     # ------------------------------------------------------------ the tick
     def step(self, user_codes):
@@ -223,38 +261,79 @@ class Oracle:
         tokens = np.zeros((self.B, 9), np.int64)
         user_pred = np.zeros((self.B, dm.dep_q - 8), np.int64)
         chosen = np.zeros((self.B, 9), np.int64)
+        agent_frame = np.zeros((self.B, 8), np.int64)
+        agent_frame_valid = np.zeros(self.B, bool)
         for b in range(self.B):
             st = self.slots[b]
-            forced = st.queue.pop(0) if st.queue else None
-            if forced is None:
+            frame = st.queue.pop(0) if st.queue else None
+            if frame is None:
                 st.live = True
-            r = self._tick_slot(st, user_codes[b], forced)
+            col, forced, x = self._column(st, user_codes[b], frame)
+            r = self._tick_slot(st, col, forced, x)
             hidden[:, b] = r["hidden"]
             text_logits[b] = r["text_logits"]
             dep_logits[b] = r["dep_logits"]
             tokens[b] = r["tokens"]
             user_pred[b] = r["user_pred"]
             chosen[b] = r["chosen"]
+            agent_frame[b], agent_frame_valid[b] = self._agent_frame(st, r["chosen"][1:])
         self.taps = dict(hidden=hidden, text_logits=text_logits, dep_logits=dep_logits,
-                         user_pred=user_pred, chosen=chosen)
+                         user_pred=user_pred, chosen=chosen, agent_frame=agent_frame,
+                         agent_frame_valid=agent_frame_valid)
         return tokens
 
-    def _tick_slot(self, st, user, forced):
+    def _column(self, st, user, frame):
+        """This tick's column, forced choices (-1 free) and given input x.
+
+        The frame-aligned user frame and forced agent row of this tick enter
+        the column for the text row and codebook 0 now, and for codebooks
+        1-7 D ticks later."""
+        A, D = self.dm.audio_card, self.delay
+        if frame is None:
+            u_now, f_now, x = np.array(user, np.int64), np.full(9, -1, np.int64), None
+        else:
+            u_now, f_now, x = frame["user"], frame["force"], frame["x"]
+        u_old = st.user_hist[-D] if D and len(st.user_hist) >= D else (u_now if not D else None)
+        f_old = st.force_hist[-D] if D and len(st.force_hist) >= D else (f_now[1:] if not D else None)
+        user_rows = np.full(8, A, np.int64)
+        if u_now is not None:
+            user_rows[0] = u_now[0]
+        if u_old is not None:
+            user_rows[1:] = u_old[1:]
+        forced = f_now.copy()
+        forced[2:] = f_old[1:] if f_old is not None else -1
+        st.user_hist = (st.user_hist + [u_now])[-max(D, 1):]
+        st.force_hist = (st.force_hist + [f_now[1:].copy()])[-max(D, 1):]
+        col = np.concatenate([st.prev, user_rows])
+        return col, (forced if (forced >= 0).any() else None), x
+
+    def _agent_frame(self, st, chosen_agent):
+        """The agent frame completed by this tick: codebook 0 chosen D ticks
+        ago, codebooks 1-7 chosen now; (frame, valid)."""
+        D = self.delay
+        st.chosen_hist = (st.chosen_hist + [np.asarray(chosen_agent, np.int64).copy()])[-(D + 1):]
+        st.ticks += 1
+        if st.ticks <= D:
+            return np.zeros(8, np.int64), False
+        return np.concatenate([st.chosen_hist[0][:1], st.chosen_hist[-1][1:]]), True
+
+    def _tick_slot(self, st, col, forced, x_given=None):
+        """One slot's tick.  col: the 17-row column (prev text+agent tokens,
+        then the user rows); forced: 9 choices (-1 free) or None; x_given:
+        an embedding-form frame's temporal input, or None."""
         dm, dt, W = self.dm, self.dt, self.W
         d, H, Dh, F = dm.d, dm.n_heads, dm.head_dim, dm.ffn
         eps = dm.norm_eps
 
-        # 1. column: prev text+agent tokens (rows 0-8) then the user frame
-        #    (rows 9-16); a forced frame supplies the user rows itself.
-        if forced is not None:
-            user = forced[USER_ROWS]
-        col = np.concatenate([st.prev, np.asarray(user, np.int64)])
-
-        # 2. embedding: sum of the 17 row embeddings, in row order.
-        x = np.zeros(d, dt)
-        x += self.row("emb.text", col[0])
-        for r in range(1, 17):
-            x += self.row(f"emb.audio.{r - 1}", col[r])
+        # 2. embedding: sum of the 17 row embeddings, in row order, unless
+        #    the frame gives the input itself.
+        if x_given is not None:
+            x = np.array(x_given, dt)
+        else:
+            x = np.zeros(d, dt)
+            x += self.row("emb.text", col[0])
+            for r in range(1, 17):
+                x += self.row(f"emb.audio.{r - 1}", col[r])
         hidden = [x.copy()]
 
         # 3. temporal transformer, one frame at absolute position pos.

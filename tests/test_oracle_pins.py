@@ -586,3 +586,132 @@ def test_state_rules(tiny_weights):
     o.slot_reset(0)
     o.ring_fill(0, k, v)
     o.prefill_forced(0, teacher_frames(2))
+
+
+# ------------------------------------------------------------------ acoustic delay, embedding-form prefill
+
+def test_acoustic_delay_column_layout(tiny_weights):
+    """Delay D: the column's user rows 10-16 (codebooks 1-7) carry the frame
+    D ticks back, the initial audio token before the first; row 9 (codebook
+    0) and the text row are not delayed (recipe: an 80 ms acoustic delay
+    behind the 80 ms frame)."""
+    w = _digit_tables(tiny_weights, DM)
+    A = DM.audio_card
+    codes = synth.user_codes(4, 4)
+    for D in (1, 2):
+        o = Oracle(DM, w, 1, W)
+        o.set_acoustic_delay(D)
+        for t in range(4):
+            o.step(codes[t:t + 1])
+            col = _read_column(o.taps["hidden"][0, 0])
+            assert col[9] == codes[t, 0]
+            want = list(codes[t - D, 1:]) if t >= D else [A] * 7
+            np.testing.assert_array_equal(col[10:17], want)
+
+
+def test_acoustic_delay_forced_agent_rows(tiny_weights):
+    """With D = 1 a forced frame forces the text row and codebook 0 on its
+    own tick and codebooks 1-7 one tick later; on tick 0 those are free."""
+    o = Oracle(DM, tiny_weights, 1, W)
+    o.set_acoustic_delay(1)
+    f = teacher_frames(3, seed=9)
+    o.prefill_forced(0, f)
+    for t in range(3):
+        tok = o.step(np.zeros((1, 8), np.int64))
+        ch = o.taps["chosen"][0]
+        assert ch[0] == f[t, 0] and ch[1] == f[t, 1]
+        np.testing.assert_array_equal(ch[2:9], f[t - 1, 2:9] if t else tok[0, 2:9])
+    # first free tick: the last forced frame's codebooks 1-7 still apply
+    o.step(np.zeros((1, 8), np.int64))
+    np.testing.assert_array_equal(o.taps["chosen"][0, 2:9], f[2, 2:9])
+
+
+def test_acoustic_delay_equals_shifted_inputs(tiny_weights):
+    """A delayed run is the undelayed model fed the shifted user frames:
+    bit-identical hidden states, logits and tokens."""
+    A = DM.audio_card
+    codes = synth.user_codes(6, 5)
+    o1 = Oracle(DM, tiny_weights, 1, W)
+    o1.set_acoustic_delay(1)
+    o0 = Oracle(DM, tiny_weights, 1, W)
+    for t in range(5):
+        shifted = np.concatenate([codes[t, :1], codes[t - 1, 1:] if t else np.full(7, A)])
+        t1 = o1.step(codes[t:t + 1])
+        t0 = o0.step(shifted[None])
+        np.testing.assert_array_equal(t1, t0)
+        for k in ("hidden", "text_logits", "dep_logits", "chosen"):
+            np.testing.assert_array_equal(o1.taps[k], o0.taps[k])
+
+
+def test_agent_frames_are_frame_aligned(tiny_weights):
+    """Agent frame f = codebook 0 chosen at tick f, codebooks 1-7 chosen at
+    tick f + D; none before tick D; with D = 0 the tick's own choice."""
+    codes = synth.user_codes(8, 5)
+    for D in (0, 1, 2):
+        o = Oracle(DM, tiny_weights, 1, W)
+        o.set_acoustic_delay(D)
+        chosen = []
+        for t in range(5):
+            o.step(codes[t:t + 1])
+            chosen.append(o.taps["chosen"][0, 1:].copy())
+            assert bool(o.taps["agent_frame_valid"][0]) == (t >= D)
+            if t >= D:
+                np.testing.assert_array_equal(o.taps["agent_frame"][0, :1], chosen[t - D][:1])
+                np.testing.assert_array_equal(o.taps["agent_frame"][0, 1:], chosen[t][1:])
+
+
+def test_embedding_frame_replaces_the_gather_sum(tiny_weights):
+    """An embedding-form prefill frame's x is the tick's input itself:
+    with digit tables, x = the digits of a column reproduces the token frame
+    bit for bit, and x = 0 leaves no trace of the column."""
+    w = _digit_tables(tiny_weights, DM)
+    f = teacher_frames(2, seed=13)
+    ot_ = Oracle(DM, w, 1, W)
+    ot_.prefill_forced(0, f)
+    oe = Oracle(DM, w, 1, W)
+    for t in range(2):
+        ot_.step(np.zeros((1, 8), np.int64))
+        x = ot_.taps["hidden"][0, 0].copy()     # integer digits: exact in fp32
+        col = _read_column(x)
+        np.testing.assert_array_equal(col[9:], f[t, 9:])
+        oe.prefill_embed(0, x[None], f[t:t + 1, :9])
+        tok = oe.step(np.zeros((1, 8), np.int64))
+        for k in ("hidden", "text_logits", "dep_logits", "chosen"):
+            np.testing.assert_array_equal(oe.taps[k], ot_.taps[k])
+    oz = Oracle(DM, w, 1, W)
+    oz.prefill_embed(0, np.zeros((1, DM.d), np.float32))
+    oz.step(np.full((1, 8), 5))
+    assert not oz.taps["hidden"][0, 0].any()
+    # a zero input stays zero through every temporal layer (no biases)
+    assert not oz.taps["hidden"].any()
+
+
+def test_embedding_frame_forces_and_user_history(tiny_weights):
+    """Forced choices of an embedding frame apply as for a token frame
+    (-1 free); with D = 1 the frame gives no user codes, so the next
+    column's delayed user rows hold the initial audio token."""
+    w = _digit_tables(tiny_weights, DM)
+    o = Oracle(DM, w, 1, W)
+    o.set_acoustic_delay(1)
+    force = np.array([[7, 1, 2, -1, -1, -1, -1, -1, -1]])
+    o.prefill_embed(0, np.ones((1, DM.d), np.float32), force)
+    tok = o.step(np.zeros((1, 8), np.int64))
+    ch = o.taps["chosen"][0]
+    assert ch[0] == 7 and ch[1] == 1
+    np.testing.assert_array_equal(ch[2:], tok[0, 2:])   # codebooks 1-7: forced only a tick later
+    codes = synth.user_codes(3, 1)
+    o.step(codes)
+    col = _read_column(o.taps["hidden"][0, 0])
+    assert col[9] == codes[0, 0]
+    np.testing.assert_array_equal(col[10:], [DM.audio_card] * 7)
+    assert o.taps["chosen"][0, 2] == 2                  # the frame's codebook-1 force, one tick late
+
+
+def test_delay_rules(tiny_weights):
+    o = Oracle(DM, tiny_weights, 1, W)
+    with pytest.raises(ValueError):
+        o.set_acoustic_delay(5)
+    o.set_acoustic_delay(2)
+    o.step(np.zeros((1, 8)))
+    with pytest.raises(RuntimeError):
+        o.set_acoustic_delay(1)
