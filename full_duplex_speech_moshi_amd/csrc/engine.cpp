@@ -29,7 +29,7 @@ static_assert(DEP_WINDOW <= DEP_MAX_KEYS, "depformer attention holds at most DEP
 struct Layout {
   // byte offsets into the arena
   size_t ring, x, xa, part, q, att_part, o, m, hidden, text_logits, tamax_v, tamax_i, dep_logits, ti, to, inv_freq,
-      split_part, wide_rms, rope, att_cnt, total;
+      split_part, wide_rms, rope, att_cnt, xin, total;
   // depformer buffers, two sets: the agent codebooks of tick t+1 run beside
   // the user-stream codebooks of tick t, which keep using the other set
   size_t dkv[2], amax_v[2], amax_i[2], u[2], y[2], ya[2], dpart[2], dq[2], dout[2], dm[2];
@@ -104,6 +104,7 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   }
   L.dep_logits = take(B * Q * A * 4);
   L.ti = take(B * TI_STRIDE * 4);
+  L.xin = take((size_t)B * d * 4);
   L.to = take(B * TO_STRIDE * 4);
   L.inv_freq = take((hd / 2) * 8);
   // scratch of the large-batch GEMM path: the largest partial area of any GEMM of the tick
@@ -120,11 +121,32 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   return L;
 }
 
+// A queued prefill frame: rows 0-8 the tokens to choose (-1 free), rows
+// 9-16 the user codes; an embedding-form frame also carries the tick's
+// temporal input x (d floats) and no user codes.
+struct Frame {
+  std::array<int32_t, 17> tok;
+  std::vector<float> x;
+};
+
+using Row8 = std::array<int32_t, 8>;
+
 struct Slot {
   int64_t pos = 0;
   int32_t prev[9];
-  std::deque<std::array<int32_t, 17>> queue;
+  std::deque<Frame> queue;
   bool live = false, ticked = false;
+  // Acoustic delay D: frame-aligned user frames and forced agent rows of the
+  // last ticks (newest last; a user row of -1s = none given) feed codebooks
+  // 1-7 of the column D ticks later; the chosen agent rows of the last D + 1
+  // ticks form the completed agent frame.
+  std::deque<Row8> user_hist, force_hist, chosen_hist;
+  int64_t ticks = 0;  // ticks since the last reset
+  Row8 frame_out{};
+  bool frame_valid = false;
+  // this tick's frame-aligned user frame and forced agent row (set with the
+  // tick input, committed to the history once the tick has run)
+  Row8 tick_user{}, tick_force{};
 };
 
 thread_local std::string g_create_error;
@@ -153,6 +175,8 @@ struct pp_handle {
   bool user_pending = false;  // PH_USER of the last tick not launched yet
   int32_t* ti_host = nullptr;
   int32_t* to_host = nullptr;
+  float* xin_host = nullptr;  // [B][d] given temporal inputs of embedding-form frames
+  int delay = 0;              // acoustic delay of codebooks 1-7, frames
   std::vector<Slot> slots;
   std::vector<std::function<void(hipStream_t)>> timed[6];  // per layer
   double timed_bytes[6] = {0, 0, 0, 0, 0, 0};
@@ -189,6 +213,12 @@ void reset_slot(const pp_dims& dm, Slot& s) {
   s.queue.clear();
   s.live = false;
   s.ticked = false;
+  s.user_hist.clear();
+  s.force_hist.clear();
+  s.chosen_hist.clear();
+  s.ticks = 0;
+  s.frame_out.fill(0);
+  s.frame_valid = false;
 }
 
 enum Phase { PH_TEMPORAL = 0, PH_AGENT = 1, PH_USER = 2 };
@@ -215,6 +245,7 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
     ea.d = d;
     ea.emb_text = w.emb_text;
     ea.emb_audio = w.emb_audio;
+    ea.xin = h->at<float>(L.xin);
     ea.text_rows = Vt + 1;
     ea.audio_rows = A + 1;
     ea.alpha = w.attn_norm;
@@ -426,8 +457,8 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
   };
 
   // All 16 projections run here: z (the normalised final hidden state) is
-  // overwritten by the next tick's temporal stack, which may run alongside
-  // this tick's user-stream codebooks.
+  // overwritten by the next tick's temporal stack, which runs before this
+  // tick's user-stream codebooks.
   if (phase == PH_AGENT) {
     in_proj(0, Q);
     launch_finish(fa, s);
@@ -578,17 +609,63 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
   }
 }
 
-// Fill the tick-input staging buffer from slot state; frames[b] = forced
-// frame consumed this tick or nullptr.
-void build_tick_input(pp_handle* h, const int32_t* user_codes, const std::array<int32_t, 17>** frames) {
+// Fill the tick-input staging buffer from slot state; frames[b] = prefill
+// frame consumed this tick or nullptr.  Reads the delay history without
+// changing it.  Text row and codebook 0 take this tick's frame; codebooks
+// 1-7 (user rows 10-16 and the forced choices of agent rows 2-8) take the
+// frame D ticks back: the initial audio token and no force before the first.
+void build_tick_input(pp_handle* h, const int32_t* user_codes, const Frame** frames) {
+  const int A = h->dm.audio_card, D = h->delay;
   for (int b = 0; b < h->B; ++b) {
     int32_t* t = h->ti_host + b * TI_STRIDE;
-    const Slot& s = h->slots[b];
+    Slot& s = h->slots[b];
     t[TI_POS] = (int32_t)s.pos;
     for (int i = 0; i < 9; ++i) t[TI_COL + i] = s.prev[i];
-    const std::array<int32_t, 17>* f = frames ? frames[b] : nullptr;
-    for (int i = 0; i < 8; ++i) t[TI_COL + 9 + i] = f ? (*f)[9 + i] : (user_codes ? user_codes[b * 8 + i] : 0);
-    for (int i = 0; i < 9; ++i) t[TI_FORCE + i] = f ? (*f)[i] : -1;
+    const Frame* f = frames ? frames[b] : nullptr;
+    const bool has_x = f && !f->x.empty();
+    int32_t force_text = -1;
+    for (int i = 0; i < 8; ++i) {
+      s.tick_user[i] = has_x ? -1 : f ? f->tok[9 + i] : (user_codes ? user_codes[b * 8 + i] : 0);
+      s.tick_force[i] = f ? f->tok[1 + i] : -1;
+    }
+    if (f) force_text = f->tok[0];
+    const Row8* u_old = nullptr;
+    const Row8* f_old = nullptr;
+    if (D == 0) {
+      u_old = &s.tick_user;
+      f_old = &s.tick_force;
+    } else {
+      if ((int)s.user_hist.size() >= D) u_old = &s.user_hist[s.user_hist.size() - D];
+      if ((int)s.force_hist.size() >= D) f_old = &s.force_hist[s.force_hist.size() - D];
+    }
+    if (u_old && (*u_old)[0] < 0) u_old = nullptr;  // that tick gave no user codes
+    t[TI_COL + 9] = s.tick_user[0] >= 0 ? s.tick_user[0] : A;
+    for (int i = 1; i < 8; ++i) t[TI_COL + 9 + i] = u_old ? (*u_old)[i] : A;
+    t[TI_FORCE] = force_text;
+    t[TI_FORCE + 1] = s.tick_force[0];
+    for (int i = 1; i < 8; ++i) t[TI_FORCE + 1 + i] = f_old ? (*f_old)[i] : -1;
+    t[TI_XIN] = has_x ? 1 : 0;
+  }
+}
+
+// After a tick has run: this tick's frame-aligned rows join the delay
+// history, and the agent frame completed by it (codebook 0 chosen D ticks
+// ago, codebooks 1-7 chosen now) is kept for pp_agent_frames.
+void commit_history(pp_handle* h, Slot& s, const int32_t* chosen_agent) {
+  const size_t keep = (size_t)std::max(h->delay, 1);
+  Row8 c;
+  std::memcpy(c.data(), chosen_agent, sizeof c);
+  s.user_hist.push_back(s.tick_user);
+  s.force_hist.push_back(s.tick_force);
+  s.chosen_hist.push_back(c);
+  while (s.user_hist.size() > keep) s.user_hist.pop_front();
+  while (s.force_hist.size() > keep) s.force_hist.pop_front();
+  while (s.chosen_hist.size() > (size_t)h->delay + 1) s.chosen_hist.pop_front();
+  s.ticks += 1;
+  s.frame_valid = s.ticks > h->delay;
+  if (s.frame_valid) {
+    s.frame_out[0] = s.chosen_hist.front()[0];
+    for (int i = 1; i < 8; ++i) s.frame_out[i] = s.chosen_hist.back()[i];
   }
 }
 
@@ -684,7 +761,11 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
     return bail("hipHostMalloc", e);
   if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->to_host), B * TO_STRIDE * 4, hipHostMallocDefault)) != hipSuccess)
     return bail("hipHostMalloc", e);
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->xin_host), (size_t)B * dims->d * 4, hipHostMallocDefault)) !=
+      hipSuccess)
+    return bail("hipHostMalloc", e);
   std::memset(h->ti_host, 0, B * TI_STRIDE * 4);
+  std::memset(h->xin_host, 0, (size_t)B * dims->d * 4);
   std::memset(h->to_host, 0, B * TO_STRIDE * 4);
 
   // RoPE frequencies base^(-2i/head_dim), fp64 host math.
@@ -742,9 +823,59 @@ int pp_prefill_forced(pp_handle* h, int slot, const int32_t* frames, int n) {
       if (f[r] < 0 || f[r] >= A) return h->fail(PP_EINVAL, "frame %d: user code %d out of range", i, f[r]);
   }
   for (int i = 0; i < n; ++i) {
-    std::array<int32_t, 17> a;
-    std::memcpy(a.data(), frames + i * 17, sizeof a);
-    s.queue.push_back(a);
+    Frame fr;
+    std::memcpy(fr.tok.data(), frames + i * 17, sizeof fr.tok);
+    s.queue.push_back(std::move(fr));
+  }
+  return PP_OK;
+}
+
+int pp_prefill_embed(pp_handle* h, int slot, const float* x, const int32_t* force, int n) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (slot < 0 || slot >= h->B) return h->fail(PP_EINVAL, "slot %d out of [0,%d)", slot, h->B);
+  if (n < 0 || (n > 0 && !x)) return h->fail(PP_EINVAL, "bad frame count or NULL inputs");
+  Slot& s = h->slots[slot];
+  if (s.live) return h->fail(PP_EBUSY, "slot %d is free-running; persona and voice are fixed at open", slot);
+  if (s.queue.size() + (size_t)n > PP_MAX_QUEUE) return h->fail(PP_ENOSPC, "forced queue full");
+  const int Vt = h->dm.text_card, A = h->dm.audio_card, d = h->dm.d;
+  for (int i = 0; i < n; ++i) {
+    if (force) {
+      const int32_t* f = force + i * 9;
+      if (f[0] < -1 || f[0] >= Vt) return h->fail(PP_EINVAL, "frame %d: text token %d out of range", i, f[0]);
+      for (int r = 1; r < 9; ++r)
+        if (f[r] < -1 || f[r] >= A) return h->fail(PP_EINVAL, "frame %d: agent code %d out of range", i, f[r]);
+    }
+    for (int j = 0; j < d; ++j)
+      if (!std::isfinite(x[(size_t)i * d + j])) return h->fail(PP_EINVAL, "frame %d: input %d not finite", i, j);
+  }
+  for (int i = 0; i < n; ++i) {
+    Frame fr;
+    fr.tok.fill(0);
+    for (int r = 0; r < 9; ++r) fr.tok[r] = force ? force[i * 9 + r] : -1;
+    fr.x.assign(x + (size_t)i * d, x + (size_t)(i + 1) * d);
+    s.queue.push_back(std::move(fr));
+  }
+  return PP_OK;
+}
+
+int pp_set_acoustic_delay(pp_handle* h, int frames) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (frames < 0 || frames > PP_MAX_DELAY) return h->fail(PP_EINVAL, "delay %d outside [0,%d]", frames, PP_MAX_DELAY);
+  for (int b = 0; b < h->B; ++b)
+    if (h->slots[b].ticked) return h->fail(PP_EBUSY, "slot %d has ticked since its reset", b);
+  h->delay = frames;
+  return PP_OK;
+}
+
+int pp_agent_frames(const pp_handle* h, int32_t* frames, int32_t* valid) {
+  if (!h || !frames || !valid) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  for (int b = 0; b < h->B; ++b) {
+    const Slot& s = h->slots[b];
+    valid[b] = s.frame_valid ? 1 : 0;
+    for (int i = 0; i < 8; ++i) frames[b * 8 + i] = s.frame_valid ? s.frame_out[i] : 0;
   }
   return PP_OK;
 }
@@ -762,12 +893,22 @@ int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
       if (c < 0 || c >= A) return h->fail(PP_EINVAL, "slot %d user code %d out of range", b, c);
     }
   }
-  std::vector<const std::array<int32_t, 17>*> frames(h->B, nullptr);
+  std::vector<const Frame*> frames(h->B, nullptr);
+  bool any_x = false;
   for (int b = 0; b < h->B; ++b)
-    if (!h->slots[b].queue.empty()) frames[b] = &h->slots[b].queue.front();
+    if (!h->slots[b].queue.empty()) {
+      frames[b] = &h->slots[b].queue.front();
+      if (!frames[b]->x.empty()) {
+        std::memcpy(h->xin_host + (size_t)b * h->dm.d, frames[b]->x.data(), (size_t)h->dm.d * 4);
+        any_x = true;
+      }
+    }
   build_tick_input(h, user_codes, frames.data());
   HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.ti), h->ti_host, h->B * TI_STRIDE * 4, hipMemcpyHostToDevice,
                                 h->stream));
+  if (any_x)
+    HIP_OR_FAIL(h, hipMemcpyAsync(h->at<float>(h->lay.xin), h->xin_host, (size_t)h->B * h->dm.d * 4,
+                                  hipMemcpyHostToDevice, h->stream));
   HIP_OR_FAIL(h, launch_tick(h));
   // the agent outputs only (the user-stream codebooks may still be writing theirs)
   HIP_OR_FAIL(h, hipMemcpy2DAsync(h->to_host + TO_PRED, TO_STRIDE * 4, h->at<int>(h->lay.to) + TO_PRED, TO_STRIDE * 4,
@@ -782,6 +923,7 @@ int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
       tokens[b * 9 + i] = o[TO_PRED + i];
       s.prev[i] = o[TO_CHOSEN + i];
     }
+    commit_history(h, s, o + TO_CHOSEN + 1);
     if (frames[b]) s.queue.pop_front();
     else s.live = true;
     s.ticked = true;
@@ -932,6 +1074,7 @@ void pp_destroy(pp_handle* h) {
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->cap) (void)hipStreamDestroy(h->cap);
   if (h->ti_host) (void)hipHostFree(h->ti_host);
+  if (h->xin_host) (void)hipHostFree(h->xin_host);
   if (h->to_host) (void)hipHostFree(h->to_host);
   delete h;
 }

@@ -12,6 +12,7 @@ enum {
   TI_POS = 0,        // absolute position of this tick
   TI_COL = 1,        // 17 column rows: [1..9] previous chosen text+agent, [10..17] user codes
   TI_FORCE = 18,     // 9 forced choices for text, agent 0..7 (-1 = free)
+  TI_XIN = 27,       // 1: the temporal input is the given row of EmbedArgs::xin, not the gather-sum
   TI_STRIDE = 32
 };
 
@@ -117,6 +118,7 @@ struct EmbedArgs {
   const int* ti; int B, d;
   const double* inv_freq; int head_dim; float* rope;  // RoPE table of the tick (see GemmArgs::rope)
   const bf16_t* emb_text; const bf16_t* emb_audio; int text_rows, audio_rows;
+  const float* xin;  // [B][d] given temporal inputs (embedding-form prefill frames), read where TI_XIN is set
   const float* alpha;   // first attention-norm alpha
   float* x; bf16_t* xa; long xa_lo; float* part; float* tap;
 };

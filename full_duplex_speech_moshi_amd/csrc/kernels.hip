@@ -1126,24 +1126,33 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   const int g8 = blockIdx.x * blockDim.x + threadIdx.x;  // 8-feature group
   if (g8 >= a.d / 8) return;                              // d % 16 == 0: pairs stay whole
   const int* t = a.ti + b * TI_STRIDE + TI_COL;
-  u32x4 v[17];
-#pragma unroll
-  for (int r = 0; r < 17; ++r) {
-    const bf16_t* e = (r == 0) ? a.emb_text + (long)t[0] * a.d
-                               : a.emb_audio + ((long)(r - 1) * a.audio_rows + t[r]) * a.d;
-    v[r] = ld16(e + g8 * 8);
-  }
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int r = 0; r < 17; ++r) {
-    float f[8];
-    unpack8(v[r], f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += f[i];
-  }
   const long off = (long)b * a.d + g8 * 8;
+  float acc[8];
+  if (a.xin && a.ti[b * TI_STRIDE + TI_XIN]) {
+    // embedding-form prefill frame: the given input replaces the gather-sum
+    // (the flag is per slot, so the branch is uniform over the workgroup)
+    const float4 x0 = *reinterpret_cast<const float4*>(a.xin + off);
+    const float4 x1 = *reinterpret_cast<const float4*>(a.xin + off + 4);
+    acc[0] = x0.x; acc[1] = x0.y; acc[2] = x0.z; acc[3] = x0.w;
+    acc[4] = x1.x; acc[5] = x1.y; acc[6] = x1.z; acc[7] = x1.w;
+  } else {
+    u32x4 v[17];
+#pragma unroll
+    for (int r = 0; r < 17; ++r) {
+      const bf16_t* e = (r == 0) ? a.emb_text + (long)t[0] * a.d
+                                 : a.emb_audio + ((long)(r - 1) * a.audio_rows + t[r]) * a.d;
+      v[r] = ld16(e + g8 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 17; ++r) {
+      float f[8];
+      unpack8(v[r], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

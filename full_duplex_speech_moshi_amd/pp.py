@@ -17,9 +17,10 @@ PP_OK, PP_EINVAL, PP_EBUSY, PP_ENOSPC, PP_EDEVICE = 0, -1, -2, -3, -4
 PP_MAX_BATCH = 32
 TO_STRIDE = 32
 
-EXPORTS = ("pp_arena_bytes", "pp_create", "pp_prefill_forced", "pp_step", "pp_slot_reset",
-           "pp_ring_fill", "pp_taps", "pp_time_kernel", "pp_time_graph", "pp_destroy",
-           "pp_last_error", "pp_packed_elems", "pp_pack_matrix")
+EXPORTS = ("pp_arena_bytes", "pp_create", "pp_prefill_forced", "pp_prefill_embed", "pp_step",
+           "pp_set_acoustic_delay", "pp_agent_frames", "pp_slot_reset", "pp_ring_fill", "pp_taps",
+           "pp_time_kernel", "pp_time_graph", "pp_destroy", "pp_last_error", "pp_packed_elems",
+           "pp_pack_matrix")
 
 KERNELS = {"qkv": 0, "attention": 1, "out_proj": 2, "gate_up": 3, "down": 4, "text_head": 5}
 
@@ -68,6 +69,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pp_create.argtypes = [ctypes.POINTER(PPDims), I, I, ctypes.POINTER(PPWeights), P, SZ, P,
                               ctypes.POINTER(P)]
     lib.pp_prefill_forced.argtypes = [P, I, P, I]
+    lib.pp_prefill_embed.argtypes = [P, I, P, P, I]
+    lib.pp_set_acoustic_delay.argtypes = [P, I]
+    lib.pp_agent_frames.argtypes = [P, P, P]
     lib.pp_step.argtypes = [P, P, P]
     lib.pp_slot_reset.argtypes = [P, I]
     lib.pp_ring_fill.argtypes = [P, I, I, P, P]
@@ -127,6 +131,24 @@ def pp_create(dims: PPDims, B: int, window: int, weights: PPWeights, arena_ptr: 
 def pp_prefill_forced(h: int, slot: int, frames) -> None:
     f = np.ascontiguousarray(frames, dtype=np.int32).reshape(-1, 17)
     _check(load_library().pp_prefill_forced(h, slot, f.ctypes.data, f.shape[0]), h)
+
+
+def pp_prefill_embed(h: int, slot: int, x, force=None) -> None:
+    xv = np.ascontiguousarray(x, dtype=np.float32)
+    n = xv.shape[0] if xv.ndim == 2 else 1
+    f = None if force is None else np.ascontiguousarray(force, dtype=np.int32).reshape(n, 9)
+    _check(load_library().pp_prefill_embed(h, slot, xv.ctypes.data, None if f is None else f.ctypes.data, n), h)
+
+
+def pp_set_acoustic_delay(h: int, frames: int) -> None:
+    _check(load_library().pp_set_acoustic_delay(h, frames), h)
+
+
+def pp_agent_frames(h: int, B: int):
+    frames = np.empty((B, 8), np.int32)
+    valid = np.empty(B, np.int32)
+    _check(load_library().pp_agent_frames(h, frames.ctypes.data, valid.ctypes.data), h)
+    return frames, valid.astype(bool)
 
 
 def pp_step(h: int, user_codes, B: int) -> np.ndarray:
@@ -267,6 +289,15 @@ class Engine:
     # thin wrappers
     def prefill_forced(self, slot, frames):
         pp_prefill_forced(self.h, slot, frames)
+
+    def prefill_embed(self, slot, x, force=None):
+        pp_prefill_embed(self.h, slot, x, force)
+
+    def set_acoustic_delay(self, frames):
+        pp_set_acoustic_delay(self.h, frames)
+
+    def agent_frames(self):
+        return pp_agent_frames(self.h, self.B)
 
     def step(self, user_codes) -> np.ndarray:
         return pp_step(self.h, user_codes, self.B)

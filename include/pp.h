@@ -58,6 +58,7 @@ extern "C" {
 #define PP_MAX_BATCH     32    /* slots per handle */
 #define PP_MAX_WINDOW    4096  /* ring frames per slot (the decode pass combines at most 16 splits of 256 keys) */
 #define PP_MAX_QUEUE     4096  /* forced frames queued per slot */
+#define PP_MAX_DELAY     4     /* acoustic delay, frames (pp_set_acoustic_delay) */
 #define PP_COLUMN_ROWS   17    /* token column: text, 8 agent, 8 user */
 
 /* Model shape.  Constraints (checked by pp_create / pp_arena_bytes):
@@ -153,8 +154,23 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w,
  * replace that slot's user_codes.  Ranges: row 0 in [-1,Vt), rows 1-8 in
  * [-1,A), rows 9-16 in [0,A).  Legal only before the slot's first
  * free-running tick (else PP_EBUSY, as persona/voice cannot change after
- * session open).  PP_ENOSPC if the queue would exceed PP_MAX_QUEUE. */
+ * session open).  PP_ENOSPC if the queue would exceed PP_MAX_QUEUE.
+ * With an acoustic delay D (pp_set_acoustic_delay) the frames are
+ * frame-aligned: rows 1 and 9 (codebook 0) and row 0 act on their own tick,
+ * rows 2-8 and 10-16 (codebooks 1-7) D ticks later. */
 int pp_prefill_forced(pp_handle* h, int slot, const int32_t* frames, int n);
+
+/* Queue n embedding-form prefill frames for `slot`, in the same queue as
+ * pp_prefill_forced (recipe "Architecture": the prompt is assembled from
+ * voice embedding rows, silence frames and persona-token embeddings; guide
+ * "Persona Voice 注入").  x: host fp32 [n][d], the temporal input of each
+ * frame's tick, which replaces the 17-row embedding gather-sum; it is copied
+ * before the call returns.  force: host int32 [n][9] (rows as rows 0-8 of a
+ * forced frame, -1 = free) or NULL for all free.  The frame gives no user
+ * codes: with a delay, the user rows that would take them hold the initial
+ * audio token.  Errors as pp_prefill_forced, and PP_EINVAL for a
+ * non-finite input. */
+int pp_prefill_embed(pp_handle* h, int slot, const float* x, const int32_t* force, int n);
 
 /* One lockstep tick for all B slots.  user_codes: host int32 [B][8] in
  * [0,A) (ignored for slots consuming a forced frame).  tokens: host int32
@@ -171,6 +187,25 @@ int pp_prefill_forced(pp_handle* h, int slot, const int32_t* frames, int n);
  * if still pending and wait for them; pp_destroy drops them.  The work and
  * its results are those of the plain sequence. */
 int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens);
+
+/* Acoustic delay (recipe, interruption latency: an 80 ms frame plus an
+ * 80 ms acoustic delay, i.e. D = 1 at 12.5 Hz): audio codebooks 1-7 of both
+ * streams run D frames behind the text row and codebook 0.  user_codes (and
+ * the user rows of forced frames) are frame-aligned: the column's row 9
+ * takes this tick's codebook 0, rows 10-16 take codebooks 1-7 of the frame
+ * given D ticks earlier (the initial audio token before the slot's first D
+ * ticks).  Forced agent rows shift the same way.  The agent rows of the
+ * column and the returned tokens stay per tick.  D in [0, PP_MAX_DELAY]
+ * (PP_EINVAL); legal only while no slot has ticked since its reset
+ * (PP_EBUSY).  Default 0. */
+int pp_set_acoustic_delay(pp_handle* h, int frames);
+
+/* The agent audio frame completed by the last pp_step, per slot: frame
+ * f = t - D gets codebook 0 chosen at tick f and codebooks 1-7 chosen at
+ * tick t (chosen = forced where forced, else predicted).  frames: host
+ * int32 [B][8]; valid: host int32 [B], 0 while the slot has ticked D times
+ * or fewer since its reset (its row is then zeros). */
+int pp_agent_frames(const pp_handle* h, int32_t* frames, int32_t* valid);
 
 /* Recycle `slot`: position 0, column back to the initial tokens
  * [Vt, A x 8], forced queue cleared, ring logically empty.  A recycled slot
@@ -201,7 +236,7 @@ int pp_taps(const pp_handle* h, pp_taps_t* out);
  * that the next tick recomputes before use, so slot state is not disturbed. */
 int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* bytes);
 
-/* Time `iters` back-to-back ticks (the three graphs of each, pipelined as in
+/* Time `iters` back-to-back ticks (the graphs of each, pipelined as in
  * pp_step) with HIP events (no host copies); *avg_ms = mean device time per
  * tick, the last tick's user-stream codebooks included.  The
  * launches recompute the tick for the current tick inputs without advancing

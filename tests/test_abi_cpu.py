@@ -75,6 +75,9 @@ def test_null_handle_calls_are_rejected(lib):
     assert lib.pp_step(None, None, None) == pp.PP_EINVAL
     assert lib.pp_slot_reset(None, 0) == pp.PP_EINVAL
     assert lib.pp_prefill_forced(None, 0, None, 0) == pp.PP_EINVAL
+    assert lib.pp_prefill_embed(None, 0, None, None, 0) == pp.PP_EINVAL
+    assert lib.pp_set_acoustic_delay(None, 1) == pp.PP_EINVAL
+    assert lib.pp_agent_frames(None, None, None) == pp.PP_EINVAL
     lib.pp_destroy(None)
 
 

@@ -273,6 +273,19 @@ def test_errors_leave_state_unchanged(tiny_weights, dev):
     with pytest.raises(pp.PPError) as ei:
         e.ring_fill(0, kb, vb)
     assert ei.value.code == pp.PP_EINVAL
+    x_bad = np.zeros((2, DM.d), np.float32)
+    x_bad[1, 5] = np.nan
+    with pytest.raises(pp.PPError) as ei:          # the whole call is rejected, frame 0 included
+        e.prefill_embed(0, x_bad)
+    assert ei.value.code == pp.PP_EINVAL
+    with pytest.raises(pp.PPError) as ei:
+        e.prefill_embed(0, np.zeros((1, DM.d), np.float32), np.full((1, 9), DM.audio_card, np.int32))
+    assert ei.value.code == pp.PP_EINVAL
+    with pytest.raises(pp.PPError) as ei:
+        e.set_acoustic_delay(5)
+    assert ei.value.code == pp.PP_EINVAL
+    fr, ok = e.agent_frames()
+    assert not ok.any()
     # nothing above changed any state: same results as an untouched handle
     np.testing.assert_array_equal(e.step(codes[0]), ref.step(codes[0]))
     with pytest.raises(pp.PPError) as ei:           # both slots now free-running
@@ -282,6 +295,170 @@ def test_errors_leave_state_unchanged(tiny_weights, dev):
     with pytest.raises(pp.PPError) as ei:
         e.ring_fill(0, kb, vb)
     assert ei.value.code == pp.PP_EBUSY
+    with pytest.raises(pp.PPError) as ei:
+        e.prefill_embed(1, np.zeros((1, DM.d), np.float32))
+    assert ei.value.code == pp.PP_EBUSY
+    with pytest.raises(pp.PPError) as ei:           # a slot has ticked
+        e.set_acoustic_delay(1)
+    assert ei.value.code == pp.PP_EBUSY
     np.testing.assert_array_equal(e.step(codes[1]), ref.step(codes[1]))
     e.close()
     ref.close()
+
+
+# ------------------------------------------------------------------ acoustic delay, embedding-form prefill
+
+def _oracle_ticks(o, codes, n):
+    """Per-tick oracle records with the frame-aligned agent frames."""
+    recs = []
+    for t in range(n):
+        tok = o.step(codes[t:t + 1])
+        tp = o.taps
+        recs.append(dict(tokens=tok[0].copy(), hidden=tp["hidden"][:, 0].copy(),
+                         text_logits=tp["text_logits"][0].copy(), dep_logits=tp["dep_logits"][0].copy(),
+                         chosen=tp["chosen"][0].copy(), user_pred=tp["user_pred"][0].copy(),
+                         frame=tp["agent_frame"][0].copy(), frame_valid=bool(tp["agent_frame_valid"][0])))
+    return recs
+
+
+def test_acoustic_delay_teacher_forced_parity(tiny_weights, dev):
+    """Delay 1 at the tiny shape, 40 ticks: frame-aligned teacher frames (the
+    oracle's choices: text and codebook 0 of tick t, codebooks 1-7 of tick
+    t + 1) replayed into both the oracle and the GPU; taps, choices and the
+    completed agent frames compared every tick."""
+    _say("case: acoustic delay 1, teacher-forced parity, 40 ticks, B=1")
+    n = 40
+    codes = synth.user_codes(21, n)
+    free = Oracle(DM, tiny_weights, 1, W)
+    free.set_acoustic_delay(1)
+    first = _oracle_ticks(free, codes, n)
+    frames = np.full((n, 17), -1, np.int32)
+    for t in range(n):
+        frames[t, 0:2] = first[t]["chosen"][0:2]
+        if t + 1 < n:
+            frames[t, 2:9] = first[t + 1]["chosen"][2:9]
+        frames[t, 9:17] = codes[t]
+    o = Oracle(DM, tiny_weights, 1, W)
+    o.set_acoustic_delay(1)
+    o.prefill_forced(0, frames)
+    recs = _oracle_ticks(o, codes, n)
+    e = engine(tiny_weights, dev, 1)
+    e.set_acoustic_delay(1)
+    e.prefill_forced(0, frames)
+    fails, report = [], {}
+    for t in range(n):
+        e.step(np.zeros((1, 8), np.int32))
+        g = parity.gpu_slot(e.taps(), 0)
+        np.testing.assert_array_equal(g["hidden"][0], recs[t]["hidden"][0])
+        if t == 0:  # codebooks 1-7 are free on tick 0: compare where the margin decides
+            for k in range(1, 8):
+                if parity.margin(recs[0]["dep_logits"][k]) > parity.MARGIN:
+                    assert g["chosen"][1 + k] == recs[0]["chosen"][1 + k]
+        np.testing.assert_array_equal(g["chosen"], recs[t]["chosen"])
+        fr, ok = e.agent_frames()
+        assert bool(ok[0]) == recs[t]["frame_valid"]
+        np.testing.assert_array_equal(fr[0], recs[t]["frame"] if recs[t]["frame_valid"] else np.zeros(8))
+        fails += parity.compare_tick(g, recs[t], t, report)
+    e.close()
+    _say(f"worst hidden rel-L2 {max(report['hidden_rel_l2']):.3e}, tokens checked {report.get('tok_checked', 0)}")
+    assert not fails, "\n".join(fails[:20])
+
+
+def test_acoustic_delay_agent_frames_on_gpu(tiny_weights, dev):
+    """Delay 2, B = 2, free-running: each completed agent frame is codebook 0
+    chosen two ticks back and codebooks 1-7 chosen now; none before tick 2;
+    a reset slot starts over."""
+    _say("case: acoustic delay 2, agent frames, 12 ticks, B=2")
+    n, D = 12, 2
+    codes = np.stack([synth.user_codes(31, n), synth.user_codes(32, n)], 1)   # [n][2][8]
+    e = engine(tiny_weights, dev, 2)
+    e.set_acoustic_delay(D)
+    chosen, since_reset = [], [0, 0]
+    for t in range(n):
+        if t == 7:
+            e.slot_reset(1)
+            since_reset[1] = 0
+        e.step(codes[t])
+        chosen.append(e.taps()["chosen"][:, 1:9].copy())
+        fr, ok = e.agent_frames()
+        for b in range(2):
+            since_reset[b] += 1
+            assert bool(ok[b]) == (since_reset[b] > D)
+            if ok[b]:
+                np.testing.assert_array_equal(fr[b, 0], chosen[t - D][b, 0])
+                np.testing.assert_array_equal(fr[b, 1:], chosen[t][b, 1:])
+            else:
+                assert not fr[b].any()
+    e.close()
+
+
+def test_embedding_frames_parity(tiny_weights, dev):
+    """Embedding-form prefill (seeded N(0,1) fp32 inputs in place of the
+    gather-sum) for slot 0 beside token frames for slot 1, then free ticks;
+    all choices forced to the oracle's (a first oracle pass), taps compared."""
+    _say("case: embedding-form prefill parity, B=2, 6 prefill + 6 free ticks")
+    n_pre, n = 6, 12
+    x = np.random.default_rng(41).standard_normal((n_pre, DM.d), dtype=np.float32)
+    codes = np.stack([synth.user_codes(42, n), synth.user_codes(43, n)], 1)
+    tok_frames = np.concatenate([np.full((n_pre, 9), -1), codes[:n_pre, 1]], 1).astype(np.int32)
+
+    def run_oracle(force0, force1):
+        o = Oracle(DM, tiny_weights, 2, W)
+        o.prefill_embed(0, x, force0)
+        f1 = tok_frames.copy()
+        if force1 is not None:
+            f1[:, :9] = force1
+        o.prefill_forced(1, f1)
+        out = []
+        for t in range(n):
+            tok = o.step(codes[t])
+            out.append(dict({k: np.array(v) for k, v in o.taps.items()}, tokens=tok))
+        return out
+
+    first = run_oracle(None, None)
+    force0 = np.stack([first[t]["chosen"][0] for t in range(n_pre)])
+    force1 = np.stack([first[t]["chosen"][1] for t in range(n_pre)])
+    ref = run_oracle(force0, force1)
+    e = engine(tiny_weights, dev, 2)
+    e.prefill_embed(0, x, force0)
+    f1 = tok_frames.copy()
+    f1[:, :9] = force1
+    e.prefill_forced(1, f1)
+    fails, report = [], {}
+    for t in range(n):
+        e.step(codes[t])
+        tp = e.taps()
+        if t < n_pre:
+            np.testing.assert_array_equal(tp["hidden"][0, 0], x[t])
+        for b in range(2):
+            g = parity.gpu_slot(tp, b)
+            r = dict(hidden=ref[t]["hidden"][:, b], text_logits=ref[t]["text_logits"][b],
+                     dep_logits=ref[t]["dep_logits"][b], tokens=ref[t]["tokens"][b],
+                     user_pred=ref[t]["user_pred"][b], chosen=ref[t]["chosen"][b])
+            if t < n_pre:
+                np.testing.assert_array_equal(g["chosen"], r["chosen"])
+            fails += parity.compare_tick(g, r, t, report)
+    e.close()
+    _say(f"worst hidden rel-L2 {max(report['hidden_rel_l2']):.3e}, tokens checked {report.get('tok_checked', 0)}")
+    assert not fails, "\n".join(fails[:20])
+
+
+def test_embedding_frame_of_a_gather_sum_equals_the_token_frame(tiny_weights, dev):
+    """A token frame's own embedding sum, fed back as an embedding-form frame
+    with the same forced choices, reproduces that tick bit for bit."""
+    _say("case: embedding frame = token frame's gather-sum, B=1, 3 ticks")
+    frames = np.random.default_rng(51).integers(0, DM.audio_card, (3, 17)).astype(np.int32)
+    frames[:, 0] = np.random.default_rng(52).integers(0, DM.text_card, 3)
+    et = engine(tiny_weights, dev, 1)
+    et.prefill_forced(0, frames)
+    ee = engine(tiny_weights, dev, 1)
+    for t in range(3):
+        et.step(np.zeros((1, 8), np.int32))
+        tt = et.taps()
+        ee.prefill_embed(0, tt["hidden"][0, 0].copy()[None], frames[t:t + 1, :9])
+        ee.step(np.zeros((1, 8), np.int32))
+        te = ee.taps()
+        for key in ("hidden", "text_logits", "dep_logits", "chosen", "user_pred", "tokens"):
+            np.testing.assert_array_equal(te[key], tt[key])
+    et.close()
+    ee.close()
