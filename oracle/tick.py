@@ -60,6 +60,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from oracle import sampling
+
 TEXT_ROW = 0
 AGENT_ROWS = slice(1, 9)
 USER_ROWS = slice(9, 17)
@@ -148,6 +150,7 @@ class _Slot:
         self.user_hist = []    # frame-aligned user frames of past ticks (None: none given)
         self.force_hist = []   # frame-aligned forced agent rows of past ticks (-1: free)
         self.chosen_hist = []  # chosen agent rows of past ticks
+        self.text_hist = []    # chosen text tokens of the last sampling.REP_WINDOW ticks
         self.live = False      # True after the first free-running tick
         self.ticked = False    # True after any tick since the last reset
         self.K[...] = 0
@@ -175,6 +178,8 @@ class Oracle:
         self.slots = [_Slot(dims, self.W, self.dt) for _ in range(self.B)]
         self.taps = {}
         self.delay = 0
+        self.sampling = None   # None: greedy; else dict(t_text, t_audio, top_k, top_p, rho)
+        self.seeds = [0] * self.B
 
     def _store(self, v):
         """Value as kept in a key/value cache."""
@@ -240,6 +245,14 @@ class Oracle:
         for xi, fi in zip(x, force):
             st.queue.append(dict(force=fi.copy(), user=None, x=xi.astype(self.dt)))
 
+    def set_sampling(self, t_text, t_audio, top_k=0, top_p=1.0, rho=1.0):
+        """Replace the greedy choice by sampling (the sampling module)."""
+        self.sampling = dict(t_text=float(t_text), t_audio=float(t_audio), top_k=int(top_k), top_p=float(top_p),
+                             rho=float(rho))
+
+    def slot_seed(self, s, seed):
+        self.seeds[s] = int(seed)
+
     def set_acoustic_delay(self, frames):
         """Delay of audio codebooks 1-7 behind the text row and codebook 0,
         in frames; only before any slot has ticked."""
@@ -269,7 +282,7 @@ class Oracle:
             if frame is None:
                 st.live = True
             col, forced, x = self._column(st, user_codes[b], frame)
-            r = self._tick_slot(st, col, forced, x)
+            r = self._tick_slot(st, col, forced, x, self.seeds[b])
             hidden[:, b] = r["hidden"]
             text_logits[b] = r["text_logits"]
             dep_logits[b] = r["dep_logits"]
@@ -317,7 +330,17 @@ class Oracle:
             return np.zeros(8, np.int64), False
         return np.concatenate([st.chosen_hist[0][:1], st.chosen_hist[-1][1:]]), True
 
-    def _tick_slot(self, st, col, forced, x_given=None):
+    def _choose(self, logits, seed, tick, row, history=()):
+        """The model's own token for one row: greedy, or sampled."""
+        if self.sampling is None:
+            return greedy(logits)
+        sp = self.sampling
+        u = sampling.uniform(seed, tick, row)
+        if row == 0:
+            return sampling.sample(logits, u, sp["t_text"], sp["top_k"], sp["top_p"], sp["rho"], history)
+        return sampling.sample(logits, u, sp["t_audio"], sp["top_k"], sp["top_p"])
+
+    def _tick_slot(self, st, col, forced, x_given=None, seed=0):
         """One slot's tick.  col: the 17-row column (prev text+agent tokens,
         then the user rows); forced: 9 choices (-1 free) or None; x_given:
         an embedding-form frame's temporal input, or None."""
@@ -361,7 +384,7 @@ class Oracle:
         # 4-5. output norm, text head, greedy text token.
         z = rmsnorm(x, self.w("out_norm"), eps)
         text_logits = self.w("text_head") @ z
-        pred_text = greedy(text_logits)
+        pred_text = self._choose(text_logits, seed, st.ticks, 0, st.text_hist)
         chosen_text = int(forced[0]) if forced is not None and forced[0] >= 0 else pred_text
 
         # 6. depformer over the 16 codebooks of this frame; its per-step
@@ -393,7 +416,7 @@ class Oracle:
             yn = rmsnorm(y, self.w("dep.out_norm"), eps)
             lg = self.w(f"dep.head.{kq}") @ yn
             dep_logits[kq] = lg
-            p = greedy(lg)
+            p = self._choose(lg, seed, st.ticks, 1 + kq)
             preds.append(p)
             c = p
             if kq < 8 and forced is not None and forced[1 + kq] >= 0:
@@ -403,6 +426,7 @@ class Oracle:
 
         # 7. outputs and state.
         chosen = np.array([chosen_text] + chosen_audio[:8], np.int64)
+        st.text_hist = (st.text_hist + [chosen_text])[-sampling.REP_WINDOW:]
         st.prev = chosen
         st.pos = pos + 1
         st.ticked = True
