@@ -176,6 +176,9 @@ def main():
     ap.add_argument("--batch", type=int, default=None, help="slots (default: the config's own B)")
     ap.add_argument("--cpu-ticks", type=int, default=1, help="oracle ticks timed on the host (0: skip)")
     ap.add_argument("--kernel-iters", type=int, default=30)
+    ap.add_argument("--sampling", action="store_true",
+                    help="sample the token choices (text temperature 0.7, audio temperature 0.3, top-p 0.9, "
+                         "repetition penalty 1.2) instead of greedy")
     ap.add_argument("--mode", default="bench", choices=["bench", "traffic"],
                     help="traffic: one tick, then the dominant kernel once per layer outside the graph and the "
                          "copy probe, nothing else (for rocprofv3 --pmc runs)")
@@ -215,6 +218,12 @@ def main():
     log(f"weights uploaded and packed in {time.time() - t0:.1f} s")
     eng = pp.Engine(dm, weights, B, W, device=dev, device_weights=dw)
     log(f"engine created: B={B} W={W} arena {eng.arena.numel() / 2**30:.2f} GiB")
+    sampling = dict(text_temperature=0.7, audio_temperature=0.3, top_k=0, top_p=0.9,
+                    repetition_penalty=1.2) if args.sampling else None
+    if sampling:
+        eng.set_sampling(**sampling)
+        for b in range(B):
+            eng.slot_seed(b, 1000 + b)
     wl = Workload(args.config, dm, W, B, K, WU, synth)
 
     t0 = time.time()
@@ -302,7 +311,7 @@ def main():
                                 "C4": "7B RQ-Transformer tick, B=32 elastic, mixed occupancy, p=0.01 turnover",
                                 "sweep": "7B RQ-Transformer tick, all rings full",
                                 "sweep_empty": "7B RQ-Transformer tick, all rings empty"}[args.config],
-                   "B": B, "window": W, "config": args.config},
+                   "B": B, "window": W, "config": args.config, "choice": sampling or "greedy"},
         "p50_tick_ms": float(np.median(tick_ms)),
         "p90_tick_ms": float(np.percentile(tick_ms, 90)),
         "p99_tick_ms": float(np.percentile(tick_ms, 99)),
@@ -320,6 +329,10 @@ def main():
         from oracle.tick import Oracle
         cores = len(os.sched_getaffinity(0))
         o = Oracle(dm, weights, 1, W)
+        if sampling:
+            o.set_sampling(sampling["text_temperature"], sampling["audio_temperature"], sampling["top_k"],
+                           sampling["top_p"], sampling["repetition_penalty"])
+            o.slot_seed(0, 1000)
         c0 = wl.codes[0]
         ts = []
         for t in range(args.cpu_ticks):

@@ -32,7 +32,8 @@ struct Layout {
       split_part, wide_rms, rope, att_cnt, xin, total;
   // depformer buffers, two sets: the agent codebooks of tick t+1 run beside
   // the user-stream codebooks of tick t, which keep using the other set
-  size_t dkv[2], amax_v[2], amax_i[2], u[2], y[2], ya[2], dpart[2], dq[2], dout[2], dm[2];
+  size_t dkv[2], amax_v[2], amax_i[2], u[2], y[2], ya[2], dpart[2], dq[2], dout[2], dm[2], sctx[2];
+  size_t samp, rep;  // sampling parameters; recent chosen text tokens [B][SAMPLE_REP]
   long wide_part_max;
   int max_chunks, n_amax;
   long ring_slot_elems, ring_layer_elems, ring_v_off;
@@ -101,6 +102,7 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
     L.dq[s] = take(B * dd * 4);
     L.dout[s] = take(2 * B * dd * 2);
     L.dm[s] = take(2 * B * dF * 2);
+    L.sctx[s] = take((size_t)B * 4 * 4);
   }
   L.dep_logits = take(B * Q * A * 4);
   L.ti = take(B * TI_STRIDE * 4);
@@ -116,6 +118,8 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.split_part = B > 16 ? take((size_t)L.wide_part_max * 4) : take(0);
   L.wide_rms = take(MAX_COLS * 4);
   L.rope = take((size_t)B * hd * 4);
+  L.samp = take(sizeof(SampleParams));
+  L.rep = take((size_t)B * SAMPLE_REP * 4);
   L.att_cnt = take((size_t)B * H * 4);
   L.total = off;
   return L;
@@ -142,6 +146,8 @@ struct Slot {
   // ticks form the completed agent frame.
   std::deque<Row8> user_hist, force_hist, chosen_hist;
   int64_t ticks = 0;  // ticks since the last reset
+  uint64_t seed = 0;  // sampling seed (kept across resets)
+  std::deque<int32_t> text_hist;  // chosen text tokens of the last SAMPLE_REP ticks
   Row8 frame_out{};
   bool frame_valid = false;
   // this tick's frame-aligned user frame and forced agent row (set with the
@@ -176,6 +182,8 @@ struct pp_handle {
   int32_t* ti_host = nullptr;
   int32_t* to_host = nullptr;
   float* xin_host = nullptr;  // [B][d] given temporal inputs of embedding-form frames
+  int32_t* rep_host = nullptr;  // [B][SAMPLE_REP] recent chosen text tokens (-1 empty)
+  SampleParams samp{};        // host copy of the device sampling parameters
   int delay = 0;              // acoustic delay of codebooks 1-7, frames
   std::vector<Slot> slots;
   std::vector<std::function<void(hipStream_t)>> timed[6];  // per layer
@@ -217,6 +225,7 @@ void reset_slot(const pp_dims& dm, Slot& s) {
   s.force_hist.clear();
   s.chosen_hist.clear();
   s.ticks = 0;
+  s.text_hist.clear();
   s.frame_out.fill(0);
   s.frame_valid = false;
 }
@@ -434,6 +443,12 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
   fa.ya = h->at<bf16_t>(L.ya[ds]);
   fa.ya_lo = (long)B * dd;
   fa.part = h->at<float>(L.dpart[ds]);
+  fa.sp = h->at<SampleParams>(L.samp);
+  fa.logits = h->at<float>(L.text_logits);
+  fa.ld_logits = Vt;
+  fa.n_logits = Vt;
+  fa.rep = h->at<int>(L.rep);
+  fa.sctx = h->at<unsigned>(L.sctx[ds]);
 
   // depformer input projections u_k = P_k z for codebooks [c0, c1), one GEMM
   auto in_proj = [&](int c0, int c1) {
@@ -605,6 +620,10 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
     f.amax_v = h->at<float>(L.amax_v[ds]);
     f.amax_i = h->at<int>(L.amax_i[ds]);
     f.table = (k + 1 < Q) ? w.dep_emb_audio + (long)k * (A + 1) * dd : nullptr;
+    f.logits = h->at<float>(L.dep_logits) + (long)k * A;
+    f.ld_logits = (long)Q * A;
+    f.n_logits = A;
+    f.rep = nullptr;
     launch_finish(f, s);
   }
 }
@@ -645,6 +664,10 @@ void build_tick_input(pp_handle* h, const int32_t* user_codes, const Frame** fra
     t[TI_FORCE + 1] = s.tick_force[0];
     for (int i = 1; i < 8; ++i) t[TI_FORCE + 1 + i] = f_old ? (*f_old)[i] : -1;
     t[TI_XIN] = has_x ? 1 : 0;
+    t[TI_SEED] = (int32_t)(uint32_t)s.seed;
+    t[TI_SEED + 1] = (int32_t)(uint32_t)(s.seed >> 32);
+    t[TI_TICK] = (int32_t)(uint32_t)s.ticks;
+    t[TI_TICK + 1] = (int32_t)(uint32_t)((uint64_t)s.ticks >> 32);
   }
 }
 
@@ -652,6 +675,8 @@ void build_tick_input(pp_handle* h, const int32_t* user_codes, const Frame** fra
 // history, and the agent frame completed by it (codebook 0 chosen D ticks
 // ago, codebooks 1-7 chosen now) is kept for pp_agent_frames.
 void commit_history(pp_handle* h, Slot& s, const int32_t* chosen_agent) {
+  s.text_hist.push_back(chosen_agent[-1]);  // the chosen text token precedes the agent rows
+  while (s.text_hist.size() > (size_t)SAMPLE_REP) s.text_hist.pop_front();
   const size_t keep = (size_t)std::max(h->delay, 1);
   Row8 c;
   std::memcpy(c.data(), chosen_agent, sizeof c);
@@ -764,6 +789,9 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
   if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->xin_host), (size_t)B * dims->d * 4, hipHostMallocDefault)) !=
       hipSuccess)
     return bail("hipHostMalloc", e);
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->rep_host), (size_t)B * SAMPLE_REP * 4,
+                         hipHostMallocDefault)) != hipSuccess)
+    return bail("hipHostMalloc", e);
   std::memset(h->ti_host, 0, B * TI_STRIDE * 4);
   std::memset(h->xin_host, 0, (size_t)B * dims->d * 4);
   std::memset(h->to_host, 0, B * TO_STRIDE * 4);
@@ -783,7 +811,11 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
 
   if ((e = hipMemsetAsync(h->at<char>(lay.att_cnt), 0, (size_t)B * dims->n_heads * 4, h->stream)) != hipSuccess)
     return bail("hipMemsetAsync", e);
+  if ((e = hipMemcpyAsync(h->at<char>(lay.samp), &h->samp, sizeof(SampleParams), hipMemcpyHostToDevice, h->stream)) !=
+      hipSuccess)
+    return bail("hipMemcpyAsync", e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
+  finish_prepare();
   if ((e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
   if ((e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
   for (hipEvent_t* ev : {&h->temporal_done, &h->agent_done, &h->user_done[0], &h->user_done[1]}) {
@@ -869,6 +901,42 @@ int pp_set_acoustic_delay(pp_handle* h, int frames) {
   return PP_OK;
 }
 
+int pp_set_sampling(pp_handle* h, const pp_sampling* sp) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  SampleParams p{};
+  if (sp) {
+    const bool ok = std::isfinite(sp->text_temperature) && sp->text_temperature >= 0.f &&
+                    std::isfinite(sp->audio_temperature) && sp->audio_temperature >= 0.f && sp->top_k >= 0 &&
+                    sp->top_p > 0.f && sp->top_p <= 1.f && std::isfinite(sp->repetition_penalty) &&
+                    sp->repetition_penalty >= 1.f;
+    if (!ok) return h->fail(PP_EINVAL, "sampling parameters out of range");
+    if (h->dm.text_card > SAMPLE_MAX_N || h->dm.audio_card > SAMPLE_MAX_N)
+      return h->fail(PP_EINVAL, "logits rows wider than %d cannot be sampled", SAMPLE_MAX_N);
+    p.enabled = 1;
+    p.t_text = sp->text_temperature;
+    p.t_audio = sp->audio_temperature;
+    p.top_k = sp->top_k;
+    p.top_p = sp->top_p;
+    p.rho = sp->repetition_penalty;
+  }
+  // the pending user-stream codebooks belong to the last tick: they keep its parameters
+  HIP_OR_FAIL(h, launch_user(h, nullptr));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->side));
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->at<char>(h->lay.samp), &p, sizeof p, hipMemcpyHostToDevice, h->stream));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  h->samp = p;
+  return PP_OK;
+}
+
+int pp_slot_seed(pp_handle* h, int slot, uint64_t seed) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (slot < 0 || slot >= h->B) return h->fail(PP_EINVAL, "slot %d out of [0,%d)", slot, h->B);
+  h->slots[slot].seed = seed;
+  return PP_OK;
+}
+
 int pp_agent_frames(const pp_handle* h, int32_t* frames, int32_t* valid) {
   if (!h || !frames || !valid) return PP_EINVAL;
   if (h->poisoned) return PP_EDEVICE;
@@ -909,6 +977,15 @@ int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
   if (any_x)
     HIP_OR_FAIL(h, hipMemcpyAsync(h->at<float>(h->lay.xin), h->xin_host, (size_t)h->B * h->dm.d * 4,
                                   hipMemcpyHostToDevice, h->stream));
+  if (h->samp.enabled && h->samp.rho != 1.f) {
+    for (int b = 0; b < h->B; ++b) {
+      int32_t* r = h->rep_host + (size_t)b * SAMPLE_REP;
+      const auto& th = h->slots[b].text_hist;
+      for (int i = 0; i < SAMPLE_REP; ++i) r[i] = i < (int)th.size() ? th[i] : -1;
+    }
+    HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.rep), h->rep_host, (size_t)h->B * SAMPLE_REP * 4,
+                                  hipMemcpyHostToDevice, h->stream));
+  }
   HIP_OR_FAIL(h, launch_tick(h));
   // the agent outputs only (the user-stream codebooks may still be writing theirs)
   HIP_OR_FAIL(h, hipMemcpy2DAsync(h->to_host + TO_PRED, TO_STRIDE * 4, h->at<int>(h->lay.to) + TO_PRED, TO_STRIDE * 4,
@@ -1075,6 +1152,7 @@ void pp_destroy(pp_handle* h) {
   if (h->cap) (void)hipStreamDestroy(h->cap);
   if (h->ti_host) (void)hipHostFree(h->ti_host);
   if (h->xin_host) (void)hipHostFree(h->xin_host);
+  if (h->rep_host) (void)hipHostFree(h->rep_host);
   if (h->to_host) (void)hipHostFree(h->to_host);
   delete h;
 }

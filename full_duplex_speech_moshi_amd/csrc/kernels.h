@@ -13,6 +13,8 @@ enum {
   TI_COL = 1,        // 17 column rows: [1..9] previous chosen text+agent, [10..17] user codes
   TI_FORCE = 18,     // 9 forced choices for text, agent 0..7 (-1 = free)
   TI_XIN = 27,       // 1: the temporal input is the given row of EmbedArgs::xin, not the gather-sum
+  TI_SEED = 28,      // 2: the slot's sampling seed (low, high word)
+  TI_TICK = 30,      // 2: ticks since the slot's reset (low, high word)
   TI_STRIDE = 32
 };
 
@@ -124,6 +126,18 @@ struct EmbedArgs {
 };
 void launch_embed(const EmbedArgs& a, hipStream_t s);
 
+// Sampling of the token choice (device copy, set by pp_set_sampling).
+struct SampleParams {
+  int enabled;
+  float t_text, t_audio;  // temperatures; 0 = greedy for that row
+  int top_k;              // 0 = off
+  float top_p;            // 1 = off
+  float rho;              // repetition penalty on the text row; 1 = off
+  int pad[2];
+};
+constexpr int SAMPLE_REP = 64;       // chosen text tokens the penalty looks back over
+constexpr int SAMPLE_MAX_N = 32768;  // widest logits row that can be sampled (LDS)
+
 struct FinishArgs {
   int B, step;          // step -1: text head; 0..dep_q-1: depformer codebook step
   int n_part;           // argmax partials per slot
@@ -135,7 +149,16 @@ struct FinishArgs {
   const bf16_t* table;   // input table of step+1 ([rows][dd])
   const float* alpha;    // first depformer attention-norm alpha
   float* y; bf16_t* ya; long ya_lo; float* part;
+  // sampling (sp->enabled): the row's full logits, the text row's recent
+  // chosen tokens [B][SAMPLE_REP] (-1 empty), and each slot's (seed, tick)
+  // [B][4]: written by the text finisher from the tick input, read by the
+  // codebook finishers (which may run after the next tick input is in place)
+  const SampleParams* sp;
+  const float* logits; long ld_logits; int n_logits;
+  const int* rep;
+  unsigned* sctx;
 };
 void launch_finish(const FinishArgs& a, hipStream_t s);
+void finish_prepare();  // once per process, before the first finisher launch
 
 }  // namespace pp

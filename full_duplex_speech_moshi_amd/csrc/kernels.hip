@@ -1186,7 +1186,274 @@ __device__ __forceinline__ bool amax_better(float v2, int i2, float v, int i) {
   return i2 != 0x7fffffff && (i == 0x7fffffff || v2 > v || (v2 == v && i2 < i));
 }
 
-__device__ void finish_unit(const FinishArgs& a, const int b) {
+// ---------------------------------------------------------------------------
+// Sampling variant of the token choice (the guides' deployment knobs:
+// temperature, top-p, repetition penalty; top-k).  For one logits row, in
+// this order: the repetition penalty on the text row (a positive logit of a
+// recently chosen token divided by rho, a negative one multiplied; each
+// distinct token once); z = logit / T (T = 0: the argmax of the penalised
+// logits, lowest index on ties); top-k = the k first entries of the order
+// (z descending, index ascending); p = exp(z - max) over the kept entries;
+// top-p = the shortest prefix of the order (p descending, index ascending)
+// whose sum reaches top_p times the total; then the inverse CDF over the
+// kept entries in index order at u times their sum.  u = Philox4x32-10
+// (Salmon, Moraes, Dror and Shaw, SC 2011) of counter (tick since the slot's
+// reset, row, 0) and key (the slot's seed), first word >> 8, times 2^-24;
+// row 0 is the text token, 1 + k codebook k.
+//
+// One 256-thread workgroup per decision; the row lives in LDS; thread t owns
+// the contiguous entries [t * per, (t + 1) * per).  The k-th largest z and
+// the top-p threshold are found by bisection over order-preserving 32-bit
+// keys (32 counting passes each), ties resolved in index order with a scan.
+// ---------------------------------------------------------------------------
+
+constexpr int SAMPLE_NT = 256;
+
+__device__ __forceinline__ void philox4x32_10(unsigned c[4], unsigned k0, unsigned k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const unsigned lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const unsigned n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// larger float -> larger key (for -0 canonicalised to +0 beforehand)
+__device__ __forceinline__ unsigned order_key(float x) {
+  const unsigned u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct SampleSmem {
+  float f[SAMPLE_NT];
+  int i[SAMPLE_NT];
+  float red[4];
+  int redi[4];
+};
+
+__device__ __forceinline__ float blk_sum(float v, SampleSmem& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if (lane == 0) sh.red[wave] = v;
+  __syncthreads();
+  return ((sh.red[0] + sh.red[1]) + sh.red[2]) + sh.red[3];
+}
+
+__device__ __forceinline__ int blk_isum(int v, SampleSmem& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if (lane == 0) sh.redi[wave] = v;
+  __syncthreads();
+  return sh.redi[0] + sh.redi[1] + sh.redi[2] + sh.redi[3];
+}
+
+__device__ __forceinline__ float blk_max(float v, SampleSmem& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  __syncthreads();
+  if (lane == 0) sh.red[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
+}
+
+__device__ __forceinline__ int blk_imin(int v, SampleSmem& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  __syncthreads();
+  if (lane == 0) sh.redi[wave] = v;
+  __syncthreads();
+  return min(min(sh.redi[0], sh.redi[1]), min(sh.redi[2], sh.redi[3]));
+}
+
+// exclusive prefix of the threads' values in thread order (a fixed
+// shuffle-up scan within each wave, then the wave totals in order); returns
+// this thread's prefix, *total the sum of all
+__device__ __forceinline__ float blk_scan(float v, SampleSmem& sh, float* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  __syncthreads();
+  if (lane == 63) sh.red[wave] = inc;
+  __syncthreads();
+  float base = 0.f;
+  for (int w = 0; w < wave; ++w) base += sh.red[w];
+  *total = ((sh.red[0] + sh.red[1]) + sh.red[2]) + sh.red[3];
+  return base + (inc - v);
+}
+
+__device__ __forceinline__ int blk_iscan(int v, SampleSmem& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  __syncthreads();
+  if (lane == 63) sh.redi[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += sh.redi[w];
+  return base + inc - v;
+}
+
+// The sampled token of slot b for the finisher's row; z: LDS of n floats.
+__device__ int sample_row(const FinishArgs& a, const int b, const unsigned* ctx, float* z, SampleSmem& sh) {
+  const SampleParams sp = *a.sp;
+  const int n = a.n_logits, tid = threadIdx.x;
+  const int per = (n + SAMPLE_NT - 1) / SAMPLE_NT, i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  const float* lg = a.logits + (long)b * a.ld_logits;
+  // the row into LDS, 16 loads in flight per thread
+  for (int i0b = 0; i0b < n; i0b += 16 * SAMPLE_NT) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = i0b + q * SAMPLE_NT + tid;
+      v[q] = lg[min(i, n - 1)];
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = i0b + q * SAMPLE_NT + tid;
+      if (i < n) z[i] = v[q];
+    }
+  }
+  if (a.step < 0 && sp.rho != 1.f) {
+    if (tid < SAMPLE_REP) sh.i[tid] = a.rep[(long)b * SAMPLE_REP + tid];
+    __syncthreads();
+    if (tid < SAMPLE_REP) {
+      const int v = sh.i[tid];
+      bool first = v >= 0 && v < n;
+      for (int j = 0; j < tid; ++j) first = first && sh.i[j] != v;
+      if (first) {
+        const float x = z[v];
+        z[v] = x > 0.f ? x / sp.rho : x * sp.rho;
+      }
+    }
+  }
+  __syncthreads();
+  const float T = a.step < 0 ? sp.t_text : sp.t_audio;
+  if (T == 0.f) {  // argmax of the penalised logits, lowest index on ties
+    float bv = -INFINITY;
+    int bi = n;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i)
+      if (z[i] > bv || bi == n) { bv = z[i]; bi = i; }
+    const float m = blk_max(bv, sh);
+    return blk_imin(bv == m ? bi : n, sh);
+  }
+#pragma unroll 8
+  for (int i = i0; i < i1; ++i) z[i] = z[i] / T + 0.0f;  // + 0 turns -0 into +0
+  __syncthreads();
+  if (sp.top_k > 0 && sp.top_k < n) {
+    unsigned res = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned cand = res | (1u << bit);
+      int c = 0;
+#pragma unroll 8
+      for (int i = i0; i < i1; ++i) c += order_key(z[i]) >= cand;
+      if (blk_isum(c, sh) >= sp.top_k) res = cand;
+    }
+    int gt = 0, eq = 0;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) {
+      const unsigned k = order_key(z[i]);
+      gt += k > res;
+      eq += k == res;
+    }
+    const int need = sp.top_k - blk_isum(gt, sh);
+    int rank = blk_iscan(eq, sh);
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) {
+      const unsigned k = order_key(z[i]);
+      bool keep = k > res;
+      if (k == res) keep = rank++ < need;
+      if (!keep) z[i] = -INFINITY;
+    }
+    __syncthreads();
+  }
+  float mx = -INFINITY;
+#pragma unroll 8
+  for (int i = i0; i < i1; ++i) mx = fmaxf(mx, z[i]);
+  const float m = blk_max(mx, sh);
+  float cs = 0.f;
+#pragma unroll 8
+  for (int i = i0; i < i1; ++i) {
+    const float p = z[i] == -INFINITY ? 0.f : expf(z[i] - m);
+    z[i] = p;
+    cs += p;
+  }
+  __syncthreads();
+  if (sp.top_p < 1.f) {
+    const float target = sp.top_p * blk_sum(cs, sh);
+    unsigned res = 0;  // 0 <= p <= 1: its bits order like its value and stay below 2^30
+    for (int bit = 29; bit >= 0; --bit) {
+      const unsigned cand = res | (1u << bit);
+      float sm = 0.f;
+#pragma unroll 8
+      for (int i = i0; i < i1; ++i) sm += __float_as_uint(z[i]) >= cand ? z[i] : 0.f;
+      if (blk_sum(sm, sh) >= target) res = cand;
+    }
+    float g = 0.f, eq = 0.f;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) {
+      const unsigned k = __float_as_uint(z[i]);
+      g += k > res ? z[i] : 0.f;
+      eq += k == res ? z[i] : 0.f;
+    }
+    const float G = blk_sum(g, sh);
+    float tot;
+    float run = blk_scan(eq, sh, &tot);
+    cs = 0.f;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) {
+      const unsigned k = __float_as_uint(z[i]);
+      bool keep = k > res;
+      if (k == res) {
+        keep = G + run < target;
+        run += z[i];
+      }
+      if (!keep) z[i] = 0.f;
+      cs += z[i];
+    }
+    __syncthreads();
+  }
+  unsigned c[4] = {ctx[2], ctx[3], (unsigned)(a.step + 1), 0u};
+  philox4x32_10(c, ctx[0], ctx[1]);
+  const float u = (float)(c[0] >> 8) * 5.9604644775390625e-8f;  // 2^-24
+  float total;
+  float run = blk_scan(cs, sh, &total);
+  const float target = u * total;
+  int pick = n, last = -1;
+#pragma unroll 8
+  for (int i = i0; i < i1; ++i) {
+    if (z[i] > 0.f) {
+      last = i;
+      run += z[i];
+      if (pick == n && run > target) pick = i;
+    }
+  }
+  pick = blk_imin(pick, sh);
+  if (pick == n) pick = -blk_imin(-last, sh);  // rounding left the target at the total: the last kept entry
+  return pick;
+}
+
+__device__ void finish_unit(const FinishArgs& a, const int b, float* zrow) {
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float sv[8];
   __shared__ int si[8];
@@ -1240,10 +1507,33 @@ __device__ void finish_unit(const FinishArgs& a, const int b) {
     si[wave] = bi;
   }
   __syncthreads();
+  // sampling: the slot's (seed, tick) travel from the tick input (text
+  // finisher) to the codebook finishers through a.sctx
+  __shared__ SampleSmem ssm;
+  __shared__ int spred;
+  const bool samp = a.sp && a.sp->enabled;
+  if (samp) {
+    unsigned* ctx = a.sctx + (long)b * 4;
+    if (a.step < 0) {
+      __shared__ unsigned tctx[4];
+      if (tid < 4) tctx[tid] = (unsigned)a.ti[b * TI_STRIDE + TI_SEED + tid];
+      __syncthreads();
+      if (tid < 4) ctx[tid] = tctx[tid];
+      const int p = sample_row(a, b, tctx, zrow, ssm);
+      if (tid == 0) spred = p;
+    } else {
+      __shared__ unsigned uctx[4];
+      if (tid < 4) uctx[tid] = ctx[tid];
+      __syncthreads();
+      const int p = sample_row(a, b, uctx, zrow, ssm);
+      if (tid == 0) spred = p;
+    }
+    __syncthreads();
+  }
   if (tid == 0) {
     for (int w = 1; w < nt / 64; ++w)
       if (amax_better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
-    const int pred = bi;
+    const int pred = samp ? spred : bi;
     int* to = a.to + b * TO_STRIDE;
     const int chosen = forced >= 0 ? forced : pred;  // step -1 -> text force
     if (a.step < 8) {
@@ -1276,10 +1566,20 @@ __device__ void finish_unit(const FinishArgs& a, const int b) {
   }
 }
 
-__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) { finish_unit(a, blockIdx.x); }
+__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
+  extern __shared__ float zrow[];  // the logits row when sampling (n_logits floats, at most SAMPLE_MAX_N)
+  finish_unit(a, blockIdx.x, zrow);
+}
+
+void finish_prepare() {
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(finish_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            SAMPLE_MAX_N * 4);
+}
 
 void launch_finish(const FinishArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(finish_kernel, dim3(a.B), dim3(256), 0, s, a);
+  // room for the row only where it can be sampled (pp_set_sampling refuses wider rows)
+  const size_t lds = (a.sp && a.n_logits <= SAMPLE_MAX_N) ? (size_t)a.n_logits * 4 : 0;
+  hipLaunchKernelGGL(finish_kernel, dim3(a.B), dim3(256), lds, s, a);
 }
 
 }  // namespace pp

@@ -18,7 +18,8 @@ PP_MAX_BATCH = 32
 TO_STRIDE = 32
 
 EXPORTS = ("pp_arena_bytes", "pp_create", "pp_prefill_forced", "pp_prefill_embed", "pp_step",
-           "pp_set_acoustic_delay", "pp_agent_frames", "pp_slot_reset", "pp_ring_fill", "pp_taps",
+           "pp_set_acoustic_delay", "pp_agent_frames", "pp_set_sampling", "pp_slot_seed", "pp_slot_reset",
+           "pp_ring_fill", "pp_taps",
            "pp_time_kernel", "pp_time_graph", "pp_destroy", "pp_last_error", "pp_packed_elems",
            "pp_pack_matrix")
 
@@ -47,6 +48,11 @@ class PPTaps(ctypes.Structure):
                 ("dep_logits", ctypes.c_void_p), ("tokens", ctypes.c_void_p)]
 
 
+class PPSampling(ctypes.Structure):
+    _fields_ = [("text_temperature", ctypes.c_float), ("audio_temperature", ctypes.c_float),
+                ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float), ("repetition_penalty", ctypes.c_float)]
+
+
 class PPError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"{msg} (code {code})")
@@ -72,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pp_prefill_embed.argtypes = [P, I, P, P, I]
     lib.pp_set_acoustic_delay.argtypes = [P, I]
     lib.pp_agent_frames.argtypes = [P, P, P]
+    lib.pp_set_sampling.argtypes = [P, ctypes.POINTER(PPSampling)]
+    lib.pp_slot_seed.argtypes = [P, I, ctypes.c_uint64]
     lib.pp_step.argtypes = [P, P, P]
     lib.pp_slot_reset.argtypes = [P, I]
     lib.pp_ring_fill.argtypes = [P, I, I, P, P]
@@ -142,6 +150,20 @@ def pp_prefill_embed(h: int, slot: int, x, force=None) -> None:
 
 def pp_set_acoustic_delay(h: int, frames: int) -> None:
     _check(load_library().pp_set_acoustic_delay(h, frames), h)
+
+
+def pp_set_sampling(h: int, text_temperature=None, audio_temperature=0.0, top_k=0, top_p=1.0,
+                    repetition_penalty=1.0) -> None:
+    """text_temperature None: back to greedy."""
+    if text_temperature is None:
+        _check(load_library().pp_set_sampling(h, None), h)
+        return
+    sp = PPSampling(text_temperature, audio_temperature, top_k, top_p, repetition_penalty)
+    _check(load_library().pp_set_sampling(h, ctypes.byref(sp)), h)
+
+
+def pp_slot_seed(h: int, slot: int, seed: int) -> None:
+    _check(load_library().pp_slot_seed(h, slot, seed), h)
 
 
 def pp_agent_frames(h: int, B: int):
@@ -298,6 +320,12 @@ class Engine:
 
     def agent_frames(self):
         return pp_agent_frames(self.h, self.B)
+
+    def set_sampling(self, text_temperature=None, audio_temperature=0.0, top_k=0, top_p=1.0, repetition_penalty=1.0):
+        pp_set_sampling(self.h, text_temperature, audio_temperature, top_k, top_p, repetition_penalty)
+
+    def slot_seed(self, slot, seed):
+        pp_slot_seed(self.h, slot, seed)
 
     def step(self, user_codes) -> np.ndarray:
         return pp_step(self.h, user_codes, self.B)

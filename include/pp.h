@@ -120,6 +120,18 @@ typedef struct pp_taps_t {
                                   [17..25] chosen tokens (forced where forced, else predicted) */
 } pp_taps_t;
 
+/* Sampling of the token choice (pp_set_sampling).  The guides' deployment
+ * knobs: a sampling temperature of 0.7-0.8, a repetition penalty of about
+ * 1.1 (the Korean Moshi guide's risk list), top_p 0.9 and a separate audio
+ * temperature (the PersonaPlex configuration walkthrough); top-k as well. */
+typedef struct pp_sampling {
+  float text_temperature;   /* text row; 0 = greedy */
+  float audio_temperature;  /* depformer codebooks 0-15; 0 = greedy */
+  int   top_k;              /* 0 = off */
+  float top_p;              /* (0, 1]; 1 = off */
+  float repetition_penalty; /* >= 1 (1 = off), text row: the slot's last 64 chosen text tokens */
+} pp_sampling;
+
 typedef struct pp_handle pp_handle;
 
 /* Elements of one [M][K] matrix in the tile layout: ceil(M/16)*16*K.
@@ -199,6 +211,27 @@ int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens);
  * (PP_EINVAL); legal only while no slot has ticked since its reset
  * (PP_EBUSY).  Default 0. */
 int pp_set_acoustic_delay(pp_handle* h, int frames);
+
+/* Replace the greedy choice by sampling from the next tick on (NULL: back
+ * to greedy, the default).  Per decision (one logits row): the repetition
+ * penalty on the text row (a positive logit of a token among the slot's
+ * last 64 chosen text tokens is divided by the penalty, a negative one
+ * multiplied, each distinct token once); z = logit / T; top-k = the k first
+ * of the order (z descending, index ascending); p = exp(z - max z) over the
+ * kept entries; top-p = the shortest prefix of the order (p descending,
+ * index ascending) whose sum reaches top_p of the total; the token = the
+ * inverse CDF over the kept entries in index order at u times their sum.
+ * u = Philox4x32-10 (Salmon et al., SC 2011) of counter (ticks since the
+ * slot's reset as 64 bits, row, 0) and key (the slot's seed), first output
+ * word >> 8, times 2^-24; row 0 is the text token, 1 + k codebook k.  The
+ * sampled tokens are the model's own predictions (pp_step's tokens); forced
+ * rows still override the choice.  PP_EINVAL for a negative or non-finite
+ * temperature, top_k < 0, top_p outside (0, 1], a penalty below 1, or
+ * logits rows wider than 32768.  Waits for the device work in flight. */
+int pp_set_sampling(pp_handle* h, const pp_sampling* s);
+
+/* The sampling seed of `slot` (default 0; kept across pp_slot_reset). */
+int pp_slot_seed(pp_handle* h, int slot, uint64_t seed);
 
 /* The agent audio frame completed by the last pp_step, per slot: frame
  * f = t - D gets codebook 0 chosen at tick f and codebooks 1-7 chosen at

@@ -78,6 +78,8 @@ def test_null_handle_calls_are_rejected(lib):
     assert lib.pp_prefill_embed(None, 0, None, None, 0) == pp.PP_EINVAL
     assert lib.pp_set_acoustic_delay(None, 1) == pp.PP_EINVAL
     assert lib.pp_agent_frames(None, None, None) == pp.PP_EINVAL
+    assert lib.pp_set_sampling(None, None) == pp.PP_EINVAL
+    assert lib.pp_slot_seed(None, 0, 1) == pp.PP_EINVAL
     lib.pp_destroy(None)
 
 

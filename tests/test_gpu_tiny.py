@@ -284,6 +284,11 @@ def test_errors_leave_state_unchanged(tiny_weights, dev):
     with pytest.raises(pp.PPError) as ei:
         e.set_acoustic_delay(5)
     assert ei.value.code == pp.PP_EINVAL
+    for bad in [dict(text_temperature=-1.0), dict(text_temperature=1.0, top_p=0.0),
+                dict(text_temperature=1.0, top_k=-2), dict(text_temperature=1.0, repetition_penalty=0.5)]:
+        with pytest.raises(pp.PPError) as ei:
+            e.set_sampling(**bad)
+        assert ei.value.code == pp.PP_EINVAL
     fr, ok = e.agent_frames()
     assert not ok.any()
     # nothing above changed any state: same results as an untouched handle
@@ -462,3 +467,104 @@ def test_embedding_frame_of_a_gather_sum_equals_the_token_frame(tiny_weights, de
             np.testing.assert_array_equal(te[key], tt[key])
     et.close()
     ee.close()
+
+
+# ------------------------------------------------------------------ sampling variant
+
+def test_sampling_with_top_k_1_equals_greedy(tiny_weights, dev):
+    _say("case: sampling with top_k = 1 vs greedy, B=2, 8 ticks")
+    codes = np.stack([synth.user_codes(61, 8), synth.user_codes(62, 8)], 1)
+    eg = engine(tiny_weights, dev, 2)
+    es = engine(tiny_weights, dev, 2)
+    es.set_sampling(0.8, 0.3, top_k=1)
+    es.slot_seed(0, 5)
+    es.slot_seed(1, 6)
+    for t in range(8):
+        np.testing.assert_array_equal(es.step(codes[t]), eg.step(codes[t]))
+        ts, tg = es.taps(), eg.taps()
+        for key in ("hidden", "text_logits", "dep_logits", "chosen", "user_pred"):
+            np.testing.assert_array_equal(ts[key], tg[key])
+    eg.close()
+    es.close()
+
+
+def _oracle_choice_or_boundary(logits, seed, tick, row, temp, top_k, top_p, rho, hist, got):
+    """The oracle sampler's token for the GPU's own logits row; a different
+    GPU token is accepted only if nudging u or top_p by 1e-5 (a decision at a
+    rounding boundary) yields it.  Returns (ok, exact)."""
+    from oracle import sampling as sm
+    u = sm.uniform(seed, tick, row)
+    want = sm.sample(logits, u, temp, top_k, top_p, rho, hist)
+    if want == got:
+        return True, True
+    for du in (-1e-5, 1e-5):
+        if sm.sample(logits, min(max(u + du, 0.0), 1 - 2 ** -24), temp, top_k, top_p, rho, hist) == got:
+            return True, False
+    for dp in (-1e-5, 1e-5):
+        if top_p < 1.0 and sm.sample(logits, u, temp, top_k, min(top_p + dp, 1.0), rho, hist) == got:
+            return True, False
+    return False, False
+
+
+@pytest.mark.parametrize("knobs", [(0.8, 0.7, 0, 1.0, 1.0), (0.75, 0.3, 50, 0.9, 1.2), (1.3, 1.0, 7, 1.0, 1.1)])
+def test_sampling_matches_oracle_sampler(tiny_weights, dev, knobs):
+    """Free-running sampled ticks, B = 2 with seeds 11 and 2^40 + 12: every
+    text and codebook choice (17 rows) equals the oracle sampler applied to
+    the GPU's own logits with the same draw (Philox of seed, tick, row) and
+    the slot's recent chosen text tokens."""
+    t_text, t_audio, top_k, top_p, rho = knobs
+    _say(f"case: sampling parity {knobs}, B=2, 12 ticks")
+    n = 12
+    seeds = [11, 2 ** 40 + 12]
+    codes = np.stack([synth.user_codes(63, n), synth.user_codes(64, n)], 1)
+    e = engine(tiny_weights, dev, 2)
+    e.set_sampling(t_text, t_audio, top_k, top_p, rho)
+    for b, sd in enumerate(seeds):
+        e.slot_seed(b, sd)
+    hist = [[], []]
+    exact = boundary = 0
+    for t in range(n):
+        tok = e.step(codes[t])
+        tp = e.taps()
+        for b in range(2):
+            rows = [(tp["text_logits"][b], t_text, rho, list(hist[b]), tok[b, 0])]
+            for k in range(DM.dep_q):
+                got = tok[b, 1 + k] if k < 8 else tp["user_pred"][b, k - 8]
+                rows.append((tp["dep_logits"][b, k], t_audio, 1.0, [], got))
+            for row, (lg, temp, r, h, got) in enumerate(rows):
+                ok, ex = _oracle_choice_or_boundary(lg, seeds[b], t, row, temp, top_k, top_p, r, h, int(got))
+                assert ok, f"tick {t} slot {b} row {row}: GPU {got} is not the oracle's choice"
+                exact += ex
+                boundary += not ex
+            hist[b] = (hist[b] + [int(tp["chosen"][b, 0])])[-64:]
+    e.close()
+    _say(f"decisions: {exact} exact, {boundary} at a rounding boundary")
+    assert boundary <= 2
+
+
+def test_sampling_isolation_and_recycle(tiny_weights, dev):
+    """Sampled slots keep strong isolation: B = 3 equals B = 1 engines with the
+    same seeds, and a recycled slot draws as a fresh engine does."""
+    _say("case: sampling isolation and recycle, B=3 vs B=1, 6 ticks")
+    n = 6
+    seeds = [3, 4, 5]
+    codes = np.stack([synth.user_codes(70 + b, n) for b in range(3)], 1)
+    knobs = (0.9, 0.8, 20, 0.95, 1.15)
+    eb = engine(tiny_weights, dev, 3)
+    eb.set_sampling(*knobs)
+    for b, sd in enumerate(seeds):
+        eb.slot_seed(b, sd)
+    toks = []
+    for t in range(n):
+        if t == 3:
+            eb.slot_reset(2)
+        toks.append(eb.step(codes[t]))
+    eb.close()
+    for b in range(3):
+        e1 = engine(tiny_weights, dev, 1)
+        e1.set_sampling(*knobs)
+        e1.slot_seed(0, seeds[b])
+        t_from = 3 if b == 2 else 0
+        for t in range(t_from, n):
+            np.testing.assert_array_equal(e1.step(codes[t, b:b + 1])[0], toks[t][b])
+        e1.close()
