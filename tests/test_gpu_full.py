@@ -197,3 +197,63 @@ def test_full_isolation_b32_bit_exact(full):
             np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
             np.testing.assert_array_equal(tp["user_pred"][0], taps[t]["user_pred"][b])
         e1.close()
+
+
+@pytest.mark.timeout(900)
+def test_full_sampling_matches_oracle_sampler(full):
+    """Sampling at the 7B shape (the 32000-way text row held in LDS), B = 2,
+    3 ticks with the pages' knobs plus top-k: every choice equals the oracle
+    sampler on the GPU's own logits with the same draw (a rounding-boundary
+    decision is accepted and counted)."""
+    from tests.test_gpu_tiny import _oracle_choice_or_boundary
+    _say("case: 7B sampling parity, B=2, 3 ticks")
+    knobs = (0.7, 0.3, 400, 0.9, 1.2)
+    seeds = [21, 22]
+    codes = [synth.user_codes(900 + b, 3) for b in range(2)]
+    e = _engine(full, 2)
+    e.set_sampling(*knobs)
+    for b, sd in enumerate(seeds):
+        e.slot_seed(b, sd)
+    hist = [[], []]
+    boundary = 0
+    for t in range(3):
+        tok = e.step(np.stack([codes[b][t] for b in range(2)]))
+        tp = e.taps()
+        for b in range(2):
+            rows = [(tp["text_logits"][b], knobs[0], knobs[4], list(hist[b]), tok[b, 0])]
+            for k in range(DM.dep_q):
+                got = tok[b, 1 + k] if k < 8 else tp["user_pred"][b, k - 8]
+                rows.append((tp["dep_logits"][b, k], knobs[1], 1.0, [], got))
+            for row, (lg, temp, rho, h, got) in enumerate(rows):
+                ok, ex = _oracle_choice_or_boundary(lg, seeds[b], t, row, temp, knobs[2], knobs[3], rho, h, int(got))
+                assert ok, f"tick {t} slot {b} row {row}: GPU {got} is not the oracle's choice"
+                boundary += not ex
+            hist[b] = (hist[b] + [int(tp["chosen"][b, 0])])[-64:]
+    e.close()
+    _say(f"rounding-boundary decisions: {boundary}")
+    assert boundary <= 1
+
+
+@pytest.mark.timeout(900)
+def test_full_embedding_frame_equals_token_frame(full):
+    """At 7B, a token frame's own embedding sum fed back as an
+    embedding-form frame (same forced choices) reproduces the tick bit for
+    bit, with an acoustic delay of 1 set on both engines (on a slot's first
+    tick the delayed user rows hold the initial token either way)."""
+    _say("case: 7B embedding frame = token frame's gather-sum, delay 1, 1 tick")
+    frames = np.random.default_rng(81).integers(0, DM.audio_card, (2, 17)).astype(np.int32)
+    frames[:, 0] = np.random.default_rng(82).integers(0, DM.text_card, 2)
+    et = _engine(full, 1)
+    ee = _engine(full, 1)
+    et.set_acoustic_delay(1)
+    ee.set_acoustic_delay(1)
+    et.prefill_forced(0, frames[:1])
+    et.step(np.zeros((1, 8), np.int32))
+    x0 = et.taps()["hidden"][0, 0].copy()
+    ee.prefill_embed(0, x0[None], frames[:1, :9])
+    ee.step(np.zeros((1, 8), np.int32))
+    ta, tb = et.taps(), ee.taps()
+    for key in ("hidden", "text_logits", "dep_logits", "chosen", "user_pred", "tokens"):
+        np.testing.assert_array_equal(ta[key], tb[key])
+    et.close()
+    ee.close()
