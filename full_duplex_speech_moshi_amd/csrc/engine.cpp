@@ -474,9 +474,26 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
   // All 16 projections run here: z (the normalised final hidden state) is
   // overwritten by the next tick's temporal stack, which runs before this
   // tick's user-stream codebooks.
+  // Greedy ticks at B <= DEP_FUSE_B fold each finisher into the next step's
+  // first QKV projection, except codebook 7's (its tokens are returned by
+  // pp_step before the user-stream codebooks run) and the last codebook's.
+  const bool fuse_fin = B <= DEP_FUSE_B && dd <= DEP_FUSE_D && !h->samp.enabled;
+  auto finish_of = [&](int k) {  // the finisher of codebook step k
+    FinishArgs f = fa;
+    f.step = k;
+    f.n_part = (A + ROWS - 1) / ROWS;
+    f.amax_v = h->at<float>(L.amax_v[ds]);
+    f.amax_i = h->at<int>(L.amax_i[ds]);
+    f.table = (k + 1 < Q) ? w.dep_emb_audio + (long)k * (A + 1) * dd : nullptr;
+    f.logits = h->at<float>(L.dep_logits) + (long)k * A;
+    f.ld_logits = (long)Q * A;
+    f.n_logits = A;
+    f.rep = nullptr;
+    return f;
+  };
   if (phase == PH_AGENT) {
     in_proj(0, Q);
-    launch_finish(fa, s);
+    if (!fuse_fin) launch_finish(fa, s);
   }
 
   // codebook steps: the agent stream in PH_AGENT, the user stream in PH_USER
@@ -511,6 +528,10 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       g.inv_freq = nullptr;
       g.split_part = split_part;
       g.wide_rms = wide_rms;
+      if (l == 0 && fuse_fin && k != dm.n_q) {
+        g.fuse_fin = 1;
+        g.fin = k == 0 ? fa : finish_of(k - 1);
+      }
       launch_gemm(EPI_QKV, g, s);
 
       // attention over steps 0..k of this frame: inside the out-projection at
@@ -614,17 +635,7 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
     gh.wide_rms = wide_rms;
     launch_gemm(EPI_LOGITS, gh, s);
 
-    FinishArgs f = fa;
-    f.step = k;
-    f.n_part = (A + ROWS - 1) / ROWS;
-    f.amax_v = h->at<float>(L.amax_v[ds]);
-    f.amax_i = h->at<int>(L.amax_i[ds]);
-    f.table = (k + 1 < Q) ? w.dep_emb_audio + (long)k * (A + 1) * dd : nullptr;
-    f.logits = h->at<float>(L.dep_logits) + (long)k * A;
-    f.ld_logits = (long)Q * A;
-    f.n_logits = A;
-    f.rep = nullptr;
-    launch_finish(f, s);
+    if (!fuse_fin || k == dm.n_q - 1 || k == Q - 1) launch_finish(finish_of(k), s);
   }
 }
 
@@ -692,6 +703,29 @@ void commit_history(pp_handle* h, Slot& s, const int32_t* chosen_agent) {
     s.frame_out[0] = s.chosen_hist.front()[0];
     for (int i = 1; i < 8; ++i) s.frame_out[i] = s.chosen_hist.back()[i];
   }
+}
+
+// Capture the five graphs of the tick (replacing any earlier ones), from the
+// handle's current settings.  The caller has no device work in flight.
+hipError_t capture_graphs(pp_handle* h) {
+  hipError_t e;
+  for (auto& t : h->timed) t.clear();
+  for (int g = 0; g < 5; ++g) {
+    if (h->exec[g]) (void)hipGraphExecDestroy(h->exec[g]);
+    if (h->graph[g]) (void)hipGraphDestroy(h->graph[g]);
+    h->exec[g] = nullptr;
+    h->graph[g] = nullptr;
+  }
+  for (int g = 0; g < 5; ++g) {
+    const Phase ph = g == 0 ? PH_TEMPORAL : g < 3 ? PH_AGENT : PH_USER;
+    const int ds = g == 0 ? 0 : (g - 1) % 2;
+    if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
+    record_tick(h, h->cap, ph, ds, ph == PH_TEMPORAL);
+    if ((e = hipStreamEndCapture(h->cap, &h->graph[g])) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGraphInstantiate(&h->exec[g], h->graph[g], nullptr, nullptr, 0)) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Launch the last tick's PH_USER on the side stream, after that tick's
@@ -822,17 +856,7 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
     if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return bail("hipEventCreate", e);
     if ((e = hipEventRecord(*ev, h->side)) != hipSuccess) return bail("hipEventRecord", e);
   }
-  for (int g = 0; g < 5; ++g) {
-    const Phase ph = g == 0 ? PH_TEMPORAL : g < 3 ? PH_AGENT : PH_USER;
-    const int ds = g == 0 ? 0 : (g - 1) % 2;
-    if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess)
-      return bail("hipStreamBeginCapture", e);
-    record_tick(h, h->cap, ph, ds, ph == PH_TEMPORAL);
-    if ((e = hipStreamEndCapture(h->cap, &h->graph[g])) != hipSuccess) return bail("hipStreamEndCapture", e);
-    if ((e = hipGetLastError()) != hipSuccess) return bail("kernel launch during capture", e);
-    if ((e = hipGraphInstantiate(&h->exec[g], h->graph[g], nullptr, nullptr, 0)) != hipSuccess)
-      return bail("hipGraphInstantiate", e);
-  }
+  if ((e = capture_graphs(h)) != hipSuccess) return bail("graph capture", e);
   *out = h;
   return PP_OK;
 }
@@ -925,7 +949,9 @@ int pp_set_sampling(pp_handle* h, const pp_sampling* sp) {
   HIP_OR_FAIL(h, hipStreamSynchronize(h->side));
   HIP_OR_FAIL(h, hipMemcpyAsync(h->at<char>(h->lay.samp), &p, sizeof p, hipMemcpyHostToDevice, h->stream));
   HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  const bool recapture = p.enabled != h->samp.enabled;  // greedy ticks fold the finishers into the QKV launches
   h->samp = p;
+  if (recapture) HIP_OR_FAIL(h, capture_graphs(h));
   return PP_OK;
 }
 

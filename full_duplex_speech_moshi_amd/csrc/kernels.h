@@ -48,6 +48,39 @@ struct DepAttnArgs {
 };
 void launch_dep_attention(const DepAttnArgs& a, hipStream_t s);
 
+// Sampling of the token choice (device copy, set by pp_set_sampling).
+struct SampleParams {
+  int enabled;
+  float t_text, t_audio;  // temperatures; 0 = greedy for that row
+  int top_k;              // 0 = off
+  float top_p;            // 1 = off
+  float rho;              // repetition penalty on the text row; 1 = off
+  int pad[2];
+};
+constexpr int SAMPLE_REP = 64;       // chosen text tokens the penalty looks back over
+constexpr int SAMPLE_MAX_N = 32768;  // widest logits row that can be sampled (LDS)
+
+struct FinishArgs {
+  int B, step;          // step -1: text head; 0..dep_q-1: depformer codebook step
+  int n_part;           // argmax partials per slot
+  const float* amax_v; const int* amax_i; int ld_amax;
+  const int* ti; int* to;
+  // next depformer input (step + 1 < dep_q)
+  int dep_q, dd;
+  const float* u;        // [B][dep_q][dd] input projections of z
+  const bf16_t* table;   // input table of step+1 ([rows][dd])
+  const float* alpha;    // first depformer attention-norm alpha
+  float* y; bf16_t* ya; long ya_lo; float* part;
+  // sampling (sp->enabled): the row's full logits, the text row's recent
+  // chosen tokens [B][SAMPLE_REP] (-1 empty), and each slot's (seed, tick)
+  // [B][4]: written by the text finisher from the tick input, read by the
+  // codebook finishers (which may run after the next tick input is in place)
+  const SampleParams* sp;
+  const float* logits; long ld_logits; int n_logits;
+  const int* rep;
+  unsigned* sctx;
+};
+
 struct GemmArgs {
   const bf16_t* W;      // [M][K] in the tile layout (gated: gate rows, up rows from row gate_off)
   int w_keep;           // W is re-read within the tick: load it cacheable (else non-temporal)
@@ -88,6 +121,11 @@ struct GemmArgs {
   // output, computed by every workgroup from `att` instead of read from X
   int fuse_att;
   DepAttnArgs att;
+  // EPI_QKV with B <= DEP_FUSE_B: the input X (and its norm partials) is the
+  // previous step's finisher output, computed by every workgroup from `fin`
+  // (greedy choice only); workgroup 0 also writes the tokens and y
+  int fuse_fin;
+  FinishArgs fin;
 };
 
 // Large-batch path: weight tiles (gate and up tiles counted apart) and
@@ -126,38 +164,6 @@ struct EmbedArgs {
 };
 void launch_embed(const EmbedArgs& a, hipStream_t s);
 
-// Sampling of the token choice (device copy, set by pp_set_sampling).
-struct SampleParams {
-  int enabled;
-  float t_text, t_audio;  // temperatures; 0 = greedy for that row
-  int top_k;              // 0 = off
-  float top_p;            // 1 = off
-  float rho;              // repetition penalty on the text row; 1 = off
-  int pad[2];
-};
-constexpr int SAMPLE_REP = 64;       // chosen text tokens the penalty looks back over
-constexpr int SAMPLE_MAX_N = 32768;  // widest logits row that can be sampled (LDS)
-
-struct FinishArgs {
-  int B, step;          // step -1: text head; 0..dep_q-1: depformer codebook step
-  int n_part;           // argmax partials per slot
-  const float* amax_v; const int* amax_i; int ld_amax;
-  const int* ti; int* to;
-  // next depformer input (step + 1 < dep_q)
-  int dep_q, dd;
-  const float* u;        // [B][dep_q][dd] input projections of z
-  const bf16_t* table;   // input table of step+1 ([rows][dd])
-  const float* alpha;    // first depformer attention-norm alpha
-  float* y; bf16_t* ya; long ya_lo; float* part;
-  // sampling (sp->enabled): the row's full logits, the text row's recent
-  // chosen tokens [B][SAMPLE_REP] (-1 empty), and each slot's (seed, tick)
-  // [B][4]: written by the text finisher from the tick input, read by the
-  // codebook finishers (which may run after the next tick input is in place)
-  const SampleParams* sp;
-  const float* logits; long ld_logits; int n_logits;
-  const int* rep;
-  unsigned* sctx;
-};
 void launch_finish(const FinishArgs& a, hipStream_t s);
 void finish_prepare();  // once per process, before the first finisher launch
 

@@ -393,10 +393,116 @@ void launch_dep_attention(const DepAttnArgs& d, hipStream_t s) {
   }
 }
 
+// (value, index) pairs: larger value wins, then the lower index; index
+// 0x7fffffff marks an empty pair.
+__device__ __forceinline__ bool amax_better(float v2, int i2, float v, int i) {
+  return i2 != 0x7fffffff && (i == 0x7fffffff || v2 > v || (v2 == v && i2 < i));
+}
+
+// The greedy finisher of the previous depformer step (or of the text head),
+// computed by every workgroup of the next step's first QKV projection for
+// its B <= DEP_FUSE_B slots: the same choice as finish_unit (the argmax
+// winner does not depend on the reduction order), the same y = u + table
+// row, and the same x * alpha (hi/lo, into `olds`) and per-16-feature sums
+// of squares (into `fparts`).  Workgroup 0 also writes the tokens and y.
+__device__ void fin_into_lds(const FinishArgs& f, const int B, bf16_t* olds, float* fparts) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  constexpr long OPL = (long)DEP_FUSE_B * DEP_FUSE_D;
+  constexpr int PB = 8;  // partials per thread requested in one batch
+  __shared__ float fsv[GEMM_WAVES];
+  __shared__ int fsi[GEMM_WAVES];
+  __shared__ int tok_s[DEP_FUSE_B];
+  const int nk = f.step + 1, ng = f.dd / 16;
+  // requests that do not depend on the choice go out first: this thread's
+  // item (slot, 16-feature group) of u and alpha, and every slot's partials
+  const bool item = tid < B * ng;
+  const int ib = item ? tid / ng : 0, ig = item ? tid - ib * ng : 0;
+  float uu[16], al[16];
+  {
+    const float* u = f.u + ((long)ib * f.dep_q + nk) * f.dd + ig * 16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uu[i] = item ? u[i] : 0.f;
+      al[i] = item ? f.alpha[ig * 16 + i] : 0.f;
+    }
+  }
+  const int per = (f.n_part + nt - 1) / nt, t0 = tid * per, t1 = min(f.n_part, t0 + per);
+  float vv[DEP_FUSE_B][PB];
+  int ii[DEP_FUSE_B][PB];
+#pragma unroll
+  for (int b = 0; b < DEP_FUSE_B; ++b)
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const bool ok = b < B && t0 + j < t1;
+      vv[b][j] = ok ? f.amax_v[(long)b * f.ld_amax + t0 + j] : 0.f;
+      ii[b][j] = ok ? f.amax_i[(long)b * f.ld_amax + t0 + j] : 0x7fffffff;
+    }
+  for (int b = 0; b < B; ++b) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      if (amax_better(vv[b][j], ii[b][j], bv, bi)) { bv = vv[b][j]; bi = ii[b][j]; }
+    for (int t = t0 + PB; t < t1; ++t) {  // more than PB partials per thread (n_part > PB * nt)
+      const float v = f.amax_v[(long)b * f.ld_amax + t];
+      const int i = f.amax_i[(long)b * f.ld_amax + t];
+      if (amax_better(v, i, bv, bi)) { bv = v; bi = i; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float v2 = __shfl_xor(bv, off);
+      const int i2 = __shfl_xor(bi, off);
+      if (amax_better(v2, i2, bv, bi)) { bv = v2; bi = i2; }
+    }
+    if (lane == 0) {
+      fsv[wave] = bv;
+      fsi[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < nt / 64; ++w)
+        if (amax_better(fsv[w], fsi[w], bv, bi)) { bv = fsv[w]; bi = fsi[w]; }
+      const int forced = f.step < 8 ? f.ti[b * TI_STRIDE + TI_FORCE + 1 + f.step] : -1;
+      const int chosen = forced >= 0 ? forced : bi;
+      if (blockIdx.x == 0) {
+        int* to = f.to + b * TO_STRIDE;
+        if (f.step < 8) {
+          to[TO_PRED + 1 + f.step] = bi;
+          to[TO_CHOSEN + 1 + f.step] = chosen;
+        } else {
+          to[TO_USER + f.step - 8] = bi;
+        }
+      }
+      tok_s[b] = chosen;
+    }
+    __syncthreads();
+  }
+  if (item) {
+    const bf16_t* e = f.table + (long)tok_s[ib] * f.dd + ig * 16;
+    float fe[16];
+    unpack8(ld16(e), fe);
+    unpack8(ld16(e + 8), fe + 8);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = ig * 16 + i;
+      const float v = uu[i] + fe[i];
+      if (blockIdx.x == 0) f.y[(long)ib * f.dd + m] = v;
+      store_split(olds + (long)ib * DEP_FUSE_D + m, OPL, v * al[i]);
+      ss += v * v;
+    }
+    fparts[ib * (DEP_FUSE_D / 16) + ig] = ss;
+  }
+  __syncthreads();
+}
+
 // One 16-row tile (gate+up pair for EPI_GATED) of the GEMM, computed by a
-// 512-thread workgroup; `smem` holds a GemmSmem<RT, NT>.
-template <int EPI, int NT, bool NTL, bool ATT = false>
-__device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t* olds = nullptr) {
+// 512-thread workgroup; `smem` holds a GemmSmem<RT, NT>.  XS: where the
+// input X comes from: 0 global memory; 1 the depformer attention, computed
+// here (ATT); 2 the previous step's finisher, computed here (FIN).
+template <int EPI, int NT, bool NTL, int XS = 0>
+__device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t* olds = nullptr,
+                          float* fparts = nullptr) {
   constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
   constexpr int U = (RT * NT > 1) ? 4 : 8;
   GemmSmem<RT, NT>& sm = *reinterpret_cast<GemmSmem<RT, NT>*>(smem);
@@ -432,18 +538,35 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t*
   // epilogue inputs requested now, consumed after the weight stream
   const EpiPre pre = epi_preload<EPI, NT>(a, tile);
   RmsPre<NT> rp;
-  if (EPI != EPI_RESID) rms_preload<NT>(a, rp);
+  if (EPI != EPI_RESID && XS != 2) rms_preload<NT>(a, rp);
 
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
-  // ATT: the input is the depformer attention output, computed here into LDS
-  // ([plane][slot][DEP_FUSE_D]) while the first weight batch is in flight.
+  // XS 1 / 2: the input is the depformer attention output / the previous
+  // step's finisher output, computed here into LDS ([plane][slot][DEP_FUSE_D])
+  // while the first weight batch is in flight.
   u32x4 pf[RT][U];
   constexpr long OPL = (long)DEP_FUSE_B * DEP_FUSE_D;  // LDS plane stride
-  if constexpr (ATT) {
+  if constexpr (XS != 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) pf[rt][u] = (s0 + u < s1) ? ldw16<NTL>(arow[rt] + (long)(s0 + u) * 512) : zero;
+  }
+  if constexpr (XS == 2) {
+    fin_into_lds(a.fin, a.B, olds, fparts);
+    // the slots' norm partials, in the lanes rms_preload would have used
+    const int lane_ = tid & 63;
+#pragma unroll
+    for (int k = 0; k < (NT * 16 + GEMM_WAVES - 1) / GEMM_WAVES; ++k) {
+      const int c = wave + k * GEMM_WAVES;
+#pragma unroll
+      for (int q = 0; q < RMS_PRE; ++q) {
+        const int i = lane_ + 64 * q;
+        rp.v[k][q] = (c < a.B && i < a.n_part) ? fparts[c * (DEP_FUSE_D / 16) + i] : 0.f;
+      }
+    }
+  }
+  if constexpr (XS == 1) {
     const int ppw = 128 / a.att.head_dim;
     for (int pp = wave * ppw; pp < a.B * a.att.n_heads; pp += GEMM_WAVES * ppw) {
       const DepAttnOut r = a.att.head_dim == 32   ? dep_attend<32>(a.att, pp)
@@ -466,10 +589,10 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t*
       const int k = (s + u) * 32;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
-        av[rt][u] = (ATT && s == s0) ? pf[rt][u] : ok ? ldw16<NTL>(arow[rt] + (long)(s + u) * 512) : zero;
+        av[rt][u] = (XS != 0 && s == s0) ? pf[rt][u] : ok ? ldw16<NTL>(arow[rt] + (long)(s + u) * 512) : zero;
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        if constexpr (ATT) {
+        if constexpr (XS != 0) {
           const bf16_t* xo = olds + (long)(ct * 16 + r16) * DEP_FUSE_D + g * 8 + k;
           bh[ct][u] = (ok && b_ok[ct]) ? *reinterpret_cast<const u32x4*>(xo) : zero;
           bl[ct][u] = (ok && b_ok[ct]) ? *reinterpret_cast<const u32x4*>(xo + OPL) : zero;
@@ -562,7 +685,17 @@ __global__ __launch_bounds__(512) void gemm_halves_kernel(GemmArgs a) {
 __global__ __launch_bounds__(512) void gemm_att_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
   __shared__ __attribute__((aligned(16))) bf16_t olds[2 * DEP_FUSE_B * DEP_FUSE_D];
-  gemm_unit<EPI_RESID, 1, false, true>(a, blockIdx.x, smem, olds);
+  gemm_unit<EPI_RESID, 1, false, 1>(a, blockIdx.x, smem, olds);
+}
+
+// Depformer first QKV projection of a codebook step that computes its input,
+// the previous step's greedy finisher, itself (B <= DEP_FUSE_B): saves the
+// finisher launch of every step.
+__global__ __launch_bounds__(512) void gemm_fin_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) bf16_t olds[2 * DEP_FUSE_B * DEP_FUSE_D];
+  __shared__ float fparts[DEP_FUSE_B * (DEP_FUSE_D / 16)];
+  gemm_unit<EPI_QKV, 1, false, 2>(a, blockIdx.x, smem, olds, fparts);
 }
 
 // ---------------------------------------------------------------------------
@@ -867,6 +1000,10 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
   const int tiles = (a.M + ROWS - 1) / ROWS;
   if (EPI == EPI_RESID && a.fuse_att) {  // caller guarantees B <= DEP_FUSE_B, K <= DEP_FUSE_D
     hipLaunchKernelGGL(gemm_att_kernel, dim3(tiles), dim3(512), 0, s, a);
+    return;
+  }
+  if (EPI == EPI_QKV && a.fuse_fin) {  // caller guarantees B <= DEP_FUSE_B, K <= DEP_FUSE_D, greedy choice
+    hipLaunchKernelGGL(gemm_fin_kernel, dim3(tiles), dim3(512), 0, s, a);
     return;
   }
   if (use_wide(a)) {
@@ -1180,11 +1317,6 @@ void launch_embed(const EmbedArgs& a, hipStream_t s) {
 // Slot b of the finisher, computed by the whole workgroup (up to 512
 // threads).  The argmax selection (largest value, then lowest index) does not
 // depend on the reduction tree, so the block size does not change results.
-// (value, index) pairs: larger value wins, then the lower index; index
-// 0x7fffffff marks an empty pair.
-__device__ __forceinline__ bool amax_better(float v2, int i2, float v, int i) {
-  return i2 != 0x7fffffff && (i == 0x7fffffff || v2 > v || (v2 == v && i2 < i));
-}
 
 // ---------------------------------------------------------------------------
 // Sampling variant of the token choice (the guides' deployment knobs:
