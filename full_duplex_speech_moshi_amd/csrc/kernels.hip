@@ -1363,10 +1363,10 @@ __device__ __forceinline__ unsigned order_key(float x) {
 }
 
 struct SampleSmem {
-  float f[SAMPLE_NT];
   int i[SAMPLE_NT];
   float red[4];
   int redi[4];
+  float red3[3][4];
 };
 
 __device__ __forceinline__ float blk_sum(float v, SampleSmem& sh) {
@@ -1377,6 +1377,22 @@ __device__ __forceinline__ float blk_sum(float v, SampleSmem& sh) {
   if (lane == 0) sh.red[wave] = v;
   __syncthreads();
   return ((sh.red[0] + sh.red[1]) + sh.red[2]) + sh.red[3];
+}
+
+// three sums at once (the 4-way threshold search)
+__device__ __forceinline__ void blk_sum3(float (&v)[3], SampleSmem& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v[j] += __shfl_xor(v[j], off);
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) sh.red3[j][wave] = v[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 3; ++j) v[j] = ((sh.red3[j][0] + sh.red3[j][1]) + sh.red3[j][2]) + sh.red3[j][3];
 }
 
 __device__ __forceinline__ int blk_isum(int v, SampleSmem& sh) {
@@ -1493,13 +1509,23 @@ __device__ int sample_row(const FinishArgs& a, const int b, const unsigned* ctx,
   for (int i = i0; i < i1; ++i) z[i] = z[i] / T + 0.0f;  // + 0 turns -0 into +0
   __syncthreads();
   if (sp.top_k > 0 && sp.top_k < n) {
+    // res = the largest key t with count(key >= t) >= k (the k-th largest),
+    // two bits per pass: the counts of the three candidates go out together
     unsigned res = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const unsigned cand = res | (1u << bit);
-      int c = 0;
+    for (int sh2 = 30; sh2 >= 0; sh2 -= 2) {
+      float c[3] = {0.f, 0.f, 0.f};  // counts below 2^24: exact in fp32
 #pragma unroll 8
-      for (int i = i0; i < i1; ++i) c += order_key(z[i]) >= cand;
-      if (blk_isum(c, sh) >= sp.top_k) res = cand;
+      for (int i = i0; i < i1; ++i) {
+        const unsigned k = order_key(z[i]);
+#pragma unroll
+        for (int d = 1; d <= 3; ++d) c[d - 1] += k >= (res | ((unsigned)d << sh2)) ? 1.f : 0.f;
+      }
+      blk_sum3(c, sh);
+      int dd = 0;
+#pragma unroll
+      for (int d = 1; d <= 3; ++d)
+        if (c[d - 1] >= (float)sp.top_k) dd = d;
+      res |= (unsigned)dd << sh2;
     }
     int gt = 0, eq = 0;
 #pragma unroll 8
@@ -1533,13 +1559,24 @@ __device__ int sample_row(const FinishArgs& a, const int b, const unsigned* ctx,
   __syncthreads();
   if (sp.top_p < 1.f) {
     const float target = sp.top_p * blk_sum(cs, sh);
-    unsigned res = 0;  // 0 <= p <= 1: its bits order like its value and stay below 2^30
-    for (int bit = 29; bit >= 0; --bit) {
-      const unsigned cand = res | (1u << bit);
-      float sm = 0.f;
+    // res = the largest t with the sum of p over bits(p) >= t reaching the
+    // target (0 <= p <= 1: its bits order like its value and stay below
+    // 2^30); two bits per pass, three candidate sums together
+    unsigned res = 0;
+    for (int sh2 = 28; sh2 >= 0; sh2 -= 2) {
+      float sm[3] = {0.f, 0.f, 0.f};
 #pragma unroll 8
-      for (int i = i0; i < i1; ++i) sm += __float_as_uint(z[i]) >= cand ? z[i] : 0.f;
-      if (blk_sum(sm, sh) >= target) res = cand;
+      for (int i = i0; i < i1; ++i) {
+        const unsigned k = __float_as_uint(z[i]);
+#pragma unroll
+        for (int d = 1; d <= 3; ++d) sm[d - 1] += k >= (res | ((unsigned)d << sh2)) ? z[i] : 0.f;
+      }
+      blk_sum3(sm, sh);
+      int dd = 0;
+#pragma unroll
+      for (int d = 1; d <= 3; ++d)
+        if (sm[d - 1] >= target) dd = d;
+      res |= (unsigned)dd << sh2;
     }
     float g = 0.f, eq = 0.f;
 #pragma unroll 8
