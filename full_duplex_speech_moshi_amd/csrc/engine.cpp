@@ -115,7 +115,7 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
                                              {EPI_GATED, dF}, {EPI_LOGITS, A}};
   L.wide_part_max = 0;
   for (const auto& g : wide) L.wide_part_max = std::max(L.wide_part_max, wide_part_floats(g.epi, (int)g.M));
-  L.split_part = B > 16 ? take((size_t)L.wide_part_max * 4) : take(0);
+  L.split_part = B >= WIDE_MIN_B ? take((size_t)L.wide_part_max * 4) : take(0);
   L.wide_rms = take(MAX_COLS * 4);
   L.rope = take((size_t)B * hd * 4);
   L.samp = take(sizeof(SampleParams));

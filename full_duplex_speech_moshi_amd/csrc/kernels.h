@@ -130,6 +130,10 @@ struct GemmArgs {
 
 // Large-batch path: weight tiles (gate and up tiles counted apart) and
 // partial floats (8 ranges x 512 per weight tile).
+// The large-batch GEMM path (split k-ranges, activation slice in LDS) from
+// this batch on, for K >= 4096: its cost hardly depends on B, and it beats
+// the small-batch path (activations read per tile) from about B = 13.
+constexpr int WIDE_MIN_B = 13;
 inline long wide_tiles(int epi, int M) { return (epi == EPI_GATED ? 2L : 1L) * ((M + ROWS - 1) / ROWS); }
 inline long wide_part_floats(int epi, int M) { return wide_tiles(epi, M) * 8 * 512; }
 

@@ -699,7 +699,7 @@ __global__ __launch_bounds__(512) void gemm_fin_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The same GEMM for large batches (B > 16, K >= 4096).  The per-slot
+// The same GEMM for large batches (B >= WIDE_MIN_B, K >= 4096).  The per-slot
 // arithmetic is the contract above, computed in another order of work.  At
 // B = 32 the activation operand is 4x the weight bytes per k-step, so it is
 // staged in LDS and shared by 8 weight tiles:
@@ -991,9 +991,9 @@ void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s) {
 
 // Path choice per launch: both paths compute the same bits (the contract),
 // so the choice only moves time.  The k-range split pays off once the
-// activation operand outweighs the weights (B > 16) and the k-ranges are long
-// enough to amortise staging and the partial exchange (K >= 4096).
-static bool use_wide(const GemmArgs& a) { return a.B > 16 && a.K >= 4096; }
+// activation operand outweighs the weights (B >= WIDE_MIN_B) and the k-ranges
+// are long enough to amortise staging and the partial exchange (K >= 4096).
+static bool use_wide(const GemmArgs& a) { return a.B >= WIDE_MIN_B && a.K >= 4096; }
 
 template <int EPI>
 static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
