@@ -84,6 +84,7 @@ struct FinishArgs {
 struct GemmArgs {
   const bf16_t* W;      // [M][K] in the tile layout (gated: gate rows, up rows from row gate_off)
   int w_keep;           // W is re-read within the tick: load it cacheable (else non-temporal)
+  int slot_grp;         // slots per workgroup of gemm_group_kernel (set by the launcher)
   const bf16_t* X;      // activations as a bf16 pair: hi plane [B][ldx], lo plane at X + x_lo
   long x_lo;
   int M, K, ldx, B;

@@ -657,6 +657,7 @@ __device__ __forceinline__ GemmArgs slot_view(const GemmArgs& a, const int s0, c
   v.X = a.X + (long)s0 * a.ldx;
   if (a.part_in) v.part_in = a.part_in + (long)s0 * a.n_part;
   if (a.q_out) v.q_out = a.q_out + (long)s0 * a.ldq;
+  if (a.rope) v.rope = a.rope + (long)s0 * a.head_dim;
   if (a.kv) v.kv = a.kv + (long)s0 * a.kv_slot_stride;
   if (a.ti) v.ti = a.ti + (long)s0 * TI_STRIDE;
   if (a.x) v.x = a.x + (long)s0 * a.ldres;
@@ -670,13 +671,16 @@ __device__ __forceinline__ GemmArgs slot_view(const GemmArgs& a, const int s0, c
   return v;
 }
 
-// B in 17..32 with cache-resident weights: two 16-slot halves (blockIdx.y),
-// each the B <= 16 kernel; the weights are read twice, from the cache.
+// Slot groups: blockIdx.y takes slots G*y .. G*y+G-1 (G = a.slot_grp <= 16),
+// each group the 16-column kernel; the weights are read once per group, so
+// this serves cache-resident weights.  It trades weight re-reads for fewer
+// activation bytes per workgroup, which is what bounds these launches once
+// the batch is large.
 template <int EPI, bool NTL>
-__global__ __launch_bounds__(512) void gemm_halves_kernel(GemmArgs a) {
+__global__ __launch_bounds__(512) void gemm_group_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
-  const int s0 = blockIdx.y * 16;
-  const GemmArgs v = slot_view(a, s0, min(16, a.B - s0));
+  const int s0 = blockIdx.y * a.slot_grp;
+  const GemmArgs v = slot_view(a, s0, min(a.slot_grp, a.B - s0));
   gemm_unit<EPI, 1, NTL>(v, blockIdx.x, smem);
 }
 
@@ -995,6 +999,21 @@ void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s) {
 // are long enough to amortise staging and the partial exchange (K >= 4096).
 static bool use_wide(const GemmArgs& a) { return a.B >= WIDE_MIN_B && a.K >= 4096; }
 
+// Slots per workgroup for the other paths: 32 (both column tiles in one
+// workgroup) or a group size G <= 16 (gemm_group_kernel, blockIdx.y = slot
+// group).  Weights streamed from HBM once per tick are never split: every
+// group would stream them again.  Cache-resident weights may be: each group
+// re-reads them from the cache and carries G/B of the activation bytes.
+// That pays for the depformer down-projection (K = 2816 > M = 1024, the
+// largest activation row): four groups took 0.18 ms off the 7B device tick
+// at B = 16 and 0.04 ms at B = 8, and were neutral at B = 32 and B = 4,
+// while splitting the other depformer GEMMs further was neutral or slower.
+static int slot_group(int epi, const GemmArgs& a) {
+  if (a.w_keep && epi == EPI_RESID && a.K > a.M && a.B >= 8) return (a.B + 3) / 4;
+  if (a.B <= 16) return 16;
+  return a.w_keep ? 16 : 32;
+}
+
 template <int EPI>
 static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
   const int tiles = (a.M + ROWS - 1) / ROWS;
@@ -1019,12 +1038,21 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
                          w);
     }
     hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, w);
-  } else if (a.B > 16) {
-    if (a.w_keep) hipLaunchKernelGGL((gemm_halves_kernel<EPI, false>), dim3(tiles, 2), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<EPI, 2, true>), dim3(tiles), dim3(512), 0, s, a);
   } else {
-    if (a.w_keep) hipLaunchKernelGGL((gemm_kernel<EPI, 1, false>), dim3(tiles), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<EPI, 1, true>), dim3(tiles), dim3(512), 0, s, a);
+    const int G = slot_group(EPI, a);
+    GemmArgs v = a;
+    v.slot_grp = G;
+    const unsigned groups = (unsigned)((a.B + G - 1) / G);
+    if (G > 16) {
+      if (a.w_keep) hipLaunchKernelGGL((gemm_kernel<EPI, 2, false>), dim3(tiles), dim3(512), 0, s, v);
+      else hipLaunchKernelGGL((gemm_kernel<EPI, 2, true>), dim3(tiles), dim3(512), 0, s, v);
+    } else if (groups > 1) {
+      if (a.w_keep) hipLaunchKernelGGL((gemm_group_kernel<EPI, false>), dim3(tiles, groups), dim3(512), 0, s, v);
+      else hipLaunchKernelGGL((gemm_group_kernel<EPI, true>), dim3(tiles, groups), dim3(512), 0, s, v);
+    } else {
+      if (a.w_keep) hipLaunchKernelGGL((gemm_kernel<EPI, 1, false>), dim3(tiles), dim3(512), 0, s, v);
+      else hipLaunchKernelGGL((gemm_kernel<EPI, 1, true>), dim3(tiles), dim3(512), 0, s, v);
+    }
   }
 }
 

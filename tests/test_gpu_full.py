@@ -167,9 +167,40 @@ def test_full_isolation_large_batch_path_bit_exact(full):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("B", [8, 16])
+def test_full_isolation_slot_groups_bit_exact(full, B):
+    """B = 8 and 16 run the depformer down-projection in slot groups of 2 and
+    4 slots per workgroup (B = 16 also takes the large-batch temporal path);
+    the first and last slots must equal B = 1 handles bit for bit."""
+    _say(f"case: 7B isolation, B={B} (depformer slot groups) vs B=1")
+    fill = synth.ring_fill(DM, 9, 24)
+    codes = [synth.user_codes(900 + b, 2) for b in range(B)]
+    eb = _engine(full, B)
+    eb.ring_fill(B - 1, *fill)
+    toks, taps = [], []
+    for t in range(2):
+        toks.append(eb.step(np.stack([codes[b][t] for b in range(B)])))
+        taps.append(eb.taps())
+    eb.close()
+    for b in (0, B - 1):
+        e1 = _engine(full, 1)
+        if b == B - 1:
+            e1.ring_fill(0, *fill)
+        for t in range(2):
+            tk = e1.step(codes[b][t:t + 1])
+            tp = e1.taps()
+            np.testing.assert_array_equal(tk[0], toks[t][b])
+            np.testing.assert_array_equal(tp["hidden"][:, 0], taps[t]["hidden"][:, b])
+            np.testing.assert_array_equal(tp["text_logits"][0], taps[t]["text_logits"][b])
+            np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
+            np.testing.assert_array_equal(tp["user_pred"][0], taps[t]["user_pred"][b])
+        e1.close()
+
+
+@pytest.mark.timeout(900)
 def test_full_isolation_b32_bit_exact(full):
     """B = 32, the batch the large-batch benchmarks run (large-batch GEMM path,
-    depformer slot halves, standalone depformer attention): slots 0, 7 and 31
+    depformer slot groups, standalone depformer attention): slots 0, 7 and 31
     with occupancies 0, 300 and 700 equal B = 1 handles bit for bit."""
     _say("case: 7B isolation, B=32 vs B=1, occupancy 0/300/700")
     B = 32
