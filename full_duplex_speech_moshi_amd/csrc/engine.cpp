@@ -296,6 +296,8 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       g.rope = h->at<float>(L.rope);
       g.split_part = split_part;
       g.wide_rms = wide_rms;
+      // large-batch path: the decode pass below finishes q, k and v itself
+      g.qkv_to_attn = gemm_splits_k(EPI_QKV, g) ? 1 : 0;
       launch_gemm(EPI_QKV, g, s);
       if (keep_timed) h->timed[0].push_back([g](hipStream_t st) { launch_gemm(EPI_QKV, g, st); });
       if (keep_timed && l == 0) {
@@ -319,6 +321,11 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       at.ldo = d;
       at.o_lo = (long)B * d;
       at.cnt = h->at<unsigned>(L.att_cnt);
+      if (g.qkv_to_attn) {
+        at.qkv_part = split_part;
+        at.qkv_rms = wide_rms;
+        at.rope = h->at<float>(L.rope);
+      }
       launch_attention(at, s);
       if (keep_timed) h->timed[1].push_back([at](hipStream_t st) { launch_attention(at, st); });
       if (keep_timed && l == 0) {

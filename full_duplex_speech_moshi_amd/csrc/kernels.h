@@ -85,6 +85,8 @@ struct GemmArgs {
   const bf16_t* W;      // [M][K] in the tile layout (gated: gate rows, up rows from row gate_off)
   int w_keep;           // W is re-read within the tick: load it cacheable (else non-temporal)
   int slot_grp;         // slots per workgroup of gemm_group_kernel (set by the launcher)
+  int qkv_to_attn;      // EPI_QKV on the large-batch path: partials stored slot-major and no reduce
+                        // launch; the decode pass finishes q, k and v (AttnArgs::qkv_part)
   const bf16_t* X;      // activations as a bf16 pair: hi plane [B][ldx], lo plane at X + x_lo
   long x_lo;
   int M, K, ldx, B;
@@ -139,13 +141,15 @@ inline long wide_tiles(int epi, int M) { return (epi == EPI_GATED ? 2L : 1L) * (
 inline long wide_part_floats(int epi, int M) { return wide_tiles(epi, M) * 8 * 512; }
 
 void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s);
+// True when launch_gemm takes the large-batch (k-range split) path for `a`.
+bool gemm_splits_k(Epi epi, const GemmArgs& a);
 void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s);
 inline long packed_elems(int M, int K) { return (long)((M + ROWS - 1) / ROWS) * ROWS * K; }
 
 struct AttnArgs {
   const float* q;       // [B][ldq], head h at q + h*head_dim
   int ldq;
-  const bf16_t* kv;     // ring base of this layer (see GemmArgs)
+  bf16_t* kv;           // ring base of this layer (see GemmArgs); written only on the large-batch path
   long kv_slot_stride, kv_v_off;
   int n_heads, head_dim, window, B;
   const int* ti; int pos_const;
@@ -155,6 +159,14 @@ struct AttnArgs {
   int ldo;
   long o_lo;
   unsigned* cnt;        // [B][n_heads] split tickets, zero between launches (unused with one split)
+  // Large-batch path: q, k and v are not formed by the QKV launch.  Each
+  // workgroup sums its head's q rows from the QKV k-range partials
+  // ([tile][8 ranges][32 slots][16 rows] fp32), scales them by the slot's
+  // inverse RMS and rotates them (rope: [B][head_dim] cos/sin); the last
+  // split also forms k and v and writes them to the ring.  Null otherwise.
+  const float* qkv_part;
+  const float* qkv_rms;   // [MAX_COLS]
+  const float* rope;
 };
 
 void launch_attention(const AttnArgs& a, hipStream_t s);

@@ -206,6 +206,22 @@ __device__ __forceinline__ EpiPre epi_preload(const GemmArgs& a, const int tile)
   return p;
 }
 
+// The QKV epilogue's arithmetic for rows (2i, 2i+1) of one slot: the ordered
+// sums s0, s1 scaled by the slot's inverse RMS, then, for q and k, rotated by
+// the pair's (cos, sin) at the slot's position (interleaved RoPE).  Every
+// path that finishes q, k or v goes through this function.
+__device__ __forceinline__ void qkv_pair(float s0, float s1, float inv, bool rot, float cs, float sn, float& y0,
+                                         float& y1) {
+  y0 = s0 * inv;
+  y1 = s1 * inv;
+  if (rot) {
+    const float r0 = y0 * cs - y1 * sn;
+    const float r1 = y0 * sn + y1 * cs;
+    y0 = r0;
+    y1 = r1;
+  }
+}
+
 // Epilogue of one finished tile (rows 16*tile..): e.fin holds W x for the
 // tile's rows and every slot, e.inv_rms the slots' inverse RMS where needed.
 template <int EPI, int NT>
@@ -220,25 +236,20 @@ __device__ void gemm_epilogue(const GemmArgs& a, const int tile, EpiSmem<(EPI ==
       if (c >= a.B) continue;
       const int r = row0 + 2 * pr;
       if (r >= a.M) continue;
-      float y0 = e.fin[0][2 * pr][c] * e.inv_rms[c];
-      float y1 = e.fin[0][2 * pr + 1][c] * e.inv_rms[c];
       const int which = r / d;  // 0 q, 1 k, 2 v
       const int rr = r - which * d;
       const int h = rr / a.head_dim, dd = rr - h * a.head_dim;
       // workgroup: item idx == tid, pre holds its position and rotation
       const int pos = pre.pos;
-      if (which < 2 && a.inv_freq) {
-        float cs = pre.cs, sn = pre.sn;
-        if (!a.rope) {
-          const double th = (double)pos * a.inv_freq[dd >> 1];
-          cs = (float)cos(th);
-          sn = (float)sin(th);
-        }
-        const float r0 = y0 * cs - y1 * sn;
-        const float r1 = y0 * sn + y1 * cs;
-        y0 = r0;
-        y1 = r1;
+      const bool rot = which < 2 && a.inv_freq;
+      float cs = pre.cs, sn = pre.sn;
+      if (rot && !a.rope) {
+        const double th = (double)pos * a.inv_freq[dd >> 1];
+        cs = (float)cos(th);
+        sn = (float)sin(th);
       }
+      float y0, y1;
+      qkv_pair(e.fin[0][2 * pr][c], e.fin[0][2 * pr + 1][c], e.inv_rms[c], rot, cs, sn, y0, y1);
       if (which == 0) {
         a.q_out[(long)c * a.ldq + rr] = y0;
         a.q_out[(long)c * a.ldq + rr + 1] = y1;
@@ -720,6 +731,25 @@ __global__ __launch_bounds__(512) void gemm_fin_kernel(GemmArgs a) {
 
 constexpr int WIDE_SK = 8;  // k-steps per stage (activations in LDS, weights in registers)
 
+// Store p_j of weight tile t.  Default layout [t][j][ct][q][lane] (the
+// reduce kernel reads it with one thread per element); with qkv_to_attn,
+// slot-major [t][j][slot][16 rows], so that the decode pass reads one slot's
+// 16 rows as 64 contiguous bytes.  MFMA accumulator q of lane l holds row
+// 4 * (l >> 4) + q of column (slot) ct * 16 + (l & 15).
+__device__ __forceinline__ void store_partial(const GemmArgs& a, long t, int j, const f32x4 (&acc)[2], int lane) {
+  if (a.qkv_to_attn) {
+    float* P = a.split_part + (t * GEMM_WAVES + j) * 512 + (lane & 15) * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) *reinterpret_cast<f32x4*>(P + ct * 256) = acc[ct];
+  } else {
+    float* P = a.split_part + (t * GEMM_WAVES + j) * 512 + lane;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) P[ct * 256 + q * 64] = acc[ct][q];
+  }
+}
+
 // LDS rows of the activation slice are 64 bytes (32 bf16 of one column);
 // the 16-byte chunk `part` of column c is stored at chunk part ^ ((c >> 1) & 3),
 // so the 8 lanes of a 128-bit read (8 consecutive columns, one chunk) hit 8
@@ -821,14 +851,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < WIDE_SK; ++u) wr[u] = wn[u];
   }
-  // p_j of tile t: [t][j][ct][q][lane]
-  if (t_ok) {
-    float* P = a.split_part + ((long)t * GEMM_WAVES + j) * (NT * 256) + lane;
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) P[ct * 256 + q * 64] = acc[ct][q];
-  }
+  if (t_ok) store_partial(a, t, j, acc, lane);
 }
 
 // The same partials for k-ranges of exactly WIDE_RES k-steps (K = 4096):
@@ -923,14 +946,7 @@ __global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < WIDE_RES; ++q) mul(q, acc);
     }
-    // p_j of tile t: [t][j][ct][q][lane]
-    if (t < T) {
-      float* Pp = a.split_part + (t * GEMM_WAVES + j) * (NT * 256) + lane;
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) Pp[ct * 256 + q * 64] = acc[ct][q];
-    }
+    if (t < T) store_partial(a, t, j, acc, lane);
   }
 }
 
@@ -1037,7 +1053,7 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s,
                          w);
     }
-    hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, w);
+    if (!(EPI == EPI_QKV && a.qkv_to_attn)) hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, w);
   } else {
     const int G = slot_group(EPI, a);
     GemmArgs v = a;
@@ -1054,6 +1070,10 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
       else hipLaunchKernelGGL((gemm_kernel<EPI, 1, true>), dim3(tiles), dim3(512), 0, s, v);
     }
   }
+}
+
+bool gemm_splits_k(Epi epi, const GemmArgs& a) {
+  return !(epi == EPI_RESID && a.fuse_att) && !(epi == EPI_QKV && a.fuse_fin) && use_wide(a);
 }
 
 void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s) {
@@ -1113,8 +1133,10 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
   const int sub = lane % LPK, kg = lane / LPK;
   const float scale = 1.0f / sqrtf((float)DH);
 
+  const bool fused = a.qkv_part != nullptr;
+  const bool last = c == P.nc - 1;  // the split that holds the current position (its last key)
   float qv[8];
-  {
+  if (!fused) {
     const float* qp = a.q + (long)b * a.ldq + h * DH + sub * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) qv[i] = qp[i];
@@ -1136,13 +1158,73 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
     }
   }
 
+  // Large-batch path: finish this head's q (and, in the last split, k and v)
+  // from the QKV partials while the keys and values are in flight.  Row r of
+  // vector `which` (0 q, 1 k, 2 v) is GEMM row which * d + h * DH + r, in
+  // tile T = row / 16; the 8 range partials of (T, slot b) are 16 contiguous
+  // rows.  Sums in range order, then qkv_pair: the bits of the reduce kernel.
+  __shared__ float qp_s[3][DH][GEMM_WAVES + 1];
+  __shared__ float q_s[DH];
+  __shared__ __attribute__((aligned(16))) bf16_t kv_s[2][DH];
+  if (fused) {
+    const int nvec = last ? 3 : 1;
+    const int tiles_d = a.n_heads * DH / ROWS;
+    // piece i: vector i / (2 DH), tile (i / 32) % (DH / 16), range (i / 4) % 8,
+    // rows 4 (i % 4) .. +3 (16 bytes)
+#pragma unroll 1
+    for (int i = threadIdx.x; i < nvec * 2 * DH; i += blockDim.x) {
+      const int which = i / (2 * DH), ii = i - which * 2 * DH;
+      const int ti = ii >> 5, jj = (ii >> 2) & 7, qq = ii & 3;
+      const long T = (long)which * tiles_d + h * (DH / ROWS) + ti;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.qkv_part + ((T * GEMM_WAVES + jj) * MAX_COLS + b) * 16 + 4 * qq);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qp_s[which][ti * 16 + 4 * qq + r][jj] = v[r];
+    }
+    __syncthreads();
+    const int pos = P.pos;
+    if ((int)threadIdx.x < nvec * (DH / 2)) {
+      const int which = threadIdx.x / (DH / 2), pr = threadIdx.x - which * (DH / 2);
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < GEMM_WAVES; ++jj) s0 += qp_s[which][2 * pr][jj];
+#pragma unroll
+      for (int jj = 0; jj < GEMM_WAVES; ++jj) s1 += qp_s[which][2 * pr + 1][jj];
+      const float cs = a.rope[(long)b * DH + 2 * pr], sn = a.rope[(long)b * DH + 2 * pr + 1];
+      float y0, y1;
+      qkv_pair(s0, s1, a.qkv_rms[b], which < 2, cs, sn, y0, y1);
+      if (which == 0) {
+        q_s[2 * pr] = y0;
+        q_s[2 * pr + 1] = y1;
+      } else {
+        const bf16_t e0 = f2bf(y0), e1 = f2bf(y1);
+        kv_s[which - 1][2 * pr] = e0;
+        kv_s[which - 1][2 * pr + 1] = e1;
+        bf16_t* dst = a.kv + (long)b * a.kv_slot_stride + (which == 2 ? a.kv_v_off : 0) +
+                      ((long)h * a.window + (pos % a.window)) * DH + 2 * pr;
+        dst[0] = e0;
+        dst[1] = e1;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = q_s[sub * 8 + i];
+  }
+  // the current key and value (last key of the last split) from LDS: the
+  // ring row loaded above still holds the position W ticks back
+  auto key_at = [&](int it, int j) -> u32x4 {
+    return (fused && last && j == kn - 1) ? *reinterpret_cast<const u32x4*>(&kv_s[0][sub * 8]) : kr[it];
+  };
+  auto val_at = [&](int it, int j) -> u32x4 {
+    return (fused && last && j == kn - 1) ? *reinterpret_cast<const u32x4*>(&kv_s[1][sub * 8]) : vr[it];
+  };
+
   float s[ITER];
   float mloc = -INFINITY;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int j = active ? wave * 64 + it * KPI + kg : ATT_CHUNK;
     float kf[8];
-    unpack8(kr[it], kf);
+    unpack8(key_at(it, j), kf);
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) dot += qv[i] * kf[i];
@@ -1163,7 +1245,7 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
       const float p = expf(s[it] - mloc);
       if (sub == 0) lsum += p;
       float vf[8];
-      unpack8(vr[it], vf);
+      unpack8(val_at(it, j), vf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] += p * vf[i];
     }
