@@ -116,7 +116,7 @@ struct GemmArgs {
   long m_lo;
   float* f_out; long ldf;        // store / logits: [B][ldf] fp32
   float* amax_v; int* amax_i; int ld_amax;  // logits: per-workgroup (max, argmax) [B][ld_amax]
-  // large-batch path (B > 16): per-tile partial sums, and the slots' inverse
+  // large-batch path (B >= WIDE_MIN_B): per-tile partial sums, and the slots' inverse
   // RMS (computed once per launch by the main kernel, read by the reduce)
   float* split_part;    // [weight tile][8 ranges][512] fp32
   float* wide_rms;      // [MAX_COLS] fp32
