@@ -539,6 +539,28 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t*
     b_ok[ct] = c < a.B;
     xrow[ct] = a.X + (long)(b_ok[ct] ? c : 0) * a.ldx + g * 8;
   }
+  // With more than a few slots the activation rows are loaded in row order
+  // (lane 4c + p takes 16-byte piece p of slot c's 64 bytes, so each group
+  // of 4 lanes reads one contiguous piece instead of 4 rows 2 KB apart) and
+  // moved into the MFMA operand order (lane 16p + c) by a lane permute
+  // before use; the operand values are the same either way.
+  const bool xperm = XS == 0 && a.B > 4;
+  const int xsrc = ((lane & 15) * 4 + (lane >> 4)) * 4;  // permute source (bytes) of this lane
+  if (xperm) {
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const int c = ct * 16 + (lane >> 2);
+      b_ok[ct] = c < a.B;
+      xrow[ct] = a.X + (long)(b_ok[ct] ? c : 0) * a.ldx + (lane & 3) * 8;
+    }
+  }
+  auto xop = [&](const u32x4& v) -> bf16x8 {
+    if (!xperm) return __builtin_bit_cast(bf16x8, v);
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc, (int)v[i]);
+    return __builtin_bit_cast(bf16x8, r);
+  };
 
   f32x4 acc[RT][NT];
 #pragma unroll
@@ -621,10 +643,8 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t*
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
           const bf16x8 w8 = __builtin_bit_cast(bf16x8, av[rt][u]);
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh[ct][u]),
-                                                                acc[rt][ct], 0, 0, 0);
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl[ct][u]),
-                                                                acc[rt][ct], 0, 0, 0);
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, xop(bh[ct][u]), acc[rt][ct], 0, 0, 0);
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, xop(bl[ct][u]), acc[rt][ct], 0, 0, 0);
         }
   }
 
