@@ -1,0 +1,85 @@
+"""bench.py on the host: the algorithmic byte counts its roofline uses, the
+one-GPU contract, and the HBM-traffic summary built from rocprofv3 counter
+files (synthetic files here; no GPU)."""
+import csv
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from full_duplex_speech_moshi_amd import synth  # noqa: E402
+
+
+def test_weight_bytes_per_tick_match_the_shape_arithmetic():
+    # 32 layers of 3d^2 + d^2 + 2Fd + dF bf16, the text head, 16 input
+    # projections, 6 depformer layers and 16 heads, plus the fp32 norm scales
+    # (65 temporal and 13 depformer rows): 13,772,066,816 bytes at 7B.
+    assert bench.weight_stream_bytes(synth.FULL) == 13_772_066_816
+
+
+@pytest.mark.parametrize("n", [0, 1, 250, 3000])
+def test_slot_bytes_are_rows_plus_keys(n):
+    # 17 temporal + 16 depformer embedding rows, then K and V of every layer
+    # for each of the slot's n keys: 172,032 + 524,288 n bytes at 7B.
+    assert bench.slot_bytes(synth.FULL, n) == 172_032 + 524_288 * n
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _counter_csv(path, name, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for kern, grid, val in rows:
+            w.writerow({"Kernel_Name": kern, "Grid_Size": grid, "Workgroup_Size": 512, "Counter_Name": name,
+                        "Counter_Value": val})
+
+
+def test_traffic_summary_scales_counters_by_the_copy_probe(tmp_path, monkeypatch):
+    # a stand-in repository: the summary hashes kernels.hip and writes
+    # profiles/traffic.json under ROOT
+    src = tmp_path / "full_duplex_speech_moshi_amd" / "csrc"
+    src.mkdir(parents=True)
+    (src / "kernels.hip").write_bytes(b"// kernels\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    run = tmp_path / "run"
+    copy_kib = bench.COPY_PROBE_BYTES / 1024
+    dom = f"void pp::{bench.DOMINANT_KERNEL}(pp::GemmArgs)"
+    grid = bench.DOMINANT_WGS * 512
+    # FETCH_SIZE reads half the copy probe's bytes (scale 2), WRITE_SIZE all of them
+    _counter_csv(str(run / "pmc_fetch" / "c1_counter_collection.csv"), "FETCH_SIZE",
+                 [("__amd_rocclr_copyBuffer", 256 * 512, copy_kib / 2), (dom, grid, 1000.0), (dom, grid, 1002.0),
+                  (dom, 3 * 512, 5.0), ("void pp::other(pp::GemmArgs)", grid, 7.0)])
+    _counter_csv(str(run / "pmc_write" / "c1_counter_collection.csv"), "WRITE_SIZE",
+                 [("__amd_rocclr_copyBuffer", 256 * 512, copy_kib), (dom, grid, 4.0), (dom, grid, 4.0)])
+    algo = 2_000_000.0
+    (run / "traffic_mode.json").write_text(json.dumps({"copy_probe_bytes": bench.COPY_PROBE_BYTES,
+                                                       "algorithmic_bytes_per_launch": algo}))
+    bench.summarize_traffic(str(run))
+    t = json.load(open(tmp_path / "profiles" / "traffic.json"))
+    assert t["dispatches"] == 2  # other kernels and other grid sizes are left out
+    assert t["fetch_scale"] == pytest.approx(2.0)
+    assert t["write_scale"] == pytest.approx(1.0)
+    assert t["bytes_per_launch"] == round(1024 * (1001.0 * 2.0 + 4.0))
+    assert t["kernels_hip_sha256_16"] == hashlib.sha256(b"// kernels\n").hexdigest()[:16]
+    # reported only for the same kernel source and the same launch shape
+    assert bench.measured_traffic(algo) == t["bytes_per_launch"]
+    assert bench.measured_traffic(2 * algo) is None
+    (src / "kernels.hip").write_bytes(b"// kernels, changed\n")
+    assert bench.measured_traffic(algo) is None
