@@ -33,6 +33,13 @@ def test_exports_every_declared_entry_point(lib):
         assert getattr(lib, n) is not None
 
 
+def test_binding_limits_match_the_header():
+    src = open(os.path.join(ROOT, "include", "pp.h")).read()
+    limits = {k: int(v) for k, v in re.findall(r"#define\s+(PP_MAX_\w+)\s+(\d+)", src)}
+    assert limits["PP_MAX_BATCH"] == pp.PP_MAX_BATCH
+    assert limits["PP_MAX_WINDOW"] == pp.PP_MAX_WINDOW
+
+
 def test_arena_bytes_matches_ring_layout(lib):
     dims = pp.make_dims(synth.FULL)
     n1 = pp.pp_arena_bytes(dims, 1, 3000)

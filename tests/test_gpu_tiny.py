@@ -222,6 +222,36 @@ def test_ring_fill_then_teacher_forced_parity(tiny_weights, dev):
     assert not fails, "\n".join(fails[:20])
 
 
+def test_max_window_ring_wraps_teacher_forced_parity(tiny_weights, dev):
+    """The largest window (4096 frames: 16 splits of 256 keys per head, the
+    most the decode combines) with B = 2: slot 0 pre-filled to 4090 frames,
+    so the ring fills and wraps during the run; slot 1 pre-filled to 1000
+    (4 splits).  10 teacher-forced ticks per slot against the oracle."""
+    from full_duplex_speech_moshi_amd import pp
+    Wm, n, fills = pp.PP_MAX_WINDOW, 10, (4090, 1000)
+    _say(f"case: window {Wm}, fills {fills}, {n} teacher-forced ticks, B=2")
+    codes = [synth.user_codes(40 + b, n) for b in range(2)]
+    kv = [synth.ring_fill(DM, 50 + b, f) for b, f in enumerate(fills)]
+    recs = []
+    for b in range(2):
+        o = Oracle(DM, tiny_weights, 1, Wm)
+        o.ring_fill(0, *kv[b])
+        recs.append(parity.oracle_run(o, codes[b]))
+    e = engine(tiny_weights, dev, 2, Wm)
+    for b in range(2):
+        e.ring_fill(b, *kv[b])
+        e.prefill_forced(b, parity.teacher_frames(recs[b], codes[b]))
+    fails, rep = [], {}
+    for t in range(n):
+        e.step(np.zeros((2, 8), np.int32))
+        tp = e.taps()
+        for b in range(2):
+            fails += parity.compare_tick(parity.gpu_slot(tp, b), recs[b][t], t, rep)
+    e.close()
+    _say(f"worst hidden rel-L2 {max(rep['hidden_rel_l2']):.3e}")
+    assert not fails, "\n".join(fails[:20])
+
+
 def test_session_open_schedule_parity(tiny_weights, dev):
     """Session-open forced schedule (voice, silence, persona, silence) then free
     ticks, B = 2 with different schedules, teacher-forced on free rows."""
