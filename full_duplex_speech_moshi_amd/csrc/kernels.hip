@@ -511,11 +511,13 @@ __device__ void fin_into_lds(const FinishArgs& f, const int B, bf16_t* olds, flo
 // 512-thread workgroup; `smem` holds a GemmSmem<RT, NT>.  XS: where the
 // input X comes from: 0 global memory; 1 the depformer attention, computed
 // here (ATT); 2 the previous step's finisher, computed here (FIN).
-template <int EPI, int NT, bool NTL, int XS = 0>
+template <int EPI, int NT, bool NTL, int XS = 0, int UB = 0>
 __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t* olds = nullptr,
                           float* fparts = nullptr) {
   constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
-  constexpr int U = (RT * NT > 1) ? 4 : 8;
+  // k-steps per load batch (UB: a larger batch, so that a wave's whole
+  // k-range is requested at once)
+  constexpr int U = UB > 0 ? UB : (RT * NT > 1) ? 4 : 8;
   GemmSmem<RT, NT>& sm = *reinterpret_cast<GemmSmem<RT, NT>*>(smem);
 
   const int tid = threadIdx.x;
@@ -672,10 +674,10 @@ __device__ void gemm_unit(const GemmArgs& a, const int tile, char* smem, bf16_t*
 
 constexpr size_t GEMM_SMEM_BYTES = sizeof(GemmSmem<2, 2>);
 
-template <int EPI, int NT, bool NTL>
+template <int EPI, int NT, bool NTL, int UB = 0>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
-  gemm_unit<EPI, NT, NTL>(a, blockIdx.x, smem);
+  gemm_unit<EPI, NT, NTL, 0, UB>(a, blockIdx.x, smem);
 }
 
 // The arguments seen by slots s0 .. s0+n-1 only: every per-slot pointer
@@ -707,12 +709,12 @@ __device__ __forceinline__ GemmArgs slot_view(const GemmArgs& a, const int s0, c
 // this serves cache-resident weights.  It trades weight re-reads for fewer
 // activation bytes per workgroup, which is what bounds these launches once
 // the batch is large.
-template <int EPI, bool NTL>
+template <int EPI, bool NTL, int UB = 0>
 __global__ __launch_bounds__(512) void gemm_group_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GEMM_SMEM_BYTES];
   const int s0 = blockIdx.y * a.slot_grp;
   const GemmArgs v = slot_view(a, s0, min(a.slot_grp, a.B - s0));
-  gemm_unit<EPI, 1, NTL>(v, blockIdx.x, smem);
+  gemm_unit<EPI, 1, NTL, 0, UB>(v, blockIdx.x, smem);
 }
 
 // Depformer out-projection that computes its input, the attention output,
@@ -1044,6 +1046,17 @@ static bool use_wide(const GemmArgs& a) { return a.B >= WIDE_MIN_B && a.K >= 409
 // largest activation row): four groups took 0.18 ms off the 7B device tick
 // at B = 16 and 0.04 ms at B = 8, and were neutral at B = 32 and B = 4,
 // while splitting the other depformer GEMMs further was neutral or slower.
+// A wave's k-range of 9..12 k-steps (the depformer down-projection, K = 2816)
+// in one load batch instead of two: these launches are latency-bound.  Only
+// without slot groups: the batch's registers leave one workgroup per compute
+// unit, which costs more than the saved round trip once there are groups.
+// Measured on the 7B device tick: -0.029 ms at B = 1, -0.033 ms at B = 2;
+// with groups +0.10 ms at B = 8 and +0.11 ms at B = 32.
+static bool deep_batch(const GemmArgs& a) {
+  const int per_wave = ((a.K >> 5) + GEMM_WAVES - 1) / GEMM_WAVES;
+  return per_wave > 8 && per_wave <= 12;
+}
+
 static int slot_group(int epi, const GemmArgs& a) {
   if (a.w_keep && epi == EPI_RESID && a.K > a.M && a.B >= 8) return (a.B + 3) / 4;
   if (a.B <= 16) return 16;
@@ -1082,6 +1095,10 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
     if (G > 16) {
       if (a.w_keep) hipLaunchKernelGGL((gemm_kernel<EPI, 2, false>), dim3(tiles), dim3(512), 0, s, v);
       else hipLaunchKernelGGL((gemm_kernel<EPI, 2, true>), dim3(tiles), dim3(512), 0, s, v);
+    } else if (EPI == EPI_RESID && a.w_keep && groups == 1 && deep_batch(a)) {
+      // cache-resident weights, 9..12 k-steps per wave, one workgroup per
+      // tile: the whole k-range in one load batch
+      hipLaunchKernelGGL((gemm_kernel<EPI_RESID, 1, false, 12>), dim3(tiles), dim3(512), 0, s, v);
     } else if (groups > 1) {
       if (a.w_keep) hipLaunchKernelGGL((gemm_group_kernel<EPI, false>), dim3(tiles, groups), dim3(512), 0, s, v);
       else hipLaunchKernelGGL((gemm_group_kernel<EPI, true>), dim3(tiles, groups), dim3(512), 0, s, v);
