@@ -49,7 +49,7 @@ def measured_traffic(algorithmic_bytes):
     return t.get("bytes_per_launch")
 
 
-DOMINANT_KERNEL = "gemm_kernel<2, 1, true>"  # temporal gate/up below the large-batch path, weights read once per tick
+DOMINANT_KERNEL = "gemm_kernel<2, 1, true, 0>"  # temporal gate/up below the large-batch path, weights read once per tick
 DOMINANT_WGS = 704                             # its workgroups at the 7B shape (one per gate/up row-tile pair)
 
 
