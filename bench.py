@@ -1,6 +1,6 @@
 """Benchmark of the lockstep tick on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config C1|C2|C3|C4|sweep] [--cpu-ticks N]
+    python bench.py [--steps K] [--warmup W] [--config C1|C2|C3|C4|sweep] [--cpu-seconds S]
 
 A step is one lockstep tick of the whole hot path (column assembly, embedding
 gather-sum, 32 temporal layers against the ring KV, text head, 16-step
@@ -174,7 +174,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C1", choices=["C0", "C1", "C2", "C3", "C4", "sweep", "sweep_empty"])
     ap.add_argument("--batch", type=int, default=None, help="slots (default: the config's own B)")
-    ap.add_argument("--cpu-ticks", type=int, default=1, help="oracle ticks timed on the host (0: skip)")
+    ap.add_argument("--cpu-ticks", type=int, default=100000,
+                    help="at most this many oracle ticks timed on the host (0: skip the CPU baseline)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle ticks are timed until this much host time has been spent (a bounded sample)")
     ap.add_argument("--kernel-iters", type=int, default=30)
     ap.add_argument("--sampling", action="store_true",
                     help="sample the token choices (text temperature 0.7, audio temperature 0.3, top-p 0.9, "
@@ -333,17 +336,26 @@ def main():
             o.set_sampling(sampling["text_temperature"], sampling["audio_temperature"], sampling["top_k"],
                            sampling["top_p"], sampling["repetition_penalty"])
             o.slot_seed(0, 1000)
+        n_fill = wl.fill_n[0]
+        if n_fill:  # the same pre-filled ring and session-open schedule as slot 0 of the workload
+            o.ring_fill(0, wl.fill[0][:, :n_fill], wl.fill[1][:, :n_fill])
+        if wl.sched[0] is not None:
+            o.prefill_forced(0, wl.sched[0])
         c0 = wl.codes[0]
         ts = []
-        for t in range(args.cpu_ticks):
+        while len(ts) < args.cpu_ticks and sum(ts) < args.cpu_seconds:
+            t = len(ts) % len(c0)
             a = time.perf_counter()
             o.step(c0[t:t + 1])
             ts.append(time.perf_counter() - a)
-            log(f"oracle tick {t}: {ts[-1]:.2f} s")
+            if len(ts) <= 3 or len(ts) % 100 == 0:
+                log(f"oracle tick {len(ts) - 1}: {ts[-1]:.3f} s")
+        log(f"oracle: {len(ts)} ticks in {sum(ts):.1f} s")
         result["cpu_baseline"] = {"value": len(ts) / sum(ts), "unit": "frames/s", "cores": cores,
                                   "kind": "oracle",
-                                  "sample": f"{len(ts)} ticks of one slot from an empty ring "
-                                            f"(numpy fp32, BLAS threads = host cores)"}
+                                  "sample": f"{len(ts)} ticks of one slot "
+                                            f"{'after a ring fill of %d frames' % n_fill if n_fill else 'from an empty ring'}"
+                                            f", {sum(ts):.1f} s of host time (numpy fp32, BLAS threads = host cores)"}
     print(json.dumps(result), flush=True)
 
 
