@@ -323,6 +323,7 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       at.cnt = h->at<unsigned>(L.att_cnt);
       if (g.qkv_to_attn) {
         at.qkv_part = split_part;
+        at.qkv_cols = gemm_wide_cols(g);
         at.qkv_rms = wide_rms;
         at.rope = h->at<float>(L.rope);
       }

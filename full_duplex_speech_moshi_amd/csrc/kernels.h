@@ -134,15 +134,19 @@ struct GemmArgs {
 // Large-batch path: weight tiles (gate and up tiles counted apart) and
 // partial floats (8 ranges x 512 per weight tile).
 // The large-batch GEMM path (split k-ranges, activation slice in LDS) from
-// this batch on, for K >= 4096: its cost hardly depends on B, and it beats
-// the small-batch path (activations read per tile) from about B = 13.
-constexpr int WIDE_MIN_B = 13;
+// this batch on, for K >= 4096: its cost hardly depends on B, and with one
+// 16-column tile up to B = 16 it beats the small-batch path (activations read
+// per tile) from B = 10 on.
+constexpr int WIDE_MIN_B = 10;
 inline long wide_tiles(int epi, int M) { return (epi == EPI_GATED ? 2L : 1L) * ((M + ROWS - 1) / ROWS); }
 inline long wide_part_floats(int epi, int M) { return wide_tiles(epi, M) * 8 * 512; }
 
 void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s);
 // True when launch_gemm takes the large-batch (k-range split) path for `a`.
 bool gemm_splits_k(Epi epi, const GemmArgs& a);
+// Columns (slots) the large-batch path carries for `a`: 16 when every slot
+// fits one MFMA column tile, else 32.  Its partials hold that many slots.
+int gemm_wide_cols(const GemmArgs& a);
 void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s);
 inline long packed_elems(int M, int K) { return (long)((M + ROWS - 1) / ROWS) * ROWS * K; }
 
@@ -161,10 +165,11 @@ struct AttnArgs {
   unsigned* cnt;        // [B][n_heads] split tickets, zero between launches (unused with one split)
   // Large-batch path: q, k and v are not formed by the QKV launch.  Each
   // workgroup sums its head's q rows from the QKV k-range partials
-  // ([tile][8 ranges][32 slots][16 rows] fp32), scales them by the slot's
+  // ([tile][8 ranges][qkv_cols slots][16 rows] fp32), scales them by the slot's
   // inverse RMS and rotates them (rope: [B][head_dim] cos/sin); the last
   // split also forms k and v and writes them to the ring.  Null otherwise.
   const float* qkv_part;
+  int qkv_cols;           // slots per partial block (gemm_wide_cols)
   const float* qkv_rms;   // [MAX_COLS]
   const float* rope;
 };

@@ -749,24 +749,30 @@ __global__ __launch_bounds__(512) void gemm_fin_kernel(GemmArgs a) {
 //     weights (non-temporal) through the staged slice and stores p_j;
 //   * gemm_wide_reduce: one workgroup per output tile sums p_0..p_7 in order
 //     and runs the common epilogue.
+//
+// Up to B = 16 every kernel of the path carries one 16-column MFMA tile
+// (NT = 1): half the activation slice, half the partials and half the MFMAs
+// of the 32-column form, whose second tile would hold only padding.
 // ---------------------------------------------------------------------------
 
 constexpr int WIDE_SK = 8;  // k-steps per stage (activations in LDS, weights in registers)
 
-// Store p_j of weight tile t.  Default layout [t][j][ct][q][lane] (the
-// reduce kernel reads it with one thread per element); with qkv_to_attn,
-// slot-major [t][j][slot][16 rows], so that the decode pass reads one slot's
-// 16 rows as 64 contiguous bytes.  MFMA accumulator q of lane l holds row
+// Store p_j of weight tile t for NT column tiles (NT * 16 slots, NT * 256
+// floats).  Default layout [t][j][ct][q][lane] (the reduce kernel reads it
+// with one thread per element); with qkv_to_attn, slot-major
+// [t][j][slot][16 rows], so that the decode pass reads one slot's 16 rows as
+// 64 contiguous bytes.  MFMA accumulator q of lane l holds row
 // 4 * (l >> 4) + q of column (slot) ct * 16 + (l & 15).
-__device__ __forceinline__ void store_partial(const GemmArgs& a, long t, int j, const f32x4 (&acc)[2], int lane) {
+template <int NT>
+__device__ __forceinline__ void store_partial(const GemmArgs& a, long t, int j, const f32x4 (&acc)[NT], int lane) {
   if (a.qkv_to_attn) {
-    float* P = a.split_part + (t * GEMM_WAVES + j) * 512 + (lane & 15) * 16 + 4 * (lane >> 4);
+    float* P = a.split_part + (t * GEMM_WAVES + j) * (NT * 256) + (lane & 15) * 16 + 4 * (lane >> 4);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) *reinterpret_cast<f32x4*>(P + ct * 256) = acc[ct];
+    for (int ct = 0; ct < NT; ++ct) *reinterpret_cast<f32x4*>(P + ct * 256) = acc[ct];
   } else {
-    float* P = a.split_part + (t * GEMM_WAVES + j) * 512 + lane;
+    float* P = a.split_part + (t * GEMM_WAVES + j) * (NT * 256) + lane;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
       for (int q = 0; q < 4; ++q) P[ct * 256 + q * 64] = acc[ct][q];
   }
@@ -777,16 +783,16 @@ __device__ __forceinline__ void store_partial(const GemmArgs& a, long t, int j, 
 // so the 8 lanes of a 128-bit read (8 consecutive columns, one chunk) hit 8
 // different bank groups instead of 2.
 __device__ __forceinline__ int xs_chunk(int c, int part) { return part ^ ((c >> 1) & 3); }
-constexpr int WIDE_XL = 2 * WIDE_SK * 32 * 4 / 512;  // 16-byte activation pieces per thread per stage
 
 // Stage st of the k-range is software-pipelined: while the waves multiply
 // stage st (weights in registers, activations in LDS buffer st & 1), the
 // weights and activations of stage st + 1 are in flight; one barrier per
 // stage.  Every wave still accumulates its k-range in k-step order, hi then
 // lo, as the contract requires.
-template <int RT>
+template <int RT, int NT>
 __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
-  constexpr int NT = 2, NTC = 32;
+  constexpr int NTC = NT * 16, CS = NT == 2 ? 5 : 4;     // columns held, log2 of it
+  constexpr int WIDE_XL = 2 * WIDE_SK * NTC * 4 / 512;  // 16-byte activation pieces per thread per stage
   __shared__ __attribute__((aligned(16))) bf16_t xs[2][2][WIDE_SK][NTC][32];  // [buffer][hi/lo][k-step][column]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -812,12 +818,12 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
   }
 
   // activation piece i of a stage (i = tid + 512 u): 16 bytes of plane
-  // i >> 10, k-step (i >> 7) & 7, column (i >> 2) & 31, part i & 3
+  // i >> (5 + CS), k-step (i >> (2 + CS)) & 7, column (i >> 2) % NTC, part i & 3
   auto load_x = [&](int c0, int nsub, u32x4 (&xr)[WIDE_XL]) {
 #pragma unroll
     for (int u = 0; u < WIDE_XL; ++u) {
       const int i = tid + 512 * u;
-      const int part = i & 3, c = (i >> 2) & 31, q = (i >> 7) & 7, pl = i >> 10;
+      const int part = i & 3, c = (i >> 2) & (NTC - 1), q = (i >> (2 + CS)) & 7, pl = i >> (5 + CS);
       xr[u] = (q < nsub && c < a.B) ? ld16(a.X + (pl ? a.x_lo : 0) + (long)c * a.ldx + (c0 + q) * 32 + part * 8) : zero;
     }
   };
@@ -825,7 +831,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < WIDE_XL; ++u) {
       const int i = tid + 512 * u;
-      const int part = i & 3, c = (i >> 2) & 31, q = (i >> 7) & 7, pl = i >> 10;
+      const int part = i & 3, c = (i >> 2) & (NTC - 1), q = (i >> (2 + CS)) & 7, pl = i >> (5 + CS);
       *reinterpret_cast<u32x4*>(&xs[buf][pl][q][c][xs_chunk(c, part) * 8]) = xr[u];
     }
   };
@@ -873,7 +879,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < WIDE_SK; ++u) wr[u] = wn[u];
   }
-  if (t_ok) store_partial(a, t, j, acc, lane);
+  if (t_ok) store_partial<NT>(a, t, j, acc, lane);
 }
 
 // The same partials for k-ranges of exactly WIDE_RES k-steps (K = 4096):
@@ -889,9 +895,9 @@ constexpr int WIDE_RES_WGS = 512;  // workgroups: two per compute unit
 
 inline int wide_res_tpw(long tiles) { return (int)((tiles + 8L * (WIDE_RES_WGS / 8) - 1) / (8L * (WIDE_RES_WGS / 8))); }
 
-template <int RT>
+template <int RT, int NT>
 __global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
-  constexpr int NT = 2, NTC = 32;
+  constexpr int NTC = NT * 16, CS = NT == 2 ? 5 : 4;  // columns held, log2 of it
   __shared__ __attribute__((aligned(16))) bf16_t xs[2][WIDE_RES][NTC][32];  // [hi/lo][k-step][column]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -931,11 +937,11 @@ __global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
     for (int q = 0; q < WIDE_RES; ++q) wr[q] = zero;
   }
   // the range's activation slice: piece i = tid + 512 u is 16 bytes of plane
-  // i >> 11, k-step (i >> 7) & 15, column (i >> 2) & 31, part i & 3
+  // i >> (6 + CS), k-step (i >> (2 + CS)) & 15, column (i >> 2) % NTC, part i & 3
 #pragma unroll
   for (int u = 0; u < 2 * WIDE_RES * NTC * 4 / 512; ++u) {
     const int i = tid + 512 * u;
-    const int part = i & 3, c = (i >> 2) & 31, q = (i >> 7) & 15, pl = i >> 11;
+    const int part = i & 3, c = (i >> 2) & (NTC - 1), q = (i >> (2 + CS)) & 15, pl = i >> (6 + CS);
     const u32x4 v = ld16(a.X + (pl ? a.x_lo : 0) + (long)min(c, a.B - 1) * a.ldx + (s0 + q) * 32 + part * 8);
     *reinterpret_cast<u32x4*>(&xs[pl][q][c][xs_chunk(c, part) * 8]) = c < a.B ? v : zero;
   }
@@ -968,23 +974,26 @@ __global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < WIDE_RES; ++q) mul(q, acc);
     }
-    if (t < T) store_partial(a, t, j, acc, lane);
+    if (t < T) store_partial<NT>(a, t, j, acc, lane);
   }
 }
 
-template <int EPI>
+template <int EPI, int NT>
 __global__ __launch_bounds__(512) void gemm_wide_reduce(GemmArgs a) {
-  constexpr int NT = 2, RT = (EPI == EPI_GATED) ? 2 : 1;
+  constexpr int RT = (EPI == EPI_GATED) ? 2 : 1;
   __shared__ EpiSmem<RT, NT> e;
   const int tile = blockIdx.x, tid = threadIdx.x;
   const int n_out = (a.M + ROWS - 1) / ROWS;
-  // element tid of the partial tile: column tile ct, accumulator q, lane ln
+  // element tid (< NT * 256) of the partial tile: column tile ct,
+  // accumulator q, lane ln
+  const bool el = tid < NT * 256;
   float v[RT][GEMM_WAVES];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const long tt = rt ? (long)tile + n_out : (long)tile;
 #pragma unroll
-    for (int jj = 0; jj < GEMM_WAVES; ++jj) v[rt][jj] = a.split_part[(tt * GEMM_WAVES + jj) * (NT * 256) + tid];
+    for (int jj = 0; jj < GEMM_WAVES; ++jj)
+      v[rt][jj] = el ? a.split_part[(tt * GEMM_WAVES + jj) * (NT * 256) + tid] : 0.f;
   }
   // inverse RMS: from the main kernel, or formed here when no buffer is given
   RmsPre<NT> rp;
@@ -1002,7 +1011,7 @@ __global__ __launch_bounds__(512) void gemm_wide_reduce(GemmArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int jj = 0; jj < GEMM_WAVES; ++jj) s += v[rt][jj];
-    e.fin[rt][4 * (ln >> 4) + q][ct * 16 + (ln & 15)] = s;
+    if (el) e.fin[rt][4 * (ln >> 4) + q][ct * 16 + (ln & 15)] = s;
   }
   if (EPI != EPI_RESID && !a.wide_rms) rms_finish<NT>(a, rp, e.inv_rms);
   __syncthreads();
@@ -1078,15 +1087,21 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
     const long groups = (wide_tiles(EPI, a.M) + GEMM_WAVES - 1) / GEMM_WAVES;
     GemmArgs w = a;
     if (EPI == EPI_RESID) w.wide_rms = nullptr;  // no normalised input
+    constexpr int RT = EPI == EPI_GATED ? 2 : 1;
+    const bool one = gemm_wide_cols(a) == 16;  // one 16-column tile holds every slot
     if ((a.K >> 5) == GEMM_WAVES * WIDE_RES) {
       const long T = wide_tiles(EPI, a.M);
       const long P = (T + 8L * wide_res_tpw(T) - 1) / (8L * wide_res_tpw(T));
-      hipLaunchKernelGGL((gemm_wide_res_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(P * GEMM_WAVES), dim3(512), 0, s, w);
+      if (one) hipLaunchKernelGGL((gemm_wide_res_kernel<RT, 1>), dim3(P * GEMM_WAVES), dim3(512), 0, s, w);
+      else hipLaunchKernelGGL((gemm_wide_res_kernel<RT, 2>), dim3(P * GEMM_WAVES), dim3(512), 0, s, w);
     } else {
-      hipLaunchKernelGGL((gemm_wide_kernel<EPI == EPI_GATED ? 2 : 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s,
-                         w);
+      if (one) hipLaunchKernelGGL((gemm_wide_kernel<RT, 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, w);
+      else hipLaunchKernelGGL((gemm_wide_kernel<RT, 2>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, w);
     }
-    if (!(EPI == EPI_QKV && a.qkv_to_attn)) hipLaunchKernelGGL((gemm_wide_reduce<EPI>), dim3(tiles), dim3(512), 0, s, w);
+    if (!(EPI == EPI_QKV && a.qkv_to_attn)) {
+      if (one) hipLaunchKernelGGL((gemm_wide_reduce<EPI, 1>), dim3(tiles), dim3(512), 0, s, w);
+      else hipLaunchKernelGGL((gemm_wide_reduce<EPI, 2>), dim3(tiles), dim3(512), 0, s, w);
+    }
   } else {
     const int G = slot_group(EPI, a);
     GemmArgs v = a;
@@ -1108,6 +1123,8 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
     }
   }
 }
+
+int gemm_wide_cols(const GemmArgs& a) { return a.B <= 16 ? 16 : 32; }
 
 bool gemm_splits_k(Epi epi, const GemmArgs& a) {
   return !(epi == EPI_RESID && a.fuse_att) && !(epi == EPI_QKV && a.fuse_fin) && use_wide(a);
@@ -1213,7 +1230,7 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
       const int which = i / (2 * DH), ii = i - which * 2 * DH;
       const int ti = ii >> 5, jj = (ii >> 2) & 7, qq = ii & 3;
       const long T = (long)which * tiles_d + h * (DH / ROWS) + ti;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.qkv_part + ((T * GEMM_WAVES + jj) * MAX_COLS + b) * 16 + 4 * qq);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.qkv_part + ((T * GEMM_WAVES + jj) * a.qkv_cols + b) * 16 + 4 * qq);
 #pragma unroll
       for (int r = 0; r < 4; ++r) qp_s[which][ti * 16 + 4 * qq + r][jj] = v[r];
     }
