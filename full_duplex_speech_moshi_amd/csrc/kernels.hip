@@ -1114,6 +1114,12 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
       // cache-resident weights, 9..12 k-steps per wave, one workgroup per
       // tile: the whole k-range in one load batch
       hipLaunchKernelGGL((gemm_kernel<EPI_RESID, 1, false, 12>), dim3(tiles), dim3(512), 0, s, v);
+    } else if (EPI == EPI_RESID && !a.w_keep && groups == 1 && a.K > a.M) {
+      // streamed down-projection (K = 11264: 44 k-steps per wave) in load
+      // batches of 4 k-steps: 72 registers instead of 120.  Measured on the
+      // 7B device tick: -0.03 ms at B = 1, -0.04 at B = 4, -0.06 at B = 8;
+      // batches of 2, 3, 6 and 16 were slower than 4.
+      hipLaunchKernelGGL((gemm_kernel<EPI_RESID, 1, true, 4>), dim3(tiles), dim3(512), 0, s, v);
     } else if (groups > 1) {
       if (a.w_keep) hipLaunchKernelGGL((gemm_group_kernel<EPI, false>), dim3(tiles, groups), dim3(512), 0, s, v);
       else hipLaunchKernelGGL((gemm_group_kernel<EPI, true>), dim3(tiles, groups), dim3(512), 0, s, v);
