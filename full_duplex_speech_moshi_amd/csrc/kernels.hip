@@ -755,7 +755,10 @@ __global__ __launch_bounds__(512) void gemm_fin_kernel(GemmArgs a) {
 // of the 32-column form, whose second tile would hold only padding.
 // ---------------------------------------------------------------------------
 
-constexpr int WIDE_SK = 8;  // k-steps per stage (activations in LDS, weights in registers)
+// k-steps per stage (activations in LDS, weights in registers).  Measured
+// on the 7B device tick against 8: stages of 12 k-steps were neutral
+// (-0.01 ms at B = 16, +0.01 at B = 32), of 16 slower (+0.01, +0.04).
+constexpr int WIDE_SK = 8;
 
 // Store p_j of weight tile t for NT column tiles (NT * 16 slots, NT * 256
 // floats).  Default layout [t][j][ct][q][lane] (the reduce kernel reads it
@@ -793,6 +796,7 @@ template <int RT, int NT>
 __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
   constexpr int NTC = NT * 16, CS = NT == 2 ? 5 : 4;     // columns held, log2 of it
   constexpr int WIDE_XL = 2 * WIDE_SK * NTC * 4 / 512;  // 16-byte activation pieces per thread per stage
+  static_assert(WIDE_XL * 512 == 2 * WIDE_SK * NTC * 4, "a stage's pieces must split evenly over 512 threads");
   __shared__ __attribute__((aligned(16))) bf16_t xs[2][2][WIDE_SK][NTC][32];  // [buffer][hi/lo][k-step][column]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -817,21 +821,22 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
     if (tid < NTC) a.wide_rms[tid] = inv[tid];
   }
 
-  // activation piece i of a stage (i = tid + 512 u): 16 bytes of plane
-  // i >> (5 + CS), k-step (i >> (2 + CS)) & 7, column (i >> 2) % NTC, part i & 3
+  // activation piece i of a stage (i = tid + 512 u): 16 bytes of row
+  // r = i >> (2 + CS), i.e. plane r / WIDE_SK and k-step r % WIDE_SK, column
+  // (i >> 2) % NTC, part i & 3
   auto load_x = [&](int c0, int nsub, u32x4 (&xr)[WIDE_XL]) {
 #pragma unroll
     for (int u = 0; u < WIDE_XL; ++u) {
-      const int i = tid + 512 * u;
-      const int part = i & 3, c = (i >> 2) & (NTC - 1), q = (i >> (2 + CS)) & 7, pl = i >> (5 + CS);
+      const int i = tid + 512 * u, r = i >> (2 + CS);
+      const int part = i & 3, c = (i >> 2) & (NTC - 1), q = r % WIDE_SK, pl = r / WIDE_SK;
       xr[u] = (q < nsub && c < a.B) ? ld16(a.X + (pl ? a.x_lo : 0) + (long)c * a.ldx + (c0 + q) * 32 + part * 8) : zero;
     }
   };
   auto store_x = [&](int buf, const u32x4 (&xr)[WIDE_XL]) {
 #pragma unroll
     for (int u = 0; u < WIDE_XL; ++u) {
-      const int i = tid + 512 * u;
-      const int part = i & 3, c = (i >> 2) & (NTC - 1), q = (i >> (2 + CS)) & 7, pl = i >> (5 + CS);
+      const int i = tid + 512 * u, r = i >> (2 + CS);
+      const int part = i & 3, c = (i >> 2) & (NTC - 1), q = r % WIDE_SK, pl = r / WIDE_SK;
       *reinterpret_cast<u32x4*>(&xs[buf][pl][q][c][xs_chunk(c, part) * 8]) = xr[u];
     }
   };
