@@ -2,6 +2,8 @@
 against its published known-answer vectors, the sampler against brute-force
 definitions and library routines, and the tick with sampling against its
 greedy special case."""
+import os
+
 import numpy as np
 import pytest
 import scipy.special
@@ -16,14 +18,17 @@ W = synth.TINY_WINDOW
 
 def test_philox4x32_10_known_answers():
     """Known-answer vectors published with the Random123 reference
-    implementation of Philox4x32-10 (Salmon et al., SC 2011): counter and key
-    all zeros, all ones, and the hexadecimal digits of pi."""
-    kat = [
-        ([0, 0, 0, 0], [0, 0], [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]),
-        ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2, [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]),
-        ([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344], [0xA4093822, 0x299F31D0],
-         [0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1]),
-    ]
+    implementation of Philox4x32-10 (Salmon et al., SC 2011), stored with
+    their citation in tests/golden/philox4x32_10_kat.txt: counter and key all
+    zeros, all ones, and the hexadecimal digits of pi."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "philox4x32_10_kat.txt")
+    kat = []
+    for line in open(path):
+        line = line.split("#", 1)[0].split()
+        if line:
+            words = [int(w, 16) for w in line]
+            kat.append((words[0:4], words[4:6], words[6:10]))
+    assert len(kat) == 3
     for ctr, key, want in kat:
         assert sm.philox4x32_10(ctr, key) == want
 
