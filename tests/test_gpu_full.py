@@ -232,6 +232,42 @@ def test_full_isolation_b32_bit_exact(full):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("B", [16, 32])
+def test_full_isolation_full_rings_large_batch_bit_exact(full, B):
+    """The large-batch benchmark configuration: rings full at 3000 frames, so
+    every tick writes over the oldest key.  On the large-batch path (one
+    16-column tile at B = 16, two at B = 32) the decode finishes q, k and v
+    from the QKV partials and uses the new key and value in place of the ring
+    row it is about to replace.  Two full slots and an empty one must equal
+    B = 1 handles (small-batch path, checked against the oracle at a full
+    window) bit for bit over 3 ticks."""
+    _say(f"case: 7B isolation, B={B}, rings full at {W} (wrapping) vs B=1")
+    fill = synth.ring_fill(DM, 61, W)
+    full_slots = (3, B - 1)
+    codes = [synth.user_codes(1300 + b, 3) for b in range(B)]
+    eb = _engine(full, B)
+    for b in full_slots:
+        eb.ring_fill(b, *fill)
+    toks, taps = [], []
+    for t in range(3):
+        toks.append(eb.step(np.stack([codes[b][t] for b in range(B)])))
+        taps.append(eb.taps())
+    eb.close()
+    for b in (0,) + full_slots:
+        e1 = _engine(full, 1)
+        if b in full_slots:
+            e1.ring_fill(0, *fill)
+        for t in range(3):
+            tk = e1.step(codes[b][t:t + 1])
+            tp = e1.taps()
+            np.testing.assert_array_equal(tk[0], toks[t][b])
+            np.testing.assert_array_equal(tp["hidden"][:, 0], taps[t]["hidden"][:, b])
+            np.testing.assert_array_equal(tp["text_logits"][0], taps[t]["text_logits"][b])
+            np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
+        e1.close()
+
+
+@pytest.mark.timeout(900)
 def test_full_sampling_matches_oracle_sampler(full):
     """Sampling at the 7B shape (the 32000-way text row held in LDS), B = 2,
     3 ticks with the pages' knobs plus top-k: every choice equals the oracle
