@@ -51,10 +51,10 @@ def _cache_ok():
         return False
 
 
-def _engine(full, B):
+def _engine(full, B, window=W):
     from full_duplex_speech_moshi_amd import pp
     w, dev = full
-    return pp.Engine(DM, w, B, W, device_weights=dev)
+    return pp.Engine(DM, w, B, window, device_weights=dev)
 
 
 def _parity_run(full, w32, n_ticks, fill_seed=None, codes=None):
@@ -258,6 +258,41 @@ def test_full_isolation_full_rings_large_batch_bit_exact(full, B):
         if b in full_slots:
             e1.ring_fill(0, *fill)
         for t in range(3):
+            tk = e1.step(codes[b][t:t + 1])
+            tp = e1.taps()
+            np.testing.assert_array_equal(tk[0], toks[t][b])
+            np.testing.assert_array_equal(tp["hidden"][:, 0], taps[t]["hidden"][:, b])
+            np.testing.assert_array_equal(tp["text_logits"][0], taps[t]["text_logits"][b])
+            np.testing.assert_array_equal(tp["dep_logits"][0], taps[t]["dep_logits"][b])
+        e1.close()
+
+
+@pytest.mark.timeout(900)
+def test_full_isolation_max_batch_and_window_bit_exact(full):
+    """The largest handle the library takes: B = 32 slots with a 4096-frame
+    window (16 decode splits per head) on the large-batch path.  A slot whose
+    ring is full (each tick overwrites the oldest key), one at 4000 keys (a
+    ragged last split) and an empty one must equal B = 1 handles with the
+    same window bit for bit over 2 ticks."""
+    from full_duplex_speech_moshi_amd import pp
+    Wm, B = pp.PP_MAX_WINDOW, pp.PP_MAX_BATCH
+    _say(f"case: 7B isolation, B={B}, window {Wm}, rings full / 4000 / empty vs B=1")
+    fill = synth.ring_fill(DM, 62, Wm)
+    occ = {5: Wm, B - 1: 4000}
+    codes = [synth.user_codes(1500 + b, 2) for b in range(B)]
+    eb = _engine(full, B, Wm)
+    for b, n in occ.items():
+        eb.ring_fill(b, fill[0][:, :n], fill[1][:, :n])
+    toks, taps = [], []
+    for t in range(2):
+        toks.append(eb.step(np.stack([codes[b][t] for b in range(B)])))
+        taps.append(eb.taps())
+    eb.close()
+    for b in (0, 5, B - 1):
+        e1 = _engine(full, 1, Wm)
+        if b in occ:
+            e1.ring_fill(0, fill[0][:, :occ[b]], fill[1][:, :occ[b]])
+        for t in range(2):
             tk = e1.step(codes[b][t:t + 1])
             tp = e1.taps()
             np.testing.assert_array_equal(tk[0], toks[t][b])
