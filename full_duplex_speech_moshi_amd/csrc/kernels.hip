@@ -1049,7 +1049,16 @@ void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s) {
 // so the choice only moves time.  The k-range split pays off once the
 // activation operand outweighs the weights (B >= WIDE_MIN_B) and the k-ranges
 // are long enough to amortise staging and the partial exchange (K >= 4096).
-static bool use_wide(const GemmArgs& a) { return a.B >= WIDE_MIN_B && a.K >= 4096; }
+// The square out-projection (EPI_RESID, K = M) joins only past one column
+// tile: its 256 tiles give each wave of the large-batch form a single tile,
+// and the reduce launch then costs more than the activation reads it saves.
+// Measured on the 7B device tick, small-batch against large-batch for it:
+// -0.07 ms at B = 10, -0.045 at B = 12, -0.025 at B = 14, -0.007 at B = 16,
+// +0.21 at B = 32.
+static bool use_wide(int epi, const GemmArgs& a) {
+  const int min_b = (epi == EPI_RESID && a.K == a.M) ? 17 : WIDE_MIN_B;
+  return a.B >= min_b && a.K >= 4096;
+}
 
 // Slots per workgroup for the other paths: 32 (both column tiles in one
 // workgroup) or a group size G <= 16 (gemm_group_kernel, blockIdx.y = slot
@@ -1088,7 +1097,7 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(gemm_fin_kernel, dim3(tiles), dim3(512), 0, s, a);
     return;
   }
-  if (use_wide(a)) {
+  if (use_wide(EPI, a)) {
     const long groups = (wide_tiles(EPI, a.M) + GEMM_WAVES - 1) / GEMM_WAVES;
     GemmArgs w = a;
     if (EPI == EPI_RESID) w.wide_rms = nullptr;  // no normalised input
@@ -1138,7 +1147,7 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
 int gemm_wide_cols(const GemmArgs& a) { return a.B <= 16 ? 16 : 32; }
 
 bool gemm_splits_k(Epi epi, const GemmArgs& a) {
-  return !(epi == EPI_RESID && a.fuse_att) && !(epi == EPI_QKV && a.fuse_fin) && use_wide(a);
+  return !(epi == EPI_RESID && a.fuse_att) && !(epi == EPI_QKV && a.fuse_fin) && use_wide(epi, a);
 }
 
 void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s) {
