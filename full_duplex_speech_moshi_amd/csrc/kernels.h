@@ -133,11 +133,11 @@ struct GemmArgs {
 
 // Large-batch path: weight tiles (gate and up tiles counted apart) and
 // partial floats (8 ranges x 512 per weight tile).
-// The large-batch GEMM path (split k-ranges, activation slice in LDS) from
-// this batch on, for K >= 4096: its cost hardly depends on B, and with one
-// 16-column tile up to B = 16 it beats the small-batch path (activations read
-// per tile) from B = 10 on.
-constexpr int WIDE_MIN_B = 10;
+// The smallest batch at which any GEMM takes the large-batch path (split
+// k-ranges, activation slice in LDS; K >= 4096): the temporal QKV, from B = 9.
+// Each GEMM has its own threshold at or above it; the partial buffer exists
+// from this batch on.
+constexpr int WIDE_MIN_B = 9;
 inline long wide_tiles(int epi, int M) { return (epi == EPI_GATED ? 2L : 1L) * ((M + ROWS - 1) / ROWS); }
 inline long wide_part_floats(int epi, int M) { return wide_tiles(epi, M) * 8 * 512; }
 

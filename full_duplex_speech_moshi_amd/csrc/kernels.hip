@@ -1047,18 +1047,32 @@ void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s) {
 
 // Path choice per launch: both paths compute the same bits (the contract),
 // so the choice only moves time.  The k-range split pays off once the
-// activation operand outweighs the weights (B >= WIDE_MIN_B) and the k-ranges
-// are long enough to amortise staging and the partial exchange (K >= 4096).
-// The square out-projection (EPI_RESID, K = M) joins only past one column
-// tile: its 256 tiles give each wave of the large-batch form a single tile,
-// and the reduce launch then costs more than the activation reads it saves.
-// Measured on the 7B device tick, small-batch against large-batch for it:
-// -0.07 ms at B = 10, -0.045 at B = 12, -0.025 at B = 14, -0.007 at B = 16,
-// +0.21 at B = 32.
-static bool use_wide(int epi, const GemmArgs& a) {
-  const int min_b = (epi == EPI_RESID && a.K == a.M) ? 17 : WIDE_MIN_B;
-  return a.B >= min_b && a.K >= 4096;
+// activation operand outweighs the weights and the k-ranges are long enough
+// to amortise staging and the partial exchange (K >= 4096).  Where that
+// happens depends on the GEMM; each threshold below is the batch from which
+// the large-batch form measured faster on the 7B device tick (the other
+// GEMMs held fixed):
+//   * QKV from B = 9 (-0.04 ms at B = 9, neutral at 8): its partials go
+//     straight to the decode, with no reduce launch;
+//   * down-projection, text head and input projections from B = 10 (neutral
+//     at 9);
+//   * gate/up from B = 14: its small-batch kernel, two tiles per workgroup,
+//     was faster by 0.12 ms at B = 10, 0.07 at 12 and 0.025 at 13, slower by
+//     0.015 at 14 and 0.11 at 16;
+//   * the square out-projection (K = M) from B = 17: its 256 tiles give each
+//     wave of the large-batch form a single tile, and the reduce launch costs
+//     more than the activation reads it saves while one column tile holds
+//     every slot (-0.07 ms at B = 10, -0.007 at 16, +0.21 at 32 on the
+//     small-batch kernel).
+static int wide_min_b(int epi, const GemmArgs& a) {
+  if (epi == EPI_QKV) return WIDE_MIN_B;
+  if (epi == EPI_GATED) return 14;
+  if (epi == EPI_RESID && a.K == a.M) return 17;
+  return 10;
 }
+static_assert(WIDE_MIN_B <= 10 && WIDE_MIN_B <= 14 && WIDE_MIN_B <= 17, "the partial buffer must exist for every GEMM's threshold");
+
+static bool use_wide(int epi, const GemmArgs& a) { return a.B >= wide_min_b(epi, a) && a.K >= 4096; }
 
 // Slots per workgroup for the other paths: 32 (both column tiles in one
 // workgroup) or a group size G <= 16 (gemm_group_kernel, blockIdx.y = slot
