@@ -83,3 +83,18 @@ def test_traffic_summary_scales_counters_by_the_copy_probe(tmp_path, monkeypatch
     assert bench.measured_traffic(2 * algo) is None
     (src / "kernels.hip").write_bytes(b"// kernels, changed\n")
     assert bench.measured_traffic(algo) is None
+
+
+def test_dominant_kernel_is_the_largest_per_tick():
+    # B = 1 from an empty ring: the gate/up GEMM (30 us x 32 layers) beats a
+    # 45 us text head launched once and a 6 us decode per layer
+    kern = {"gate_up": {"ms": 0.030}, "qkv": {"ms": 0.019}, "down": {"ms": 0.018}, "out_proj": {"ms": 0.0085},
+            "attention": {"ms": 0.006}, "text_head": {"ms": 0.045}}
+    assert bench.dominant_kernel(kern, 32) == "gate_up"
+    # every ring full at B = 32: the decode (255 us per layer) dominates
+    kern["attention"]["ms"] = 0.255
+    kern["gate_up"]["ms"] = 0.044
+    assert bench.dominant_kernel(kern, 32) == "attention"
+    # a one-layer model: the text head's single launch can win
+    assert bench.dominant_kernel({"gate_up": {"ms": 0.03}, "text_head": {"ms": 0.045}}, 1) == "text_head"
+    assert set(bench.KERNEL_LABELS) >= set(kern)
