@@ -1064,13 +1064,16 @@ void launch_pack(const bf16_t* src, int M, int K, bf16_t* dst, hipStream_t s) {
 //     more than the activation reads it saves while one column tile holds
 //     every slot (-0.07 ms at B = 10, -0.007 at 16, +0.21 at 32 on the
 //     small-batch kernel).
+constexpr int WIDE_B_QKV = 9, WIDE_B_DOWN_HEADS = 10, WIDE_B_GATED = 14, WIDE_B_OUT = 17;
+static_assert(WIDE_MIN_B == WIDE_B_QKV && WIDE_B_DOWN_HEADS >= WIDE_MIN_B && WIDE_B_GATED >= WIDE_MIN_B &&
+                  WIDE_B_OUT >= WIDE_MIN_B,
+              "WIDE_MIN_B sizes the partial buffer: it must be the smallest per-GEMM threshold");
 static int wide_min_b(int epi, const GemmArgs& a) {
-  if (epi == EPI_QKV) return WIDE_MIN_B;
-  if (epi == EPI_GATED) return 14;
-  if (epi == EPI_RESID && a.K == a.M) return 17;
-  return 10;
+  if (epi == EPI_QKV) return WIDE_B_QKV;
+  if (epi == EPI_GATED) return WIDE_B_GATED;
+  if (epi == EPI_RESID && a.K == a.M) return WIDE_B_OUT;
+  return WIDE_B_DOWN_HEADS;
 }
-static_assert(WIDE_MIN_B <= 10 && WIDE_MIN_B <= 14 && WIDE_MIN_B <= 17, "the partial buffer must exist for every GEMM's threshold");
 
 static bool use_wide(int epi, const GemmArgs& a) { return a.B >= wide_min_b(epi, a) && a.K >= 4096; }
 
