@@ -5,9 +5,12 @@
 A step is one lockstep tick of the whole hot path (column assembly, embedding
 gather-sum, 32 temporal layers against the ring KV, text head, 16-step
 depformer, greedy decoding) for every slot.  Default workload: the 7B shape,
-B = 1, 250 ticks from an empty ring, synthetic bf16 weights N(0, 0.02) from
-seed 0 and uniform user codes from seed 1.  Prints one JSON line on stdout;
-progress goes to stderr.
+B = 1, from an empty ring (250 timed ticks unless --steps says otherwise),
+synthetic bf16 weights N(0, 0.02) from seed 0 and uniform user codes from
+seed 1; the line also carries a B = 32 elastic sub-record (C4: mixed ring
+occupancy, slots joining and leaving), timed by a child run of this script
+before this process uses the GPU.  Prints one JSON line on stdout; progress
+goes to stderr.
 """
 from __future__ import annotations
 
@@ -52,11 +55,11 @@ def measured_traffic(algorithmic_bytes):
 # The kernels bench.py times one launch of, and what each is.  The GEMMs
 # cover all their launches (main loop and reduce on the large-batch path).
 KERNEL_LABELS = {
-    "gate_up": "temporal gate/up GEMM (EPI_GATED), layer 0",
-    "qkv": "temporal QKV GEMM (EPI_QKV), layer 0",
-    "down": "temporal down-projection GEMM (EPI_RESID), layer 0",
-    "out_proj": "temporal out-projection GEMM (EPI_RESID), layer 0",
-    "attention": "attn_kernel<128>: ring decode, layer 0",
+    "gate_up": "temporal gate/up GEMM (EPI_GATED), mean of one launch per layer over all 32 layers",
+    "qkv": "temporal QKV GEMM (EPI_QKV), mean of one launch per layer over all 32 layers",
+    "down": "temporal down-projection GEMM (EPI_RESID), mean of one launch per layer over all 32 layers",
+    "out_proj": "temporal out-projection GEMM (EPI_RESID), mean of one launch per layer over all 32 layers",
+    "attention": "attn_kernel<128>: ring decode, mean of one launch per layer over all 32 layers",
     "text_head": "text head GEMM (EPI_LOGITS)",
 }
 
@@ -187,6 +190,90 @@ class Workload:
             self.open_slot(eng, b, self.fill_n[b], self.sched[b])
 
 
+def workload_label(config, B, W, K, WU):
+    """What was timed, from the actual counts."""
+    what = {"C0": f"tiny RQ-Transformer tick, ring window {W}",
+            "C1": "7B RQ-Transformer tick, empty ring at the start of the warm-up",
+            "C2": f"7B RQ-Transformer tick, ring pre-filled to {W} frames",
+            "C3": f"7B RQ-Transformer tick, occupancy U[0,{W}], 92-frame session open",
+            "C4": "7B RQ-Transformer tick, elastic batch, mixed occupancy, p=0.01 turnover per slot-tick",
+            "sweep": "7B RQ-Transformer tick, all rings full",
+            "sweep_empty": "7B RQ-Transformer tick, all rings empty"}[config]
+    return f"{what}; B={B}, {WU} warm-up ticks, then {K} timed ticks"
+
+
+def run_sub_c4(args):
+    """The B=32 elastic workload (C4) timed by a child run of this script,
+    before this process touches the GPU (one engine per process); returns the
+    fields of its JSON line that the sub-record carries, or an error note."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--config", "C4", "--steps", str(args.sub_steps),
+           "--warmup", "10", "--cpu-ticks", "0", "--kernel-iters", "5", "--no-sub"]
+    log("sub-record: " + " ".join(cmd[1:]))
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    if r.returncode != 0 or not lines:
+        return {"error": f"C4 child exited with {r.returncode}"}
+    c = json.loads(lines[-1])
+    keys = ("metric", "value", "unit", "steps", "warmup", "ms_per_step", "p50_tick_ms", "p90_tick_ms", "p99_tick_ms",
+            "device_tick_ms", "tick_hbm_roofline_frac_p50", "tick_bytes_p50", "roofline", "kernels_gbs", "config")
+    return {k: c[k] for k in keys if k in c}
+
+
+def cpu_baseline(args, dm, W, B, weights, wl, sampling):
+    """The oracle as it stands, one slot at a time on the host cores, on a
+    bounded sample of the workload: C0-C2 tick slot 0; C3 ticks slots 0 and 1
+    in turn, C4 its first four sessions in turn (each with its own ring fill
+    and schedule).  The oracle runs slots one after another, so B slots take B
+    per-slot ticks: its frames/s does not depend on B, and the B-slot tick time
+    it implies is labelled as an extrapolation."""
+    from oracle.tick import Oracle
+    cores = len(os.sched_getaffinity(0))
+    if args.config == "C3":
+        picks = [(b, wl.fill_n[b], wl.sched[b], wl.codes[b]) for b in range(min(2, B))]
+    elif args.config == "C4":
+        picks = []
+        for sess in wl.sessions[:4]:
+            c = wl.codes[sess["slot"]][sess["start_tick"]:]
+            picks.append((sess["slot"], sess["fill_n"], None, c))
+    else:
+        picks = [(0, wl.fill_n[0], wl.sched[0], wl.codes[0])]
+    runs = []
+    for slot, n_fill, sched, codes in picks:
+        o = Oracle(dm, weights, 1, W)
+        if sampling:
+            o.set_sampling(sampling["text_temperature"], sampling["audio_temperature"], sampling["top_k"],
+                           sampling["top_p"], sampling["repetition_penalty"])
+            o.slot_seed(0, 1000 + slot)
+        if n_fill:  # the same pre-filled ring and session-open schedule as that slot of the workload
+            o.ring_fill(0, wl.fill[0][:, :n_fill], wl.fill[1][:, :n_fill])
+        if sched is not None:
+            o.prefill_forced(0, sched)
+        runs.append([o, codes, 0])
+    ts = []
+    while len(ts) < args.cpu_ticks and sum(ts) < args.cpu_seconds:
+        run = runs[len(ts) % len(runs)]
+        o, codes, t = run
+        a = time.perf_counter()
+        o.step(codes[t % len(codes):t % len(codes) + 1])
+        ts.append(time.perf_counter() - a)
+        run[2] += 1
+        if len(ts) <= 3 or len(ts) % 100 == 0:
+            log(f"oracle tick {len(ts) - 1}: {ts[-1]:.3f} s")
+    log(f"oracle: {len(ts)} ticks in {sum(ts):.1f} s")
+    what = ", ".join(f"slot {s} ({'ring fill of %d frames' % n if n else 'empty ring'}"
+                     f"{', session-open schedule' if sc is not None else ''})" for s, n, sc, _ in picks)
+    out = {"value": len(ts) / sum(ts), "unit": "frames/s", "cores": cores, "kind": "oracle",
+           "sample": f"{len(ts)} slot-ticks of {what}, taken in turn, {sum(ts):.1f} s of host time "
+                     f"(numpy fp32, BLAS threads = host cores)",
+           "p50_slot_tick_s": float(np.median(ts))}
+    if B > 1:
+        out["extrapolated_tick_s_for_B"] = {"B": B, "tick_s": B * float(np.median(ts)),
+                                            "label": "extrapolation: B x the per-slot-tick p50 (slots run one "
+                                                     "after another)"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +294,9 @@ def main():
                          "copy probe, nothing else (for rocprofv3 --pmc runs)")
     ap.add_argument("--summarize-traffic", metavar="RUN_DIR", default=None,
                     help="no GPU: write profiles/traffic.json from the counter runs of --mode traffic under RUN_DIR")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="default workload only: skip the B=32 elastic sub-record (C4, timed in a child process)")
+    ap.add_argument("--sub-steps", type=int, default=100, help="timed ticks of the C4 sub-record")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic)
@@ -215,6 +305,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (sessions shard across GPUs "
               "with no exchange; run one process per GPU)", file=sys.stderr)
         sys.exit(2)
+
+    sub = None
+    if args.config == "C1" and args.batch is None and not args.no_sub and args.mode == "bench":
+        sub = run_sub_c4(args)
 
     import torch
     from full_duplex_speech_moshi_amd import pp, synth
@@ -305,12 +399,22 @@ def main():
         log(f"kernel {name}: {ms * 1e3:.1f} us, {by / 1e6:.1f} MB, {kern[name]['gbs']:.0f} GB/s")
     eng.close()
 
-    # copy probe: one device-to-device copy of COPY_PROBE_BYTES (reads and
-    # writes that many bytes), the reference for HBM counter calibration
+    # copy probe: device-to-device copies of COPY_PROBE_BYTES (each reads and
+    # writes that many bytes), the reference for HBM counter calibration and
+    # the measured copy bandwidth reported beside the 8 TB/s peak
     src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_copy = 20
+    e0.record()
+    for _ in range(n_copy):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    copy_gbs = 2 * COPY_PROBE_BYTES * n_copy / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    log(f"device copy: {copy_gbs:.0f} GB/s (read + write of {COPY_PROBE_BYTES >> 20} MiB, {n_copy} copies)")
 
     dom_name = dominant_kernel(kern, dm.n_layers)
     dom = kern[dom_name]
@@ -328,13 +432,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": {"C0": "tiny RQ-Transformer tick, B=1, ring window 32",
-                                "C1": "7B RQ-Transformer tick, B=1, empty ring, 250 ticks",
-                                "C2": "7B RQ-Transformer tick, ring pre-filled to 3000 frames",
-                                "C3": "7B RQ-Transformer tick, B=8, occupancy U[0,3000], 92-frame session open",
-                                "C4": "7B RQ-Transformer tick, B=32 elastic, mixed occupancy, p=0.01 turnover",
-                                "sweep": "7B RQ-Transformer tick, all rings full",
-                                "sweep_empty": "7B RQ-Transformer tick, all rings empty"}[args.config],
+        "config": {"workload": workload_label(args.config, B, W, K, WU),
                    "B": B, "window": W, "config": args.config, "choice": sampling or "greedy"},
         "p50_tick_ms": float(np.median(tick_ms)),
         "p90_tick_ms": float(np.percentile(tick_ms, 90)),
@@ -346,38 +444,15 @@ def main():
                      "achieved": dom["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": dom["gbs"] / PEAK_HBM_GBS,
                      "traffic": measured_traffic(dom["bytes"]) if dom_name == "gate_up" else None},
+        "device_copy_gbs": copy_gbs,
         "kernels_us": {k: round(v["ms"] * 1e3, 2) for k, v in kern.items()},
         "kernels_gbs": {k: round(v["gbs"], 1) for k, v in kern.items()},
     }
 
     if args.cpu_ticks > 0:
-        from oracle.tick import Oracle
-        cores = len(os.sched_getaffinity(0))
-        o = Oracle(dm, weights, 1, W)
-        if sampling:
-            o.set_sampling(sampling["text_temperature"], sampling["audio_temperature"], sampling["top_k"],
-                           sampling["top_p"], sampling["repetition_penalty"])
-            o.slot_seed(0, 1000)
-        n_fill = wl.fill_n[0]
-        if n_fill:  # the same pre-filled ring and session-open schedule as slot 0 of the workload
-            o.ring_fill(0, wl.fill[0][:, :n_fill], wl.fill[1][:, :n_fill])
-        if wl.sched[0] is not None:
-            o.prefill_forced(0, wl.sched[0])
-        c0 = wl.codes[0]
-        ts = []
-        while len(ts) < args.cpu_ticks and sum(ts) < args.cpu_seconds:
-            t = len(ts) % len(c0)
-            a = time.perf_counter()
-            o.step(c0[t:t + 1])
-            ts.append(time.perf_counter() - a)
-            if len(ts) <= 3 or len(ts) % 100 == 0:
-                log(f"oracle tick {len(ts) - 1}: {ts[-1]:.3f} s")
-        log(f"oracle: {len(ts)} ticks in {sum(ts):.1f} s")
-        result["cpu_baseline"] = {"value": len(ts) / sum(ts), "unit": "frames/s", "cores": cores,
-                                  "kind": "oracle",
-                                  "sample": f"{len(ts)} ticks of one slot "
-                                            f"{'after a ring fill of %d frames' % n_fill if n_fill else 'from an empty ring'}"
-                                            f", {sum(ts):.1f} s of host time (numpy fp32, BLAS threads = host cores)"}
+        result["cpu_baseline"] = cpu_baseline(args, dm, W, B, weights, wl, sampling)
+    if sub is not None:
+        result["sub"] = {"C4": sub}
     print(json.dumps(result), flush=True)
 
 

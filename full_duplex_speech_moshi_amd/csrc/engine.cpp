@@ -109,10 +109,12 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.xin = take((size_t)B * d * 4);
   L.to = take(B * TO_STRIDE * 4);
   L.inv_freq = take((hd / 2) * 8);
-  // scratch of the large-batch GEMM path: the largest partial area of any GEMM of the tick
+  // scratch of the large-batch GEMM path: the largest partial area of any GEMM
+  // that may take it (the temporal stack, the text head and the depformer
+  // input projections; the depformer layers and heads are given no scratch
+  // and never take that path)
   const struct { Epi epi; long M; } wide[] = {{EPI_QKV, 3L * d}, {EPI_RESID, d}, {EPI_GATED, F}, {EPI_LOGITS, Vt},
-                                             {EPI_STORE, (long)Q * dd}, {EPI_QKV, 3L * dd}, {EPI_RESID, dd},
-                                             {EPI_GATED, dF}, {EPI_LOGITS, A}};
+                                             {EPI_STORE, (long)Q * dd}};
   L.wide_part_max = 0;
   for (const auto& g : wide) L.wide_part_max = std::max(L.wide_part_max, wide_part_floats(g.epi, (int)g.M));
   L.split_part = B >= WIDE_MIN_B ? take((size_t)L.wide_part_max * 4) : take(0);
@@ -534,8 +536,6 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       g.ti = nullptr;
       g.pos_const = k;
       g.inv_freq = nullptr;
-      g.split_part = split_part;
-      g.wide_rms = wide_rms;
       if (l == 0 && fuse_fin && k != dm.n_q) {
         g.fuse_fin = 1;
         g.fin = k == 0 ? fa : finish_of(k - 1);
@@ -576,8 +576,6 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       go.xa_lo = (long)B * dd;
       go.alpha_next = w.dep_mlp_norm + (long)l * dd;
       go.part_out = h->at<float>(L.dpart[ds]);
-      go.split_part = split_part;
-      go.wide_rms = wide_rms;
       go.fuse_att = fuse_att;
       go.att = da;
       launch_gemm(EPI_RESID, go, s);
@@ -599,8 +597,6 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       gu.m_out = h->at<bf16_t>(L.dm[ds]);
       gu.ldm = dF;
       gu.m_lo = (long)B * dF;
-      gu.split_part = split_part;
-      gu.wide_rms = wide_rms;
       launch_gemm(EPI_GATED, gu, s);
 
       GemmArgs gd{};
@@ -618,8 +614,6 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       gd.xa_lo = (long)B * dd;
       gd.alpha_next = (l + 1 < dm.dep_layers) ? w.dep_attn_norm + (long)(l + 1) * dd : w.dep_out_norm;
       gd.part_out = h->at<float>(L.dpart[ds]);
-      gd.split_part = split_part;
-      gd.wide_rms = wide_rms;
       launch_gemm(EPI_RESID, gd, s);
     }
     GemmArgs gh{};
@@ -639,8 +633,6 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
     gh.amax_v = h->at<float>(L.amax_v[ds]);
     gh.amax_i = h->at<int>(L.amax_i[ds]);
     gh.ld_amax = L.n_amax;
-    gh.split_part = split_part;
-    gh.wide_rms = wide_rms;
     launch_gemm(EPI_LOGITS, gh, s);
 
     if (!fuse_fin || k == dm.n_q - 1 || k == Q - 1) launch_finish(finish_of(k), s);

@@ -1075,7 +1075,12 @@ static int wide_min_b(int epi, const GemmArgs& a) {
   return WIDE_B_DOWN_HEADS;
 }
 
-static bool use_wide(int epi, const GemmArgs& a) { return a.B >= wide_min_b(epi, a) && a.K >= 4096; }
+// The large-batch path needs the partial buffer: a launch given none (the
+// depformer layers and heads, whose user-stream half runs on a second stream
+// beside other phases of the tick) always takes the other paths.
+static bool use_wide(int epi, const GemmArgs& a) {
+  return a.split_part != nullptr && a.B >= wide_min_b(epi, a) && a.K >= 4096;
+}
 
 // Slots per workgroup for the other paths: 32 (both column tiles in one
 // workgroup) or a group size G <= 16 (gemm_group_kernel, blockIdx.y = slot

@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libpp.so")
 PP_OK, PP_EINVAL, PP_EBUSY, PP_ENOSPC, PP_EDEVICE = 0, -1, -2, -3, -4
 PP_MAX_BATCH = 32
 PP_MAX_WINDOW = 4096
+PP_MAX_QUEUE = 4096
+PP_MAX_DELAY = 4
 TO_STRIDE = 32
 
 EXPORTS = ("pp_arena_bytes", "pp_create", "pp_prefill_forced", "pp_prefill_embed", "pp_step",

@@ -10,9 +10,9 @@
  *   temporal transformer (4096-d / 32 layers / 32 heads) decoding one frame
  *   against a ring KV cache with a 3000-frame sliding window and per-slot
  *   recycle; then the depformer (1024-d / 6 layers / 16 heads) runs
- *   autoregressively over 16 codebooks, reset each frame.  "1 user frame in
- *   -> 1 agent frame + 1 text token" per tick ("Why it is different from
- *   MiniCPM-o / JoyVL duplex").
+ *   autoregressively over 16 codebooks, reset each frame.  Each tick takes
+ *   one user audio frame and gives one agent audio frame and one text token
+ *   ("Why it is different from MiniCPM-o / JoyVL duplex").
  *
  *   vLLM-Omni PersonaPlex guide (mhpq.cn), "架构": RMSNorm with fp32 alpha,
  *   fused in-projection attention, interleaved RoPE at absolute positions,

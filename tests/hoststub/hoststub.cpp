@@ -1,0 +1,136 @@
+// Host-only stand-ins for the HIP runtime and for the tick's kernel launchers
+// (see hip/hip_runtime.h here).  TEST INFRASTRUCTURE ONLY.
+//
+// The launchers do no model arithmetic.  The embedding launcher records the
+// tick input block it is given (positions, the 17-row column, the forced
+// choices), and every finisher (standalone or folded into a QKV launch)
+// writes a made-up greedy prediction that depends only on the slot's
+// position and the step, pred = (7 pos + 13 (step + 1) + 5) mod n, then
+// applies the forced choice as the device finisher does.  That is enough to
+// check the host's bookkeeping: which frame, codes and previous choices a
+// tick is given, and how the returned choices are committed.
+#include <cstdlib>
+#include <cstring>
+#include <functional>
+#include <vector>
+
+#include "../../full_duplex_speech_moshi_amd/csrc/kernels.h"
+
+struct stub_stream { std::vector<std::function<void()>>* capture = nullptr; };
+struct stub_event { int dummy = 0; };
+struct stub_graph { std::vector<std::function<void()>> ops; };
+struct stub_graph_exec { std::vector<std::function<void()>> ops; };
+
+namespace {
+std::vector<int32_t> g_last_ti;
+long g_ticks = 0;
+int g_fail_launches = 0;
+
+void submit(hipStream_t s, std::function<void()> f) {
+  if (s && s->capture) s->capture->push_back(std::move(f));
+  else f();
+}
+}  // namespace
+
+const char* hipGetErrorString(hipError_t e) { return e == hipSuccess ? "no error" : "stub launch failure"; }
+hipError_t hipGetLastError() { return hipSuccess; }
+hipError_t hipHostMalloc(void** p, size_t n, unsigned) {
+  *p = std::aligned_alloc(256, (n + 255) / 256 * 256);
+  return *p ? hipSuccess : hipErrorLaunchFailure;
+}
+hipError_t hipHostFree(void* p) { std::free(p); return hipSuccess; }
+hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind, hipStream_t) {
+  std::memmove(dst, src, n);
+  return hipSuccess;
+}
+hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t height,
+                            hipMemcpyKind, hipStream_t) {
+  for (size_t r = 0; r < height; ++r)
+    std::memmove(static_cast<char*>(dst) + r * dpitch, static_cast<const char*>(src) + r * spitch, width);
+  return hipSuccess;
+}
+hipError_t hipMemsetAsync(void* p, int v, size_t n, hipStream_t) { std::memset(p, v, n); return hipSuccess; }
+hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned) { *s = new stub_stream(); return hipSuccess; }
+hipError_t hipStreamDestroy(hipStream_t s) { delete s; return hipSuccess; }
+hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned) { return hipSuccess; }
+hipError_t hipStreamBeginCapture(hipStream_t s, hipStreamCaptureMode) {
+  s->capture = new std::vector<std::function<void()>>();
+  return hipSuccess;
+}
+hipError_t hipStreamEndCapture(hipStream_t s, hipGraph_t* g) {
+  *g = new stub_graph{std::move(*s->capture)};
+  delete s->capture;
+  s->capture = nullptr;
+  return hipSuccess;
+}
+hipError_t hipGraphInstantiate(hipGraphExec_t* e, hipGraph_t g, hipGraphNode_t*, char*, size_t) {
+  *e = new stub_graph_exec{g->ops};
+  return hipSuccess;
+}
+hipError_t hipGraphLaunch(hipGraphExec_t e, hipStream_t s) {
+  if (g_fail_launches > 0) {
+    --g_fail_launches;
+    return hipErrorLaunchFailure;
+  }
+  for (auto& f : e->ops) submit(s, f);
+  return hipSuccess;
+}
+hipError_t hipGraphExecDestroy(hipGraphExec_t e) { delete e; return hipSuccess; }
+hipError_t hipGraphDestroy(hipGraph_t g) { delete g; return hipSuccess; }
+hipError_t hipEventCreate(hipEvent_t* e) { *e = new stub_event(); return hipSuccess; }
+hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) { *e = new stub_event(); return hipSuccess; }
+hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
+hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
+hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) { *ms = 0.f; return hipSuccess; }
+hipError_t hipEventDestroy(hipEvent_t e) { delete e; return hipSuccess; }
+hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+
+namespace pp {
+
+static void emulate_finish(const FinishArgs& f) {
+  for (int b = 0; b < f.B; ++b) {
+    const int pos = f.ti[b * TI_STRIDE + TI_POS];
+    const int pred = (int)((7L * pos + 13L * (f.step + 1) + 5) % f.n_logits);
+    const int forced = f.step < 8 ? f.ti[b * TI_STRIDE + TI_FORCE + 1 + f.step] : -1;
+    int* to = f.to + b * TO_STRIDE;
+    if (f.step < 8) {
+      to[TO_PRED + 1 + f.step] = pred;
+      to[TO_CHOSEN + 1 + f.step] = forced >= 0 ? forced : pred;
+    } else {
+      to[TO_USER + f.step - 8] = pred;
+    }
+  }
+}
+
+void launch_embed(const EmbedArgs& a, hipStream_t s) {
+  submit(s, [a] {
+    g_last_ti.assign(a.ti, a.ti + (size_t)a.B * TI_STRIDE);
+    ++g_ticks;
+  });
+}
+void launch_gemm(Epi epi, const GemmArgs& a, hipStream_t s) {
+  if (epi == EPI_QKV && a.fuse_fin) submit(s, [f = a.fin] { emulate_finish(f); });
+}
+bool gemm_splits_k(Epi, const GemmArgs&) { return false; }
+int gemm_wide_cols(const GemmArgs& a) { return a.B <= 16 ? 16 : 32; }
+void launch_pack(const bf16_t*, int, int, bf16_t*, hipStream_t) {}
+void launch_attention(const AttnArgs&, hipStream_t) {}
+void launch_dep_attention(const DepAttnArgs&, hipStream_t) {}
+void launch_finish(const FinishArgs& a, hipStream_t s) { submit(s, [a] { emulate_finish(a); }); }
+void finish_prepare() {}
+
+}  // namespace pp
+
+extern "C" {
+// The tick input block of the last tick run (int32 [B][TI_STRIDE]); returns
+// the number of ints copied.
+int stub_last_tick_input(int32_t* out, int n) {
+  const int m = (int)g_last_ti.size() < n ? (int)g_last_ti.size() : n;
+  if (m > 0) std::memcpy(out, g_last_ti.data(), (size_t)m * 4);
+  return m;
+}
+long stub_ticks_run() { return g_ticks; }
+// Make the next n graph launches fail (a device error).
+void stub_fail_launches(int n) { g_fail_launches = n; }
+}

@@ -59,6 +59,11 @@ def compare_tick(gpu, ref, t, report):
         if e > HIDDEN_REL_L2:
             fails.append(f"tick {t} hidden[{j}] rel-L2 {e:.3e}")
     report.setdefault("hidden_rel_l2", []).append(worst)
+    # each layer's own contribution (attention + MLP added to the residual),
+    # so that error in a small update cannot hide behind the residual stream
+    contrib = max(rel_l2(gpu["hidden"][j + 1] - gpu["hidden"][j], ref["hidden"][j + 1] - ref["hidden"][j])
+                  for j in range(L1 - 1))
+    report.setdefault("contrib_rel_l2", []).append(contrib)
     d = float(np.abs(gpu["text_logits"] - ref["text_logits"]).max())
     report.setdefault("text_logit_abs", []).append(d)
     if d > LOGIT_ABS:

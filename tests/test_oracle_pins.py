@@ -436,6 +436,51 @@ def test_depformer_attention_closed_form(tiny_weights):
         tok = int(f[0, 1 + k]) if k < 8 else int(np.argmax(lg))
 
 
+def test_depformer_mlp_sublayers_closed_form():
+    """Two-layer depformer with zero input projections and zero attention
+    output (W_o = 0).  Layer l's MLP has gate rows = g_l I, up rows = c_l I
+    and W_out = I (g = 1, 0.5; c = 2, 3; all exact in bf16), so step k is
+    y = e_k; y += silu(g_l h) * c_l h with h = rmsnorm(y, mlp alpha of layer
+    l), for l = 0, 1; logits = head_k . rmsnorm(y, out alpha).  A swapped
+    [gate; up] order, the attention alpha in place of the MLP alpha, or layer
+    0's weights reused at layer 1 each move the logits."""
+    import dataclasses
+    dm = dataclasses.replace(DM, dep_layers=2)
+    w = synth.make_weights(dm, seed=0)
+    dd, dF = dm.dep_d, dm.dep_ffn
+    gains, ups = (1.0, 0.5), (2.0, 3.0)
+    for k in range(dm.dep_q):
+        w[f"dep.in_proj.{k}"] = zeros_bf((dd, dm.d))
+    for l in range(dm.dep_layers):
+        w[f"dep.layers.{l}.wo"] = zeros_bf((dd, dd))
+        win = np.zeros((2 * dF, dd), np.float32)
+        win[:dd] = gains[l] * np.eye(dd)
+        win[dF:dF + dd] = ups[l] * np.eye(dd)
+        w[f"dep.layers.{l}.w_in"] = bf(win)
+        wout = np.zeros((dd, dF), np.float32)
+        wout[:, :dd] = np.eye(dd)
+        w[f"dep.layers.{l}.w_out"] = bf(wout)
+    assert not np.array_equal(w["dep.layers.0.mlp_norm"], w["dep.layers.1.mlp_norm"])
+    assert not np.array_equal(w["dep.layers.0.mlp_norm"], w["dep.layers.0.attn_norm"])
+    f = teacher_frames(1, seed=19, dm=dm)
+    o = Oracle(dm, w, 1, W, dtype=np.float64)
+    o.prefill_forced(0, f)
+    o.step(np.zeros((1, 8)))
+    up = lambda n: ot.upcast_bf16(w[n], np.float64)
+    ao = w["dep.out_norm"].astype(np.float64)
+    tok = int(f[0, 0])
+    for k in range(dm.dep_q):
+        y = up("dep.emb.text" if k == 0 else f"dep.emb.audio.{k}")[tok].copy()
+        for l in range(dm.dep_layers):
+            a = w[f"dep.layers.{l}.mlp_norm"].astype(np.float64)
+            h = y * a / np.sqrt(np.mean(y * y) + dm.norm_eps)
+            g = gains[l] * h
+            y = y + g * scipy.special.expit(g) * ups[l] * h
+        lg = up(f"dep.head.{k}") @ (y * ao / np.sqrt(np.mean(y * y) + dm.norm_eps))
+        np.testing.assert_allclose(o.taps["dep_logits"][0, k], lg, rtol=1e-10, atol=1e-13)
+        tok = int(f[0, 1 + k]) if k < 8 else int(np.argmax(lg))
+
+
 def test_depformer_is_causal_over_codebooks(tiny_weights):
     """Changing the table used at step 5 leaves logits of steps 0-4 unchanged."""
     o1 = Oracle(DM, tiny_weights, 1, W)
