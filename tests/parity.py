@@ -47,9 +47,10 @@ def teacher_frames(recs, codes, schedule=None):
     return f
 
 
-def compare_tick(gpu, ref, t, report):
+def compare_tick(gpu, ref, t, report, tokens=True):
     """Compare one tick's GPU taps (dict for one slot) with the oracle's
-    record; appends stats to report; returns a list of failure strings."""
+    record; appends stats to report; returns a list of failure strings.
+    tokens=False: hidden states and logits only."""
     fails = []
     L1 = ref["hidden"].shape[0]
     worst = 0.0
@@ -68,7 +69,7 @@ def compare_tick(gpu, ref, t, report):
     report.setdefault("text_logit_abs", []).append(d)
     if d > LOGIT_ABS:
         fails.append(f"tick {t} text logits max abs {d:.3e}")
-    if margin(ref["text_logits"]) > MARGIN:
+    if tokens and margin(ref["text_logits"]) > MARGIN:
         report["tok_checked"] = report.get("tok_checked", 0) + 1
         if gpu["tokens"][0] != ref["tokens"][0]:
             fails.append(f"tick {t} text token {gpu['tokens'][0]} != {ref['tokens'][0]}")
@@ -80,7 +81,7 @@ def compare_tick(gpu, ref, t, report):
             fails.append(f"tick {t} dep logits step {k} max abs {dk:.3e}")
         g_pred = gpu["tokens"][1 + k] if k < 8 else gpu["user_pred"][k - 8]
         r_pred = ref["tokens"][1 + k] if k < 8 else ref["user_pred"][k - 8]
-        if margin(ref["dep_logits"][k]) > MARGIN:
+        if tokens and margin(ref["dep_logits"][k]) > MARGIN:
             report["tok_checked"] = report.get("tok_checked", 0) + 1
             if g_pred != r_pred:
                 fails.append(f"tick {t} dep step {k} token {g_pred} != {r_pred}")

@@ -98,14 +98,26 @@ def _parity_run(full, w32, n_ticks, fill_seed=None, codes=None, fill_n=W, sched=
             np.testing.assert_array_equal(g["chosen"], recs[t]["chosen"])
         fails += parity.compare_tick(g, recs[t], t, rep)
         if exact:
-            # The GPU must meet the tolerances against the unrounded-cache
-            # oracle on every tick where the bf16-cache oracle itself meets
-            # them (where a bf16 cache can meet them at all).
-            attainable = not parity.compare_tick(recs[t], recs_exact[t], t, rep_o)
-            fx = parity.compare_tick(g, recs_exact[t], t, rep_x)
+            # Against the unrounded-cache oracle: the hidden-state and logit
+            # tolerances on every tick where the bf16-cache oracle itself
+            # meets them (where a bf16 cache can meet them at all), and on
+            # every tick a distance no larger than 1.25 times the bf16-cache
+            # oracle's own (the GPU's departure from unrounded caches is the
+            # cache rounding's, not more).  Tokens are reported, not gated:
+            # near the 1e-2 margin the two oracles' own logit gap decides them.
+            attainable = not parity.compare_tick(recs[t], recs_exact[t], t, rep_o, tokens=False)
+            fx = parity.compare_tick(g, recs_exact[t], t, rep_x, tokens=False)
             if attainable:
                 fails_x += fx
             rep_x.setdefault("attainable", []).append(attainable)
+            for key, slack in (("hidden_rel_l2", 1e-3), ("text_logit_abs", 1e-2), ("dep_logit_abs", 1e-2)):
+                if rep_x[key][-1] > 1.25 * rep_o[key][-1] + slack:
+                    fails_x.append(f"tick {t} {key} {rep_x[key][-1]:.3e} vs the bf16-cache oracle's own "
+                                   f"{rep_o[key][-1]:.3e}")
+            nd = sum(int(g["tokens"][1 + k] if k < 8 else g["user_pred"][k - 8]) !=
+                     int(recs_exact[t]["tokens"][1 + k] if k < 8 else recs_exact[t]["user_pred"][k - 8])
+                     for k in range(DM.dep_q)) + int(g["tokens"][0] != recs_exact[t]["tokens"][0])
+            rep_x.setdefault("token_diff", []).append(nd)
     e.close()
     _say(f"vs bf16-cache oracle: worst hidden rel-L2 {max(rep['hidden_rel_l2']):.3e}, layer contribution "
          f"{max(rep['contrib_rel_l2']):.3e}, text logit abs {max(rep['text_logit_abs']):.3e}, dep logit abs "
@@ -117,18 +129,22 @@ def _parity_run(full, w32, n_ticks, fill_seed=None, codes=None, fill_n=W, sched=
                  + " ".join(f"{v:.2e}" for v in r["contrib_rel_l2"]) + "; text logit abs "
                  + " ".join(f"{v:.2e}" for v in r["text_logit_abs"]))
         _say(f"ticks where a bf16 cache meets the tolerances against the unrounded-cache oracle: "
-             f"{[t for t, a in enumerate(rep_x['attainable']) if a]}")
+             f"{[t for t, a in enumerate(rep_x['attainable']) if a]}; GPU predictions (17 per tick) that differ "
+             f"from the unrounded-cache oracle's, per tick: {rep_x['token_diff']}")
     return fails, fails_x, rep
 
 
 @pytest.mark.timeout(900)
 def test_full_empty_ring_teacher_forced(full, w32):
     """From an empty ring, 20 teacher-forced ticks (20 keys at the end), the
-    GPU against the oracle with bf16 caches, and against the oracle that keeps
-    its caches unrounded at the same tolerances on every tick where the
-    bf16-cache oracle meets them against it.  With these random weights the
-    two oracles drift apart (the rounding of the stored keys and values is
-    amplified layer by layer): the test prints both distances per tick."""
+    GPU against the oracle with bf16 caches (all tolerances, tokens
+    included), and against the oracle that keeps its caches unrounded: the
+    hidden-state and logit tolerances on every tick where the bf16-cache
+    oracle meets them against it, and on every tick no more than 1.25 times
+    the bf16-cache oracle's own distance.  With these random weights the two
+    oracles drift apart (the rounding of the stored keys and values is
+    amplified layer by layer, past 1e-2 hidden rel-L2 from the fourth tick):
+    the test prints both distances per tick."""
     _say("case: 7B, B=1, empty ring, 20 teacher-forced ticks, bf16-cache and unrounded-cache oracles")
     fails, fails_x, _ = _parity_run(full, w32, 20, exact=True)
     assert not fails, "\n".join(fails[:20])
