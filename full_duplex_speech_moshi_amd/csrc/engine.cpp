@@ -34,6 +34,8 @@ struct Layout {
   // the user-stream codebooks of tick t, which keep using the other set
   size_t dkv[2], amax_v[2], amax_i[2], u[2], y[2], ya[2], dpart[2], dq[2], dout[2], dm[2], sctx[2];
   size_t samp, rep;  // sampling parameters; recent chosen text tokens [B][SAMPLE_REP]
+  // the same work buffers laid out in the library's static array (pp_step_static)
+  size_t s_att_cnt, s_wide_rms, s_att_part, s_split_part, s_total;
   long wide_part_max;
   int max_chunks, n_amax;
   long ring_slot_elems, ring_layer_elems, ring_v_off;
@@ -124,6 +126,13 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.rep = take((size_t)B * SAMPLE_REP * 4);
   L.att_cnt = take((size_t)B * H * 4);
   L.total = off;
+  // work buffers only (partials, tickets, inverse RMS), for the static array
+  off = 0;
+  L.s_att_cnt = take((size_t)B * H * 4);
+  L.s_wide_rms = take(MAX_COLS * 4);
+  L.s_att_part = take((size_t)B * H * L.max_chunks * (hd + 2) * 4);
+  L.s_split_part = B >= WIDE_MIN_B ? take((size_t)L.wide_part_max * 4) : take(0);
+  L.s_total = off;
   return L;
 }
 
@@ -178,6 +187,12 @@ struct pp_handle {
   hipStream_t stream = nullptr, cap = nullptr, side = nullptr;
   hipGraph_t graph[5] = {};
   hipGraphExec_t exec[5] = {};
+  // PH_TEMPORAL and the two PH_AGENT graphs again, with the work buffers in
+  // the library's static array (pp_step_static); PH_USER uses none of them
+  char* sptr = nullptr;    // device address of that array on this handle's device
+  bool static_ok = false;  // this handle's work buffers fit in it
+  hipGraph_t graph_s[3] = {};
+  hipGraphExec_t exec_s[3] = {};
   hipEvent_t temporal_done = nullptr, agent_done = nullptr, user_done[2] = {nullptr, nullptr};
   int parity = 0;             // depformer buffer set of the next tick
   bool user_pending = false;  // PH_USER of the last tick not launched yet
@@ -236,7 +251,8 @@ enum Phase { PH_TEMPORAL = 0, PH_AGENT = 1, PH_USER = 2 };
 
 // Record the kernels of one phase of the tick on stream s.
 // `ds`: the depformer buffer set (PH_AGENT and PH_USER of one tick share one).
-void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_timed) {
+// `stat`: the work buffers are in the library's static array, not the arena.
+void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_timed, bool stat = false) {
   const pp_dims& dm = h->dm;
   const Layout& L = h->lay;
   const int B = h->B, W = h->W;
@@ -246,10 +262,15 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
   const int* ti = h->at<int>(L.ti);
   int* to = h->at<int>(L.to);
   const double* inv_freq = h->at<double>(L.inv_freq);
-  float* split_part = h->at<float>(L.split_part);
-  float* wide_rms = h->at<float>(L.wide_rms);
+  float* split_part = stat ? reinterpret_cast<float*>(h->sptr + L.s_split_part) : h->at<float>(L.split_part);
+  float* wide_rms = stat ? reinterpret_cast<float*>(h->sptr + L.s_wide_rms) : h->at<float>(L.wide_rms);
+  float* att_part = stat ? reinterpret_cast<float*>(h->sptr + L.s_att_part) : h->at<float>(L.att_part);
+  unsigned* att_cnt = stat ? reinterpret_cast<unsigned*>(h->sptr + L.s_att_cnt) : h->at<unsigned>(L.att_cnt);
 
   if (phase == PH_TEMPORAL) {
+    // the split tickets must start at zero: the static array keeps whatever
+    // the last call on this GPU left there
+    if (stat) launch_zero_u32(att_cnt, (long)B * H, s);
     EmbedArgs ea{};
     ea.ti = ti;
     ea.B = B;
@@ -317,12 +338,12 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
       at.window = W;
       at.B = B;
       at.ti = ti;
-      at.part = h->at<float>(L.att_part);
+      at.part = att_part;
       at.max_chunks = L.max_chunks;
       at.o = h->at<bf16_t>(L.o);
       at.ldo = d;
       at.o_lo = (long)B * d;
-      at.cnt = h->at<unsigned>(L.att_cnt);
+      at.cnt = att_cnt;
       if (g.qkv_to_attn) {
         at.qkv_part = split_part;
         at.qkv_cols = gemm_wide_cols(g);
@@ -725,6 +746,20 @@ hipError_t capture_graphs(pp_handle* h) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipGraphInstantiate(&h->exec[g], h->graph[g], nullptr, nullptr, 0)) != hipSuccess) return e;
   }
+  for (int g = 0; g < 3; ++g) {
+    if (h->exec_s[g]) (void)hipGraphExecDestroy(h->exec_s[g]);
+    if (h->graph_s[g]) (void)hipGraphDestroy(h->graph_s[g]);
+    h->exec_s[g] = nullptr;
+    h->graph_s[g] = nullptr;
+    if (!h->static_ok) continue;
+    const Phase ph = g == 0 ? PH_TEMPORAL : PH_AGENT;
+    const int ds = g == 0 ? 0 : g - 1;
+    if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
+    record_tick(h, h->cap, ph, ds, false, true);
+    if ((e = hipStreamEndCapture(h->cap, &h->graph_s[g])) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGraphInstantiate(&h->exec_s[g], h->graph_s[g], nullptr, nullptr, 0)) != hipSuccess) return e;
+  }
   return hipSuccess;
 }
 
@@ -745,15 +780,16 @@ hipError_t launch_user(pp_handle* h, hipEvent_t after) {
 
 // Launch one tick: PH_TEMPORAL; then the previous tick's PH_USER on the side
 // stream; then, once PH_USER of two ticks back has released this tick's
-// buffer set, PH_AGENT.  This tick's PH_USER is left pending.
-hipError_t launch_tick(pp_handle* h) {
+// buffer set, PH_AGENT.  This tick's PH_USER is left pending.  `stat`: the
+// graphs whose work buffers are in the library's static array.
+hipError_t launch_tick(pp_handle* h, bool stat = false) {
   const int ds = h->parity;
   hipError_t e;
-  if ((e = hipGraphLaunch(h->exec[0], h->stream)) != hipSuccess) return e;
+  if ((e = hipGraphLaunch(stat ? h->exec_s[0] : h->exec[0], h->stream)) != hipSuccess) return e;
   if ((e = hipEventRecord(h->temporal_done, h->stream)) != hipSuccess) return e;
   if ((e = launch_user(h, h->temporal_done)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(h->stream, h->user_done[ds], 0)) != hipSuccess) return e;
-  if ((e = hipGraphLaunch(h->exec[1 + ds], h->stream)) != hipSuccess) return e;
+  if ((e = hipGraphLaunch(stat ? h->exec_s[1 + ds] : h->exec[1 + ds], h->stream)) != hipSuccess) return e;
   if ((e = hipEventRecord(h->agent_done, h->stream)) != hipSuccess) return e;
   h->user_pending = true;
   h->parity = 1 - ds;
@@ -850,6 +886,12 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
     return bail("hipMemcpyAsync", e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
   finish_prepare();
+  {
+    void* sp = nullptr;
+    if ((e = static_scratch(&sp)) != hipSuccess) return bail("hipGetSymbolAddress (static work buffers)", e);
+    h->sptr = static_cast<char*>(sp);
+    h->static_ok = lay.s_total <= STATIC_SCRATCH_BYTES;
+  }
   if ((e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
   if ((e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
   for (hipEvent_t* ev : {&h->temporal_done, &h->agent_done, &h->user_done[0], &h->user_done[1]}) {
@@ -974,10 +1016,19 @@ int pp_agent_frames(const pp_handle* h, int32_t* frames, int32_t* valid) {
   return PP_OK;
 }
 
-int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
+}  // extern "C"
+
+namespace {
+
+// One tick (pp_step, and pp_step_static with `stat`).  Allocates no memory:
+// the frames in use sit in a fixed array.
+int step_impl(pp_handle* h, const int32_t* user_codes, int32_t* tokens, bool stat) {
   if (!h) return PP_EINVAL;
   if (h->poisoned) return PP_EDEVICE;
   if (!user_codes || !tokens) return h->fail(PP_EINVAL, "NULL user_codes or tokens");
+  if (stat && !h->static_ok)
+    return h->fail(PP_ENOSPC, "work buffers of %zu bytes exceed the static array of %zu bytes", h->lay.s_total,
+                   STATIC_SCRATCH_BYTES);
   const int A = h->dm.audio_card;
   for (int b = 0; b < h->B; ++b) {
     if (h->slots[b].pos >= 0x7fffffff) return h->fail(PP_EINVAL, "slot %d position overflow", b);
@@ -987,7 +1038,7 @@ int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
       if (c < 0 || c >= A) return h->fail(PP_EINVAL, "slot %d user code %d out of range", b, c);
     }
   }
-  std::vector<const Frame*> frames(h->B, nullptr);
+  std::array<const Frame*, PP_MAX_BATCH> frames{};
   bool any_x = false;
   for (int b = 0; b < h->B; ++b)
     if (!h->slots[b].queue.empty()) {
@@ -1012,7 +1063,7 @@ int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
     HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(h->lay.rep), h->rep_host, (size_t)h->B * SAMPLE_REP * 4,
                                   hipMemcpyHostToDevice, h->stream));
   }
-  HIP_OR_FAIL(h, launch_tick(h));
+  HIP_OR_FAIL(h, launch_tick(h, stat));
   // the agent outputs only (the user-stream codebooks may still be writing theirs)
   HIP_OR_FAIL(h, hipMemcpy2DAsync(h->to_host + TO_PRED, TO_STRIDE * 4, h->at<int>(h->lay.to) + TO_PRED, TO_STRIDE * 4,
                                   9 * 4, h->B, hipMemcpyDeviceToHost, h->stream));
@@ -1033,6 +1084,18 @@ int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
     s.pos += 1;
   }
   return PP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
+  return step_impl(h, user_codes, tokens, false);
+}
+
+int pp_step_static(pp_handle* h, const int32_t* user_codes, int32_t* tokens) {
+  return step_impl(h, user_codes, tokens, true);
 }
 
 int pp_slot_reset(pp_handle* h, int slot) {
@@ -1171,6 +1234,10 @@ void pp_destroy(pp_handle* h) {
   for (int g = 0; g < 5; ++g) {
     if (h->exec[g]) (void)hipGraphExecDestroy(h->exec[g]);
     if (h->graph[g]) (void)hipGraphDestroy(h->graph[g]);
+  }
+  for (int g = 0; g < 3; ++g) {
+    if (h->exec_s[g]) (void)hipGraphExecDestroy(h->exec_s[g]);
+    if (h->graph_s[g]) (void)hipGraphDestroy(h->graph_s[g]);
   }
   for (hipEvent_t ev : {h->temporal_done, h->agent_done, h->user_done[0], h->user_done[1]})
     if (ev) (void)hipEventDestroy(ev);

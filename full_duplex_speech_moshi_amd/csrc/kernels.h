@@ -189,4 +189,12 @@ void launch_embed(const EmbedArgs& a, hipStream_t s);
 void launch_finish(const FinishArgs& a, hipStream_t s);
 void finish_prepare();  // once per process, before the first finisher launch
 
+// The library's own work-buffer array for the allocation-free entry point
+// (pp_step_static): STATIC_SCRATCH_BYTES of device memory per GPU, held until
+// the process ends.  static_scratch() returns its device address on the
+// current device, looked up once per device; launch_zero_u32 clears n words.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t static_scratch(void** out);
+void launch_zero_u32(unsigned* p, long n, hipStream_t s);
+
 }  // namespace pp

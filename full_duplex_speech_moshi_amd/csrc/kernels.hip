@@ -10,6 +10,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace pp {
 
 // ---------------------------------------------------------------------------
@@ -1802,6 +1804,43 @@ void launch_finish(const FinishArgs& a, hipStream_t s) {
   // room for the row only where it can be sampled (pp_set_sampling refuses wider rows)
   const size_t lds = (a.sp && a.n_logits <= SAMPLE_MAX_N) ? (size_t)a.n_logits * 4 : 0;
   hipLaunchKernelGGL(finish_kernel, dim3(a.B), dim3(256), lds, s, a);
+}
+
+// ---------------------------------------------------------------------------
+// Work buffers held by the library for callers that cannot allocate device
+// memory.  In host code `scratch` names a host-side stand-in, not the device
+// array: kernels are only ever given the address hipGetSymbolAddress returns
+// for the current device, kept per device below.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(void** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(unsigned* p, long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+void launch_zero_u32(unsigned* p, long n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
 }
 
 }  // namespace pp

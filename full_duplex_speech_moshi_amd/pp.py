@@ -20,7 +20,7 @@ PP_MAX_QUEUE = 4096
 PP_MAX_DELAY = 4
 TO_STRIDE = 32
 
-EXPORTS = ("pp_arena_bytes", "pp_create", "pp_prefill_forced", "pp_prefill_embed", "pp_step",
+EXPORTS = ("pp_arena_bytes", "pp_create", "pp_prefill_forced", "pp_prefill_embed", "pp_step", "pp_step_static",
            "pp_set_acoustic_delay", "pp_agent_frames", "pp_set_sampling", "pp_slot_seed", "pp_slot_reset",
            "pp_ring_fill", "pp_taps",
            "pp_time_kernel", "pp_time_graph", "pp_destroy", "pp_last_error", "pp_packed_elems",
@@ -84,6 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pp_set_sampling.argtypes = [P, ctypes.POINTER(PPSampling)]
     lib.pp_slot_seed.argtypes = [P, I, ctypes.c_uint64]
     lib.pp_step.argtypes = [P, P, P]
+    lib.pp_step_static.argtypes = [P, P, P]
     lib.pp_slot_reset.argtypes = [P, I]
     lib.pp_ring_fill.argtypes = [P, I, I, P, P]
     lib.pp_taps.argtypes = [P, ctypes.POINTER(PPTaps)]
@@ -180,6 +181,13 @@ def pp_step(h: int, user_codes, B: int) -> np.ndarray:
     u = _i32(user_codes, (B, 8))
     tok = np.empty((B, 9), np.int32)
     _check(load_library().pp_step(h, u.ctypes.data, tok.ctypes.data), h)
+    return tok
+
+
+def pp_step_static(h: int, user_codes, B: int) -> np.ndarray:
+    u = _i32(user_codes, (B, 8))
+    tok = np.empty((B, 9), np.int32)
+    _check(load_library().pp_step_static(h, u.ctypes.data, tok.ctypes.data), h)
     return tok
 
 
@@ -332,6 +340,9 @@ class Engine:
 
     def step(self, user_codes) -> np.ndarray:
         return pp_step(self.h, user_codes, self.B)
+
+    def step_static(self, user_codes) -> np.ndarray:
+        return pp_step_static(self.h, user_codes, self.B)
 
     def slot_reset(self, slot):
         pp_slot_reset(self.h, slot)

@@ -200,6 +200,21 @@ int pp_prefill_embed(pp_handle* h, int slot, const float* x, const int32_t* forc
  * its results are those of the plain sequence. */
 int pp_step(pp_handle* h, const int32_t* user_codes, int32_t* tokens);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): the same tick as
+ * pp_step, with the same arguments, errors and results, whose kernels keep
+ * their work buffers (split-decode partials and tickets, large-batch GEMM
+ * partials, per-launch inverse RMS) in an array of PP_STATIC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends,
+ * instead of in the handle's arena.  Calls no allocation routine.  Every
+ * call on one GPU shares that array and it keeps the last call's contents:
+ * the tickets that must start at zero are cleared at the start of each tick,
+ * and calls on one GPU that overlap in time (handles on different streams)
+ * race.  pp_step and pp_step_static may be mixed on one handle.  PP_ENOSPC
+ * if the handle's work buffers exceed PP_STATIC_SCRATCH_BYTES. */
+#define PP_STATIC_SCRATCH_BYTES (64u << 20)
+int pp_step_static(pp_handle* h, const int32_t* user_codes, int32_t* tokens);
+
 /* Acoustic delay (recipe, interruption latency: an 80 ms frame plus an
  * 80 ms acoustic delay, i.e. D = 1 at 12.5 Hz): audio codebooks 1-7 of both
  * streams run D frames behind the text row and codebook 0.  user_codes (and

@@ -119,6 +119,14 @@ void launch_attention(const AttnArgs&, hipStream_t) {}
 void launch_dep_attention(const DepAttnArgs&, hipStream_t) {}
 void launch_finish(const FinishArgs& a, hipStream_t s) { submit(s, [a] { emulate_finish(a); }); }
 void finish_prepare() {}
+hipError_t static_scratch(void** out) {
+  static std::vector<char> buf(STATIC_SCRATCH_BYTES);
+  *out = buf.data();
+  return hipSuccess;
+}
+void launch_zero_u32(unsigned* p, long n, hipStream_t s) {
+  submit(s, [p, n] { std::memset(p, 0, (size_t)n * 4); });
+}
 
 }  // namespace pp
 

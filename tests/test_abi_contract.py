@@ -303,3 +303,45 @@ def test_create_arguments(lib):
                          ctypes.byref(h)) == pp.PP_EINVAL
     assert lib.pp_create(ctypes.byref(dims), 2, W, ctypes.byref(w), base, n.value, None, ctypes.byref(h)) == 0
     lib.pp_destroy(h.value)
+
+
+def test_step_static_same_state_machine_and_size_limit(lib):
+    """pp_step_static gives the ticks pp_step gives; a handle whose work
+    buffers exceed PP_STATIC_SCRATCH_BYTES is refused with PP_ENOSPC and no
+    state change (B = 9 with a 70000-token text head: 70 MB of partials)."""
+    lib.pp_step_static.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pp_step_static.restype = ctypes.c_int
+    a, b = Handle(lib), Handle(lib)
+    c = codes(8, 3)
+    tok = np.zeros((B, 9), np.int32)
+    for t in range(3):
+        cc = np.ascontiguousarray(c[t])
+        assert lib.pp_step_static(a.h, cc.ctypes.data, tok.ctypes.data) == 0
+        tia = a.ti()
+        rb, tb = b.step(c[t])
+        np.testing.assert_array_equal(tok, tb)
+        np.testing.assert_array_equal(tia, b.ti())
+    a.close()
+    b.close()
+    import dataclasses
+    big = dataclasses.replace(DM, text_card=70000)
+    dims = pp.make_dims(big)
+    n = ctypes.c_size_t()
+    assert lib.pp_arena_bytes(ctypes.byref(dims), 9, W, ctypes.byref(n)) == 0
+    buf = np.zeros(n.value + 256, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    wbuf = np.zeros(64, np.uint8)
+    w = pp.PPWeights(**{f: wbuf.ctypes.data for f in pp.WEIGHT_FIELDS})
+    h = ctypes.c_void_p()
+    assert lib.pp_create(ctypes.byref(dims), 9, W, ctypes.byref(w), base, n.value, None, ctypes.byref(h)) == 0
+    cc = np.zeros((9, 8), np.int32)
+    tok = np.zeros((9, 9), np.int32)
+    runs = lib.stub_ticks_run()
+    assert lib.pp_step_static(h.value, cc.ctypes.data, tok.ctypes.data) == pp.PP_ENOSPC
+    assert b"static array" in lib.pp_last_error(h.value)
+    assert lib.stub_ticks_run() == runs
+    assert lib.pp_step(h.value, cc.ctypes.data, tok.ctypes.data) == 0
+    out = np.zeros(9 * TI_STRIDE, np.int32)
+    lib.stub_last_tick_input(out.ctypes.data, out.size)
+    assert out[TI_POS] == 0      # the refused call did not advance the slot
+    lib.pp_destroy(h.value)
