@@ -42,7 +42,7 @@ def build(verbose: bool = True) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     with tempfile.TemporaryDirectory() as tmp:
         objs = []
-        for src, flags in (("kernels.hip", HIP_FLAGS), ("engine.cpp", HOST_FLAGS)):
+        for src, flags in (("kernels.hip", HIP_FLAGS), ("dep_loop.hip", HIP_FLAGS), ("engine.cpp", HOST_FLAGS)):
             obj = os.path.join(tmp, src + ".o")
             _run([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
             objs.append(obj)

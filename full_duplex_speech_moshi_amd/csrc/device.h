@@ -37,6 +37,30 @@ __device__ __forceinline__ void store_split(bf16_t* p, long lo, float v) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Pointers with their address space spelled out (LDS: 3, global: 1), for
+// code whose pointers travel through structures: accesses through them
+// compile to ds_* and global_* instructions, not flat ones (which would make
+// every LDS read wait for all global loads in flight).
+typedef __attribute__((address_space(3))) float lfloat;
+typedef __attribute__((address_space(3))) bf16_t lbf16;
+typedef __attribute__((address_space(3))) int lint;
+typedef __attribute__((address_space(3))) uint32_t lu32;
+typedef __attribute__((address_space(3))) char lchar;
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) bf16_t gbf16;
+typedef __attribute__((address_space(1))) int gint;
+typedef __attribute__((address_space(1))) uint32_t gu32;
+typedef __attribute__((address_space(1))) uint64_t gu64;
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
+
+__device__ __forceinline__ const uint32_t* as_u32(const bf16_t* p) { return reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ const lu32* as_u32(const lbf16* p) { return reinterpret_cast<const lu32*>(p); }
+__device__ __forceinline__ void store_split(lbf16* p, long lo, float v) {
+  const bf16_t h = f2bf(v);
+  p[0] = h;
+  p[lo] = f2bf(v - bf2f(h));
+}
 // Weight loads.  Weights read once per tick (temporal stack, heads, input
 // projections: far larger than the caches) carry the non-temporal hint; the
 // depformer layers, re-read at every codebook step, are loaded normally so
@@ -117,19 +141,21 @@ struct DepAttnOut {
   bool ok;
 };
 
-template <int DH>
-__device__ DepAttnOut dep_attend(const DepAttnArgs& d, const int pair0) {
+// Args: DepAttnArgs (global memory), or a structure with the same fields
+// pointing into LDS; the arithmetic is the same either way.
+template <int DH, class Args>
+__device__ __forceinline__ DepAttnOut dep_attend(const Args& d, const int pair0) {
   constexpr int LP = DH / 2;  // lanes per pair
   const int lane = threadIdx.x & 63;
   const int pair = pair0 + lane / LP, f = 2 * (lane % LP);
   const bool ok = pair < d.B * d.n_heads;
   const int b = ok ? pair / d.n_heads : 0, h = ok ? pair - b * d.n_heads : 0;
-  const float* qp = d.q + (long)b * d.ldq + h * DH + f;
+  const auto qp = d.q + (long)b * d.ldq + h * DH + f;
   const float q0 = ok ? qp[0] : 0.f, q1 = ok ? qp[1] : 0.f;
-  const bf16_t* kb = d.kv + (long)b * d.slot_stride + (long)h * d.window * DH + f;
-  const uint32_t* kw = reinterpret_cast<const uint32_t*>(kb);
-  const uint32_t* vw = reinterpret_cast<const uint32_t*>(kb + d.v_off);
-  const int n = d.n_keys;
+  const auto kb = d.kv + (long)b * d.slot_stride + (long)h * d.window * DH + f;
+  const auto kw = as_u32(kb);
+  const auto vw = as_u32(kb + d.v_off);
+  const int n = d.n_keys_b ? d.n_keys_b[b] : d.n_keys;
   uint32_t kk[DEP_MAX_KEYS], vv[DEP_MAX_KEYS];
 #pragma unroll
   for (int p = 0; p < DEP_MAX_KEYS; ++p) {

@@ -36,6 +36,12 @@ struct Layout {
   size_t samp, rep;  // sampling parameters; recent chosen text tokens [B][SAMPLE_REP]
   // the same work buffers laid out in the library's static array (pp_step_static)
   size_t s_att_cnt, s_wide_rms, s_att_part, s_split_part, s_total;
+  // fused depformer loop (B <= 2 and supported dims): exchange words, tagged
+  // key/value cache [2 sets][B slots], the agent halves' cache tags, control
+  bool dl_ok;
+  size_t dl_x, dl_kv, dl_kvtag, dl_ctl;
+  DepLoopLayout dl;
+  long dl_kv_slot_words;
   long wide_part_max;
   int max_chunks, n_amax;
   long ring_slot_elems, ring_layer_elems, ring_v_off;
@@ -125,6 +131,13 @@ Layout make_layout(const pp_dims& dm, int B, int W) {
   L.samp = take(sizeof(SampleParams));
   L.rep = take((size_t)B * SAMPLE_REP * 4);
   L.att_cnt = take((size_t)B * H * 4);
+  L.dl_ok = B <= 2 && dep_loop_supported((int)dd, (int)dH, (int)dF, (int)A, nullptr);
+  L.dl = dep_loop_layout((int)dd, (int)dF, dm.dep_layers, (int)A, 2 * B);
+  L.dl_kv_slot_words = dep_loop_kv_words((int)dd, dm.dep_layers);
+  L.dl_x = take(L.dl_ok ? (size_t)L.dl.total * 8 : 0);
+  L.dl_kv = take(L.dl_ok ? (size_t)2 * B * L.dl_kv_slot_words * 8 : 0);
+  L.dl_kvtag = take(L.dl_ok ? 2 * PP_MAX_BATCH * 4 : 0);
+  L.dl_ctl = take(L.dl_ok ? 64 : 0);
   L.total = off;
   // work buffers only (partials, tickets, inverse RMS), for the static array
   off = 0;
@@ -193,6 +206,17 @@ struct pp_handle {
   bool static_ok = false;  // this handle's work buffers fit in it
   hipGraph_t graph_s[3] = {};
   hipGraphExec_t exec_s[3] = {};
+  // The fused depformer loop (B <= 2, greedy, supported dims): the depformer
+  // of a tick is one persistent launch after the input projections.  The
+  // user-stream half of tick t runs as extra columns of tick t+1's launch, on
+  // the caller's stream.  exec_f[ds] = agent half on set ds with the pending
+  // user half (set 1 - ds); exec_f[2 + ds] = agent half alone; exec_f[4 + ds] =
+  // user half of set ds alone (flushes).
+  bool dl_on = false;         // use the fused loop where it applies (pp_set_depformer_loop)
+  bool fused = false;         // it applies now (dl_ok, dl_on and greedy)
+  bool pending_fused = false; // the pending user half belongs to the fused path
+  hipGraph_t graph_f[6] = {};
+  hipGraphExec_t exec_f[6] = {};
   hipEvent_t temporal_done = nullptr, agent_done = nullptr, user_done[2] = {nullptr, nullptr};
   int parity = 0;             // depformer buffer set of the next tick
   bool user_pending = false;  // PH_USER of the last tick not launched yet
@@ -660,6 +684,89 @@ void record_tick(pp_handle* h, hipStream_t s, Phase phase, int ds, bool keep_tim
   }
 }
 
+// Record the depformer of a tick as one fused launch on stream s: the input
+// projections of set ds (with the agent half) and the loop over the agent
+// half of set ds and / or the user half of set su.
+void record_fused(pp_handle* h, hipStream_t s, bool agent, int ds, bool user, int su) {
+  const pp_dims& dm = h->dm;
+  const Layout& L = h->lay;
+  const int B = h->B, d = dm.d, dd = dm.dep_d, Q = dm.dep_q, A = dm.audio_card, Vt = dm.text_card;
+  const pp_weights& w = h->w;
+  if (agent) {
+    GemmArgs gp{};
+    gp.W = w.dep_in_proj;
+    gp.X = h->at<bf16_t>(L.xa);
+    gp.x_lo = (long)B * d;
+    gp.M = Q * dd;
+    gp.K = d;
+    gp.ldx = d;
+    gp.B = B;
+    gp.part_in = h->at<float>(L.part);
+    gp.n_part = d / 16;
+    gp.feat = d;
+    gp.eps = dm.norm_eps;
+    gp.f_out = h->at<float>(L.u[ds]);
+    gp.ldf = (long)Q * dd;
+    launch_gemm(EPI_STORE, gp, s);  // B <= 2: the small-batch path, no scratch
+  }
+  DepLoopArgs a{};
+  int c = 0;
+  for (int half = 0; half < 2; ++half) {
+    if (half == 0 ? !agent : !user) continue;
+    const int set = half == 0 ? ds : su;
+    for (int b = 0; b < B; ++b, ++c) {
+      a.col[c].slot = b;
+      a.col[c].k0 = half == 0 ? 0 : dm.n_q;
+      a.col[c].set = set;
+    }
+  }
+  a.ncols = c;
+  for (int set = 0; set < 2; ++set) {
+    a.u[set] = h->at<float>(L.u[set]);
+    a.y[set] = h->at<float>(L.y[set]);
+  }
+  a.logits = h->at<float>(L.dep_logits);
+  a.dd = dd;
+  a.dH = dm.dep_heads;
+  a.dhd = dd / dm.dep_heads;
+  a.dF = dm.dep_ffn;
+  a.Ld = dm.dep_layers;
+  a.A = A;
+  a.dep_q = Q;
+  a.n_q = dm.n_q;
+  a.eps = dm.norm_eps;
+  a.wqkv = w.dep_wqkv;
+  a.wo = w.dep_wo;
+  a.w_in = w.dep_w_in;
+  a.w_out = w.dep_w_out;
+  a.heads = w.dep_heads;
+  a.emb_text = w.dep_emb_text;
+  a.emb_audio = w.dep_emb_audio;
+  a.attn_norm = w.dep_attn_norm;
+  a.mlp_norm = w.dep_mlp_norm;
+  a.out_norm = w.dep_out_norm;
+  a.tamax_v = h->at<float>(L.tamax_v);
+  a.tamax_i = h->at<int>(L.tamax_i);
+  a.ld_amax = L.n_amax;
+  a.n_tpart = (Vt + ROWS - 1) / ROWS;
+  a.ti = h->at<int>(L.ti);
+  a.to = h->at<int>(L.to);
+  uint64_t* x = h->at<uint64_t>(L.dl_x);
+  const DepLoopLayout xl = dep_loop_layout(dd, dm.dep_ffn, dm.dep_layers, A, c);
+  a.xq = x + xl.q;
+  a.xo = x + xl.o;
+  a.xm = x + xl.m;
+  a.xd = x + xl.d;
+  a.xh = x + xl.h;
+  a.kv = h->at<uint64_t>(L.dl_kv);
+  a.kv_slot_words = L.dl_kv_slot_words;
+  a.kv_set_words = (long)B * L.dl_kv_slot_words;
+  a.kvtag = h->at<uint32_t>(L.dl_kvtag);
+  a.ctl = h->at<uint32_t>(L.dl_ctl);
+  a.spin_limit = 1L << 20;  // polls (about a microsecond each) before a wait gives up
+  launch_dep_loop(a, s);
+}
+
 // Fill the tick-input staging buffer from slot state; frames[b] = prefill
 // frame consumed this tick or nullptr.  Reads the delay history without
 // changing it.  Text row and codebook 0 take this tick's frame; codebooks
@@ -746,6 +853,20 @@ hipError_t capture_graphs(pp_handle* h) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipGraphInstantiate(&h->exec[g], h->graph[g], nullptr, nullptr, 0)) != hipSuccess) return e;
   }
+  h->fused = h->lay.dl_ok && h->dl_on && !h->samp.enabled;
+  for (int g = 0; g < 6; ++g) {
+    if (h->exec_f[g]) (void)hipGraphExecDestroy(h->exec_f[g]);
+    if (h->graph_f[g]) (void)hipGraphDestroy(h->graph_f[g]);
+    h->exec_f[g] = nullptr;
+    h->graph_f[g] = nullptr;
+    if (!h->fused) continue;
+    const int ds = g & 1, kind = g >> 1;  // 0 agent + pending user, 1 agent, 2 user
+    if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
+    record_fused(h, h->cap, kind != 2, ds, kind != 1, kind == 0 ? 1 - ds : ds);
+    if ((e = hipStreamEndCapture(h->cap, &h->graph_f[g])) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGraphInstantiate(&h->exec_f[g], h->graph_f[g], nullptr, nullptr, 0)) != hipSuccess) return e;
+  }
   for (int g = 0; g < 3; ++g) {
     if (h->exec_s[g]) (void)hipGraphExecDestroy(h->exec_s[g]);
     if (h->graph_s[g]) (void)hipGraphDestroy(h->graph_s[g]);
@@ -770,6 +891,12 @@ hipError_t launch_user(pp_handle* h, hipEvent_t after) {
   if (!h->user_pending) return hipSuccess;
   const int ds = 1 - h->parity;
   hipError_t e;
+  if (h->pending_fused) {  // the fused loop's user half alone, on the caller's stream
+    if ((e = hipGraphLaunch(h->exec_f[4 + ds], h->stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(h->user_done[ds], h->stream)) != hipSuccess) return e;
+    h->user_pending = false;
+    return hipSuccess;
+  }
   if ((e = hipStreamWaitEvent(h->side, h->agent_done, 0)) != hipSuccess) return e;
   if (after && (e = hipStreamWaitEvent(h->side, after, 0)) != hipSuccess) return e;
   if ((e = hipGraphLaunch(h->exec[3 + ds], h->side)) != hipSuccess) return e;
@@ -785,6 +912,28 @@ hipError_t launch_user(pp_handle* h, hipEvent_t after) {
 hipError_t launch_tick(pp_handle* h, bool stat = false) {
   const int ds = h->parity;
   hipError_t e;
+  const bool fz = h->fused && !stat;  // pp_step_static takes the per-launch graphs
+  // a pending user half of the other kind completes first, in its own way;
+  // before a fused launch the caller's stream waits for it (the persistent
+  // launch needs every compute unit)
+  if (h->user_pending && h->pending_fused != fz) {
+    if ((e = launch_user(h, nullptr)) != hipSuccess) return e;
+    if (fz && (e = hipStreamWaitEvent(h->stream, h->user_done[1 - ds], 0)) != hipSuccess) return e;
+  }
+  if (fz) {
+    // the temporal stack, then one launch for the agent half of this tick
+    // and the pending user half of the last one (all on the caller's stream)
+    if ((e = hipGraphLaunch(h->exec[0], h->stream)) != hipSuccess) return e;
+    // a user half of set ds run on the second stream (by a per-launch tick)
+    // must be done before this tick's agent half reuses the set
+    if ((e = hipStreamWaitEvent(h->stream, h->user_done[ds], 0)) != hipSuccess) return e;
+    if ((e = hipGraphLaunch(h->exec_f[(h->user_pending ? 0 : 2) + ds], h->stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(h->user_done[1 - ds], h->stream)) != hipSuccess) return e;
+    h->user_pending = true;
+    h->pending_fused = true;
+    h->parity = 1 - ds;
+    return hipSuccess;
+  }
   if ((e = hipGraphLaunch(stat ? h->exec_s[0] : h->exec[0], h->stream)) != hipSuccess) return e;
   if ((e = hipEventRecord(h->temporal_done, h->stream)) != hipSuccess) return e;
   if ((e = launch_user(h, h->temporal_done)) != hipSuccess) return e;
@@ -792,6 +941,7 @@ hipError_t launch_tick(pp_handle* h, bool stat = false) {
   if ((e = hipGraphLaunch(stat ? h->exec_s[1 + ds] : h->exec[1 + ds], h->stream)) != hipSuccess) return e;
   if ((e = hipEventRecord(h->agent_done, h->stream)) != hipSuccess) return e;
   h->user_pending = true;
+  h->pending_fused = false;
   h->parity = 1 - ds;
   return hipSuccess;
 }
@@ -803,6 +953,24 @@ hipError_t flush_user(pp_handle* h, hipStream_t s) {
   for (int i = 0; i < 2; ++i)
     if ((e = hipStreamWaitEvent(s, h->user_done[i], 0)) != hipSuccess) return e;
   return hipSuccess;
+}
+
+// A fused depformer loop left an error code in the tick output: the
+// handle is poisoned (the tick's outputs are not valid).
+int loop_error(pp_handle* h, int code) {
+  return h->fail(PP_EDEVICE, "fused depformer loop: %s (code %d)",
+                 code == DL_ERR_PLACEMENT ? "a workgroup ran on an unexpected XCD"
+                                          : "a wait for another workgroup's results gave up",
+                 code);
+}
+
+// After device work that may include a fused user half outside pp_step:
+// read the error word.
+int check_loop_error(pp_handle* h) {
+  if (!h->lay.dl_ok) return PP_OK;
+  int32_t code = 0;
+  HIP_OR_FAIL(h, hipMemcpy(&code, h->at<int>(h->lay.to) + TO_ERR, 4, hipMemcpyDeviceToHost));
+  return code ? loop_error(h, code) : PP_OK;
 }
 
 }  // namespace
@@ -881,11 +1049,17 @@ int pp_create(const pp_dims* dims, int B, int window, const pp_weights* w, void*
 
   if ((e = hipMemsetAsync(h->at<char>(lay.att_cnt), 0, (size_t)B * dims->n_heads * 4, h->stream)) != hipSuccess)
     return bail("hipMemsetAsync", e);
+  if ((e = hipMemsetAsync(h->at<char>(lay.to), 0, (size_t)B * TO_STRIDE * 4, h->stream)) != hipSuccess)
+    return bail("hipMemsetAsync", e);
+  // the fused loop's memory starts at zero: no word carries a launch tag yet
+  if (lay.dl_ok && (e = hipMemsetAsync(h->at<char>(lay.dl_x), 0, lay.total - lay.dl_x, h->stream)) != hipSuccess)
+    return bail("hipMemsetAsync", e);
   if ((e = hipMemcpyAsync(h->at<char>(lay.samp), &h->samp, sizeof(SampleParams), hipMemcpyHostToDevice, h->stream)) !=
       hipSuccess)
     return bail("hipMemcpyAsync", e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
   finish_prepare();
+  dep_loop_prepare();
   {
     void* sp = nullptr;
     if ((e = static_scratch(&sp)) != hipSuccess) return bail("hipGetSymbolAddress (static work buffers)", e);
@@ -991,10 +1165,35 @@ int pp_set_sampling(pp_handle* h, const pp_sampling* sp) {
   HIP_OR_FAIL(h, hipStreamSynchronize(h->side));
   HIP_OR_FAIL(h, hipMemcpyAsync(h->at<char>(h->lay.samp), &p, sizeof p, hipMemcpyHostToDevice, h->stream));
   HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  if (const int rc = check_loop_error(h)) return rc;
   const bool recapture = p.enabled != h->samp.enabled;  // greedy ticks fold the finishers into the QKV launches
   h->samp = p;
   if (recapture) HIP_OR_FAIL(h, capture_graphs(h));
   return PP_OK;
+}
+
+int pp_set_depformer_loop(pp_handle* h, int on) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (on != 0 && on != 1) return h->fail(PP_EINVAL, "on must be 0 or 1");
+  const char* why = "more than 2 slots";
+  if (on && !h->lay.dl_ok && (h->B > 2 || !dep_loop_supported(h->dm.dep_d, h->dm.dep_heads, h->dm.dep_ffn,
+                                                                h->dm.audio_card, &why)))
+    return h->fail(PP_EINVAL, "the fused depformer loop does not apply to this handle: %s", why);
+  // the pending user half completes in its own way before the graphs change
+  HIP_OR_FAIL(h, launch_user(h, nullptr));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->side));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  if (const int rc = check_loop_error(h)) return rc;
+  h->dl_on = on != 0;
+  HIP_OR_FAIL(h, capture_graphs(h));
+  return PP_OK;
+}
+
+int pp_depformer_loop_active(const pp_handle* h) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  return h->fused ? 1 : 0;
 }
 
 int pp_slot_seed(pp_handle* h, int slot, uint64_t seed) {
@@ -1068,8 +1267,10 @@ int step_impl(pp_handle* h, const int32_t* user_codes, int32_t* tokens, bool sta
   HIP_OR_FAIL(h, hipMemcpy2DAsync(h->to_host + TO_PRED, TO_STRIDE * 4, h->at<int>(h->lay.to) + TO_PRED, TO_STRIDE * 4,
                                   9 * 4, h->B, hipMemcpyDeviceToHost, h->stream));
   HIP_OR_FAIL(h, hipMemcpy2DAsync(h->to_host + TO_CHOSEN, TO_STRIDE * 4, h->at<int>(h->lay.to) + TO_CHOSEN,
-                                  TO_STRIDE * 4, 9 * 4, h->B, hipMemcpyDeviceToHost, h->stream));
+                                  TO_STRIDE * 4, (TO_ERR + 1 - TO_CHOSEN) * 4, h->B, hipMemcpyDeviceToHost,
+                                  h->stream));
   HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  if (h->to_host[TO_ERR] != 0) return loop_error(h, h->to_host[TO_ERR]);
   for (int b = 0; b < h->B; ++b) {
     Slot& s = h->slots[b];
     const int32_t* o = h->to_host + b * TO_STRIDE;
@@ -1143,6 +1344,7 @@ int pp_taps(const pp_handle* h, pp_taps_t* out) {
     hm->poisoned = true;
     return PP_EDEVICE;
   }
+  if (const int rc = check_loop_error(hm)) return rc;
   out->hidden = h->at<float>(h->lay.hidden);
   out->text_logits = h->at<float>(h->lay.text_logits);
   out->dep_logits = h->at<float>(h->lay.dep_logits);
@@ -1185,6 +1387,7 @@ int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* by
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   HIP_OR_FAIL(h, hipGetLastError());
+  if (const int rc = check_loop_error(h)) return rc;
   *avg_ms = ms / (iters * (float)fns.size());
   return PP_OK;
 }
@@ -1211,6 +1414,7 @@ int pp_time_graph(pp_handle* h, int iters, float* avg_ms) {
   HIP_OR_FAIL(h, hipEventElapsedTime(&ms, e0, e1));
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
+  if (const int rc = check_loop_error(h)) return rc;
   *avg_ms = ms / iters;
   return PP_OK;
 }
@@ -1238,6 +1442,10 @@ void pp_destroy(pp_handle* h) {
   for (int g = 0; g < 3; ++g) {
     if (h->exec_s[g]) (void)hipGraphExecDestroy(h->exec_s[g]);
     if (h->graph_s[g]) (void)hipGraphDestroy(h->graph_s[g]);
+  }
+  for (int g = 0; g < 6; ++g) {
+    if (h->exec_f[g]) (void)hipGraphExecDestroy(h->exec_f[g]);
+    if (h->graph_f[g]) (void)hipGraphDestroy(h->graph_f[g]);
   }
   for (hipEvent_t ev : {h->temporal_done, h->agent_done, h->user_done[0], h->user_done[1]})
     if (ev) (void)hipEventDestroy(ev);

@@ -23,6 +23,7 @@ enum {
   TO_PRED = 0,       // 9: text, agent 0..7 predictions
   TO_USER = 9,       // 8: depformer steps 8..15 predictions
   TO_CHOSEN = 17,    // 9: chosen text, agent 0..7
+  TO_ERR = 26,       // slot 0's row: a fused depformer loop's error code (DL_ERR_*), else 0
   TO_STRIDE = 32
 };
 
@@ -45,6 +46,7 @@ struct DepAttnArgs {
   long slot_stride, v_off;
   int n_heads, head_dim, window, n_keys, B;
   bf16_t* o; int ldo; long o_lo;    // [B][ldo] output as a bf16 hi/lo pair (standalone kernel)
+  const int* n_keys_b;              // per-slot key counts [B] in place of n_keys, or null
 };
 void launch_dep_attention(const DepAttnArgs& a, hipStream_t s);
 
@@ -188,6 +190,97 @@ void launch_embed(const EmbedArgs& a, hipStream_t s);
 
 void launch_finish(const FinishArgs& a, hipStream_t s);
 void finish_prepare();  // once per process, before the first finisher launch
+
+// ---------------------------------------------------------------------------
+// Fused depformer loop (dep_loop.hip): one persistent launch runs the 8
+// codebook steps of one or two depformer halves for a few columns, with the
+// tick's GEMM arithmetic (the 8 k-ranges of the contract map onto the 8
+// XCDs).  A column is one slot of one half: the agent half (codebooks 0..7 of
+// this tick) or the user half (codebooks 8..15 of the previous tick).
+// ---------------------------------------------------------------------------
+constexpr int DL_MAX_COLS = 4;   // MFMA columns in use: up to 2 slots x 2 halves
+constexpr int DL_XCDS = 8;       // XCDs of the part (= ranges of the GEMM contract)
+constexpr int DL_GRID = 256;     // workgroups: one per compute unit, DL_GRID / DL_XCDS per XCD
+constexpr int DL_MAX_DD = 1024;  // depformer width held in LDS per column
+constexpr int DL_MAX_KW = 12;    // k-steps a wave holds for one job (down-projection range)
+
+// Error codes the loop leaves in its control block (ctl[2]).
+enum { DL_OK = 0, DL_ERR_PLACEMENT = 1, DL_ERR_TIMEOUT = 2 };
+
+struct DepLoopCol {
+  int slot;              // slot of the tick input / output blocks and taps
+  int k0;                // first codebook: 0 (agent half) or n_q (user half)
+  int set;               // depformer buffer set: input projections, first input, key/value cache
+};
+
+struct DepLoopArgs {
+  int ncols;
+  DepLoopCol col[DL_MAX_COLS];
+  // per buffer set: input projections of z [B][dep_q][dd]; the user half's
+  // first input y = u_8 + table_8[chosen codebook 7] [B][dd] (written by the
+  // agent half's last step, read by the user half)
+  const float* u[2];
+  float* y[2];
+  float* logits;         // depformer logits [B][dep_q][A] (taps)
+  int dd, dH, dhd, dF, Ld, A, dep_q, n_q;
+  float eps;
+  // weights (tile layout for matrices)
+  const bf16_t *wqkv, *wo, *w_in, *w_out, *heads;  // stacked per layer / per codebook
+  const bf16_t *emb_text, *emb_audio;              // input tables: text [Vt+1][dd]; audio [dep_q-1][A+1][dd]
+  const float *attn_norm, *mlp_norm, *out_norm;
+  // tick I/O: the text head's per-tile argmax partials (agent columns' first
+  // choice), the tick input (forced choices) and output blocks
+  const float* tamax_v; const int* tamax_i; int ld_amax; int n_tpart;
+  const int* ti; int* to;
+  // exchange memory (tagged 8-byte words), laid out by dep_loop_layout
+  uint64_t* xq;          // per (step, layer): queries [C][dd]
+  uint64_t* xo;          // per (step, layer): out-projection partials [8][C][dd] + done words [8][32]
+  uint64_t* xm;          // per (step, layer): gate/up outputs [C][dF]
+  uint64_t* xd;          // per (step, layer): down-projection partials [8][C][dd] + done words [8][32]
+  uint64_t* xh;          // per step: head tile argmax [2][A/16][C][2]
+  uint64_t* kv;          // per set and slot: key/value cache [Ld][2][dH][16][dhd/2], tagged pairs
+  uint32_t* kvtag;       // [set * PP_MAX_BATCH + slot]: the launch tag of the agent half's cache entries
+  long kv_slot_words, kv_set_words;
+  uint32_t* ctl;         // [0] last launch tag, [1] exit count, [2] error, [4..11] per-XCD arrival counts
+  long spin_limit;       // polls before a wait gives up (DL_ERR_TIMEOUT)
+};
+
+// Words of exchange memory for C columns (xq, xo, xm, xd, xh in that order):
+// per (step, layer) queries [C][dd], out-projection partials [8][C][dd] and 64
+// done words, gate/up outputs [C][dF], down-projection partials [8][C][dd]
+// and 64 done words; per step the head tiles' (max, argmax) [2][A/16][C][2].
+struct DepLoopLayout { long q, o, m, d, h, total; };
+inline DepLoopLayout dep_loop_layout(int dd, int dF, int Ld, int A, int C) {
+  DepLoopLayout l{};
+  const long sl = 8L * Ld;
+  l.q = 0;
+  l.o = l.q + sl * C * dd;
+  l.m = l.o + sl * (8L * C * dd + 64);
+  l.d = l.m + sl * (long)C * dF;
+  l.h = l.d + sl * (8L * C * dd + 64);
+  l.total = l.h + 8L * 2 * (A / 16) * C * 2;
+  return l;
+}
+// Words of the tagged key/value cache of one slot of one buffer set.
+inline long dep_loop_kv_words(int dd, int Ld) { return (long)Ld * 2 * 16 * dd / 2; }
+// Whether the loop supports these depformer dims: dd <= DL_MAX_DD, dd and dF
+// multiples of 256, heads aligned with the 8 k-ranges, one job per
+// workgroup per phase, every head tile a workgroup.  *why: the reason when not.
+inline bool dep_loop_supported(int dd, int dH, int dF, int A, const char** why) {
+  auto no = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (dd > DL_MAX_DD || dd % 256 || dF % 256) return no("depformer width above 1024, or width or FFN not a multiple of 256");
+  if (dH % DL_XCDS || (dd / DL_XCDS) % (dd / dH)) return no("depformer heads do not split evenly over the 8 k-ranges");
+  if (2 * (dd / 256) > DL_MAX_KW || dF / 256 > DL_MAX_KW) return no("a k-range too long for one wave's registers");
+  const int per = DL_GRID / DL_XCDS;
+  if (3 * dd / 128 > per || dF / 128 > per || dd / 128 > per) return no("more than one job per workgroup in a phase");
+  if (A % 16 || 2 * (A / 16) > DL_GRID) return no("more head tiles than workgroups");
+  return true;
+}
+void launch_dep_loop(const DepLoopArgs& a, hipStream_t s);
+void dep_loop_prepare();  // once per process, before the first launch
 
 // The library's own work-buffer array for the allocation-free entry point
 // (pp_step_static): STATIC_SCRATCH_BYTES of device memory per GPU, held until

@@ -23,8 +23,8 @@ TO_STRIDE = 32
 EXPORTS = ("pp_arena_bytes", "pp_create", "pp_prefill_forced", "pp_prefill_embed", "pp_step", "pp_step_static",
            "pp_set_acoustic_delay", "pp_agent_frames", "pp_set_sampling", "pp_slot_seed", "pp_slot_reset",
            "pp_ring_fill", "pp_taps",
-           "pp_time_kernel", "pp_time_graph", "pp_destroy", "pp_last_error", "pp_packed_elems",
-           "pp_pack_matrix")
+           "pp_time_kernel", "pp_time_graph", "pp_set_depformer_loop", "pp_depformer_loop_active", "pp_destroy",
+           "pp_last_error", "pp_packed_elems", "pp_pack_matrix")
 
 KERNELS = {"qkv": 0, "attention": 1, "out_proj": 2, "gate_up": 3, "down": 4, "text_head": 5}
 
@@ -90,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pp_taps.argtypes = [P, ctypes.POINTER(PPTaps)]
     lib.pp_time_kernel.argtypes = [P, I, I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
     lib.pp_time_graph.argtypes = [P, I, ctypes.POINTER(ctypes.c_float)]
+    lib.pp_set_depformer_loop.argtypes = [P, I]
+    lib.pp_depformer_loop_active.argtypes = [P]
     lib.pp_destroy.argtypes = [P]
     lib.pp_destroy.restype = None
     lib.pp_last_error.argtypes = [P]
@@ -220,6 +222,17 @@ def pp_time_graph(h: int, iters: int) -> float:
     ms = ctypes.c_float()
     _check(load_library().pp_time_graph(h, iters, ctypes.byref(ms)), h)
     return ms.value
+
+
+def pp_set_depformer_loop(h: int, on: bool) -> None:
+    _check(load_library().pp_set_depformer_loop(h, 1 if on else 0), h)
+
+
+def pp_depformer_loop_active(h: int) -> bool:
+    rc = load_library().pp_depformer_loop_active(h)
+    if rc < 0:
+        _check(rc, h)
+    return rc == 1
 
 
 def pp_packed_elems(M: int, K: int) -> int:
@@ -355,6 +368,12 @@ class Engine:
 
     def time_graph(self, iters=10):
         return pp_time_graph(self.h, iters)
+
+    def set_depformer_loop(self, on: bool):
+        pp_set_depformer_loop(self.h, on)
+
+    def depformer_loop_active(self) -> bool:
+        return pp_depformer_loop_active(self.h)
 
     def taps(self) -> dict:
         """Host copies of the last tick's taps."""

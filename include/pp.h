@@ -291,6 +291,20 @@ int pp_time_kernel(pp_handle* h, int which, int iters, float* avg_ms, double* by
  * any slot, so they leave slot state (positions, columns, queues) as is. */
 int pp_time_graph(pp_handle* h, int iters, float* avg_ms);
 
+/* Measurement hook: the depformer as one fused persistent launch per tick
+ * (on = 1) or as per-layer kernel launches (on = 0, the default: the faster
+ * of the two on MI355X at the 7B shape); both compute the same bits.  The fused loop applies to handles
+ * of at most 2 slots with greedy choices and depformer dims it supports
+ * (width <= 1024 and a multiple of 256, FFN a multiple of 256, heads
+ * splitting evenly over 8 ranges); with sampling on, the per-layer launches
+ * run.  PP_EINVAL for on = 1 where it cannot apply.  Waits for the device
+ * work in flight and re-captures the tick's graphs. */
+int pp_set_depformer_loop(pp_handle* h, int on);
+
+/* 1 if the handle's ticks run the fused depformer loop, 0 if not (or a
+ * negative PP_E* code). */
+int pp_depformer_loop_active(const pp_handle* h);
+
 /* Waits for the handle's device work, then frees its host resources. */
 void pp_destroy(pp_handle* h);
 

@@ -39,6 +39,10 @@ hipError_t hipHostMalloc(void** p, size_t n, unsigned) {
   return *p ? hipSuccess : hipErrorLaunchFailure;
 }
 hipError_t hipHostFree(void* p) { std::free(p); return hipSuccess; }
+hipError_t hipMemcpy(void* dst, const void* src, size_t n, hipMemcpyKind) {
+  std::memmove(dst, src, n);
+  return hipSuccess;
+}
 hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind, hipStream_t) {
   std::memmove(dst, src, n);
   return hipSuccess;
@@ -119,6 +123,38 @@ void launch_attention(const AttnArgs&, hipStream_t) {}
 void launch_dep_attention(const DepAttnArgs&, hipStream_t) {}
 void launch_finish(const FinishArgs& a, hipStream_t s) { submit(s, [a] { emulate_finish(a); }); }
 void finish_prepare() {}
+// The fused loop: per column, the agent half's text and 8 codebook choices
+// (k0 = 0) or the user half's 8 predictions (k0 = n_q), with the made-up
+// prediction above; or, when armed, an error code in slot 0's error word.
+static int g_loop_text_card = 1, g_loop_error = 0;
+static long g_loop_launches = 0;
+void launch_dep_loop(const DepLoopArgs& a, hipStream_t s) {
+  submit(s, [a] {
+    ++g_loop_launches;
+    if (g_loop_error) {
+      a.to[TO_ERR] = g_loop_error;
+      g_loop_error = 0;
+      return;
+    }
+    for (int c = 0; c < a.ncols; ++c) {
+      const int b = a.col[c].slot;
+      const int pos = a.ti[b * TI_STRIDE + TI_POS];
+      int* to = a.to + b * TO_STRIDE;
+      for (int k = a.col[c].k0 == 0 ? -1 : a.n_q; k < (a.col[c].k0 == 0 ? a.n_q : 2 * a.n_q); ++k) {
+        const int n = k < 0 ? g_loop_text_card : a.A;
+        const int pred = (int)((7L * pos + 13L * (k + 1) + 5) % n);
+        if (k < a.n_q) {
+          const int forced = a.ti[b * TI_STRIDE + TI_FORCE + 1 + k];
+          to[TO_PRED + 1 + k] = pred;
+          to[TO_CHOSEN + 1 + k] = forced >= 0 ? forced : pred;
+        } else {
+          to[TO_USER + k - a.n_q] = pred;
+        }
+      }
+    }
+  });
+}
+void dep_loop_prepare() {}
 hipError_t static_scratch(void** out) {
   static std::vector<char> buf(STATIC_SCRATCH_BYTES);
   *out = buf.data();
@@ -141,4 +177,9 @@ int stub_last_tick_input(int32_t* out, int n) {
 long stub_ticks_run() { return g_ticks; }
 // Make the next n graph launches fail (a device error).
 void stub_fail_launches(int n) { g_fail_launches = n; }
+// The fused loop's text vocabulary (its launches do not carry it).
+void stub_loop_text_card(int n) { pp::g_loop_text_card = n; }
+// The next fused loop launch leaves this error code instead of its outputs.
+void stub_loop_error(int code) { pp::g_loop_error = code; }
+long stub_loop_launches() { return pp::g_loop_launches; }
 }

@@ -63,9 +63,9 @@ def lib(tmp_path_factory):
 class Handle:
     """A handle of the stub build with a host arena and dummy weight pointers."""
 
-    def __init__(self, L, nB=B, window=W):
+    def __init__(self, L, nB=B, window=W, dm=DM):
         self.L, self.B = L, nB
-        self.dims = pp.make_dims(DM)
+        self.dims = pp.make_dims(dm)
         n = ctypes.c_size_t()
         assert L.pp_arena_bytes(ctypes.byref(self.dims), nB, window, ctypes.byref(n)) == 0
         self.buf = np.zeros(n.value + 256, np.uint8)
@@ -345,3 +345,72 @@ def test_step_static_same_state_machine_and_size_limit(lib):
     lib.stub_last_tick_input(out.ctypes.data, out.size)
     assert out[TI_POS] == 0      # the refused call did not advance the slot
     lib.pp_destroy(h.value)
+
+
+def test_fused_loop_toggle_same_state_machine(lib):
+    """pp_set_depformer_loop: off by default; refused with PP_EINVAL and no
+    change where the fused loop cannot apply (3 slots; a depformer width that
+    is not a multiple of 256); where it applies, ticks give the tokens and
+    tick inputs of the per-layer launches, with forced frames, taps between
+    ticks (which launch the pending user half on its own) and the loop turned
+    off and on between ticks; an error code left by a loop launch poisons the
+    handle (PP_EDEVICE)."""
+    import dataclasses
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.pp_set_depformer_loop.argtypes = [P, I]
+    lib.pp_set_depformer_loop.restype = I
+    lib.pp_depformer_loop_active.argtypes = [P]
+    lib.pp_depformer_loop_active.restype = I
+    lib.pp_taps.argtypes = [P, ctypes.POINTER(pp.PPTaps)]
+    lib.pp_taps.restype = I
+    lib.stub_loop_text_card.argtypes = [I]
+    lib.stub_loop_error.argtypes = [I]
+    lib.stub_loop_launches.restype = ctypes.c_long
+    lib.stub_loop_text_card(VT)
+
+    h3 = Handle(lib)
+    assert lib.pp_depformer_loop_active(h3.h) == 0
+    assert lib.pp_set_depformer_loop(h3.h, 1) == pp.PP_EINVAL
+    assert lib.pp_depformer_loop_active(h3.h) == 0
+    assert lib.pp_set_depformer_loop(h3.h, 0) == 0
+    h3.close()
+    h1 = Handle(lib, nB=1)  # depformer width 128
+    assert lib.pp_set_depformer_loop(h1.h, 1) == pp.PP_EINVAL
+    assert b"fused depformer loop" in lib.pp_last_error(h1.h)
+    h1.close()
+
+    small = dataclasses.replace(DM, dep_d=256, dep_heads=8, dep_ffn=768, dep_layers=2)
+    a, b = Handle(lib, nB=2, dm=small), Handle(lib, nB=2, dm=small)
+    assert lib.pp_depformer_loop_active(a.h) == 0
+    assert lib.pp_set_depformer_loop(a.h, 1) == 0
+    assert lib.pp_depformer_loop_active(a.h) == 1
+    rng = np.random.default_rng(3)
+    fr = np.full((2, 17), -1, np.int32)
+    fr[:, 1:9] = rng.integers(0, A, (2, 8))
+    fr[:, 9:] = rng.integers(0, A, (2, 8))
+    fr[1, 0] = 17
+    for h in (a, b):
+        assert h.prefill(1, fr) == 0
+    c = codes(11, 8, 2)
+    n0 = lib.stub_loop_launches()
+    taps = pp.PPTaps()
+    for t in range(7):
+        if t == 3:
+            assert lib.pp_set_depformer_loop(a.h, 0) == 0
+            assert lib.pp_depformer_loop_active(a.h) == 0
+        if t == 5:
+            assert lib.pp_set_depformer_loop(a.h, 1) == 0
+        ra, ta = a.step(c[t])
+        rb, tb = b.step(c[t])
+        assert ra == 0 and rb == 0
+        np.testing.assert_array_equal(ta, tb, err_msg=f"tick {t}")
+        np.testing.assert_array_equal(a.ti(), b.ti(), err_msg=f"tick {t}")
+        if t in (1, 5):
+            assert lib.pp_taps(a.h, ctypes.byref(taps)) == 0
+    assert lib.stub_loop_launches() - n0 >= 5
+    lib.stub_loop_error(2)
+    assert a.step(c[7])[0] == pp.PP_EDEVICE
+    assert b"fused depformer loop" in lib.pp_last_error(a.h)
+    assert a.step(c[7])[0] == pp.PP_EDEVICE
+    a.close()
+    b.close()
