@@ -29,23 +29,35 @@ PEAK_HBM_GBS = 8000.0
 COPY_PROBE_BYTES = 256 << 20   # a plain device copy of known size, for counter calibration
 
 
+KERNEL_SOURCES = ("kernels.hip", "kernels.h", "device.h")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the sources the timed kernels are built from."""
     import hashlib
-    src = os.path.join(ROOT, "full_duplex_speech_moshi_amd", "csrc", "kernels.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        path = os.path.join(ROOT, "full_duplex_speech_moshi_amd", "csrc", name)
+        if os.path.exists(path):
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(algorithmic_bytes):
-    """HBM bytes per launch of the dominant kernel from profiles/traffic.json
+def traffic_file(kernel: str, config: str, B: int) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{config}_b{B}.json")
+
+
+def measured_traffic(kernel, config, B, algorithmic_bytes):
+    """HBM bytes per launch of a timed kernel from its counter summary
     (rocprofv3 FETCH_SIZE / WRITE_SIZE runs, calibrated on the copy probe),
-    or None when the kernels changed since the counters were taken or the
-    kernel timed here is another shape than the one measured."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    or None when there is none for this kernel and workload, the kernels
+    changed since the counters were taken, or the launch timed here has
+    other algorithmic bytes than the one measured."""
     try:
-        t = json.load(open(path))
+        t = json.load(open(traffic_file(kernel, config, B)))
     except (OSError, ValueError):
         return None
-    if t.get("kernels_hip_sha256_16") != kernel_source_hash():
+    if t.get("kernel_sources_sha256_16") != kernel_source_hash():
         return None
     if abs(t.get("algorithmic_bytes_per_launch", 0) - algorithmic_bytes) > 1e-3 * algorithmic_bytes:
         return None
@@ -72,48 +84,71 @@ def dominant_kernel(kern: dict, n_layers: int) -> str:
     return max(per_tick, key=per_tick.get)
 
 
-DOMINANT_KERNEL = "gemm_kernel<2, 1, true, 0>"  # temporal gate/up below the large-batch path, weights read once per tick
-DOMINANT_WGS = 704                             # its workgroups at the 7B shape (one per gate/up row-tile pair)
+def traffic_parts(kernel: str, B: int):
+    """The dispatches that make up one launch of a timed kernel at the 7B
+    shape: (kernel-name substring, workgroups or None for any).  The temporal
+    gate/up runs as one small-batch launch below B = 14 (704 workgroups, one
+    per gate/up row-tile pair) and as main loop plus ordered reduce from
+    B = 14 on (one 16-column tile up to B = 16, two above)."""
+    if kernel == "gate_up":
+        if B < 14:
+            return [["gemm_kernel<2, 1, true, 0>", 704]]
+        c = 1 if B <= 16 else 2
+        return [[f"gemm_wide_res_kernel<2, {c}>", None], [f"gemm_wide_reduce<2, {c}>", None]]
+    if kernel == "attention":
+        return [["attn_kernel<128>", None]]
+    raise ValueError(f"no counter recipe for {kernel}")
 
 
 def summarize_traffic(run_dir):
-    """Write profiles/traffic.json from two rocprofv3 counter runs of
-    `bench.py --mode traffic` kept under run_dir: pmc_fetch/ (FETCH_SIZE) and
-    pmc_write/ (WRITE_SIZE), each with its *_counter_collection.csv, and
-    traffic_mode.json (the JSON line that mode printed).  The counters are
-    scaled by what they read for the copy probe (COPY_PROBE_BYTES read and
-    written); the dominant kernel's dispatches are averaged."""
+    """Write profiles/traffic_<kernel>_<config>_b<B>.json from two rocprofv3
+    counter runs of `bench.py --mode traffic` kept under run_dir: pmc_fetch/
+    (FETCH_SIZE) and pmc_write/ (WRITE_SIZE), each with its
+    *_counter_collection.csv, and traffic_mode.json (the JSON line that mode
+    printed).  The counters are scaled by what they read for the copy probe
+    (COPY_PROBE_BYTES read and written).  Each part of the launch (main loop,
+    reduce) is averaged over its dispatches, and the parts are added."""
     import csv
     import glob
     meta = json.load(open(os.path.join(run_dir, "traffic_mode.json")))
+    parts = meta["parts"]
 
     def counter(sub, name):
         path = glob.glob(os.path.join(run_dir, sub, "*counter_collection.csv"))[0]
-        copy, kern = [], []
+        copy, per = [], [[] for _ in parts]
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != name:
                 continue
             v = float(r["Counter_Value"])
             if "copyBuffer" in r["Kernel_Name"]:
                 copy.append(v)
-            elif DOMINANT_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == DOMINANT_WGS * int(r["Workgroup_Size"]):
-                kern.append(v)
-        return max(copy), sum(kern) / len(kern), len(kern)
+                continue
+            for i, (sub_name, wgs) in enumerate(parts):
+                if sub_name in r["Kernel_Name"] and (wgs is None or
+                                                     int(r["Grid_Size"]) == wgs * int(r["Workgroup_Size"])):
+                    per[i].append(v)
+        if not all(per):
+            raise SystemExit(f"{sub}: no dispatches of " + ", ".join(p[0] for p, d in zip(parts, per) if not d))
+        return max(copy), [sum(d) / len(d) for d in per], [len(d) for d in per]
 
     f_copy, f_kern, n = counter("pmc_fetch", "FETCH_SIZE")
     w_copy, w_kern, _ = counter("pmc_write", "WRITE_SIZE")
     kib = meta["copy_probe_bytes"] / 1024
     f_scale, w_scale = kib / f_copy, kib / w_copy
+    by = 1024 * (sum(f_kern) * f_scale + sum(w_kern) * w_scale)
     out = {
-        "kernel": f"{DOMINANT_KERNEL} temporal gate/up, 7B, B=1 ({DOMINANT_WGS} workgroups)",
-        "kernels_hip_sha256_16": kernel_source_hash(),
-        "bytes_per_launch": round(1024 * (f_kern * f_scale + w_kern * w_scale)),
-        "fetch_kib_raw": f_kern, "write_kib_raw": w_kern, "dispatches": n,
+        "kernel": meta["kernel"], "config": meta["config"], "B": meta["B"],
+        "parts": [{"name": p[0], "workgroups": p[1], "dispatches": c, "fetch_kib_raw": f, "write_kib_raw": w,
+                   "bytes": round(1024 * (f * f_scale + w * w_scale))}
+                  for p, c, f, w in zip(parts, n, f_kern, w_kern)],
+        "kernel_sources_sha256_16": kernel_source_hash(),
+        "bytes_per_launch": round(by),
         "fetch_scale": f_scale, "write_scale": w_scale,
         "copy_probe_bytes": meta["copy_probe_bytes"],
         "algorithmic_bytes_per_launch": meta["algorithmic_bytes_per_launch"],
+        "traffic_over_algorithmic": by / meta["algorithmic_bytes_per_launch"],
     }
-    json.dump(out, open(os.path.join(ROOT, "profiles", "traffic.json"), "w"), indent=1)
+    json.dump(out, open(traffic_file(meta["kernel"], meta["config"], meta["B"]), "w"), indent=1)
     print(json.dumps(out))
 
 
@@ -290,10 +325,12 @@ def main():
                     help="sample the token choices (text temperature 0.7, audio temperature 0.3, top-p 0.9, "
                          "repetition penalty 1.2) instead of greedy")
     ap.add_argument("--mode", default="bench", choices=["bench", "traffic"],
-                    help="traffic: one tick, then the dominant kernel once per layer outside the graph and the "
+                    help="traffic: one tick, then --traffic-kernel once per layer outside the graph and the "
                          "copy probe, nothing else (for rocprofv3 --pmc runs)")
+    ap.add_argument("--traffic-kernel", default="gate_up", choices=["gate_up", "attention"])
     ap.add_argument("--summarize-traffic", metavar="RUN_DIR", default=None,
-                    help="no GPU: write profiles/traffic.json from the counter runs of --mode traffic under RUN_DIR")
+                    help="no GPU: write profiles/traffic_<kernel>_<config>_b<B>.json from the counter runs of "
+                         "--mode traffic under RUN_DIR")
     ap.add_argument("--no-sub", action="store_true",
                     help="default workload only: skip the B=32 elastic sub-record (C4, timed in a child process)")
     ap.add_argument("--sub-steps", type=int, default=100, help="timed ticks of the C4 sub-record")
@@ -348,15 +385,16 @@ def main():
     log(f"slots opened in {time.time() - t0:.1f} s")
     if args.mode == "traffic":
         eng.step(np.stack([wl.codes[b][0] for b in range(B)]))
-        ms, by = eng.time_kernel("gate_up", 1)
+        ms, by = eng.time_kernel(args.traffic_kernel, 1)
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
         torch.empty_like(src).copy_(src)
         torch.cuda.synchronize()
         eng.close()
-        log(f"traffic mode: gate_up {ms * 1e3:.1f} us per launch, {by / 1e6:.1f} MB algorithmic; copy probe "
-            f"{COPY_PROBE_BYTES} B")
-        print(json.dumps({"mode": "traffic", "algorithmic_bytes_per_launch": by,
-                          "copy_probe_bytes": COPY_PROBE_BYTES}))
+        log(f"traffic mode: {args.traffic_kernel} {ms * 1e3:.1f} us per launch, {by / 1e6:.1f} MB algorithmic; "
+            f"copy probe {COPY_PROBE_BYTES} B")
+        print(json.dumps({"mode": "traffic", "kernel": args.traffic_kernel, "config": args.config, "B": B,
+                          "parts": traffic_parts(args.traffic_kernel, B), "us_per_launch": ms * 1e3,
+                          "algorithmic_bytes_per_launch": by, "copy_probe_bytes": COPY_PROBE_BYTES}))
         return
     pos = list(wl.fill_n)
     for t in range(WU):
@@ -443,7 +481,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": KERNEL_LABELS[dom_name],
                      "achieved": dom["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": dom["gbs"] / PEAK_HBM_GBS,
-                     "traffic": measured_traffic(dom["bytes"]) if dom_name == "gate_up" else None},
+                     "traffic": measured_traffic(dom_name, args.config, B, dom["bytes"])},
         "device_copy_gbs": copy_gbs,
         "kernels_us": {k: round(v["ms"] * 1e3, 2) for k, v in kern.items()},
         "kernels_gbs": {k: round(v["gbs"], 1) for k, v in kern.items()},

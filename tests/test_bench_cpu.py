@@ -51,8 +51,8 @@ def _counter_csv(path, name, rows):
 
 
 def test_traffic_summary_scales_counters_by_the_copy_probe(tmp_path, monkeypatch):
-    # a stand-in repository: the summary hashes kernels.hip and writes
-    # profiles/traffic.json under ROOT
+    # a stand-in repository: the summary hashes the kernel sources and writes
+    # profiles/traffic_<kernel>_<config>_b<B>.json under ROOT
     src = tmp_path / "full_duplex_speech_moshi_amd" / "csrc"
     src.mkdir(parents=True)
     (src / "kernels.hip").write_bytes(b"// kernels\n")
@@ -60,8 +60,9 @@ def test_traffic_summary_scales_counters_by_the_copy_probe(tmp_path, monkeypatch
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     run = tmp_path / "run"
     copy_kib = bench.COPY_PROBE_BYTES / 1024
-    dom = f"void pp::{bench.DOMINANT_KERNEL}(pp::GemmArgs)"
-    grid = bench.DOMINANT_WGS * 512
+    (name, wgs), = bench.traffic_parts("gate_up", 1)
+    dom = f"void pp::{name}(pp::GemmArgs)"
+    grid = wgs * 512
     # FETCH_SIZE reads half the copy probe's bytes (scale 2), WRITE_SIZE all of them
     _counter_csv(str(run / "pmc_fetch" / "c1_counter_collection.csv"), "FETCH_SIZE",
                  [("__amd_rocclr_copyBuffer", 256 * 512, copy_kib / 2), (dom, grid, 1000.0), (dom, grid, 1002.0),
@@ -69,20 +70,56 @@ def test_traffic_summary_scales_counters_by_the_copy_probe(tmp_path, monkeypatch
     _counter_csv(str(run / "pmc_write" / "c1_counter_collection.csv"), "WRITE_SIZE",
                  [("__amd_rocclr_copyBuffer", 256 * 512, copy_kib), (dom, grid, 4.0), (dom, grid, 4.0)])
     algo = 2_000_000.0
-    (run / "traffic_mode.json").write_text(json.dumps({"copy_probe_bytes": bench.COPY_PROBE_BYTES,
-                                                       "algorithmic_bytes_per_launch": algo}))
+    (run / "traffic_mode.json").write_text(json.dumps({
+        "kernel": "gate_up", "config": "C1", "B": 1, "parts": bench.traffic_parts("gate_up", 1),
+        "copy_probe_bytes": bench.COPY_PROBE_BYTES, "algorithmic_bytes_per_launch": algo}))
     bench.summarize_traffic(str(run))
-    t = json.load(open(tmp_path / "profiles" / "traffic.json"))
-    assert t["dispatches"] == 2  # other kernels and other grid sizes are left out
+    t = json.load(open(tmp_path / "profiles" / "traffic_gate_up_C1_b1.json"))
+    assert t["parts"][0]["dispatches"] == 2  # other kernels and other grid sizes are left out
     assert t["fetch_scale"] == pytest.approx(2.0)
     assert t["write_scale"] == pytest.approx(1.0)
     assert t["bytes_per_launch"] == round(1024 * (1001.0 * 2.0 + 4.0))
-    assert t["kernels_hip_sha256_16"] == hashlib.sha256(b"// kernels\n").hexdigest()[:16]
-    # reported only for the same kernel source and the same launch shape
-    assert bench.measured_traffic(algo) == t["bytes_per_launch"]
-    assert bench.measured_traffic(2 * algo) is None
-    (src / "kernels.hip").write_bytes(b"// kernels, changed\n")
-    assert bench.measured_traffic(algo) is None
+    assert t["kernel_sources_sha256_16"] == hashlib.sha256(b"// kernels\n").hexdigest()[:16]
+    # reported only for the same kernel sources, kernel, workload and launch shape
+    assert bench.measured_traffic("gate_up", "C1", 1, algo) == t["bytes_per_launch"]
+    assert bench.measured_traffic("gate_up", "C1", 1, 2 * algo) is None
+    assert bench.measured_traffic("gate_up", "C4", 32, algo) is None
+    assert bench.measured_traffic("attention", "C1", 1, algo) is None
+    (src / "device.h").write_bytes(b"// helpers\n")
+    assert bench.measured_traffic("gate_up", "C1", 1, algo) is None
+
+
+def test_traffic_summary_adds_main_loop_and_reduce(tmp_path, monkeypatch):
+    # the large-batch gate/up at B = 32: a main loop and an ordered reduce per
+    # launch, each averaged over its own dispatches, then added
+    src = tmp_path / "full_duplex_speech_moshi_amd" / "csrc"
+    src.mkdir(parents=True)
+    (src / "kernels.hip").write_bytes(b"// kernels\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    parts = bench.traffic_parts("gate_up", 32)
+    assert [p[0] for p in parts] == ["gemm_wide_res_kernel<2, 2>", "gemm_wide_reduce<2, 2>"]
+    assert [p[0] for p in bench.traffic_parts("gate_up", 16)] == ["gemm_wide_res_kernel<2, 1>",
+                                                                   "gemm_wide_reduce<2, 1>"]
+    run = tmp_path / "run"
+    copy_kib = bench.COPY_PROBE_BYTES / 1024
+    main, red = "void pp::gemm_wide_res_kernel<2, 2>(pp::WideArgs)", "void pp::gemm_wide_reduce<2, 2>(pp::WideArgs)"
+    _counter_csv(str(run / "pmc_fetch" / "b32_counter_collection.csv"), "FETCH_SIZE",
+                 [("__amd_rocclr_copyBuffer", 256 * 512, copy_kib / 2), (main, 472 * 512, 100.0),
+                  (main, 472 * 512, 110.0), (red, 704 * 512, 20.0)])
+    _counter_csv(str(run / "pmc_write" / "b32_counter_collection.csv"), "WRITE_SIZE",
+                 [("__amd_rocclr_copyBuffer", 256 * 512, copy_kib), (main, 472 * 512, 30.0),
+                  (red, 704 * 512, 6.0), (red, 704 * 512, 8.0)])
+    (run / "traffic_mode.json").write_text(json.dumps({
+        "kernel": "gate_up", "config": "sweep", "B": 32, "parts": parts,
+        "copy_probe_bytes": bench.COPY_PROBE_BYTES, "algorithmic_bytes_per_launch": 500_000.0}))
+    bench.summarize_traffic(str(run))
+    t = json.load(open(tmp_path / "profiles" / "traffic_gate_up_sweep_b32.json"))
+    assert [p["dispatches"] for p in t["parts"]] == [2, 1]
+    assert t["parts"][0]["bytes"] == round(1024 * (105.0 * 2 + 30.0))
+    assert t["parts"][1]["bytes"] == round(1024 * (20.0 * 2 + 7.0))
+    assert t["bytes_per_launch"] == round(1024 * ((105.0 + 20.0) * 2 + 30.0 + 7.0))
+    assert t["traffic_over_algorithmic"] == pytest.approx(t["bytes_per_launch"] / 500_000.0, rel=1e-6)
 
 
 def test_dominant_kernel_is_the_largest_per_tick():
