@@ -123,14 +123,14 @@ struct Glb {
   gu32 *kvtag, *ctl;
 };
 
-// The attention function's arguments, pointing into LDS (the same fields as
-// DepAttnArgs).
+// The attention function's arguments, pointing into LDS (the fields of
+// DepAttnArgs it reads), with each column's own key count.
 struct DepAttnLds {
   const lfloat* q;
   int ldq;
   const lbf16* kv;
   long slot_stride, v_off;
-  int n_heads, head_dim, window, n_keys, B;
+  int n_heads, head_dim, window, B;
   const lint* n_keys_b;
 };
 
@@ -742,13 +742,14 @@ __global__ __launch_bounds__(512) void dep_loop_kernel(DepLoopArgs a) {
           da.n_heads = D.HX;
           da.head_dim = a.dhd;
           da.window = 16;
-          da.n_keys = 0;
           da.B = C;
           da.n_keys_b = L.nk;
           const int ppw = 128 / a.dhd;
           for (int pp0 = wave * ppw; pp0 < C * D.HX; pp0 += 8 * ppw) {
-            const DepAttnOut o = a.dhd == 32 ? dep_attend<32>(da, pp0) : a.dhd == 64 ? dep_attend<64>(da, pp0)
-                                                                                      : dep_attend<128>(da, pp0);
+            DepAttnOut o;
+            [[clang::always_inline]] o = a.dhd == 32 ? dep_attend<32>(da, pp0)
+                                       : a.dhd == 64 ? dep_attend<64>(da, pp0)
+                                                     : dep_attend<128>(da, pp0);
             if (o.ok) {
               const int c = o.pair / D.HX, hh = o.pair - c * D.HX;
               lbf16* op = L.oatt + c * (DL_MAX_DD / 8) + hh * a.dhd + o.feat;

@@ -3,6 +3,7 @@
 // per-slot arithmetic that every path computing the same value goes through
 // (so that a slot's bits do not depend on which kernel produced them).
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -141,10 +142,17 @@ struct DepAttnOut {
   bool ok;
 };
 
+// Argument types with a key count per slot (member n_keys_b) in place of
+// DepAttnArgs' one count for every slot.
+template <class T, class = void>
+struct per_slot_keys : std::false_type {};
+template <class T>
+struct per_slot_keys<T, std::void_t<decltype(T::n_keys_b)>> : std::true_type {};
+
 // Args: DepAttnArgs (global memory), or a structure with the same fields
 // pointing into LDS; the arithmetic is the same either way.
 template <int DH, class Args>
-__device__ __forceinline__ DepAttnOut dep_attend(const Args& d, const int pair0) {
+__device__ DepAttnOut dep_attend(const Args& d, const int pair0) {
   constexpr int LP = DH / 2;  // lanes per pair
   const int lane = threadIdx.x & 63;
   const int pair = pair0 + lane / LP, f = 2 * (lane % LP);
@@ -155,7 +163,9 @@ __device__ __forceinline__ DepAttnOut dep_attend(const Args& d, const int pair0)
   const auto kb = d.kv + (long)b * d.slot_stride + (long)h * d.window * DH + f;
   const auto kw = as_u32(kb);
   const auto vw = as_u32(kb + d.v_off);
-  const int n = d.n_keys_b ? d.n_keys_b[b] : d.n_keys;
+  int n;
+  if constexpr (per_slot_keys<Args>::value) n = d.n_keys_b[b];
+  else n = d.n_keys;
   uint32_t kk[DEP_MAX_KEYS], vv[DEP_MAX_KEYS];
 #pragma unroll
   for (int p = 0; p < DEP_MAX_KEYS; ++p) {

@@ -46,7 +46,6 @@ struct DepAttnArgs {
   long slot_stride, v_off;
   int n_heads, head_dim, window, n_keys, B;
   bf16_t* o; int ldo; long o_lo;    // [B][ldo] output as a bf16 hi/lo pair (standalone kernel)
-  const int* n_keys_b;              // per-slot key counts [B] in place of n_keys, or null
 };
 void launch_dep_attention(const DepAttnArgs& a, hipStream_t s);
 
