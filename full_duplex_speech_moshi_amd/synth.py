@@ -176,6 +176,102 @@ def make_weights(dm: Dims, seed: int = 0, threads: int | None = None) -> dict:
     return out
 
 
+# ---------------------------------------------------------------- codec
+
+@dataclasses.dataclass(frozen=True)
+class CodecDims:
+    """A streaming codec decoder of the SoundStream / EnCodec family with a
+    transformer (the chenxutan.com PersonaPlex article, section 2.3 on Mimi:
+    24 kHz audio <-> 12.5 Hz tokens, 1.1 kbps, causal, transformers in the
+    encoder and decoder; the recipe's "Architecture": 8 codebooks of 2048,
+    1920 samples per 80 ms frame).  Everything else here is this build's
+    choice: the pages give neither the layer structure nor the weights."""
+    n_q: int = 8                  # codebooks per frame (agent rows 1-8)
+    card: int = 2048              # entries per codebook
+    d: int = 512                  # latent width = transformer width
+    n_layers: int = 8
+    n_heads: int = 8
+    ffn: int = 2048
+    window: int = 250             # transformer context, frames (20 s)
+    conv_k: int = 7               # first and last convolutions
+    res_k: int = 3                # first convolution of each residual unit
+    strides: tuple = (2, 8, 6, 5, 4)
+    channels: tuple = (512, 256, 128, 64, 32, 16)   # after the first convolution, then after each stage
+    norm_eps: float = 1e-5
+    rope_base: float = 10000.0
+
+    @property
+    def head_dim(self) -> int:
+        return self.d // self.n_heads
+
+    @property
+    def samples(self) -> int:
+        """Output samples per frame."""
+        return int(np.prod(self.strides))
+
+
+CODEC = CodecDims()
+CODEC_TINY = CodecDims(d=128, n_layers=2, n_heads=2, ffn=256, window=8, strides=(2, 3, 4),
+                       channels=(64, 32, 16, 8))
+
+
+def codec_manifest(cd: CodecDims):
+    """Ordered list of (name, shape, kind, scale).  kind 'bf16': N(0, scale)
+    stored as bf16 bits; 'alpha': RMSNorm scale 1 + N(0, 0.01), fp32; 'bias':
+    N(0, scale), fp32.  Convolution weights are [C_out][C_in][K] for both the
+    causal and the transposed convolutions, drawn with scale 1/sqrt(fan-in)
+    so that activations stay of order one."""
+    d, F = cd.d, cd.ffn
+    m = [(f"codebook.{q}", (cd.card, d), "bf16", 1.0 / np.sqrt(cd.n_q)) for q in range(cd.n_q)]
+    for l in range(cd.n_layers):
+        m += [(f"layers.{l}.attn_norm", (d,), "alpha", 0.0),
+              (f"layers.{l}.wqkv", (3 * d, d), "bf16", 0.02),
+              (f"layers.{l}.wo", (d, d), "bf16", 0.02),
+              (f"layers.{l}.mlp_norm", (d,), "alpha", 0.0),
+              (f"layers.{l}.w_in", (2 * F, d), "bf16", 0.02),
+              (f"layers.{l}.w_out", (d, F), "bf16", 0.02)]
+    m.append(("out_norm", (d,), "alpha", 0.0))
+    c = cd.channels
+    m += [("conv_in.w", (c[0], d, cd.conv_k), "bf16", 1.0 / np.sqrt(d * cd.conv_k)),
+          ("conv_in.b", (c[0],), "bias", 0.01)]
+    for i, st in enumerate(cd.strides):
+        ci, co = c[i], c[i + 1]
+        m += [(f"up.{i}.w", (co, ci, 2 * st), "bf16", 1.0 / np.sqrt(2 * ci)),
+              (f"up.{i}.b", (co,), "bias", 0.01),
+              (f"res.{i}.a.w", (co // 2, co, cd.res_k), "bf16", 1.0 / np.sqrt(co * cd.res_k)),
+              (f"res.{i}.a.b", (co // 2,), "bias", 0.01),
+              (f"res.{i}.b.w", (co, co // 2, 1), "bf16", 0.5 / np.sqrt(co // 2)),
+              (f"res.{i}.b.b", (co,), "bias", 0.01)]
+    m += [("conv_out.w", (1, c[-1], cd.conv_k), "bf16", 1.0 / np.sqrt(c[-1] * cd.conv_k)),
+          ("conv_out.b", (1,), "bias", 0.01)]
+    return m
+
+
+def _make_codec_tensor(seed: int, index: int, shape, kind: str, scale: float) -> np.ndarray:
+    rng = _rng(seed, 100000 + index)
+    if kind == "bf16":
+        return _normal_bf16(rng, shape, scale)
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if kind == "alpha":
+        a *= np.float32(0.01)
+        a += np.float32(1.0)
+    else:
+        a *= np.float32(scale)
+    return a
+
+
+def make_codec_weights(cd: CodecDims, seed: int = 0) -> dict:
+    """All codec weights, name -> array (uint16 bf16 bits or fp32), each from
+    its own child stream."""
+    return {name: _make_codec_tensor(seed, i, shp, kind, scale)
+            for i, (name, shp, kind, scale) in enumerate(codec_manifest(cd))}
+
+
+def agent_frames(seed: int, n_frames: int, card: int = 2048) -> np.ndarray:
+    """i.i.d. uniform agent-audio frames for the codec, int32 [n_frames, 8]."""
+    return _rng(seed).integers(0, card, (n_frames, N_AGENT), dtype=np.int32)
+
+
 # ---------------------------------------------------------------- streams
 
 def user_codes(seed: int, n_ticks: int, card: int = 2048) -> np.ndarray:

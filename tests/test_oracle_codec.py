@@ -1,0 +1,191 @@
+"""Pins of the codec-decoder oracle (oracle/codec.py) to things outside it.
+
+* Its causal and transposed convolutions against PyTorch's CPU routines
+  (conv1d with left padding, conv_transpose1d), fp64.
+* Its streaming state: frame-by-frame decoding equals the whole-sequence
+  definition, which carries no state; a reset slot equals a fresh one.
+* Its transformer against the tick oracle's temporal block (itself pinned in
+  test_oracle_pins.py): the same weights, fed as embedding-form frames, give
+  the same hidden state, over more frames than the window holds.
+* The residual-quantiser sum against one-hot codebooks.
+* The convolutional stack's wiring (ELU placement, upsampling, channel
+  order, residual skip from the pre-activation signal, biases) against a
+  closed form with pass-through weights.
+
+The codec's layer structure is this build's reading of the pages (section
+2.3 of the chenxutan.com article: a SoundStream/EnCodec-family codec with a
+transformer, 12.5 Hz frames, 24 kHz audio); parity with the real Mimi codec
+is unpinned: its weights and exact layers are not available."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from full_duplex_speech_moshi_amd import synth
+from oracle import codec, tick
+
+CD = synth.CODEC_TINY
+
+
+def _bits(x):
+    return synth.to_bf16_bits(np.asarray(x, np.float32))
+
+
+def test_frame_is_1920_samples_at_the_pages_rate():
+    # 24 kHz / 12.5 Hz = 1920 samples per 80 ms frame
+    assert synth.CODEC.samples == 24000 * 80 // 1000 == 1920
+    assert synth.CODEC.n_q == 8 and synth.CODEC.card == 2048
+
+
+@pytest.mark.parametrize("K", [1, 3, 7])
+def test_causal_conv_matches_torch(K):
+    rng = np.random.default_rng(K)
+    ci, co, T = 5, 4, 9
+    x, w, b = rng.normal(size=(ci, T)), rng.normal(size=(co, ci, K)), rng.normal(size=co)
+    y = codec.causal_conv(x, w, b, np.zeros((ci, K - 1)))
+    ref = torch.nn.functional.conv1d(torch.nn.functional.pad(torch.tensor(x)[None], (K - 1, 0)),
+                                     torch.tensor(w), torch.tensor(b))[0].numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # a history is the inputs before x: the same as convolving the concatenation
+    h = rng.normal(size=(ci, K - 1))
+    y2 = codec.causal_conv(x, w, b, h)
+    full = np.concatenate([h, x], axis=1)
+    ref2 = torch.nn.functional.conv1d(torch.nn.functional.pad(torch.tensor(full)[None], (K - 1, 0)),
+                                      torch.tensor(w), torch.tensor(b))[0].numpy()[:, K - 1:]
+    np.testing.assert_allclose(y2, ref2, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("s", [2, 3, 5, 8])
+def test_conv_transpose_matches_torch(s):
+    rng = np.random.default_rng(s)
+    ci, co, T = 4, 3, 6
+    x, w, b = rng.normal(size=(ci, T)), rng.normal(size=(co, ci, 2 * s)), rng.normal(size=co)
+    # torch's weight layout is [C_in][C_out][K]; its output has (T - 1) s + K
+    # samples, of which the causal call keeps the first T s
+    ref = torch.nn.functional.conv_transpose1d(torch.tensor(x)[None], torch.tensor(w.transpose(1, 0, 2)),
+                                               torch.tensor(b), stride=s)[0].numpy()
+    y = codec.conv_transpose_causal(x, w, b, np.zeros((ci, 1)), s)
+    np.testing.assert_allclose(y, ref[:, :T * s], rtol=1e-12, atol=1e-12)
+    # with the previous input given, the outputs are those of the longer
+    # sequence, shifted by one input
+    prev = rng.normal(size=(ci, 1))
+    full = torch.nn.functional.conv_transpose1d(torch.tensor(np.concatenate([prev, x], 1))[None],
+                                                torch.tensor(w.transpose(1, 0, 2)), torch.tensor(b),
+                                                stride=s)[0].numpy()
+    y2 = codec.conv_transpose_causal(x, w, b, prev, s)
+    np.testing.assert_allclose(y2, full[:, s:s + T * s], rtol=1e-12, atol=1e-12)
+
+
+def test_elu_values():
+    x = np.array([-2.0, -1.0, -1e-8, 0.0, 1e-8, 0.5, 3.0])
+    # e^-2 - 1, e^-1 - 1 and e^-1e-8 - 1 to 17 digits
+    np.testing.assert_allclose(codec.elu(x), [-0.8646647167633873, -0.6321205588285577, -9.9999999500000002e-09,
+                                              0.0, 1e-8, 0.5, 3.0], rtol=1e-15, atol=0)
+
+
+def test_streaming_equals_whole_sequence_and_reset_equals_fresh():
+    w = synth.make_codec_weights(CD, seed=3)
+    n = 2 * CD.window + 3  # past the transformer's window
+    codes = synth.agent_frames(11, n)
+    o = codec.CodecOracle(CD, w, 2, np.float64)
+    other = synth.agent_frames(12, 5)
+    pcm = []
+    for t in range(n):
+        c = np.stack([codes[t], other[t % 5]])
+        pcm.append(o.decode(c)[0])
+    ref = codec.decode_sequence(CD, w, codes, np.float64)
+    np.testing.assert_allclose(np.concatenate(pcm), ref, rtol=0, atol=1e-12)
+    # slot 1 reset mid-stream, then fed the sequence: the same samples
+    o.reset(1)
+    got = [o.decode(np.stack([other[0], codes[t]]))[1] for t in range(6)]
+    np.testing.assert_allclose(np.concatenate(got), ref[:6 * CD.samples], rtol=0, atol=1e-12)
+
+
+def test_latent_is_the_codebook_sum_in_order():
+    w = synth.make_codec_weights(CD, seed=0)
+    for q in range(CD.n_q):
+        t = np.zeros((CD.card, CD.d), np.float32)
+        t[np.arange(CD.card), (np.arange(CD.card) + 3 * q) % CD.d] = 2.0 ** -q
+        w[f"codebook.{q}"] = _bits(t)
+    o = codec.CodecOracle(CD, w, 1, np.float64)
+    codes = np.array([5, 900, 17, 17, 2047, 0, 64, 127])
+    x = o.latent(codes)
+    ref = np.zeros(CD.d)
+    for q, c in enumerate(codes):
+        ref[(c + 3 * q) % CD.d] += 2.0 ** -q
+    np.testing.assert_array_equal(x, ref)
+
+
+def test_transformer_is_the_temporal_block():
+    """The codec's layers against the tick oracle's temporal layers with the
+    same weights: embedding-form frames give the tick its input x, and the
+    tick's hidden state after the last layer must equal the codec's, frame by
+    frame, beyond the window (ring wrap)."""
+    cw = synth.make_codec_weights(CD, seed=5)
+    dm = synth.Dims(d=CD.d, n_layers=CD.n_layers, n_heads=CD.n_heads, ffn=CD.ffn, text_card=64,
+                    audio_card=64, n_q=8, dep_d=32, dep_layers=1, dep_heads=1, dep_ffn=32, dep_q=16,
+                    norm_eps=CD.norm_eps, rope_base=CD.rope_base)
+    tw = synth.make_weights(dm, seed=1)
+    for l in range(CD.n_layers):
+        for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "w_in", "w_out"):
+            tw[f"layers.{l}.{k}"] = cw[f"layers.{l}.{k}"]
+    n = CD.window + 4
+    rng = np.random.default_rng(9)
+    xs = rng.normal(size=(n, CD.d))
+    t = tick.Oracle(dm, tw, 1, CD.window, dtype=np.float64)
+    t.prefill_embed(0, xs)
+    o = codec.CodecOracle(CD, cw, 1, np.float64)
+    st = o.slots[0]
+    for i in range(n):
+        t.step(np.zeros((1, 8), np.int64))
+        got = o.blocks(st, xs[i].copy())
+        st.pos += 1
+        np.testing.assert_allclose(got, t.taps["hidden"][-1, 0], rtol=1e-12, atol=1e-12, err_msg=f"frame {i}")
+
+
+def test_conv_stack_closed_form():
+    """Pass-through weights: the first convolution picks z's channel 0 from
+    its current tap, each upsampling holds channel 0 of its ELU'd input for
+    `stride` samples (weights 1 on taps 0..s-1), each residual unit adds only
+    its second bias beta_i (zero weights), the last convolution picks channel
+    0.  Then every sample of frame t is elu(v_n), with v_0 = z_t[0] + b_in
+    and v_{i+1} = elu(v_i) + b_up_i + beta_i."""
+    w = synth.make_codec_weights(CD, seed=2)
+    c = CD.channels
+    rng = np.random.default_rng(4)
+
+    def onehot(co, ci, K, taps):
+        a = np.zeros((co, ci, K), np.float32)
+        for k in taps:
+            a[0, 0, k] = 1.0
+        return _bits(a)
+
+    w["conv_in.w"] = onehot(c[0], CD.d, CD.conv_k, [CD.conv_k - 1])
+    w["conv_in.b"] = np.zeros(c[0], np.float32)
+    w["conv_in.b"][0] = 0.25
+    b_up, beta = [], []
+    for i, s in enumerate(CD.strides):
+        w[f"up.{i}.w"] = onehot(c[i + 1], c[i], 2 * s, range(s))
+        w[f"up.{i}.b"] = np.zeros(c[i + 1], np.float32)
+        b_up.append(float(np.float32(rng.normal() * 0.5)))
+        w[f"up.{i}.b"][0] = b_up[-1]
+        w[f"res.{i}.a.w"] = _bits(rng.normal(size=w[f"res.{i}.a.w"].shape))
+        w[f"res.{i}.b.w"] = _bits(np.zeros(w[f"res.{i}.b.w"].shape))
+        w[f"res.{i}.b.b"] = np.zeros(c[i + 1], np.float32)
+        beta.append(float(np.float32(rng.normal() * 0.5)))
+        w[f"res.{i}.b.b"][0] = beta[-1]
+    w["conv_out.w"] = onehot(1, c[-1], CD.conv_k, [CD.conv_k - 1])
+    w["conv_out.b"] = np.zeros(1, np.float32)
+    o = codec.CodecOracle(CD, w, 1, np.float64)
+    codes = synth.agent_frames(21, 4)
+    for t in range(4):
+        st = o.slots[0]
+        z = o.transformer(st, o.latent(codes[t]))
+        pcm = o.convs(st, z)
+        st.pos += 1
+        v = z[0] + 0.25
+        for i in range(len(CD.strides)):
+            v = (np.expm1(v) if v <= 0 else v) + b_up[i] + beta[i]
+        v = np.expm1(v) if v <= 0 else v
+        np.testing.assert_allclose(pcm, np.full(CD.samples, v), rtol=1e-12, atol=1e-12)
