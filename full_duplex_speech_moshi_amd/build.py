@@ -11,6 +11,7 @@ import os
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -41,11 +42,14 @@ def _run(cmd, verbose):
 def build(verbose: bool = True) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     with tempfile.TemporaryDirectory() as tmp:
-        objs = []
-        for src, flags in (("kernels.hip", HIP_FLAGS), ("dep_loop.hip", HIP_FLAGS), ("engine.cpp", HOST_FLAGS)):
-            obj = os.path.join(tmp, src + ".o")
-            _run([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-            objs.append(obj)
+        units = (("kernels.hip", HIP_FLAGS), ("dep_loop.hip", HIP_FLAGS), ("codec.hip", HIP_FLAGS),
+                 ("engine.cpp", HOST_FLAGS), ("codec.cpp", HOST_FLAGS))
+        objs = [os.path.join(tmp, src + ".o") for src, _ in units]
+        # the compilations are independent: run them side by side
+        with ThreadPoolExecutor(len(units)) as ex:
+            for f in [ex.submit(_run, [hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+                      for (src, flags), obj in zip(units, objs)]:
+                f.result()
         tmp_lib = LIB + ".tmp"
         _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib], verbose)
         os.replace(tmp_lib, LIB)

@@ -1,0 +1,640 @@
+// Host side of the streaming codec decoder (codec.h): validation, the arena
+// layout, the slots' frame positions, and four captured graphs (two for
+// decode calls, two for timing launches).
+//
+// One call decodes one frame per slot (chenxutan.com PersonaPlex article,
+// section 2.3: Mimi turns 12.5 Hz frames of 8 codebooks into 24 kHz audio,
+// causally; recipe "Architecture": 1920 samples per frame).  The graph runs
+// the latent sum, the transformer layers on the tick's GEMM and ring-decode
+// launchers, the output norm, the convolution stack and the state update.
+// The convolutions' histories are double-buffered: a call's graph reads set
+// p and writes set 1 - p, and consecutive calls alternate; timing launches
+// write a third set, which no call reads.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/codec.h"
+#include "codec_kernels.h"
+#include "kernels.h"
+
+namespace pp {
+namespace {
+
+constexpr size_t ALIGN = 256;
+std::string g_codec_create_error;
+
+bool codec_dims_ok(const pp_codec_dims* dm, std::string* why) {
+  auto fail = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (!dm) return fail("dims is NULL");
+  if (dm->n_q < 1 || dm->n_q > 16 || dm->card < 1) return fail("n_q must be 1..16 and card >= 1");
+  if (dm->d <= 0 || dm->d % 32 || dm->n_layers <= 0 || dm->n_heads <= 0 || dm->ffn <= 0 || dm->ffn % 32)
+    return fail("d and ffn must be positive multiples of 32");
+  if (dm->d % dm->n_heads) return fail("d not divisible by n_heads");
+  const int hd = dm->d / dm->n_heads;
+  if (hd != 32 && hd != 64 && hd != 128) return fail("head_dim must be 32, 64 or 128");
+  if (dm->window < 1 || dm->window > PP_CODEC_MAX_WINDOW) return fail("window outside 1..PP_CODEC_MAX_WINDOW");
+  if (dm->conv_k < 1 || dm->res_k < 1) return fail("kernels must be >= 1");
+  if (dm->n_stages < 1 || dm->n_stages > PP_CODEC_MAX_STAGES) return fail("n_stages outside 1..PP_CODEC_MAX_STAGES");
+  long samples = 1;
+  for (int i = 0; i < dm->n_stages; ++i) {
+    if (dm->strides[i] < 1) return fail("strides must be >= 1");
+    samples *= dm->strides[i];
+    if (samples > (1 << 20)) return fail("too many samples per frame");
+  }
+  for (int i = 0; i <= dm->n_stages; ++i)
+    if (dm->channels[i] < 1 || (i > 0 && dm->channels[i] % 2)) return fail("channels must be >= 1, even after stage 0");
+  if (!(dm->norm_eps >= 0.f) || !(dm->rope_base > 0.f)) return fail("bad eps or rope base");
+  return true;
+}
+
+long codec_samples(const pp_codec_dims& dm) {
+  long s = 1;
+  for (int i = 0; i < dm.n_stages; ++i) s *= dm.strides[i];
+  return s;
+}
+
+// History entries: conv_in, then per stage the upsampling and the residual
+// unit's first convolution, then conv_out (entries with H = 0 are left out).
+struct HistSpec {
+  int C, H;
+  size_t off[3];  // per set: two that calls alternate between, one that timing launches write
+};
+
+struct CodecLayout {
+  size_t ti, codes, inv_freq, rope, x, xa, part, q, o, m, ring, att_part, att_cnt, z;
+  size_t h0, pcm;
+  size_t u[PP_CODEC_MAX_STAGES], r[PP_CODEC_MAX_STAGES], hs[PP_CODEC_MAX_STAGES];
+  long T[PP_CODEC_MAX_STAGES + 1];  // samples per call at each rate: T[0] = 1
+  long ring_layer_elems, ring_slot_elems, ring_v_off;
+  std::vector<HistSpec> hist;  // 0: conv_in, then up_i / res_a_i, then conv_out
+  int h_conv_in, h_up[PP_CODEC_MAX_STAGES], h_res[PP_CODEC_MAX_STAGES], h_conv_out;
+  size_t total;
+};
+
+CodecLayout make_codec_layout(const pp_codec_dims& dm, int B) {
+  CodecLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + ALIGN - 1) / ALIGN * ALIGN;
+    return o;
+  };
+  const long d = dm.d, H = dm.n_heads, hd = d / H, F = dm.ffn, W = dm.window;
+  L.ring_layer_elems = 2 * H * W * hd;
+  L.ring_slot_elems = dm.n_layers * L.ring_layer_elems;
+  L.ring_v_off = H * W * hd;
+  L.ti = take((size_t)B * TI_STRIDE * 4);
+  L.codes = take((size_t)B * 16 * 4);
+  L.inv_freq = take((size_t)hd / 2 * 8);
+  L.rope = take((size_t)B * hd * 4);
+  L.x = take((size_t)B * d * 4);
+  L.xa = take((size_t)2 * B * d * 2);
+  L.part = take((size_t)B * (d / 16) * 4);
+  L.q = take((size_t)B * d * 4);
+  L.o = take((size_t)2 * B * d * 2);
+  L.m = take((size_t)2 * B * F * 2);
+  L.ring = take((size_t)B * L.ring_slot_elems * 2);
+  L.att_part = take((size_t)B * H * (hd + 2) * 4);
+  L.att_cnt = take((size_t)B * H * 4);
+  L.z = take((size_t)B * d * 4);
+  L.T[0] = 1;
+  for (int i = 0; i < dm.n_stages; ++i) L.T[i + 1] = L.T[i] * dm.strides[i];
+  L.h0 = take((size_t)B * dm.channels[0] * 4);
+  for (int i = 0; i < dm.n_stages; ++i) {
+    const long co = dm.channels[i + 1], T = L.T[i + 1];
+    L.u[i] = take((size_t)B * co * T * 4);
+    L.r[i] = take((size_t)B * (co / 2) * T * 4);
+    L.hs[i] = take((size_t)B * co * T * 4);
+  }
+  L.pcm = take((size_t)B * L.T[dm.n_stages] * 4);
+  auto add_hist = [&](int C, int Hh) {
+    if (Hh <= 0) return -1;
+    HistSpec s{C, Hh, {0, 0, 0}};
+    L.hist.push_back(s);
+    return (int)L.hist.size() - 1;
+  };
+  L.h_conv_in = add_hist(dm.d, dm.conv_k - 1);
+  for (int i = 0; i < dm.n_stages; ++i) {
+    L.h_up[i] = add_hist(dm.channels[i], 1);
+    L.h_res[i] = add_hist(dm.channels[i + 1], dm.res_k - 1);
+  }
+  L.h_conv_out = add_hist(dm.channels[dm.n_stages], dm.conv_k - 1);
+  for (int set = 0; set < 3; ++set)
+    for (auto& s : L.hist) s.off[set] = take((size_t)B * s.C * s.H * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+}  // namespace pp
+
+using namespace pp;
+
+struct pp_codec {
+  pp_codec_dims dm{};
+  int B = 0;
+  long S = 0;
+  pp_codec_weights w{};
+  CodecLayout lay;
+  char* arena = nullptr;
+  hipStream_t stream = nullptr;  // caller's
+  hipStream_t cap = nullptr;     // capture stream
+  // graphs [p][o]: read history set p, write set o = 1 - p (decode calls)
+  // or set 2 (timing launches)
+  hipGraph_t graph[2][2] = {};
+  hipGraphExec_t exec[2][2] = {};
+  int parity = 0;
+  std::vector<int> pos;
+  int32_t* ti_host = nullptr;     // pinned [B][TI_STRIDE]
+  int32_t* codes_host = nullptr;  // pinned [B][16]
+  float* pcm_host = nullptr;      // pinned [B][S]
+  bool poisoned = false;
+  std::string err;
+
+  template <class T>
+  T* at(size_t off) const {
+    return reinterpret_cast<T*>(arena + off);
+  }
+  int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    err = buf;
+    if (code == PP_EDEVICE) poisoned = true;
+    return code;
+  }
+};
+
+#define CODEC_HIP_OR_FAIL(h, call)                                                       \
+  do {                                                                                   \
+    const hipError_t e_ = (call);                                                        \
+    if (e_ != hipSuccess) return (h)->fail(PP_EDEVICE, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+namespace {
+
+// The whole decode of one call, recorded on stream s; reads history set p,
+// writes set po.
+void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
+  const pp_codec_dims& dm = h->dm;
+  const CodecLayout& L = h->lay;
+  const int B = h->B, d = dm.d, H = dm.n_heads, hd = d / H, F = dm.ffn, W = dm.window;
+  const pp_codec_weights& w = h->w;
+  const int* ti = h->at<int>(L.ti);
+
+  CodecEmbedArgs ea{};
+  ea.codes = h->at<int>(L.codes);
+  ea.ti = ti;
+  ea.B = B;
+  ea.d = d;
+  ea.n_q = dm.n_q;
+  ea.card = dm.card;
+  ea.codebooks = reinterpret_cast<const bf16_t*>(w.codebooks);
+  ea.alpha = w.attn_norm;
+  ea.x = h->at<float>(L.x);
+  ea.xa = h->at<bf16_t>(L.xa);
+  ea.xa_lo = (long)B * d;
+  ea.part = h->at<float>(L.part);
+  ea.inv_freq = h->at<double>(L.inv_freq);
+  ea.head_dim = hd;
+  ea.rope = h->at<float>(L.rope);
+  launch_codec_embed(ea, s);
+
+  const long pq = packed_elems(3 * d, d), pwo = packed_elems(d, d), pi = packed_elems(2 * F, d),
+             pd = packed_elems(d, F);
+  for (int l = 0; l < dm.n_layers; ++l) {
+    bf16_t* ring_l = h->at<bf16_t>(L.ring) + (long)l * L.ring_layer_elems;
+    GemmArgs g{};
+    g.W = reinterpret_cast<const bf16_t*>(w.wqkv) + (long)l * pq;
+    g.X = h->at<bf16_t>(L.xa);
+    g.x_lo = (long)B * d;
+    g.M = 3 * d;
+    g.K = d;
+    g.ldx = d;
+    g.B = B;
+    g.part_in = h->at<float>(L.part);
+    g.n_part = d / 16;
+    g.feat = d;
+    g.eps = dm.norm_eps;
+    g.q_out = h->at<float>(L.q);
+    g.ldq = d;
+    g.kv = ring_l;
+    g.kv_slot_stride = L.ring_slot_elems;
+    g.kv_v_off = L.ring_v_off;
+    g.n_heads = H;
+    g.head_dim = hd;
+    g.window = W;
+    g.ti = ti;
+    g.inv_freq = h->at<double>(L.inv_freq);
+    g.rope = h->at<float>(L.rope);
+    launch_gemm(EPI_QKV, g, s);
+
+    AttnArgs at{};
+    at.q = h->at<float>(L.q);
+    at.ldq = d;
+    at.kv = ring_l;
+    at.kv_slot_stride = L.ring_slot_elems;
+    at.kv_v_off = L.ring_v_off;
+    at.n_heads = H;
+    at.head_dim = hd;
+    at.window = W;
+    at.B = B;
+    at.ti = ti;
+    at.part = h->at<float>(L.att_part);
+    at.max_chunks = 1;
+    at.o = h->at<bf16_t>(L.o);
+    at.ldo = d;
+    at.o_lo = (long)B * d;
+    at.cnt = h->at<unsigned>(L.att_cnt);
+    launch_attention(at, s);
+
+    GemmArgs go{};
+    go.W = reinterpret_cast<const bf16_t*>(w.wo) + (long)l * pwo;
+    go.X = h->at<bf16_t>(L.o);
+    go.x_lo = (long)B * d;
+    go.M = d;
+    go.K = d;
+    go.ldx = d;
+    go.B = B;
+    go.x = h->at<float>(L.x);
+    go.ldres = d;
+    go.xa_out = h->at<bf16_t>(L.xa);
+    go.xa_lo = (long)B * d;
+    go.alpha_next = w.mlp_norm + (long)l * d;
+    go.part_out = h->at<float>(L.part);
+    launch_gemm(EPI_RESID, go, s);
+
+    GemmArgs gu{};
+    gu.W = reinterpret_cast<const bf16_t*>(w.w_in) + (long)l * pi;
+    gu.X = h->at<bf16_t>(L.xa);
+    gu.x_lo = (long)B * d;
+    gu.M = F;
+    gu.K = d;
+    gu.ldx = d;
+    gu.B = B;
+    gu.gate_off = F;
+    gu.part_in = h->at<float>(L.part);
+    gu.n_part = d / 16;
+    gu.feat = d;
+    gu.eps = dm.norm_eps;
+    gu.m_out = h->at<bf16_t>(L.m);
+    gu.ldm = F;
+    gu.m_lo = (long)B * F;
+    launch_gemm(EPI_GATED, gu, s);
+
+    GemmArgs gd{};
+    gd.W = reinterpret_cast<const bf16_t*>(w.w_out) + (long)l * pd;
+    gd.X = h->at<bf16_t>(L.m);
+    gd.x_lo = (long)B * F;
+    gd.M = d;
+    gd.K = F;
+    gd.ldx = F;
+    gd.B = B;
+    gd.x = h->at<float>(L.x);
+    gd.ldres = d;
+    gd.xa_out = h->at<bf16_t>(L.xa);
+    gd.xa_lo = (long)B * d;
+    gd.alpha_next = (l + 1 < dm.n_layers) ? w.attn_norm + (long)(l + 1) * d : w.out_norm;
+    gd.part_out = h->at<float>(L.part);
+    launch_gemm(EPI_RESID, gd, s);
+  }
+
+  CodecNormArgs na{};
+  na.x = h->at<float>(L.x);
+  na.part = h->at<float>(L.part);
+  na.alpha = w.out_norm;
+  na.eps = dm.norm_eps;
+  na.B = B;
+  na.d = d;
+  na.z = h->at<float>(L.z);
+  launch_codec_norm(na, s);
+
+  auto hist_in = [&](int e) { return e < 0 ? nullptr : h->at<float>(L.hist[e].off[p]); };
+  auto hist_H = [&](int e) { return e < 0 ? 0 : L.hist[e].H; };
+  const int* ch = dm.channels;
+
+  ConvArgs c0{};
+  c0.x = h->at<float>(L.z);
+  c0.C_in = d;
+  c0.T_in = 1;
+  c0.hist = hist_in(L.h_conv_in);
+  c0.H = hist_H(L.h_conv_in);
+  c0.w = reinterpret_cast<const bf16_t*>(w.conv_in_w);
+  c0.bias = w.conv_in_b;
+  c0.C_out = ch[0];
+  c0.K = dm.conv_k;
+  c0.stride = 1;
+  c0.act = 0;
+  c0.y = h->at<float>(L.h0);
+  c0.B = B;
+  launch_codec_conv(c0, s);
+
+  const float* hin = h->at<float>(L.h0);
+  for (int i = 0; i < dm.n_stages; ++i) {
+    const int ci = ch[i], co = ch[i + 1];
+    const long T = L.T[i];
+    ConvArgs up{};
+    up.x = hin;
+    up.C_in = ci;
+    up.T_in = (int)T;
+    up.hist = hist_in(L.h_up[i]);
+    up.H = 1;
+    up.w = reinterpret_cast<const bf16_t*>(w.up_w[i]);
+    up.bias = w.up_b[i];
+    up.C_out = co;
+    up.K = 2 * dm.strides[i];
+    up.stride = dm.strides[i];
+    up.transposed = 1;
+    up.act = 1;
+    up.y = h->at<float>(L.u[i]);
+    up.B = B;
+    launch_codec_conv(up, s);
+
+    ConvArgs ra{};
+    ra.x = h->at<float>(L.u[i]);
+    ra.C_in = co;
+    ra.T_in = (int)L.T[i + 1];
+    ra.hist = hist_in(L.h_res[i]);
+    ra.H = hist_H(L.h_res[i]);
+    ra.w = reinterpret_cast<const bf16_t*>(w.res_a_w[i]);
+    ra.bias = w.res_a_b[i];
+    ra.C_out = co / 2;
+    ra.K = dm.res_k;
+    ra.stride = 1;
+    ra.act = 1;
+    ra.y = h->at<float>(L.r[i]);
+    ra.B = B;
+    launch_codec_conv(ra, s);
+
+    ConvArgs rb{};
+    rb.x = h->at<float>(L.r[i]);
+    rb.C_in = co / 2;
+    rb.T_in = (int)L.T[i + 1];
+    rb.hist = nullptr;
+    rb.H = 0;
+    rb.w = reinterpret_cast<const bf16_t*>(w.res_b_w[i]);
+    rb.bias = w.res_b_b[i];
+    rb.C_out = co;
+    rb.K = 1;
+    rb.stride = 1;
+    rb.act = 1;
+    rb.skip = h->at<float>(L.u[i]);
+    rb.y = h->at<float>(L.hs[i]);
+    rb.B = B;
+    launch_codec_conv(rb, s);
+    hin = h->at<float>(L.hs[i]);
+  }
+
+  ConvArgs cz{};
+  cz.x = hin;
+  cz.C_in = ch[dm.n_stages];
+  cz.T_in = (int)L.T[dm.n_stages];
+  cz.hist = hist_in(L.h_conv_out);
+  cz.H = hist_H(L.h_conv_out);
+  cz.w = reinterpret_cast<const bf16_t*>(w.conv_out_w);
+  cz.bias = w.conv_out_b;
+  cz.C_out = 1;
+  cz.K = dm.conv_k;
+  cz.stride = 1;
+  cz.act = 1;
+  cz.y = h->at<float>(L.pcm);
+  cz.B = B;
+  launch_codec_conv(cz, s);
+
+  // the histories for the next call
+  HistArgs ha{};
+  ha.B = B;
+  auto entry = [&](int e, const float* x, int T) {
+    if (e < 0) return;
+    HistEntry& he = ha.e[ha.n++];
+    he.x = x;
+    he.C = L.hist[e].C;
+    he.T = T;
+    he.H = L.hist[e].H;
+    he.old_h = h->at<float>(L.hist[e].off[p]);
+    he.new_h = h->at<float>(L.hist[e].off[po]);
+  };
+  entry(L.h_conv_in, h->at<float>(L.z), 1);
+  const float* xin = h->at<float>(L.h0);
+  for (int i = 0; i < dm.n_stages; ++i) {
+    entry(L.h_up[i], xin, (int)L.T[i]);
+    entry(L.h_res[i], h->at<float>(L.u[i]), (int)L.T[i + 1]);
+    xin = h->at<float>(L.hs[i]);
+  }
+  entry(L.h_conv_out, xin, (int)L.T[dm.n_stages]);
+  launch_codec_hist(ha, s);
+}
+
+hipError_t capture_codec(pp_codec* h) {
+  hipError_t e;
+  for (int p = 0; p < 2; ++p)
+    for (int t = 0; t < 2; ++t) {
+      if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
+      record_codec(h, h->cap, p, t ? 2 : 1 - p);
+      if ((e = hipStreamEndCapture(h->cap, &h->graph[p][t])) != hipSuccess) return e;
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipGraphInstantiate(&h->exec[p][t], h->graph[p][t], nullptr, nullptr, 0)) != hipSuccess) return e;
+    }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pp_codec_samples(const pp_codec_dims* dims) {
+  if (!codec_dims_ok(dims, nullptr)) return PP_EINVAL;
+  return (int)codec_samples(*dims);
+}
+
+int pp_codec_arena_bytes(const pp_codec_dims* dims, int B, size_t* out_bytes) {
+  if (!out_bytes || !codec_dims_ok(dims, nullptr) || B < 1 || B > PP_CODEC_MAX_BATCH) return PP_EINVAL;
+  *out_bytes = make_codec_layout(*dims, B).total;
+  return PP_OK;
+}
+
+int pp_codec_create(const pp_codec_dims* dims, int B, const pp_codec_weights* w, void* arena, size_t arena_bytes,
+                    void* stream, pp_codec** out) {
+  std::string why;
+  if (!out) { g_codec_create_error = "out is NULL"; return PP_EINVAL; }
+  *out = nullptr;
+  if (!codec_dims_ok(dims, &why)) { g_codec_create_error = why; return PP_EINVAL; }
+  if (B < 1 || B > PP_CODEC_MAX_BATCH) { g_codec_create_error = "B outside 1..PP_CODEC_MAX_BATCH"; return PP_EINVAL; }
+  if (!w || !arena) { g_codec_create_error = "weights or arena is NULL"; return PP_EINVAL; }
+  {
+    const void* req[] = {w->codebooks, w->attn_norm, w->wqkv, w->wo, w->mlp_norm, w->w_in, w->w_out,
+                         w->out_norm, w->conv_in_w, w->conv_in_b, w->conv_out_w, w->conv_out_b};
+    for (const void* p : req)
+      if (!p) { g_codec_create_error = "a weight pointer is NULL"; return PP_EINVAL; }
+    for (int i = 0; i < dims->n_stages; ++i)
+      if (!w->up_w[i] || !w->up_b[i] || !w->res_a_w[i] || !w->res_a_b[i] || !w->res_b_w[i] || !w->res_b_b[i]) {
+        g_codec_create_error = "a stage weight pointer is NULL";
+        return PP_EINVAL;
+      }
+  }
+  if (reinterpret_cast<uintptr_t>(arena) % ALIGN) { g_codec_create_error = "arena not 256-byte aligned"; return PP_EINVAL; }
+  CodecLayout lay = make_codec_layout(*dims, B);
+  if (arena_bytes < lay.total) { g_codec_create_error = "arena too small"; return PP_ENOSPC; }
+
+  pp_codec* h = new (std::nothrow) pp_codec();
+  if (!h) { g_codec_create_error = "out of host memory"; return PP_ENOSPC; }
+  h->dm = *dims;
+  h->B = B;
+  h->S = codec_samples(*dims);
+  h->w = *w;
+  h->lay = lay;
+  h->arena = static_cast<char*>(arena);
+  h->stream = static_cast<hipStream_t>(stream);
+  h->pos.assign(B, 0);
+  auto bail = [&](const char* what, hipError_t e) {
+    g_codec_create_error = std::string(what) + ": " + hipGetErrorString(e);
+    pp_codec_destroy(h);
+    return PP_EDEVICE;
+  };
+  hipError_t e;
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->ti_host), (size_t)B * TI_STRIDE * 4, hipHostMallocDefault)) !=
+      hipSuccess)
+    return bail("hipHostMalloc", e);
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->codes_host), (size_t)B * 16 * 4, hipHostMallocDefault)) !=
+      hipSuccess)
+    return bail("hipHostMalloc", e);
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->pcm_host), (size_t)B * h->S * 4, hipHostMallocDefault)) !=
+      hipSuccess)
+    return bail("hipHostMalloc", e);
+  std::memset(h->ti_host, 0, (size_t)B * TI_STRIDE * 4);
+  std::memset(h->codes_host, 0, (size_t)B * 16 * 4);
+
+  const int hd = dims->d / dims->n_heads;
+  std::vector<double> freq(hd / 2);
+  for (int i = 0; i < hd / 2; ++i) freq[i] = std::pow((double)dims->rope_base, -2.0 * i / hd);
+  if ((e = hipMemcpyAsync(h->at<double>(lay.inv_freq), freq.data(), freq.size() * 8, hipMemcpyHostToDevice,
+                          h->stream)) != hipSuccess)
+    return bail("hipMemcpyAsync", e);
+  // every slot fresh: positions 0, zero histories (both sets), tickets zero
+  if ((e = hipMemcpyAsync(h->at<int>(lay.ti), h->ti_host, (size_t)B * TI_STRIDE * 4, hipMemcpyHostToDevice,
+                          h->stream)) != hipSuccess)
+    return bail("hipMemcpyAsync", e);
+  if ((e = hipMemcpyAsync(h->at<int>(lay.codes), h->codes_host, (size_t)B * 16 * 4, hipMemcpyHostToDevice,
+                          h->stream)) != hipSuccess)
+    return bail("hipMemcpyAsync", e);
+  if ((e = hipMemsetAsync(h->at<char>(lay.att_cnt), 0, (size_t)B * dims->n_heads * 4, h->stream)) != hipSuccess)
+    return bail("hipMemsetAsync", e);
+  for (const auto& s : lay.hist)
+    for (int set = 0; set < 3; ++set)
+      if ((e = hipMemsetAsync(h->at<char>(s.off[set]), 0, (size_t)B * s.C * s.H * 4, h->stream)) != hipSuccess)
+        return bail("hipMemsetAsync", e);
+  if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
+  if ((e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
+  if ((e = capture_codec(h)) != hipSuccess) return bail("graph capture", e);
+  *out = h;
+  return PP_OK;
+}
+
+int pp_codec_decode(pp_codec* h, const int32_t* codes, float* pcm) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (!codes || !pcm) return h->fail(PP_EINVAL, "codes or pcm is NULL");
+  const int B = h->B, nq = h->dm.n_q;
+  for (int b = 0; b < B; ++b)
+    for (int q = 0; q < nq; ++q) {
+      const int c = codes[b * nq + q];
+      if (c < 0 || c >= h->dm.card) return h->fail(PP_EINVAL, "slot %d codebook %d: code %d outside [0, %d)", b, q, c, h->dm.card);
+    }
+  for (int b = 0; b < B; ++b) {
+    h->ti_host[b * TI_STRIDE + TI_POS] = h->pos[b];
+    for (int q = 0; q < nq; ++q) h->codes_host[b * nq + q] = codes[b * nq + q];
+  }
+  const CodecLayout& L = h->lay;
+  CODEC_HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(L.ti), h->ti_host, (size_t)B * TI_STRIDE * 4, hipMemcpyHostToDevice,
+                                      h->stream));
+  CODEC_HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(L.codes), h->codes_host, (size_t)B * nq * 4, hipMemcpyHostToDevice,
+                                      h->stream));
+  CODEC_HIP_OR_FAIL(h, hipGraphLaunch(h->exec[h->parity][0], h->stream));
+  CODEC_HIP_OR_FAIL(h, hipMemcpyAsync(h->pcm_host, h->at<float>(L.pcm), (size_t)B * h->S * 4, hipMemcpyDeviceToHost,
+                                      h->stream));
+  CODEC_HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  std::memcpy(pcm, h->pcm_host, (size_t)B * h->S * 4);
+  for (int b = 0; b < B; ++b) ++h->pos[b];
+  h->parity ^= 1;
+  return PP_OK;
+}
+
+int pp_codec_reset(pp_codec* h, int slot) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (slot < 0 || slot >= h->B) return h->fail(PP_EINVAL, "slot %d outside [0, %d)", slot, h->B);
+  // the set the next call reads
+  for (const auto& s : h->lay.hist)
+    CODEC_HIP_OR_FAIL(h, hipMemsetAsync(h->at<char>(s.off[h->parity]) + (size_t)slot * s.C * s.H * 4, 0,
+                                        (size_t)s.C * s.H * 4, h->stream));
+  CODEC_HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  h->pos[slot] = 0;
+  return PP_OK;
+}
+
+int pp_codec_time(pp_codec* h, int iters, float* avg_ms) {
+  if (!h || !avg_ms || iters < 1) return h ? h->fail(PP_EINVAL, "bad arguments") : PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  // the last call's work again: it reads the history set the last call read
+  // and writes the timing set, so the set the next call reads is untouched;
+  // the ring entry it rewrites (the last call's position) gets the same key
+  // and value, or, for a slot reset since, lies outside that slot's window
+  // until the slot's own calls overwrite it
+  const int p = h->parity ^ 1;
+  hipEvent_t e0, e1;
+  CODEC_HIP_OR_FAIL(h, hipEventCreate(&e0));
+  CODEC_HIP_OR_FAIL(h, hipEventCreate(&e1));
+  CODEC_HIP_OR_FAIL(h, hipGraphLaunch(h->exec[p][1], h->stream));  // warm
+  CODEC_HIP_OR_FAIL(h, hipEventRecord(e0, h->stream));
+  for (int i = 0; i < iters; ++i) CODEC_HIP_OR_FAIL(h, hipGraphLaunch(h->exec[p][1], h->stream));
+  CODEC_HIP_OR_FAIL(h, hipEventRecord(e1, h->stream));
+  CODEC_HIP_OR_FAIL(h, hipEventSynchronize(e1));
+  float ms = 0.f;
+  CODEC_HIP_OR_FAIL(h, hipEventElapsedTime(&ms, e0, e1));
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *avg_ms = ms / iters;
+  return PP_OK;
+}
+
+int pp_codec_taps(pp_codec* h, pp_codec_taps_t* out) {
+  if (!h || !out) return h ? h->fail(PP_EINVAL, "out is NULL") : PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  CODEC_HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  out->ring = h->at<uint16_t>(h->lay.ring);
+  out->z = h->at<float>(h->lay.z);
+  return PP_OK;
+}
+
+void pp_codec_destroy(pp_codec* h) {
+  if (!h) return;
+  if (h->stream) (void)hipStreamSynchronize(h->stream);
+  for (int p = 0; p < 2; ++p)
+    for (int t = 0; t < 2; ++t) {
+      if (h->exec[p][t]) (void)hipGraphExecDestroy(h->exec[p][t]);
+      if (h->graph[p][t]) (void)hipGraphDestroy(h->graph[p][t]);
+    }
+  if (h->cap) (void)hipStreamDestroy(h->cap);
+  if (h->ti_host) (void)hipHostFree(h->ti_host);
+  if (h->codes_host) (void)hipHostFree(h->codes_host);
+  if (h->pcm_host) (void)hipHostFree(h->pcm_host);
+  delete h;
+}
+
+const char* pp_codec_last_error(const pp_codec* h) {
+  return h ? h->err.c_str() : g_codec_create_error.c_str();
+}
+
+}  // extern "C"

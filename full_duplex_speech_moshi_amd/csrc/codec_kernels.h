@@ -1,0 +1,72 @@
+// Kernels of the streaming codec decoder (codec.hip) and their arguments.
+// The decoder's transformer layers run on the tick's GEMM and ring-decode
+// launchers (kernels.h); these are the rest: the residual-quantiser sum, the
+// output norm, the causal (transposed) convolutions and the streaming-state
+// update.  Layouts: activations fp32 [B][C][T] (T = samples of this call at
+// the layer's rate), convolution weights bf16 [C_out][C_in][K], histories
+// fp32 [B][C][H] (the H inputs before this call, raw: the activation is
+// applied when they are read).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace pp {
+
+constexpr int CODEC_MAX_HIST = 24;   // history entries (convolutions with memory)
+
+struct CodecEmbedArgs {
+  const int* codes;       // [B][n_q]
+  const int* ti;          // tick-input layout: the slot's frame position at TI_POS
+  int B, d, n_q, card;
+  const bf16_t* codebooks;  // [n_q][card][d]
+  const float* alpha;       // first attention-norm alpha
+  float* x;                 // [B][d] residual stream
+  bf16_t* xa; long xa_lo;   // [B][d] x * alpha as a bf16 hi/lo pair
+  float* part;              // [B][d/16] sums of squares per 16 features
+  const double* inv_freq; int head_dim; float* rope;  // RoPE table [B][head_dim] (cos, sin) at the position
+};
+void launch_codec_embed(const CodecEmbedArgs& a, hipStream_t s);
+
+struct CodecNormArgs {
+  const float* x;        // [B][d]
+  const float* part;     // [B][d/16] sums of squares of x per 16 features
+  const float* alpha;    // [d]
+  float eps;
+  int B, d;
+  float* z;              // [B][d]
+};
+void launch_codec_norm(const CodecNormArgs& a, hipStream_t s);
+
+// One convolution.  transposed = 0: causal convolution of kernel K (stride
+// 1); transposed = 1: causal transposed convolution with stride `stride` and
+// K = 2 stride.  Input x [B][C_in][T_in] with history hist [B][C_in][H]
+// (H = K - 1 for the causal form, 1 for the transposed form); act = 1
+// applies ELU to every input read (history included).  Output y
+// [B][C_out][T_out], T_out = T_in * stride, plus skip [B][C_out][T_out] when
+// given.
+struct ConvArgs {
+  const float* x; int C_in, T_in;
+  const float* hist; int H;
+  const bf16_t* w; const float* bias; int C_out, K, stride, transposed;
+  int act;
+  const float* skip;
+  float* y;
+  int B;
+};
+void launch_codec_conv(const ConvArgs& a, hipStream_t s);
+
+// The streaming-state update after a call: for each convolution with memory,
+// the new history is the last H entries of (old history, this call's input).
+struct HistEntry {
+  const float* x; int C, T;     // this call's input [B][C][T]
+  const float* old_h; float* new_h; int H;  // [B][C][H] each
+};
+struct HistArgs {
+  HistEntry e[CODEC_MAX_HIST];
+  int n, B;
+};
+void launch_codec_hist(const HistArgs& a, hipStream_t s);
+
+}  // namespace pp

@@ -110,6 +110,13 @@ class CodecOracle:
         for k, v in weights.items():
             self.wts[k] = upcast_bf16(v, dtype) if v.dtype == np.uint16 else np.asarray(v, dtype)
         self.slots = [_State(cd, self.W, dtype) for _ in range(B)]
+        # Test hook for the bf16 rounding of stored keys and values, a decision
+        # with two valid outcomes where the exact value lies at a rounding
+        # midpoint within another implementation's rounding error:
+        # store_hook(slot, layer, pos, k, v, k_stored, v_stored) -> the (k, v)
+        # to store.  None: store this oracle's own rounding.
+        self.store_hook = None
+        self._slot = 0
 
     def reset(self, s):
         self.slots[s].reset(self.cd, self.dt)
@@ -120,7 +127,11 @@ class CodecOracle:
     def decode(self, codes) -> np.ndarray:
         """codes int [B][8] -> pcm [B][samples]."""
         codes = np.asarray(codes).reshape(self.B, self.cd.n_q)
-        return np.stack([self._frame(self.slots[b], codes[b]) for b in range(self.B)])
+        out = []
+        for b in range(self.B):
+            self._slot = b
+            out.append(self._frame(self.slots[b], codes[b]))
+        return np.stack(out)
 
     # -- the pieces, in order
 
@@ -147,8 +158,12 @@ class CodecOracle:
             qkv = w[f"layers.{l}.wqkv"] @ h
             q = rope_interleaved(qkv[0:d].reshape(H, Dh), pos, cd.rope_base)
             k = rope_interleaved(qkv[d:2 * d].reshape(H, Dh), pos, cd.rope_base)
-            st.K[l, pos % W] = self._store(k)
-            st.V[l, pos % W] = self._store(qkv[2 * d:3 * d].reshape(H, Dh))
+            v = qkv[2 * d:3 * d].reshape(H, Dh)
+            ks, vs = self._store(k), self._store(v)
+            if self.store_hook is not None:
+                ks, vs = self.store_hook(self._slot, l, pos, k, v, ks, vs)
+            st.K[l, pos % W] = ks
+            st.V[l, pos % W] = vs
             o = softmax_attend(q, st.K[l, ring_idx], st.V[l, ring_idx])
             x = x + w[f"layers.{l}.wo"] @ o.reshape(d)
             h = rmsnorm(x, w[f"layers.{l}.mlp_norm"], cd.norm_eps)
@@ -182,6 +197,7 @@ class CodecOracle:
 
     def _frame(self, st, codes) -> np.ndarray:
         z = self.transformer(st, self.latent(codes))
+        st.last_z = z
         pcm = self.convs(st, z)
         st.pos += 1
         return pcm

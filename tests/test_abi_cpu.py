@@ -12,8 +12,8 @@ from full_duplex_speech_moshi_amd import pp, synth
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
-    src = open(os.path.join(ROOT, "include", "pp.h")).read()
+def declared_functions(header="pp.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pp_\w+)\s*\(", src, flags=re.M)))
 
@@ -31,6 +31,58 @@ def test_exports_every_declared_entry_point(lib):
     assert set(names) == set(pp.EXPORTS)
     for n in names:
         assert getattr(lib, n) is not None
+
+
+def test_exports_every_codec_entry_point(lib):
+    from full_duplex_speech_moshi_amd import codec
+    names = declared_functions("codec.h")
+    assert len(names) == 9
+    assert set(names) == set(codec.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_codec_limits_and_structs_match_the_header():
+    from full_duplex_speech_moshi_amd import codec
+    src = open(os.path.join(ROOT, "include", "codec.h")).read()
+    limits = {k: int(v) for k, v in re.findall(r"#define\s+(PP_CODEC_MAX_\w+)\s+(\d+)", src)}
+    assert limits == {"PP_CODEC_MAX_STAGES": codec.PP_CODEC_MAX_STAGES, "PP_CODEC_MAX_BATCH": codec.PP_CODEC_MAX_BATCH,
+                      "PP_CODEC_MAX_WINDOW": codec.PP_CODEC_MAX_WINDOW}
+    body = re.sub(r"/\*.*?\*/", "", src[src.index("typedef struct pp_codec_weights"):], flags=re.S)
+    body = body[:body.index("}")]
+    fields = re.findall(r"(\w+)(?:\[PP_CODEC_MAX_STAGES\])?;", body)
+    assert fields == [f[0] for f in codec.PPCodecWeights._fields_]
+
+
+def test_codec_dims_validated_on_the_host(lib):
+    import dataclasses
+    from full_duplex_speech_moshi_amd import codec
+    assert codec.pp_codec_samples(codec.make_codec_dims(synth.CODEC)) == 1920
+    assert codec.pp_codec_samples(codec.make_codec_dims(synth.CODEC_TINY)) == 24
+    bad = [dict(n_heads=3), dict(d=500), dict(window=257), dict(strides=(0, 2)), dict(channels=(8, 5, 4)),
+           dict(n_q=17), dict(ffn=100)]
+    for kw in bad:
+        cd = dataclasses.replace(synth.CODEC_TINY, **kw)
+        if "strides" in kw:
+            cd = dataclasses.replace(cd, channels=cd.channels[:len(cd.strides) + 1])
+        if "channels" in kw:
+            cd = dataclasses.replace(cd, strides=cd.strides[:len(cd.channels) - 1])
+        out = ctypes.c_size_t()
+        assert codec._lib().pp_codec_arena_bytes(ctypes.byref(codec.make_codec_dims(cd)), 1, ctypes.byref(out)) \
+            == pp.PP_EINVAL, kw
+    out = ctypes.c_size_t()
+    for B in (0, 33):
+        assert codec._lib().pp_codec_arena_bytes(ctypes.byref(codec.make_codec_dims(synth.CODEC)), B,
+                                                 ctypes.byref(out)) == pp.PP_EINVAL
+    # one slot's ring: layers x {k, v} x heads x window x head_dim bf16
+    n1 = codec.pp_codec_arena_bytes(codec.make_codec_dims(synth.CODEC), 1)
+    n2 = codec.pp_codec_arena_bytes(codec.make_codec_dims(synth.CODEC), 2)
+    assert n2 - n1 >= 8 * 2 * 8 * 250 * 64 * 2
+    h = ctypes.c_void_p()
+    w = codec.PPCodecWeights()
+    rc = codec._lib().pp_codec_create(ctypes.byref(codec.make_codec_dims(synth.CODEC)), 1, ctypes.byref(w),
+                                      ctypes.c_void_p(256), 1 << 30, None, ctypes.byref(h))
+    assert rc == pp.PP_EINVAL and not h.value and b"NULL" in codec._lib().pp_codec_last_error(None)
 
 
 def test_binding_limits_match_the_header():

@@ -1,0 +1,160 @@
+"""The codec decoder's HIP path (include/codec.h) against the codec oracle
+(oracle/codec.py, fp64), and its slot isolation and streaming state.
+
+Stored keys and values: both sides round them to bf16, the GPU from its
+fp32 value and the oracle from the fp64 value, so where the two lie on
+opposite sides of a rounding point the stored values differ, and either is a
+correct rounding.  The GPU's error on a key or value comes from its GEMM
+input's bf16 hi/lo representation (2^-17 of each input) and fp32 sums,
+added over the dot product: bounded by 2^-12 of the head vector's RMS (about
+18 terms' worth of |W_i h_i| at 2^-17 each, with margin), which can be many
+bf16 steps of a near-zero element.  Each stored value must be within half a
+bf16 step of the exact value plus that bound; values that differ from the
+oracle's own rounding are counted and reported.  The oracle then takes the
+GPU's stored values, so everything downstream is compared on identical
+caches.
+
+Tolerance on the samples and on the transformer output: the GPU computes in
+fp32 with bf16 weights (the transformer's GEMM inputs as bf16 hi/lo pairs),
+the oracle in fp64 with the same weights; the oracle's own fp32 run sits
+about 3e-6 (relative L2) from its fp64 run at the full shape, and the bound
+is 5e-5 relative L2 and 5e-5 of the frame's largest sample elementwise.
+Parity with the real Mimi codec is unpinned: its layers and weights are not
+available (the structure is a reading of the SoundStream / EnCodec family
+the pages name)."""
+import numpy as np
+import pytest
+
+from full_duplex_speech_moshi_amd import synth
+from oracle import codec as oracle_codec
+from oracle.tick import upcast_bf16
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 5e-5
+MAX_REL = 5e-5
+KV_ERR = 2.0 ** -12  # of the head vector's RMS
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _engine(cd, w, B, dev=None):
+    import torch
+    from full_duplex_speech_moshi_amd import codec
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return codec.CodecEngine(cd, w, B, device_weights=dev)
+
+
+def _compare(got, ref, what):
+    err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    mx = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err <= REL_L2 and mx <= MAX_REL, f"{what}: rel-L2 {err:.2e}, max {mx:.2e}"
+    return err, mx
+
+
+class _GpuCaches:
+    """The oracle's store hook: checks the GPU's stored keys and values of
+    the frame just decoded and hands them to the oracle."""
+
+    def __init__(self, cd):
+        self.cd, self.ring, self.flips, self.checked = cd, None, 0, 0
+
+    def __call__(self, slot, layer, pos, k, v, ks, vs):
+        out = []
+        for which, exact, mine in ((0, k, ks), (1, v, vs)):
+            gpu = upcast_bf16(self.ring[slot, layer, which, :, pos % self.cd.window, :], np.float64)
+            rms = np.sqrt(np.mean(exact ** 2, axis=1, keepdims=True))
+            # half a bf16 step at the value's magnitude: 2^(floor(log2|x|) - 8)
+            half = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 8)
+            bad = np.abs(gpu - exact) > half + KV_ERR * rms
+            assert not bad.any(), \
+                f"slot {slot} layer {layer} pos {pos} {'kv'[which]}: GPU stored {gpu[bad][:4]}, exact {exact[bad][:4]}"
+            self.flips += int((gpu != mine).sum())
+            self.checked += gpu.size
+            out.append(gpu)
+        return out[0], out[1]
+
+
+def _parity_run(cd, w, B, n, seed, report):
+    codes = [synth.agent_frames(seed + b, n) for b in range(B)]
+    o = oracle_codec.CodecOracle(cd, w, B, np.float64)
+    hook = _GpuCaches(cd)
+    o.store_hook = hook
+    e = _engine(cd, w, B)
+    worst = [0.0, 0.0, 0.0]
+    for t in range(n):
+        c = np.stack([codes[b][t] for b in range(B)])
+        got = e.decode(c)
+        taps = e.taps()
+        hook.ring = taps["ring"]
+        ref = o.decode(c)
+        for b in range(B):
+            err, mx = _compare(got[b], ref[b], f"frame {t} slot {b}")
+            zerr, _ = _compare(taps["z"][b], o.slots[b].last_z, f"frame {t} slot {b} transformer output")
+            worst = [max(worst[0], err), max(worst[1], mx), max(worst[2], zerr)]
+    timing = e.time(10)
+    e.close()
+    report(f"worst rel-L2 {worst[0]:.2e}, worst max {worst[1]:.2e}, transformer output {worst[2]:.2e}; "
+           f"stored keys and values checked "
+           f"{hook.checked}, of which {hook.flips} differ from the oracle's rounding; device time per call {timing:.3f} ms")
+
+
+@pytest.mark.timeout(600)
+def test_tiny_codec_matches_oracle_over_a_wrapping_window():
+    cd = synth.CODEC_TINY
+    _say(f"case: tiny codec, B=2, {3 * cd.window + 2} frames (window {cd.window})")
+    _parity_run(cd, synth.make_codec_weights(cd, seed=1), 2, 3 * cd.window + 2, 30, _say)
+
+
+@pytest.mark.timeout(600)
+def test_full_codec_matches_oracle():
+    cd = synth.CODEC
+    _say("case: codec at the full shape (1920 samples per frame), B=2, 8 frames")
+    _parity_run(cd, synth.make_codec_weights(cd, seed=0), 2, 8, 40, _say)
+
+
+@pytest.mark.timeout(600)
+def test_codec_slots_are_independent_and_reset_is_fresh():
+    """B = 5 against B = 1, bit for bit: slot 3 of the batch carries the same
+    stream as the single slot; slot 1 is reset mid-stream and then fed that
+    stream from its start, which must give the single slot's samples; timing
+    launches and a rejected call in between change nothing."""
+    import torch
+    from full_duplex_speech_moshi_amd import codec, pp
+    cd = synth.CODEC_TINY
+    w = synth.make_codec_weights(cd, seed=2)
+    dev = codec.upload_codec_weights(cd, w, torch.device("cuda:0"))
+    n = 2 * cd.window + 3
+    mine = synth.agent_frames(50, n)
+    noise = synth.agent_frames(51, 2 * n)
+    single = _engine(cd, w, 1, dev)
+    ref = [single.decode(mine[t][None])[0] for t in range(n)]
+    single.close()
+    _say("case: tiny codec, B=5 vs B=1, reset at frame 7")
+    e = _engine(cd, w, 5, dev)
+    t1 = 0
+    for t in range(n):
+        c = noise[t % len(noise)][None].repeat(5, 0)
+        c[0] = noise[(t + 3) % len(noise)]
+        c[3] = mine[t]
+        if t == 7:
+            e.reset(1)
+            t1 = 0
+        if t >= 7:
+            c[1] = mine[t1]
+        if t == 9:
+            e.time(3)
+            bad = c.copy()
+            bad[2, 4] = cd.card
+            with pytest.raises(pp.PPError) as ex:
+                e.decode(bad)
+            assert ex.value.code == pp.PP_EINVAL
+        got = e.decode(c)
+        np.testing.assert_array_equal(got[3], ref[t], err_msg=f"frame {t} slot 3")
+        if t >= 7:
+            np.testing.assert_array_equal(got[1], ref[t1], err_msg=f"frame {t} slot 1 (reset at 7)")
+            t1 += 1
+    e.close()
