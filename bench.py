@@ -255,6 +255,73 @@ def run_sub_c4(args):
     return {k: c[k] for k in keys if k in c}
 
 
+def codec_call_bytes(cd, B: int, n_keys: int) -> int:
+    """Bytes one decode call must move at least: every weight once (bf16
+    matrices and conv weights, fp32 norms and biases), each slot's 8 codebook
+    rows, and each slot's stored keys and values over n_keys frames."""
+    d, F, L, H = cd.d, cd.ffn, cd.n_layers, cd.n_heads
+    mats = L * (3 * d * d + d * d + 2 * F * d + d * F)
+    c = cd.channels
+    conv = c[0] * d * cd.conv_k + c[-1] * cd.conv_k
+    bias = c[0] + 1
+    for i, s in enumerate(cd.strides):
+        ci, co = c[i], c[i + 1]
+        conv += co * ci * 2 * s + (co // 2) * co * cd.res_k + co * (co // 2)
+        bias += co + co // 2 + co
+    norms = (2 * L + 1) * d
+    per_slot = cd.n_q * d * 2 + L * 2 * n_keys * d * 2
+    return 2 * (mats + conv) + 4 * (norms + bias) + B * per_slot
+
+
+def run_codec(args):
+    """The codec decoder on its own: B slots (default 32), the window filled
+    by warm-up calls, then timed calls of pp_codec_decode (host clock per
+    call, device time of the call's graph from pp_codec_time)."""
+    import torch
+    from full_duplex_speech_moshi_amd import codec, synth
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    cd = synth.CODEC
+    B = args.batch or 32
+    K = args.steps or 200
+    WU = max(args.warmup, cd.window)
+    w = synth.make_codec_weights(cd, seed=0)
+    e = codec.CodecEngine(cd, w, B)
+    frames = [synth.agent_frames(60 + b, WU + K) for b in range(B)]
+    for t in range(WU):
+        e.decode(np.stack([frames[b][t] for b in range(B)]))
+    torch.cuda.synchronize()
+    ms = np.empty(K)
+    for t in range(K):
+        c = np.stack([frames[b][WU + t] for b in range(B)])
+        t0 = time.perf_counter()
+        e.decode(c)
+        ms[t] = (time.perf_counter() - t0) * 1e3
+    dev_ms = e.time(20)
+    e.close()
+    by = codec_call_bytes(cd, B, cd.window)
+    return {"metric": "decoded frames/sec (codec, 1920 samples per frame)", "value": B * K / (ms.sum() / 1e3),
+            "unit": "frames/s", "steps": K, "warmup": WU, "p50_call_ms": float(np.median(ms)),
+            "device_call_ms": dev_ms, "call_bytes": by, "call_hbm_frac": by / (dev_ms * 1e-3) / (PEAK_HBM_GBS * 1e9),
+            "config": {"workload": f"codec decoder (d {cd.d}, {cd.n_layers} layers, strides {list(cd.strides)}), "
+                                   f"B={B}, window of {cd.window} frames filled by {WU} warm-up calls, then {K} "
+                                   f"timed calls", "B": B}}
+
+
+def run_sub_codec(args):
+    """The codec decoder timed by a child run of this script (B = 32)."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--config", "codec", "--batch", "32", "--steps", "200",
+           "--no-sub", "--cpu-ticks", "0"]
+    log("sub-record: " + " ".join(cmd[1:]))
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    if r.returncode != 0 or not lines:
+        return {"error": f"codec child exited with {r.returncode}"}
+    return json.loads(lines[-1])
+
+
 def cpu_baseline(args, dm, W, B, weights, wl, sampling):
     """The oracle as it stands, one slot at a time on the host cores, on a
     bounded sample of the workload: C0-C2 tick slot 0; C3 ticks slots 0 and 1
@@ -314,7 +381,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed ticks (default: the config's own count)")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="C1", choices=["C0", "C1", "C2", "C3", "C4", "sweep", "sweep_empty"])
+    ap.add_argument("--config", default="C1", choices=["C0", "C1", "C2", "C3", "C4", "sweep", "sweep_empty", "codec"])
     ap.add_argument("--batch", type=int, default=None, help="slots (default: the config's own B)")
     ap.add_argument("--cpu-ticks", type=int, default=100000,
                     help="at most this many oracle ticks timed on the host (0: skip the CPU baseline)")
@@ -343,9 +410,12 @@ def main():
               "with no exchange; run one process per GPU)", file=sys.stderr)
         sys.exit(2)
 
+    if args.config == "codec":
+        print(json.dumps(run_codec(args)), flush=True)
+        return
     sub = None
     if args.config == "C1" and args.batch is None and not args.no_sub and args.mode == "bench":
-        sub = run_sub_c4(args)
+        sub = {"C4": run_sub_c4(args), "codec": run_sub_codec(args)}
 
     import torch
     from full_duplex_speech_moshi_amd import pp, synth
@@ -490,7 +560,7 @@ def main():
     if args.cpu_ticks > 0:
         result["cpu_baseline"] = cpu_baseline(args, dm, W, B, weights, wl, sampling)
     if sub is not None:
-        result["sub"] = {"C4": sub}
+        result["sub"] = sub
     print(json.dumps(result), flush=True)
 
 

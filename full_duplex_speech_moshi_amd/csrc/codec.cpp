@@ -43,11 +43,11 @@ bool codec_dims_ok(const pp_codec_dims* dm, std::string* why) {
   const int hd = dm->d / dm->n_heads;
   if (hd != 32 && hd != 64 && hd != 128) return fail("head_dim must be 32, 64 or 128");
   if (dm->window < 1 || dm->window > PP_CODEC_MAX_WINDOW) return fail("window outside 1..PP_CODEC_MAX_WINDOW");
-  if (dm->conv_k < 1 || dm->res_k < 1) return fail("kernels must be >= 1");
+  if (dm->conv_k < 1 || dm->res_k < 1 || dm->conv_k > 8 || dm->res_k > 8) return fail("kernels must be 1..8");
   if (dm->n_stages < 1 || dm->n_stages > PP_CODEC_MAX_STAGES) return fail("n_stages outside 1..PP_CODEC_MAX_STAGES");
   long samples = 1;
   for (int i = 0; i < dm->n_stages; ++i) {
-    if (dm->strides[i] < 1) return fail("strides must be >= 1");
+    if (dm->strides[i] < 1 || dm->strides[i] > 8) return fail("strides must be 1..8");
     samples *= dm->strides[i];
     if (samples > (1 << 20)) return fail("too many samples per frame");
   }
@@ -65,6 +65,8 @@ long codec_samples(const pp_codec_dims& dm) {
 
 // History entries: conv_in, then per stage the upsampling and the residual
 // unit's first convolution, then conv_out (entries with H = 0 are left out).
+// Each holds its convolution's input as fed: z for conv_in, the ELU'd
+// signals for the others.
 struct HistSpec {
   int C, H;
   size_t off[3];  // per set: two that calls alternate between, one that timing launches write
@@ -72,8 +74,11 @@ struct HistSpec {
 
 struct CodecLayout {
   size_t ti, codes, inv_freq, rope, x, xa, part, q, o, m, ring, att_part, att_cnt, z;
-  size_t h0, pcm;
-  size_t u[PP_CODEC_MAX_STAGES], r[PP_CODEC_MAX_STAGES], hs[PP_CODEC_MAX_STAGES];
+  size_t h0a, pcm;  // h0a: ELU of the first convolution's output
+  // per stage: the upsampled signal u (raw, the residual unit's skip) and its
+  // ELU, the ELU of the residual unit's first convolution, and the ELU of the
+  // stage's output (each consumer's input as it is fed)
+  size_t u[PP_CODEC_MAX_STAGES], ua[PP_CODEC_MAX_STAGES], ra[PP_CODEC_MAX_STAGES], ha[PP_CODEC_MAX_STAGES];
   long T[PP_CODEC_MAX_STAGES + 1];  // samples per call at each rate: T[0] = 1
   long ring_layer_elems, ring_slot_elems, ring_v_off;
   std::vector<HistSpec> hist;  // 0: conv_in, then up_i / res_a_i, then conv_out
@@ -109,12 +114,13 @@ CodecLayout make_codec_layout(const pp_codec_dims& dm, int B) {
   L.z = take((size_t)B * d * 4);
   L.T[0] = 1;
   for (int i = 0; i < dm.n_stages; ++i) L.T[i + 1] = L.T[i] * dm.strides[i];
-  L.h0 = take((size_t)B * dm.channels[0] * 4);
+  L.h0a = take((size_t)B * dm.channels[0] * 4);
   for (int i = 0; i < dm.n_stages; ++i) {
     const long co = dm.channels[i + 1], T = L.T[i + 1];
     L.u[i] = take((size_t)B * co * T * 4);
-    L.r[i] = take((size_t)B * (co / 2) * T * 4);
-    L.hs[i] = take((size_t)B * co * T * 4);
+    L.ua[i] = take((size_t)B * co * T * 4);
+    L.ra[i] = take((size_t)B * (co / 2) * T * 4);
+    L.ha[i] = take((size_t)B * co * T * 4);
   }
   L.pcm = take((size_t)B * L.T[dm.n_stages] * 4);
   auto add_hist = [&](int C, int Hh) {
@@ -336,19 +342,17 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
   c0.C_out = ch[0];
   c0.K = dm.conv_k;
   c0.stride = 1;
-  c0.act = 0;
-  c0.y = h->at<float>(L.h0);
+  c0.ya = h->at<float>(L.h0a);
   c0.B = B;
   launch_codec_conv(c0, s);
 
-  const float* hin = h->at<float>(L.h0);
+  const float* hin = h->at<float>(L.h0a);  // the current stage's input, after its ELU
   for (int i = 0; i < dm.n_stages; ++i) {
     const int ci = ch[i], co = ch[i + 1];
-    const long T = L.T[i];
     ConvArgs up{};
     up.x = hin;
     up.C_in = ci;
-    up.T_in = (int)T;
+    up.T_in = (int)L.T[i];
     up.hist = hist_in(L.h_up[i]);
     up.H = 1;
     up.w = reinterpret_cast<const bf16_t*>(w.up_w[i]);
@@ -357,13 +361,13 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     up.K = 2 * dm.strides[i];
     up.stride = dm.strides[i];
     up.transposed = 1;
-    up.act = 1;
     up.y = h->at<float>(L.u[i]);
+    up.ya = h->at<float>(L.ua[i]);
     up.B = B;
     launch_codec_conv(up, s);
 
     ConvArgs ra{};
-    ra.x = h->at<float>(L.u[i]);
+    ra.x = h->at<float>(L.ua[i]);
     ra.C_in = co;
     ra.T_in = (int)L.T[i + 1];
     ra.hist = hist_in(L.h_res[i]);
@@ -373,13 +377,12 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     ra.C_out = co / 2;
     ra.K = dm.res_k;
     ra.stride = 1;
-    ra.act = 1;
-    ra.y = h->at<float>(L.r[i]);
+    ra.ya = h->at<float>(L.ra[i]);
     ra.B = B;
     launch_codec_conv(ra, s);
 
     ConvArgs rb{};
-    rb.x = h->at<float>(L.r[i]);
+    rb.x = h->at<float>(L.ra[i]);
     rb.C_in = co / 2;
     rb.T_in = (int)L.T[i + 1];
     rb.hist = nullptr;
@@ -389,12 +392,11 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     rb.C_out = co;
     rb.K = 1;
     rb.stride = 1;
-    rb.act = 1;
     rb.skip = h->at<float>(L.u[i]);
-    rb.y = h->at<float>(L.hs[i]);
+    rb.ya = h->at<float>(L.ha[i]);
     rb.B = B;
     launch_codec_conv(rb, s);
-    hin = h->at<float>(L.hs[i]);
+    hin = h->at<float>(L.ha[i]);
   }
 
   ConvArgs cz{};
@@ -408,7 +410,6 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
   cz.C_out = 1;
   cz.K = dm.conv_k;
   cz.stride = 1;
-  cz.act = 1;
   cz.y = h->at<float>(L.pcm);
   cz.B = B;
   launch_codec_conv(cz, s);
@@ -427,11 +428,11 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     he.new_h = h->at<float>(L.hist[e].off[po]);
   };
   entry(L.h_conv_in, h->at<float>(L.z), 1);
-  const float* xin = h->at<float>(L.h0);
+  const float* xin = h->at<float>(L.h0a);
   for (int i = 0; i < dm.n_stages; ++i) {
     entry(L.h_up[i], xin, (int)L.T[i]);
-    entry(L.h_res[i], h->at<float>(L.u[i]), (int)L.T[i + 1]);
-    xin = h->at<float>(L.hs[i]);
+    entry(L.h_res[i], h->at<float>(L.ua[i]), (int)L.T[i + 1]);
+    xin = h->at<float>(L.ha[i]);
   }
   entry(L.h_conv_out, xin, (int)L.T[dm.n_stages]);
   launch_codec_hist(ha, s);

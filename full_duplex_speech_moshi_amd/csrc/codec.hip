@@ -87,68 +87,160 @@ void launch_codec_norm(const CodecNormArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Convolutions.  Output (b, o, t) = bias[o] + sum over j of w * act(input),
-// j running over (input channel i, tap): K taps for the causal form (tap k
-// reads time t - (K-1-k)), 2 for the transposed form (m = t / s, r = t % s:
-// tap r reads input m, tap r + s reads input m - 1).  Times before this
-// call's first input come from the history.  LPO lanes share one output:
-// lane l adds j = l, l + LPO, ... in order, then the LPO partial sums are
-// folded by a fixed butterfly.
+// Convolutions.  Output (b, o, t) = bias[o] + sum over input channels i and
+// taps of w * input (plus the skip), stored raw and/or after ELU; the inputs
+// arrive already activated.  A group of LPO lanes owns TT consecutive
+// outputs of one (slot, output channel): lane l takes input channels
+// l, l + LPO, ... in order, keeps the K + TT - 1 inputs its taps reach in
+// registers and the channel's K weights, then the LPO partial sums of each
+// output are folded by a fixed butterfly.  The causal form reads time
+// t - (K-1-k) at tap k; the transposed form gives each thread the `stride`
+// outputs of one input position m (output m s + r reads input m at tap r and
+// input m - 1 at tap r + s).  Times before this call's first input come from
+// the history.
 // ---------------------------------------------------------------------------
+constexpr int CONV_KMAX = 8;
+
 __device__ __forceinline__ float elu_f(float v) { return v > 0.f ? v : expm1f(v); }
 
-template <int LPO>
-__global__ __launch_bounds__(256) void codec_conv_kernel(ConvArgs a) {
-  const int T_out = a.T_in * a.stride;
-  const long n_out = (long)a.B * a.C_out * T_out;
-  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPO;
-  const int l = threadIdx.x % LPO;
-  const bool live = gid < n_out;
-  const long g = live ? gid : 0;
-  const int t = (int)(g % T_out);
-  const int o = (int)((g / T_out) % a.C_out);
-  const int b = (int)(g / ((long)T_out * a.C_out));
-  const float* xb = a.x + (long)b * a.C_in * a.T_in;
-  const float* hb = a.hist + (long)b * a.C_in * a.H;
-  const bf16_t* wo = a.w + (long)o * a.C_in * a.K;
-  float acc = 0.f;
-  if (!a.transposed) {
-    const int R = a.C_in * a.K;
-    for (int j = l; j < R; j += LPO) {
-      const int i = j / a.K, k = j - i * a.K;
-      const int u = t - (a.K - 1 - k);  // input time
-      float v = u >= 0 ? xb[(long)i * a.T_in + u] : hb[(long)i * a.H + a.H + u];
-      if (a.act) v = elu_f(v);
-      acc = __builtin_fmaf(bf2f(wo[j]), v, acc);
-    }
-  } else {
-    const int s = a.stride, m = t / s, r = t - m * s;
-    const int R = a.C_in * 2;
-    for (int j = l; j < R; j += LPO) {
-      const int i = j >> 1, e = j & 1;
-      const int u = m - e;
-      float v = u >= 0 ? xb[(long)i * a.T_in + u] : hb[(long)i * a.H + a.H - 1];
-      if (a.act) v = elu_f(v);
-      acc = __builtin_fmaf(bf2f(wo[(long)i * a.K + r + e * s]), v, acc);
+template <int LPO, int TT>
+__device__ __forceinline__ void conv_store(const ConvArgs& a, bool live, int l, int b, int o, int t0, int T_out,
+                                           float (&acc)[TT], int n) {
+#pragma unroll
+  for (int u = 0; u < TT; ++u) {
+    if (u < n) {  // n is the same for the whole group (for the whole launch unless ragged)
+#pragma unroll
+      for (int off = LPO / 2; off >= 1; off >>= 1) acc[u] += __shfl_xor(acc[u], off, LPO);
     }
   }
+  if (!live || l != 0) return;
+  const long base = ((long)b * a.C_out + o) * T_out + t0;
+  const float bo = a.bias[o];
 #pragma unroll
-  for (int off = LPO / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPO);
-  if (live && l == 0) {
-    float y = a.bias[o] + acc;
-    const long oi = ((long)b * a.C_out + o) * T_out + t;
-    if (a.skip) y += a.skip[oi];
-    a.y[oi] = y;
+  for (int u = 0; u < TT; ++u) {
+    if (u < n) {
+      float y = bo + acc[u];
+      if (a.skip) y += a.skip[base + u];
+      if (a.y) a.y[base + u] = y;
+      if (a.ya) a.ya[base + u] = elu_f(y);
+    }
   }
 }
 
+// causal convolution: TT consecutive outputs per group
+template <int LPO, int TT>
+__global__ __launch_bounds__(256) void codec_conv_kernel(ConvArgs a) {
+  const int T = a.T_in, nt = (T + TT - 1) / TT;
+  const long n_grp = (long)a.B * a.C_out * nt;
+  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPO;
+  const int l = threadIdx.x % LPO;
+  const bool live = gid < n_grp;
+  const long g = live ? gid : 0;
+  const int t0 = (int)(g % nt) * TT;
+  const int o = (int)((g / nt) % a.C_out);
+  const int b = (int)(g / ((long)nt * a.C_out));
+  const int K = a.K;
+  float acc[TT];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) acc[u] = 0.f;
+#pragma unroll 2
+  for (int i = l; i < a.C_in; i += LPO) {
+    const float* xi = a.x + ((long)b * a.C_in + i) * T;
+    const float* hi = a.hist ? a.hist + ((long)b * a.C_in + i) * a.H : nullptr;
+    const bf16_t* wi = a.w + ((long)o * a.C_in + i) * K;
+    // inputs t0 - (K-1) .. t0 + TT - 1
+    float xv[CONV_KMAX - 1 + TT];
+    float wv[CONV_KMAX];
+#pragma unroll
+    for (int k = 0; k < CONV_KMAX; ++k) wv[k] = k < K ? bf2f(wi[k]) : 0.f;
+#pragma unroll
+    for (int j = 0; j < CONV_KMAX - 1 + TT; ++j) {
+      const int tt = t0 - (K - 1) + j;
+      xv[j] = j >= K - 1 + TT ? 0.f : tt >= T ? 0.f : tt >= 0 ? xi[tt] : hi[a.H + tt];
+    }
+#pragma unroll
+    for (int k = 0; k < CONV_KMAX; ++k) {
+      if (k < K) {
+#pragma unroll
+        for (int u = 0; u < TT; ++u) acc[u] = __builtin_fmaf(wv[k], xv[u + k], acc[u]);
+      }
+    }
+  }
+  conv_store<LPO, TT>(a, live, l, b, o, t0, T, acc, T - t0);
+}
+
+// transposed convolution: the `stride` outputs of one input position per group
+template <int LPO>
+__global__ __launch_bounds__(256) void codec_convt_kernel(ConvArgs a) {
+  const int s = a.stride, T = a.T_in, T_out = T * s;
+  const long n_grp = (long)a.B * a.C_out * T;
+  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPO;
+  const int l = threadIdx.x % LPO;
+  const bool live = gid < n_grp;
+  const long g = live ? gid : 0;
+  const int m = (int)(g % T);
+  const int o = (int)((g / T) % a.C_out);
+  const int b = (int)(g / ((long)T * a.C_out));
+  float acc[CONV_KMAX];
+#pragma unroll
+  for (int r = 0; r < CONV_KMAX; ++r) acc[r] = 0.f;
+#pragma unroll 2
+  for (int i = l; i < a.C_in; i += LPO) {
+    const float* xi = a.x + ((long)b * a.C_in + i) * T;
+    const float x0 = xi[m];
+    const float x1 = m > 0 ? xi[m - 1] : a.hist[((long)b * a.C_in + i) * a.H + a.H - 1];
+    const bf16_t* wi = a.w + ((long)o * a.C_in + i) * a.K;
+#pragma unroll
+    for (int r = 0; r < CONV_KMAX; ++r) {
+      if (r < s) acc[r] = __builtin_fmaf(bf2f(wi[r + s]), x1, __builtin_fmaf(bf2f(wi[r]), x0, acc[r]));
+    }
+  }
+  conv_store<LPO, CONV_KMAX>(a, live, l, b, o, m * s, T_out, acc, s);
+}
+
+// Enough lanes for the part (256 CUs x 4 SIMDs x 2 waves of 64).
+constexpr long CONV_LANES = 1L << 17;
+
+template <int LPO>
+static void launch_conv_lpo(const ConvArgs& a, hipStream_t s, int tt) {
+  const long groups = (long)a.B * a.C_out * (a.transposed ? a.T_in : (a.T_in + tt - 1) / tt);
+  const dim3 grid((unsigned)((groups * LPO + 255) / 256));
+  if (a.transposed) {
+    hipLaunchKernelGGL(codec_convt_kernel<LPO>, grid, dim3(256), 0, s, a);
+    return;
+  }
+  switch (tt) {
+    case 8: hipLaunchKernelGGL((codec_conv_kernel<LPO, 8>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((codec_conv_kernel<LPO, 4>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((codec_conv_kernel<LPO, 2>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((codec_conv_kernel<LPO, 1>), grid, dim3(256), 0, s, a); break;
+  }
+}
+
+// Launch shape: the fewest lanes per output group (1, 8 or 64, at most the
+// input channels) that still gives CONV_LANES lanes, else the most; then, for
+// the causal form, the most outputs per group (8, 4, 2 or 1, at most the
+// samples of the call) that keeps CONV_LANES lanes.  Fewer lanes per group
+// fold fewer partial sums; more outputs per group re-read fewer inputs.
 void launch_codec_conv(const ConvArgs& a, hipStream_t s) {
-  const long n_out = (long)a.B * a.C_out * a.T_in * a.stride;
-  const int R = a.C_in * (a.transposed ? 2 : a.K);
-  auto blocks = [&](int lpo) { return dim3((unsigned)((n_out * lpo + 255) / 256)); };
-  if (R >= 1024) hipLaunchKernelGGL(codec_conv_kernel<64>, blocks(64), dim3(256), 0, s, a);
-  else if (R >= 128) hipLaunchKernelGGL(codec_conv_kernel<8>, blocks(8), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(codec_conv_kernel<1>, blocks(1), dim3(256), 0, s, a);
+  const long outs = (long)a.B * a.C_out * a.T_in;  // groups of one output (or one input position)
+  int lpo = 1;
+  for (int c : {1, 8, 64}) {
+    if (c > 1 && a.C_in < c) break;
+    lpo = c;
+    if (outs * c >= CONV_LANES) break;
+  }
+  int tt = 1;
+  if (!a.transposed)
+    for (int c : {8, 4, 2}) {
+      if (c <= a.T_in && (long)a.B * a.C_out * ((a.T_in + c - 1) / c) * lpo >= CONV_LANES) {
+        tt = c;
+        break;
+      }
+    }
+  if (lpo == 64) launch_conv_lpo<64>(a, s, tt);
+  else if (lpo == 8) launch_conv_lpo<8>(a, s, tt);
+  else launch_conv_lpo<1>(a, s, tt);
 }
 
 // ---------------------------------------------------------------------------

@@ -39,20 +39,21 @@ struct CodecNormArgs {
 };
 void launch_codec_norm(const CodecNormArgs& a, hipStream_t s);
 
-// One convolution.  transposed = 0: causal convolution of kernel K (stride
-// 1); transposed = 1: causal transposed convolution with stride `stride` and
-// K = 2 stride.  Input x [B][C_in][T_in] with history hist [B][C_in][H]
-// (H = K - 1 for the causal form, 1 for the transposed form); act = 1
-// applies ELU to every input read (history included).  Output y
-// [B][C_out][T_out], T_out = T_in * stride, plus skip [B][C_out][T_out] when
-// given.
+// One convolution.  transposed = 0: causal convolution of kernel K <= 8
+// (stride 1); transposed = 1: causal transposed convolution with stride
+// `stride` <= 8 and K = 2 stride.  Input x [B][C_in][T_in] with its history
+// hist [B][C_in][H] (H = K - 1 for the causal form, 1 for the transposed
+// form); both already hold the layer's input as it is fed (after its ELU).
+// Output [B][C_out][T_out], T_out = T_in * stride: bias + sum, plus skip
+// [B][C_out][T_out] when given, stored raw into y and/or after ELU into ya
+// (either may be null).
 struct ConvArgs {
   const float* x; int C_in, T_in;
   const float* hist; int H;
   const bf16_t* w; const float* bias; int C_out, K, stride, transposed;
-  int act;
   const float* skip;
   float* y;
+  float* ya;
   int B;
 };
 void launch_codec_conv(const ConvArgs& a, hipStream_t s);

@@ -65,10 +65,10 @@ typedef struct pp_codec_dims {
   int32_t d;          /* latent and transformer width (a multiple of 32) */
   int32_t n_layers, n_heads, ffn;   /* transformer; head_dim = d / n_heads in {32, 64, 128}; ffn % 32 == 0 */
   int32_t window;     /* frames the attention sees, 1..PP_CODEC_MAX_WINDOW */
-  int32_t conv_k;     /* kernel of the first and the last convolution (>= 1) */
-  int32_t res_k;      /* kernel of each residual unit's first convolution (>= 1) */
+  int32_t conv_k;     /* kernel of the first and the last convolution (1..8) */
+  int32_t res_k;      /* kernel of each residual unit's first convolution (1..8) */
   int32_t n_stages;   /* 1..PP_CODEC_MAX_STAGES */
-  int32_t strides[PP_CODEC_MAX_STAGES];       /* each >= 1 */
+  int32_t strides[PP_CODEC_MAX_STAGES];       /* each 1..8 */
   int32_t channels[PP_CODEC_MAX_STAGES + 1];  /* channels[0] after the first convolution, then after each
                                                  stage; channels[i] for i >= 1 even */
   float norm_eps;

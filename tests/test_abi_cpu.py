@@ -59,7 +59,8 @@ def test_codec_dims_validated_on_the_host(lib):
     from full_duplex_speech_moshi_amd import codec
     assert codec.pp_codec_samples(codec.make_codec_dims(synth.CODEC)) == 1920
     assert codec.pp_codec_samples(codec.make_codec_dims(synth.CODEC_TINY)) == 24
-    bad = [dict(n_heads=3), dict(d=500), dict(window=257), dict(strides=(0, 2)), dict(channels=(8, 5, 4)),
+    bad = [dict(n_heads=3), dict(d=500), dict(window=257), dict(strides=(0, 2)), dict(strides=(9, 2)),
+           dict(conv_k=9), dict(channels=(8, 5, 4)),
            dict(n_q=17), dict(ffn=100)]
     for kw in bad:
         cd = dataclasses.replace(synth.CODEC_TINY, **kw)

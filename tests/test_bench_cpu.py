@@ -135,3 +135,15 @@ def test_dominant_kernel_is_the_largest_per_tick():
     # a one-layer model: the text head's single launch can win
     assert bench.dominant_kernel({"gate_up": {"ms": 0.03}, "text_head": {"ms": 0.045}}, 1) == "text_head"
     assert set(bench.KERNEL_LABELS) >= set(kern)
+
+
+def test_codec_call_bytes_are_the_weights_rows_and_caches():
+    # every weight of the manifest once (codebooks excepted: one row per
+    # codebook per slot), plus each slot's keys and values over the window
+    w = synth.make_codec_weights(synth.CODEC_TINY, seed=0)
+    cd = synth.CODEC_TINY
+    weights = sum(v.nbytes for k, v in w.items() if not k.startswith("codebook."))
+    for B, n in ((1, 1), (3, cd.window)):
+        rows = B * cd.n_q * cd.d * 2
+        cache = B * cd.n_layers * 2 * n * cd.d * 2
+        assert bench.codec_call_bytes(cd, B, n) == weights + rows + cache
