@@ -244,6 +244,29 @@ def codec_manifest(cd: CodecDims):
               (f"res.{i}.b.b", (co,), "bias", 0.01)]
     m += [("conv_out.w", (1, c[-1], cd.conv_k), "bf16", 1.0 / np.sqrt(c[-1] * cd.conv_k)),
           ("conv_out.b", (1,), "bias", 0.01)]
+    # the encoder mirrors the decoder: stage j runs at the channels and the
+    # stride of decoder stage n - 1 - j, downsampling where that one upsamples
+    n = len(cd.strides)
+    m += [("enc.conv_in.w", (c[-1], 1, cd.conv_k), "bf16", 1.0 / np.sqrt(cd.conv_k)),
+          ("enc.conv_in.b", (c[-1],), "bias", 0.01)]
+    for j in range(n):
+        ci, co, st = c[n - j], c[n - 1 - j], cd.strides[n - 1 - j]
+        m += [(f"enc.res.{j}.a.w", (ci // 2, ci, cd.res_k), "bf16", 1.0 / np.sqrt(ci * cd.res_k)),
+              (f"enc.res.{j}.a.b", (ci // 2,), "bias", 0.01),
+              (f"enc.res.{j}.b.w", (ci, ci // 2, 1), "bf16", 0.5 / np.sqrt(ci // 2)),
+              (f"enc.res.{j}.b.b", (ci,), "bias", 0.01),
+              (f"enc.down.{j}.w", (co, ci, 2 * st), "bf16", 1.0 / np.sqrt(2 * st * ci)),
+              (f"enc.down.{j}.b", (co,), "bias", 0.01)]
+    m += [("enc.conv_out.w", (d, c[0], cd.conv_k), "bf16", 1.0 / np.sqrt(c[0] * cd.conv_k)),
+          ("enc.conv_out.b", (d,), "bias", 0.01)]
+    for l in range(cd.n_layers):
+        m += [(f"enc.layers.{l}.attn_norm", (d,), "alpha", 0.0),
+              (f"enc.layers.{l}.wqkv", (3 * d, d), "bf16", 0.02),
+              (f"enc.layers.{l}.wo", (d, d), "bf16", 0.02),
+              (f"enc.layers.{l}.mlp_norm", (d,), "alpha", 0.0),
+              (f"enc.layers.{l}.w_in", (2 * F, d), "bf16", 0.02),
+              (f"enc.layers.{l}.w_out", (d, F), "bf16", 0.02)]
+    m.append(("enc.out_norm", (d,), "alpha", 0.0))
     return m
 
 
@@ -265,6 +288,21 @@ def make_codec_weights(cd: CodecDims, seed: int = 0) -> dict:
     its own child stream."""
     return {name: _make_codec_tensor(seed, i, shp, kind, scale)
             for i, (name, shp, kind, scale) in enumerate(codec_manifest(cd))}
+
+
+def user_audio(seed: int, n_frames: int, samples: int = 1920) -> np.ndarray:
+    """Synthetic 24 kHz user audio, fp32 [n_frames, samples]: a sum of three
+    sinusoids at seeded frequencies (80-1000 Hz) and phases, amplitude 0.3
+    each, plus N(0, 0.01) noise; speech-like in level and band, not in
+    content."""
+    rng = _rng(seed)
+    t = np.arange(n_frames * samples, dtype=np.float64) / 24000.0
+    x = np.zeros_like(t)
+    for _ in range(3):
+        f, ph = rng.uniform(80.0, 1000.0), rng.uniform(0.0, 2 * np.pi)
+        x += 0.3 * np.sin(2 * np.pi * f * t + ph)
+    x += rng.normal(0.0, 0.01, t.size)
+    return x.astype(np.float32).reshape(n_frames, samples)
 
 
 def agent_frames(seed: int, n_frames: int, card: int = 2048) -> np.ndarray:

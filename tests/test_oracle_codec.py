@@ -189,3 +189,169 @@ def test_conv_stack_closed_form():
             v = (np.expm1(v) if v <= 0 else v) + b_up[i] + beta[i]
         v = np.expm1(v) if v <= 0 else v
         np.testing.assert_allclose(pcm, np.full(CD.samples, v), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- the encoder
+
+@pytest.mark.parametrize("s", [2, 4, 5, 8])
+def test_strided_conv_matches_torch(s):
+    rng = np.random.default_rng(10 + s)
+    ci, co, To = 3, 4, 5
+    x, w, b = rng.normal(size=(ci, To * s)), rng.normal(size=(co, ci, 2 * s)), rng.normal(size=co)
+    # causal: left padding K - s, stride s
+    ref = torch.nn.functional.conv1d(torch.nn.functional.pad(torch.tensor(x)[None], (s, 0)), torch.tensor(w),
+                                     torch.tensor(b), stride=s)[0].numpy()
+    y = codec.strided_conv_causal(x, w, b, np.zeros((ci, s)), s)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # a history is the s inputs before x
+    h = rng.normal(size=(ci, s))
+    full = np.concatenate([h, x], axis=1)
+    ref2 = torch.nn.functional.conv1d(torch.nn.functional.pad(torch.tensor(full)[None], (s, 0)), torch.tensor(w),
+                                      torch.tensor(b), stride=s)[0].numpy()[:, 1:]
+    np.testing.assert_allclose(codec.strided_conv_causal(x, w, b, h, s), ref2, rtol=1e-12, atol=1e-12)
+
+
+def test_nearest_is_brute_force_with_lowest_index_on_ties():
+    rng = np.random.default_rng(4)
+    table = rng.normal(size=(40, 6))
+    table[17] = table[5]            # an exact tie: index 5 must win
+    for trial in range(50):
+        r = rng.normal(size=6) if trial else table[5] + 1e-3
+        best, bd = None, None
+        for j in range(len(table)):
+            dj = sum((table[j][i] - r[i]) ** 2 for i in range(6))
+            if bd is None or dj < bd:
+                best, bd = j, dj
+        assert codec.nearest(r, table)[0] == best
+
+
+def test_quantiser_closed_form():
+    """Codebooks built so that z = C_0[a] + C_1[b] exactly, codebook 0 coarse
+    (rows of scale 1) and codebook 1 fine (scale 0.05), and codebooks 2..7
+    each hold an exact zero row (index z_q), a copy of C_0[a] (index 77) and
+    otherwise rows far away: the codes are (a, b, z_2, ..., z_7) only if each
+    stage quantises what the stages before it left."""
+    cd = CD
+    w = synth.make_codec_weights(cd, seed=0)
+    rng = np.random.default_rng(5)
+    a, b = 700, 1234
+    zq = [3, 2047, 0, 555, 1024, 9]
+    tabs = []
+    for q in range(cd.n_q):
+        t = rng.normal(size=(cd.card, cd.d)).astype(np.float32) * (1.0 if q == 0 else 0.05)
+        if q >= 2:
+            t += 10.0                      # far from any residual left after two stages
+            t[zq[q - 2]] = 0.0
+            t[77] = tabs[0][a]
+        tabs.append(synth.bf16_bits_to_f32(_bits(t)))
+        w[f"codebook.{q}"] = _bits(t)
+    z = tabs[0][a].astype(np.float64) + tabs[1][b]
+    o = codec.CodecOracle(cd, w, 1, np.float64)
+    np.testing.assert_array_equal(o.quantise(z), [a, b] + zq)
+
+
+def test_encoder_output_norm_is_its_own():
+    """With every layer's updates zero (out- and down-projections zero), the
+    encoder's transformer output is the RMS-normalised latent scaled by the
+    encoder's output-norm alpha, not the decoder's: the two alphas are set to
+    0.5 and 2 and the ratio z / (y / rms(y)) must be 0.5 everywhere."""
+    w = synth.make_codec_weights(CD, seed=9)
+    for l in range(CD.n_layers):
+        for k in ("wo", "w_out"):
+            w[f"enc.layers.{l}.{k}"] = _bits(np.zeros(w[f"enc.layers.{l}.{k}"].shape))
+    w["enc.out_norm"] = np.full(CD.d, 0.5, np.float32)
+    w["out_norm"] = np.full(CD.d, 2.0, np.float32)
+    o = codec.CodecOracle(CD, w, 1, np.float64)
+    y = np.random.default_rng(12).normal(size=CD.d)
+    z = o.transformer(o.enc_slots[0], y.copy(), "enc.")
+    rms = np.sqrt(np.mean(y ** 2) + CD.norm_eps)
+    np.testing.assert_allclose(z / (y / rms), 0.5, rtol=1e-12)
+
+
+def test_encoder_streaming_equals_whole_sequence_and_reset_is_fresh():
+    w = synth.make_codec_weights(CD, seed=6)
+    n = 2 * CD.window + 3
+    pcm = synth.user_audio(7, n, CD.samples)
+    other = synth.user_audio(8, 5, CD.samples)
+    o = codec.CodecOracle(CD, w, 2, np.float64)
+    got = [o.encode(np.stack([pcm[t], other[t % 5]]))[0] for t in range(n)]
+    ref = codec.encode_sequence(CD, w, pcm.reshape(-1), np.float64)
+    np.testing.assert_array_equal(np.stack(got), ref)
+    o.reset(1)
+    got = [o.encode(np.stack([other[0], pcm[t]]))[1] for t in range(6)]
+    np.testing.assert_array_equal(np.stack(got), ref[:6])
+
+
+def test_encoder_transformer_is_the_temporal_block():
+    cw = synth.make_codec_weights(CD, seed=7)
+    dm = synth.Dims(d=CD.d, n_layers=CD.n_layers, n_heads=CD.n_heads, ffn=CD.ffn, text_card=64,
+                    audio_card=64, n_q=8, dep_d=32, dep_layers=1, dep_heads=1, dep_ffn=32, dep_q=16,
+                    norm_eps=CD.norm_eps, rope_base=CD.rope_base)
+    tw = synth.make_weights(dm, seed=2)
+    for l in range(CD.n_layers):
+        for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "w_in", "w_out"):
+            tw[f"layers.{l}.{k}"] = cw[f"enc.layers.{l}.{k}"]
+    n = CD.window + 3
+    xs = np.random.default_rng(10).normal(size=(n, CD.d))
+    t = tick.Oracle(dm, tw, 1, CD.window, dtype=np.float64)
+    t.prefill_embed(0, xs)
+    o = codec.CodecOracle(CD, cw, 1, np.float64)
+    st = o.enc_slots[0]
+    for i in range(n):
+        t.step(np.zeros((1, 8), np.int64))
+        got = o.blocks(st, xs[i].copy(), "enc.")
+        st.pos += 1
+        np.testing.assert_allclose(got, t.taps["hidden"][-1, 0], rtol=1e-12, atol=1e-12, err_msg=f"frame {i}")
+
+
+def test_encoder_conv_stack_closed_form():
+    """Pass-through weights: the first convolution takes the current sample
+    plus beta_in, each residual unit adds only its second bias beta_j, each
+    strided convolution takes channel 0 of its ELU'd input at its last tap
+    (the last sample of its block) plus b_j, the last convolution takes
+    channel 0 plus b_out.  The latent's channel 0 for frame f is then
+    elu(v_n) + b_out with v_0 = x[last sample of frame f] + beta_in and
+    v_{j+1} = elu(v_j + beta_j) + b_j."""
+    w = synth.make_codec_weights(CD, seed=8)
+    c, n = CD.channels, len(CD.strides)
+    rng = np.random.default_rng(11)
+
+    def onehot(shape, taps):
+        a = np.zeros(shape, np.float32)
+        for k in taps:
+            a[0, 0, k] = 1.0
+        return _bits(a)
+
+    def bias(m, v):
+        b = np.zeros(m, np.float32)
+        b[0] = v
+        return b
+
+    f32 = lambda v: float(np.float32(v))
+    b_in = f32(0.125)
+    w["enc.conv_in.w"] = onehot(w["enc.conv_in.w"].shape, [CD.conv_k - 1])
+    w["enc.conv_in.b"] = bias(c[-1], b_in)
+    beta, bd = [], []
+    for j in range(n):
+        ci = c[n - j]
+        w[f"enc.res.{j}.b.w"] = _bits(np.zeros(w[f"enc.res.{j}.b.w"].shape))
+        beta.append(f32(rng.normal() * 0.5))
+        w[f"enc.res.{j}.b.b"] = bias(ci, beta[-1])
+        K = w[f"enc.down.{j}.w"].shape[2]
+        w[f"enc.down.{j}.w"] = onehot(w[f"enc.down.{j}.w"].shape, [K - 1])
+        bd.append(f32(rng.normal() * 0.5))
+        w[f"enc.down.{j}.b"] = bias(c[n - 1 - j], bd[-1])
+    b_out = f32(-0.25)
+    w["enc.conv_out.w"] = onehot(w["enc.conv_out.w"].shape, [CD.conv_k - 1])
+    w["enc.conv_out.b"] = bias(CD.d, b_out)
+    o = codec.CodecOracle(CD, w, 1, np.float64)
+    pcm = synth.user_audio(12, 4, CD.samples)
+    for t in range(4):
+        y = o.enc_convs(o.enc_slots[0], pcm[t].astype(np.float64))
+        v = float(pcm[t][-1]) + b_in
+        for j in range(n):
+            u = v + beta[j]
+            v = (u if u > 0 else np.expm1(u)) + bd[j]
+        v = (v if v > 0 else np.expm1(v)) + b_out
+        np.testing.assert_allclose(y[0], v, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(y[1:], 0.0, atol=0)
