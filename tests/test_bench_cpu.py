@@ -142,7 +142,7 @@ def test_codec_call_bytes_are_the_weights_rows_and_caches():
     # codebook per slot), plus each slot's keys and values over the window
     w = synth.make_codec_weights(synth.CODEC_TINY, seed=0)
     cd = synth.CODEC_TINY
-    weights = sum(v.nbytes for k, v in w.items() if not k.startswith("codebook."))
+    weights = sum(v.nbytes for k, v in w.items() if not k.startswith(("codebook.", "enc.")))  # the decoder's
     for B, n in ((1, 1), (3, cd.window)):
         rows = B * cd.n_q * cd.d * 2
         cache = B * cd.n_layers * 2 * n * cd.d * 2
