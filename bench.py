@@ -273,6 +273,26 @@ def codec_call_bytes(cd, B: int, n_keys: int) -> int:
     return 2 * (mats + conv) + 4 * (norms + bias) + B * per_slot
 
 
+def codec_encode_bytes(cd, B: int, n_keys: int) -> int:
+    """Bytes one encode call must move at least: every encoder weight once,
+    every codebook once (each quantiser stage scores its whole codebook),
+    each slot's samples, and each slot's stored keys and values over n_keys
+    frames."""
+    d, F, L = cd.d, cd.ffn, cd.n_layers
+    mats = L * (3 * d * d + d * d + 2 * F * d + d * F)
+    c, n = cd.channels, len(cd.strides)
+    conv = c[-1] * cd.conv_k + d * c[0] * cd.conv_k
+    bias = c[-1] + d
+    for j in range(n):
+        ci, co, st = c[n - j], c[n - 1 - j], cd.strides[n - 1 - j]
+        conv += (ci // 2) * ci * cd.res_k + ci * (ci // 2) + co * ci * 2 * st
+        bias += ci // 2 + ci + co
+    norms = (2 * L + 1) * d
+    books = cd.n_q * cd.card * d
+    per_slot = cd.samples * 4 + L * 2 * n_keys * d * 2
+    return 2 * (mats + conv + books) + 4 * (norms + bias) + B * per_slot
+
+
 def run_codec(args):
     """The codec decoder on its own: B slots (default 32), the window filled
     by warm-up calls, then timed calls of pp_codec_decode (host clock per
@@ -299,14 +319,30 @@ def run_codec(args):
         e.decode(c)
         ms[t] = (time.perf_counter() - t0) * 1e3
     dev_ms = e.time(20)
+    # the encoder on the same handle: user audio, the window filled likewise
+    pcm = [synth.user_audio(90 + b, WU + K, cd.samples) for b in range(B)]
+    for t in range(WU):
+        e.encode(np.stack([pcm[b][t] for b in range(B)]))
+    torch.cuda.synchronize()
+    ems = np.empty(K)
+    for t in range(K):
+        x = np.stack([pcm[b][WU + t] for b in range(B)])
+        t0 = time.perf_counter()
+        e.encode(x)
+        ems[t] = (time.perf_counter() - t0) * 1e3
+    enc_dev_ms = e.time_encode(20)
     e.close()
     by = codec_call_bytes(cd, B, cd.window)
+    eby = codec_encode_bytes(cd, B, cd.window)
     return {"metric": "decoded frames/sec (codec, 1920 samples per frame)", "value": B * K / (ms.sum() / 1e3),
             "unit": "frames/s", "steps": K, "warmup": WU, "p50_call_ms": float(np.median(ms)),
             "device_call_ms": dev_ms, "call_bytes": by, "call_hbm_frac": by / (dev_ms * 1e-3) / (PEAK_HBM_GBS * 1e9),
-            "config": {"workload": f"codec decoder (d {cd.d}, {cd.n_layers} layers, strides {list(cd.strides)}), "
-                                   f"B={B}, window of {cd.window} frames filled by {WU} warm-up calls, then {K} "
-                                   f"timed calls", "B": B}}
+            "encode": {"metric": "encoded frames/sec (1920 samples per frame)", "value": B * K / (ems.sum() / 1e3),
+                       "unit": "frames/s", "p50_call_ms": float(np.median(ems)), "device_call_ms": enc_dev_ms,
+                       "call_bytes": eby, "call_hbm_frac": eby / (enc_dev_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)},
+            "config": {"workload": f"codec decoder and encoder (d {cd.d}, {cd.n_layers} layers each, strides "
+                                   f"{list(cd.strides)}), B={B}, window of {cd.window} frames filled by {WU} "
+                                   f"warm-up calls, then {K} timed calls, each direction", "B": B}}
 
 
 def run_sub_codec(args):

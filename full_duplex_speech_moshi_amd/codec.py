@@ -1,7 +1,7 @@
-"""Python binding of the streaming codec decoder in libpp.so (include/codec.h):
-the C entry points under the same names, plus a CodecEngine that owns the
-device buffers (torch tensors) a handle needs.  Argument marshalling only:
-every step of the decode runs in the library's HIP kernels."""
+"""Python binding of the streaming codec (decoder and encoder) in libpp.so
+(include/codec.h): the C entry points under the same names, plus a
+CodecEngine that owns the device buffers (torch tensors) a handle needs.
+Argument marshalling only: every step runs in the library's HIP kernels."""
 from __future__ import annotations
 
 import ctypes
@@ -14,8 +14,9 @@ PP_CODEC_MAX_STAGES = 6
 PP_CODEC_MAX_BATCH = 32
 PP_CODEC_MAX_WINDOW = 256
 
-EXPORTS = ("pp_codec_samples", "pp_codec_arena_bytes", "pp_codec_create", "pp_codec_decode", "pp_codec_reset",
-           "pp_codec_time", "pp_codec_taps", "pp_codec_destroy", "pp_codec_last_error")
+EXPORTS = ("pp_codec_samples", "pp_codec_arena_bytes", "pp_codec_create", "pp_codec_decode", "pp_codec_encode",
+           "pp_codec_reset", "pp_codec_time", "pp_codec_time_encode", "pp_codec_taps", "pp_codec_destroy",
+           "pp_codec_last_error")
 
 _S = PP_CODEC_MAX_STAGES
 
@@ -33,13 +34,21 @@ CODEC_STAGE_FIELDS = ("up_w", "up_b", "res_a_w", "res_a_b", "res_b_w", "res_b_b"
 
 
 class PPCodecTaps(ctypes.Structure):
-    _fields_ = [("ring", ctypes.c_void_p), ("z", ctypes.c_void_p)]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("ring", "z", "enc_ring", "enc_y", "enc_z")]
+
+
+ENC_STAGE_FIELDS = ("enc_res_a_w", "enc_res_a_b", "enc_res_b_w", "enc_res_b_b", "enc_down_w", "enc_down_b")
+ENC_TAIL_FIELDS = ("enc_conv_out_w", "enc_conv_out_b", "enc_attn_norm", "enc_wqkv", "enc_wo", "enc_mlp_norm",
+                   "enc_w_in", "enc_w_out", "enc_out_norm")
 
 
 class PPCodecWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in CODEC_WEIGHT_FIELDS] + \
                [(n, ctypes.c_void_p * _S) for n in CODEC_STAGE_FIELDS] + \
-               [("conv_out_w", ctypes.c_void_p), ("conv_out_b", ctypes.c_void_p)]
+               [("conv_out_w", ctypes.c_void_p), ("conv_out_b", ctypes.c_void_p),
+                ("enc_conv_in_w", ctypes.c_void_p), ("enc_conv_in_b", ctypes.c_void_p)] + \
+               [(n, ctypes.c_void_p * _S) for n in ENC_STAGE_FIELDS] + \
+               [(n, ctypes.c_void_p) for n in ENC_TAIL_FIELDS]
 
 
 _ready = False
@@ -55,6 +64,8 @@ def _lib() -> ctypes.CDLL:
         lib.pp_codec_create.argtypes = [ctypes.POINTER(PPCodecDims), I, ctypes.POINTER(PPCodecWeights), P, SZ, P,
                                         ctypes.POINTER(P)]
         lib.pp_codec_decode.argtypes = [P, P, P]
+        lib.pp_codec_encode.argtypes = [P, P, P]
+        lib.pp_codec_time_encode.argtypes = [P, I, ctypes.POINTER(ctypes.c_float)]
         lib.pp_codec_reset.argtypes = [P, I]
         lib.pp_codec_time.argtypes = [P, I, ctypes.POINTER(ctypes.c_float)]
         lib.pp_codec_taps.argtypes = [P, ctypes.POINTER(PPCodecTaps)]
@@ -111,6 +122,19 @@ def pp_codec_decode(h: int, codes, B: int, n_q: int, samples: int) -> np.ndarray
     return pcm
 
 
+def pp_codec_encode(h: int, pcm, B: int, n_q: int, samples: int) -> np.ndarray:
+    x = np.ascontiguousarray(pcm, dtype=np.float32).reshape(B, samples)
+    codes = np.empty((B, n_q), np.int32)
+    _check(_lib().pp_codec_encode(h, x.ctypes.data, codes.ctypes.data), h)
+    return codes
+
+
+def pp_codec_time_encode(h: int, iters: int) -> float:
+    ms = ctypes.c_float()
+    _check(_lib().pp_codec_time_encode(h, iters, ctypes.byref(ms)), h)
+    return ms.value
+
+
 def pp_codec_reset(h: int, slot: int) -> None:
     _check(_lib().pp_codec_reset(h, slot), h)
 
@@ -145,25 +169,26 @@ def upload_codec_weights(cd, w: dict, device):
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else np.ascontiguousarray(a)).to(device)
 
     t["codebooks"] = dev(np.stack([w[f"codebook.{q}"] for q in range(cd.n_q)]))
-    for k in ("attn_norm", "mlp_norm"):
-        t[k] = dev(np.stack([w[f"layers.{l}.{k}"] for l in range(cd.n_layers)]))
     shapes = {"wqkv": (3 * cd.d, cd.d), "wo": (cd.d, cd.d), "w_in": (2 * cd.ffn, cd.d), "w_out": (cd.d, cd.ffn)}
-    for k, (M, K) in shapes.items():
-        pe = pp.pp_packed_elems(M, K)
-        out = torch.empty(cd.n_layers * pe, dtype=torch.int16, device=device)
-        for l in range(cd.n_layers):
-            src = dev(w[f"layers.{l}.{k}"])
-            pp.pp_pack_matrix(src.data_ptr(), M, K, out.data_ptr() + 2 * l * pe, stream.cuda_stream)
-            stream.synchronize()
-        t[k] = out
-    t["out_norm"] = dev(w["out_norm"])
-    for k in ("conv_in.w", "conv_in.b", "conv_out.w", "conv_out.b"):
+    for pre in ("", "enc."):
+        for k in ("attn_norm", "mlp_norm"):
+            t[pre + k] = dev(np.stack([w[f"{pre}layers.{l}.{k}"] for l in range(cd.n_layers)]))
+        for k, (M, K) in shapes.items():
+            pe = pp.pp_packed_elems(M, K)
+            out = torch.empty(cd.n_layers * pe, dtype=torch.int16, device=device)
+            for l in range(cd.n_layers):
+                src = dev(w[f"{pre}layers.{l}.{k}"])
+                pp.pp_pack_matrix(src.data_ptr(), M, K, out.data_ptr() + 2 * l * pe, stream.cuda_stream)
+                stream.synchronize()
+            t[pre + k] = out
+        t[pre + "out_norm"] = dev(w[pre + "out_norm"])
+    for k in ("conv_in.w", "conv_in.b", "conv_out.w", "conv_out.b", "enc.conv_in.w", "enc.conv_in.b",
+              "enc.conv_out.w", "enc.conv_out.b"):
         t[k] = dev(w[k])
     for i in range(len(cd.strides)):
         for k in ("w", "b"):
-            t[f"up.{i}.{k}"] = dev(w[f"up.{i}.{k}"])
-            t[f"res.{i}.a.{k}"] = dev(w[f"res.{i}.a.{k}"])
-            t[f"res.{i}.b.{k}"] = dev(w[f"res.{i}.b.{k}"])
+            for name in (f"up.{i}", f"res.{i}.a", f"res.{i}.b", f"enc.res.{i}.a", f"enc.res.{i}.b", f"enc.down.{i}"):
+                t[f"{name}.{k}"] = dev(w[f"{name}.{k}"])
     torch.cuda.synchronize(device)
     p = PPCodecWeights()
     for k in ("codebooks", "attn_norm", "wqkv", "wo", "mlp_norm", "w_in", "w_out", "out_norm"):
@@ -174,6 +199,13 @@ def upload_codec_weights(cd, w: dict, device):
         p.up_w[i], p.up_b[i] = t[f"up.{i}.w"].data_ptr(), t[f"up.{i}.b"].data_ptr()
         p.res_a_w[i], p.res_a_b[i] = t[f"res.{i}.a.w"].data_ptr(), t[f"res.{i}.a.b"].data_ptr()
         p.res_b_w[i], p.res_b_b[i] = t[f"res.{i}.b.w"].data_ptr(), t[f"res.{i}.b.b"].data_ptr()
+        p.enc_res_a_w[i], p.enc_res_a_b[i] = t[f"enc.res.{i}.a.w"].data_ptr(), t[f"enc.res.{i}.a.b"].data_ptr()
+        p.enc_res_b_w[i], p.enc_res_b_b[i] = t[f"enc.res.{i}.b.w"].data_ptr(), t[f"enc.res.{i}.b.b"].data_ptr()
+        p.enc_down_w[i], p.enc_down_b[i] = t[f"enc.down.{i}.w"].data_ptr(), t[f"enc.down.{i}.b"].data_ptr()
+    p.enc_conv_in_w, p.enc_conv_in_b = t["enc.conv_in.w"].data_ptr(), t["enc.conv_in.b"].data_ptr()
+    p.enc_conv_out_w, p.enc_conv_out_b = t["enc.conv_out.w"].data_ptr(), t["enc.conv_out.b"].data_ptr()
+    for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "w_in", "w_out", "out_norm"):
+        setattr(p, "enc_" + k, t["enc." + k].data_ptr())
     return t, p
 
 
@@ -203,6 +235,12 @@ class CodecEngine:
     def decode(self, codes) -> np.ndarray:
         return pp_codec_decode(self.h, codes, self.B, self.cd.n_q, self.samples)
 
+    def encode(self, pcm) -> np.ndarray:
+        return pp_codec_encode(self.h, pcm, self.B, self.cd.n_q, self.samples)
+
+    def time_encode(self, iters=20) -> float:
+        return pp_codec_time_encode(self.h, iters)
+
     def reset(self, slot):
         pp_codec_reset(self.h, slot)
 
@@ -223,8 +261,12 @@ class CodecEngine:
             off, n = ptr - base, int(np.prod(shape))
             return self.arena[off:off + n * isz].view(dtype).reshape(shape).cpu().numpy()
 
-        ring = view(t.ring, torch.int16, 2, (B, cd.n_layers, 2, cd.n_heads, cd.window, cd.head_dim))
-        return {"ring": ring.view(np.uint16), "z": view(t.z, torch.float32, 4, (B, cd.d))}
+        shape = (B, cd.n_layers, 2, cd.n_heads, cd.window, cd.head_dim)
+        return {"ring": view(t.ring, torch.int16, 2, shape).view(np.uint16),
+                "z": view(t.z, torch.float32, 4, (B, cd.d)),
+                "enc_ring": view(t.enc_ring, torch.int16, 2, shape).view(np.uint16),
+                "enc_y": view(t.enc_y, torch.float32, 4, (B, cd.d)),
+                "enc_z": view(t.enc_z, torch.float32, 4, (B, cd.d))}
 
     def close(self):
         if getattr(self, "h", None):

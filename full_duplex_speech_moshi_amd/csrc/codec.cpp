@@ -1,12 +1,18 @@
-// Host side of the streaming codec decoder (codec.h): validation, the arena
-// layout, the slots' frame positions, and four captured graphs (two for
-// decode calls, two for timing launches).
+// Host side of the streaming codec (codec.h), decoder and encoder:
+// validation, the arena layout, the slots' frame positions in each direction,
+// and eight captured graphs (per direction two for calls, two for timing
+// launches).
 //
-// One call decodes one frame per slot (chenxutan.com PersonaPlex article,
-// section 2.3: Mimi turns 12.5 Hz frames of 8 codebooks into 24 kHz audio,
-// causally; recipe "Architecture": 1920 samples per frame).  The graph runs
-// the latent sum, the transformer layers on the tick's GEMM and ring-decode
-// launchers, the output norm, the convolution stack and the state update.
+// A decode call turns one frame of 8 codes per slot into 1920 samples; an
+// encode call turns 1920 samples per slot into 8 codes (chenxutan.com
+// PersonaPlex article, section 2.3: Mimi maps 24 kHz audio to 12.5 Hz frames
+// of 8 codebooks and back, causally; recipe "Architecture": 1920 samples per
+// frame).  A decode graph runs the latent sum, the transformer layers on the
+// tick's GEMM and ring-decode launchers, the output norm, the convolution
+// stack and the state update; an encode graph runs the convolution stack,
+// the transformer, the residual quantiser and the state update.  The two
+// directions share the transformer's activation buffers (their calls never
+// overlap) and keep separate rings, positions and histories.
 // The convolutions' histories are double-buffered: a call's graph reads set
 // p and writes set 1 - p, and consecutive calls alternate; timing launches
 // write a third set, which no call reads.
@@ -39,6 +45,7 @@ bool codec_dims_ok(const pp_codec_dims* dm, std::string* why) {
   if (dm->n_q < 1 || dm->n_q > 16 || dm->card < 1) return fail("n_q must be 1..16 and card >= 1");
   if (dm->d <= 0 || dm->d % 32 || dm->n_layers <= 0 || dm->n_heads <= 0 || dm->ffn <= 0 || dm->ffn % 32)
     return fail("d and ffn must be positive multiples of 32");
+  if (dm->d > 8192) return fail("d must be at most 8192");
   if (dm->d % dm->n_heads) return fail("d not divisible by n_heads");
   const int hd = dm->d / dm->n_heads;
   if (hd != 32 && hd != 64 && hd != 128) return fail("head_dim must be 32, 64 or 128");
@@ -83,6 +90,16 @@ struct CodecLayout {
   long ring_layer_elems, ring_slot_elems, ring_v_off;
   std::vector<HistSpec> hist;  // 0: conv_in, then up_i / res_a_i, then conv_out
   int h_conv_in, h_up[PP_CODEC_MAX_STAGES], h_res[PP_CODEC_MAX_STAGES], h_conv_out;
+  // encoder: input samples, positions, RoPE table, ring, the latent y fed to
+  // the transformer, its output z, the codes; per stage j the stage's input
+  // (raw for the residual skip, and after ELU), the ELU of the residual
+  // unit's first convolution, the ELU of the residual unit's output
+  size_t pcm_in, e_ti, e_rope, e_ring, e_y, e_z, e_codes, e_qv, e_qi, e_qr;
+  size_t e_h[PP_CODEC_MAX_STAGES + 1], e_ha[PP_CODEC_MAX_STAGES + 1], e_ra[PP_CODEC_MAX_STAGES],
+      e_h2a[PP_CODEC_MAX_STAGES];
+  long eT[PP_CODEC_MAX_STAGES + 1];  // samples per call at each encoder stage: eT[0] = samples per frame
+  std::vector<HistSpec> ehist;      // conv_in, then res_a_j / down_j, then conv_out
+  int e_conv_in, e_res[PP_CODEC_MAX_STAGES], e_down[PP_CODEC_MAX_STAGES], e_conv_out;
   size_t total;
 };
 
@@ -137,6 +154,43 @@ CodecLayout make_codec_layout(const pp_codec_dims& dm, int B) {
   L.h_conv_out = add_hist(dm.channels[dm.n_stages], dm.conv_k - 1);
   for (int set = 0; set < 3; ++set)
     for (auto& s : L.hist) s.off[set] = take((size_t)B * s.C * s.H * 4);
+
+  const int n = dm.n_stages;
+  const long S = L.T[n];
+  L.pcm_in = take((size_t)B * S * 4);
+  L.e_ti = take((size_t)B * TI_STRIDE * 4);
+  L.e_rope = take((size_t)B * hd * 4);
+  L.e_ring = take((size_t)B * L.ring_slot_elems * 2);
+  L.e_y = take((size_t)B * d * 4);
+  L.e_z = take((size_t)B * d * 4);
+  L.e_codes = take((size_t)B * 16 * 4);
+  L.e_qv = take((size_t)2 * B * rvq_tiles(dm.card) * 4);
+  L.e_qi = take((size_t)2 * B * rvq_tiles(dm.card) * 4);
+  L.e_qr = take((size_t)2 * B * d * 4);
+  L.eT[0] = S;
+  for (int j = 0; j < n; ++j) L.eT[j + 1] = L.eT[j] / dm.strides[n - 1 - j];
+  for (int j = 0; j <= n; ++j) {
+    const long C = dm.channels[n - j];
+    L.e_h[j] = take((size_t)B * C * L.eT[j] * 4);
+    L.e_ha[j] = take((size_t)B * C * L.eT[j] * 4);
+    if (j < n) {
+      L.e_ra[j] = take((size_t)B * (C / 2) * L.eT[j] * 4);
+      L.e_h2a[j] = take((size_t)B * C * L.eT[j] * 4);
+    }
+  }
+  auto add_ehist = [&](int C, int Hh) {
+    if (Hh <= 0) return -1;
+    L.ehist.push_back(HistSpec{C, Hh, {0, 0, 0}});
+    return (int)L.ehist.size() - 1;
+  };
+  L.e_conv_in = add_ehist(1, dm.conv_k - 1);
+  for (int j = 0; j < n; ++j) {
+    L.e_res[j] = add_ehist(dm.channels[n - j], dm.res_k - 1);
+    L.e_down[j] = add_ehist(dm.channels[n - j], dm.strides[n - 1 - j]);
+  }
+  L.e_conv_out = add_ehist(dm.channels[0], dm.conv_k - 1);
+  for (int set = 0; set < 3; ++set)
+    for (auto& s : L.ehist) s.off[set] = take((size_t)B * s.C * s.H * 4);
   L.total = off;
   return L;
 }
@@ -159,11 +213,16 @@ struct pp_codec {
   // or set 2 (timing launches)
   hipGraph_t graph[2][2] = {};
   hipGraphExec_t exec[2][2] = {};
-  int parity = 0;
-  std::vector<int> pos;
+  hipGraph_t e_graph[2][2] = {};  // the encoder's, the same way
+  hipGraphExec_t e_exec[2][2] = {};
+  int parity = 0, e_parity = 0;
+  std::vector<int> pos, e_pos;
   int32_t* ti_host = nullptr;     // pinned [B][TI_STRIDE]
   int32_t* codes_host = nullptr;  // pinned [B][16]
   float* pcm_host = nullptr;      // pinned [B][S]
+  int32_t* e_ti_host = nullptr;   // pinned [B][TI_STRIDE]
+  float* pcm_in_host = nullptr;   // pinned [B][S]
+  int32_t* e_codes_host = nullptr;  // pinned [B][16]
   bool poisoned = false;
   std::string err;
 
@@ -191,39 +250,47 @@ struct pp_codec {
 
 namespace {
 
-// The whole decode of one call, recorded on stream s; reads history set p,
-// writes set po.
-void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
+// One direction's transformer weights.
+struct TfWeights {
+  const uint16_t *wqkv, *wo, *w_in, *w_out;
+  const float *attn_norm, *mlp_norm, *out_norm;
+};
+
+// The transformer for one frame per slot: its input (the codebook sum of
+// `codes`, or the latent y), the layers against the ring at `ring` with
+// positions at `ti`, and the output norm into `z`.
+void record_transformer(pp_codec* h, hipStream_t s, const TfWeights& tw, size_t ti_off, size_t rope_off,
+                        size_t ring_off, size_t z_off, const float* y, const int* codes) {
   const pp_codec_dims& dm = h->dm;
   const CodecLayout& L = h->lay;
   const int B = h->B, d = dm.d, H = dm.n_heads, hd = d / H, F = dm.ffn, W = dm.window;
-  const pp_codec_weights& w = h->w;
-  const int* ti = h->at<int>(L.ti);
+  const int* ti = h->at<int>(ti_off);
 
   CodecEmbedArgs ea{};
-  ea.codes = h->at<int>(L.codes);
+  ea.y = y;
+  ea.codes = codes;
   ea.ti = ti;
   ea.B = B;
   ea.d = d;
   ea.n_q = dm.n_q;
   ea.card = dm.card;
-  ea.codebooks = reinterpret_cast<const bf16_t*>(w.codebooks);
-  ea.alpha = w.attn_norm;
+  ea.codebooks = reinterpret_cast<const bf16_t*>(h->w.codebooks);
+  ea.alpha = tw.attn_norm;
   ea.x = h->at<float>(L.x);
   ea.xa = h->at<bf16_t>(L.xa);
   ea.xa_lo = (long)B * d;
   ea.part = h->at<float>(L.part);
   ea.inv_freq = h->at<double>(L.inv_freq);
   ea.head_dim = hd;
-  ea.rope = h->at<float>(L.rope);
+  ea.rope = h->at<float>(rope_off);
   launch_codec_embed(ea, s);
 
   const long pq = packed_elems(3 * d, d), pwo = packed_elems(d, d), pi = packed_elems(2 * F, d),
              pd = packed_elems(d, F);
   for (int l = 0; l < dm.n_layers; ++l) {
-    bf16_t* ring_l = h->at<bf16_t>(L.ring) + (long)l * L.ring_layer_elems;
+    bf16_t* ring_l = h->at<bf16_t>(ring_off) + (long)l * L.ring_layer_elems;
     GemmArgs g{};
-    g.W = reinterpret_cast<const bf16_t*>(w.wqkv) + (long)l * pq;
+    g.W = reinterpret_cast<const bf16_t*>(tw.wqkv) + (long)l * pq;
     g.X = h->at<bf16_t>(L.xa);
     g.x_lo = (long)B * d;
     g.M = 3 * d;
@@ -244,7 +311,7 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     g.window = W;
     g.ti = ti;
     g.inv_freq = h->at<double>(L.inv_freq);
-    g.rope = h->at<float>(L.rope);
+    g.rope = h->at<float>(rope_off);
     launch_gemm(EPI_QKV, g, s);
 
     AttnArgs at{};
@@ -267,7 +334,7 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     launch_attention(at, s);
 
     GemmArgs go{};
-    go.W = reinterpret_cast<const bf16_t*>(w.wo) + (long)l * pwo;
+    go.W = reinterpret_cast<const bf16_t*>(tw.wo) + (long)l * pwo;
     go.X = h->at<bf16_t>(L.o);
     go.x_lo = (long)B * d;
     go.M = d;
@@ -278,12 +345,12 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     go.ldres = d;
     go.xa_out = h->at<bf16_t>(L.xa);
     go.xa_lo = (long)B * d;
-    go.alpha_next = w.mlp_norm + (long)l * d;
+    go.alpha_next = tw.mlp_norm + (long)l * d;
     go.part_out = h->at<float>(L.part);
     launch_gemm(EPI_RESID, go, s);
 
     GemmArgs gu{};
-    gu.W = reinterpret_cast<const bf16_t*>(w.w_in) + (long)l * pi;
+    gu.W = reinterpret_cast<const bf16_t*>(tw.w_in) + (long)l * pi;
     gu.X = h->at<bf16_t>(L.xa);
     gu.x_lo = (long)B * d;
     gu.M = F;
@@ -301,7 +368,7 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     launch_gemm(EPI_GATED, gu, s);
 
     GemmArgs gd{};
-    gd.W = reinterpret_cast<const bf16_t*>(w.w_out) + (long)l * pd;
+    gd.W = reinterpret_cast<const bf16_t*>(tw.w_out) + (long)l * pd;
     gd.X = h->at<bf16_t>(L.m);
     gd.x_lo = (long)B * F;
     gd.M = d;
@@ -312,7 +379,7 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
     gd.ldres = d;
     gd.xa_out = h->at<bf16_t>(L.xa);
     gd.xa_lo = (long)B * d;
-    gd.alpha_next = (l + 1 < dm.n_layers) ? w.attn_norm + (long)(l + 1) * d : w.out_norm;
+    gd.alpha_next = (l + 1 < dm.n_layers) ? tw.attn_norm + (long)(l + 1) * d : tw.out_norm;
     gd.part_out = h->at<float>(L.part);
     launch_gemm(EPI_RESID, gd, s);
   }
@@ -320,12 +387,23 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
   CodecNormArgs na{};
   na.x = h->at<float>(L.x);
   na.part = h->at<float>(L.part);
-  na.alpha = w.out_norm;
+  na.alpha = tw.out_norm;
   na.eps = dm.norm_eps;
   na.B = B;
   na.d = d;
-  na.z = h->at<float>(L.z);
+  na.z = h->at<float>(z_off);
   launch_codec_norm(na, s);
+}
+
+// The whole decode of one call, recorded on stream s; reads history set p,
+// writes set po.
+void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
+  const pp_codec_dims& dm = h->dm;
+  const CodecLayout& L = h->lay;
+  const int B = h->B, d = dm.d;
+  const pp_codec_weights& w = h->w;
+  record_transformer(h, s, TfWeights{w.wqkv, w.wo, w.w_in, w.w_out, w.attn_norm, w.mlp_norm, w.out_norm}, L.ti,
+                     L.rope, L.ring, L.z, nullptr, h->at<int>(L.codes));
 
   auto hist_in = [&](int e) { return e < 0 ? nullptr : h->at<float>(L.hist[e].off[p]); };
   auto hist_H = [&](int e) { return e < 0 ? 0 : L.hist[e].H; };
@@ -438,16 +516,149 @@ void record_codec(pp_codec* h, hipStream_t s, int p, int po) {
   launch_codec_hist(ha, s);
 }
 
+// The whole encode of one call, recorded on stream s; reads history set p,
+// writes set po.
+void record_encoder(pp_codec* h, hipStream_t s, int p, int po) {
+  const pp_codec_dims& dm = h->dm;
+  const CodecLayout& L = h->lay;
+  const int B = h->B, d = dm.d, n = dm.n_stages;
+  const pp_codec_weights& w = h->w;
+  const int* ch = dm.channels;
+  auto hist_in = [&](int e) { return e < 0 ? nullptr : h->at<float>(L.ehist[e].off[p]); };
+  auto hist_H = [&](int e) { return e < 0 ? 0 : L.ehist[e].H; };
+
+  ConvArgs c0{};
+  c0.x = h->at<float>(L.pcm_in);
+  c0.C_in = 1;
+  c0.T_in = (int)L.eT[0];
+  c0.hist = hist_in(L.e_conv_in);
+  c0.H = hist_H(L.e_conv_in);
+  c0.w = reinterpret_cast<const bf16_t*>(w.enc_conv_in_w);
+  c0.bias = w.enc_conv_in_b;
+  c0.C_out = ch[n];
+  c0.K = dm.conv_k;
+  c0.stride = 1;
+  c0.y = h->at<float>(L.e_h[0]);
+  c0.ya = h->at<float>(L.e_ha[0]);
+  c0.B = B;
+  launch_codec_conv(c0, s);
+  for (int j = 0; j < n; ++j) {
+    const int C = ch[n - j], st = dm.strides[n - 1 - j];
+    const int T = (int)L.eT[j];
+    ConvArgs ra{};
+    ra.x = h->at<float>(L.e_ha[j]);
+    ra.C_in = C;
+    ra.T_in = T;
+    ra.hist = hist_in(L.e_res[j]);
+    ra.H = hist_H(L.e_res[j]);
+    ra.w = reinterpret_cast<const bf16_t*>(w.enc_res_a_w[j]);
+    ra.bias = w.enc_res_a_b[j];
+    ra.C_out = C / 2;
+    ra.K = dm.res_k;
+    ra.stride = 1;
+    ra.ya = h->at<float>(L.e_ra[j]);
+    ra.B = B;
+    launch_codec_conv(ra, s);
+
+    ConvArgs rb{};
+    rb.x = h->at<float>(L.e_ra[j]);
+    rb.C_in = C / 2;
+    rb.T_in = T;
+    rb.w = reinterpret_cast<const bf16_t*>(w.enc_res_b_w[j]);
+    rb.bias = w.enc_res_b_b[j];
+    rb.C_out = C;
+    rb.K = 1;
+    rb.stride = 1;
+    rb.skip = h->at<float>(L.e_h[j]);
+    rb.ya = h->at<float>(L.e_h2a[j]);
+    rb.B = B;
+    launch_codec_conv(rb, s);
+
+    ConvArgs dn{};
+    dn.x = h->at<float>(L.e_h2a[j]);
+    dn.C_in = C;
+    dn.T_in = T;
+    dn.hist = hist_in(L.e_down[j]);
+    dn.H = hist_H(L.e_down[j]);
+    dn.w = reinterpret_cast<const bf16_t*>(w.enc_down_w[j]);
+    dn.bias = w.enc_down_b[j];
+    dn.C_out = ch[n - 1 - j];
+    dn.K = 2 * st;
+    dn.stride = st;
+    dn.strided = 1;
+    dn.y = h->at<float>(L.e_h[j + 1]);
+    dn.ya = h->at<float>(L.e_ha[j + 1]);
+    dn.B = B;
+    launch_codec_conv(dn, s);
+  }
+  ConvArgs cz{};
+  cz.x = h->at<float>(L.e_ha[n]);
+  cz.C_in = ch[0];
+  cz.T_in = 1;
+  cz.hist = hist_in(L.e_conv_out);
+  cz.H = hist_H(L.e_conv_out);
+  cz.w = reinterpret_cast<const bf16_t*>(w.enc_conv_out_w);
+  cz.bias = w.enc_conv_out_b;
+  cz.C_out = d;
+  cz.K = dm.conv_k;
+  cz.stride = 1;
+  cz.y = h->at<float>(L.e_y);
+  cz.B = B;
+  launch_codec_conv(cz, s);
+
+  record_transformer(h, s,
+                     TfWeights{w.enc_wqkv, w.enc_wo, w.enc_w_in, w.enc_w_out, w.enc_attn_norm, w.enc_mlp_norm,
+                               w.enc_out_norm},
+                     L.e_ti, L.e_rope, L.e_ring, L.e_z, h->at<float>(L.e_y), nullptr);
+
+  RvqArgs qa{};
+  qa.z = h->at<float>(L.e_z);
+  qa.B = B;
+  qa.d = d;
+  qa.n_q = dm.n_q;
+  qa.card = dm.card;
+  qa.codebooks = reinterpret_cast<const bf16_t*>(w.codebooks);
+  qa.codes = h->at<int>(L.e_codes);
+  qa.part_v = h->at<float>(L.e_qv);
+  qa.part_i = h->at<int>(L.e_qi);
+  qa.res = h->at<float>(L.e_qr);
+  launch_codec_rvq(qa, s);
+
+  HistArgs ha{};
+  ha.B = B;
+  auto entry = [&](int e, const float* x, int T) {
+    if (e < 0) return;
+    HistEntry& he = ha.e[ha.n++];
+    he.x = x;
+    he.C = L.ehist[e].C;
+    he.T = T;
+    he.H = L.ehist[e].H;
+    he.old_h = h->at<float>(L.ehist[e].off[p]);
+    he.new_h = h->at<float>(L.ehist[e].off[po]);
+  };
+  entry(L.e_conv_in, h->at<float>(L.pcm_in), (int)L.eT[0]);
+  for (int j = 0; j < n; ++j) {
+    entry(L.e_res[j], h->at<float>(L.e_ha[j]), (int)L.eT[j]);
+    entry(L.e_down[j], h->at<float>(L.e_h2a[j]), (int)L.eT[j]);
+  }
+  entry(L.e_conv_out, h->at<float>(L.e_ha[n]), 1);
+  launch_codec_hist(ha, s);
+}
+
 hipError_t capture_codec(pp_codec* h) {
   hipError_t e;
-  for (int p = 0; p < 2; ++p)
-    for (int t = 0; t < 2; ++t) {
-      if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
-      record_codec(h, h->cap, p, t ? 2 : 1 - p);
-      if ((e = hipStreamEndCapture(h->cap, &h->graph[p][t])) != hipSuccess) return e;
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      if ((e = hipGraphInstantiate(&h->exec[p][t], h->graph[p][t], nullptr, nullptr, 0)) != hipSuccess) return e;
-    }
+  for (int dir = 0; dir < 2; ++dir)
+    for (int p = 0; p < 2; ++p)
+      for (int t = 0; t < 2; ++t) {
+        hipGraph_t& g = dir ? h->e_graph[p][t] : h->graph[p][t];
+        hipGraphExec_t& x = dir ? h->e_exec[p][t] : h->exec[p][t];
+        if ((e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) return e;
+        if (dir) record_encoder(h, h->cap, p, t ? 2 : 1 - p);
+        else record_codec(h, h->cap, p, t ? 2 : 1 - p);
+        if ((e = hipStreamEndCapture(h->cap, &g)) != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0)) != hipSuccess) return e;
+      }
   return hipSuccess;
 }
 
@@ -479,8 +690,15 @@ int pp_codec_create(const pp_codec_dims* dims, int B, const pp_codec_weights* w,
                          w->out_norm, w->conv_in_w, w->conv_in_b, w->conv_out_w, w->conv_out_b};
     for (const void* p : req)
       if (!p) { g_codec_create_error = "a weight pointer is NULL"; return PP_EINVAL; }
+    const void* ereq[] = {w->enc_conv_in_w, w->enc_conv_in_b, w->enc_conv_out_w, w->enc_conv_out_b,
+                          w->enc_attn_norm, w->enc_wqkv, w->enc_wo, w->enc_mlp_norm, w->enc_w_in, w->enc_w_out,
+                          w->enc_out_norm};
+    for (const void* p : ereq)
+      if (!p) { g_codec_create_error = "an encoder weight pointer is NULL"; return PP_EINVAL; }
     for (int i = 0; i < dims->n_stages; ++i)
-      if (!w->up_w[i] || !w->up_b[i] || !w->res_a_w[i] || !w->res_a_b[i] || !w->res_b_w[i] || !w->res_b_b[i]) {
+      if (!w->up_w[i] || !w->up_b[i] || !w->res_a_w[i] || !w->res_a_b[i] || !w->res_b_w[i] || !w->res_b_b[i] ||
+          !w->enc_res_a_w[i] || !w->enc_res_a_b[i] || !w->enc_res_b_w[i] || !w->enc_res_b_b[i] || !w->enc_down_w[i] ||
+          !w->enc_down_b[i]) {
         g_codec_create_error = "a stage weight pointer is NULL";
         return PP_EINVAL;
       }
@@ -499,6 +717,7 @@ int pp_codec_create(const pp_codec_dims* dims, int B, const pp_codec_weights* w,
   h->arena = static_cast<char*>(arena);
   h->stream = static_cast<hipStream_t>(stream);
   h->pos.assign(B, 0);
+  h->e_pos.assign(B, 0);
   auto bail = [&](const char* what, hipError_t e) {
     g_codec_create_error = std::string(what) + ": " + hipGetErrorString(e);
     pp_codec_destroy(h);
@@ -514,8 +733,19 @@ int pp_codec_create(const pp_codec_dims* dims, int B, const pp_codec_weights* w,
   if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->pcm_host), (size_t)B * h->S * 4, hipHostMallocDefault)) !=
       hipSuccess)
     return bail("hipHostMalloc", e);
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->e_ti_host), (size_t)B * TI_STRIDE * 4, hipHostMallocDefault)) !=
+      hipSuccess)
+    return bail("hipHostMalloc", e);
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->pcm_in_host), (size_t)B * h->S * 4, hipHostMallocDefault)) !=
+      hipSuccess)
+    return bail("hipHostMalloc", e);
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->e_codes_host), (size_t)B * 16 * 4, hipHostMallocDefault)) !=
+      hipSuccess)
+    return bail("hipHostMalloc", e);
   std::memset(h->ti_host, 0, (size_t)B * TI_STRIDE * 4);
   std::memset(h->codes_host, 0, (size_t)B * 16 * 4);
+  std::memset(h->e_ti_host, 0, (size_t)B * TI_STRIDE * 4);
+  std::memset(h->pcm_in_host, 0, (size_t)B * h->S * 4);
 
   const int hd = dims->d / dims->n_heads;
   std::vector<double> freq(hd / 2);
@@ -530,12 +760,19 @@ int pp_codec_create(const pp_codec_dims* dims, int B, const pp_codec_weights* w,
   if ((e = hipMemcpyAsync(h->at<int>(lay.codes), h->codes_host, (size_t)B * 16 * 4, hipMemcpyHostToDevice,
                           h->stream)) != hipSuccess)
     return bail("hipMemcpyAsync", e);
+  if ((e = hipMemcpyAsync(h->at<int>(lay.e_ti), h->e_ti_host, (size_t)B * TI_STRIDE * 4, hipMemcpyHostToDevice,
+                          h->stream)) != hipSuccess)
+    return bail("hipMemcpyAsync", e);
+  if ((e = hipMemcpyAsync(h->at<float>(lay.pcm_in), h->pcm_in_host, (size_t)B * h->S * 4, hipMemcpyHostToDevice,
+                          h->stream)) != hipSuccess)
+    return bail("hipMemcpyAsync", e);
   if ((e = hipMemsetAsync(h->at<char>(lay.att_cnt), 0, (size_t)B * dims->n_heads * 4, h->stream)) != hipSuccess)
     return bail("hipMemsetAsync", e);
-  for (const auto& s : lay.hist)
-    for (int set = 0; set < 3; ++set)
-      if ((e = hipMemsetAsync(h->at<char>(s.off[set]), 0, (size_t)B * s.C * s.H * 4, h->stream)) != hipSuccess)
-        return bail("hipMemsetAsync", e);
+  for (const auto* hv : {&lay.hist, &lay.ehist})
+    for (const auto& s : *hv)
+      for (int set = 0; set < 3; ++set)
+        if ((e = hipMemsetAsync(h->at<char>(s.off[set]), 0, (size_t)B * s.C * s.H * 4, h->stream)) != hipSuccess)
+          return bail("hipMemsetAsync", e);
   if ((e = hipStreamSynchronize(h->stream)) != hipSuccess) return bail("hipStreamSynchronize", e);
   if ((e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking)) != hipSuccess) return bail("hipStreamCreate", e);
   if ((e = capture_codec(h)) != hipSuccess) return bail("graph capture", e);
@@ -572,6 +809,31 @@ int pp_codec_decode(pp_codec* h, const int32_t* codes, float* pcm) {
   return PP_OK;
 }
 
+int pp_codec_encode(pp_codec* h, const float* pcm, int32_t* codes) {
+  if (!h) return PP_EINVAL;
+  if (h->poisoned) return PP_EDEVICE;
+  if (!codes || !pcm) return h->fail(PP_EINVAL, "pcm or codes is NULL");
+  const int B = h->B, nq = h->dm.n_q;
+  const long S = h->S;
+  for (long i = 0; i < (long)B * S; ++i)
+    if (!std::isfinite(pcm[i])) return h->fail(PP_EINVAL, "slot %ld sample %ld is not finite", i / S, i % S);
+  for (int b = 0; b < B; ++b) h->e_ti_host[b * TI_STRIDE + TI_POS] = h->e_pos[b];
+  std::memcpy(h->pcm_in_host, pcm, (size_t)B * S * 4);
+  const CodecLayout& L = h->lay;
+  CODEC_HIP_OR_FAIL(h, hipMemcpyAsync(h->at<int>(L.e_ti), h->e_ti_host, (size_t)B * TI_STRIDE * 4,
+                                      hipMemcpyHostToDevice, h->stream));
+  CODEC_HIP_OR_FAIL(h, hipMemcpyAsync(h->at<float>(L.pcm_in), h->pcm_in_host, (size_t)B * S * 4,
+                                      hipMemcpyHostToDevice, h->stream));
+  CODEC_HIP_OR_FAIL(h, hipGraphLaunch(h->e_exec[h->e_parity][0], h->stream));
+  CODEC_HIP_OR_FAIL(h, hipMemcpyAsync(h->e_codes_host, h->at<int>(L.e_codes), (size_t)B * nq * 4,
+                                      hipMemcpyDeviceToHost, h->stream));
+  CODEC_HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  std::memcpy(codes, h->e_codes_host, (size_t)B * nq * 4);
+  for (int b = 0; b < B; ++b) ++h->e_pos[b];
+  h->e_parity ^= 1;
+  return PP_OK;
+}
+
 int pp_codec_reset(pp_codec* h, int slot) {
   if (!h) return PP_EINVAL;
   if (h->poisoned) return PP_EDEVICE;
@@ -580,26 +842,31 @@ int pp_codec_reset(pp_codec* h, int slot) {
   for (const auto& s : h->lay.hist)
     CODEC_HIP_OR_FAIL(h, hipMemsetAsync(h->at<char>(s.off[h->parity]) + (size_t)slot * s.C * s.H * 4, 0,
                                         (size_t)s.C * s.H * 4, h->stream));
+  for (const auto& s : h->lay.ehist)
+    CODEC_HIP_OR_FAIL(h, hipMemsetAsync(h->at<char>(s.off[h->e_parity]) + (size_t)slot * s.C * s.H * 4, 0,
+                                        (size_t)s.C * s.H * 4, h->stream));
   CODEC_HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
   h->pos[slot] = 0;
+  h->e_pos[slot] = 0;
   return PP_OK;
 }
 
-int pp_codec_time(pp_codec* h, int iters, float* avg_ms) {
-  if (!h || !avg_ms || iters < 1) return h ? h->fail(PP_EINVAL, "bad arguments") : PP_EINVAL;
+namespace {
+int time_graphs(pp_codec* h, hipGraphExec_t (&ex)[2][2], int parity, int iters, float* avg_ms) {
+  if (!avg_ms || iters < 1) return h->fail(PP_EINVAL, "bad arguments");
   if (h->poisoned) return PP_EDEVICE;
   // the last call's work again: it reads the history set the last call read
   // and writes the timing set, so the set the next call reads is untouched;
   // the ring entry it rewrites (the last call's position) gets the same key
   // and value, or, for a slot reset since, lies outside that slot's window
   // until the slot's own calls overwrite it
-  const int p = h->parity ^ 1;
+  const int p = parity ^ 1;
   hipEvent_t e0, e1;
   CODEC_HIP_OR_FAIL(h, hipEventCreate(&e0));
   CODEC_HIP_OR_FAIL(h, hipEventCreate(&e1));
-  CODEC_HIP_OR_FAIL(h, hipGraphLaunch(h->exec[p][1], h->stream));  // warm
+  CODEC_HIP_OR_FAIL(h, hipGraphLaunch(ex[p][1], h->stream));  // warm
   CODEC_HIP_OR_FAIL(h, hipEventRecord(e0, h->stream));
-  for (int i = 0; i < iters; ++i) CODEC_HIP_OR_FAIL(h, hipGraphLaunch(h->exec[p][1], h->stream));
+  for (int i = 0; i < iters; ++i) CODEC_HIP_OR_FAIL(h, hipGraphLaunch(ex[p][1], h->stream));
   CODEC_HIP_OR_FAIL(h, hipEventRecord(e1, h->stream));
   CODEC_HIP_OR_FAIL(h, hipEventSynchronize(e1));
   float ms = 0.f;
@@ -609,6 +876,15 @@ int pp_codec_time(pp_codec* h, int iters, float* avg_ms) {
   *avg_ms = ms / iters;
   return PP_OK;
 }
+}  // namespace
+
+int pp_codec_time(pp_codec* h, int iters, float* avg_ms) {
+  return h ? time_graphs(h, h->exec, h->parity, iters, avg_ms) : PP_EINVAL;
+}
+
+int pp_codec_time_encode(pp_codec* h, int iters, float* avg_ms) {
+  return h ? time_graphs(h, h->e_exec, h->e_parity, iters, avg_ms) : PP_EINVAL;
+}
 
 int pp_codec_taps(pp_codec* h, pp_codec_taps_t* out) {
   if (!h || !out) return h ? h->fail(PP_EINVAL, "out is NULL") : PP_EINVAL;
@@ -616,6 +892,9 @@ int pp_codec_taps(pp_codec* h, pp_codec_taps_t* out) {
   CODEC_HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
   out->ring = h->at<uint16_t>(h->lay.ring);
   out->z = h->at<float>(h->lay.z);
+  out->enc_ring = h->at<uint16_t>(h->lay.e_ring);
+  out->enc_y = h->at<float>(h->lay.e_y);
+  out->enc_z = h->at<float>(h->lay.e_z);
   return PP_OK;
 }
 
@@ -626,11 +905,16 @@ void pp_codec_destroy(pp_codec* h) {
     for (int t = 0; t < 2; ++t) {
       if (h->exec[p][t]) (void)hipGraphExecDestroy(h->exec[p][t]);
       if (h->graph[p][t]) (void)hipGraphDestroy(h->graph[p][t]);
+      if (h->e_exec[p][t]) (void)hipGraphExecDestroy(h->e_exec[p][t]);
+      if (h->e_graph[p][t]) (void)hipGraphDestroy(h->e_graph[p][t]);
     }
   if (h->cap) (void)hipStreamDestroy(h->cap);
   if (h->ti_host) (void)hipHostFree(h->ti_host);
   if (h->codes_host) (void)hipHostFree(h->codes_host);
   if (h->pcm_host) (void)hipHostFree(h->pcm_host);
+  if (h->e_ti_host) (void)hipHostFree(h->e_ti_host);
+  if (h->pcm_in_host) (void)hipHostFree(h->pcm_in_host);
+  if (h->e_codes_host) (void)hipHostFree(h->e_codes_host);
   delete h;
 }
 

@@ -18,9 +18,10 @@
 namespace pp {
 
 // ---------------------------------------------------------------------------
-// Latent: x = sum of the n_q codebooks' rows in codebook order (fp32), with
-// x * alpha as a bf16 pair and the per-16 sums of squares for the first
-// layer's QKV launch, and the frame's RoPE table.  One thread per 8 features.
+// Transformer input: x = the sum of the n_q codebooks' rows in codebook order
+// (fp32; the decoder) or the given latent (the encoder), with x * alpha as a
+// bf16 pair and the per-16 sums of squares for the first layer's QKV launch,
+// and the frame's RoPE table.  One thread per 8 features.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void codec_embed_kernel(CodecEmbedArgs a) {
   const int b = blockIdx.y;
@@ -37,8 +38,8 @@ __global__ __launch_bounds__(256) void codec_embed_kernel(CodecEmbedArgs a) {
   const int* c = a.codes + (long)b * a.n_q;
   float acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int q = 0; q < a.n_q; ++q) {
+  for (int i = 0; i < 8; ++i) acc[i] = a.y ? a.y[(long)b * a.d + g8 * 8 + i] : 0.f;
+  for (int q = 0; q < (a.y ? 0 : a.n_q); ++q) {
     const u32x4 v = ld16(a.codebooks + ((long)q * a.card + c[q]) * a.d + g8 * 8);
     float f[8];
     unpack8(v, f);
@@ -201,12 +202,47 @@ __global__ __launch_bounds__(256) void codec_convt_kernel(ConvArgs a) {
 // Enough lanes for the part (256 CUs x 4 SIMDs x 2 waves of 64).
 constexpr long CONV_LANES = 1L << 17;
 
+// strided convolution: one output per group
+template <int LPO>
+__global__ __launch_bounds__(256) void codec_convs_kernel(ConvArgs a) {
+  const int s = a.stride, T = a.T_in, T_out = T / s;
+  const long n_grp = (long)a.B * a.C_out * T_out;
+  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPO;
+  const int l = threadIdx.x % LPO;
+  const bool live = gid < n_grp;
+  const long g = live ? gid : 0;
+  const int t = (int)(g % T_out);
+  const int o = (int)((g / T_out) % a.C_out);
+  const int b = (int)(g / ((long)T_out * a.C_out));
+  float acc[1] = {0.f};
+#pragma unroll 2
+  for (int i = l; i < a.C_in; i += LPO) {
+    const float* xi = a.x + ((long)b * a.C_in + i) * T;
+    const float* hi = a.hist + ((long)b * a.C_in + i) * a.H;
+    const bf16_t* wi = a.w + ((long)o * a.C_in + i) * a.K;
+#pragma unroll
+    for (int k = 0; k < 2 * CONV_KMAX; ++k) {
+      if (k < a.K) {
+        const int u = t * s - s + k;  // input time, >= -s
+        const float v = u >= 0 ? xi[u] : hi[a.H + u];
+        acc[0] = __builtin_fmaf(bf2f(wi[k]), v, acc[0]);
+      }
+    }
+  }
+  conv_store<LPO, 1>(a, live, l, b, o, t, T_out, acc, 1);
+}
+
 template <int LPO>
 static void launch_conv_lpo(const ConvArgs& a, hipStream_t s, int tt) {
-  const long groups = (long)a.B * a.C_out * (a.transposed ? a.T_in : (a.T_in + tt - 1) / tt);
+  const long groups = (long)a.B * a.C_out *
+                      (a.transposed ? a.T_in : a.strided ? a.T_in / a.stride : (a.T_in + tt - 1) / tt);
   const dim3 grid((unsigned)((groups * LPO + 255) / 256));
   if (a.transposed) {
     hipLaunchKernelGGL(codec_convt_kernel<LPO>, grid, dim3(256), 0, s, a);
+    return;
+  }
+  if (a.strided) {
+    hipLaunchKernelGGL(codec_convs_kernel<LPO>, grid, dim3(256), 0, s, a);
     return;
   }
   switch (tt) {
@@ -217,21 +253,23 @@ static void launch_conv_lpo(const ConvArgs& a, hipStream_t s, int tt) {
   }
 }
 
-// Launch shape: the fewest lanes per output group (1, 8 or 64, at most the
-// input channels) that still gives CONV_LANES lanes, else the most; then, for
-// the causal form, the most outputs per group (8, 4, 2 or 1, at most the
-// samples of the call) that keeps CONV_LANES lanes.  Fewer lanes per group
-// fold fewer partial sums; more outputs per group re-read fewer inputs.
+// Launch shape: lanes per output group (1, 8 or 64, at most the input
+// channels) so that each lane walks at most 4 input channels where it can
+// (each channel is a dependent round of loads), more if the groups alone do
+// not give CONV_LANES lanes; then, for the causal form, the most outputs per
+// group (8, 4, 2 or 1, at most the samples of the call) that keeps
+// CONV_LANES lanes.  More outputs per group re-read fewer inputs.
 void launch_codec_conv(const ConvArgs& a, hipStream_t s) {
-  const long outs = (long)a.B * a.C_out * a.T_in;  // groups of one output (or one input position)
+  // groups of one output (or one input position)
+  const long outs = (long)a.B * a.C_out * (a.strided ? a.T_in / a.stride : a.T_in);
   int lpo = 1;
   for (int c : {1, 8, 64}) {
     if (c > 1 && a.C_in < c) break;
     lpo = c;
-    if (outs * c >= CONV_LANES) break;
+    if (a.C_in <= 4 * c && outs * c >= CONV_LANES) break;
   }
   int tt = 1;
-  if (!a.transposed)
+  if (!a.transposed && !a.strided)
     for (int c : {8, 4, 2}) {
       if (c <= a.T_in && (long)a.B * a.C_out * ((a.T_in + c - 1) / c) * lpo >= CONV_LANES) {
         tt = c;
@@ -241,6 +279,129 @@ void launch_codec_conv(const ConvArgs& a, hipStream_t s) {
   if (lpo == 64) launch_conv_lpo<64>(a, s, tt);
   else if (lpo == 8) launch_conv_lpo<8>(a, s, tt);
   else launch_conv_lpo<1>(a, s, tt);
+}
+
+// ---------------------------------------------------------------------------
+// Residual vector quantisation.  Stage q is one launch of (codeword tile,
+// slot) workgroups: each first finishes stage q - 1 for its slot (the
+// minimum over that stage's tile minima, lowest index among equals; the
+// residual r_q = r_{q-1} - row), then takes RVQ_ROWS codewords of codebook q
+// with 4 lanes per codeword: distance |c|^2 - 2 r.c (the |r|^2 common to
+// every row left out), each lane summing a quarter of the features in order
+// in fp32, the 4 quarters folded by a fixed butterfly; the tile's minimum
+// (lowest index among equals) is written for the next stage.  Tile 0 writes
+// the finished code and residual.  A last launch finishes stage n_q - 1.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool rvq_better(float v2, int i2, float v, int i) {
+  return v2 < v || (v2 == v && i2 < i);
+}
+
+// stage q - 1's code for slot b from its tile minima (every thread gets it)
+__device__ int rvq_finish(const RvqArgs& a, int q, int b, int* red_i) {
+  const int tiles = rvq_tiles(a.card), tid = threadIdx.x;
+  const float* pv = a.part_v + ((long)((q - 1) & 1) * a.B + b) * tiles;
+  const int* pi = a.part_i + ((long)((q - 1) & 1) * a.B + b) * tiles;
+  if (tid < 64) {
+    float bv = INFINITY;
+    int bi = 0x7fffffff;
+    for (int t = tid; t < tiles; t += 64)
+      if (rvq_better(pv[t], pi[t], bv, bi)) {
+        bv = pv[t];
+        bi = pi[t];
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float v2 = __shfl_xor(bv, off);
+      const int i2 = __shfl_xor(bi, off);
+      if (rvq_better(v2, i2, bv, bi)) {
+        bv = v2;
+        bi = i2;
+      }
+    }
+    if (tid == 0) red_i[0] = min(bi, a.card - 1);
+  }
+  __syncthreads();
+  return red_i[0];
+}
+
+__global__ __launch_bounds__(256) void codec_rvq_stage_kernel(RvqArgs a, int q) {
+  extern __shared__ float rr[];  // [d] this stage's residual
+  __shared__ float red_v[4];
+  __shared__ int red_i[4];
+  const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // this stage's residual: z, or the previous stage's residual minus its row
+  const float* rin = q == 0 ? a.z + (long)b * a.d : a.res + ((long)((q - 1) & 1) * a.B + b) * a.d;
+  int prev = -1;
+  if (q > 0) prev = rvq_finish(a, q, b, red_i);
+  const bf16_t* prow = q > 0 ? a.codebooks + ((long)(q - 1) * a.card + prev) * a.d : nullptr;
+  for (int i = tid; i < a.d; i += 256) rr[i] = q > 0 ? rin[i] - bf2f(prow[i]) : rin[i];
+  __syncthreads();
+  if (tile == 0 && q > 0) {
+    if (tid == 0) a.codes[b * a.n_q + q - 1] = prev;
+    for (int i = tid; i < a.d; i += 256) a.res[((long)(q & 1) * a.B + b) * a.d + i] = rr[i];
+  } else if (tile == 0) {
+    for (int i = tid; i < a.d; i += 256) a.res[((long)(q & 1) * a.B + b) * a.d + i] = rr[i];
+  }
+  if (q == a.n_q) return;  // the finishing launch
+  // 4 lanes per codeword: lane quarter k sums features k*d/4 .. (k+1)*d/4 - 1
+  const int cw = tid >> 2, qk = tid & 3;
+  const int j = tile * RVQ_ROWS + cw;
+  const int n4 = a.d / 4;
+  float dot = 0.f, cc = 0.f;
+  if (j < a.card) {
+    const bf16_t* row = a.codebooks + ((long)q * a.card + j) * a.d;
+    for (int i = qk * n4; i < (qk + 1) * n4; i += 8) {
+      float f[8];
+      unpack8(ld16(row + i), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dot = __builtin_fmaf(f[e], rr[i + e], dot);
+        cc = __builtin_fmaf(f[e], f[e], cc);
+      }
+    }
+  }
+  dot += __shfl_xor(dot, 1);
+  cc += __shfl_xor(cc, 1);
+  dot += __shfl_xor(dot, 2);
+  cc += __shfl_xor(cc, 2);
+  // rows past the codebook's end (the last tile's tail) never win; a NaN
+  // distance counts as +inf, so the winner is always a real row
+  float bv = j < a.card ? cc - 2.f * dot : INFINITY;
+  if (bv != bv) bv = INFINITY;
+  int bi = j < a.card ? j : 0x7fffffff;
+#pragma unroll
+  for (int off = 4; off <= 32; off <<= 1) {
+    const float v2 = __shfl_xor(bv, off);
+    const int i2 = __shfl_xor(bi, off);
+    if (rvq_better(v2, i2, bv, bi)) {
+      bv = v2;
+      bi = i2;
+    }
+  }
+  if (lane == 0) {
+    red_v[wave] = bv;
+    red_i[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float v = red_v[0];
+    int ix = red_i[0];
+    for (int w = 1; w < 4; ++w)
+      if (rvq_better(red_v[w], red_i[w], v, ix)) {
+        v = red_v[w];
+        ix = red_i[w];
+      }
+    const long o = ((long)(q & 1) * a.B + b) * rvq_tiles(a.card) + tile;
+    a.part_v[o] = v;
+    a.part_i[o] = ix;
+  }
+}
+
+void launch_codec_rvq(const RvqArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)a.d * 4;
+  for (int q = 0; q < a.n_q; ++q)
+    hipLaunchKernelGGL(codec_rvq_stage_kernel, dim3(rvq_tiles(a.card), a.B), dim3(256), lds, s, a, q);
+  hipLaunchKernelGGL(codec_rvq_stage_kernel, dim3(1, a.B), dim3(256), lds, s, a, a.n_q);
 }
 
 // ---------------------------------------------------------------------------

@@ -17,6 +17,7 @@ namespace pp {
 constexpr int CODEC_MAX_HIST = 24;   // history entries (convolutions with memory)
 
 struct CodecEmbedArgs {
+  const float* y;         // [B][d] the transformer's input itself (the encoder), or null: the codebook sum
   const int* codes;       // [B][n_q]
   const int* ti;          // tick-input layout: the slot's frame position at TI_POS
   int B, d, n_q, card;
@@ -39,24 +40,42 @@ struct CodecNormArgs {
 };
 void launch_codec_norm(const CodecNormArgs& a, hipStream_t s);
 
-// One convolution.  transposed = 0: causal convolution of kernel K <= 8
-// (stride 1); transposed = 1: causal transposed convolution with stride
-// `stride` <= 8 and K = 2 stride.  Input x [B][C_in][T_in] with its history
-// hist [B][C_in][H] (H = K - 1 for the causal form, 1 for the transposed
-// form); both already hold the layer's input as it is fed (after its ELU).
-// Output [B][C_out][T_out], T_out = T_in * stride: bias + sum, plus skip
-// [B][C_out][T_out] when given, stored raw into y and/or after ELU into ya
-// (either may be null).
+// One convolution.  transposed = strided = 0: causal convolution of kernel
+// K <= 8 (stride 1); transposed = 1: causal transposed convolution with
+// stride `stride` <= 8 and K = 2 stride, T_out = T_in * stride; strided = 1:
+// causal strided convolution with stride `stride` <= 8 and K = 2 stride,
+// T_out = T_in / stride, output t reading inputs t s - s + k.  Input x
+// [B][C_in][T_in] with its history hist [B][C_in][H] (H = K - 1 for the
+// causal form, 1 for the transposed form, `stride` for the strided form);
+// both already hold the layer's input as it is fed (after its ELU).  Output
+// [B][C_out][T_out]: bias + sum, plus skip [B][C_out][T_out] when given,
+// stored raw into y and/or after ELU into ya (either may be null).
 struct ConvArgs {
   const float* x; int C_in, T_in;
   const float* hist; int H;
-  const bf16_t* w; const float* bias; int C_out, K, stride, transposed;
+  const bf16_t* w; const float* bias; int C_out, K, stride, transposed, strided;
   const float* skip;
   float* y;
   float* ya;
   int B;
 };
 void launch_codec_conv(const ConvArgs& a, hipStream_t s);
+
+// Residual vector quantisation: per slot, for q = 0..n_q-1, the row of
+// codebook q nearest to the residual (squared distance, lowest index on
+// ties), then residual -= that row.  z [B][d] fp32 in, codes [B][n_q] out.
+struct RvqArgs {
+  const float* z; int B, d, n_q, card;
+  const bf16_t* codebooks;  // [n_q][card][d]
+  int* codes;
+  // work buffers: per-tile minima [2][B][card / RVQ_ROWS] (value, index),
+  // alternating by stage, and the residual [2][B][d]
+  float* part_v; int* part_i;
+  float* res;
+};
+constexpr int RVQ_ROWS = 64;  // codewords per workgroup and stage
+inline __host__ __device__ int rvq_tiles(int card) { return (card + RVQ_ROWS - 1) / RVQ_ROWS; }
+void launch_codec_rvq(const RvqArgs& a, hipStream_t s);
 
 // The streaming-state update after a call: for each convolution with memory,
 // the new history is the last H entries of (old history, this call's input).

@@ -1,10 +1,12 @@
 /*
- * codec.h -- C ABI of the streaming codec decoder (code2wav) in libpp.so
- * for MI355X (gfx950).
+ * codec.h -- C ABI of the streaming codec (decoder / code2wav, and encoder)
+ * in libpp.so for MI355X (gfx950).
  *
  * One call of pp_codec_decode turns one 80 ms frame of 8 codebook indices per
- * session slot into 1920 audio samples at 24 kHz, carrying each slot's
- * streaming state to the next call.
+ * session slot into 1920 audio samples at 24 kHz; one call of
+ * pp_codec_encode turns 1920 samples of user audio per slot into 8 codebook
+ * indices.  Each direction carries each slot's streaming state to its next
+ * call.
  *
  *   chenxutan.com PersonaPlex article, section 2.3 on Mimi: a streaming neural
  *   codec of the SoundStream / EnCodec family, 24 kHz audio <-> 12.5 Hz
@@ -32,6 +34,18 @@
  *      to the stage's upsampled signal;
  *   5. ELU and a causal convolution of kernel conv_k to one channel: the
  *      samples.  The strides multiply to the samples per frame.
+ *
+ * The encoder mirrors it: a causal convolution of kernel conv_k from one
+ * channel to channels[n_stages]; per stage j = 0 .. n_stages-1 (decoder
+ * stage i = n_stages-1-j in reverse) a residual unit on channels[i+1] as
+ * above, then ELU and a causal strided convolution of kernel 2 s_i and
+ * stride s_i to channels[i]; then ELU and a causal convolution of kernel
+ * conv_k to d channels (one latent per frame); the transformer block with the
+ * encoder's own weights and output norm; then residual vector quantisation
+ * against the decoder's codebooks: code_q = the row of codebook q nearest to
+ * the residual (squared Euclidean distance, the lowest index on ties),
+ * residual -= that row, for q = 0 .. n_q-1.  Causal strided convolution:
+ * output t = b + sum_i sum_k w[o][i][k] x[i][t s - s + k].
  *
  * Causal convolution: y[o][t] = b[o] + sum_i sum_k w[o][i][k] x[i][t-(K-1-k)]
  * with zeros before the stream's first frame.  Causal transposed convolution
@@ -62,7 +76,7 @@ extern "C" {
 typedef struct pp_codec_dims {
   int32_t n_q;        /* codebooks per frame (1..16) */
   int32_t card;       /* entries per codebook */
-  int32_t d;          /* latent and transformer width (a multiple of 32) */
+  int32_t d;          /* latent and transformer width (a multiple of 32, at most 8192) */
   int32_t n_layers, n_heads, ffn;   /* transformer; head_dim = d / n_heads in {32, 64, 128}; ffn % 32 == 0 */
   int32_t window;     /* frames the attention sees, 1..PP_CODEC_MAX_WINDOW */
   int32_t conv_k;     /* kernel of the first and the last convolution (1..8) */
@@ -98,6 +112,24 @@ typedef struct pp_codec_weights {
   const float* res_b_b[PP_CODEC_MAX_STAGES];     /* [channels[i+1]] */
   const uint16_t* conv_out_w; /* [1][channels[n_stages]][conv_k] */
   const float* conv_out_b;    /* [1] */
+  /* the encoder (stage j works at decoder stage i = n_stages-1-j's channels and stride) */
+  const uint16_t* enc_conv_in_w;  /* [channels[n_stages]][1][conv_k] */
+  const float* enc_conv_in_b;     /* [channels[n_stages]] */
+  const uint16_t* enc_res_a_w[PP_CODEC_MAX_STAGES];  /* [channels[i+1]/2][channels[i+1]][res_k] */
+  const float* enc_res_a_b[PP_CODEC_MAX_STAGES];     /* [channels[i+1]/2] */
+  const uint16_t* enc_res_b_w[PP_CODEC_MAX_STAGES];  /* [channels[i+1]][channels[i+1]/2][1] */
+  const float* enc_res_b_b[PP_CODEC_MAX_STAGES];     /* [channels[i+1]] */
+  const uint16_t* enc_down_w[PP_CODEC_MAX_STAGES];   /* [channels[i]][channels[i+1]][2 strides[i]] */
+  const float* enc_down_b[PP_CODEC_MAX_STAGES];      /* [channels[i]] */
+  const uint16_t* enc_conv_out_w; /* [d][channels[0]][conv_k] */
+  const float* enc_conv_out_b;    /* [d] */
+  const float* enc_attn_norm;     /* as the decoder's transformer fields */
+  const uint16_t* enc_wqkv;
+  const uint16_t* enc_wo;
+  const float* enc_mlp_norm;
+  const uint16_t* enc_w_in;
+  const uint16_t* enc_w_out;
+  const float* enc_out_norm;
 } pp_codec_weights;
 
 typedef struct pp_codec pp_codec;
@@ -124,8 +156,14 @@ int pp_codec_create(const pp_codec_dims* dims, int B, const pp_codec_weights* w,
  * receives the samples.  Synchronous; advances every slot by one frame. */
 int pp_codec_decode(pp_codec* h, const int32_t* codes, float* pcm);
 
-/* Makes slot a fresh stream (position 0, zero history); the other slots are
- * untouched.  PP_EINVAL for a slot outside [0, B). */
+/* Encodes one frame for every slot: pcm host float [B][samples] (finite,
+ * else PP_EINVAL and nothing runs), codes host int32 [B][n_q] receives the
+ * codebook indices.  Synchronous; advances every slot's encoder by one frame. */
+int pp_codec_encode(pp_codec* h, const float* pcm, int32_t* codes);
+
+/* Makes slot a fresh stream in both directions (positions 0, zero
+ * histories); the other slots are untouched.  PP_EINVAL for a slot outside
+ * [0, B). */
 int pp_codec_reset(pp_codec* h, int slot);
 
 /* Measurement hook: average device time of one decode call's graph over
@@ -134,15 +172,22 @@ int pp_codec_reset(pp_codec* h, int slot);
  * slots' state is unchanged. */
 int pp_codec_time(pp_codec* h, int iters, float* avg_ms);
 
+/* The same for one encode call's graph. */
+int pp_codec_time_encode(pp_codec* h, int iters, float* avg_ms);
+
 /* Device views of the decoder's state after the last call. */
 typedef struct pp_codec_taps_t {
   const uint16_t* ring;  /* bf16 [B][n_layers][2][n_heads][window][head_dim]: the transformer's stored keys
                             (index 0) and values (index 1), position p at p mod window */
   const float* z;        /* [B][d]: the last call's transformer output after the output norm */
+  const uint16_t* enc_ring;  /* the encoder's, laid out as ring */
+  const float* enc_y;    /* [B][d]: the last encode call's latent (the transformer's input) */
+  const float* enc_z;    /* [B][d]: the last encode call's transformer output after the output norm */
 } pp_codec_taps_t;
 
 /* Test hook: fills *out with device pointers into the arena (valid until
- * the next call on the handle).  Waits for the handle's device work. */
+ * the handle is destroyed; the contents are those of the last call in each
+ * direction).  Waits for the handle's device work. */
 int pp_codec_taps(pp_codec* h, pp_codec_taps_t* out);
 
 /* Waits for the handle's device work, then frees its host resources. */

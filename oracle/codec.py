@@ -306,7 +306,8 @@ class CodecOracle:
         return np.array(codes, np.int64)
 
     def _enc_frame(self, st, pcm) -> np.ndarray:
-        z = self.transformer(st, self.enc_convs(st, pcm), "enc.")
+        st.last_y = self.enc_convs(st, pcm)
+        z = self.transformer(st, st.last_y, "enc.")
         st.last_z = z
         st.pos += 1
         return self.quantise(z)

@@ -36,7 +36,7 @@ def test_exports_every_declared_entry_point(lib):
 def test_exports_every_codec_entry_point(lib):
     from full_duplex_speech_moshi_amd import codec
     names = declared_functions("codec.h")
-    assert len(names) == 9
+    assert len(names) == 11
     assert set(names) == set(codec.EXPORTS)
     for n in names:
         assert getattr(lib, n) is not None
@@ -61,7 +61,7 @@ def test_codec_dims_validated_on_the_host(lib):
     assert codec.pp_codec_samples(codec.make_codec_dims(synth.CODEC_TINY)) == 24
     bad = [dict(n_heads=3), dict(d=500), dict(window=257), dict(strides=(0, 2)), dict(strides=(9, 2)),
            dict(conv_k=9), dict(channels=(8, 5, 4)),
-           dict(n_q=17), dict(ffn=100)]
+           dict(n_q=17), dict(ffn=100), dict(card=0), dict(d=8320, n_heads=65)]
     for kw in bad:
         cd = dataclasses.replace(synth.CODEC_TINY, **kw)
         if "strides" in kw:

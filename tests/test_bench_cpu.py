@@ -147,3 +147,15 @@ def test_codec_call_bytes_are_the_weights_rows_and_caches():
         rows = B * cd.n_q * cd.d * 2
         cache = B * cd.n_layers * 2 * n * cd.d * 2
         assert bench.codec_call_bytes(cd, B, n) == weights + rows + cache
+
+
+def test_codec_encode_bytes_are_the_encoder_weights_codebooks_samples_and_caches():
+    # every encoder weight and every codebook once, plus each slot's samples
+    # and its keys and values over the window
+    w = synth.make_codec_weights(synth.CODEC_TINY, seed=0)
+    cd = synth.CODEC_TINY
+    weights = sum(v.nbytes for k, v in w.items() if k.startswith(("codebook.", "enc.")))
+    for B, n in ((1, 1), (3, cd.window)):
+        pcm = B * cd.samples * 4
+        cache = B * cd.n_layers * 2 * n * cd.d * 2
+        assert bench.codec_encode_bytes(cd, B, n) == weights + pcm + cache

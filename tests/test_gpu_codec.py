@@ -1,5 +1,6 @@
-"""The codec decoder's HIP path (include/codec.h) against the codec oracle
-(oracle/codec.py, fp64), and its slot isolation and streaming state.
+"""The codec's HIP path (include/codec.h), decoder and encoder, against the
+codec oracle (oracle/codec.py, fp64), and its slot isolation and streaming
+state.
 
 Stored keys and values: both sides round them to bf16, the GPU from its
 fp32 value and the oracle from the fp64 value, so where the two lie on
@@ -19,6 +20,15 @@ fp32 with bf16 weights (the transformer's GEMM inputs as bf16 hi/lo pairs),
 the oracle in fp64 with the same weights; the oracle's own fp32 run sits
 about 3e-6 (relative L2) from its fp64 run at the full shape, and the bound
 is 5e-5 relative L2 and 5e-5 of the frame's largest sample elementwise.
+Encoder: the latent fed to the transformer (fp32 convolutions over 1920
+samples) and the transformer output are held to the same bounds.  The
+quantiser's argmin is an integer decision from floating point: the GPU's
+distances are fp32 (|c|^2 - 2 r.c), the oracle's fp64 (|r - c|^2), so at a
+near tie they can pick different rows.  The oracle takes the GPU's code
+where it is its own choice or within 2^-14 of |r|^2 + |c|^2 of its best
+distance (a near tie); such substitutions are counted and reported, and the
+residual then carries on from the same row on both sides.
+
 Parity with the real Mimi codec is unpinned: its layers and weights are not
 available (the structure is a reading of the SoundStream / EnCodec family
 the pages name)."""
@@ -34,6 +44,7 @@ pytestmark = pytest.mark.gpu
 REL_L2 = 5e-5
 MAX_REL = 5e-5
 KV_ERR = 2.0 ** -12  # of the head vector's RMS
+TIE = 2.0 ** -14     # of |r|^2 + |c|^2
 
 
 def _say(msg):
@@ -153,6 +164,115 @@ def test_codec_slots_are_independent_and_reset_is_fresh():
                 e.decode(bad)
             assert ex.value.code == pp.PP_EINVAL
         got = e.decode(c)
+        np.testing.assert_array_equal(got[3], ref[t], err_msg=f"frame {t} slot 3")
+        if t >= 7:
+            np.testing.assert_array_equal(got[1], ref[t1], err_msg=f"frame {t} slot 1 (reset at 7)")
+            t1 += 1
+    e.close()
+
+
+class _GpuCodes:
+    """The oracle's quantiser hook: takes the GPU's code of the frame just
+    encoded where it is the oracle's own choice or a near tie with it."""
+
+    def __init__(self):
+        self.codes, self.subs, self.checked = None, 0, 0
+
+    def __call__(self, slot, q, r, dist, c):
+        g = int(self.codes[slot, q])
+        self.checked += 1
+        if g != c:
+            scale = float(np.dot(r, r)) + float(dist[c]) + 1e-30
+            assert dist[g] - dist[c] <= TIE * scale, \
+                f"slot {slot} stage {q}: GPU code {g} at distance {dist[g]:.6g}, oracle's {c} at {dist[c]:.6g}"
+            self.subs += 1
+        return g
+
+
+def _encoder_parity_run(cd, w, B, n, seed, report):
+    pcm = [synth.user_audio(seed + b, n, cd.samples) for b in range(B)]
+    o = oracle_codec.CodecOracle(cd, w, B, np.float64)
+    caches, codes = _GpuCaches(cd), _GpuCodes()
+    o.enc_store_hook, o.code_hook = caches, codes
+    e = _engine(cd, w, B)
+    worst = [0.0, 0.0]
+    for t in range(n):
+        x = np.stack([pcm[b][t] for b in range(B)])
+        got = e.encode(x)
+        taps = e.taps()
+        caches.ring, codes.codes = taps["enc_ring"], got
+        ref = o.encode(x)
+        np.testing.assert_array_equal(got, ref, err_msg=f"frame {t}")  # the hook took the GPU's only at near ties
+        for b in range(B):
+            ye, _ = _compare(taps["enc_y"][b], o.enc_slots[b].last_y, f"frame {t} slot {b} latent")
+            ze, _ = _compare(taps["enc_z"][b], o.enc_slots[b].last_z, f"frame {t} slot {b} transformer output")
+            worst = [max(worst[0], ye), max(worst[1], ze)]
+    timing = e.time_encode(10)
+    e.close()
+    report(f"latent worst rel-L2 {worst[0]:.2e}, transformer output {worst[1]:.2e}; codes {codes.checked}, "
+           f"near-tie substitutions {codes.subs}; stored keys and values {caches.checked}, of which {caches.flips} "
+           f"differ from the oracle's rounding; device time per call {timing:.3f} ms")
+
+
+@pytest.mark.timeout(600)
+def test_tiny_encoder_matches_oracle_over_a_wrapping_window():
+    cd = synth.CODEC_TINY
+    _say(f"case: tiny codec encoder, B=2, {3 * cd.window + 2} frames (window {cd.window})")
+    _encoder_parity_run(cd, synth.make_codec_weights(cd, seed=1), 2, 3 * cd.window + 2, 70, _say)
+
+
+@pytest.mark.timeout(600)
+def test_encoder_with_a_ragged_codebook_matches_oracle():
+    """100 codewords: the quantiser's last tile of codewords is partly past
+    the codebook's end; 3 codebooks, B=3."""
+    import dataclasses
+    cd = dataclasses.replace(synth.CODEC_TINY, card=100, n_q=3)
+    _say(f"case: tiny codec encoder, card 100, n_q 3, B=3, {cd.window + 3} frames")
+    _encoder_parity_run(cd, synth.make_codec_weights(cd, seed=2), 3, cd.window + 3, 90, _say)
+
+
+@pytest.mark.timeout(600)
+def test_full_encoder_matches_oracle():
+    cd = synth.CODEC
+    _say("case: codec encoder at the full shape (1920 samples per frame), B=2, 6 frames")
+    _encoder_parity_run(cd, synth.make_codec_weights(cd, seed=0), 2, 6, 80, _say)
+
+
+@pytest.mark.timeout(600)
+def test_encoder_slots_are_independent_and_reset_is_fresh():
+    """B = 5 against B = 1, bit for bit, as for the decoder: slot 3 carries the
+    single slot's audio; slot 1 is reset mid-stream and fed it from the
+    start; a timing launch and a rejected call (a NaN sample) in between."""
+    import torch
+    from full_duplex_speech_moshi_amd import codec, pp
+    cd = synth.CODEC_TINY
+    w = synth.make_codec_weights(cd, seed=3)
+    dev = codec.upload_codec_weights(cd, w, torch.device("cuda:0"))
+    n = 2 * cd.window + 3
+    mine = synth.user_audio(90, n, cd.samples)
+    noise = synth.user_audio(91, n, cd.samples)
+    single = _engine(cd, w, 1, dev)
+    ref = [single.encode(mine[t][None])[0] for t in range(n)]
+    single.close()
+    _say("case: tiny codec encoder, B=5 vs B=1, reset at frame 7")
+    e = _engine(cd, w, 5, dev)
+    t1 = 0
+    for t in range(n):
+        x = np.stack([noise[(t + b) % n] for b in range(5)])
+        x[3] = mine[t]
+        if t == 7:
+            e.reset(1)
+            t1 = 0
+        if t >= 7:
+            x[1] = mine[t1]
+        if t == 9:
+            e.time_encode(3)
+            bad = x.copy()
+            bad[2, cd.samples // 2] = np.nan
+            with pytest.raises(pp.PPError) as ex:
+                e.encode(bad)
+            assert ex.value.code == pp.PP_EINVAL
+        got = e.encode(x)
         np.testing.assert_array_equal(got[3], ref[t], err_msg=f"frame {t} slot 3")
         if t >= 7:
             np.testing.assert_array_equal(got[1], ref[t1], err_msg=f"frame {t} slot 1 (reset at 7)")
