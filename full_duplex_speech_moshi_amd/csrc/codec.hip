@@ -253,12 +253,11 @@ static void launch_conv_lpo(const ConvArgs& a, hipStream_t s, int tt) {
   }
 }
 
-// Launch shape: lanes per output group (1, 8 or 64, at most the input
-// channels) so that each lane walks at most 4 input channels where it can
-// (each channel is a dependent round of loads), more if the groups alone do
-// not give CONV_LANES lanes; then, for the causal form, the most outputs per
-// group (8, 4, 2 or 1, at most the samples of the call) that keeps
-// CONV_LANES lanes.  More outputs per group re-read fewer inputs.
+// Launch shape: the fewest lanes per output group (1, 8 or 64, at most the
+// input channels) that still gives CONV_LANES lanes, else the most; then, for
+// the causal form, the most outputs per group (8, 4, 2 or 1, at most the
+// samples of the call) that keeps CONV_LANES lanes.  Fewer lanes per group
+// fold fewer partial sums; more outputs per group re-read fewer inputs.
 void launch_codec_conv(const ConvArgs& a, hipStream_t s) {
   // groups of one output (or one input position)
   const long outs = (long)a.B * a.C_out * (a.strided ? a.T_in / a.stride : a.T_in);
@@ -266,7 +265,7 @@ void launch_codec_conv(const ConvArgs& a, hipStream_t s) {
   for (int c : {1, 8, 64}) {
     if (c > 1 && a.C_in < c) break;
     lpo = c;
-    if (a.C_in <= 4 * c && outs * c >= CONV_LANES) break;
+    if (outs * c >= CONV_LANES) break;
   }
   int tt = 1;
   if (!a.transposed && !a.strided)
