@@ -442,7 +442,7 @@ def main():
         summarize_traffic(args.summarize_traffic)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sessions shard across GPUs "
+        print("bench.py measures one GPU: there is no multi-GPU path (sessions shard across GPUs "
               "with no exchange; run one process per GPU)", file=sys.stderr)
         sys.exit(2)
 

@@ -184,8 +184,9 @@ class CodecDims:
     transformer (the chenxutan.com PersonaPlex article, section 2.3 on Mimi:
     24 kHz audio <-> 12.5 Hz tokens, 1.1 kbps, causal, transformers in the
     encoder and decoder; the recipe's "Architecture": 8 codebooks of 2048,
-    1920 samples per 80 ms frame).  Everything else here is this build's
-    choice: the pages give neither the layer structure nor the weights."""
+    1920 samples per 80 ms frame).  Everything else here is a choice made
+    where the pages are silent: they give neither the layer structure nor the
+    weights."""
     n_q: int = 8                  # codebooks per frame (agent rows 1-8)
     card: int = 2048              # entries per codebook
     d: int = 512                  # latent width = transformer width

@@ -11,8 +11,8 @@ PersonaPlex recipe, "Architecture"): a neural codec of the SoundStream /
 EnCodec family that turns 12.5 Hz frames of 8 codebooks (2048 entries each,
 1.1 kbps) back into 24 kHz audio, 1920 samples per frame; fully causal and
 streaming; a transformer inside the decoder.  The pages give neither its
-layers nor its weights, so the decoder here is this build's reading of that
-family (each point is listed with its reason in the design notes):
+layers nor its weights, so the decoder here is one plain reading of that
+family:
 
 * residual-quantiser decoding: the frame's latent is the sum of the 8
   codebooks' rows, taken in codebook order;

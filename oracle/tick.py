@@ -22,7 +22,7 @@ What one tick computes, per session slot, in the pages' order:
   AUDIO_INITIAL_TOKEN = codec cardinality (the tokens a fresh session's
   column starts from).
 
-Readings taken where the pages are silent (listed with reasons in the design doc):
+Readings taken where the pages are silent:
 eps 1e-5 inside the square root; RoPE base 10000 on pairs (2i, 2i+1) with the
 angle in fp64; window = the W most recent positions including the current
 one; scale 1/sqrt(head_dim), no biases; fused rows laid out [q; k; v] and

@@ -1,4 +1,5 @@
-"""Pins of the codec-decoder oracle (oracle/codec.py) to things outside it.
+"""Pins of the codec oracle (oracle/codec.py, decoder and encoder) to things
+outside it.
 
 * Its causal and transposed convolutions against PyTorch's CPU routines
   (conv1d with left padding, conv_transpose1d), fp64.
@@ -11,8 +12,15 @@
 * The convolutional stack's wiring (ELU placement, upsampling, channel
   order, residual skip from the pre-activation signal, biases) against a
   closed form with pass-through weights.
+* The encoder: its strided convolution against PyTorch's conv1d (stride s,
+  left padding); the nearest-row search against brute force with the
+  lowest index on ties; the residual quantiser against codebooks built so
+  that only stage-by-stage quantisation of what is left gives the codes;
+  its transformer against the tick oracle's temporal block and its own
+  output norm; its streaming against the whole-sequence definition; its
+  convolutional wiring against a closed form with pass-through weights.
 
-The codec's layer structure is this build's reading of the pages (section
+The codec's layer structure is a reading of the pages (section
 2.3 of the chenxutan.com article: a SoundStream/EnCodec-family codec with a
 transformer, 12.5 Hz frames, 24 kHz audio); parity with the real Mimi codec
 is unpinned: its weights and exact layers are not available."""
