@@ -88,196 +88,325 @@ void launch_codec_norm(const CodecNormArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Convolutions.  Output (b, o, t) = bias[o] + sum over input channels i and
-// taps of w * input (plus the skip), stored raw and/or after ELU; the inputs
-// arrive already activated.  A group of LPO lanes owns TT consecutive
-// outputs of one (slot, output channel): lane l takes input channels
-// l, l + LPO, ... in order, keeps the K + TT - 1 inputs its taps reach in
-// registers and the channel's K weights, then the LPO partial sums of each
-// output are folded by a fixed butterfly.  The causal form reads time
-// t - (K-1-k) at tap k; the transposed form gives each thread the `stride`
-// outputs of one input position m (output m s + r reads input m at tap r and
-// input m - 1 at tap r + s).  Times before this call's first input come from
-// the history.
+// Convolutions.  Every form is a sum over (input channel i, tap k) of
+// w[o][i][k] x_ext(i, tau), where x_ext is this call's input after the
+// stream's history (times -H .. -1) and tau depends on the form: causal
+// t - (K-1) + k; strided t s - s + k; transposed (output m s + r, taps r and
+// r + s) m and m - 1.  The inputs arrive already activated.  The output is
+// bias + sum (+ skip), stored raw and/or after ELU.
+//
+// The order of the sum is fixed by the layer's shape alone, never by the
+// batch or the launch shape, so every batch size gives the same bits:
+//   * few input channels (at most CONV_CHAIN_C): one FMA chain per output
+//     over i ascending and, within i, k ascending (transposed: tap r, then
+//     tap r + s), from zero (codec_conv_long_kernel);
+//   * more input channels: the LANES lanes of a workgroup (256 above
+//     CONV_WIDE_KD terms per output, else 64) take the reduction index
+//     kd = lane, lane + LANES, ... (kd = i K + k; transposed kd = 2 i + j for
+//     tap r + j s), each as one FMA chain from zero; lane sums are then added
+//     in runs of 32 lanes, each run in lane order from zero, and the run sums
+//     in run order from zero (codec_conv_deep_kernel).
 // ---------------------------------------------------------------------------
-constexpr int CONV_KMAX = 8;
+constexpr int CONV_CHAIN_C = 32;    // input channels up to which one lane sums an output
+constexpr int CONV_WIDE_KD = 256;   // terms per output above which 256 lanes share a sum
 
 __device__ __forceinline__ float elu_f(float v) { return v > 0.f ? v : expm1f(v); }
 
-template <int LPO, int TT>
-__device__ __forceinline__ void conv_store(const ConvArgs& a, bool live, int l, int b, int o, int t0, int T_out,
-                                           float (&acc)[TT], int n) {
-#pragma unroll
-  for (int u = 0; u < TT; ++u) {
-    if (u < n) {  // n is the same for the whole group (for the whole launch unless ragged)
-#pragma unroll
-      for (int off = LPO / 2; off >= 1; off >>= 1) acc[u] += __shfl_xor(acc[u], off, LPO);
-    }
-  }
-  if (!live || l != 0) return;
-  const long base = ((long)b * a.C_out + o) * T_out + t0;
-  const float bo = a.bias[o];
-#pragma unroll
-  for (int u = 0; u < TT; ++u) {
-    if (u < n) {
-      float y = bo + acc[u];
-      if (a.skip) y += a.skip[base + u];
-      if (a.y) a.y[base + u] = y;
-      if (a.ya) a.ya[base + u] = elu_f(y);
-    }
-  }
+// x_ext(i, tau) of slot b, tau >= -H
+__device__ __forceinline__ float conv_x(const ConvArgs& a, int b, int i, int tau) {
+  return tau >= 0 ? a.x[((long)b * a.C_in + i) * a.T_in + tau] : a.hist[((long)b * a.C_in + i) * a.H + a.H + tau];
 }
 
-// causal convolution: TT consecutive outputs per group
-template <int LPO, int TT>
-__global__ __launch_bounds__(256) void codec_conv_kernel(ConvArgs a) {
-  const int T = a.T_in, nt = (T + TT - 1) / TT;
-  const long n_grp = (long)a.B * a.C_out * nt;
-  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPO;
-  const int l = threadIdx.x % LPO;
-  const bool live = gid < n_grp;
-  const long g = live ? gid : 0;
-  const int t0 = (int)(g % nt) * TT;
-  const int o = (int)((g / nt) % a.C_out);
-  const int b = (int)(g / ((long)nt * a.C_out));
-  const int K = a.K;
-  float acc[TT];
-#pragma unroll
-  for (int u = 0; u < TT; ++u) acc[u] = 0.f;
-#pragma unroll 2
-  for (int i = l; i < a.C_in; i += LPO) {
-    const float* xi = a.x + ((long)b * a.C_in + i) * T;
-    const float* hi = a.hist ? a.hist + ((long)b * a.C_in + i) * a.H : nullptr;
-    const bf16_t* wi = a.w + ((long)o * a.C_in + i) * K;
-    // inputs t0 - (K-1) .. t0 + TT - 1
-    float xv[CONV_KMAX - 1 + TT];
-    float wv[CONV_KMAX];
-#pragma unroll
-    for (int k = 0; k < CONV_KMAX; ++k) wv[k] = k < K ? bf2f(wi[k]) : 0.f;
-#pragma unroll
-    for (int j = 0; j < CONV_KMAX - 1 + TT; ++j) {
-      const int tt = t0 - (K - 1) + j;
-      xv[j] = j >= K - 1 + TT ? 0.f : tt >= T ? 0.f : tt >= 0 ? xi[tt] : hi[a.H + tt];
-    }
-#pragma unroll
-    for (int k = 0; k < CONV_KMAX; ++k) {
-      if (k < K) {
-#pragma unroll
-        for (int u = 0; u < TT; ++u) acc[u] = __builtin_fmaf(wv[k], xv[u + k], acc[u]);
-      }
-    }
-  }
-  conv_store<LPO, TT>(a, live, l, b, o, t0, T, acc, T - t0);
-}
+// the per-slot output columns and the rows of the form (transposed: rows
+// (o, r), row o s + r)
+__device__ __forceinline__ int conv_cols(const ConvArgs& a) { return a.strided ? a.T_in / a.stride : a.T_in; }
+__device__ __forceinline__ int conv_rows(const ConvArgs& a) { return a.transposed ? a.C_out * a.stride : a.C_out; }
 
-// transposed convolution: the `stride` outputs of one input position per group
-template <int LPO>
-__global__ __launch_bounds__(256) void codec_convt_kernel(ConvArgs a) {
-  const int s = a.stride, T = a.T_in, T_out = T * s;
-  const long n_grp = (long)a.B * a.C_out * T;
-  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPO;
-  const int l = threadIdx.x % LPO;
-  const bool live = gid < n_grp;
-  const long g = live ? gid : 0;
-  const int m = (int)(g % T);
-  const int o = (int)((g / T) % a.C_out);
-  const int b = (int)(g / ((long)T * a.C_out));
-  float acc[CONV_KMAX];
-#pragma unroll
-  for (int r = 0; r < CONV_KMAX; ++r) acc[r] = 0.f;
-#pragma unroll 2
-  for (int i = l; i < a.C_in; i += LPO) {
-    const float* xi = a.x + ((long)b * a.C_in + i) * T;
-    const float x0 = xi[m];
-    const float x1 = m > 0 ? xi[m - 1] : a.hist[((long)b * a.C_in + i) * a.H + a.H - 1];
-    const bf16_t* wi = a.w + ((long)o * a.C_in + i) * a.K;
-#pragma unroll
-    for (int r = 0; r < CONV_KMAX; ++r) {
-      if (r < s) acc[r] = __builtin_fmaf(bf2f(wi[r + s]), x1, __builtin_fmaf(bf2f(wi[r]), x0, acc[r]));
-    }
-  }
-  conv_store<LPO, CONV_KMAX>(a, live, l, b, o, m * s, T_out, acc, s);
-}
-
-// Enough lanes for the part (256 CUs x 4 SIMDs x 2 waves of 64).
-constexpr long CONV_LANES = 1L << 17;
-
-// strided convolution: one output per group
-template <int LPO>
-__global__ __launch_bounds__(256) void codec_convs_kernel(ConvArgs a) {
-  const int s = a.stride, T = a.T_in, T_out = T / s;
-  const long n_grp = (long)a.B * a.C_out * T_out;
-  const long gid = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPO;
-  const int l = threadIdx.x % LPO;
-  const bool live = gid < n_grp;
-  const long g = live ? gid : 0;
-  const int t = (int)(g % T_out);
-  const int o = (int)((g / T_out) % a.C_out);
-  const int b = (int)(g / ((long)T_out * a.C_out));
-  float acc[1] = {0.f};
-#pragma unroll 2
-  for (int i = l; i < a.C_in; i += LPO) {
-    const float* xi = a.x + ((long)b * a.C_in + i) * T;
-    const float* hi = a.hist + ((long)b * a.C_in + i) * a.H;
-    const bf16_t* wi = a.w + ((long)o * a.C_in + i) * a.K;
-#pragma unroll
-    for (int k = 0; k < 2 * CONV_KMAX; ++k) {
-      if (k < a.K) {
-        const int u = t * s - s + k;  // input time, >= -s
-        const float v = u >= 0 ? xi[u] : hi[a.H + u];
-        acc[0] = __builtin_fmaf(bf2f(wi[k]), v, acc[0]);
-      }
-    }
-  }
-  conv_store<LPO, 1>(a, live, l, b, o, t, T_out, acc, 1);
-}
-
-template <int LPO>
-static void launch_conv_lpo(const ConvArgs& a, hipStream_t s, int tt) {
-  const long groups = (long)a.B * a.C_out *
-                      (a.transposed ? a.T_in : a.strided ? a.T_in / a.stride : (a.T_in + tt - 1) / tt);
-  const dim3 grid((unsigned)((groups * LPO + 255) / 256));
+// bias + v (+ skip) of (row, slot b, column t), stored raw and/or after ELU
+__device__ __forceinline__ void conv_out(const ConvArgs& a, int row, int b, int t, float v) {
+  int o = row, to = t, T_out = a.T_in;
   if (a.transposed) {
-    hipLaunchKernelGGL(codec_convt_kernel<LPO>, grid, dim3(256), 0, s, a);
-    return;
+    o = row / a.stride;
+    to = t * a.stride + (row - o * a.stride);
+    T_out = a.T_in * a.stride;
+  } else if (a.strided) {
+    T_out = a.T_in / a.stride;
   }
-  if (a.strided) {
-    hipLaunchKernelGGL(codec_convs_kernel<LPO>, grid, dim3(256), 0, s, a);
-    return;
+  const long idx = ((long)b * a.C_out + o) * T_out + to;
+  float y = a.bias[o] + v;
+  if (a.skip) y += a.skip[idx];
+  if (a.y) a.y[idx] = y;
+  if (a.ya) a.ya[idx] = elu_f(y);
+}
+
+// Split sums: a workgroup of LANES lanes (64 or 256) computes OC rows x NC
+// columns (column = slot * columns per slot + t), E = OC NC <= 32 outputs.
+template <int LANES, int OC, int NC>
+__global__ __launch_bounds__(LANES) void codec_conv_deep_kernel(ConvArgs a) {
+  constexpr int E = OC * NC, RUNS = LANES / 32;
+  static_assert(E <= 32 && LANES % 32 == 0, "at most 32 outputs; runs of 32 lanes");
+  __shared__ float red[LANES][E + 1];
+  __shared__ float run[RUNS][E];
+  const int tid = threadIdx.x;
+  const int Tc = conv_cols(a), Mr = conv_rows(a), KK = a.transposed ? 2 : a.K, Kd = a.C_in * KK;
+  const int s = a.stride, row0 = blockIdx.y * OC;
+  const long ncols = (long)a.B * Tc, col0 = (long)blockIdx.x * NC;
+  int cb[NC], ct[NC];
+  bool cok[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const long col = col0 + c;
+    cok[c] = col < ncols;
+    const long cc = cok[c] ? col : 0;
+    cb[c] = (int)(cc / Tc);
+    ct[c] = (int)(cc - (long)cb[c] * Tc);
   }
-  switch (tt) {
-    case 8: hipLaunchKernelGGL((codec_conv_kernel<LPO, 8>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((codec_conv_kernel<LPO, 4>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((codec_conv_kernel<LPO, 2>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((codec_conv_kernel<LPO, 1>), grid, dim3(256), 0, s, a); break;
+  // weight row offsets (transposed: o's row and the phase r)
+  long wro[OC];
+  int wph[OC];
+  bool rok[OC];
+#pragma unroll
+  for (int oc = 0; oc < OC; ++oc) {
+    const int row = row0 + oc;
+    rok[oc] = row < Mr;
+    const int rr = rok[oc] ? row : 0;
+    const int o = a.transposed ? rr / s : rr;
+    wph[oc] = a.transposed ? rr - o * s : 0;
+    wro[oc] = (long)o * a.C_in * a.K;
+  }
+  float acc[OC][NC];
+#pragma unroll
+  for (int oc = 0; oc < OC; ++oc)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[oc][c] = 0.f;
+  // four reduction steps' loads in flight at once
+#pragma unroll 4
+  for (int kd = tid; kd < Kd; kd += LANES) {
+    const int i = kd / KK, k = kd - i * KK;
+    float wv[OC];
+#pragma unroll
+    for (int oc = 0; oc < OC; ++oc) {
+      const int tap = a.transposed ? wph[oc] + k * s : k;
+      wv[oc] = rok[oc] ? bf2f(a.w[wro[oc] + (long)i * a.K + tap]) : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!cok[c]) continue;  // uniform over the workgroup
+      const int tau = a.transposed ? ct[c] - k : a.strided ? ct[c] * s - s + k : ct[c] - (a.K - 1) + k;
+      const float xv = conv_x(a, cb[c], i, tau);
+#pragma unroll
+      for (int oc = 0; oc < OC; ++oc) acc[oc][c] = __builtin_fmaf(wv[oc], xv, acc[oc][c]);
+    }
+  }
+#pragma unroll
+  for (int oc = 0; oc < OC; ++oc)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) red[tid][oc * NC + c] = acc[oc][c];
+  __syncthreads();
+  // run p of output e: lanes 32 p .. 32 p + 31 in lane order
+  for (int t = tid; t < RUNS * E; t += LANES) {
+    const int e = t % E, p = t / E;
+    float v = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) v += red[p * 32 + j][e];
+    run[p][e] = v;
+  }
+  __syncthreads();
+  if (tid < E) {
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < RUNS; ++p) v += run[p][tid];
+    const int oc = tid / NC, c = tid - oc * NC;
+    const int row = row0 + oc;
+    const long col = col0 + c;
+    if (row < Mr && col < ncols) {
+      const int b = (int)(col / Tc);
+      conv_out(a, row, b, (int)(col - (long)b * Tc), v);
+    }
   }
 }
 
-// Launch shape: the fewest lanes per output group (1, 8 or 64, at most the
-// input channels) that still gives CONV_LANES lanes, else the most; then, for
-// the causal form, the most outputs per group (8, 4, 2 or 1, at most the
-// samples of the call) that keeps CONV_LANES lanes.  Fewer lanes per group
-// fold fewer partial sums; more outputs per group re-read fewer inputs.
-void launch_codec_conv(const ConvArgs& a, hipStream_t s) {
-  // groups of one output (or one input position)
-  const long outs = (long)a.B * a.C_out * (a.strided ? a.T_in / a.stride : a.T_in);
-  int lpo = 1;
-  for (int c : {1, 8, 64}) {
-    if (c > 1 && a.C_in < c) break;
-    lpo = c;
-    if (outs * c >= CONV_LANES) break;
+// Chained sums: workgroup (thread block, channel block) stages the OC output
+// channels' weights in LDS as fp32 [C_in][K][OC]; thread n owns TT
+// consecutive columns of those channels for slot n / (column tiles per
+// slot) (transposed: TT input positions, S outputs each; strided: S is the
+// stride; for the causal form S is the kernel K).  FORM 0 causal,
+// 1 strided, 2 transposed.
+template <int FORM, int OC, int TT, int S>
+__global__ __launch_bounds__(256) void codec_conv_long_kernel(ConvArgs a) {
+  extern __shared__ float wl[];
+  constexpr int K = FORM == 0 ? S : 2 * S;
+  const int tid = threadIdx.x, o0 = blockIdx.y * OC;
+  for (int e = tid; e < a.C_in * K * OC; e += 256) {
+    const int oc = e % OC, k = (e / OC) % K, i = e / (OC * K);
+    const int o = o0 + oc;
+    wl[e] = o < a.C_out ? bf2f(a.w[((long)o * a.C_in + i) * K + k]) : 0.f;
   }
-  int tt = 1;
-  if (!a.transposed && !a.strided)
-    for (int c : {8, 4, 2}) {
-      if (c <= a.T_in && (long)a.B * a.C_out * ((a.T_in + c - 1) / c) * lpo >= CONV_LANES) {
-        tt = c;
-        break;
+  __syncthreads();
+  const int Tc = FORM == 1 ? a.T_in / S : a.T_in;
+  const int nt = (Tc + TT - 1) / TT;
+  const long n = (long)blockIdx.x * 256 + tid;
+  if (n >= (long)a.B * nt) return;
+  const int b = (int)(n / nt), t0 = (int)(n - (long)b * nt) * TT;
+  // inputs the thread's taps reach, from time tau0
+  constexpr int NW = FORM == 0 ? TT + K - 1 : FORM == 1 ? TT * S + S : TT + 1;
+  const int tau0 = FORM == 0 ? t0 - (K - 1) : FORM == 1 ? t0 * S - S : t0 - 1;
+  constexpr int NO = FORM == 2 ? TT * S : TT;  // outputs per channel
+  float acc[OC][NO];
+#pragma unroll
+  for (int oc = 0; oc < OC; ++oc)
+#pragma unroll
+    for (int u = 0; u < NO; ++u) acc[oc][u] = 0.f;
+  // several channels' loads in flight at once: more for small tiles
+  // (a channel holds NW inputs and K x OC weights in registers: about 96 of
+  // them over the channels in flight, at most 32 channels)
+  constexpr int PER_CH = NW + K * OC;
+  constexpr int UNR = PER_CH * 32 <= 96 ? 32 : PER_CH * 16 <= 96 ? 16 : PER_CH * 8 <= 96 ? 8
+                      : PER_CH * 4 <= 96 ? 4 : PER_CH * 2 <= 96 ? 2 : 1;
+#pragma unroll UNR
+  for (int i = 0; i < a.C_in; ++i) {
+    float xw[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int tau = tau0 + j;
+      // past this call's inputs only for a slot's last tile
+      xw[j] = tau < a.T_in ? conv_x(a, b, i, tau) : 0.f;
+    }
+    const float* wi = wl + (long)i * K * OC;
+    if constexpr (FORM == 0) {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int oc = 0; oc < OC; ++oc) {
+          const float w = wi[k * OC + oc];
+#pragma unroll
+          for (int u = 0; u < TT; ++u) acc[oc][u] = __builtin_fmaf(w, xw[u + k], acc[oc][u]);
+        }
+    } else if constexpr (FORM == 1) {
+#pragma unroll
+      for (int k = 0; k < 2 * S; ++k)
+#pragma unroll
+        for (int oc = 0; oc < OC; ++oc) {
+          const float w = wi[k * OC + oc];
+#pragma unroll
+          for (int u = 0; u < TT; ++u) acc[oc][u] = __builtin_fmaf(w, xw[u * S + k], acc[oc][u]);
+        }
+    } else {
+      // output (u, r): tap r on input t0 + u (xw[u + 1]), then tap r + S on
+      // input t0 + u - 1 (xw[u])
+#pragma unroll
+      for (int r = 0; r < S; ++r)
+#pragma unroll
+        for (int oc = 0; oc < OC; ++oc) {
+          const float w0 = wi[r * OC + oc], w1 = wi[(r + S) * OC + oc];
+#pragma unroll
+          for (int u = 0; u < TT; ++u) {
+            acc[oc][u * S + r] = __builtin_fmaf(w0, xw[u + 1], acc[oc][u * S + r]);
+            acc[oc][u * S + r] = __builtin_fmaf(w1, xw[u], acc[oc][u * S + r]);
+          }
+        }
+    }
+  }
+#pragma unroll
+  for (int oc = 0; oc < OC; ++oc) {
+    if (o0 + oc >= a.C_out) continue;
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+      if (t0 + u >= Tc) continue;
+      if constexpr (FORM == 2) {
+#pragma unroll
+        for (int r = 0; r < S; ++r) conv_out(a, (o0 + oc) * S + r, b, t0 + u, acc[oc][u * S + r]);
+      } else {
+        conv_out(a, o0 + oc, b, t0 + u, acc[oc][u]);
       }
     }
-  if (lpo == 64) launch_conv_lpo<64>(a, s, tt);
-  else if (lpo == 8) launch_conv_lpo<8>(a, s, tt);
-  else launch_conv_lpo<1>(a, s, tt);
+  }
+}
+
+// Threads a chained-sum launch should reach before its tile grows.
+constexpr long CONV_THREADS = 1L << 15;
+
+template <int FORM, int OC, int TT, int S>
+static void launch_long(const ConvArgs& a, hipStream_t st, int Tc) {
+  const long threads = (long)a.B * ((Tc + TT - 1) / TT);
+  const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)((a.C_out + OC - 1) / OC));
+  const size_t lds = (size_t)a.C_in * a.K * OC * 4;
+  hipLaunchKernelGGL((codec_conv_long_kernel<FORM, OC, TT, S>), grid, dim3(256), lds, st, a);
+}
+
+// Chained-sum launch shape (the arithmetic does not depend on it): the largest
+// tile of OC output channels x TT columns that still gives CONV_THREADS
+// threads, else one output channel and one column per thread.
+template <int FORM, int S>
+static void launch_long_tile(const ConvArgs& a, hipStream_t st, int Tc) {
+  auto threads = [&](int oc, int tt) { return (long)a.B * ((a.C_out + oc - 1) / oc) * ((Tc + tt - 1) / tt); };
+  if constexpr (FORM == 0) {  // S = K
+    if (a.C_out >= 8 && threads(8, 4) >= CONV_THREADS) launch_long<0, 8, 4, S>(a, st, Tc);
+    else if (a.C_out >= 8 && threads(8, 2) >= CONV_THREADS) launch_long<0, 8, 2, S>(a, st, Tc);
+    else if (a.C_out >= 4 && threads(4, 1) >= CONV_THREADS) launch_long<0, 4, 1, S>(a, st, Tc);
+    else launch_long<0, 1, 1, S>(a, st, Tc);
+  } else if constexpr (FORM == 1) {
+    if (a.C_out >= 8 && threads(8, 2) >= CONV_THREADS) launch_long<1, 8, 2, S>(a, st, Tc);
+    else if (a.C_out >= 4 && threads(4, 1) >= CONV_THREADS) launch_long<1, 4, 1, S>(a, st, Tc);
+    else launch_long<1, 1, 1, S>(a, st, Tc);
+  } else {
+    constexpr int TT = S >= 8 ? 1 : 8 / S;
+    if (a.C_out >= 4 && threads(4, TT) >= CONV_THREADS) launch_long<2, 4, TT, S>(a, st, Tc);
+    else launch_long<2, 1, 1, S>(a, st, Tc);
+  }
+}
+
+// FORM 0: by the kernel K; else by the stride
+template <int FORM>
+static void launch_long_s(const ConvArgs& a, hipStream_t st, int Tc) {
+  switch (FORM == 0 ? a.K : a.stride) {
+    case 1: launch_long_tile<FORM, 1>(a, st, Tc); break;
+    case 2: launch_long_tile<FORM, 2>(a, st, Tc); break;
+    case 3: launch_long_tile<FORM, 3>(a, st, Tc); break;
+    case 4: launch_long_tile<FORM, 4>(a, st, Tc); break;
+    case 5: launch_long_tile<FORM, 5>(a, st, Tc); break;
+    case 6: launch_long_tile<FORM, 6>(a, st, Tc); break;
+    case 7: launch_long_tile<FORM, 7>(a, st, Tc); break;
+    default: launch_long_tile<FORM, 8>(a, st, Tc); break;
+  }
+}
+
+template <int LANES, int OC, int NC>
+static void launch_deep_tile(const ConvArgs& a, hipStream_t st, long ncols, int rows) {
+  const dim3 grid((unsigned)((ncols + NC - 1) / NC), (unsigned)((rows + OC - 1) / OC));
+  hipLaunchKernelGGL((codec_conv_deep_kernel<LANES, OC, NC>), grid, dim3(LANES), 0, st, a);
+}
+
+// Split-sum tile (launch shape only): 32 outputs per workgroup, in columns
+// when the batch has at least as many columns as rows, while that leaves
+// CONV_DEEP_WGS workgroups; else 8; with a single column, 4 rows.
+constexpr long CONV_DEEP_WGS = 512;
+template <int LANES>
+static void launch_deep(const ConvArgs& a, hipStream_t st, int Tc) {
+  const long ncols = (long)a.B * Tc;
+  const int rows = a.transposed ? a.C_out * a.stride : a.C_out;
+  auto wgs = [&](int oc, int nc) { return ((rows + oc - 1) / oc) * ((ncols + nc - 1) / nc); };
+  const bool wide = ncols >= rows;
+  if (ncols == 1) launch_deep_tile<LANES, 4, 1>(a, st, ncols, rows);
+  else if (wide && wgs(4, 8) >= CONV_DEEP_WGS) launch_deep_tile<LANES, 4, 8>(a, st, ncols, rows);
+  else if (!wide && wgs(8, 4) >= CONV_DEEP_WGS) launch_deep_tile<LANES, 8, 4>(a, st, ncols, rows);
+  else if (wide) launch_deep_tile<LANES, 2, 4>(a, st, ncols, rows);
+  else launch_deep_tile<LANES, 4, 2>(a, st, ncols, rows);
+}
+
+// The kernel by the layer's shape (input channels, terms per output), the
+// tile by the launch.
+void launch_codec_conv(const ConvArgs& a, hipStream_t st) {
+  const int Tc = a.strided ? a.T_in / a.stride : a.T_in;
+  if (a.C_in <= CONV_CHAIN_C) {  // weights of 8 channels in LDS: at most 32 x 16 x 8 floats
+    if (a.transposed) launch_long_s<2>(a, st, Tc);
+    else if (a.strided) launch_long_s<1>(a, st, Tc);
+    else launch_long_s<0>(a, st, Tc);
+    return;
+  }
+  const long kd = (long)a.C_in * (a.transposed ? 2 : a.K);
+  if (kd > CONV_WIDE_KD) launch_deep<256>(a, st, Tc);
+  else launch_deep<64>(a, st, Tc);
 }
 
 // ---------------------------------------------------------------------------

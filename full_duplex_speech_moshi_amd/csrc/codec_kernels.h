@@ -1,11 +1,12 @@
-// Kernels of the streaming codec decoder (codec.hip) and their arguments.
-// The decoder's transformer layers run on the tick's GEMM and ring-decode
-// launchers (kernels.h); these are the rest: the residual-quantiser sum, the
-// output norm, the causal (transposed) convolutions and the streaming-state
-// update.  Layouts: activations fp32 [B][C][T] (T = samples of this call at
-// the layer's rate), convolution weights bf16 [C_out][C_in][K], histories
-// fp32 [B][C][H] (the H inputs before this call, raw: the activation is
-// applied when they are read).
+// Kernels of the streaming codec (codec.hip) and their arguments.  The
+// transformer layers of both directions run on the tick's GEMM and
+// ring-decode launchers (kernels.h); these are the rest: the codebook sum
+// (or the encoder's latent) into the first layer, the output norm, the causal
+// (transposed, strided) convolutions, the residual quantiser and the
+// streaming-state update.  Layouts: activations fp32 [B][C][T] (T = samples
+// of this call at the layer's rate), convolution weights bf16
+// [C_out][C_in][K], histories fp32 [B][C][H] (the H inputs before this call,
+// as the layer is fed them: after their ELU).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -278,3 +278,92 @@ def test_encoder_slots_are_independent_and_reset_is_fresh():
             np.testing.assert_array_equal(got[1], ref[t1], err_msg=f"frame {t} slot 1 (reset at 7)")
             t1 += 1
     e.close()
+
+
+# The launch configuration the codec benchmark times: B = 32 at the full
+# shape.  Two slots (the first and the last) against the oracle, with the
+# stored keys and values checked and adopted as in the B = 2 runs, and one
+# slot against a B = 1 handle bit for bit (every launch shape of the batch
+# must give a slot the same arithmetic).
+B32, PICKS, SAME = 32, (0, 31), 17
+
+
+@pytest.mark.timeout(900)
+def test_full_codec_b32_matches_oracle_and_b1():
+    import torch
+    from full_duplex_speech_moshi_amd import codec
+    cd = synth.CODEC
+    w = synth.make_codec_weights(cd, seed=0)
+    dev = codec.upload_codec_weights(cd, w, torch.device("cuda:0"))
+    n = 4
+    frames = [synth.agent_frames(200 + b, n) for b in range(B32)]
+    _say(f"case: codec decoder at the full shape, B=1 reference for slot {SAME}, {n} frames")
+    single = _engine(cd, w, 1, dev)
+    ref1 = []
+    for t in range(n):
+        pcm = single.decode(frames[SAME][t][None])[0]
+        ref1.append((pcm, single.taps()["z"][0]))
+    single.close()
+    _say(f"case: codec decoder at the full shape, B={B32}, slots {PICKS} against the oracle")
+    o = oracle_codec.CodecOracle(cd, w, len(PICKS), np.float64)
+    hook = _GpuCaches(cd)
+    o.store_hook = hook
+    e = _engine(cd, w, B32, dev)
+    worst = [0.0, 0.0]
+    for t in range(n):
+        c = np.stack([frames[b][t] for b in range(B32)])
+        got = e.decode(c)
+        taps = e.taps()
+        np.testing.assert_array_equal(got[SAME], ref1[t][0], err_msg=f"frame {t}: B={B32} slot {SAME} vs B=1")
+        np.testing.assert_array_equal(taps["z"][SAME], ref1[t][1], err_msg=f"frame {t}: transformer output")
+        hook.ring = taps["ring"][list(PICKS)]
+        ref = o.decode(c[list(PICKS)])
+        for k, b in enumerate(PICKS):
+            err, _ = _compare(got[b], ref[k], f"frame {t} slot {b}")
+            zerr, _ = _compare(taps["z"][b], o.slots[k].last_z, f"frame {t} slot {b} transformer output")
+            worst = [max(worst[0], err), max(worst[1], zerr)]
+    e.close()
+    _say(f"samples worst rel-L2 {worst[0]:.2e}, transformer output {worst[1]:.2e}; stored keys and values "
+         f"{hook.checked}, {hook.flips} on the other side of a rounding point")
+
+
+@pytest.mark.timeout(900)
+def test_full_encoder_b32_matches_oracle_and_b1():
+    import torch
+    from full_duplex_speech_moshi_amd import codec
+    cd = synth.CODEC
+    w = synth.make_codec_weights(cd, seed=0)
+    dev = codec.upload_codec_weights(cd, w, torch.device("cuda:0"))
+    n = 4
+    pcm = [synth.user_audio(300 + b, n, cd.samples) for b in range(B32)]
+    _say(f"case: codec encoder at the full shape, B=1 reference for slot {SAME}, {n} frames")
+    single = _engine(cd, w, 1, dev)
+    ref1 = []
+    for t in range(n):
+        codes1 = single.encode(pcm[SAME][t][None])[0]
+        tp = single.taps()
+        ref1.append((codes1, tp["enc_y"][0], tp["enc_z"][0]))
+    single.close()
+    _say(f"case: codec encoder at the full shape, B={B32}, slots {PICKS} against the oracle")
+    o = oracle_codec.CodecOracle(cd, w, len(PICKS), np.float64)
+    caches, codes = _GpuCaches(cd), _GpuCodes()
+    o.enc_store_hook, o.code_hook = caches, codes
+    e = _engine(cd, w, B32, dev)
+    worst = [0.0, 0.0]
+    for t in range(n):
+        x = np.stack([pcm[b][t] for b in range(B32)])
+        got = e.encode(x)
+        taps = e.taps()
+        np.testing.assert_array_equal(got[SAME], ref1[t][0], err_msg=f"frame {t}: B={B32} slot {SAME} vs B=1")
+        np.testing.assert_array_equal(taps["enc_y"][SAME], ref1[t][1], err_msg=f"frame {t}: latent")
+        np.testing.assert_array_equal(taps["enc_z"][SAME], ref1[t][2], err_msg=f"frame {t}: transformer output")
+        caches.ring, codes.codes = taps["enc_ring"][list(PICKS)], got[list(PICKS)]
+        ref = o.encode(x[list(PICKS)])
+        np.testing.assert_array_equal(got[list(PICKS)], ref, err_msg=f"frame {t}")
+        for k, b in enumerate(PICKS):
+            ye, _ = _compare(taps["enc_y"][b], o.enc_slots[k].last_y, f"frame {t} slot {b} latent")
+            ze, _ = _compare(taps["enc_z"][b], o.enc_slots[k].last_z, f"frame {t} slot {b} transformer output")
+            worst = [max(worst[0], ye), max(worst[1], ze)]
+    e.close()
+    _say(f"latent worst rel-L2 {worst[0]:.2e}, transformer output {worst[1]:.2e}; codes {codes.checked}, "
+         f"near-tie substitutions {codes.subs}")
