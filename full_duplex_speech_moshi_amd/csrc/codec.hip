@@ -1,17 +1,17 @@
-// Streaming codec decoder (code2wav) kernels for gfx950: the residual-
-// quantiser sum, the output norm, the causal and transposed convolutions of
-// the upsampling stack, and the streaming-state update.
+// Streaming codec kernels for gfx950, both directions: the transformer's
+// input (the codebook sum, or the encoder's latent), the output norm, the
+// causal, transposed and strided convolutions, residual vector quantisation,
+// and the streaming-state update.
 //
 // chenxutan.com PersonaPlex article, section 2.3 on Mimi: a causal codec of
-// the SoundStream / EnCodec family that turns 12.5 Hz frames of 8 codebooks
-// back into 24 kHz audio; PersonaPlex recipe, "Architecture": 1920 samples
-// per 80 ms frame.  The layer structure is this library's reading of that
-// family (codec.h).  The work is small and latency-bound (at most a few
-// hundred thousand outputs per call, each a sum of 16 to 3584 products), so
-// the convolutions are direct sums on the vector ALU in fp32: a group of
-// lanes per output splits the (input channel, tap) sum in a fixed order and
-// folds it with a fixed butterfly, so each slot's result depends only on its
-// own inputs.
+// the SoundStream / EnCodec family between 24 kHz audio and 12.5 Hz frames
+// of codebook indices; PersonaPlex recipe, "Architecture": 8 codebooks of
+// 2048 entries, 1920 samples per 80 ms frame.  The layer structure is this
+// library's reading of that family (codec.h).  The work is small and
+// latency-bound (at most a few hundred thousand outputs per call, each a sum
+// of 8 to 3584 products), so the convolutions are direct sums on the vector
+// ALU in fp32, each output's sum in an order fixed by the layer's shape, so
+// that a slot's result depends only on its own inputs.
 #include "codec_kernels.h"
 #include "device.h"
 
@@ -99,13 +99,13 @@ void launch_codec_norm(const CodecNormArgs& a, hipStream_t s) {
 // batch or the launch shape, so every batch size gives the same bits:
 //   * few input channels (at most CONV_CHAIN_C): one FMA chain per output
 //     over i ascending and, within i, k ascending (transposed: tap r, then
-//     tap r + s), from zero (codec_conv_long_kernel);
+//     tap r + s), from zero (codec_conv_chain_kernel);
 //   * more input channels: the LANES lanes of a workgroup (256 above
 //     CONV_WIDE_KD terms per output, else 64) take the reduction index
 //     kd = lane, lane + LANES, ... (kd = i K + k; transposed kd = 2 i + j for
 //     tap r + j s), each as one FMA chain from zero; lane sums are then added
 //     in runs of 32 lanes, each run in lane order from zero, and the run sums
-//     in run order from zero (codec_conv_deep_kernel).
+//     in run order from zero (codec_conv_split_kernel).
 // ---------------------------------------------------------------------------
 constexpr int CONV_CHAIN_C = 32;    // input channels up to which one lane sums an output
 constexpr int CONV_WIDE_KD = 256;   // terms per output above which 256 lanes share a sum
@@ -142,7 +142,7 @@ __device__ __forceinline__ void conv_out(const ConvArgs& a, int row, int b, int 
 // Split sums: a workgroup of LANES lanes (64 or 256) computes OC rows x NC
 // columns (column = slot * columns per slot + t), E = OC NC <= 32 outputs.
 template <int LANES, int OC, int NC>
-__global__ __launch_bounds__(LANES) void codec_conv_deep_kernel(ConvArgs a) {
+__global__ __launch_bounds__(LANES) void codec_conv_split_kernel(ConvArgs a) {
   constexpr int E = OC * NC, RUNS = LANES / 32;
   static_assert(E <= 32 && LANES % 32 == 0, "at most 32 outputs; runs of 32 lanes");
   __shared__ float red[LANES][E + 1];
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(LANES) void codec_conv_deep_kernel(ConvArgs a) {
 // stride; for the causal form S is the kernel K).  FORM 0 causal,
 // 1 strided, 2 transposed.
 template <int FORM, int OC, int TT, int S>
-__global__ __launch_bounds__(256) void codec_conv_long_kernel(ConvArgs a) {
+__global__ __launch_bounds__(256) void codec_conv_chain_kernel(ConvArgs a) {
   extern __shared__ float wl[];
   constexpr int K = FORM == 0 ? S : 2 * S;
   const int tid = threadIdx.x, o0 = blockIdx.y * OC;
@@ -327,71 +327,71 @@ __global__ __launch_bounds__(256) void codec_conv_long_kernel(ConvArgs a) {
 constexpr long CONV_THREADS = 1L << 15;
 
 template <int FORM, int OC, int TT, int S>
-static void launch_long(const ConvArgs& a, hipStream_t st, int Tc) {
+static void launch_chain(const ConvArgs& a, hipStream_t st, int Tc) {
   const long threads = (long)a.B * ((Tc + TT - 1) / TT);
   const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)((a.C_out + OC - 1) / OC));
   const size_t lds = (size_t)a.C_in * a.K * OC * 4;
-  hipLaunchKernelGGL((codec_conv_long_kernel<FORM, OC, TT, S>), grid, dim3(256), lds, st, a);
+  hipLaunchKernelGGL((codec_conv_chain_kernel<FORM, OC, TT, S>), grid, dim3(256), lds, st, a);
 }
 
 // Chained-sum launch shape (the arithmetic does not depend on it): the largest
 // tile of OC output channels x TT columns that still gives CONV_THREADS
 // threads, else one output channel and one column per thread.
 template <int FORM, int S>
-static void launch_long_tile(const ConvArgs& a, hipStream_t st, int Tc) {
+static void launch_chain_tile(const ConvArgs& a, hipStream_t st, int Tc) {
   auto threads = [&](int oc, int tt) { return (long)a.B * ((a.C_out + oc - 1) / oc) * ((Tc + tt - 1) / tt); };
   if constexpr (FORM == 0) {  // S = K
-    if (a.C_out >= 8 && threads(8, 4) >= CONV_THREADS) launch_long<0, 8, 4, S>(a, st, Tc);
-    else if (a.C_out >= 8 && threads(8, 2) >= CONV_THREADS) launch_long<0, 8, 2, S>(a, st, Tc);
-    else if (a.C_out >= 4 && threads(4, 1) >= CONV_THREADS) launch_long<0, 4, 1, S>(a, st, Tc);
-    else launch_long<0, 1, 1, S>(a, st, Tc);
+    if (a.C_out >= 8 && threads(8, 4) >= CONV_THREADS) launch_chain<0, 8, 4, S>(a, st, Tc);
+    else if (a.C_out >= 8 && threads(8, 2) >= CONV_THREADS) launch_chain<0, 8, 2, S>(a, st, Tc);
+    else if (a.C_out >= 4 && threads(4, 1) >= CONV_THREADS) launch_chain<0, 4, 1, S>(a, st, Tc);
+    else launch_chain<0, 1, 1, S>(a, st, Tc);
   } else if constexpr (FORM == 1) {
-    if (a.C_out >= 8 && threads(8, 2) >= CONV_THREADS) launch_long<1, 8, 2, S>(a, st, Tc);
-    else if (a.C_out >= 4 && threads(4, 1) >= CONV_THREADS) launch_long<1, 4, 1, S>(a, st, Tc);
-    else launch_long<1, 1, 1, S>(a, st, Tc);
+    if (a.C_out >= 8 && threads(8, 2) >= CONV_THREADS) launch_chain<1, 8, 2, S>(a, st, Tc);
+    else if (a.C_out >= 4 && threads(4, 1) >= CONV_THREADS) launch_chain<1, 4, 1, S>(a, st, Tc);
+    else launch_chain<1, 1, 1, S>(a, st, Tc);
   } else {
     constexpr int TT = S >= 8 ? 1 : 8 / S;
-    if (a.C_out >= 4 && threads(4, TT) >= CONV_THREADS) launch_long<2, 4, TT, S>(a, st, Tc);
-    else launch_long<2, 1, 1, S>(a, st, Tc);
+    if (a.C_out >= 4 && threads(4, TT) >= CONV_THREADS) launch_chain<2, 4, TT, S>(a, st, Tc);
+    else launch_chain<2, 1, 1, S>(a, st, Tc);
   }
 }
 
 // FORM 0: by the kernel K; else by the stride
 template <int FORM>
-static void launch_long_s(const ConvArgs& a, hipStream_t st, int Tc) {
+static void launch_chain_s(const ConvArgs& a, hipStream_t st, int Tc) {
   switch (FORM == 0 ? a.K : a.stride) {
-    case 1: launch_long_tile<FORM, 1>(a, st, Tc); break;
-    case 2: launch_long_tile<FORM, 2>(a, st, Tc); break;
-    case 3: launch_long_tile<FORM, 3>(a, st, Tc); break;
-    case 4: launch_long_tile<FORM, 4>(a, st, Tc); break;
-    case 5: launch_long_tile<FORM, 5>(a, st, Tc); break;
-    case 6: launch_long_tile<FORM, 6>(a, st, Tc); break;
-    case 7: launch_long_tile<FORM, 7>(a, st, Tc); break;
-    default: launch_long_tile<FORM, 8>(a, st, Tc); break;
+    case 1: launch_chain_tile<FORM, 1>(a, st, Tc); break;
+    case 2: launch_chain_tile<FORM, 2>(a, st, Tc); break;
+    case 3: launch_chain_tile<FORM, 3>(a, st, Tc); break;
+    case 4: launch_chain_tile<FORM, 4>(a, st, Tc); break;
+    case 5: launch_chain_tile<FORM, 5>(a, st, Tc); break;
+    case 6: launch_chain_tile<FORM, 6>(a, st, Tc); break;
+    case 7: launch_chain_tile<FORM, 7>(a, st, Tc); break;
+    default: launch_chain_tile<FORM, 8>(a, st, Tc); break;
   }
 }
 
 template <int LANES, int OC, int NC>
-static void launch_deep_tile(const ConvArgs& a, hipStream_t st, long ncols, int rows) {
+static void launch_split_tile(const ConvArgs& a, hipStream_t st, long ncols, int rows) {
   const dim3 grid((unsigned)((ncols + NC - 1) / NC), (unsigned)((rows + OC - 1) / OC));
-  hipLaunchKernelGGL((codec_conv_deep_kernel<LANES, OC, NC>), grid, dim3(LANES), 0, st, a);
+  hipLaunchKernelGGL((codec_conv_split_kernel<LANES, OC, NC>), grid, dim3(LANES), 0, st, a);
 }
 
 // Split-sum tile (launch shape only): 32 outputs per workgroup, in columns
 // when the batch has at least as many columns as rows, while that leaves
-// CONV_DEEP_WGS workgroups; else 8; with a single column, 4 rows.
-constexpr long CONV_DEEP_WGS = 512;
+// CONV_SPLIT_WGS workgroups; else 8; with a single column, 4 rows.
+constexpr long CONV_SPLIT_WGS = 512;
 template <int LANES>
-static void launch_deep(const ConvArgs& a, hipStream_t st, int Tc) {
+static void launch_split(const ConvArgs& a, hipStream_t st, int Tc) {
   const long ncols = (long)a.B * Tc;
   const int rows = a.transposed ? a.C_out * a.stride : a.C_out;
   auto wgs = [&](int oc, int nc) { return ((rows + oc - 1) / oc) * ((ncols + nc - 1) / nc); };
   const bool wide = ncols >= rows;
-  if (ncols == 1) launch_deep_tile<LANES, 4, 1>(a, st, ncols, rows);
-  else if (wide && wgs(4, 8) >= CONV_DEEP_WGS) launch_deep_tile<LANES, 4, 8>(a, st, ncols, rows);
-  else if (!wide && wgs(8, 4) >= CONV_DEEP_WGS) launch_deep_tile<LANES, 8, 4>(a, st, ncols, rows);
-  else if (wide) launch_deep_tile<LANES, 2, 4>(a, st, ncols, rows);
-  else launch_deep_tile<LANES, 4, 2>(a, st, ncols, rows);
+  if (ncols == 1) launch_split_tile<LANES, 4, 1>(a, st, ncols, rows);
+  else if (wide && wgs(4, 8) >= CONV_SPLIT_WGS) launch_split_tile<LANES, 4, 8>(a, st, ncols, rows);
+  else if (!wide && wgs(8, 4) >= CONV_SPLIT_WGS) launch_split_tile<LANES, 8, 4>(a, st, ncols, rows);
+  else if (wide) launch_split_tile<LANES, 2, 4>(a, st, ncols, rows);
+  else launch_split_tile<LANES, 4, 2>(a, st, ncols, rows);
 }
 
 // The kernel by the layer's shape (input channels, terms per output), the
@@ -399,14 +399,14 @@ static void launch_deep(const ConvArgs& a, hipStream_t st, int Tc) {
 void launch_codec_conv(const ConvArgs& a, hipStream_t st) {
   const int Tc = a.strided ? a.T_in / a.stride : a.T_in;
   if (a.C_in <= CONV_CHAIN_C) {  // weights of 8 channels in LDS: at most 32 x 16 x 8 floats
-    if (a.transposed) launch_long_s<2>(a, st, Tc);
-    else if (a.strided) launch_long_s<1>(a, st, Tc);
-    else launch_long_s<0>(a, st, Tc);
+    if (a.transposed) launch_chain_s<2>(a, st, Tc);
+    else if (a.strided) launch_chain_s<1>(a, st, Tc);
+    else launch_chain_s<0>(a, st, Tc);
     return;
   }
   const long kd = (long)a.C_in * (a.transposed ? 2 : a.K);
-  if (kd > CONV_WIDE_KD) launch_deep<256>(a, st, Tc);
-  else launch_deep<64>(a, st, Tc);
+  if (kd > CONV_WIDE_KD) launch_split<256>(a, st, Tc);
+  else launch_split<64>(a, st, Tc);
 }
 
 // ---------------------------------------------------------------------------

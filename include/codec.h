@@ -56,6 +56,9 @@
  * Conventions are those of pp.h: bf16 as uint16_t bit patterns, caller-owned
  * device buffers and stream, validate-then-commit, PP_E* return codes,
  * PP_EDEVICE poisons the handle, no C++ exception crosses the interface.
+ * Slots are isolated: a slot's samples and codes depend only on its own
+ * stream, bit for bit the same for every batch size B and every other
+ * slot's content.
  */
 #ifndef PP_CODEC_H
 #define PP_CODEC_H
