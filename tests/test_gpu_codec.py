@@ -32,6 +32,8 @@ residual then carries on from the same row on both sides.
 Parity with the real Mimi codec is unpinned: its layers and weights are not
 available (the structure is a reading of the SoundStream / EnCodec family
 the pages name)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -90,7 +92,7 @@ class _GpuCaches:
 
 
 def _parity_run(cd, w, B, n, seed, report):
-    codes = [synth.agent_frames(seed + b, n) for b in range(B)]
+    codes = [synth.agent_frames(seed + b, n, cd.card)[:, :cd.n_q] for b in range(B)]
     o = oracle_codec.CodecOracle(cd, w, B, np.float64)
     hook = _GpuCaches(cd)
     o.store_hook = hook
@@ -367,3 +369,26 @@ def test_full_encoder_b32_matches_oracle_and_b1():
     e.close()
     _say(f"latent worst rel-L2 {worst[0]:.2e}, transformer output {worst[1]:.2e}; codes {codes.checked}, "
          f"near-tie substitutions {codes.subs}")
+
+
+# Odd shapes that reach the convolution kernels' other branches: fewer than
+# 4 output channels (one channel per thread), stride 1 (transposed and
+# strided), kernels of 1 and 2 taps, a split sum over 64 lanes; then wide
+# kernels (8 and 5 taps, stride 8 with 16 taps), a split sum over 256 lanes,
+# channel counts that are not multiples of 8, and a codebook of 300 rows.
+ODD = [dataclasses.replace(synth.CODEC_TINY, d=64, n_layers=1, n_heads=2, ffn=64, window=3, conv_k=1, res_k=2,
+                           strides=(1, 5), channels=(6, 4, 2), n_q=3, card=130),
+       dataclasses.replace(synth.CODEC_TINY, d=256, n_layers=1, n_heads=2, ffn=256, window=4, conv_k=8, res_k=5,
+                           strides=(8, 3), channels=(96, 44, 40), n_q=4, card=300)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("k", range(len(ODD)))
+def test_odd_codec_shapes_match_oracle_both_directions(k):
+    cd = ODD[k]
+    w = synth.make_codec_weights(cd, seed=10 + k)
+    _say(f"case: codec shape {k}: d {cd.d}, strides {cd.strides}, channels {cd.channels}, kernels "
+         f"{cd.conv_k}/{cd.res_k}, card {cd.card}, B=3, {cd.window + 3} frames, decoder")
+    _parity_run(cd, w, 3, cd.window + 3, 110 + 10 * k, _say)
+    _say(f"case: codec shape {k}, encoder")
+    _encoder_parity_run(cd, w, 3, cd.window + 3, 120 + 10 * k, _say)
