@@ -377,9 +377,10 @@ static void launch_split_tile(const ConvArgs& a, hipStream_t st, long ncols, int
   hipLaunchKernelGGL((codec_conv_split_kernel<LANES, OC, NC>), grid, dim3(LANES), 0, st, a);
 }
 
-// Split-sum tile (launch shape only): 32 outputs per workgroup, in columns
-// when the batch has at least as many columns as rows, while that leaves
-// CONV_SPLIT_WGS workgroups; else 8; with a single column, 4 rows.
+// Split-sum tile (launch shape only): with at most 4 columns in the batch,
+// one row of those columns per workgroup; else 32 outputs per workgroup, in
+// columns when the batch has at least as many columns as rows, while that
+// leaves CONV_SPLIT_WGS workgroups; else 8.
 constexpr long CONV_SPLIT_WGS = 512;
 template <int LANES>
 static void launch_split(const ConvArgs& a, hipStream_t st, int Tc) {
@@ -387,7 +388,9 @@ static void launch_split(const ConvArgs& a, hipStream_t st, int Tc) {
   const int rows = a.transposed ? a.C_out * a.stride : a.C_out;
   auto wgs = [&](int oc, int nc) { return ((rows + oc - 1) / oc) * ((ncols + nc - 1) / nc); };
   const bool wide = ncols >= rows;
-  if (ncols == 1) launch_split_tile<LANES, 4, 1>(a, st, ncols, rows);
+  if (ncols == 1) launch_split_tile<LANES, 1, 1>(a, st, ncols, rows);
+  else if (ncols == 2) launch_split_tile<LANES, 1, 2>(a, st, ncols, rows);
+  else if (ncols <= 4) launch_split_tile<LANES, 1, 4>(a, st, ncols, rows);
   else if (wide && wgs(4, 8) >= CONV_SPLIT_WGS) launch_split_tile<LANES, 4, 8>(a, st, ncols, rows);
   else if (!wide && wgs(8, 4) >= CONV_SPLIT_WGS) launch_split_tile<LANES, 8, 4>(a, st, ncols, rows);
   else if (wide) launch_split_tile<LANES, 2, 4>(a, st, ncols, rows);
