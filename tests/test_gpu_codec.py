@@ -392,3 +392,24 @@ def test_odd_codec_shapes_match_oracle_both_directions(k):
     _parity_run(cd, w, 3, cd.window + 3, 110 + 10 * k, _say)
     _say(f"case: codec shape {k}, encoder")
     _encoder_parity_run(cd, w, 3, cd.window + 3, 120 + 10 * k, _say)
+
+
+# The degenerate and the largest settings: a 1-frame window (attention sees
+# the current frame only) with a single codebook of 64 rows, and the largest
+# window (PP_CODEC_MAX_WINDOW = 256 frames, one full decode split) over more
+# frames than it holds.
+EDGE = [dataclasses.replace(synth.CODEC_TINY, window=1, n_q=1, card=64),
+        dataclasses.replace(synth.CODEC_TINY, window=256)]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("k", range(len(EDGE)))
+def test_edge_codec_windows_match_oracle_both_directions(k):
+    cd = EDGE[k]
+    w = synth.make_codec_weights(cd, seed=20 + k)
+    n = cd.window + 4
+    B = 2 if k == 0 else 1
+    _say(f"case: codec window {cd.window}, n_q {cd.n_q}, card {cd.card}, B={B}, {n} frames, decoder")
+    _parity_run(cd, w, B, n, 130 + 10 * k, _say)
+    _say(f"case: codec window {cd.window}, encoder")
+    _encoder_parity_run(cd, w, B, n, 140 + 10 * k, _say)
