@@ -287,6 +287,13 @@ void record_transformer(pp_codec* h, hipStream_t s, const TfWeights& tw, size_t 
 
   const long pq = packed_elems(3 * d, d), pwo = packed_elems(d, d), pi = packed_elems(2 * F, d),
              pd = packed_elems(d, F);
+  // From 8 slots on, the codec's matrices (a few MB per layer) are loaded as
+  // cache-resident weights: that lets the GEMMs split the batch into slot
+  // groups, each re-reading the weights from the cache with fewer activation
+  // bytes per workgroup (decode call at B = 32: 0.545 against 0.638 ms; at
+  // B = 8: 0.396 against 0.417 ms; at B = 1 streamed weights stay faster,
+  // 0.288 against 0.300 ms).  The arithmetic is the same either way.
+  const int KEEP = B >= 8 ? 1 : 0;
   for (int l = 0; l < dm.n_layers; ++l) {
     bf16_t* ring_l = h->at<bf16_t>(ring_off) + (long)l * L.ring_layer_elems;
     GemmArgs g{};
@@ -312,6 +319,7 @@ void record_transformer(pp_codec* h, hipStream_t s, const TfWeights& tw, size_t 
     g.ti = ti;
     g.inv_freq = h->at<double>(L.inv_freq);
     g.rope = h->at<float>(rope_off);
+    g.w_keep = KEEP;
     launch_gemm(EPI_QKV, g, s);
 
     AttnArgs at{};
@@ -347,6 +355,7 @@ void record_transformer(pp_codec* h, hipStream_t s, const TfWeights& tw, size_t 
     go.xa_lo = (long)B * d;
     go.alpha_next = tw.mlp_norm + (long)l * d;
     go.part_out = h->at<float>(L.part);
+    go.w_keep = KEEP;
     launch_gemm(EPI_RESID, go, s);
 
     GemmArgs gu{};
@@ -365,6 +374,7 @@ void record_transformer(pp_codec* h, hipStream_t s, const TfWeights& tw, size_t 
     gu.m_out = h->at<bf16_t>(L.m);
     gu.ldm = F;
     gu.m_lo = (long)B * F;
+    gu.w_keep = KEEP;
     launch_gemm(EPI_GATED, gu, s);
 
     GemmArgs gd{};
@@ -381,6 +391,7 @@ void record_transformer(pp_codec* h, hipStream_t s, const TfWeights& tw, size_t 
     gd.xa_lo = (long)B * d;
     gd.alpha_next = (l + 1 < dm.n_layers) ? tw.attn_norm + (long)(l + 1) * d : tw.out_norm;
     gd.part_out = h->at<float>(L.part);
+    gd.w_keep = KEEP;
     launch_gemm(EPI_RESID, gd, s);
   }
 
