@@ -363,3 +363,31 @@ def test_encoder_conv_stack_closed_form():
         v = (v if v > 0 else np.expm1(v)) + b_out
         np.testing.assert_allclose(y[0], v, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(y[1:], 0.0, atol=0)
+
+
+def test_convolutions_match_torch_on_random_shapes():
+    """The three convolution forms against PyTorch's routines over 60 random
+    shapes each (channels 1-9, kernels 1-8, strides 1-8, 1-7 frames' worth of
+    inputs), each call with a random history: the output must equal the
+    tail of the routine's output over (history, input)."""
+    rng = np.random.default_rng(2026)
+    F = torch.nn.functional
+    for _ in range(60):
+        ci, co = int(rng.integers(1, 10)), int(rng.integers(1, 10))
+        K, s, n = int(rng.integers(1, 9)), int(rng.integers(1, 9)), int(rng.integers(1, 8))
+        b = rng.normal(size=co)
+        # causal, kernel K: history K - 1
+        x, w, h = rng.normal(size=(ci, n)), rng.normal(size=(co, ci, K)), rng.normal(size=(ci, K - 1))
+        ref = F.conv1d(torch.tensor(np.concatenate([h, x], 1))[None], torch.tensor(w), torch.tensor(b))[0].numpy()
+        np.testing.assert_allclose(codec.causal_conv(x, w, b, h), ref, rtol=1e-12, atol=1e-12)
+        # strided, stride s, kernel 2 s: history s, n blocks of s inputs
+        x, w, h = rng.normal(size=(ci, n * s)), rng.normal(size=(co, ci, 2 * s)), rng.normal(size=(ci, s))
+        ref = F.conv1d(torch.tensor(np.concatenate([h, x], 1))[None], torch.tensor(w), torch.tensor(b),
+                       stride=s)[0].numpy()
+        np.testing.assert_allclose(codec.strided_conv_causal(x, w, b, h, s), ref, rtol=1e-12, atol=1e-12)
+        # transposed, stride s, kernel 2 s: the previous input, then n inputs;
+        # the routine's outputs s .. s + n s - 1 are this call's
+        x, w, p = rng.normal(size=(ci, n)), rng.normal(size=(co, ci, 2 * s)), rng.normal(size=(ci, 1))
+        ref = F.conv_transpose1d(torch.tensor(np.concatenate([p, x], 1))[None], torch.tensor(w.transpose(1, 0, 2)),
+                                 torch.tensor(b), stride=s)[0].numpy()[:, s:s + n * s]
+        np.testing.assert_allclose(codec.conv_transpose_causal(x, w, b, p, s), ref, rtol=1e-12, atol=1e-12)
