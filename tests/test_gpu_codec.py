@@ -413,3 +413,27 @@ def test_edge_codec_windows_match_oracle_both_directions(k):
     _parity_run(cd, w, B, n, 130 + 10 * k, _say)
     _say(f"case: codec window {cd.window}, encoder")
     _encoder_parity_run(cd, w, B, n, 140 + 10 * k, _say)
+
+
+def _random_dims(seed):
+    """A small codec with random stage count (1-3), strides (1-8), kernels
+    (1-8), channel counts (even, up to 48 after the first convolution's up to
+    80) and codebooks: reaches the convolution kernels' template branches."""
+    r = np.random.default_rng(seed)
+    n = int(r.integers(1, 4))
+    strides = tuple(int(v) for v in r.integers(1, 9, n))
+    channels = (int(r.integers(4, 81)),) + tuple(2 * int(v) for v in r.integers(1, 25, n))
+    return dataclasses.replace(synth.CODEC_TINY, d=64, n_layers=1, n_heads=2, ffn=64, window=2,
+                               conv_k=int(r.integers(1, 9)), res_k=int(r.integers(1, 9)), strides=strides,
+                               channels=channels, n_q=int(r.integers(1, 5)), card=int(r.integers(16, 200)))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("seed", range(6))
+def test_random_codec_shapes_match_oracle_both_directions(seed):
+    cd = _random_dims(1000 + seed)
+    w = synth.make_codec_weights(cd, seed=40 + seed)
+    _say(f"case: random codec {seed}: strides {cd.strides}, channels {cd.channels}, kernels {cd.conv_k}/{cd.res_k}, "
+         f"n_q {cd.n_q}, card {cd.card}, B=2, 5 frames")
+    _parity_run(cd, w, 2, 5, 200 + seed, _say)
+    _encoder_parity_run(cd, w, 2, 5, 300 + seed, _say)
