@@ -146,7 +146,7 @@ int pp_codec_samples(const pp_codec_dims* dims);
  * or B outside 1..PP_CODEC_MAX_BATCH. */
 int pp_codec_arena_bytes(const pp_codec_dims* dims, int B, size_t* out_bytes);
 
-/* Creates a decoder for B slots in the caller's arena (256-byte aligned, at
+/* Creates a codec handle (decoder and encoder) for B slots in the caller's arena (256-byte aligned, at
  * least pp_codec_arena_bytes) on the caller's stream, every slot fresh
  * (position 0, zero history).  Captures its graphs.  PP_EINVAL for a NULL or
  * invalid argument, PP_ENOSPC for a small arena, PP_EDEVICE if a HIP call
