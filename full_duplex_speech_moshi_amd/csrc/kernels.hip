@@ -566,6 +566,128 @@ __global__ __launch_bounds__(512) void gemm_group_kernel(GemmArgs a) {
   gemm_unit<EPI, 1, NTL, 0, UB>(v, blockIdx.x, smem);
 }
 
+// Slot groups with two row tiles per workgroup, for the cache-resident
+// (depformer) GEMMs once the batch spans two slot groups: blockIdx.y takes
+// slots G*y .. G*y+G-1 as gemm_group_kernel does, and workgroup x the TT
+// output tiles TT*x .. TT*x+TT-1 (for the gated MLP each output tile is a
+// gate and an up weight tile) over the whole K.  Wave w owns k-range
+// R_(w+x) mod 8 of every one of them and accumulates it in k-step order, hi
+// then lo, as the one-tile kernel's wave w accumulates R_w; the 8 range
+// partials of a tile are summed in range order in LDS and the common epilogue
+// runs per tile, so the bits are the contract's.  Each k-step's activation
+// operand (16 slots) is loaded once for RT*TT weight tiles, halving the
+// activation reads that bound these launches at large batch; the range
+// rotation keeps neighbouring workgroups on different activation lines.
+template <int EPI, int TT>
+__global__ __launch_bounds__(512) void gemm_tiles_kernel(GemmArgs a0) {
+  constexpr int NT = 1;
+  const int gs0 = blockIdx.y * a0.slot_grp;
+  const GemmArgs a = slot_view(a0, gs0, min(a0.slot_grp, a0.B - gs0));
+  constexpr int RT = (EPI == EPI_GATED) ? 2 : 1, NW = RT * TT, U = 2;
+  __shared__ float red[GEMM_WAVES][NW * NT][256];  // [range][weight tile * NT + column tile][element]
+  __shared__ EpiSmem<RT, NT> e;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = (wave + (int)blockIdx.x) & (GEMM_WAVES - 1);  // this wave's k-range
+  const int ksteps = a.K >> 5;
+  const int s0 = (ksteps * rg) / GEMM_WAVES, s1 = (ksteps * (rg + 1)) / GEMM_WAVES;
+  const int n_out = (a.M + ROWS - 1) / ROWS;
+  const int tile0 = (int)blockIdx.x * TT;
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+
+  // weight tile w = rt * TT + tt: output tile tile0 + tt (a tile past the
+  // last loads the last one's weights again; its results are not stored)
+  const bf16_t* arow[NW];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const long t = min(tile0 + tt, n_out - 1) + (rt ? a.gate_off / ROWS : 0);
+      arow[rt * TT + tt] = a.W + t * ksteps * 512 + lane * 8;
+    }
+  // activation rows in row order (lane 4c + p: 16-byte piece p of slot c),
+  // moved into the MFMA operand order (lane 16p + c) by a lane permute
+  const int xsrc = ((lane & 15) * 4 + (lane >> 4)) * 4;
+  const bf16_t* xrow[NT];
+  bool b_ok[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    const int c = ct * 16 + (lane >> 2);
+    b_ok[ct] = c < a.B;
+    xrow[ct] = a.X + (long)(b_ok[ct] ? c : 0) * a.ldx + (lane & 3) * 8;
+  }
+  auto xop = [&](const u32x4& v) -> bf16x8 {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc, (int)v[i]);
+    return __builtin_bit_cast(bf16x8, r);
+  };
+
+  EpiPre pre[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) pre[tt] = epi_preload<EPI, NT>(a, min(tile0 + tt, n_out - 1));
+  RmsPre<NT> rp;
+  if (EPI != EPI_RESID) rms_preload<NT>(a, rp);
+
+  f32x4 acc[NW][NT];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[w][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int s = s0; s < s1; s += U) {
+    u32x4 av[NW][U], bh[NT][U], bl[NT][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = (s + u) < s1;
+      const int k = (s + u) * 32;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) av[w][u] = ok ? ldw16<false>(arow[w] + (long)(s + u) * 512) : zero;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        bh[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + k) : zero;
+        bl[ct][u] = (ok && b_ok[ct]) ? ld16(xrow[ct] + a.x_lo + k) : zero;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const bf16x8 xh = xop(bh[ct][u]), xl = xop(bl[ct][u]);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const bf16x8 w8 = __builtin_bit_cast(bf16x8, av[w][u]);
+          acc[w][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, xh, acc[w][ct], 0, 0, 0);
+          acc[w][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, xl, acc[w][ct], 0, 0, 0);
+        }
+      }
+  }
+
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[rg][w * NT + ct][j * 64 + lane] = acc[w][ct][j];
+  if (EPI != EPI_RESID) rms_finish<NT>(a, rp, e.inv_rms);
+  __syncthreads();
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int tile = tile0 + tt;
+    if (tile >= n_out) break;  // the same in every thread
+    for (int idx = tid; idx < RT * NT * 256; idx += 512) {
+      const int b = idx >> 8, el = idx & 255;
+      const int rt = b / NT, ct = b % NT, j = el >> 6, ln = el & 63;
+      const int blk = (rt * TT + tt) * NT + ct;
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < GEMM_WAVES; ++r) sum += red[r][blk][el];
+      e.fin[rt][4 * (ln >> 4) + j][ct * 16 + (ln & 15)] = sum;
+    }
+    __syncthreads();
+    gemm_epilogue<EPI, NT>(a, tile, e, pre[tt]);
+    __syncthreads();
+  }
+}
+
 // Depformer out-projection that computes its input, the attention output,
 // itself (B <= DEP_FUSE_B): saves the attention launch of every layer-step.
 __global__ __launch_bounds__(512) void gemm_att_kernel(GemmArgs a) {
@@ -1005,6 +1127,15 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
       // 7B device tick: -0.03 ms at B = 1, -0.04 at B = 4, -0.06 at B = 8;
       // batches of 2, 3, 6 and 16 were slower than 4.
       hipLaunchKernelGGL((gemm_kernel<EPI_RESID, 1, true, 4>), dim3(tiles), dim3(512), 0, s, v);
+    } else if (a.w_keep && groups > 1 && (EPI == EPI_QKV || EPI == EPI_GATED || (EPI == EPI_RESID && a.K == a.M))) {
+      // cache-resident weights, two slot groups or more: two row tiles per
+      // workgroup.  Measured on the 7B device tick with every ring full, for
+      // the QKV, gate/up and out-projection GEMMs of the depformer: -0.16 ms
+      // at B = 24, -0.22 ms at B = 32.  With one group it lost (+0.04 ms at
+      // B = 8, 12 and 16); at B = 32, against two tiles, so did 4 tiles
+      // (+0.27 ms), 3 tiles for QKV (+0.03 ms) and the down-projection in
+      // two-tile groups of 16 slots (+0.08 ms)
+      hipLaunchKernelGGL((gemm_tiles_kernel<EPI, 2>), dim3((tiles + 1) / 2, groups), dim3(512), 0, s, v);
     } else if (groups > 1) {
       if (a.w_keep) hipLaunchKernelGGL((gemm_group_kernel<EPI, false>), dim3(tiles, groups), dim3(512), 0, s, v);
       else hipLaunchKernelGGL((gemm_group_kernel<EPI, true>), dim3(tiles, groups), dim3(512), 0, s, v);
