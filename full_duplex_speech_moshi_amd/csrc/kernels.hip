@@ -1082,6 +1082,7 @@ static int slot_group(int epi, const GemmArgs& a) {
 template <int EPI>
 static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
   const int tiles = (a.M + ROWS - 1) / ROWS;
+  constexpr bool TILES2 = EPI == EPI_QKV || EPI == EPI_GATED || EPI == EPI_RESID;  // epilogues with a two-tile form
   if (EPI == EPI_RESID && a.fuse_att) {  // caller guarantees B <= DEP_FUSE_B, K <= DEP_FUSE_D
     hipLaunchKernelGGL(gemm_att_kernel, dim3(tiles), dim3(512), 0, s, a);
     return;
@@ -1127,7 +1128,7 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
       // 7B device tick: -0.03 ms at B = 1, -0.04 at B = 4, -0.06 at B = 8;
       // batches of 2, 3, 6 and 16 were slower than 4.
       hipLaunchKernelGGL((gemm_kernel<EPI_RESID, 1, true, 4>), dim3(tiles), dim3(512), 0, s, v);
-    } else if (a.w_keep && groups > 1 && (EPI == EPI_QKV || EPI == EPI_GATED || (EPI == EPI_RESID && a.K == a.M))) {
+    } else if (TILES2 && a.w_keep && groups > 1 && (EPI != EPI_RESID || a.K == a.M)) {
       // cache-resident weights, two slot groups or more: two row tiles per
       // workgroup.  Measured on the 7B device tick with every ring full, for
       // the QKV, gate/up and out-projection GEMMs of the depformer: -0.16 ms
@@ -1135,7 +1136,7 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
       // B = 8, 12 and 16); at B = 32, against two tiles, so did 4 tiles
       // (+0.27 ms), 3 tiles for QKV (+0.03 ms) and the down-projection in
       // two-tile groups of 16 slots (+0.08 ms)
-      hipLaunchKernelGGL((gemm_tiles_kernel<EPI, 2>), dim3((tiles + 1) / 2, groups), dim3(512), 0, s, v);
+      if constexpr (TILES2) hipLaunchKernelGGL((gemm_tiles_kernel<EPI, 2>), dim3((tiles + 1) / 2, groups), dim3(512), 0, s, v);
     } else if (groups > 1) {
       if (a.w_keep) hipLaunchKernelGGL((gemm_group_kernel<EPI, false>), dim3(tiles, groups), dim3(512), 0, s, v);
       else hipLaunchKernelGGL((gemm_group_kernel<EPI, true>), dim3(tiles, groups), dim3(512), 0, s, v);
