@@ -243,14 +243,16 @@ def test_full_isolation_large_batch_path_bit_exact(full):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("B", [8, 9, 10, 13, 16])
+@pytest.mark.parametrize("B", [8, 9, 10, 13, 16, 17, 24])
 def test_full_isolation_slot_groups_bit_exact(full, B):
     """B = 8 to 16 run the depformer down-projection in slot groups of
     ceil(B / 4) slots per workgroup.  From B = 9 the temporal GEMMs take the
     large-batch path one by one, each with one 16-column tile (QKV from 9;
     down-projection and heads from 10; gate/up from 14), so B = 9, 10, 13 and
-    16 mix the two paths within a layer.  The first and last slots must equal
-    B = 1 handles bit for bit."""
+    16 mix the two paths within a layer.  From B = 17 the depformer QKV,
+    gate/up and out-projection run two row tiles per workgroup in 16-slot
+    groups: B = 17 leaves one slot in the second group, B = 24 eight.  The
+    first and last slots must equal B = 1 handles bit for bit."""
     _say(f"case: 7B isolation, B={B} (depformer slot groups) vs B=1")
     fill = synth.ring_fill(DM, 9, 24)
     codes = [synth.user_codes(900 + b, 2) for b in range(B)]
