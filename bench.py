@@ -89,12 +89,13 @@ def traffic_parts(kernel: str, B: int):
     shape: (kernel-name substring, workgroups or None for any).  The temporal
     gate/up runs as one small-batch launch below B = 14 (704 workgroups, one
     per gate/up row-tile pair) and as main loop plus ordered reduce from
-    B = 14 on (one 16-column tile up to B = 16, two above)."""
+    B = 14 on (one 16-column tile up to B = 16, two above; each wave of the
+    main loop takes 3 of the 1408 gate and up weight tiles side by side)."""
     if kernel == "gate_up":
         if B < 14:
             return [["gemm_kernel<2, 1, true, 0>", 704]]
         c = 1 if B <= 16 else 2
-        return [[f"gemm_wide_res_kernel<2, {c}>", None], [f"gemm_wide_reduce<2, {c}>", None]]
+        return [[f"gemm_wide_res_kernel<2, {c}, 3>", None], [f"gemm_wide_reduce<2, {c}>", None]]
     if kernel == "attention":
         return [["attn_kernel<128>", None]]
     raise ValueError(f"no counter recipe for {kernel}")

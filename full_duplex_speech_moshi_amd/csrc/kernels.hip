@@ -11,6 +11,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace pp {
 
@@ -860,18 +861,18 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs a) {
 
 // The same partials for k-ranges of exactly WIDE_RES k-steps (K = 4096):
 // workgroup (p, j), j = blockIdx % 8, loads the activation slice of range
-// R_j into LDS once, then each wave streams the weights of tiles
-// p * 8 + wave + i * 8P (P = gridDim / 8, i < tiles per wave) through it.
-// The weights roll: once k-step q of tile i has been multiplied, its
-// registers are refilled with k-step q of tile i + 1, so a whole range of
-// loads stays in flight per wave; no barrier after the slice is loaded.  Per
-// tile, a wave's accumulation is the contract's k-step order, hi then lo.
+// R_j into LDS once, then each wave streams the weights of its TPW tiles
+// p * 8 + wave + i * 8P (P = gridDim / 8, i < TPW) through it, the tiles side
+// by side: each k-step's activation fragment is read from LDS once for all of
+// them (a wave reading it once per tile was bound by LDS bandwidth at large
+// B).  No barrier after the slice is loaded.  Per tile, a wave's accumulation
+// is the contract's k-step order, hi then lo.
 constexpr int WIDE_RES = 16;  // k-steps of one range held in LDS
 constexpr int WIDE_RES_WGS = 512;  // workgroups: two per compute unit
 
 inline int wide_res_tpw(long tiles) { return (int)((tiles + 8L * (WIDE_RES_WGS / 8) - 1) / (8L * (WIDE_RES_WGS / 8))); }
 
-template <int RT, int NT>
+template <int RT, int NT, int TPW>
 __global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
   constexpr int NTC = NT * 16, CS = NT == 2 ? 5 : 4;  // columns held, log2 of it
   __shared__ __attribute__((aligned(16))) bf16_t xs[2][WIDE_RES][NTC][32];  // [hi/lo][k-step][column]
@@ -882,7 +883,6 @@ __global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
   const int s0 = j * WIDE_RES;
   const int n_out = (a.M + ROWS - 1) / ROWS;
   const long T = (long)RT * n_out;
-  const int tpw = (int)((T + 8L * P - 1) / (8L * P));
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
 
   if (a.wide_rms && blockIdx.x == 0) {
@@ -897,21 +897,29 @@ __global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
   // the wave's i-th tile: its weights at k-step s0 (nullptr past the last tile)
   auto tile_w = [&](int i) -> const bf16_t* {
     const long t = (long)p * GEMM_WAVES + wave + (long)i * 8 * P;
-    if (i >= tpw || t >= T) return nullptr;
+    if (t >= T) return nullptr;
     const long wt = (RT == 2 && t >= n_out) ? t - n_out + a.gate_off / ROWS : t;
     return a.W + (wt * ks + s0) * 512 + lane * 8;
   };
 
-  // (branches on tile validity are wave-uniform, so the loads stay in
-  // straight-line code and only wait for their own k-step)
-  u32x4 wr[WIDE_RES];
-  if (const bf16_t* w = tile_w(0)) {
+  // The wave's tiles advance side by side: at k-step q the activation
+  // fragment is read from LDS once and multiplied into every tile's
+  // accumulator; the weights of k-step q + D of every tile are requested as
+  // k-step q is consumed.  Per tile the accumulation is the contract's k-step
+  // order, hi then lo.
+  constexpr int D = TPW >= 4 ? 2 : 4;  // k-steps of each tile in flight
+  const bf16_t* wp[TPW];
+  bool wv[TPW];
 #pragma unroll
-    for (int q = 0; q < WIDE_RES; ++q) wr[q] = ldw16<true>(w + (long)q * 512);
-  } else {
-#pragma unroll
-    for (int q = 0; q < WIDE_RES; ++q) wr[q] = zero;
+  for (int i = 0; i < TPW; ++i) {
+    wp[i] = tile_w(i);
+    wv[i] = wp[i] != nullptr;
   }
+  u32x4 wr[TPW][D];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int q = 0; q < D; ++q) wr[i][q] = wv[i] ? ldw16<true>(wp[i] + (long)q * 512) : zero;
   // the range's activation slice: piece i = tid + 512 u is 16 bytes of plane
   // i >> (6 + CS), k-step (i >> (2 + CS)) & 15, column (i >> 2) % NTC, part i & 3
 #pragma unroll
@@ -923,34 +931,34 @@ __global__ __launch_bounds__(512) void gemm_wide_res_kernel(GemmArgs a) {
   }
   __syncthreads();
 
-  auto mul = [&](int q, f32x4 (&acc)[NT]) {
-    const bf16x8 w8 = __builtin_bit_cast(bf16x8, wr[q]);
+  f32x4 acc[TPW][NT];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[i][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < WIDE_RES; ++q) {
+    u32x4 bh[NT], bl[NT];
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
-      const u32x4 bh = *reinterpret_cast<const u32x4*>(&xs[0][q][ct * 16 + r16][xs_chunk(r16, g4) * 8]);
-      const u32x4 bl = *reinterpret_cast<const u32x4*>(&xs[1][q][ct * 16 + r16][xs_chunk(r16, g4) * 8]);
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh), acc[ct], 0, 0, 0);
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl), acc[ct], 0, 0, 0);
+      bh[ct] = *reinterpret_cast<const u32x4*>(&xs[0][q][ct * 16 + r16][xs_chunk(r16, g4) * 8]);
+      bl[ct] = *reinterpret_cast<const u32x4*>(&xs[1][q][ct * 16 + r16][xs_chunk(r16, g4) * 8]);
     }
-  };
-
-  for (int i = 0; i < tpw; ++i) {
-    const long t = (long)p * GEMM_WAVES + wave + (long)i * 8 * P;
-    const bf16_t* wn = tile_w(i + 1);
-    f32x4 acc[NT];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    if (wn) {
+    for (int i = 0; i < TPW; ++i) {
+      const bf16x8 w8 = __builtin_bit_cast(bf16x8, wr[i][q % D]);
 #pragma unroll
-      for (int q = 0; q < WIDE_RES; ++q) {
-        mul(q, acc);
-        wr[q] = ldw16<true>(wn + (long)q * 512);
+      for (int ct = 0; ct < NT; ++ct) {
+        acc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bh[ct]), acc[i][ct], 0, 0, 0);
+        acc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w8, __builtin_bit_cast(bf16x8, bl[ct]), acc[i][ct], 0, 0, 0);
       }
-    } else {
-#pragma unroll
-      for (int q = 0; q < WIDE_RES; ++q) mul(q, acc);
+      if (q + D < WIDE_RES) wr[i][q % D] = wv[i] ? ldw16<true>(wp[i] + (long)(q + D) * 512) : zero;
     }
-    if (t < T) store_partial<NT>(a, t, j, acc, lane);
+  }
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const long t = (long)p * GEMM_WAVES + wave + (long)i * 8 * P;
+    if (wv[i]) store_partial<NT>(a, t, j, acc[i], lane);
   }
 }
 
@@ -1100,8 +1108,20 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
     if ((a.K >> 5) == GEMM_WAVES * WIDE_RES) {
       const long T = wide_tiles(EPI, a.M);
       const long P = (T + 8L * wide_res_tpw(T) - 1) / (8L * wide_res_tpw(T));
-      if (one) hipLaunchKernelGGL((gemm_wide_res_kernel<RT, 1>), dim3(P * GEMM_WAVES), dim3(512), 0, s, w);
-      else hipLaunchKernelGGL((gemm_wide_res_kernel<RT, 2>), dim3(P * GEMM_WAVES), dim3(512), 0, s, w);
+      // the wave's tiles side by side (TPW in registers).  Measured on the 7B
+      // device tick with every ring full, against one tile after another:
+      // -0.19 to -0.30 ms at B = 32, -0.14 ms at B = 16 (gate/up 4.16 -> 4.33
+      // TB/s and QKV 4.34 -> 4.54 TB/s at B = 32)
+      const int tpw = wide_res_tpw(T);
+      auto go = [&](auto tp) {
+        constexpr int TP = decltype(tp)::value;
+        if (one) hipLaunchKernelGGL((gemm_wide_res_kernel<RT, 1, TP>), dim3(P * GEMM_WAVES), dim3(512), 0, s, w);
+        else hipLaunchKernelGGL((gemm_wide_res_kernel<RT, 2, TP>), dim3(P * GEMM_WAVES), dim3(512), 0, s, w);
+      };
+      if (tpw <= 1) go(std::integral_constant<int, 1>{});
+      else if (tpw == 2) go(std::integral_constant<int, 2>{});
+      else if (tpw == 3) go(std::integral_constant<int, 3>{});
+      else go(std::integral_constant<int, 4>{});
     } else {
       if (one) hipLaunchKernelGGL((gemm_wide_kernel<RT, 1>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, w);
       else hipLaunchKernelGGL((gemm_wide_kernel<RT, 2>), dim3(groups * GEMM_WAVES), dim3(512), 0, s, w);

@@ -98,12 +98,12 @@ def test_traffic_summary_adds_main_loop_and_reduce(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     parts = bench.traffic_parts("gate_up", 32)
-    assert [p[0] for p in parts] == ["gemm_wide_res_kernel<2, 2>", "gemm_wide_reduce<2, 2>"]
-    assert [p[0] for p in bench.traffic_parts("gate_up", 16)] == ["gemm_wide_res_kernel<2, 1>",
+    assert [p[0] for p in parts] == ["gemm_wide_res_kernel<2, 2, 3>", "gemm_wide_reduce<2, 2>"]
+    assert [p[0] for p in bench.traffic_parts("gate_up", 16)] == ["gemm_wide_res_kernel<2, 1, 3>",
                                                                    "gemm_wide_reduce<2, 1>"]
     run = tmp_path / "run"
     copy_kib = bench.COPY_PROBE_BYTES / 1024
-    main, red = "void pp::gemm_wide_res_kernel<2, 2>(pp::WideArgs)", "void pp::gemm_wide_reduce<2, 2>(pp::WideArgs)"
+    main, red = "void pp::gemm_wide_res_kernel<2, 2, 3>(pp::GemmArgs)", "void pp::gemm_wide_reduce<2, 2>(pp::GemmArgs)"
     _counter_csv(str(run / "pmc_fetch" / "b32_counter_collection.csv"), "FETCH_SIZE",
                  [("__amd_rocclr_copyBuffer", 256 * 512, copy_kib / 2), (main, 472 * 512, 100.0),
                   (main, 472 * 512, 110.0), (red, 704 * 512, 20.0)])
