@@ -1238,9 +1238,12 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
 #pragma unroll
     for (int i = 0; i < 8; ++i) qv[i] = qp[i];
   }
-  const bf16_t* kb = a.kv + (long)b * a.kv_slot_stride + (long)h * a.window * DH + sub * 8;
-  const bf16_t* vb = kb + a.kv_v_off;
 
+  // Ring row of key j: (r0 + j) mod W, with r0 < W and j < W.  The head's
+  // key and value bases are uniform; one 32-bit lane offset serves both.
+  const int r0 = (P.lo + k0) % a.window;
+  const char* kbase = reinterpret_cast<const char*>(a.kv + (long)b * a.kv_slot_stride + (long)h * a.window * DH);
+  const char* vbase = kbase + a.kv_v_off * (long)sizeof(bf16_t);
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
   u32x4 kr[ITER], vr[ITER];
 #pragma unroll
@@ -1249,9 +1252,11 @@ __device__ void attn_unit(const AttnArgs& a, const int h, const int b, const int
     kr[it] = zero;
     vr[it] = zero;
     if (j < kn) {
-      const long off = (long)((P.lo + k0 + j) % a.window) * DH;
-      kr[it] = ldw16<true>(kb + off);  // read once per tick: non-temporal
-      vr[it] = ldw16<true>(vb + off);
+      int row = r0 + j;
+      row -= row >= a.window ? a.window : 0;
+      const uint32_t off = (uint32_t)(row * DH + sub * 8) * (uint32_t)sizeof(bf16_t);
+      kr[it] = ldw16<true>(reinterpret_cast<const bf16_t*>(kbase + off));  // read once per tick: non-temporal
+      vr[it] = ldw16<true>(reinterpret_cast<const bf16_t*>(vbase + off));
     }
   }
 
