@@ -14,7 +14,12 @@ free-running on its first tick with an empty queue and then refuses
 prefills (PP_EBUSY); fills are legal only before any tick or prefill; every
 error except PP_EDEVICE leaves the state unchanged (validate-then-commit);
 a device error poisons the handle; reset equals a fresh handle; the
-acoustic delay shifts codebooks 1-7.  Test infrastructure only."""
+acoustic delay shifts codebooks 1-7.  Test infrastructure only.
+
+With PP_HOST_SANITIZE=1 the stub library is built with AddressSanitizer and
+UndefinedBehaviorSanitizer; the interpreter then needs their runtimes
+preloaded, e.g. LD_PRELOAD="$(g++ -print-file-name=libasan.so)
+$(g++ -print-file-name=libubsan.so)" ASAN_OPTIONS=detect_leaks=0."""
 import ctypes
 import os
 import subprocess
@@ -35,7 +40,10 @@ VT, A = DM.text_card, DM.audio_card
 @pytest.fixture(scope="module")
 def lib(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("hoststub") / "libpp_hoststub.so")
-    cmd = ["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-I", os.path.join(ROOT, "tests", "hoststub"),
+    checks = ",".join(("address", "undefined"))  # host code only: the stub build has no device code
+    san = (["-g", "-fsanitize=" + checks, "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+           if os.environ.get("PP_HOST_SANITIZE") == "1" else [])
+    cmd = ["g++", "-O1", *san, "-std=c++17", "-shared", "-fPIC", "-I", os.path.join(ROOT, "tests", "hoststub"),
            "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "full_duplex_speech_moshi_amd", "csrc", "engine.cpp"),
            os.path.join(ROOT, "tests", "hoststub", "hoststub.cpp"), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
