@@ -1161,6 +1161,13 @@ static void launch_gemm_nt(const GemmArgs& a, hipStream_t s) {
       // (+0.27 ms), 3 tiles for QKV (+0.03 ms) and the down-projection in
       // two-tile groups of 16 slots (+0.08 ms)
       if constexpr (TILES2) hipLaunchKernelGGL((gemm_tiles_kernel<EPI, 2>), dim3((tiles + 1) / 2, groups), dim3(512), 0, s, v);
+    } else if (EPI == EPI_RESID && a.w_keep && G >= 8 && deep_batch(a)) {
+      // the depformer down-projection in slot groups of 8 or more: the whole
+      // k-range in one load batch (256 workgroups, one per compute unit).
+      // Measured on the 7B device tick with every ring full: -0.05 to -0.10
+      // ms at B = 32 (groups of 8); with groups of 4 and 2 (B = 16 and 8) it
+      // was slower, +0.12 and +0.10 ms
+      hipLaunchKernelGGL((gemm_group_kernel<EPI_RESID, false, 12>), dim3(tiles, groups), dim3(512), 0, s, v);
     } else if (groups > 1) {
       if (a.w_keep) hipLaunchKernelGGL((gemm_group_kernel<EPI, false>), dim3(tiles, groups), dim3(512), 0, s, v);
       else hipLaunchKernelGGL((gemm_group_kernel<EPI, true>), dim3(tiles, groups), dim3(512), 0, s, v);
